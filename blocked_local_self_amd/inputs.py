@@ -1,0 +1,47 @@
+"""Seeded synthetic inputs for halo attention.
+
+This module draws random tensors and nothing else: it holds none of the
+attention arithmetic, so both the GPU path and the CPU checker can take their
+inputs from it.
+
+Recipe (one CPU ``torch.Generator`` per call, seeded): q, k, v are drawn in that
+order as N(0, 1) float32 tensors of shape [B, heads, H, W, d]; then rel_h and
+rel_w, each [2r-1, d] with r = block + 2*halo, drawn N(0, 1) and multiplied by
+d**-0.5 (the initialisation of the relative tables in the HaloAttention module
+on the pswp.cn blog page, section 4).  Every tensor is then rounded to the
+workload dtype (round-to-nearest-even for bf16), tables included.
+"""
+from __future__ import annotations
+
+import torch
+
+_DTYPES = {"fp32": torch.float32, "bf16": torch.bfloat16}
+
+
+def torch_dtype(name: str) -> torch.dtype:
+    try:
+        return _DTYPES[name]
+    except KeyError:
+        raise ValueError(f"unknown dtype {name!r}; expected one of {sorted(_DTYPES)}") from None
+
+
+def make_inputs(B: int, heads: int, H: int, W: int, d: int, block: int, halo: int,
+                dtype: str = "bf16", seed: int = 0, device: str | torch.device = "cpu"):
+    """Return (q, k, v, rel_h, rel_w) drawn as described in the module docstring."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    r = block + 2 * halo
+    shape = (B, heads, H, W, d)
+    q = torch.randn(shape, dtype=torch.float32, generator=g)
+    k = torch.randn(shape, dtype=torch.float32, generator=g)
+    v = torch.randn(shape, dtype=torch.float32, generator=g)
+    rel_h = torch.randn((2 * r - 1, d), dtype=torch.float32, generator=g) * d ** -0.5
+    rel_w = torch.randn((2 * r - 1, d), dtype=torch.float32, generator=g) * d ** -0.5
+    dt = torch_dtype(dtype)
+    return tuple(t.to(dtype=dt).to(device).contiguous() for t in (q, k, v, rel_h, rel_w))
+
+
+def make_workload_inputs(wl, seed: int = 0, device: str | torch.device = "cpu"):
+    """Inputs for a :class:`blocked_local_self_amd.workloads.Workload`."""
+    return make_inputs(wl.B, wl.heads, wl.H, wl.W, wl.d, wl.block, wl.halo,
+                       dtype=wl.dtype, seed=seed, device=device)
