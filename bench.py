@@ -1,0 +1,164 @@
+#!/usr/bin/env python3
+"""Benchmark: halo-attention forward on one MI355X.
+
+One step = one halo_attn_fwd launch over one full batch of the workload (all
+of the method's steps run inside that launch).  Inputs are seeded synthetic
+tensors already resident in HBM; several independent input/output sets are
+rotated so the working set exceeds the 256 MB Infinity Cache and every step
+reads HBM.  Prints ONE JSON line (rank 0):
+
+  value      TFLOP/s, F = 4*d*r^2 per (query, head) over the full window
+  roofline   dominant kernel vs HBM bandwidth: algorithmic bytes per launch
+             (k and v once, q at query pixels, out once) / mean launch time
+             measured with HIP events on the launch stream
+  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
+             workload on this host (reported, not a target)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+METRIC = "halo-attn fwd TFLOP/s + tokens/s per MI355X; % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MALL_BYTES = 256 * 2 ** 20     # Infinity Cache
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None, help="workload name (default: the early-stage shape)")
+    ap.add_argument("--kernel", default="auto", choices=["auto", "generic", "mfma"])
+    ap.add_argument("--sets", type=int, default=0, help="rotated input sets (0: enough to exceed the MALL)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with measured HBM bytes per launch for this workload (from rocprofv3 --pmc)")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, inputs_cpu, target_s):
+    """Time the fp64 oracle on whole (batch, head) slices of the workload."""
+    import numpy as np
+    import oracle
+    q, k, v, rh, rw = (t.to(dtype=__import__("torch").float64).numpy() for t in inputs_cpu)
+    threads = oracle.max_threads()
+    per_slice_flops = wl.flops / (wl.B * wl.heads)
+
+    def run(nsl):
+        sl = lambda a: np.ascontiguousarray(a.reshape(wl.B * wl.heads, 1, *a.shape[2:])[:nsl])
+        t0 = time.perf_counter()
+        oracle.halo_attn_ref(sl(q), sl(k), sl(v), rh, rw, wl.block, wl.halo, wl.stride, threads=threads)
+        return time.perf_counter() - t0
+
+    n = min(threads, wl.B * wl.heads)
+    t = run(n)
+    if t < target_s:
+        n2 = int(min(wl.B * wl.heads, max(n, n * target_s / max(t, 1e-3))))
+        n2 = max(n, (n2 // threads) * threads) if n2 >= threads else n2
+        if n2 > n:
+            n, t = n2, run(n2)
+    flops = per_slice_flops * n
+    tokens = wl.tokens * n / (wl.B * wl.heads)   # token = position with all heads
+    return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {wl.B * wl.heads} (batch, head) slices of {wl.name}, fp64, {t:.2f} s",
+            "seconds": round(t, 3), "tokens_per_s": round(tokens / t, 1)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the operation shards over batch x heads with no communication)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from blocked_local_self_amd import halo_attn_fwd, workloads
+    from blocked_local_self_amd.inputs import make_workload_inputs
+
+    wl = workloads.get(args.workload or workloads.BENCH_WORKLOAD)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    in_bytes = 3 * wl.elem_bytes * wl.B * wl.heads * wl.H * wl.W * wl.d
+    out_bytes = wl.elem_bytes * wl.B * wl.heads * wl.Ho * wl.Wo * wl.d
+    nsets = args.sets or max(2, -(-2 * MALL_BYTES // (in_bytes + out_bytes)))
+    sets = []
+    inputs0_cpu = None
+    for s in range(nsets):
+        cpu = make_workload_inputs(wl, seed=s)
+        if s == 0:
+            inputs0_cpu = cpu
+        dev_t = tuple(t.to(dev) for t in cpu)
+        out = torch.empty(wl.out_shape(), dtype=dev_t[0].dtype, device=dev)
+        sets.append((dev_t, out))
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        (q, k, v, rh, rw), out = sets[i % nsets]
+        halo_attn_fwd(q, k, v, rh, rw, wl.block, wl.halo, wl.stride, out=out, kernel=args.kernel,
+                      stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms = gpu_ms / args.steps
+    tflops = wl.flops / (ms * 1e-3) / 1e12
+    achieved_gbs = wl.alg_bytes / (ms * 1e-3) / 1e9
+
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        rec = json.load(open(args.traffic))
+        if rec.get("workload") == wl.name:
+            traffic = rec.get("bytes_per_launch")
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {**wl.describe(), "kernel": args.kernel, "rotated_input_sets": nsets},
+        "tokens_per_s": round(wl.tokens / (ms * 1e-3), 1),
+        "wall_s_timed_region": round(wall, 4),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "alg_bytes_per_launch": wl.alg_bytes,
+            "mean_launch_us": round(ms * 1e3, 3),
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, inputs0_cpu, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

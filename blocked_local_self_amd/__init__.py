@@ -1,1 +1,95 @@
-"""MI355X-native blocked local self-attention with haloing (HaloNet forward)."""
+"""MI355X-native blocked local self-attention with haloing (HaloNet forward).
+
+``halo_attn_fwd`` marshals PyTorch tensors into the C ABI of
+``libhaloattn.so`` (include/halo_attn.h); every step of the computation runs
+in the library's HIP kernels on the tensors' device and on the current HIP
+stream.  PyTorch provides device memory and streams only.
+
+The operation ("Scaling Local Self-Attention for Parameter Efficient Visual
+Backbones", sections 2.1-2.2, Figures 1-2, appendix A; the HaloAttention
+module on the pswp.cn blog page, section 4): for every query pixel, softmax
+over the in-image keys of its block's (block+2*halo)^2 window of
+scale * (q.k + q.rel_h[dy + c0] + q.rel_w[dx + c0]), c0 = block+3*halo-1,
+then the weighted sum of v; queries at multiples of ``query_stride``.
+"""
+from __future__ import annotations
+
+from . import _native
+
+__all__ = ["halo_attn_fwd", "select_kernel", "HaloError", "KERNELS"]
+
+HaloError = _native.HaloError
+KERNELS = {"auto": _native.HALO_KERNEL_AUTO, "generic": _native.HALO_KERNEL_GENERIC,
+           "mfma": _native.HALO_KERNEL_MFMA}
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return _native.HALO_F32
+    if t.dtype == torch.bfloat16:
+        return _native.HALO_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def select_kernel(d: int, block: int, halo: int, query_stride: int = 1, dtype: str = "bf16") -> str:
+    """Name of the kernel ``kernel='auto'`` runs for these arguments (host-only)."""
+    code = {"fp32": _native.HALO_F32, "bf16": _native.HALO_BF16}[dtype]
+    st = _native.load().halo_attn_select_kernel(d, block, halo, query_stride, code)
+    if st < 0:
+        _native.check(st)
+    return {v: k for k, v in KERNELS.items()}[st]
+
+
+def halo_attn_fwd(q, k, v, rel_h, rel_w, block: int, halo: int, query_stride: int = 1,
+                  scale: float | None = None, out=None, kernel: str = "auto", stream=None):
+    """Halo attention forward.
+
+    q, k, v: [B, heads, H, W, d] contiguous CUDA(HIP) tensors, float32 or bfloat16.
+    rel_h, rel_w: [2*(block+2*halo)-1, d], same dtype and device.
+    Returns out [B, heads, H/s, W/s, d] (allocated unless ``out`` is given).
+    ``scale=None`` means d**-0.5.  ``kernel`` in {"auto", "generic", "mfma"}.
+    ``stream``: a torch.cuda.Stream (default: the current stream).
+    """
+    import torch
+    tensors = {"q": q, "k": k, "v": v, "rel_h": rel_h, "rel_w": rel_w}
+    for name, t in tensors.items():
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must live on the GPU (got {t.device})")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must match q's dtype and device")
+    if q.dim() != 5 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError(f"q, k, v must share one [B, heads, H, W, d] shape; got "
+                         f"{tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    B, heads, H, W, d = q.shape
+    r = block + 2 * halo
+    if tuple(rel_h.shape) != (2 * r - 1, d) or tuple(rel_w.shape) != (2 * r - 1, d):
+        raise ValueError(f"rel_h and rel_w must be {(2 * r - 1, d)}; got "
+                         f"{tuple(rel_h.shape)}, {tuple(rel_w.shape)}")
+    s = query_stride
+    if s < 1 or H % s or W % s:
+        raise ValueError(f"query_stride={s} must divide H={H} and W={W}")
+    if scale is None:
+        scale = float(d) ** -0.5
+    oshape = (B, heads, H // s, W // s, d)
+    if out is None:
+        out = torch.empty(oshape, dtype=q.dtype, device=q.device)
+    elif (tuple(out.shape) != oshape or out.dtype != q.dtype or out.device != q.device
+          or not out.is_contiguous()):
+        raise ValueError(f"out must be a contiguous {oshape} {q.dtype} tensor on {q.device}")
+    if kernel not in KERNELS:
+        raise ValueError(f"kernel must be one of {sorted(KERNELS)}")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    lib = _native.load()
+    with torch.cuda.device(q.device):
+        st = lib.halo_attn_fwd_kernel(q.data_ptr(), k.data_ptr(), v.data_ptr(), rel_h.data_ptr(),
+                                      rel_w.data_ptr(), out.data_ptr(), B, heads, H, W, d, block,
+                                      halo, s, float(scale), _dtype_code(q), KERNELS[kernel],
+                                      stream.cuda_stream)
+    _native.check(st)
+    return out

@@ -1,0 +1,67 @@
+"""ctypes loader for libhaloattn.so (the C ABI declared in include/halo_attn.h).
+
+Loading fails loudly when the library has not been built: there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhaloattn.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "halo_attn.h")
+
+HALO_F32, HALO_BF16 = 0, 1
+HALO_KERNEL_AUTO, HALO_KERNEL_GENERIC, HALO_KERNEL_MFMA = 0, 1, 2
+STATUS = {0: "HALO_OK", -1: "HALO_ERR_NULL", -2: "HALO_ERR_SHAPE", -3: "HALO_ERR_DTYPE",
+          -4: "HALO_ERR_UNSUPPORTED", -5: "HALO_ERR_HIP", -6: "HALO_ERR_ALIAS"}
+
+_lib = None
+
+
+class HaloError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python -m blocked_local_self_amd.build, or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.halo_attn_fwd.argtypes = [vp] * 6 + [i] * 8 + [f, i, vp]
+    lib.halo_attn_fwd.restype = i
+    lib.halo_attn_fwd_kernel.argtypes = [vp] * 6 + [i] * 8 + [f, i, i, vp]
+    lib.halo_attn_fwd_kernel.restype = i
+    lib.halo_attn_select_kernel.argtypes = [i] * 5
+    lib.halo_attn_select_kernel.restype = i
+    lib.halo_attn_last_error.argtypes = []
+    lib.halo_attn_last_error.restype = ctypes.c_char_p
+    lib.halo_attn_abi_version.argtypes = []
+    lib.halo_attn_abi_version.restype = i
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().halo_attn_last_error().decode()
+
+
+def check(status: int) -> None:
+    if status != 0:
+        raise HaloError(status, last_error())
+
+
+def declared_functions() -> list[str]:
+    """Function names declared in include/halo_attn.h."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(halo_attn_\w+)\s*\(", text, flags=re.M)))

@@ -1,0 +1,37 @@
+// Shared definitions of the halo-attention kernels (gfx950).
+//
+// Geometry follows "Scaling Local Self-Attention for Parameter Efficient
+// Visual Backbones" (HaloNet), section 2.2 with Figures 1 and 2: blocks of
+// side `block` tiled from the top-left, window side r = block + 2*halo
+// starting at (by*block - halo, bx*block - halo), queries at multiples of the
+// query stride.  The relative-table row of displacement (key - query) is
+// displacement + c0, c0 = r - 1 + halo, as in the HaloAttention module of the
+// pswp.cn blog page (section 4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace halo {
+
+// Everything a kernel needs to know about one call, computed on the host.
+struct Geometry {
+    int64_t BH;        // batch * heads
+    int H, W, d;
+    int block, halo, stride;
+    int r;             // window side
+    int c0;            // table row of displacement 0
+    int Ho, Wo;        // output spatial size
+    int nbh, nbw;      // blocks per column / row (ceil)
+    float scale;       // multiplies q.k and q.rel
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return static_cast<float>(x); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+// Round to nearest even (the gfx950 conversion instruction rounds that way).
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return static_cast<__bf16>(x); }
+
+}  // namespace halo

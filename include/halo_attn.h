@@ -1,0 +1,118 @@
+/*
+ * halo_attn.h -- C ABI of the MI355X (gfx950) halo-attention library.
+ *
+ * The operation: HaloNet's blocked local self-attention with haloing, forward
+ * pass, on already projected queries, keys and values ("Scaling Local
+ * Self-Attention for Parameter Efficient Visual Backbones").
+ *
+ *  - Section 2.2, Figure 1: the H x W map is cut into non-overlapping
+ *    block x block query blocks, tiled from the top-left (a last block row or
+ *    column may be partial when block does not divide H or W).  Every query of
+ *    a block attends to the same window: the block plus a halo of `halo`
+ *    pixels on every side, side r = block + 2*halo.  Window positions outside
+ *    the image are padding and take no part in the softmax.  No centred mask.
+ *  - Section 2.1 and appendix A: the logit of key (ky,kx) for query (y,x) is
+ *    the content term plus a content-geometry term built from one relative
+ *    table per axis, shared by all heads.  The concrete form, as in the
+ *    HaloAttention module of the pswp.cn blog page (section 4):
+ *        l = scale * ( q.k + q.rel_h[ky - y + c0] + q.rel_w[kx - x + c0] )
+ *    with c0 = r - 1 + halo, tables of 2r-1 rows; out = softmax(l) . v over
+ *    the in-image window keys.
+ *  - Section 2.2, Figure 2: with query_stride s > 1 only the queries at
+ *    (s*y', s*x') are computed; their windows are the stride-1 windows.
+ *
+ * Layouts (all row-major, contiguous, d innermost):
+ *   q, k, v      [B][heads][H][W][d]
+ *   rel_h, rel_w [2r-1][d]          one pair shared by every batch and head
+ *   out          [B][heads][H/s][W/s][d]
+ * Element type: all six tensors share `dtype` (HALO_F32 or HALO_BF16).
+ * Arithmetic is fp32 (products, sums, softmax) for both dtypes; bf16 results
+ * are rounded to nearest even when stored.
+ *
+ * Memory and ownership: every tensor pointer is a DEVICE pointer allocated
+ * by the caller (any allocator; PyTorch tensors are fine).  The library
+ * allocates no device memory, keeps no state between calls and never
+ * synchronises: work is enqueued on `stream` (a hipStream_t; NULL means the
+ * default stream) and the call returns.  `out` must not overlap any input.
+ * Device-side faults surface at the caller's next synchronisation.
+ *
+ * Errors: every argument check runs on the host before any HIP call.  A
+ * non-zero status leaves `out` untouched and sets a thread-local message
+ * readable with halo_attn_last_error().  A failed launch returns
+ * HALO_ERR_HIP.  Nothing is thrown across the ABI.
+ */
+#ifndef HALO_ATTN_H
+#define HALO_ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HALO_ATTN_ABI_VERSION 1
+
+typedef enum halo_dtype {
+    HALO_F32 = 0,
+    HALO_BF16 = 1
+} halo_dtype;
+
+/* Which implementation runs.  AUTO picks the fastest one that supports the
+ * arguments.  GENERIC is the fp32-vector kernel for every supported shape;
+ * MFMA is the fused matrix-core kernel (bf16, d in {16, 32}, window side
+ * r <= 32); asking for it with other arguments returns HALO_ERR_UNSUPPORTED. */
+typedef enum halo_kernel {
+    HALO_KERNEL_AUTO = 0,
+    HALO_KERNEL_GENERIC = 1,
+    HALO_KERNEL_MFMA = 2
+} halo_kernel;
+
+typedef enum halo_status {
+    HALO_OK = 0,
+    HALO_ERR_NULL = -1,         /* a required pointer is NULL */
+    HALO_ERR_SHAPE = -2,        /* sizes inconsistent or out of range */
+    HALO_ERR_DTYPE = -3,        /* dtype not HALO_F32 / HALO_BF16 */
+    HALO_ERR_UNSUPPORTED = -4,  /* valid, but no kernel handles it */
+    HALO_ERR_HIP = -5,          /* the HIP runtime reported an error */
+    HALO_ERR_ALIAS = -6         /* out overlaps an input */
+} halo_status;
+
+/*
+ * Forward pass.  Preconditions (else HALO_ERR_SHAPE):
+ *   B, heads, H, W >= 0 (a zero makes the call a no-op returning HALO_OK;
+ *   pointers are then not inspected); 1 <= d <= 128; block >= 1;
+ *   0 <= halo; r = block + 2*halo <= 256; query_stride >= 1 with
+ *   block % query_stride == 0, H % query_stride == 0, W % query_stride == 0;
+ *   B*heads*H*W*d < 10^18 and the number of blocks B*heads*ceil(H/block)*
+ *   ceil(W/block) < 2^31.  scale must be finite (else HALO_ERR_SHAPE); pass
+ *   d^-0.5 to follow the HaloAttention module.
+ * kernel: a halo_kernel value (else HALO_ERR_SHAPE).
+ */
+int halo_attn_fwd_kernel(const void* q, const void* k, const void* v,
+                         const void* rel_h, const void* rel_w, void* out,
+                         int B, int heads, int H, int W, int d,
+                         int block, int halo, int query_stride,
+                         float scale, int dtype, int kernel, void* stream);
+
+/* halo_attn_fwd_kernel with kernel = HALO_KERNEL_AUTO. */
+int halo_attn_fwd(const void* q, const void* k, const void* v,
+                  const void* rel_h, const void* rel_w, void* out,
+                  int B, int heads, int H, int W, int d,
+                  int block, int halo, int query_stride,
+                  float scale, int dtype, void* stream);
+
+/* Host-only query: the halo_kernel value AUTO would run for these
+ * arguments (HALO_KERNEL_GENERIC or HALO_KERNEL_MFMA), or a negative
+ * status if the arguments are invalid.  Touches no device. */
+int halo_attn_select_kernel(int d, int block, int halo, int query_stride, int dtype);
+
+/* Message for the last non-zero status returned on this thread ("" if none).
+ * The pointer stays valid until the next call on this thread. */
+const char* halo_attn_last_error(void);
+
+/* HALO_ATTN_ABI_VERSION of the built library. */
+int halo_attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HALO_ATTN_H */

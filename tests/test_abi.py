@@ -1,0 +1,90 @@
+"""C-ABI library checks that need no GPU: it loads, exports every declared
+symbol, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import subprocess
+
+import pytest
+
+from blocked_local_self_amd import _native
+from blocked_local_self_amd import select_kernel, HaloError
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _native.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _native.declared_functions()
+    assert {"halo_attn_fwd", "halo_attn_fwd_kernel", "halo_attn_last_error",
+            "halo_attn_select_kernel", "halo_attn_abi_version"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", _native.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in names:
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_abi_version(lib):
+    text = open(_native.HEADER).read()
+    assert f"#define HALO_ATTN_ABI_VERSION {lib.halo_attn_abi_version()}" in text
+
+
+def call(lib, *, q=1, k=1, v=1, rh=1, rw=1, out=1 << 40, B=1, heads=1, H=8, W=8, d=16, block=4,
+         halo=1, stride=1, scale=0.25, dtype=1, kernel=0):
+    # Fake, non-overlapping pointers: every call below must fail before the
+    # library touches the device.
+    ptr = lambda x: ctypes.c_void_p(x << 32 if x not in (0, 1 << 40) else x)
+    return lib.halo_attn_fwd_kernel(ptr(q), ptr(k), ptr(v), ptr(rh), ptr(rw),
+                                    ctypes.c_void_p(out), B, heads, H, W, d, block, halo, stride,
+                                    scale, dtype, kernel, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), -1), (dict(rw=0), -1), (dict(out=0), -1),
+    (dict(dtype=7), -3),
+    (dict(d=0), -2), (dict(d=129), -2), (dict(block=0), -2), (dict(halo=-1), -2),
+    (dict(stride=0), -2), (dict(stride=3, block=4), -2), (dict(stride=2, H=9), -2),
+    (dict(B=-1), -2), (dict(W=-3), -2), (dict(kernel=9), -2),
+    (dict(block=200, halo=30), -2), (dict(scale=float("inf")), -2), (dict(scale=float("nan")), -2),
+    (dict(kernel=2, dtype=0), -4), (dict(kernel=2, d=64), -4), (dict(kernel=2, block=6), -4),
+    (dict(kernel=2, block=8, halo=13), -4),
+    (dict(B=1 << 30, heads=1 << 30, H=1 << 15, W=1 << 15), -2),
+])
+def test_invalid_arguments_rejected_on_host(lib, kw, status):
+    assert call(lib, **kw) == status
+    assert _native.last_error() != ""
+
+
+def test_alias_rejected(lib):
+    # out overlapping q
+    assert call(lib, out=1 << 32) == -6
+
+
+def test_empty_is_a_noop(lib):
+    for kw in (dict(B=0), dict(heads=0), dict(H=0), dict(W=0)):
+        assert call(lib, q=0, k=0, v=0, rh=0, rw=0, out=0, **kw) == 0
+    assert _native.last_error() == ""
+
+
+def test_kernel_selection():
+    assert select_kernel(16, 8, 3, 1, "bf16") == "mfma"
+    assert select_kernel(32, 8, 3, 1, "bf16") == "mfma"
+    assert select_kernel(16, 8, 3, 2, "bf16") == "mfma"
+    assert select_kernel(32, 12, 3, 1, "bf16") == "mfma"
+    assert select_kernel(16, 4, 1, 1, "fp32") == "generic"
+    assert select_kernel(64, 8, 3, 1, "bf16") == "generic"
+    assert select_kernel(16, 2, 1, 1, "bf16") == "generic"
+    assert select_kernel(16, 8, 13, 1, "bf16") == "generic"
+    with pytest.raises(HaloError):
+        select_kernel(16, 4, 1, 3, "bf16")
+
+
+def test_python_wrapper_validates_before_the_library():
+    import torch
+    from blocked_local_self_amd import halo_attn_fwd
+    x = torch.zeros(1, 1, 8, 8, 16)
+    t = torch.zeros(11, 16)
+    with pytest.raises(ValueError):
+        halo_attn_fwd(x, x, x, t, t, 4, 1)   # CPU tensors are refused

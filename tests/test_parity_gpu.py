@@ -1,0 +1,264 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 oracle.
+
+Tolerances (max-abs over every compared element): 1e-4 for fp32 inputs and
+2e-2 for bf16 inputs with fp32 accumulation.  Inputs come from the seeded
+recipe in blocked_local_self_amd.inputs; the oracle reads exactly the same
+(rounded) tensors.  Page references: "Scaling Local Self-Attention for
+Parameter Efficient Visual Backbones" (HaloNet) section 2.2 (Figures 1, 2),
+section 4.3 (h = 0), the HaloAttention module on the pswp.cn page (table
+offset, masking).
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from blocked_local_self_amd import halo_attn_fwd, HaloError, workloads
+from blocked_local_self_amd.inputs import make_inputs, make_workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-4, "bf16": 2e-2}
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def run(inputs, block, halo, stride=1, kernel="auto", scale=None):
+    q, k, v, rh, rw = (t.to(DEV) for t in inputs)
+    out = halo_attn_fwd(q, k, v, rh, rw, block, halo, stride, scale=scale, kernel=kernel)
+    torch.cuda.synchronize()
+    return out
+
+
+def ref(inputs, block, halo, stride=1, scale=None):
+    q, k, v, rh, rw = (f64(t) for t in inputs)
+    return oracle.halo_attn_ref(q, k, v, rh, rw, block, halo, stride, scale)
+
+
+def max_err(gpu, want):
+    g = f64(gpu)
+    assert np.isfinite(g).all(), "non-finite output"
+    return float(np.abs(g - want).max())
+
+
+# --------------------------------------------------- small shapes, several tiles
+SMALL = [
+    # (B, heads, H, W, d, block, halo, stride)
+    (2, 3, 24, 24, 16, 8, 3, 1),    # 3x3 blocks, interior + border windows
+    (2, 3, 24, 24, 32, 8, 3, 1),
+    (1, 2, 20, 28, 16, 8, 3, 1),    # ragged: partial last block row and column
+    (1, 2, 20, 28, 32, 8, 3, 1),
+    (2, 2, 24, 24, 16, 8, 3, 2),    # strided queries
+    (1, 2, 36, 36, 32, 12, 3, 1),   # 18x18 window (two column chunks)
+    (1, 2, 32, 40, 16, 12, 3, 2),   # ragged + strided + wide window
+    (1, 2, 16, 16, 16, 4, 1, 1),    # 6x6 window
+    (1, 1, 16, 16, 16, 8, 0, 1),    # h = 0 (section 4.3): attention inside blocks
+    (1, 2, 8, 8, 16, 8, 2, 1),      # one block covers the image
+    (1, 2, 12, 12, 16, 16, 1, 1),   # block larger than the image
+    (1, 1, 40, 40, 16, 20, 6, 1),   # largest matrix-core window side, r = 32
+    (1, 1, 40, 40, 16, 4, 14, 4),   # r = 32 with tiny blocks, stride = block
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("kernel", ["auto", "generic"])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_small_shapes_match_oracle(shape, kernel, dtype):
+    B, heads, H, W, d, block, halo, stride = shape
+    say(f"case {shape} kernel={kernel} dtype={dtype}")
+    inp = make_inputs(B, heads, H, W, d, block, halo, dtype=dtype, seed=sum(shape))
+    got = run(inp, block, halo, stride, kernel)
+    err = max_err(got, ref(inp, block, halo, stride))
+    assert err <= TOL[dtype], err
+
+
+@pytest.mark.parametrize("shape", [s for s in SMALL if s[4] in (16, 32) and s[5] % 4 == 0],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_matrix_core_kernel_matches_oracle(shape):
+    B, heads, H, W, d, block, halo, stride = shape
+    say(f"mfma case {shape}")
+    inp = make_inputs(B, heads, H, W, d, block, halo, dtype="bf16", seed=7 + sum(shape))
+    got = run(inp, block, halo, stride, "mfma")
+    assert max_err(got, ref(inp, block, halo, stride)) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 9, 7, 24, 3, 1, 1), (1, 1, 10, 10, 64, 4, 2, 2),
+                                   (1, 1, 6, 6, 128, 2, 1, 1), (1, 2, 7, 5, 8, 1, 2, 1),
+                                   (1, 1, 4, 4, 16, 3, 2, 1)])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_generic_kernel_odd_shapes(shape, dtype):
+    B, heads, H, W, d, block, halo, stride = shape
+    say(f"generic odd case {shape} {dtype}")
+    inp = make_inputs(B, heads, H, W, d, block, halo, dtype=dtype, seed=3 + sum(shape))
+    got = run(inp, block, halo, stride, "auto")
+    assert max_err(got, ref(inp, block, halo, stride)) <= TOL[dtype]
+
+
+# --------------------------------------------------------- the five workloads
+def sampled_slices(wl, count=6):
+    bh = wl.B * wl.heads
+    idx = sorted(set([0, 1, bh // 3, bh // 2, bh - 2, bh - 1][:count]))
+    return [(i // wl.heads, i % wl.heads) for i in idx if 0 <= i < bh]
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_workload_full_size(name):
+    wl = workloads.get(name)
+    say(f"workload {name}")
+    inp = make_workload_inputs(wl, seed=0)
+    got = run(inp, wl.block, wl.halo, wl.stride)        # the launch the benchmark times
+    g = f64(got)
+    assert g.shape == wl.out_shape()
+    assert np.isfinite(g).all()
+    q, k, v, rh, rw = inp
+    slices = [(n, h) for n in range(wl.B) for h in range(wl.heads)] if wl.B * wl.heads <= 4 else sampled_slices(wl)
+    pick = lambda t: np.stack([f64(t[n, hd]) for n, hd in slices])[:, None]
+    want = oracle.halo_attn_ref(pick(q), pick(k), pick(v), f64(rh), f64(rw), wl.block, wl.halo, wl.stride)
+    have = np.stack([g[n, hd] for n, hd in slices])[:, None]
+    worst = float(np.abs(have - want).max())
+    say(f"  max abs err over {len(slices)} slices: {worst:.3e}")
+    assert worst <= TOL[wl.dtype]
+    # every output row is a convex combination of in-window values
+    assert np.abs(g).max() <= float(v.abs().max()) + TOL[wl.dtype]
+
+
+@pytest.mark.parametrize("name", ["early_stage_bf16_64x64_d16_b8h3", "tiny_fp32_16x16_d16_b4h1"])
+def test_workload_generic_kernel_agrees(name):
+    wl = workloads.get(name)
+    inp = make_workload_inputs(wl, seed=1)
+    a = f64(run(inp, wl.block, wl.halo, wl.stride, "generic"))
+    b = f64(run(inp, wl.block, wl.halo, wl.stride, "auto"))
+    assert np.abs(a - b).max() <= TOL[wl.dtype]
+
+
+# ---------------------------------------------------------------- pins on GPU
+def test_p2_zero_query_gives_window_mean():
+    B, heads, H, W, d, block, halo = 1, 2, 24, 24, 16, 8, 3
+    q, k, v, rh, rw = make_inputs(B, heads, H, W, d, block, halo, dtype="bf16", seed=5)
+    q = torch.zeros_like(q); rh = torch.zeros_like(rh); rw = torch.zeros_like(rw)
+    got = f64(run((q, k, v, rh, rw), block, halo))
+    vv = f64(v)
+    r = block + 2 * halo
+    for y in range(H):
+        for x in range(W):
+            y0, x0 = (y // block) * block - halo, (x // block) * block - halo
+            want = vv[:, :, max(0, y0):min(H, y0 + r), max(0, x0):min(W, x0 + r)].mean(axis=(2, 3))
+            assert np.abs(got[:, :, y, x] - want).max() <= TOL["bf16"]
+
+
+def test_p6_strided_is_subsampled_stride_one():
+    inp = make_inputs(1, 2, 32, 32, 16, 8, 3, dtype="bf16", seed=6)
+    full = f64(run(inp, 8, 3, 1))
+    sub = f64(run(inp, 8, 3, 2))
+    assert np.abs(sub - full[:, :, ::2, ::2]).max() <= TOL["bf16"]
+
+
+def test_p7_constant_values_and_linearity():
+    q, k, v, rh, rw = make_inputs(1, 2, 24, 24, 16, 8, 3, dtype="bf16", seed=7)
+    ones = f64(run((q, k, torch.ones_like(v), rh, rw), 8, 3))
+    assert np.abs(ones - 1.0).max() <= 1e-6
+    v2 = torch.roll(v, 1, dims=2)
+    a = f64(run((q, k, v, rh, rw), 8, 3))
+    b = f64(run((q, k, v2, rh, rw), 8, 3))
+    c = f64(run((q, k, (v.float() + v2.float()).to(torch.bfloat16), rh, rw), 8, 3))
+    assert np.abs(c - (a + b)).max() <= 2 * TOL["bf16"]
+
+
+def test_p9_block_shift_equivariance():
+    d, block, halo = 16, 8, 3
+    g = torch.Generator().manual_seed(9)
+    content = torch.randn(3, 1, 1, 32, 32, d, generator=g).to(torch.bfloat16)
+    r = block + 2 * halo
+    rh = (torch.randn(2 * r - 1, d, generator=g) * d ** -0.5).to(torch.bfloat16)
+    rw = (torch.randn(2 * r - 1, d, generator=g) * d ** -0.5).to(torch.bfloat16)
+    canvas = torch.randn(3, 1, 1, 48, 48, d, generator=g).to(torch.bfloat16)
+    canvas[:, :, :, 8:40, 8:40] = content
+    base = f64(run((content[0], content[1], content[2], rh, rw), block, halo))
+    moved = f64(run((canvas[0].contiguous(), canvas[1].contiguous(), canvas[2].contiguous(), rh, rw), block, halo))
+    # interior blocks of the content (windows fully inside it)
+    assert np.abs(base[..., 8:24, 8:24, :] - moved[..., 16:32, 16:32, :]).max() <= 1e-6
+
+
+def test_p10_one_hot_tables_select_the_displaced_key():
+    block, halo, d, H, W = 8, 3, 16, 24, 24
+    r = block + 2 * halo
+    c0 = r - 1 + halo
+    g = torch.Generator().manual_seed(10)
+    v = torch.randn(1, 1, H, W, d, generator=g).to(torch.bfloat16)
+    q = torch.zeros(1, 1, H, W, d); q[..., 0] = 1.0
+    q = q.to(torch.bfloat16); k = torch.zeros_like(q)
+    for delta, eps in [(0, 0), (2, -3), (-3, 3), (10, 0), (0, -10)]:
+        rh = torch.zeros(2 * r - 1, d); rw = torch.zeros(2 * r - 1, d)
+        rh[c0 + delta, 0] = 64.0; rw[c0 + eps, 0] = 64.0
+        out = f64(run((q, k, v, rh.to(torch.bfloat16), rw.to(torch.bfloat16)), block, halo, scale=1.0))
+        vv = f64(v)
+        hits = 0
+        for y in range(H):
+            for x in range(W):
+                ky, kx = y + delta, x + eps
+                y0, x0 = (y // block) * block - halo, (x // block) * block - halo
+                if 0 <= ky < H and 0 <= kx < W and y0 <= ky < y0 + r and x0 <= kx < x0 + r:
+                    assert np.abs(out[0, 0, y, x] - vv[0, 0, ky, kx]).max() <= TOL["bf16"]
+                    hits += 1
+        assert hits > 0
+
+
+def test_p11_transpose_symmetry():
+    q, k, v, rh, rw = make_inputs(1, 2, 24, 32, 16, 8, 3, dtype="bf16", seed=11)
+    T = lambda t: t.transpose(2, 3).contiguous()
+    base = f64(run((q, k, v, rh, rw), 8, 3))
+    tr = f64(run((T(q), T(k), T(v), rw, rh), 8, 3))
+    assert np.abs(tr - np.swapaxes(base, 2, 3)).max() <= TOL["bf16"]
+
+
+# -------------------------------------------------------- memory hygiene, misc
+@pytest.mark.parametrize("kernel", ["mfma", "generic"])
+def test_writes_exactly_the_output(kernel):
+    B, heads, H, W, d, block, halo, stride = 2, 2, 20, 28, 16, 8, 3, 1
+    q, k, v, rh, rw = (t.to(DEV) for t in make_inputs(B, heads, H, W, d, block, halo, "bf16", seed=12))
+    n = B * heads * H * W * d
+    buf = torch.full((n + 4096,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    out = buf[:n].view(B, heads, H, W, d)
+    halo_attn_fwd(q, k, v, rh, rw, block, halo, stride, out=out, kernel=kernel)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()            # every element written
+    assert torch.isnan(buf[n:]).all()           # nothing past the end
+
+
+def test_deterministic_and_stream_aware():
+    q, k, v, rh, rw = (t.to(DEV) for t in make_inputs(2, 4, 32, 32, 32, 8, 3, "bf16", seed=13))
+    a = halo_attn_fwd(q, k, v, rh, rw, 8, 3)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        b = halo_attn_fwd(q, k, v, rh, rw, 8, 3)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_empty_batch_and_errors_on_gpu():
+    q = torch.zeros(0, 2, 8, 8, 16, dtype=torch.bfloat16, device=DEV)
+    t = torch.zeros(11, 16, dtype=torch.bfloat16, device=DEV)
+    out = halo_attn_fwd(q, q, q, t, t, 4, 1)
+    assert out.shape == (0, 2, 8, 8, 16)
+    x = torch.zeros(1, 1, 8, 8, 16, dtype=torch.float32, device=DEV)
+    with pytest.raises(HaloError):
+        halo_attn_fwd(x, x, x, t.float(), t.float(), 4, 1, kernel="mfma")   # fp32: no matrix-core path
