@@ -20,7 +20,7 @@ __all__ = ["halo_attn_fwd", "select_kernel", "HaloError", "KERNELS"]
 
 HaloError = _native.HaloError
 KERNELS = {"auto": _native.HALO_KERNEL_AUTO, "generic": _native.HALO_KERNEL_GENERIC,
-           "mfma": _native.HALO_KERNEL_MFMA}
+           "mfma": _native.HALO_KERNEL_MFMA, "mfma_strip": _native.HALO_KERNEL_MFMA_STRIP}
 
 
 def _dtype_code(t) -> int:
@@ -48,7 +48,7 @@ def halo_attn_fwd(q, k, v, rel_h, rel_w, block: int, halo: int, query_stride: in
     q, k, v: [B, heads, H, W, d] contiguous CUDA(HIP) tensors, float32 or bfloat16.
     rel_h, rel_w: [2*(block+2*halo)-1, d], same dtype and device.
     Returns out [B, heads, H/s, W/s, d] (allocated unless ``out`` is given).
-    ``scale=None`` means d**-0.5.  ``kernel`` in {"auto", "generic", "mfma"}.
+    ``scale=None`` means d**-0.5.  ``kernel`` in {"auto", "generic", "mfma", "mfma_strip"}.
     ``stream``: a torch.cuda.Stream (default: the current stream).
     """
     import torch

@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(HERE, "libhaloattn.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "halo_attn.h")
 
 HALO_F32, HALO_BF16 = 0, 1
-HALO_KERNEL_AUTO, HALO_KERNEL_GENERIC, HALO_KERNEL_MFMA = 0, 1, 2
+HALO_KERNEL_AUTO, HALO_KERNEL_GENERIC, HALO_KERNEL_MFMA, HALO_KERNEL_MFMA_STRIP = 0, 1, 2, 3
 STATUS = {0: "HALO_OK", -1: "HALO_ERR_NULL", -2: "HALO_ERR_SHAPE", -3: "HALO_ERR_DTYPE",
           -4: "HALO_ERR_UNSUPPORTED", -5: "HALO_ERR_HIP", -6: "HALO_ERR_ALIAS"}
 

@@ -28,22 +28,53 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB_PATH + f".tmp{os.getpid()}"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-Wall", "-Wno-unused-command-line-argument", "-I", INCLUDE,
-           *sources(), "-o", tmp]
+# Extra flags per source.  The matrix-core kernel keeps MFMA results in
+# ordinary VGPRs (no accumulator-register copies) and, having no NaN
+# semantics to preserve in its max reductions, skips NaN canonicalisation.
+PER_FILE_FLAGS = {
+    "kernel_mfma.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "kernel_ring.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-Wall", "-Wno-unused-command-line-argument"]
+
+
+def build(verbose: bool = False, defines: tuple = (), out: str | None = None) -> str:
+    """Compile every csrc/*.hip for gfx950 and link libhaloattn.so.
+
+    ``defines``: extra -D flags (tuning builds); ``out``: output path.
+    """
+    out = out or LIB_PATH
+    bdir = os.path.join(HERE, "_build", f"{os.getpid()}")
+    os.makedirs(bdir, exist_ok=True)
+    objs, logs = [], []
+    procs = []
+    for src in sources():
+        obj = os.path.join(bdir, os.path.basename(src) + ".o")
+        cmd = [hipcc(), f"--offload-arch={ARCH}", *COMMON, "-I", INCLUDE, *[f"-D{d}" for d in defines],
+               *PER_FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
+        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+        objs.append(obj)
+    for cmd, pr in procs:
+        text, _ = pr.communicate()
+        if pr.returncode != 0:
+            raise RuntimeError(f"hipcc failed ({pr.returncode}):\n{' '.join(cmd)}\n{text}")
+        logs.append(text)
+    tmp = out + f".tmp{os.getpid()}"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+        raise RuntimeError(f"link failed ({res.returncode}):\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
     if verbose:
         noise = "is not a recognized feature for this target"
-        for line in (res.stdout + res.stderr).splitlines():
+        for line in "".join(logs).splitlines():
             if noise not in line:
                 print(line)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    for o in objs:
+        os.remove(o)
+    os.rmdir(bdir)
+    return out
 
 
 if __name__ == "__main__":

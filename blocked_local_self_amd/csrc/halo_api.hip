@@ -14,7 +14,7 @@ hipError_t launch_generic(const void* q, const void* k, const void* v, const voi
                           const void* rw, void* out, const Geometry& g, bool bf16, hipStream_t st);
 bool mfma_supported(int d, int r, int block, int stride, bool bf16);
 hipError_t launch_mfma(const void* q, const void* k, const void* v, const void* rh,
-                       const void* rw, void* out, const Geometry& g, hipStream_t st);
+                       const void* rw, void* out, const Geometry& g, bool force_strip, hipStream_t st);
 }  // namespace halo
 
 namespace {
@@ -79,7 +79,8 @@ int halo_attn_fwd_kernel(const void* q, const void* k, const void* v,
     g_err[0] = 0;
     int st = check_config(d, block, halo, query_stride, dtype);
     if (st) return st;
-    if (kernel != HALO_KERNEL_AUTO && kernel != HALO_KERNEL_GENERIC && kernel != HALO_KERNEL_MFMA)
+    if (kernel != HALO_KERNEL_AUTO && kernel != HALO_KERNEL_GENERIC && kernel != HALO_KERNEL_MFMA &&
+        kernel != HALO_KERNEL_MFMA_STRIP)
         return fail(HALO_ERR_SHAPE, "kernel=%d is not a halo_kernel value", kernel);
     if (B < 0 || heads < 0 || H < 0 || W < 0)
         return fail(HALO_ERR_SHAPE, "negative size: B=%d heads=%d H=%d W=%d", B, heads, H, W);
@@ -115,7 +116,7 @@ int halo_attn_fwd_kernel(const void* q, const void* k, const void* v,
 
     const bool bf16 = dtype == HALO_BF16;
     const bool mfma_ok = halo::mfma_supported(d, r, block, query_stride, bf16);
-    if (kernel == HALO_KERNEL_MFMA && !mfma_ok)
+    if ((kernel == HALO_KERNEL_MFMA || kernel == HALO_KERNEL_MFMA_STRIP) && !mfma_ok)
         return fail(HALO_ERR_UNSUPPORTED,
                     "matrix-core kernel needs bf16, d in {16,32}, window side <= 32 "
                     "(got dtype=%d d=%d r=%d)", dtype, d, r);
@@ -127,8 +128,10 @@ int halo_attn_fwd_kernel(const void* q, const void* k, const void* v,
     g.nbh = nbh; g.nbw = nbw; g.scale = scale;
 
     hipStream_t s = (hipStream_t)stream;
-    const bool use_mfma = kernel == HALO_KERNEL_MFMA || (kernel == HALO_KERNEL_AUTO && mfma_ok);
-    const hipError_t e = use_mfma ? halo::launch_mfma(q, k, v, rel_h, rel_w, out, g, s)
+    const bool use_mfma = kernel == HALO_KERNEL_MFMA || kernel == HALO_KERNEL_MFMA_STRIP ||
+                          (kernel == HALO_KERNEL_AUTO && mfma_ok);
+    const hipError_t e = use_mfma ? halo::launch_mfma(q, k, v, rel_h, rel_w, out, g,
+                                                      kernel == HALO_KERNEL_MFMA_STRIP, s)
                                   : halo::launch_generic(q, k, v, rel_h, rel_w, out, g, bf16, s);
     if (e != hipSuccess)
         return fail(HALO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));

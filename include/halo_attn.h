@@ -56,13 +56,18 @@ typedef enum halo_dtype {
 } halo_dtype;
 
 /* Which implementation runs.  AUTO picks the fastest one that supports the
- * arguments.  GENERIC is the fp32-vector kernel for every supported shape;
- * MFMA is the fused matrix-core kernel (bf16, d in {16, 32}, window side
- * r <= 32); asking for it with other arguments returns HALO_ERR_UNSUPPORTED. */
+ * arguments.  GENERIC is the fp32-vector kernel for every supported shape.
+ * MFMA is the fused matrix-core path (bf16, d in {16, 32}, block % 4 == 0,
+ * window side r <= 32): a persistent kernel that walks each image down its
+ * block rows with the window rows in an LDS ring when r is 8, 10, 12, 14 or 16
+ * and the ring fits in LDS, else a kernel that stages each strip of blocks
+ * separately.  MFMA_STRIP forces the latter (for cross-checking).  Asking for
+ * an MFMA path with other arguments returns HALO_ERR_UNSUPPORTED. */
 typedef enum halo_kernel {
     HALO_KERNEL_AUTO = 0,
     HALO_KERNEL_GENERIC = 1,
-    HALO_KERNEL_MFMA = 2
+    HALO_KERNEL_MFMA = 2,
+    HALO_KERNEL_MFMA_STRIP = 3
 } halo_kernel;
 
 typedef enum halo_status {
