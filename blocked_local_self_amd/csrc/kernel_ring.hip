@@ -11,25 +11,34 @@
 // Work decomposition (MI355X-first):
 //  * one workgroup owns one (batch, head) image strip of `nbx` adjacent block
 //    columns and walks down its block rows.  Window rows live in an LDS ring
-//    of R + block rows (K as [row][col][d], V transposed to [d][row][col]):
-//    the R rows of the current window plus the `block` rows the next window
-//    adds.  So the vertical halo overlap is reused in LDS as well as the
-//    horizontal one, every K/V pixel of the strip is read from HBM once, and
-//    the next rows are fetched (16-byte loads into registers) while the
-//    current block row computes, then written to the ring: one barrier per
-//    block row, no exposed load latency after the first.
+//    of R + block rows: the R rows of the current window plus the `block`
+//    rows the next window adds.  The vertical halo overlap is reused in LDS as
+//    well as the horizontal one, so every K/V pixel of the strip is read from
+//    HBM once; the next rows (and the next query fragments) are fetched into
+//    registers while the current block row computes, then written to the
+//    ring: one barrier per block row.  Rows above or below the image are kept
+//    as zero rows, so every block row runs the same code.
+//  * LDS layouts are chosen for conflict-free fragment reads: K is
+//    [slot][col][d] with the 16-byte chunks of a pixel XOR-swizzled by column
+//    bits; V is transposed to [d][slot][col] with the channel pitch padded to
+//    4 (mod 64) dwords; the relative-logit scratch has a 20-float row stride.
 //  * a wave takes QT tiles of 16 queries of one block at a time.  Scores are
 //    computed transposed, S^T = K . Q^T, one 16x16 tile per window row (16
 //    window columns); lane (n, g) holds query n and columns 4g..4g+3, so the
 //    width term q.rel_w[col] is the MFMA accumulator input (masked columns
 //    -1e30) and the height term q.rel_h[row] is one register per (lane, row).
-//  * the window side R is a compile-time constant: both passes are fully
-//    unrolled with static register indices.  Interior block rows run without
-//    any row masking; the first and last block rows mask off-image rows.
-//  * pass 1 takes the row max; pass 2 recomputes the scores, forms base-2
-//    logits with one FMA each, exponentiates (v_exp_f32), packs bf16 P and
-//    feeds it straight into the P.V MFMA (O^T = V^T . P^T) and a row-sum MFMA
-//    against ones, so normalisation uses exactly the bf16 weights applied to V.
+//  * both passes loop over the in-image window rows only; the height term of
+//    a row is read from the conflict-free scratch.
+//  * the softmax is shifted by a per-query upper bound on its logits
+//    (|q| max|k|, with max|k|^2 bounded by running per-chunk maxima over all
+//    keys staged so far, plus the largest width and height terms) instead of an exact max, so a
+//    single pass forms base-2 logits with one FMA each, exponentiates
+//    (v_exp_f32), packs bf16 P and feeds it straight into the P.V MFMA
+//    (O^T = V^T . P^T) and a row-sum MFMA against ones (normalisation uses
+//    exactly the bf16 weights applied to V).  Should the bound overshoot
+//    enough for the weight sum to drop below 2^-60, the group is recomputed
+//    with the exact row max (an extra pass), so the result is the stable
+//    softmax in every case.
 #include <algorithm>
 #include <type_traits>
 
@@ -43,25 +52,47 @@ namespace halo {
 #ifndef HALO_RING_QT
 #define HALO_RING_QT 2
 #endif
-constexpr int kRingWaves = HALO_RING_WAVES;
-constexpr int kRingThreads = 64 * kRingWaves;
 #ifndef HALO_RING_MAXI
 #define HALO_RING_MAXI 2      // query groups per wave per block row with prefetched Q
 #endif
+constexpr int kRingWaves = HALO_RING_WAVES;
+constexpr int kRingThreads = 64 * kRingWaves;
 constexpr int kRingMaxI = HALO_RING_MAXI;
+constexpr int kScrStride = 20;        // floats per scratch row (conflict-free writes)
 
 struct RingPlan {
     int nstrips;     // column strips per image
     int nbx;         // block columns per strip
-    int SWv;         // strip width in pixels (multiple of 4): LDS row pitch
+    int SWv;         // strip width in pixels (multiple of 4)
     int ring;        // LDS ring rows (R + block)
+    int CP;          // V^T channel pitch in elements (ring*SWv, padded)
     int RP;          // relative-table rows padded to a multiple of 16
     int groups;      // QT-tile groups per block
-    int off_v, off_rel, off_scr, lds_bytes;
+    int off_v, off_rel, off_scr, off_kn, lds_bytes;
     int remap_xcd;
     int64_t nwg;
     float alpha;     // scale * log2(e)
 };
+
+template <typename T>
+__device__ inline T lds_ld(const unsigned char* base, unsigned off)
+{
+    return *reinterpret_cast<const T*>(base + off);
+}
+template <typename T>
+__device__ inline void lds_st(unsigned char* base, unsigned off, T val)
+{
+    *reinterpret_cast<T*>(base + off) = val;
+}
+
+// Byte offset, inside a pixel's D channels, of 16-byte chunk `c` of the
+// pixel at strip column `col` (XOR swizzle).
+template <int D>
+__device__ inline unsigned k_chunk(int c, int col)
+{
+    if (D == 16) return (unsigned)((c ^ ((col >> 3) & 1)) * 16);
+    return (unsigned)((c ^ ((col >> 2) & 3)) * 16);
+}
 
 template <int D, int R, int QT>
 __global__ __launch_bounds__(kRingThreads)
@@ -73,19 +104,18 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     static_assert(R <= 16, "one 16-column tile per window row");
     constexpr int KPL = D / 4;                 // channels per lane in a QK fragment
     constexpr int CPP = D / 8;                 // 16-byte chunks per pixel
+    constexpr unsigned PIXB = D * 2;           // bytes per pixel
     typedef typename Frag<D>::T FragT;
     extern __shared__ __align__(16) unsigned char smem[];
-    const int ring = p.ring, SWv = p.SWv;
-    __bf16* Kr = reinterpret_cast<__bf16*>(smem);                    // [ring][SWv][D]
-    __bf16* Vr = reinterpret_cast<__bf16*>(smem + p.off_v);          // [D][ring][SWv]
-    __bf16* Rh = reinterpret_cast<__bf16*>(smem + p.off_rel);        // [RP][D]
-    __bf16* Rw = Rh + p.RP * D;
+    const int ring = p.ring, SWv = p.SWv, CP = p.CP;
+    const unsigned rowb_k = (unsigned)SWv * PIXB;            // bytes per K ring row
+    const unsigned offv = p.off_v, offrh = p.off_rel, offrw = p.off_rel + p.RP * D * 2;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, gq = lane >> 4;
-    const int scr_stride = p.RP * 16;
-    float* scr = reinterpret_cast<float*>(smem + p.off_scr) + wave * QT * scr_stride;
+    const unsigned scr_u = (unsigned)p.RP * kScrStride * 4;  // bytes per query tile
+    const unsigned scr0 = p.off_scr + wave * QT * scr_u;
 
     int64_t wg = blockIdx.x;
     if (p.remap_xcd) {
@@ -107,64 +137,84 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         const int nrel = 2 * R - 1;
         const unsigned short* rhs = reinterpret_cast<const unsigned short*>(rel_h);
         const unsigned short* rws = reinterpret_cast<const unsigned short*>(rel_w);
-        unsigned short* rhd = reinterpret_cast<unsigned short*>(Rh);
-        unsigned short* rwd = reinterpret_cast<unsigned short*>(Rw);
         for (int e = tid; e < p.RP * D; e += kRingThreads) {
             const bool in = e < nrel * D;
-            rhd[e] = in ? rhs[e] : (unsigned short)0;
-            rwd[e] = in ? rws[e] : (unsigned short)0;
+            lds_st<unsigned short>(smem, offrh + 2 * e, in ? rhs[e] : (unsigned short)0);
+            lds_st<unsigned short>(smem, offrw + 2 * e, in ? rws[e] : (unsigned short)0);
         }
     }
 
-    // ---- staging of image rows into the ring.  Item e of the row range
-    // starting at row0: 4 adjacent pixels x 8 channels (four 16-byte loads per
-    // tensor).  Off-image columns are zero; K is stored as is, V transposed in
-    // registers to eight 8-byte rows (4 columns of one channel).
-    auto load_item = [&](int e, int row0, u32x4 (&kk)[4], u32x4 (&vv)[4]) {
-        const int ch = e % CPP;
+    // ---- staging of image rows into the ring.  Item e of a range of rows:
+    // 4 adjacent pixels x 8 channels (four 16-byte loads per tensor).
+    // Off-image pixels are zero; K is stored swizzled, V transposed in
+    // registers to eight 8-byte rows (4 columns of one channel).  The running
+    // maxima of |k chunk|^2 over everything staged so far feed the softmax
+    // shift bound.
+    struct Item { int ch, c4, dr; };            // chunk, 4-column group, row within the range
+    auto item_of = [&](int e) {
+        Item it;
+        it.ch = e % CPP;
         const int rest = e / CPP;
-        const int c4 = rest % ng4;
-        const int iy = row0 + rest / ng4;
+        it.dr = rest / ng4;
+        it.c4 = rest - it.dr * ng4;
+        return it;
+    };
+    unsigned* kmax_bits = reinterpret_cast<unsigned*>(smem + p.off_kn);
+    if (tid < 16) kmax_bits[tid] = 0u;
+    __syncthreads();
+    auto load_item = [&](const Item& it, int row0, u32x4 (&kk)[4], u32x4 (&vv)[4]) {
+        const int iy = row0 + it.dr;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int ix = sx0 + 4 * c4 + j;
+            const int ix = sx0 + 4 * it.c4 + j;
             kk[j] = u32x4{0u, 0u, 0u, 0u};
             vv[j] = u32x4{0u, 0u, 0u, 0u};
             if (ix >= 0 && ix < g.W && iy >= 0 && iy < g.H) {
-                const int64_t off = ((int64_t)iy * g.W + ix) * D + ch * 8;
+                const int64_t off = ((int64_t)iy * g.W + ix) * D + it.ch * 8;
                 kk[j] = *reinterpret_cast<const u32x4*>(kb + off);
                 vv[j] = *reinterpret_cast<const u32x4*>(vb + off);
             }
         }
     };
-    auto store_item = [&](int e, int row0, const u32x4 (&kk)[4], const u32x4 (&vv)[4]) {
-        const int ch = e % CPP;
-        const int rest = e / CPP;
-        const int c4 = rest % ng4;
-        const int iy = row0 + rest / ng4;
+    auto store_item = [&](const Item& it, int row0, const u32x4 (&kk)[4], const u32x4 (&vv)[4]) {
+        const int iy = row0 + it.dr;
         const int slot = (iy + g.halo + ring) % ring;
+        float nmax = 0.f;                         // max over the 4 pixels of |k chunk|^2
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<u32x4*>(Kr + ((size_t)(slot * SWv + 4 * c4 + j) * D + ch * 8)) = kk[j];
+        for (int j = 0; j < 4; ++j) {
+            const int col = 4 * it.c4 + j;
+            lds_st<u32x4>(smem, (unsigned)slot * rowb_k + col * PIXB + k_chunk<D>(it.ch, col), kk[j]);
+            float ss = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float lo = __builtin_bit_cast(float, kk[j][w] << 16);
+                const float hi = __builtin_bit_cast(float, kk[j][w] & 0xffff0000u);
+                ss = fmaf(lo, lo, fmaf(hi, hi, ss));
+            }
+            nmax = fmaxf(nmax, ss);
+        }
+        atomicMax(&kmax_bits[it.ch], __builtin_bit_cast(unsigned, nmax));   // non-negative: bit order = value order
 #pragma unroll
         for (int w = 0; w < 4; ++w) {             // channels 2w (low halves), 2w+1 (high)
             const u32x2 lo = {__builtin_amdgcn_perm(vv[1][w], vv[0][w], 0x05040100u),
                               __builtin_amdgcn_perm(vv[3][w], vv[2][w], 0x05040100u)};
             const u32x2 hi = {__builtin_amdgcn_perm(vv[1][w], vv[0][w], 0x07060302u),
                               __builtin_amdgcn_perm(vv[3][w], vv[2][w], 0x07060302u)};
-            *reinterpret_cast<u32x2*>(Vr + ((size_t)(ch * 8 + 2 * w) * ring + slot) * SWv + 4 * c4) = lo;
-            *reinterpret_cast<u32x2*>(Vr + ((size_t)(ch * 8 + 2 * w + 1) * ring + slot) * SWv + 4 * c4) = hi;
+            const unsigned base = offv + 2u * ((unsigned)slot * SWv + 4 * it.c4);
+            lds_st<u32x2>(smem, base + 2u * (unsigned)((it.ch * 8 + 2 * w) * CP), lo);
+            lds_st<u32x2>(smem, base + 2u * (unsigned)((it.ch * 8 + 2 * w + 1) * CP), hi);
         }
     };
 
     // prologue: the first window's rows (off-image rows are stored as zeros)
     {
-        const int lo = -g.halo, hi = R - g.halo;
-        const int total = (hi - lo) * ng4 * CPP;
+        const int lo = -g.halo;
+        const int total = R * ng4 * CPP;
         for (int e = tid; e < total; e += kRingThreads) {
             u32x4 kk[4], vv[4];
-            load_item(e, lo, kk, vv);
-            store_item(e, lo, kk, vv);
+            const Item it = item_of(e);
+            load_item(it, lo, kk, vv);
+            store_item(it, lo, kk, vv);
         }
     }
     __syncthreads();
@@ -175,21 +225,23 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     for (int e = 0; e < 8; ++e) ones[e] = (short)0x3F80;
     asm volatile("" : "+v"(ones));   // opaque: kept in registers, never rebuilt
     const int items = nbx_here * p.groups;
-    const int rowpitch = SWv * D;                     // elements per ring row of K
     const int64_t qbase = bh * plane;
 
-    // Items (QT-tile groups) of block row `by` taken by this wave: the wave
+    // Items (QT-tile groups) of block row `byy` taken by this wave: the wave
     // assignment rotates by `items` per block row to balance the waves.
     auto first_item = [&](int byy) {
         const int rot = (int)(((int64_t)byy * items) % kRingWaves);
         return (wave - rot + kRingWaves) % kRingWaves;
     };
     struct Tile {   // one group of QT query tiles
-        int xb, wcol0, nqx, nq;
-        int qpix[QT];
-        int yl[QT], xl[QT];
+        int xb, wcol0;
+        int yl[QT], xl[QT];                   // block-local query position (full resolution)
+        int qpix[QT], opix[QT];               // query pixel in the image, output pixel
         bool qvalid[QT];
     };
+    // small non-negative integer quotient a / b through an fp32 reciprocal
+    // (exact for a < 2^16: (a + 0.5) / b stays > 0.5/b away from integers)
+    auto qdiv = [](int a, float rb) { return (int)(((float)a + 0.5f) * rb); };
     auto tile_of = [&](int byy, int it) {
         Tile T;
         const int j = it / p.groups, grp = it - j * p.groups;
@@ -197,16 +249,20 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         const int nqy = (min(yb + g.block, g.H) - yb + g.stride - 1) / g.stride;
         T.xb = (bx_first + j) * g.block;
         T.wcol0 = j * g.block;
-        T.nqx = (min(T.xb + g.block, g.W) - T.xb + g.stride - 1) / g.stride;
-        T.nq = nqy * T.nqx;
+        const int nqx = (min(T.xb + g.block, g.W) - T.xb + g.stride - 1) / g.stride;
+        const int nq = nqy * nqx;
+        const float rnqx = 1.0f / (float)nqx;
+        const int opix0 = (yb / g.stride) * g.Wo + T.xb / g.stride;   // block % stride == 0
 #pragma unroll
         for (int u = 0; u < QT; ++u) {
             const int qi = (grp * QT + u) * 16 + n;
-            T.qvalid[u] = qi < T.nq;
+            T.qvalid[u] = qi < nq;
             const int qq = T.qvalid[u] ? qi : 0;
-            T.yl[u] = (qq / T.nqx) * g.stride;
-            T.xl[u] = (qq % T.nqx) * g.stride;
+            const int iy = qdiv(qq, rnqx), ix = qq - iy * nqx;
+            T.yl[u] = iy * g.stride;
+            T.xl[u] = ix * g.stride;
             T.qpix[u] = (yb + T.yl[u]) * g.W + T.xb + T.xl[u];
+            T.opix[u] = opix0 + iy * g.Wo + ix;
         }
         return T;
     };
@@ -219,7 +275,8 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 const Tile T = tile_of(byy, it);
 #pragma unroll
                 for (int u = 0; u < QT; ++u)
-                    qf[ii][u] = *reinterpret_cast<const FragT*>(q + qbase + (int64_t)T.qpix[u] * D + gq * KPL);
+                    qf[ii][u] = *reinterpret_cast<const FragT*>(
+                        q + qbase + (int64_t)T.qpix[u] * D + gq * KPL);
             }
         }
     };
@@ -237,104 +294,193 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         const int wy0 = yb - g.halo;
         const int tlo = max(0, -wy0), thi = min(R, g.H - wy0);
         const int base = yb % ring;                   // ring slot of window row 0
-        auto slot = [&](int t) { const int s2 = base + t; return s2 >= ring ? s2 - ring : s2; };
 
-        // ---- relative logits: table . Q^T on MFMA, re-indexed per query in LDS
+        // ---- relative logits: table . Q^T on MFMA, re-indexed per query in LDS.
+        // Width first (it becomes the accumulator input of every score tile),
+        // then height (left in the scratch, read once per row and pass).
         f32x4 cinit[QT];
-        float RH[QT][R];
+        float rhmax[QT];                               // max over all height-table rows
+#pragma unroll
+        for (int u = 0; u < QT; ++u) rhmax[u] = -3.0e38f;
 #pragma unroll
         for (int pass = 0; pass < 2; ++pass) {
-            const __bf16* tab = pass == 0 ? Rw : Rh;
+            const unsigned tab = pass == 0 ? offrw : offrh;
             for (int rt = 0; rt < p.RP / 16; ++rt) {
-                const FragT a = *reinterpret_cast<const FragT*>(tab + (rt * 16 + n) * D + gq * KPL);
+                const FragT a = lds_ld<FragT>(smem, tab + 2u * ((rt * 16 + n) * D + gq * KPL));
 #pragma unroll
                 for (int u = 0; u < QT; ++u) {
                     const f32x4 gr = Frag<D>::mma(a, qf[u], f32x4{0.f, 0.f, 0.f, 0.f});
+                    if (pass == 1) rhmax[u] = fmaxf(rhmax[u], max4(gr));
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) scr[u * scr_stride + (rt * 16 + gq * 4 + i) * 16 + n] = gr[i];
+                    for (int i = 0; i < 4; ++i)
+                        lds_st<float>(smem, scr0 + u * scr_u + 4u * ((rt * 16 + gq * 4 + i) * kScrStride + n), gr[i]);
                 }
             }
             wave_lds_sync();
+            if (pass == 0) {
 #pragma unroll
-            for (int u = 0; u < QT; ++u) {
-                if (pass == 0) {
+                for (int u = 0; u < QT; ++u) {
                     // width term of window column c = 4g + i (masked: off-image, c >= R)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int c = gq * 4 + i;
                         const int ix = T.xb - g.halo + c;
                         const bool ok = c < R && ix >= 0 && ix < g.W;
-                        const float val = scr[u * scr_stride + min(R - 1 - T.xl[u] + c, p.RP - 1) * 16 + n];
+                        const int row = min(R - 1 - T.xl[u] + c, p.RP - 1);
+                        const float val = lds_ld<float>(smem, scr0 + u * scr_u + 4u * (row * kScrStride + n));
                         cinit[u][i] = ok ? val : kMaskLogit;
                     }
-                } else {
-                    // height term of window row t: table row R-1-yl+t (masked: off-image rows,
-                    // whose ring rows are zeros)
-                    const float* src = scr + u * scr_stride + (R - 1 - T.yl[u]) * 16 + n;
-#pragma unroll
-                    for (int t = 0; t < R; ++t) RH[u][t] = (t >= tlo && t < thi) ? src[t * 16] : kMaskLogit;
                 }
+                wave_lds_sync();
             }
-            wave_lds_sync();
         }
+#pragma unroll
+        for (int u = 0; u < QT; ++u) rhmax[u] = max_over_rows(rhmax[u]);
+        // scratch byte offset of the height term of window row 0, per tile
+        unsigned rh0[QT];
+#pragma unroll
+        for (int u = 0; u < QT; ++u) rh0[u] = scr0 + u * scr_u + 4u * ((R - 1 - T.yl[u]) * kScrStride + n);
+        auto rhv = [&](int u, int t) { return lds_ld<float>(smem, rh0[u] + 4u * kScrStride * t); };
 
-        const __bf16* kfrag = Kr + ((size_t)(T.wcol0 + n) * D + gq * KPL);
-        const __bf16* vfrag = Vr + (size_t)n * ring * SWv + T.wcol0 + gq * 4;
-        auto kload = [&](int t) -> FragT {
-            return *reinterpret_cast<const FragT*>(kfrag + (size_t)slot(t) * rowpitch);
+        // lane-constant LDS byte offsets of this lane's K and V^T fragments
+        const int kcol = T.wcol0 + n;
+        const unsigned kl = (unsigned)kcol * PIXB + (D == 16 ? k_chunk<D>(gq >> 1, kcol) + (gq & 1) * 8
+                                                             : k_chunk<D>(gq, kcol));
+        const unsigned vl = offv + 2u * ((unsigned)n * CP + T.wcol0 + 4 * gq);
+        auto rslot = [&](int t) -> unsigned {         // uniform: ring slot of window row t
+            const int s2 = base + t;
+            return (unsigned)(s2 >= ring ? s2 - ring : s2);
         };
+        auto kload = [&](int t) -> FragT { return lds_ld<FragT>(smem, kl + rslot(t) * rowb_k); };
         auto vload = [&](int mt, int t) -> u32x2 {
-            return *reinterpret_cast<const u32x2*>(vfrag + (size_t)(mt * 16 * ring + slot(t)) * SWv);
+            return lds_ld<u32x2>(smem, vl + 2u * ((unsigned)(mt * 16 * CP) + rslot(t) * SWv));
         };
 
-        // ---- pass 1: row max over the window (all R rows; masked rows carry -1e30)
-        float M[QT];
+        // ---- exact row max (pass 1) over the in-image rows [tlo, thi); the
+        // next row's operands are loaded one row ahead (clamped).
+        auto exact_max = [&](float (&mb)[QT]) {
+            float M[QT];
 #pragma unroll
-        for (int u = 0; u < QT; ++u) M[u] = -3.0e38f;
+            for (int u = 0; u < QT; ++u) M[u] = -3.0e38f;
+            FragT a = kload(tlo);
+            float rh[QT];
 #pragma unroll
-        for (int t = 0; t < R; ++t) {
-            const FragT a = kload(t);
+            for (int u = 0; u < QT; ++u) rh[u] = rhv(u, tlo);
+            for (int t = tlo; t < thi; ++t) {
+                const int tn = min(t + 1, thi - 1);
+                const FragT an = kload(tn);
+                float rhn[QT];
 #pragma unroll
-            for (int u = 0; u < QT; ++u)
-                M[u] = fmaxf(M[u], max4(Frag<D>::mma(a, qf[u], cinit[u])) + RH[u][t]);
-        }
-        float mb[QT];
-        f32x4 O[QT][D / 16], L[QT];
+                for (int u = 0; u < QT; ++u) rhn[u] = rhv(u, tn);
 #pragma unroll
-        for (int u = 0; u < QT; ++u) {
-            M[u] = fmaxf(M[u], __shfl_xor(M[u], 16));
-            M[u] = fmaxf(M[u], __shfl_xor(M[u], 32));
-            mb[u] = alpha * M[u];
-            L[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int u = 0; u < QT; ++u)
+                    M[u] = fmaxf(M[u], max4(Frag<D>::mma(a, qf[u], cinit[u])) + rh[u]);
+                a = an;
 #pragma unroll
-            for (int mt = 0; mt < D / 16; ++mt) O[u][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+                for (int u = 0; u < QT; ++u) rh[u] = rhn[u];
+            }
+#pragma unroll
+            for (int u = 0; u < QT; ++u) mb[u] = alpha * max_over_rows(M[u]);
+        };
 
-        // ---- pass 2: P = exp2(alpha*S - mb) in bf16; O^T += V^T . P^T, L += 1 . P^T
-#pragma unroll
-        for (int t = 0; t < R; t += 2) {
-            constexpr bool odd = (R % 2) != 0;
-            const bool two = !odd || t + 1 < R;
-            const FragT a0 = kload(t);
-            const FragT a1 = two ? kload(t + 1) : FragT{};
+        // ---- pass 2: P = exp2(alpha*S - mb) in bf16; O^T += V^T . P^T and
+        // L += 1 . P^T, one K=32 step per pair of rows (a missing second row
+        // of the last pair has zero weights).  Operands of the next pair are
+        // loaded one step ahead (clamped to the last row).
+        f32x4 O[QT][D / 16], L[QT];
+        struct Ops {
+            FragT a0, a1;
             u32x4 vw[D / 16];
+            float c0[QT], c1[QT];
+        };
+        auto fetch = [&](int t0) {
+            Ops o;
+            const int t1 = min(t0 + 1, thi - 1);
+            o.a0 = kload(t0);
+            o.a1 = kload(t1);
 #pragma unroll
             for (int mt = 0; mt < D / 16; ++mt) {
-                const u32x2 x0 = vload(mt, t);
-                const u32x2 x1 = two ? vload(mt, t + 1) : u32x2{0u, 0u};
-                vw[mt] = u32x4{x0[0], x0[1], x1[0], x1[1]};
+                const u32x2 x0 = vload(mt, t0), x1 = vload(mt, t1);
+                o.vw[mt] = u32x4{x0[0], x0[1], x1[0], x1[1]};
             }
 #pragma unroll
             for (int u = 0; u < QT; ++u) {
-                const u32x2 p0 = probs(Frag<D>::mma(a0, qf[u], cinit[u]), alpha * RH[u][t] - mb[u]);
-                u32x2 p1 = {0u, 0u};
-                if (two) p1 = probs(Frag<D>::mma(a1, qf[u], cinit[u]), alpha * RH[u][t + 1] - mb[u]);
-                const s16x8 pf = __builtin_bit_cast(s16x8, u32x4{p0[0], p0[1], p1[0], p1[1]});
-#pragma unroll
-                for (int mt = 0; mt < D / 16; ++mt)
-                    O[u][mt] = mma_k32(__builtin_bit_cast(s16x8, vw[mt]), pf, O[u][mt]);
-                L[u] = mma_k32(ones, pf, L[u]);
+                o.c0[u] = rhv(u, t0);
+                o.c1[u] = rhv(u, t1);
             }
+            return o;
+        };
+        auto weighted_sum = [&](const float (&mb)[QT]) {
+#pragma unroll
+            for (int u = 0; u < QT; ++u) {
+                L[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int mt = 0; mt < D / 16; ++mt) O[u][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            // double-buffered: the operands of the next pair are issued before
+            // the current pair is computed; scheduling barriers keep the
+            // compiler from sinking those loads back to their uses
+            auto compute = [&](const Ops& c, int t) {
+                const bool two = t + 1 < thi;              // uniform
+#pragma unroll
+                for (int u = 0; u < QT; ++u) {
+                    const u32x2 p0 = probs(Frag<D>::mma(c.a0, qf[u], cinit[u]), alpha * c.c0[u] - mb[u]);
+                    const float c1 = two ? alpha * c.c1[u] - mb[u] : -3.0e38f;
+                    const u32x2 p1 = probs(Frag<D>::mma(c.a1, qf[u], cinit[u]), c1);
+                    const s16x8 pf = __builtin_bit_cast(s16x8, u32x4{p0[0], p0[1], p1[0], p1[1]});
+#pragma unroll
+                    for (int mt = 0; mt < D / 16; ++mt)
+                        O[u][mt] = mma_k32(__builtin_bit_cast(s16x8, c.vw[mt]), pf, O[u][mt]);
+                    L[u] = mma_k32(ones, pf, L[u]);
+                }
+            };
+            Ops A = fetch(tlo), B;
+            for (int t = tlo;;) {
+                B = fetch(min(t + 2, thi - 1));
+                __builtin_amdgcn_sched_barrier(0);
+                compute(A, t);
+                __builtin_amdgcn_sched_barrier(0);
+                t += 2;
+                if (t >= thi) break;
+                A = fetch(min(t + 2, thi - 1));
+                __builtin_amdgcn_sched_barrier(0);
+                compute(B, t);
+                __builtin_amdgcn_sched_barrier(0);
+                t += 2;
+                if (t >= thi) break;
+            }
+        };
+
+        // ---- softmax shift: an upper bound on every logit of the query,
+        //   |q| * max|k| + max width term + max height term (Cauchy-Schwarz;
+        // max|k|^2 <= sum over 16-byte chunks of the running chunk maxima of
+        // all keys staged so far), so exp2 never overflows.  If the bound overshoots
+        // the true maximum by so much that the weights' sum falls below 2^-60,
+        // the group is redone with the exact maximum (pass 1).
+        float kmax2 = 0.f;                            // >= max |k|^2 over the window
+#pragma unroll
+        for (int c = 0; c < CPP; ++c) kmax2 += __builtin_bit_cast(float, kmax_bits[c]);
+        float mb[QT];
+#pragma unroll
+        for (int u = 0; u < QT; ++u) {
+            float qq = 0.f;
+#pragma unroll
+            for (int e = 0; e < KPL; ++e) {
+                const float x = __builtin_bit_cast(float, (unsigned)(unsigned short)qf[u][e] << 16);
+                qq = fmaf(x, x, qq);
+            }
+            qq = sum_over_rows(qq);
+            const float rw = max_over_rows(fmaxf(fmaxf(cinit[u][0], cinit[u][1]), fmaxf(cinit[u][2], cinit[u][3])));
+            const float bound = __builtin_sqrtf(qq * kmax2) + rw + rhmax[u];
+            mb[u] = alpha * (bound + 1e-3f * (1.f + fabsf(bound)));
+        }
+        weighted_sum(mb);
+        bool redo = false;
+#pragma unroll
+        for (int u = 0; u < QT; ++u) redo |= !(L[u][0] >= 0x1p-60f);
+        if (__any(redo)) {
+            exact_max(mb);
+            weighted_sum(mb);
         }
 
         // ---- normalise and store: lane (n, g) holds channels 16*mt + 4g + i of query n
@@ -342,9 +488,7 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         for (int u = 0; u < QT; ++u) {
             if (!T.qvalid[u]) continue;
             const float inv = 1.0f / L[u][0];
-            const int yq = T.qpix[u] / g.W, xq = T.qpix[u] - yq * g.W;
-            __bf16* op = out + bh * (int64_t)g.Ho * g.Wo * D +
-                         ((int64_t)(yq / g.stride) * g.Wo + xq / g.stride) * D + gq * 4;
+            __bf16* op = out + bh * (int64_t)g.Ho * g.Wo * D + (int64_t)T.opix[u] * D + gq * 4;
 #pragma unroll
             for (int mt = 0; mt < D / 16; ++mt) {
                 const u32x2 w = {pack_bf16x2(O[u][mt][0] * inv, O[u][mt][1] * inv),
@@ -354,6 +498,7 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         }
     };
 
+    const Item my_item = item_of(tid);            // this thread's staging item (fixed)
     FragT qcur[kRingMaxI][QT];
     load_q(0, qcur);
     for (int by = 0; by < g.nbh; ++by) {
@@ -363,7 +508,7 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         const int ntotal = by + 1 < g.nbh ? g.block * ng4 * CPP : 0;
         u32x4 pk[4], pv[4];
         const bool have = tid < ntotal;
-        if (have) load_item(tid, nlo, pk, pv);
+        if (have) load_item(my_item, nlo, pk, pv);
         FragT qnext[kRingMaxI][QT];
         load_q(by + 1, qnext);
 
@@ -389,11 +534,12 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 
         // ---- the next window's new rows go into the ring slots the current
         // window does not use; then one barrier
-        if (have) store_item(tid, nlo, pk, pv);
+        if (have) store_item(my_item, nlo, pk, pv);
         for (int e = tid + kRingThreads; e < ntotal; e += kRingThreads) {
             u32x4 kk[4], vv[4];
-            load_item(e, nlo, kk, vv);
-            store_item(e, nlo, kk, vv);
+            const Item it = item_of(e);
+            load_item(it, nlo, kk, vv);
+            store_item(it, nlo, kk, vv);
         }
         __syncthreads();
     }
@@ -408,17 +554,23 @@ static RingPlan ring_plan(const Geometry& g, int R, int qt, int nbx)
     p.nstrips = (g.nbw + nbx - 1) / nbx;
     p.SWv = rup(std::max(nbx * g.block + 2 * g.halo, (nbx - 1) * g.block + 16), 4);
     p.ring = R + g.block;
+    // V^T channel pitch: at least ring*SWv elements, and (pitch/2) = 4 (mod 64)
+    // dwords so the 16 channels of a fragment read land in distinct banks
+    p.CP = p.ring * p.SWv;
+    while (p.CP % 2 || (p.CP / 2) % 64 != 4) ++p.CP;
     p.RP = rup(2 * R - 1, 16);
     const int side = (g.block + g.stride - 1) / g.stride;
     p.groups = ((side * side + 15) / 16 + qt - 1) / qt;
     const int kb = p.ring * p.SWv * g.d * 2;
-    const int vb = g.d * p.ring * p.SWv * 2;
+    const int vb = g.d * p.CP * 2;
     const int rb = 2 * p.RP * g.d * 2;
-    const int sb = kRingWaves * qt * p.RP * 16 * 4;
+    const int sb = kRingWaves * qt * p.RP * kScrStride * 4;
     p.off_v = rup(kb, 16);
     p.off_rel = rup(p.off_v + vb, 16);
     p.off_scr = rup(p.off_rel + rb, 16);
-    p.lds_bytes = p.off_scr + sb;
+    p.off_kn = rup(p.off_scr + sb, 16);
+    p.lds_bytes = p.off_kn + 16 * 4;                        // running key-chunk norm maxima
+
     return p;
 }
 
@@ -440,6 +592,13 @@ static RingPlan ring_choose(const Geometry& g, int qt)
         if (p.lds_bytes <= limit) return p;
     }
     return RingPlan{};
+}
+
+static int ring_qt(const Geometry& g)
+{
+    const int side = (g.block + g.stride - 1) / g.stride;
+    const int tiles = (side * side + 15) / 16;
+    return (HALO_RING_QT > 1 && tiles % HALO_RING_QT == 0) ? HALO_RING_QT : 1;
 }
 
 template <int D, int R, int QT>
@@ -467,10 +626,7 @@ template <int D, int R>
 static hipError_t ring_launch_r(const void* q, const void* k, const void* v, const void* rh,
                                 const void* rw, void* out, const Geometry& g, hipStream_t st)
 {
-    const int side = (g.block + g.stride - 1) / g.stride;
-    const int tiles = (side * side + 15) / 16;
-    if (HALO_RING_QT > 1 && tiles % HALO_RING_QT == 0)
-        return ring_launch_t<D, R, HALO_RING_QT>(q, k, v, rh, rw, out, g, st);
+    if (ring_qt(g) > 1) return ring_launch_t<D, R, HALO_RING_QT>(q, k, v, rh, rw, out, g, st);
     return ring_launch_t<D, R, 1>(q, k, v, rh, rw, out, g, st);
 }
 
@@ -480,7 +636,8 @@ static bool ring_side(int r) { return r == 8 || r == 10 || r == 12 || r == 14 ||
 bool ring_supported(const Geometry& g)
 {
     if (!ring_side(g.r) || (g.d != 16 && g.d != 32) || g.block % 4 != 0) return false;
-    return ring_choose(g, 1).nbx != 0;
+    if ((int64_t)g.H * g.W >= (int64_t(1) << 31)) return false;   // pixel indices are 32-bit
+    return ring_choose(g, ring_qt(g)).nbx != 0;
 }
 
 hipError_t launch_ring(const void* q, const void* k, const void* v, const void* rh,

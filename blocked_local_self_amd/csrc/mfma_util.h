@@ -52,6 +52,20 @@ __device__ inline void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Reductions over the four lanes n, n+16, n+32, n+48 (the lanes holding one
+// query in the 16x16 MFMA layouts).  The gfx950 row-swap builtins are not
+// used: this compiler folds their second result into the first.
+__device__ inline float max_over_rows(float x)
+{
+    x = fmaxf(x, __shfl_xor(x, 16));
+    return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ inline float sum_over_rows(float x)
+{
+    x += __shfl_xor(x, 16);
+    return x + __shfl_xor(x, 32);
+}
+
 __device__ inline float max4(f32x4 s)
 {
     return fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));

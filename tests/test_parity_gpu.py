@@ -181,7 +181,8 @@ def test_p7_constant_values_and_linearity():
     assert np.abs(c - (a + b)).max() <= 2 * TOL["bf16"]
 
 
-def test_p9_block_shift_equivariance():
+@pytest.mark.parametrize("kernel", ["auto", "generic"])
+def test_p9_block_shift_equivariance(kernel):
     d, block, halo = 16, 8, 3
     g = torch.Generator().manual_seed(9)
     content = torch.randn(3, 1, 1, 32, 32, d, generator=g).to(torch.bfloat16)
@@ -190,10 +191,16 @@ def test_p9_block_shift_equivariance():
     rw = (torch.randn(2 * r - 1, d, generator=g) * d ** -0.5).to(torch.bfloat16)
     canvas = torch.randn(3, 1, 1, 48, 48, d, generator=g).to(torch.bfloat16)
     canvas[:, :, :, 8:40, 8:40] = content
-    base = f64(run((content[0], content[1], content[2], rh, rw), block, halo))
-    moved = f64(run((canvas[0].contiguous(), canvas[1].contiguous(), canvas[2].contiguous(), rh, rw), block, halo))
-    # interior blocks of the content (windows fully inside it)
-    assert np.abs(base[..., 8:24, 8:24, :] - moved[..., 16:32, 16:32, :]).max() <= 1e-6
+    base = f64(run((content[0], content[1], content[2], rh, rw), block, halo, kernel=kernel))
+    moved = f64(run((canvas[0].contiguous(), canvas[1].contiguous(), canvas[2].contiguous(), rh, rw),
+                    block, halo, kernel=kernel))
+    # interior blocks of the content (windows fully inside it).  The generic
+    # kernel's softmax shift is the window's own maximum, so the shifted result
+    # is bit-identical; the matrix-core kernels shift by an upper bound that
+    # uses key norms from outside the window, which moves only the bf16
+    # rounding of the probabilities.
+    err = np.abs(base[..., 8:24, 8:24, :] - moved[..., 16:32, 16:32, :]).max()
+    assert err <= (1e-6 if kernel == "generic" else 8e-3), err
 
 
 def test_p10_one_hot_tables_select_the_displaced_key():
