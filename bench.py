@@ -29,6 +29,34 @@ METRIC = "halo-attn fwd TFLOP/s + tokens/s per MI355X; % of MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MALL_BYTES = 256 * 2 ** 20     # Infinity Cache
 
+# HBM bytes per launch of the dominant kernel, per workload: rocprofv3 --pmc
+# FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by the ratio of
+# known bytes to the same counter's reading for a plain device copy
+# (--copy-calibration).  A record holds only for the kernel sources it was
+# measured on (``sources`` = kernel_source_hash() at the time); otherwise the
+# bench reports traffic as null.
+MEASURED_TRAFFIC = {
+    "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 134580029, "read": 101025597, "write": 33554432,
+                                        "sources": "8578df035a2343e6"},
+    "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 140898433, "read": 103149697, "write": 37748736,
+                                      "sources": "8578df035a2343e6"},
+    "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 92534278, "read": 84145670, "write": 8388608,
+                                       "sources": "8578df035a2343e6"},
+    "large_bf16_128x128_d32_b12h3": {"bytes_per_launch": 268626143, "read": 201517279, "write": 67108864,
+                                     "sources": "8578df035a2343e6"},
+}
+
+
+def kernel_source_hash() -> str:
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(HERE, "blocked_local_self_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -39,37 +67,61 @@ def parse():
     ap.add_argument("--kernel", default="auto", choices=["auto", "generic", "mfma"])
     ap.add_argument("--sets", type=int, default=0, help="rotated input sets (0: enough to exceed the MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
-    ap.add_argument("--traffic", default=None,
-                    help="JSON file with measured HBM bytes per launch for this workload (from rocprofv3 --pmc)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU-oracle sample time")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run --steps plain device copies of MIB MiB each "
+                         "(the reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args()
 
 
+def copy_calibration(mib, steps):
+    import torch
+    n = mib * 2 ** 20
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_copy": n, "bytes_written_per_copy": n,
+                                           "copies": steps}}), flush=True)
+
+
 def cpu_baseline(wl, inputs_cpu, target_s):
-    """Time the fp64 oracle on whole (batch, head) slices of the workload."""
+    """Time the fp64 oracle on whole (batch, head) slices of the workload.
+
+    The sample grows (more slices, then repeated passes over all of them)
+    until it holds about ``target_s`` seconds of CPU work.
+    """
     import numpy as np
     import oracle
     q, k, v, rh, rw = (t.to(dtype=__import__("torch").float64).numpy() for t in inputs_cpu)
     threads = oracle.max_threads()
-    per_slice_flops = wl.flops / (wl.B * wl.heads)
+    nslices = wl.B * wl.heads
+    per_slice_flops = wl.flops / nslices
 
     def run(nsl):
-        sl = lambda a: np.ascontiguousarray(a.reshape(wl.B * wl.heads, 1, *a.shape[2:])[:nsl])
+        sl = lambda a: np.ascontiguousarray(a.reshape(nslices, 1, *a.shape[2:])[:nsl])
+        args = [sl(q), sl(k), sl(v)]
         t0 = time.perf_counter()
-        oracle.halo_attn_ref(sl(q), sl(k), sl(v), rh, rw, wl.block, wl.halo, wl.stride, threads=threads)
+        oracle.halo_attn_ref(*args, rh, rw, wl.block, wl.halo, wl.stride, threads=threads)
         return time.perf_counter() - t0
 
-    n = min(threads, wl.B * wl.heads)
+    n = min(threads, nslices)
     t = run(n)
-    if t < target_s:
-        n2 = int(min(wl.B * wl.heads, max(n, n * target_s / max(t, 1e-3))))
+    if t < target_s and n < nslices:
+        n2 = int(min(nslices, n * target_s / max(t, 1e-3)))
         n2 = max(n, (n2 // threads) * threads) if n2 >= threads else n2
         if n2 > n:
             n, t = n2, run(n2)
-    flops = per_slice_flops * n
-    tokens = wl.tokens * n / (wl.B * wl.heads)   # token = position with all heads
+    passes = 1
+    while t < target_s and n == nslices and passes < 200:
+        t += run(n)
+        passes += 1
+    flops = per_slice_flops * n * passes
+    tokens = wl.tokens * n * passes / nslices   # token = output position with all heads
+    what = f"{n} of {nslices} (batch, head) slices" if n < nslices else f"all {nslices} (batch, head) slices"
     return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} of {wl.B * wl.heads} (batch, head) slices of {wl.name}, fp64, {t:.2f} s",
+            "sample": f"{what} of {wl.name} x {passes} pass(es), fp64, {t:.2f} s",
             "seconds": round(t, 3), "tokens_per_s": round(tokens / t, 1)}
 
 
@@ -79,6 +131,9 @@ def main():
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(the operation shards over batch x heads with no communication)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, args.steps)
+        return
     import torch
     from blocked_local_self_amd import halo_attn_fwd, workloads
     from blocked_local_self_amd.inputs import make_workload_inputs
@@ -122,11 +177,9 @@ def main():
     tflops = wl.flops / (ms * 1e-3) / 1e12
     achieved_gbs = wl.alg_bytes / (ms * 1e-3) / 1e9
 
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        rec = json.load(open(args.traffic))
-        if rec.get("workload") == wl.name:
-            traffic = rec.get("bytes_per_launch")
+    src_hash = kernel_source_hash()
+    rec = MEASURED_TRAFFIC.get(wl.name)
+    traffic = rec["bytes_per_launch"] if rec and rec["sources"] == src_hash else None
 
     line = {
         "metric": METRIC,
@@ -153,6 +206,7 @@ def main():
             "traffic": traffic,
             "alg_bytes_per_launch": wl.alg_bytes,
             "mean_launch_us": round(ms * 1e3, 3),
+            "kernel_sources": src_hash,
         },
     }
     if not args.no_cpu_baseline:
