@@ -159,8 +159,12 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         it.c4 = rest - it.dr * ng4;
         return it;
     };
+    // Two sets of maxima, by block-row parity: rows staged during block row
+    // `by` update set (by+1)&1 while the waves computing block row `by` read
+    // set by&1, which is final since the last barrier.  The bound a query
+    // sees is therefore independent of wave timing.
     unsigned* kmax_bits = reinterpret_cast<unsigned*>(smem + p.off_kn);
-    if (tid < 16) kmax_bits[tid] = 0u;
+    if (tid < 32) kmax_bits[tid] = 0u;
     __syncthreads();
     auto load_item = [&](const Item& it, int row0, u32x4 (&kk)[4], u32x4 (&vv)[4]) {
         const int iy = row0 + it.dr;
@@ -176,7 +180,7 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             }
         }
     };
-    auto store_item = [&](const Item& it, int row0, const u32x4 (&kk)[4], const u32x4 (&vv)[4]) {
+    auto store_item = [&](const Item& it, int row0, const u32x4 (&kk)[4], const u32x4 (&vv)[4], unsigned* kmax) {
         const int iy = row0 + it.dr;
         const int slot = (iy + g.halo + ring) % ring;
         float nmax = 0.f;                         // max over the 4 pixels of |k chunk|^2
@@ -193,7 +197,7 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             }
             nmax = fmaxf(nmax, ss);
         }
-        atomicMax(&kmax_bits[it.ch], __builtin_bit_cast(unsigned, nmax));   // non-negative: bit order = value order
+        atomicMax(&kmax[it.ch], __builtin_bit_cast(unsigned, nmax));   // non-negative: bit order = value order
 #pragma unroll
         for (int w = 0; w < 4; ++w) {             // channels 2w (low halves), 2w+1 (high)
             const u32x2 lo = {__builtin_amdgcn_perm(vv[1][w], vv[0][w], 0x05040100u),
@@ -214,7 +218,7 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             u32x4 kk[4], vv[4];
             const Item it = item_of(e);
             load_item(it, lo, kk, vv);
-            store_item(it, lo, kk, vv);
+            store_item(it, lo, kk, vv, kmax_bits);
         }
     }
     __syncthreads();
@@ -459,7 +463,7 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         // the group is redone with the exact maximum (pass 1).
         float kmax2 = 0.f;                            // >= max |k|^2 over the window
 #pragma unroll
-        for (int c = 0; c < CPP; ++c) kmax2 += __builtin_bit_cast(float, kmax_bits[c]);
+        for (int c = 0; c < CPP; ++c) kmax2 += __builtin_bit_cast(float, kmax_bits[16 * (byy & 1) + c]);
         float mb[QT];
 #pragma unroll
         for (int u = 0; u < QT; ++u) {
@@ -501,7 +505,13 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const Item my_item = item_of(tid);            // this thread's staging item (fixed)
     FragT qcur[kRingMaxI][QT];
     load_q(0, qcur);
+    // Drain these loads now (vmcnt(0)).  Otherwise the first use of qcur
+    // inside the block-row loop carries a conservative wait for every vector
+    // load in flight, i.e. for the next block row's prefetch.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     for (int by = 0; by < g.nbh; ++by) {
+        unsigned* kmax_next = kmax_bits + 16 * ((by + 1) & 1);
+        if (tid < 16) atomicMax(&kmax_next[tid], kmax_bits[16 * (by & 1) + tid]);
         // ---- fetch, for the next block row, the window rows it adds (rows
         // past the image bottom are zeros) and its query fragments
         const int nlo = by * g.block + g.block + g.halo;
@@ -534,12 +544,12 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 
         // ---- the next window's new rows go into the ring slots the current
         // window does not use; then one barrier
-        if (have) store_item(my_item, nlo, pk, pv);
+        if (have) store_item(my_item, nlo, pk, pv, kmax_next);
         for (int e = tid + kRingThreads; e < ntotal; e += kRingThreads) {
             u32x4 kk[4], vv[4];
             const Item it = item_of(e);
             load_item(it, nlo, kk, vv);
-            store_item(it, nlo, kk, vv);
+            store_item(it, nlo, kk, vv, kmax_next);
         }
         __syncthreads();
     }
@@ -569,7 +579,7 @@ static RingPlan ring_plan(const Geometry& g, int R, int qt, int nbx)
     p.off_rel = rup(p.off_v + vb, 16);
     p.off_scr = rup(p.off_rel + rb, 16);
     p.off_kn = rup(p.off_scr + sb, 16);
-    p.lds_bytes = p.off_kn + 16 * 4;                        // running key-chunk norm maxima
+    p.lds_bytes = p.off_kn + 2 * 16 * 4;                    // running key-chunk norm maxima, 2 sets
 
     return p;
 }

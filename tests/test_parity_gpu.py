@@ -261,6 +261,18 @@ def test_deterministic_and_stream_aware():
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("name", ["early_stage_bf16_64x64_d16_b8h3", "mid_stage_bf16_32x32_d32_b8h3"])
+def test_full_workload_is_bitwise_reproducible(name):
+    # many workgroups in flight: results must not depend on wave timing
+    wl = workloads.get(name)
+    q, k, v, rh, rw = (t.to(DEV) for t in make_workload_inputs(wl, seed=3))
+    first = halo_attn_fwd(q, k, v, rh, rw, wl.block, wl.halo, wl.stride)
+    for _ in range(6):
+        again = halo_attn_fwd(q, k, v, rh, rw, wl.block, wl.halo, wl.stride)
+        torch.cuda.synchronize()
+        assert torch.equal(first, again)
+
+
 def test_empty_batch_and_errors_on_gpu():
     q = torch.zeros(0, 2, 8, 8, 16, dtype=torch.bfloat16, device=DEV)
     t = torch.zeros(11, 16, dtype=torch.bfloat16, device=DEV)
