@@ -10,14 +10,17 @@
 //
 // Work decomposition (MI355X-first):
 //  * one workgroup owns one (batch, head) image strip of `nbx` adjacent block
-//    columns and walks down its block rows.  Window rows live in an LDS ring
-//    of R + block rows: the R rows of the current window plus the `block`
-//    rows the next window adds.  The vertical halo overlap is reused in LDS as
-//    well as the horizontal one, so every K/V pixel of the strip is read from
-//    HBM once; the next rows (and the next query fragments) are fetched into
-//    registers while the current block row computes, then written to the
-//    ring: one barrier per block row.  Rows above or below the image are kept
-//    as zero rows, so every block row runs the same code.
+//    columns and walks down its block rows.  The R rows of the current window
+//    live in an LDS ring.  The vertical halo overlap is reused in LDS as well
+//    as the horizontal one, so every K/V pixel of the strip is read from HBM
+//    once; the `block` rows the next window adds (and the next query
+//    fragments) are fetched into registers while the current block row
+//    computes, then replace the rows the next window drops: a barrier before
+//    and one after that store.  Rows above or below the image are kept as
+//    zero rows, so every block row runs the same code.
+//  * workgroups of 4 or 8 waves: with 4, two workgroups share a CU and one's
+//    barrier waits overlap the other's compute; the strip width is the widest
+//    whose ring fits the LDS share.
 //  * LDS layouts are chosen for conflict-free fragment reads: K is
 //    [slot][col][d] with the 16-byte chunks of a pixel XOR-swizzled by column
 //    bits; V is transposed to [d][slot][col] with the channel pitch padded to
@@ -46,19 +49,20 @@
 
 namespace halo {
 
-#ifndef HALO_RING_WAVES
-#define HALO_RING_WAVES 8
-#endif
 #ifndef HALO_RING_QT
 #define HALO_RING_QT 2
+#endif
+#ifndef HALO_RING_FORCE_WAVES
+#define HALO_RING_FORCE_WAVES 0   // 4 or 8 to override the per-shape choice
 #endif
 #ifndef HALO_RING_MAXI
 #define HALO_RING_MAXI 2      // query groups per wave per block row with prefetched Q
 #endif
-constexpr int kRingWaves = HALO_RING_WAVES;
-constexpr int kRingThreads = 64 * kRingWaves;
+constexpr int kLdsPerCU = 160 * 1024;   // gfx950
 constexpr int kRingMaxI = HALO_RING_MAXI;
 constexpr int kScrStride = 20;        // floats per scratch row (conflict-free writes)
+constexpr int kRelTiles = 2;          // relative tables padded to 32 rows: 2R-1 <= 31 and
+constexpr int kRelRows = 16 * kRelTiles;   // R-1+15 <= 30 for every R <= 16
 
 struct RingPlan {
     int nstrips;     // column strips per image
@@ -66,7 +70,6 @@ struct RingPlan {
     int SWv;         // strip width in pixels (multiple of 4)
     int ring;        // LDS ring rows (R + block)
     int CP;          // V^T channel pitch in elements (ring*SWv, padded)
-    int RP;          // relative-table rows padded to a multiple of 16
     int groups;      // QT-tile groups per block
     int off_v, off_rel, off_scr, off_kn, lds_bytes;
     int remap_xcd;
@@ -94,14 +97,16 @@ __device__ inline unsigned k_chunk(int c, int col)
     return (unsigned)((c ^ ((col >> 2) & 3)) * 16);
 }
 
-template <int D, int R, int QT>
-__global__ __launch_bounds__(kRingThreads)
+template <int D, int R, int QT, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2)))
 void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                  const __bf16* __restrict__ v, const __bf16* __restrict__ rel_h,
                  const __bf16* __restrict__ rel_w, __bf16* __restrict__ out,
                  Geometry g, RingPlan p)
 {
     static_assert(R <= 16, "one 16-column tile per window row");
+    constexpr int kRingWaves = W;
+    constexpr int kRingThreads = 64 * W;
     constexpr int KPL = D / 4;                 // channels per lane in a QK fragment
     constexpr int CPP = D / 8;                 // 16-byte chunks per pixel
     constexpr unsigned PIXB = D * 2;           // bytes per pixel
@@ -109,13 +114,15 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     extern __shared__ __align__(16) unsigned char smem[];
     const int ring = p.ring, SWv = p.SWv, CP = p.CP;
     const unsigned rowb_k = (unsigned)SWv * PIXB;            // bytes per K ring row
-    const unsigned offv = p.off_v, offrh = p.off_rel, offrw = p.off_rel + p.RP * D * 2;
+    const unsigned offv = p.off_v, offrh = p.off_rel, offrw = p.off_rel + kRelRows * D * 2;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, gq = lane >> 4;
-    const unsigned scr_u = (unsigned)p.RP * kScrStride * 4;  // bytes per query tile
+    constexpr unsigned scr_u = (unsigned)kRelRows * kScrStride * 4;   // bytes per query tile
     const unsigned scr0 = p.off_scr + wave * QT * scr_u;
+    const unsigned scr_lane = scr0 + 4u * (4 * gq * kScrStride + n);   // row 4g, column n
 
     int64_t wg = blockIdx.x;
     if (p.remap_xcd) {
@@ -132,12 +139,12 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const __bf16* vb = v + bh * plane;
     const int ng4 = SWv / 4;
 
-    // ---- relative tables, zero-padded to RP rows
+    // ---- relative tables, zero-padded to kRelRows rows
     {
         const int nrel = 2 * R - 1;
         const unsigned short* rhs = reinterpret_cast<const unsigned short*>(rel_h);
         const unsigned short* rws = reinterpret_cast<const unsigned short*>(rel_w);
-        for (int e = tid; e < p.RP * D; e += kRingThreads) {
+        for (int e = tid; e < kRelRows * D; e += kRingThreads) {
             const bool in = e < nrel * D;
             lds_st<unsigned short>(smem, offrh + 2 * e, in ? rhs[e] : (unsigned short)0);
             lds_st<unsigned short>(smem, offrw + 2 * e, in ? rws[e] : (unsigned short)0);
@@ -223,6 +230,14 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
     __syncthreads();
 
+    // relative tables as MFMA A operands, kept in registers
+    FragT tabw[kRelTiles], tabh[kRelTiles];
+#pragma unroll
+    for (int rt = 0; rt < kRelTiles; ++rt) {
+        tabw[rt] = lds_ld<FragT>(smem, offrw + 2u * ((rt * 16 + n) * D + gq * KPL));
+        tabh[rt] = lds_ld<FragT>(smem, offrh + 2u * ((rt * 16 + n) * D + gq * KPL));
+    }
+
     const float alpha = p.alpha;
     s16x8 ones;
 #pragma unroll
@@ -255,7 +270,7 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         T.wcol0 = j * g.block;
         const int nqx = (min(T.xb + g.block, g.W) - T.xb + g.stride - 1) / g.stride;
         const int nq = nqy * nqx;
-        const float rnqx = 1.0f / (float)nqx;
+        const float rnqx = __builtin_amdgcn_rcpf((float)nqx);   // 1 ulp: ample for qdiv
         const int opix0 = (yb / g.stride) * g.Wo + T.xb / g.stride;   // block % stride == 0
 #pragma unroll
         for (int u = 0; u < QT; ++u) {
@@ -299,47 +314,80 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         const int tlo = max(0, -wy0), thi = min(R, g.H - wy0);
         const int base = yb % ring;                   // ring slot of window row 0
 
-        // ---- relative logits: table . Q^T on MFMA, re-indexed per query in LDS.
-        // Width first (it becomes the accumulator input of every score tile),
-        // then height (left in the scratch, read once per row and pass).
-        f32x4 cinit[QT];
-        float rhmax[QT];                               // max over all height-table rows
+        // ---- relative logits: G = table . Q^T on MFMA (both tables at once,
+        // operands in registers), re-indexed per query through the scratch.
+        // Scratch row j, column n holds G[j][n].  All scratch traffic below
+        // is this wave's own, and LDS executes one wave's accesses in program
+        // order, so no waits are needed between the stores and the loads.
+        f32x4 gw[QT][kRelTiles], gh[QT][kRelTiles];
 #pragma unroll
-        for (int u = 0; u < QT; ++u) rhmax[u] = -3.0e38f;
+        for (int u = 0; u < QT; ++u)
 #pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
-            const unsigned tab = pass == 0 ? offrw : offrh;
-            for (int rt = 0; rt < p.RP / 16; ++rt) {
-                const FragT a = lds_ld<FragT>(smem, tab + 2u * ((rt * 16 + n) * D + gq * KPL));
-#pragma unroll
-                for (int u = 0; u < QT; ++u) {
-                    const f32x4 gr = Frag<D>::mma(a, qf[u], f32x4{0.f, 0.f, 0.f, 0.f});
-                    if (pass == 1) rhmax[u] = fmaxf(rhmax[u], max4(gr));
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        lds_st<float>(smem, scr0 + u * scr_u + 4u * ((rt * 16 + gq * 4 + i) * kScrStride + n), gr[i]);
-                }
+            for (int rt = 0; rt < kRelTiles; ++rt) {
+                gw[u][rt] = Frag<D>::mma(tabw[rt], qf[u], f32x4{0.f, 0.f, 0.f, 0.f});
+                gh[u][rt] = Frag<D>::mma(tabh[rt], qf[u], f32x4{0.f, 0.f, 0.f, 0.f});
             }
-            wave_lds_sync();
-            if (pass == 0) {
+        // width products -> scratch
 #pragma unroll
-                for (int u = 0; u < QT; ++u) {
-                    // width term of window column c = 4g + i (masked: off-image, c >= R)
+        for (int u = 0; u < QT; ++u)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int c = gq * 4 + i;
-                        const int ix = T.xb - g.halo + c;
-                        const bool ok = c < R && ix >= 0 && ix < g.W;
-                        const int row = min(R - 1 - T.xl[u] + c, p.RP - 1);
-                        const float val = lds_ld<float>(smem, scr0 + u * scr_u + 4u * (row * kScrStride + n));
-                        cinit[u][i] = ok ? val : kMaskLogit;
-                    }
-                }
-                wave_lds_sync();
+            for (int rt = 0; rt < kRelTiles; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    lds_st<float>(smem, scr_lane + u * scr_u + 4u * (rt * 16 + i) * kScrStride, gw[u][rt][i]);
+        // width term of window column c = 4g + i for query n: table row
+        // R-1-xl+c (masked: off-image, c >= R)
+        const int clo = g.halo - T.xb, chi = min(R, g.W - T.xb + g.halo);
+        f32x4 cinit[QT];
+#pragma unroll
+        for (int u = 0; u < QT; ++u) {
+            const unsigned a = scr0 + u * scr_u + 4u * ((R - 1 - T.xl[u] + 4 * gq) * kScrStride + n);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = 4 * gq + i;
+                const float val = lds_ld<float>(smem, a + 4u * i * kScrStride);
+                cinit[u][i] = (c >= clo && c < chi) ? val : kMaskLogit;
             }
         }
+
+        // ---- softmax shift: an upper bound on every logit of the query,
+        //   |q| * max|k| + max width term + max height term (Cauchy-Schwarz;
+        // max|k|^2 <= sum over 16-byte chunks of the running chunk maxima of
+        // the keys staged so far; the height maximum runs over all table
+        // rows), so exp2 never overflows.  Should the bound overshoot the true
+        // maximum so far that the weights' sum falls below 2^-60, the group is
+        // redone with the exact maximum.
+        float kmax2 = 0.f;
 #pragma unroll
-        for (int u = 0; u < QT; ++u) rhmax[u] = max_over_rows(rhmax[u]);
+        for (int c = 0; c < CPP; ++c) kmax2 += __builtin_bit_cast(float, kmax_bits[16 * (byy & 1) + c]);
+        float mb[QT];
+#pragma unroll
+        for (int u = 0; u < QT; ++u) {
+            float qq = 0.f;
+#pragma unroll
+            for (int e = 0; e < KPL; ++e) {
+                const float x = __builtin_bit_cast(float, (unsigned)(unsigned short)qf[u][e] << 16);
+                qq = fmaf(x, x, qq);
+            }
+            float hm = max4(gh[u][0]);
+#pragma unroll
+            for (int rt = 1; rt < kRelTiles; ++rt) hm = fmaxf(hm, max4(gh[u][rt]));
+            qq = sum_over_rows(qq);
+            const float rw = max_over_rows(max4(cinit[u]));
+            hm = max_over_rows(hm);
+            const float bound = __builtin_sqrtf(qq * kmax2) + rw + hm;
+            mb[u] = alpha * (bound + 1e-3f * (1.f + fabsf(bound)));
+        }
+        // height products, already in shifted base-2 units alpha*G - mb,
+        // -> scratch (after the width reads above, in program order)
+#pragma unroll
+        for (int u = 0; u < QT; ++u)
+#pragma unroll
+            for (int rt = 0; rt < kRelTiles; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    lds_st<float>(smem, scr_lane + u * scr_u + 4u * (rt * 16 + i) * kScrStride,
+                                  fmaf(gh[u][rt][i], alpha, -mb[u]));
         // scratch byte offset of the height term of window row 0, per tile
         unsigned rh0[QT];
 #pragma unroll
@@ -360,37 +408,10 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             return lds_ld<u32x2>(smem, vl + 2u * ((unsigned)(mt * 16 * CP) + rslot(t) * SWv));
         };
 
-        // ---- exact row max (pass 1) over the in-image rows [tlo, thi); the
-        // next row's operands are loaded one row ahead (clamped).
-        auto exact_max = [&](float (&mb)[QT]) {
-            float M[QT];
-#pragma unroll
-            for (int u = 0; u < QT; ++u) M[u] = -3.0e38f;
-            FragT a = kload(tlo);
-            float rh[QT];
-#pragma unroll
-            for (int u = 0; u < QT; ++u) rh[u] = rhv(u, tlo);
-            for (int t = tlo; t < thi; ++t) {
-                const int tn = min(t + 1, thi - 1);
-                const FragT an = kload(tn);
-                float rhn[QT];
-#pragma unroll
-                for (int u = 0; u < QT; ++u) rhn[u] = rhv(u, tn);
-#pragma unroll
-                for (int u = 0; u < QT; ++u)
-                    M[u] = fmaxf(M[u], max4(Frag<D>::mma(a, qf[u], cinit[u])) + rh[u]);
-                a = an;
-#pragma unroll
-                for (int u = 0; u < QT; ++u) rh[u] = rhn[u];
-            }
-#pragma unroll
-            for (int u = 0; u < QT; ++u) mb[u] = alpha * max_over_rows(M[u]);
-        };
-
-        // ---- pass 2: P = exp2(alpha*S - mb) in bf16; O^T += V^T . P^T and
-        // L += 1 . P^T, one K=32 step per pair of rows (a missing second row
-        // of the last pair has zero weights).  Operands of the next pair are
-        // loaded one step ahead (clamped to the last row).
+        // ---- weighted sum: P = exp2(alpha*S + (alpha*rh - mb)) in bf16;
+        // O^T += V^T . P^T and L += 1 . P^T, one K=32 step per pair of rows (a
+        // missing second row of the last pair has zero weights).  Operands of
+        // the next pair are loaded one step ahead (clamped to the last row).
         f32x4 O[QT][D / 16], L[QT];
         struct Ops {
             FragT a0, a1;
@@ -414,7 +435,7 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             }
             return o;
         };
-        auto weighted_sum = [&](const float (&mb)[QT]) {
+        auto weighted_sum = [&]() {
 #pragma unroll
             for (int u = 0; u < QT; ++u) {
                 L[u] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -428,9 +449,8 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 const bool two = t + 1 < thi;              // uniform
 #pragma unroll
                 for (int u = 0; u < QT; ++u) {
-                    const u32x2 p0 = probs(Frag<D>::mma(c.a0, qf[u], cinit[u]), alpha * c.c0[u] - mb[u]);
-                    const float c1 = two ? alpha * c.c1[u] - mb[u] : -3.0e38f;
-                    const u32x2 p1 = probs(Frag<D>::mma(c.a1, qf[u], cinit[u]), c1);
+                    const u32x2 p0 = probs(Frag<D>::mma(c.a0, qf[u], cinit[u]), c.c0[u]);
+                    const u32x2 p1 = probs(Frag<D>::mma(c.a1, qf[u], cinit[u]), two ? c.c1[u] : -3.0e38f);
                     const s16x8 pf = __builtin_bit_cast(s16x8, u32x4{p0[0], p0[1], p1[0], p1[1]});
 #pragma unroll
                     for (int mt = 0; mt < D / 16; ++mt)
@@ -455,43 +475,39 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             }
         };
 
-        // ---- softmax shift: an upper bound on every logit of the query,
-        //   |q| * max|k| + max width term + max height term (Cauchy-Schwarz;
-        // max|k|^2 <= sum over 16-byte chunks of the running chunk maxima of
-        // all keys staged so far), so exp2 never overflows.  If the bound overshoots
-        // the true maximum by so much that the weights' sum falls below 2^-60,
-        // the group is redone with the exact maximum (pass 1).
-        float kmax2 = 0.f;                            // >= max |k|^2 over the window
-#pragma unroll
-        for (int c = 0; c < CPP; ++c) kmax2 += __builtin_bit_cast(float, kmax_bits[16 * (byy & 1) + c]);
-        float mb[QT];
-#pragma unroll
-        for (int u = 0; u < QT; ++u) {
-            float qq = 0.f;
-#pragma unroll
-            for (int e = 0; e < KPL; ++e) {
-                const float x = __builtin_bit_cast(float, (unsigned)(unsigned short)qf[u][e] << 16);
-                qq = fmaf(x, x, qq);
-            }
-            qq = sum_over_rows(qq);
-            const float rw = max_over_rows(fmaxf(fmaxf(cinit[u][0], cinit[u][1]), fmaxf(cinit[u][2], cinit[u][3])));
-            const float bound = __builtin_sqrtf(qq * kmax2) + rw + rhmax[u];
-            mb[u] = alpha * (bound + 1e-3f * (1.f + fabsf(bound)));
-        }
-        weighted_sum(mb);
+        weighted_sum();
         bool redo = false;
 #pragma unroll
         for (int u = 0; u < QT; ++u) redo |= !(L[u][0] >= 0x1p-60f);
         if (__any(redo)) {
-            exact_max(mb);
-            weighted_sum(mb);
+            // exact maximum M of the shifted base-2 logits over the in-image
+            // rows, then shift the stored height terms by -M and redo
+            float M[QT];
+#pragma unroll
+            for (int u = 0; u < QT; ++u) M[u] = -3.0e38f;
+            for (int t = tlo; t < thi; ++t) {
+                const FragT a = kload(t);
+#pragma unroll
+                for (int u = 0; u < QT; ++u)
+                    M[u] = fmaxf(M[u], fmaf(max4(Frag<D>::mma(a, qf[u], cinit[u])), alpha, rhv(u, t)));
+            }
+#pragma unroll
+            for (int u = 0; u < QT; ++u) {
+                const float m = max_over_rows(M[u]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {          // window rows 4g..4g+3 of query n
+                    const unsigned a = rh0[u] + 4u * kScrStride * (4 * gq + i);
+                    lds_st<float>(smem, a, lds_ld<float>(smem, a) - m);
+                }
+            }
+            weighted_sum();
         }
 
         // ---- normalise and store: lane (n, g) holds channels 16*mt + 4g + i of query n
 #pragma unroll
         for (int u = 0; u < QT; ++u) {
             if (!T.qvalid[u]) continue;
-            const float inv = 1.0f / L[u][0];
+            const float inv = __builtin_amdgcn_rcpf(L[u][0]);
             __bf16* op = out + bh * (int64_t)g.Ho * g.Wo * D + (int64_t)T.opix[u] * D + gq * 4;
 #pragma unroll
             for (int mt = 0; mt < D / 16; ++mt) {
@@ -542,8 +558,9 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
             for (int u = 0; u < QT; ++u) qcur[ii][u] = qnext[ii][u];
 
-        // ---- the next window's new rows go into the ring slots the current
-        // window does not use; then one barrier
+        // ---- once every wave is done with this window, the next window's new
+        // rows replace its first `block` rows in the ring
+        __syncthreads();
         if (have) store_item(my_item, nlo, pk, pv, kmax_next);
         for (int e = tid + kRingThreads; e < ntotal; e += kRingThreads) {
             u32x4 kk[4], vv[4];
@@ -557,24 +574,23 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 
 static int rup(int x, int m) { return (x + m - 1) / m * m; }
 
-static RingPlan ring_plan(const Geometry& g, int R, int qt, int nbx)
+static RingPlan ring_plan(const Geometry& g, int R, int qt, int waves, int nbx)
 {
     RingPlan p{};
     p.nbx = nbx;
     p.nstrips = (g.nbw + nbx - 1) / nbx;
     p.SWv = rup(std::max(nbx * g.block + 2 * g.halo, (nbx - 1) * g.block + 16), 4);
-    p.ring = R + g.block;
+    p.ring = R;
     // V^T channel pitch: at least ring*SWv elements, and (pitch/2) = 4 (mod 64)
     // dwords so the 16 channels of a fragment read land in distinct banks
     p.CP = p.ring * p.SWv;
     while (p.CP % 2 || (p.CP / 2) % 64 != 4) ++p.CP;
-    p.RP = rup(2 * R - 1, 16);
     const int side = (g.block + g.stride - 1) / g.stride;
     p.groups = ((side * side + 15) / 16 + qt - 1) / qt;
     const int kb = p.ring * p.SWv * g.d * 2;
     const int vb = g.d * p.CP * 2;
-    const int rb = 2 * p.RP * g.d * 2;
-    const int sb = kRingWaves * qt * p.RP * kScrStride * 4;
+    const int rb = 2 * kRelRows * g.d * 2;
+    const int sb = waves * qt * kRelRows * kScrStride * 4;
     p.off_v = rup(kb, 16);
     p.off_rel = rup(p.off_v + vb, 16);
     p.off_scr = rup(p.off_rel + rb, 16);
@@ -584,24 +600,64 @@ static RingPlan ring_plan(const Geometry& g, int R, int qt, int nbx)
     return p;
 }
 
-static int ring_lds_limit()
+// LDS a workgroup of `waves` waves may use so that 8 / waves of them share
+// a CU (the device limit per workgroup caps it too).
+static int ring_lds_limit(int waves)
 {
     int dev = 0, bytes = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 64 * 1024;
     if (hipDeviceGetAttribute(&bytes, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
         return 64 * 1024;
-    return bytes;
+    return std::min(bytes, kLdsPerCU * waves / 8);
 }
 
-// Plan for these arguments, or nbx = 0 when the ring does not fit in LDS.
-static RingPlan ring_choose(const Geometry& g, int qt)
+static int device_cus()
 {
-    const int limit = ring_lds_limit();
-    for (int nbx = g.nbw; nbx >= 1; --nbx) {
-        RingPlan p = ring_plan(g, g.r, qt, nbx);
-        if (p.lds_bytes <= limit) return p;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return 256;
+    return cus;
+}
+
+// Widest plan that fits in LDS with at least `min_strips` strips per image,
+// or nbx = 0 when even one block column does not fit.
+static RingPlan ring_choose(const Geometry& g, int qt, int waves, int min_strips = 1)
+{
+    const int limit = ring_lds_limit(waves);
+    for (int nbx = (g.nbw + min_strips - 1) / min_strips; nbx >= 1; --nbx) {
+        if (ring_plan(g, g.r, qt, waves, nbx).lds_bytes > limit) continue;
+        // as few strips as fit, then equal widths (no narrow remainder strip)
+        const int nstrips = (g.nbw + nbx - 1) / nbx;
+        return ring_plan(g, g.r, qt, waves, (g.nbw + nstrips - 1) / nstrips);
     }
     return RingPlan{};
+}
+
+// Strips per image a 4-wave launch needs for two workgroups on every CU.
+static int ring_min_strips4(const Geometry& g)
+{
+    const int64_t want = 2 * (int64_t)device_cus();
+    const int64_t s = (want + g.BH - 1) / g.BH;
+    return (int)std::min<int64_t>(std::max<int64_t>(s, 1), g.nbw);
+}
+
+// Workgroup size: two 4-wave workgroups per CU overlap one's barrier waits
+// with the other's compute, at the price of narrower strips (more halo
+// columns staged per useful column).  Take them when the launch has enough
+// workgroups to fill both slots of every CU and the price is low.
+static int ring_waves(const Geometry& g, int qt)
+{
+    if (HALO_RING_FORCE_WAVES == 4)
+        return ring_choose(g, qt, 4, ring_min_strips4(g)).nbx ? 4 : 0;
+    if (HALO_RING_FORCE_WAVES == 8)
+        return ring_choose(g, qt, 8).nbx ? 8 : 0;
+    const RingPlan p4 = ring_choose(g, qt, 4, ring_min_strips4(g)), p8 = ring_choose(g, qt, 8);
+    if (p8.nbx == 0) return p4.nbx ? 4 : 0;
+    if (p4.nbx == 0 || g.BH * p4.nstrips < 2 * (int64_t)device_cus()) return 8;
+    const double cost4 = (double)p4.SWv / (p4.nbx * g.block);
+    const double cost8 = (double)p8.SWv / (p8.nbx * g.block);
+    return cost4 <= 1.15 * cost8 ? 4 : 8;
 }
 
 static int ring_qt(const Geometry& g)
@@ -611,33 +667,43 @@ static int ring_qt(const Geometry& g)
     return (HALO_RING_QT > 1 && tiles % HALO_RING_QT == 0) ? HALO_RING_QT : 1;
 }
 
-template <int D, int R, int QT>
+template <int D, int R, int QT, int W>
 static hipError_t ring_launch_t(const void* q, const void* k, const void* v, const void* rh,
                                 const void* rw, void* out, const Geometry& g, hipStream_t st)
 {
-    RingPlan p = ring_choose(g, QT);
+    RingPlan p = W == 4 ? ring_choose(g, QT, 4, ring_min_strips4(g)) : ring_choose(g, QT, 8);
     if (p.nbx == 0) return hipErrorInvalidConfiguration;
     p.nwg = g.BH * p.nstrips;
     p.remap_xcd = (p.nwg % 8 == 0) ? 1 : 0;
     p.alpha = (float)((double)g.scale * 1.4426950408889634);
-    auto kern = ring_kernel<D, R, QT>;
+    auto kern = ring_kernel<D, R, QT, W>;
     if (p.lds_bytes > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)p.nwg), dim3(kRingThreads), p.lds_bytes, st,
+    hipLaunchKernelGGL(kern, dim3((unsigned)p.nwg), dim3(64 * W), p.lds_bytes, st,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
                        (const __bf16*)rh, (const __bf16*)rw, (__bf16*)out, g, p);
     return hipGetLastError();
+}
+
+template <int D, int R, int QT>
+static hipError_t ring_launch_w(const void* q, const void* k, const void* v, const void* rh,
+                                const void* rw, void* out, const Geometry& g, hipStream_t st)
+{
+    const int w = ring_waves(g, QT);
+    if (w == 4) return ring_launch_t<D, R, QT, 4>(q, k, v, rh, rw, out, g, st);
+    if (w == 8) return ring_launch_t<D, R, QT, 8>(q, k, v, rh, rw, out, g, st);
+    return hipErrorInvalidConfiguration;
 }
 
 template <int D, int R>
 static hipError_t ring_launch_r(const void* q, const void* k, const void* v, const void* rh,
                                 const void* rw, void* out, const Geometry& g, hipStream_t st)
 {
-    if (ring_qt(g) > 1) return ring_launch_t<D, R, HALO_RING_QT>(q, k, v, rh, rw, out, g, st);
-    return ring_launch_t<D, R, 1>(q, k, v, rh, rw, out, g, st);
+    if (ring_qt(g) > 1) return ring_launch_w<D, R, HALO_RING_QT>(q, k, v, rh, rw, out, g, st);
+    return ring_launch_w<D, R, 1>(q, k, v, rh, rw, out, g, st);
 }
 
 // Window sides with a compiled ring kernel.
@@ -647,7 +713,7 @@ bool ring_supported(const Geometry& g)
 {
     if (!ring_side(g.r) || (g.d != 16 && g.d != 32) || g.block % 4 != 0) return false;
     if ((int64_t)g.H * g.W >= (int64_t(1) << 31)) return false;   // pixel indices are 32-bit
-    return ring_choose(g, ring_qt(g)).nbx != 0;
+    return ring_waves(g, ring_qt(g)) != 0;
 }
 
 hipError_t launch_ring(const void* q, const void* k, const void* v, const void* rh,

@@ -53,17 +53,39 @@ __device__ inline void wave_lds_sync()
 }
 
 // Reductions over the four lanes n, n+16, n+32, n+48 (the lanes holding one
-// query in the 16x16 MFMA layouts).  The gfx950 row-swap builtins are not
-// used: this compiler folds their second result into the first.
+// query in the 16x16 MFMA layouts), on the gfx950 cross-row swaps (VALU, no
+// LDS traffic).  v_permlane16_swap exchanges the odd 16-lane rows of its
+// first operand with the even rows of its second, v_permlane32_swap the upper
+// 32 lanes of the first with the lower 32 of the second; fed two copies of one
+// value they return both halves of every row pair / wave half.  Written as
+// inline asm because this compiler folds the second result of the
+// corresponding builtins into the first.  The s_nop gives the two wait states
+// a VALU write needs before a permlane reads it.
+__device__ inline void swap16(float& a, float& b)
+{
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ inline void swap32(float& a, float& b)
+{
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
 __device__ inline float max_over_rows(float x)
 {
-    x = fmaxf(x, __shfl_xor(x, 16));
-    return fmaxf(x, __shfl_xor(x, 32));
+    float a = x, b = x;
+    swap16(a, b);
+    a = fmaxf(a, b);
+    b = a;
+    swap32(a, b);
+    return fmaxf(a, b);
 }
 __device__ inline float sum_over_rows(float x)
 {
-    x += __shfl_xor(x, 16);
-    return x + __shfl_xor(x, 32);
+    float a = x, b = x;
+    swap16(a, b);
+    a = a + b;
+    b = a;
+    swap32(a, b);
+    return a + b;
 }
 
 __device__ inline float max4(f32x4 s)
