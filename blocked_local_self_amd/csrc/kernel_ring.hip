@@ -10,14 +10,15 @@
 //
 // Work decomposition (MI355X-first):
 //  * one workgroup owns one (batch, head) image strip of `nbx` adjacent block
-//    columns and walks down its block rows.  The R rows of the current window
-//    live in an LDS ring.  The vertical halo overlap is reused in LDS as well
-//    as the horizontal one, so every K/V pixel of the strip is read from HBM
-//    once; the `block` rows the next window adds (and the next query
-//    fragments) are fetched into registers while the current block row
-//    computes, then replace the rows the next window drops: a barrier before
-//    and one after that store.  Rows above or below the image are kept as
-//    zero rows, so every block row runs the same code.
+//    columns and walks down its block rows.  Window rows live in an LDS ring
+//    of R + block rows: the R rows of the current window plus the `block`
+//    rows the next window adds.  The vertical halo overlap is reused in LDS as
+//    well as the horizontal one, so every K/V pixel of the strip is read from
+//    HBM once; the next rows (and the next query fragments) are fetched into
+//    registers at the start of a block row and written to the ring once the
+//    wave's first group is computed: one barrier per block row.  Rows above
+//    or below the image are kept as zero rows, so every block row runs the
+//    same code.
 //  * workgroups of 4 or 8 waves: with 4, two workgroups share a CU and one's
 //    barrier waits overlap the other's compute; the strip width is the widest
 //    whose ring fits the LDS share.
@@ -56,7 +57,7 @@ namespace halo {
 #define HALO_RING_FORCE_WAVES 0   // 4 or 8 to override the per-shape choice
 #endif
 #ifndef HALO_RING_MAXI
-#define HALO_RING_MAXI 2      // query groups per wave per block row with prefetched Q
+#define HALO_RING_MAXI 2      // query groups per wave per block row (the plan keeps within it)
 #endif
 constexpr int kLdsPerCU = 160 * 1024;   // gfx950
 constexpr int kRingMaxI = HALO_RING_MAXI;
@@ -307,8 +308,23 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                  __builtin_amdgcn_exp2f(fmaf(s[3], alpha, c)))};
     };
 
+    // Output of one group: lane (n, g) holds channels 16*mt + 4g + i of
+    // query n of tile u, packed bf16.
+    struct Result {
+        u32x2 w[QT][D / 16];
+    };
+    auto store_result = [&](const Tile& T, const Result& res) {
+#pragma unroll
+        for (int u = 0; u < QT; ++u) {
+            if (!T.qvalid[u]) continue;
+            __bf16* op = out + bh * (int64_t)g.Ho * g.Wo * D + (int64_t)T.opix[u] * D + gq * 4;
+#pragma unroll
+            for (int mt = 0; mt < D / 16; ++mt) *reinterpret_cast<u32x2*>(op + mt * 16) = res.w[u][mt];
+        }
+    };
+
     // One group of QT query tiles of block row byy.
-    auto do_item = [&](int byy, const Tile& T, const FragT (&qf)[QT]) {
+    auto do_item = [&](int byy, const Tile& T, const FragT (&qf)[QT], Result& res) {
         const int yb = byy * g.block;
         const int wy0 = yb - g.halo;
         const int tlo = max(0, -wy0), thi = min(R, g.H - wy0);
@@ -503,18 +519,14 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             weighted_sum();
         }
 
-        // ---- normalise and store: lane (n, g) holds channels 16*mt + 4g + i of query n
+        // ---- normalise and pack
 #pragma unroll
         for (int u = 0; u < QT; ++u) {
-            if (!T.qvalid[u]) continue;
             const float inv = __builtin_amdgcn_rcpf(L[u][0]);
-            __bf16* op = out + bh * (int64_t)g.Ho * g.Wo * D + (int64_t)T.opix[u] * D + gq * 4;
 #pragma unroll
-            for (int mt = 0; mt < D / 16; ++mt) {
-                const u32x2 w = {pack_bf16x2(O[u][mt][0] * inv, O[u][mt][1] * inv),
-                                 pack_bf16x2(O[u][mt][2] * inv, O[u][mt][3] * inv)};
-                *reinterpret_cast<u32x2*>(op + mt * 16) = w;
-            }
+            for (int mt = 0; mt < D / 16; ++mt)
+                res.w[u][mt] = u32x2{pack_bf16x2(O[u][mt][0] * inv, O[u][mt][1] * inv),
+                                     pack_bf16x2(O[u][mt][2] * inv, O[u][mt][3] * inv)};
         }
     };
 
@@ -538,29 +550,21 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         FragT qnext[kRingMaxI][QT];
         load_q(by + 1, qnext);
 
-        // ---- compute this block row
+        // ---- compute this block row.  The next window's new rows go into
+        // ring slots the current window does not use, so they are written as
+        // soon as the first group is computed: the wait for the prefetch then
+        // precedes every output store of the block row (one counter covers
+        // vector loads and stores, so a later wait would also wait for the
+        // stores to be acknowledged).
         const int f = first_item(by);
-#pragma unroll
-        for (int ii = 0; ii < kRingMaxI; ++ii) {
-            const int it = f + ii * kRingWaves;
-            if (it < items) do_item(by, tile_of(by, it), qcur[ii]);
+        const int it0 = f;
+        Result r0;
+        Tile T0;
+        if (it0 < items) {
+            T0 = tile_of(by, it0);
+            do_item(by, T0, qcur[0], r0);
         }
-        for (int it = f + kRingMaxI * kRingWaves; it < items; it += kRingWaves) {
-            const Tile T = tile_of(by, it);
-            FragT qf[QT];
-#pragma unroll
-            for (int u = 0; u < QT; ++u)
-                qf[u] = *reinterpret_cast<const FragT*>(q + qbase + (int64_t)T.qpix[u] * D + gq * KPL);
-            do_item(by, T, qf);
-        }
-#pragma unroll
-        for (int ii = 0; ii < kRingMaxI; ++ii)
-#pragma unroll
-            for (int u = 0; u < QT; ++u) qcur[ii][u] = qnext[ii][u];
-
-        // ---- once every wave is done with this window, the next window's new
-        // rows replace its first `block` rows in the ring
-        __syncthreads();
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the prefetch and the next queries
         if (have) store_item(my_item, nlo, pk, pv, kmax_next);
         for (int e = tid + kRingThreads; e < ntotal; e += kRingThreads) {
             u32x4 kk[4], vv[4];
@@ -568,6 +572,22 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             load_item(it, nlo, kk, vv);
             store_item(it, nlo, kk, vv, kmax_next);
         }
+        if (it0 < items) store_result(T0, r0);
+#pragma unroll
+        for (int ii = 1; ii < kRingMaxI; ++ii) {
+            const int it = f + ii * kRingWaves;
+            if (it < items) {
+                const Tile T = tile_of(by, it);
+                Result r;
+                do_item(by, T, qcur[ii], r);
+                store_result(T, r);
+            }
+        }
+#pragma unroll
+        for (int ii = 0; ii < kRingMaxI; ++ii)
+#pragma unroll
+            for (int u = 0; u < QT; ++u) qcur[ii][u] = qnext[ii][u];
+
         __syncthreads();
     }
 }
@@ -580,7 +600,7 @@ static RingPlan ring_plan(const Geometry& g, int R, int qt, int waves, int nbx)
     p.nbx = nbx;
     p.nstrips = (g.nbw + nbx - 1) / nbx;
     p.SWv = rup(std::max(nbx * g.block + 2 * g.halo, (nbx - 1) * g.block + 16), 4);
-    p.ring = R;
+    p.ring = R + g.block;
     // V^T channel pitch: at least ring*SWv elements, and (pitch/2) = 4 (mod 64)
     // dwords so the 16 channels of a fragment read land in distinct banks
     p.CP = p.ring * p.SWv;
@@ -625,7 +645,10 @@ static int device_cus()
 static RingPlan ring_choose(const Geometry& g, int qt, int waves, int min_strips = 1)
 {
     const int limit = ring_lds_limit(waves);
-    for (int nbx = (g.nbw + min_strips - 1) / min_strips; nbx >= 1; --nbx) {
+    const int side = (g.block + g.stride - 1) / g.stride;
+    const int groups = ((side * side + 15) / 16 + qt - 1) / qt;
+    const int nbx_items = kRingMaxI * waves / groups;   // every wave: <= kRingMaxI groups per block row
+    for (int nbx = std::min((g.nbw + min_strips - 1) / min_strips, nbx_items); nbx >= 1; --nbx) {
         if (ring_plan(g, g.r, qt, waves, nbx).lds_bytes > limit) continue;
         // as few strips as fit, then equal widths (no narrow remainder strip)
         const int nstrips = (g.nbw + nbx - 1) / nbx;
