@@ -1,4 +1,4 @@
-// Persistent fused halo-attention kernel for windows of at most 16 columns
+// Persistent fused halo-attention kernel for windows of at most 32 columns
 // (gfx950 matrix cores, bf16 in, fp32 accumulate).
 //
 // Method: "Scaling Local Self-Attention for Parameter Efficient Visual
@@ -27,10 +27,11 @@
 //    bits; V is transposed to [d][slot][col] with the channel pitch padded to
 //    4 (mod 64) dwords; the relative-logit scratch has a 20-float row stride.
 //  * a wave takes QT tiles of 16 queries of one block at a time.  Scores are
-//    computed transposed, S^T = K . Q^T, one 16x16 tile per window row (16
-//    window columns); lane (n, g) holds query n and columns 4g..4g+3, so the
-//    width term q.rel_w[col] is the MFMA accumulator input (masked columns
-//    -1e30) and the height term q.rel_h[row] is one register per (lane, row).
+//    computed transposed, S^T = K . Q^T, one 16x16 tile per window row and
+//    16-column tile (NCT = 1 or 2 of them); lane (n, g) holds query n and
+//    columns 4g..4g+3 of the tile, so the width term q.rel_w[col] is the MFMA
+//    accumulator input (masked columns -1e30) and the height term
+//    q.rel_h[row] is one scalar per (lane, row).
 //  * both passes loop over the in-image window rows only; the height term of
 //    a row is read from the conflict-free scratch.
 //  * the softmax is shifted by a per-query upper bound on its logits
@@ -62,8 +63,13 @@ namespace halo {
 constexpr int kLdsPerCU = 160 * 1024;   // gfx950
 constexpr int kRingMaxI = HALO_RING_MAXI;
 constexpr int kScrStride = 20;        // floats per scratch row (conflict-free writes)
-constexpr int kRelTiles = 2;          // relative tables padded to 32 rows: 2R-1 <= 31 and
-constexpr int kRelRows = 16 * kRelTiles;   // R-1+15 <= 30 for every R <= 16
+
+// Relative-table rows (padded, multiple of 16) for windows of up to 16*nct
+// columns: 2R-1 <= 32*nct - 1 and R-1+16*nct-1 < 32*nct.
+constexpr int rel_rows(int nct) { return 32 * nct; }
+// Rows of a query tile's scratch: the table-indexed layout (one column tile)
+// or the window-indexed layout with a clamp row at each end (two).
+constexpr int scr_rows(int nct) { return nct == 1 ? rel_rows(1) : 16 * nct + 2; }
 
 struct RingPlan {
     int nstrips;     // column strips per image
@@ -98,14 +104,18 @@ __device__ inline unsigned k_chunk(int c, int col)
     return (unsigned)((c ^ ((col >> 2) & 3)) * 16);
 }
 
-template <int D, int R, int QT, int W>
+template <int D, int NCT, int QT, int W>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2)))
 void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                  const __bf16* __restrict__ v, const __bf16* __restrict__ rel_h,
                  const __bf16* __restrict__ rel_w, __bf16* __restrict__ out,
                  Geometry g, RingPlan p)
 {
-    static_assert(R <= 16, "one 16-column tile per window row");
+    static_assert(NCT == 1 || NCT == 2, "windows of up to 32 columns");
+    const int R = g.r;                         // window side, <= 16 * NCT
+    constexpr int kRelTiles = 2 * NCT;
+    constexpr int kRelRows = rel_rows(NCT);
+    constexpr int kScrRows = scr_rows(NCT);
     constexpr int kRingWaves = W;
     constexpr int kRingThreads = 64 * W;
     constexpr int KPL = D / 4;                 // channels per lane in a QK fragment
@@ -121,9 +131,8 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, gq = lane >> 4;
-    constexpr unsigned scr_u = (unsigned)kRelRows * kScrStride * 4;   // bytes per query tile
-    const unsigned scr0 = p.off_scr + wave * QT * scr_u;
-    const unsigned scr_lane = scr0 + 4u * (4 * gq * kScrStride + n);   // row 4g, column n
+    constexpr unsigned scr_u = (unsigned)kScrRows * kScrStride * 4;   // bytes per query tile
+    const unsigned scr0 = p.off_scr + wave * QT * scr_u + 4u * n;     // column n of tile 0
 
     int64_t wg = blockIdx.x;
     if (p.remap_xcd) {
@@ -231,12 +240,19 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
     __syncthreads();
 
-    // relative tables as MFMA A operands, kept in registers
-    FragT tabw[kRelTiles], tabh[kRelTiles];
+    // relative tables as MFMA A operands: kept in registers for one column
+    // tile, read from LDS per use for two (register pressure)
+    constexpr int kTabRegs = NCT == 1 ? kRelTiles : 1;
+    FragT tabw[kTabRegs], tabh[kTabRegs];
+    auto tab_frag = [&](unsigned off, int rt) {
+        return lds_ld<FragT>(smem, off + 2u * ((rt * 16 + n) * D + gq * KPL));
+    };
+    if constexpr (NCT == 1) {
 #pragma unroll
-    for (int rt = 0; rt < kRelTiles; ++rt) {
-        tabw[rt] = lds_ld<FragT>(smem, offrw + 2u * ((rt * 16 + n) * D + gq * KPL));
-        tabh[rt] = lds_ld<FragT>(smem, offrh + 2u * ((rt * 16 + n) * D + gq * KPL));
+        for (int rt = 0; rt < kRelTiles; ++rt) {
+            tabw[rt] = tab_frag(offrw, rt);
+            tabh[rt] = tab_frag(offrh, rt);
+        }
     }
 
     const float alpha = p.alpha;
@@ -330,40 +346,54 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         const int tlo = max(0, -wy0), thi = min(R, g.H - wy0);
         const int base = yb % ring;                   // ring slot of window row 0
 
-        // ---- relative logits: G = table . Q^T on MFMA (both tables at once,
-        // operands in registers), re-indexed per query through the scratch.
-        // Scratch row j, column n holds G[j][n].  All scratch traffic below
-        // is this wave's own, and LDS executes one wave's accesses in program
-        // order, so no waits are needed between the stores and the loads.
+        // ---- relative logits: G = table . Q^T on MFMA (both tables), then
+        // re-indexed per query through the scratch (column n of tile u).  One
+        // column tile: scratch row = table row, read at row R-1-xl+c.  Two:
+        // scratch row = window column / row + 1, written with a clamp to the
+        // end rows for table rows no window position uses.  All scratch
+        // traffic is this wave's own, and LDS executes one wave's accesses in
+        // program order, so no waits are needed between stores and loads.
         f32x4 gw[QT][kRelTiles], gh[QT][kRelTiles];
 #pragma unroll
         for (int u = 0; u < QT; ++u)
 #pragma unroll
             for (int rt = 0; rt < kRelTiles; ++rt) {
-                gw[u][rt] = Frag<D>::mma(tabw[rt], qf[u], f32x4{0.f, 0.f, 0.f, 0.f});
-                gh[u][rt] = Frag<D>::mma(tabh[rt], qf[u], f32x4{0.f, 0.f, 0.f, 0.f});
+                const FragT aw = NCT == 1 ? tabw[rt] : tab_frag(offrw, rt);
+                const FragT ah = NCT == 1 ? tabh[rt] : tab_frag(offrh, rt);
+                gw[u][rt] = Frag<D>::mma(aw, qf[u], f32x4{0.f, 0.f, 0.f, 0.f});
+                gh[u][rt] = Frag<D>::mma(ah, qf[u], f32x4{0.f, 0.f, 0.f, 0.f});
             }
-        // width products -> scratch
+        // scratch row receiving table row j for a query whose window position
+        // 0 sits at table row s0
+        auto wrow = [&](int j, int s0) {
+            if constexpr (NCT == 1) return j;
+            else return min(max(j - s0 + 1, 0), kScrRows - 1);
+        };
 #pragma unroll
-        for (int u = 0; u < QT; ++u)
+        for (int u = 0; u < QT; ++u) {
+            const int sw = R - 1 - T.xl[u];
 #pragma unroll
             for (int rt = 0; rt < kRelTiles; ++rt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    lds_st<float>(smem, scr_lane + u * scr_u + 4u * (rt * 16 + i) * kScrStride, gw[u][rt][i]);
-        // width term of window column c = 4g + i for query n: table row
-        // R-1-xl+c (masked: off-image, c >= R)
+                    lds_st<float>(smem, scr0 + u * scr_u + 4u * kScrStride * wrow(rt * 16 + 4 * gq + i, sw),
+                                  gw[u][rt][i]);
+        }
+        // width term of window column c = 16ct + 4g + i (masked: off-image, c >= R)
         const int clo = g.halo - T.xb, chi = min(R, g.W - T.xb + g.halo);
-        f32x4 cinit[QT];
+        f32x4 cinit[QT][NCT];
 #pragma unroll
         for (int u = 0; u < QT; ++u) {
-            const unsigned a = scr0 + u * scr_u + 4u * ((R - 1 - T.xl[u] + 4 * gq) * kScrStride + n);
+            const int r0 = NCT == 1 ? R - 1 - T.xl[u] : 1;    // scratch row of column 0
+            const unsigned a = scr0 + u * scr_u + 4u * kScrStride * (r0 + 4 * gq);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int c = 4 * gq + i;
-                const float val = lds_ld<float>(smem, a + 4u * i * kScrStride);
-                cinit[u][i] = (c >= clo && c < chi) ? val : kMaskLogit;
-            }
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int c = 16 * ct + 4 * gq + i;
+                    const float val = lds_ld<float>(smem, a + 4u * kScrStride * (16 * ct + i));
+                    cinit[u][ct][i] = (c >= clo && c < chi) ? val : kMaskLogit;
+                }
         }
 
         // ---- softmax shift: an upper bound on every logit of the query,
@@ -385,32 +415,35 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 const float x = __builtin_bit_cast(float, (unsigned)(unsigned short)qf[u][e] << 16);
                 qq = fmaf(x, x, qq);
             }
-            float hm = max4(gh[u][0]);
+            float hm = max4(gh[u][0]), wm = max4(cinit[u][0]);
 #pragma unroll
             for (int rt = 1; rt < kRelTiles; ++rt) hm = fmaxf(hm, max4(gh[u][rt]));
+#pragma unroll
+            for (int ct = 1; ct < NCT; ++ct) wm = fmaxf(wm, max4(cinit[u][ct]));
             qq = sum_over_rows(qq);
-            const float rw = max_over_rows(max4(cinit[u]));
+            const float rw = max_over_rows(wm);
             hm = max_over_rows(hm);
             const float bound = __builtin_sqrtf(qq * kmax2) + rw + hm;
             mb[u] = alpha * (bound + 1e-3f * (1.f + fabsf(bound)));
         }
         // height products, already in shifted base-2 units alpha*G - mb,
         // -> scratch (after the width reads above, in program order)
+        unsigned rh0[QT];                             // scratch byte offset of window row 0
 #pragma unroll
-        for (int u = 0; u < QT; ++u)
+        for (int u = 0; u < QT; ++u) {
+            const int sh = R - 1 - T.yl[u];
 #pragma unroll
             for (int rt = 0; rt < kRelTiles; ++rt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    lds_st<float>(smem, scr_lane + u * scr_u + 4u * (rt * 16 + i) * kScrStride,
+                    lds_st<float>(smem, scr0 + u * scr_u + 4u * kScrStride * wrow(rt * 16 + 4 * gq + i, sh),
                                   fmaf(gh[u][rt][i], alpha, -mb[u]));
-        // scratch byte offset of the height term of window row 0, per tile
-        unsigned rh0[QT];
-#pragma unroll
-        for (int u = 0; u < QT; ++u) rh0[u] = scr0 + u * scr_u + 4u * ((R - 1 - T.yl[u]) * kScrStride + n);
+            rh0[u] = scr0 + u * scr_u + 4u * kScrStride * (NCT == 1 ? sh : 1);
+        }
         auto rhv = [&](int u, int t) { return lds_ld<float>(smem, rh0[u] + 4u * kScrStride * t); };
 
         // lane-constant LDS byte offsets of this lane's K and V^T fragments
+        // (column tile ct adds 16 columns; the K swizzle repeats every 16)
         const int kcol = T.wcol0 + n;
         const unsigned kl = (unsigned)kcol * PIXB + (D == 16 ? k_chunk<D>(gq >> 1, kcol) + (gq & 1) * 8
                                                              : k_chunk<D>(gq, kcol));
@@ -419,15 +452,19 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             const int s2 = base + t;
             return (unsigned)(s2 >= ring ? s2 - ring : s2);
         };
-        auto kload = [&](int t) -> FragT { return lds_ld<FragT>(smem, kl + rslot(t) * rowb_k); };
-        auto vload = [&](int mt, int t) -> u32x2 {
-            return lds_ld<u32x2>(smem, vl + 2u * ((unsigned)(mt * 16 * CP) + rslot(t) * SWv));
+        auto kload = [&](int t, int ct) -> FragT {
+            return lds_ld<FragT>(smem, kl + ct * 16 * PIXB + rslot(t) * rowb_k);
+        };
+        auto vload = [&](int mt, int t, int ct) -> u32x2 {
+            return lds_ld<u32x2>(smem, vl + 2u * ((unsigned)(mt * 16 * CP) + rslot(t) * SWv + 16 * ct));
         };
 
         // ---- weighted sum: P = exp2(alpha*S + (alpha*rh - mb)) in bf16;
-        // O^T += V^T . P^T and L += 1 . P^T, one K=32 step per pair of rows (a
-        // missing second row of the last pair has zero weights).  Operands of
-        // the next pair are loaded one step ahead (clamped to the last row).
+        // O^T += V^T . P^T and L += 1 . P^T, one K=32 step per two score
+        // tiles: rows t and t+1 (one column tile; a missing second row has
+        // zero weights) or both column tiles of row t.  Operands of the next
+        // step are loaded one step ahead (clamped to the last row).
+        constexpr int STEP = NCT == 1 ? 2 : 1;
         f32x4 O[QT][D / 16], L[QT];
         struct Ops {
             FragT a0, a1;
@@ -436,18 +473,19 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         };
         auto fetch = [&](int t0) {
             Ops o;
-            const int t1 = min(t0 + 1, thi - 1);
-            o.a0 = kload(t0);
-            o.a1 = kload(t1);
+            const int t1 = NCT == 1 ? min(t0 + 1, thi - 1) : t0;
+            const int c1 = NCT == 1 ? 0 : 1;
+            o.a0 = kload(t0, 0);
+            o.a1 = kload(t1, c1);
 #pragma unroll
             for (int mt = 0; mt < D / 16; ++mt) {
-                const u32x2 x0 = vload(mt, t0), x1 = vload(mt, t1);
+                const u32x2 x0 = vload(mt, t0, 0), x1 = vload(mt, t1, c1);
                 o.vw[mt] = u32x4{x0[0], x0[1], x1[0], x1[1]};
             }
 #pragma unroll
             for (int u = 0; u < QT; ++u) {
                 o.c0[u] = rhv(u, t0);
-                o.c1[u] = rhv(u, t1);
+                o.c1[u] = NCT == 1 ? rhv(u, t1) : o.c0[u];
             }
             return o;
         };
@@ -458,15 +496,15 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
                 for (int mt = 0; mt < D / 16; ++mt) O[u][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
-            // double-buffered: the operands of the next pair are issued before
-            // the current pair is computed; scheduling barriers keep the
+            // double-buffered: the operands of the next step are issued before
+            // the current step is computed; scheduling barriers keep the
             // compiler from sinking those loads back to their uses
             auto compute = [&](const Ops& c, int t) {
-                const bool two = t + 1 < thi;              // uniform
+                const bool two = NCT == 2 || t + 1 < thi;   // uniform
 #pragma unroll
                 for (int u = 0; u < QT; ++u) {
-                    const u32x2 p0 = probs(Frag<D>::mma(c.a0, qf[u], cinit[u]), c.c0[u]);
-                    const u32x2 p1 = probs(Frag<D>::mma(c.a1, qf[u], cinit[u]), two ? c.c1[u] : -3.0e38f);
+                    const u32x2 p0 = probs(Frag<D>::mma(c.a0, qf[u], cinit[u][0]), c.c0[u]);
+                    const u32x2 p1 = probs(Frag<D>::mma(c.a1, qf[u], cinit[u][NCT - 1]), two ? c.c1[u] : -3.0e38f);
                     const s16x8 pf = __builtin_bit_cast(s16x8, u32x4{p0[0], p0[1], p1[0], p1[1]});
 #pragma unroll
                     for (int mt = 0; mt < D / 16; ++mt)
@@ -476,17 +514,17 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             };
             Ops A = fetch(tlo), B;
             for (int t = tlo;;) {
-                B = fetch(min(t + 2, thi - 1));
+                B = fetch(min(t + STEP, thi - 1));
                 __builtin_amdgcn_sched_barrier(0);
                 compute(A, t);
                 __builtin_amdgcn_sched_barrier(0);
-                t += 2;
+                t += STEP;
                 if (t >= thi) break;
-                A = fetch(min(t + 2, thi - 1));
+                A = fetch(min(t + STEP, thi - 1));
                 __builtin_amdgcn_sched_barrier(0);
                 compute(B, t);
                 __builtin_amdgcn_sched_barrier(0);
-                t += 2;
+                t += STEP;
                 if (t >= thi) break;
             }
         };
@@ -501,20 +539,24 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             float M[QT];
 #pragma unroll
             for (int u = 0; u < QT; ++u) M[u] = -3.0e38f;
-            for (int t = tlo; t < thi; ++t) {
-                const FragT a = kload(t);
+            for (int t = tlo; t < thi; ++t)
 #pragma unroll
-                for (int u = 0; u < QT; ++u)
-                    M[u] = fmaxf(M[u], fmaf(max4(Frag<D>::mma(a, qf[u], cinit[u])), alpha, rhv(u, t)));
-            }
+                for (int ct = 0; ct < NCT; ++ct) {
+                    const FragT a = kload(t, ct);
+#pragma unroll
+                    for (int u = 0; u < QT; ++u)
+                        M[u] = fmaxf(M[u], fmaf(max4(Frag<D>::mma(a, qf[u], cinit[u][ct])), alpha, rhv(u, t)));
+                }
 #pragma unroll
             for (int u = 0; u < QT; ++u) {
                 const float m = max_over_rows(M[u]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {          // window rows 4g..4g+3 of query n
-                    const unsigned a = rh0[u] + 4u * kScrStride * (4 * gq + i);
-                    lds_st<float>(smem, a, lds_ld<float>(smem, a) - m);
-                }
+                for (int k2 = 0; k2 < NCT; ++k2)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {      // window rows 16k + 4g + i of query n
+                        const unsigned a = rh0[u] + 4u * kScrStride * (16 * k2 + 4 * gq + i);
+                        lds_st<float>(smem, a, lds_ld<float>(smem, a) - m);
+                    }
             }
             weighted_sum();
         }
@@ -594,13 +636,15 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 
 static int rup(int x, int m) { return (x + m - 1) / m * m; }
 
-static RingPlan ring_plan(const Geometry& g, int R, int qt, int waves, int nbx)
+static int ring_nct(const Geometry& g) { return (g.r + 15) / 16; }
+
+static RingPlan ring_plan(const Geometry& g, int nct, int qt, int waves, int nbx)
 {
     RingPlan p{};
     p.nbx = nbx;
     p.nstrips = (g.nbw + nbx - 1) / nbx;
-    p.SWv = rup(std::max(nbx * g.block + 2 * g.halo, (nbx - 1) * g.block + 16), 4);
-    p.ring = R + g.block;
+    p.SWv = rup(std::max(nbx * g.block + 2 * g.halo, (nbx - 1) * g.block + 16 * nct), 4);
+    p.ring = g.r + g.block;
     // V^T channel pitch: at least ring*SWv elements, and (pitch/2) = 4 (mod 64)
     // dwords so the 16 channels of a fragment read land in distinct banks
     p.CP = p.ring * p.SWv;
@@ -609,14 +653,13 @@ static RingPlan ring_plan(const Geometry& g, int R, int qt, int waves, int nbx)
     p.groups = ((side * side + 15) / 16 + qt - 1) / qt;
     const int kb = p.ring * p.SWv * g.d * 2;
     const int vb = g.d * p.CP * 2;
-    const int rb = 2 * kRelRows * g.d * 2;
-    const int sb = waves * qt * kRelRows * kScrStride * 4;
+    const int rb = 2 * rel_rows(nct) * g.d * 2;
+    const int sb = waves * qt * scr_rows(nct) * kScrStride * 4;
     p.off_v = rup(kb, 16);
     p.off_rel = rup(p.off_v + vb, 16);
     p.off_scr = rup(p.off_rel + rb, 16);
     p.off_kn = rup(p.off_scr + sb, 16);
     p.lds_bytes = p.off_kn + 2 * 16 * 4;                    // running key-chunk norm maxima, 2 sets
-
     return p;
 }
 
@@ -640,19 +683,20 @@ static int device_cus()
     return cus;
 }
 
-// Widest plan that fits in LDS with at least `min_strips` strips per image,
-// or nbx = 0 when even one block column does not fit.
-static RingPlan ring_choose(const Geometry& g, int qt, int waves, int min_strips = 1)
+// Widest plan that fits in LDS with at least `min_strips` strips per image
+// and at most kRingMaxI groups per wave per block row, or nbx = 0 when even
+// one block column does not fit.
+static RingPlan ring_choose(const Geometry& g, int nct, int qt, int waves, int min_strips = 1)
 {
     const int limit = ring_lds_limit(waves);
     const int side = (g.block + g.stride - 1) / g.stride;
     const int groups = ((side * side + 15) / 16 + qt - 1) / qt;
-    const int nbx_items = kRingMaxI * waves / groups;   // every wave: <= kRingMaxI groups per block row
+    const int nbx_items = kRingMaxI * waves / groups;
     for (int nbx = std::min((g.nbw + min_strips - 1) / min_strips, nbx_items); nbx >= 1; --nbx) {
-        if (ring_plan(g, g.r, qt, waves, nbx).lds_bytes > limit) continue;
+        if (ring_plan(g, nct, qt, waves, nbx).lds_bytes > limit) continue;
         // as few strips as fit, then equal widths (no narrow remainder strip)
         const int nstrips = (g.nbw + nbx - 1) / nbx;
-        return ring_plan(g, g.r, qt, waves, (g.nbw + nstrips - 1) / nstrips);
+        return ring_plan(g, nct, qt, waves, (g.nbw + nstrips - 1) / nstrips);
     }
     return RingPlan{};
 }
@@ -669,13 +713,13 @@ static int ring_min_strips4(const Geometry& g)
 // with the other's compute, at the price of narrower strips (more halo
 // columns staged per useful column).  Take them when the launch has enough
 // workgroups to fill both slots of every CU and the price is low.
-static int ring_waves(const Geometry& g, int qt)
+static int ring_waves(const Geometry& g, int nct, int qt)
 {
     if (HALO_RING_FORCE_WAVES == 4)
-        return ring_choose(g, qt, 4, ring_min_strips4(g)).nbx ? 4 : 0;
+        return ring_choose(g, nct, qt, 4, ring_min_strips4(g)).nbx ? 4 : 0;
     if (HALO_RING_FORCE_WAVES == 8)
-        return ring_choose(g, qt, 8).nbx ? 8 : 0;
-    const RingPlan p4 = ring_choose(g, qt, 4, ring_min_strips4(g)), p8 = ring_choose(g, qt, 8);
+        return ring_choose(g, nct, qt, 8).nbx ? 8 : 0;
+    const RingPlan p4 = ring_choose(g, nct, qt, 4, ring_min_strips4(g)), p8 = ring_choose(g, nct, qt, 8);
     if (p8.nbx == 0) return p4.nbx ? 4 : 0;
     if (p4.nbx == 0 || g.BH * p4.nstrips < 2 * (int64_t)device_cus()) return 8;
     const double cost4 = (double)p4.SWv / (p4.nbx * g.block);
@@ -683,23 +727,25 @@ static int ring_waves(const Geometry& g, int qt)
     return cost4 <= 1.15 * cost8 ? 4 : 8;
 }
 
+// Query tiles per group: two when the block's tiles pair up and a window
+// row is one column tile, else one (register pressure).
 static int ring_qt(const Geometry& g)
 {
     const int side = (g.block + g.stride - 1) / g.stride;
     const int tiles = (side * side + 15) / 16;
-    return (HALO_RING_QT > 1 && tiles % HALO_RING_QT == 0) ? HALO_RING_QT : 1;
+    return (HALO_RING_QT > 1 && ring_nct(g) == 1 && tiles % HALO_RING_QT == 0) ? HALO_RING_QT : 1;
 }
 
-template <int D, int R, int QT, int W>
+template <int D, int NCT, int QT, int W>
 static hipError_t ring_launch_t(const void* q, const void* k, const void* v, const void* rh,
                                 const void* rw, void* out, const Geometry& g, hipStream_t st)
 {
-    RingPlan p = W == 4 ? ring_choose(g, QT, 4, ring_min_strips4(g)) : ring_choose(g, QT, 8);
+    RingPlan p = W == 4 ? ring_choose(g, NCT, QT, 4, ring_min_strips4(g)) : ring_choose(g, NCT, QT, 8);
     if (p.nbx == 0) return hipErrorInvalidConfiguration;
     p.nwg = g.BH * p.nstrips;
     p.remap_xcd = (p.nwg % 8 == 0) ? 1 : 0;
     p.alpha = (float)((double)g.scale * 1.4426950408889634);
-    auto kern = ring_kernel<D, R, QT, W>;
+    auto kern = ring_kernel<D, NCT, QT, W>;
     if (p.lds_bytes > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
@@ -711,50 +757,37 @@ static hipError_t ring_launch_t(const void* q, const void* k, const void* v, con
     return hipGetLastError();
 }
 
-template <int D, int R, int QT>
+template <int D, int NCT, int QT>
 static hipError_t ring_launch_w(const void* q, const void* k, const void* v, const void* rh,
                                 const void* rw, void* out, const Geometry& g, hipStream_t st)
 {
-    const int w = ring_waves(g, QT);
-    if (w == 4) return ring_launch_t<D, R, QT, 4>(q, k, v, rh, rw, out, g, st);
-    if (w == 8) return ring_launch_t<D, R, QT, 8>(q, k, v, rh, rw, out, g, st);
+    const int w = ring_waves(g, NCT, QT);
+    if (w == 4) return ring_launch_t<D, NCT, QT, 4>(q, k, v, rh, rw, out, g, st);
+    if (w == 8) return ring_launch_t<D, NCT, QT, 8>(q, k, v, rh, rw, out, g, st);
     return hipErrorInvalidConfiguration;
 }
 
-template <int D, int R>
-static hipError_t ring_launch_r(const void* q, const void* k, const void* v, const void* rh,
+template <int D>
+static hipError_t ring_launch_d(const void* q, const void* k, const void* v, const void* rh,
                                 const void* rw, void* out, const Geometry& g, hipStream_t st)
 {
-    if (ring_qt(g) > 1) return ring_launch_w<D, R, HALO_RING_QT>(q, k, v, rh, rw, out, g, st);
-    return ring_launch_w<D, R, 1>(q, k, v, rh, rw, out, g, st);
+    if (ring_nct(g) == 2) return ring_launch_w<D, 2, 1>(q, k, v, rh, rw, out, g, st);
+    if (ring_qt(g) > 1) return ring_launch_w<D, 1, HALO_RING_QT>(q, k, v, rh, rw, out, g, st);
+    return ring_launch_w<D, 1, 1>(q, k, v, rh, rw, out, g, st);
 }
-
-// Window sides with a compiled ring kernel.
-static bool ring_side(int r) { return r == 8 || r == 10 || r == 12 || r == 14 || r == 16; }
 
 bool ring_supported(const Geometry& g)
 {
-    if (!ring_side(g.r) || (g.d != 16 && g.d != 32) || g.block % 4 != 0) return false;
+    if (g.r > 32 || (g.d != 16 && g.d != 32) || g.block % 4 != 0) return false;
     if ((int64_t)g.H * g.W >= (int64_t(1) << 31)) return false;   // pixel indices are 32-bit
-    return ring_waves(g, ring_qt(g)) != 0;
+    return ring_waves(g, ring_nct(g), ring_qt(g)) != 0;
 }
 
 hipError_t launch_ring(const void* q, const void* k, const void* v, const void* rh,
                        const void* rw, void* out, const Geometry& g, hipStream_t st)
 {
-#define HALO_RING_CASE(RR)                                                            \
-    case RR:                                                                          \
-        return g.d == 16 ? ring_launch_r<16, RR>(q, k, v, rh, rw, out, g, st)         \
-                         : ring_launch_r<32, RR>(q, k, v, rh, rw, out, g, st);
-    switch (g.r) {
-        HALO_RING_CASE(8)
-        HALO_RING_CASE(10)
-        HALO_RING_CASE(12)
-        HALO_RING_CASE(14)
-        HALO_RING_CASE(16)
-    default: return hipErrorInvalidValue;
-    }
-#undef HALO_RING_CASE
+    return g.d == 16 ? ring_launch_d<16>(q, k, v, rh, rw, out, g, st)
+                     : ring_launch_d<32>(q, k, v, rh, rw, out, g, st);
 }
 
 }  // namespace halo

@@ -59,10 +59,10 @@ typedef enum halo_dtype {
  * arguments.  GENERIC is the fp32-vector kernel for every supported shape.
  * MFMA is the fused matrix-core path (bf16, d in {16, 32}, block % 4 == 0,
  * window side r <= 32): a persistent kernel that walks each image down its
- * block rows with the window rows in an LDS ring when r is 8, 10, 12, 14 or 16
- * and the ring fits in LDS, else a kernel that stages each strip of blocks
- * separately.  MFMA_STRIP forces the latter (for cross-checking).  Asking for
- * an MFMA path with other arguments returns HALO_ERR_UNSUPPORTED. */
+ * block rows with the window rows in an LDS ring when the ring fits in LDS,
+ * else a kernel that stages each strip of blocks separately.  MFMA_STRIP
+ * forces the latter (for cross-checking).  Asking for an MFMA path with other
+ * arguments returns HALO_ERR_UNSUPPORTED. */
 typedef enum halo_kernel {
     HALO_KERNEL_AUTO = 0,
     HALO_KERNEL_GENERIC = 1,
