@@ -36,14 +36,14 @@ MALL_BYTES = 256 * 2 ** 20     # Infinity Cache
 # measured on (``sources`` = kernel_source_hash() at the time); otherwise the
 # bench reports traffic as null.
 MEASURED_TRAFFIC = {
-    "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 134580029, "read": 101025597, "write": 33554432,
-                                        "sources": "8578df035a2343e6"},
-    "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 140898433, "read": 103149697, "write": 37748736,
-                                      "sources": "8578df035a2343e6"},
-    "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 92534278, "read": 84145670, "write": 8388608,
-                                       "sources": "8578df035a2343e6"},
-    "large_bf16_128x128_d32_b12h3": {"bytes_per_launch": 268626143, "read": 201517279, "write": 67108864,
-                                     "sources": "8578df035a2343e6"},
+    "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 134535601, "read": 100981169, "write": 33554432,
+                                        "sources": "bdcdc81190e5bc0b"},
+    "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 144211055, "read": 103316591, "write": 40894464,
+                                      "sources": "bdcdc81190e5bc0b"},
+    "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 92508425, "read": 84119817, "write": 8388608,
+                                       "sources": "bdcdc81190e5bc0b"},
+    "large_bf16_128x128_d32_b12h3": {"bytes_per_launch": 273292758, "read": 206183894, "write": 67108864,
+                                     "sources": "bdcdc81190e5bc0b"},
 }
 
 
@@ -61,8 +61,9 @@ def kernel_source_hash() -> str:
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=2000,
+                    help="untimed launches first (the GPU clocks need ~0.1 s of load to ramp up)")
     ap.add_argument("--workload", default=None, help="workload name (default: the early-stage shape)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "generic", "mfma"])
     ap.add_argument("--sets", type=int, default=0, help="rotated input sets (0: enough to exceed the MALL)")
