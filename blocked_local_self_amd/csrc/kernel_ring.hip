@@ -57,11 +57,10 @@ namespace halo {
 #ifndef HALO_RING_FORCE_WAVES
 #define HALO_RING_FORCE_WAVES 0   // 4 or 8 to override the per-shape choice
 #endif
-#ifndef HALO_RING_MAXI
-#define HALO_RING_MAXI 2      // query groups per wave per block row (the plan keeps within it)
-#endif
+
 constexpr int kLdsPerCU = 160 * 1024;   // gfx950
-constexpr int kRingMaxI = HALO_RING_MAXI;
+// Query groups a wave may take per block row (the plan keeps within it).
+constexpr int ring_maxi(int nct) { return nct == 1 ? 2 : 4; }
 constexpr int kScrStride = 20;        // floats per scratch row (conflict-free writes)
 
 // Relative-table rows (padded, multiple of 16) for windows of up to 16*nct
@@ -78,6 +77,7 @@ struct RingPlan {
     int ring;        // LDS ring rows (R + block)
     int CP;          // V^T channel pitch in elements (ring*SWv, padded)
     int groups;      // QT-tile groups per block
+    int midstage;    // ring of R + block rows: next rows staged mid block row
     int off_v, off_rel, off_scr, off_kn, lds_bytes;
     int remap_xcd;
     int64_t nwg;
@@ -117,6 +117,7 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     constexpr int kRelRows = rel_rows(NCT);
     constexpr int kScrRows = scr_rows(NCT);
     constexpr int kRingWaves = W;
+    constexpr int kRingMaxI = ring_maxi(NCT);
     constexpr int kRingThreads = 64 * W;
     constexpr int KPL = D / 4;                 // channels per lane in a QK fragment
     constexpr int CPP = D / 8;                 // 16-byte chunks per pixel
@@ -606,14 +607,17 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             T0 = tile_of(by, it0);
             do_item(by, T0, qcur[0], r0);
         }
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the prefetch and the next queries
-        if (have) store_item(my_item, nlo, pk, pv, kmax_next);
-        for (int e = tid + kRingThreads; e < ntotal; e += kRingThreads) {
-            u32x4 kk[4], vv[4];
-            const Item it = item_of(e);
-            load_item(it, nlo, kk, vv);
-            store_item(it, nlo, kk, vv, kmax_next);
-        }
+        auto stage = [&]() {
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the prefetch and the next queries
+            if (have) store_item(my_item, nlo, pk, pv, kmax_next);
+            for (int e = tid + kRingThreads; e < ntotal; e += kRingThreads) {
+                u32x4 kk[4], vv[4];
+                const Item it = item_of(e);
+                load_item(it, nlo, kk, vv);
+                store_item(it, nlo, kk, vv, kmax_next);
+            }
+        };
+        if (p.midstage) stage();
         if (it0 < items) store_result(T0, r0);
 #pragma unroll
         for (int ii = 1; ii < kRingMaxI; ++ii) {
@@ -630,6 +634,12 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
             for (int u = 0; u < QT; ++u) qcur[ii][u] = qnext[ii][u];
 
+        if (!p.midstage) {
+            // ring of R rows: the new rows replace the ones this window drops
+            // once every wave is done with it
+            __syncthreads();
+            stage();
+        }
         __syncthreads();
     }
 }
@@ -638,13 +648,14 @@ static int rup(int x, int m) { return (x + m - 1) / m * m; }
 
 static int ring_nct(const Geometry& g) { return (g.r + 15) / 16; }
 
-static RingPlan ring_plan(const Geometry& g, int nct, int qt, int waves, int nbx)
+static RingPlan ring_plan(const Geometry& g, int nct, int qt, int waves, int nbx, bool mid)
 {
     RingPlan p{};
     p.nbx = nbx;
     p.nstrips = (g.nbw + nbx - 1) / nbx;
     p.SWv = rup(std::max(nbx * g.block + 2 * g.halo, (nbx - 1) * g.block + 16 * nct), 4);
-    p.ring = g.r + g.block;
+    p.midstage = mid ? 1 : 0;
+    p.ring = mid ? g.r + g.block : g.r;
     // V^T channel pitch: at least ring*SWv elements, and (pitch/2) = 4 (mod 64)
     // dwords so the 16 channels of a fragment read land in distinct banks
     p.CP = p.ring * p.SWv;
@@ -684,21 +695,40 @@ static int device_cus()
 }
 
 // Widest plan that fits in LDS with at least `min_strips` strips per image
-// and at most kRingMaxI groups per wave per block row, or nbx = 0 when even
-// one block column does not fit.
-static RingPlan ring_choose(const Geometry& g, int nct, int qt, int waves, int min_strips = 1)
+// and at most ring_maxi groups per wave per block row, for one ring size, or
+// nbx = 0 when even one block column does not fit.
+static RingPlan ring_choose1(const Geometry& g, int nct, int qt, int waves, int min_strips, bool mid)
 {
     const int limit = ring_lds_limit(waves);
     const int side = (g.block + g.stride - 1) / g.stride;
     const int groups = ((side * side + 15) / 16 + qt - 1) / qt;
-    const int nbx_items = kRingMaxI * waves / groups;
+    const int nbx_items = ring_maxi(nct) * waves / groups;
     for (int nbx = std::min((g.nbw + min_strips - 1) / min_strips, nbx_items); nbx >= 1; --nbx) {
-        if (ring_plan(g, nct, qt, waves, nbx).lds_bytes > limit) continue;
+        if (ring_plan(g, nct, qt, waves, nbx, mid).lds_bytes > limit) continue;
         // as few strips as fit, then equal widths (no narrow remainder strip)
         const int nstrips = (g.nbw + nbx - 1) / nbx;
-        return ring_plan(g, nct, qt, waves, (g.nbw + nstrips - 1) / nstrips);
+        return ring_plan(g, nct, qt, waves, (g.nbw + nstrips - 1) / nstrips, mid);
     }
     return RingPlan{};
+}
+
+// Expected efficiency of a plan: wave balance (groups per wave on average
+// over the most any wave takes) times the share of staged columns in use.
+static double ring_score(const Geometry& g, const RingPlan& p, int waves)
+{
+    if (p.nbx == 0) return 0.0;
+    const int items = p.nbx * p.groups;
+    const int most = (items + waves - 1) / waves;
+    return ((double)items / waves / most) * ((double)p.nbx * g.block / p.SWv);
+}
+
+// The ring of R + block rows (staging overlapped with compute, one barrier
+// per block row) unless the R-row ring allows a plan that is clearly better.
+static RingPlan ring_choose(const Geometry& g, int nct, int qt, int waves, int min_strips = 1)
+{
+    const RingPlan pm = ring_choose1(g, nct, qt, waves, min_strips, true);
+    const RingPlan pr = ring_choose1(g, nct, qt, waves, min_strips, false);
+    return ring_score(g, pr, waves) > 1.2 * ring_score(g, pm, waves) ? pr : pm;
 }
 
 // Strips per image a 4-wave launch needs for two workgroups on every CU.
