@@ -35,8 +35,9 @@
 //  * both passes loop over the in-image window rows only; the height term of
 //    a row is read from the conflict-free scratch.
 //  * the softmax is shifted by a per-query upper bound on its logits
-//    (|q| max|k|, with max|k|^2 bounded by running per-chunk maxima over all
-//    keys staged so far, plus the largest width and height terms) instead of an exact max, so a
+//    (sum over channels of |q_c| times the running maximum norm of k's chunk
+//    of c plus the table maxima of |rel_w_c| and |rel_h_c|, one MFMA) instead
+//    of an exact max, so a
 //    single pass forms base-2 logits with one FMA each, exponentiates
 //    (v_exp_f32), packs bf16 P and feeds it straight into the P.V MFMA
 //    (O^T = V^T . P^T) and a row-sum MFMA against ones (normalisation uses
@@ -177,7 +178,8 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         it.c4 = rest - it.dr * ng4;
         return it;
     };
-    // Two sets of maxima, by block-row parity: rows staged during block row
+    // Running maxima of |k_chunk|^2 (8-channel chunks) over the keys staged
+    // so far.  Two sets, by block-row parity: rows staged during block row
     // `by` update set (by+1)&1 while the waves computing block row `by` read
     // set by&1, which is final since the last barrier.  The bound a query
     // sees is therefore independent of wave timing.
@@ -255,6 +257,19 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             tabh[rt] = tab_frag(offrh, rt);
         }
     }
+
+    // tmax[c] = max_j |rel_w[j][c]| + max_j |rel_h[j][c]| over all table
+    // rows, one fp32 per channel in LDS (after the kmax words)
+    float* tmax = reinterpret_cast<float*>(smem + p.off_kn + 2 * 16 * 4);
+    if (tid < D) {
+        float mw = 0.f, mh = 0.f;
+        for (int j = 0; j < 2 * R - 1; ++j) {
+            mw = fmaxf(mw, fabsf((float)lds_ld<__bf16>(smem, offrw + 2u * (j * D + tid))));
+            mh = fmaxf(mh, fabsf((float)lds_ld<__bf16>(smem, offrh + 2u * (j * D + tid))));
+        }
+        tmax[tid] = mw + mh;
+    }
+    __syncthreads();
 
     const float alpha = p.alpha;
     s16x8 ones;
@@ -398,34 +413,36 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         }
 
         // ---- softmax shift: an upper bound on every logit of the query,
-        //   |q| * max|k| + max width term + max height term (Cauchy-Schwarz;
-        // max|k|^2 <= sum over 16-byte chunks of the running chunk maxima of
-        // the keys staged so far; the height maximum runs over all table
-        // rows), so exp2 never overflows.  Should the bound overshoot the true
-        // maximum so far that the weights' sum falls below 2^-60, the group is
-        // redone with the exact maximum.
-        float kmax2 = 0.f;
+        //   sum_c a_c |q_c|,  a_c = max|k_chunk(c)| + max_j |rel_w[j]_c| + max_j |rel_h[j]_c|
+        // (|k_chunk(c)|: L2 norm of the 8-channel chunk holding channel c;
+        // maxima over the keys staged so far and over all table rows).  As
+        // sum_chunks |q_chunk|_1 K_chunk >= sum_chunks |q_chunk|_2 |k_chunk|_2
+        // >= q.k, it bounds q.k + q.rel_w[.] + q.rel_h[.] for every key of the
+        // window, so exp2 never overflows.  With a_c (rounded up to bf16) in all 16 rows
+        // of an MFMA A operand and |q| as B, every lane of a query receives
+        // its bound: no cross-lane reduction.  Should the bound overshoot the
+        // true maximum so far that the weights' sum falls below 2^-60, the
+        // group is redone with the exact maximum.
+        FragT abound;
+        {
+            // this lane's channels gq*KPL .. +KPL-1 lie in chunk gq*KPL/8; the
+            // square root gets a relative margin for its rounding
+            const float kn = __builtin_sqrtf(__builtin_bit_cast(float, kmax_bits[16 * (byy & 1) + gq * KPL / 8])) *
+                             (1.f + 0x1p-20f);
 #pragma unroll
-        for (int c = 0; c < CPP; ++c) kmax2 += __builtin_bit_cast(float, kmax_bits[16 * (byy & 1) + c]);
+            for (int e = 0; e < KPL; ++e) {
+                const float a = kn + tmax[gq * KPL + e];
+                abound[e] = (short)((__builtin_bit_cast(unsigned, a) + 0xffffu) >> 16);   // round up
+            }
+        }
         float mb[QT];
 #pragma unroll
         for (int u = 0; u < QT; ++u) {
-            float qq = 0.f;
+            FragT aq = qf[u];
 #pragma unroll
-            for (int e = 0; e < KPL; ++e) {
-                const float x = __builtin_bit_cast(float, (unsigned)(unsigned short)qf[u][e] << 16);
-                qq = fmaf(x, x, qq);
-            }
-            float hm = max4(gh[u][0]), wm = max4(cinit[u][0]);
-#pragma unroll
-            for (int rt = 1; rt < kRelTiles; ++rt) hm = fmaxf(hm, max4(gh[u][rt]));
-#pragma unroll
-            for (int ct = 1; ct < NCT; ++ct) wm = fmaxf(wm, max4(cinit[u][ct]));
-            qq = sum_over_rows(qq);
-            const float rw = max_over_rows(wm);
-            hm = max_over_rows(hm);
-            const float bound = __builtin_sqrtf(qq * kmax2) + rw + hm;
-            mb[u] = alpha * (bound + 1e-3f * (1.f + fabsf(bound)));
+            for (int e = 0; e < KPL; ++e) aq[e] = (short)(aq[e] & 0x7fff);
+            const float bound = Frag<D>::mma(abound, aq, f32x4{0.f, 0.f, 0.f, 0.f})[0];
+            mb[u] = alpha * (bound + 1e-3f * (1.f + bound));
         }
         // height products, already in shifted base-2 units alpha*G - mb,
         // -> scratch (after the width reads above, in program order)
@@ -670,7 +687,7 @@ static RingPlan ring_plan(const Geometry& g, int nct, int qt, int waves, int nbx
     p.off_rel = rup(p.off_v + vb, 16);
     p.off_scr = rup(p.off_rel + rb, 16);
     p.off_kn = rup(p.off_scr + sb, 16);
-    p.lds_bytes = p.off_kn + 2 * 16 * 4;                    // running key-chunk norm maxima, 2 sets
+    p.lds_bytes = p.off_kn + 2 * 16 * 4 + g.d * 4;          // key-chunk norm maxima (2 sets), table maxima
     return p;
 }
 
