@@ -79,7 +79,7 @@ struct RingPlan {
     int CP;          // V^T channel pitch in elements (ring*SWv, padded)
     int groups;      // QT-tile groups per block
     int midstage;    // ring of R + block rows: next rows staged mid block row
-    int off_v, off_rel, off_scr, off_kn, lds_bytes;
+    int off_v, off_rel, off_scr, off_kn, off_qt, lds_bytes;
     int remap_xcd;
     int64_t nwg;
     float alpha;     // scale * log2(e)
@@ -269,6 +269,17 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         }
         tmax[tid] = mw + mh;
     }
+    // geometry of query n of tile u of group grp in a full block (every
+    // block but the partial ones at the image's right and bottom edges):
+    // {yl, xl, yl*W + xl, (yl/s)*Wo + xl/s}, or yl = -1 past the block's queries
+    const int side = g.block / g.stride;
+    for (int qi = tid; qi < p.groups * QT * 16; qi += kRingThreads) {   // qi = (grp*QT + u)*16 + n
+        const int iy = qi / side, ix = qi - iy * side;
+        const bool in = qi < side * side;
+        const int yl = iy * g.stride, xl = ix * g.stride;
+        lds_st<i32x4>(smem, p.off_qt + 16u * qi,
+                      in ? i32x4{yl, xl, yl * g.W + xl, iy * g.Wo + ix} : i32x4{-1, 0, 0, 0});
+    }
     __syncthreads();
 
     const float alpha = p.alpha;
@@ -298,6 +309,21 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         Tile T;
         const int j = it / p.groups, grp = it - j * p.groups;
         const int yb = byy * g.block;
+        if (yb + g.block <= g.H && (bx_first + j) * g.block + g.block <= g.W) {   // uniform: full block
+            T.xb = (bx_first + j) * g.block;
+            T.wcol0 = j * g.block;
+            const int qbase0 = yb * g.W + T.xb, obase0 = byy * side * g.Wo + (bx_first + j) * side;
+#pragma unroll
+            for (int u = 0; u < QT; ++u) {
+                const i32x4 e = lds_ld<i32x4>(smem, p.off_qt + 16u * ((grp * QT + u) * 16 + n));
+                T.qvalid[u] = e[0] >= 0;
+                T.yl[u] = T.qvalid[u] ? e[0] : 0;
+                T.xl[u] = e[1];
+                T.qpix[u] = qbase0 + e[2];
+                T.opix[u] = obase0 + e[3];
+            }
+            return T;
+        }
         const int nqy = (min(yb + g.block, g.H) - yb + g.stride - 1) / g.stride;
         T.xb = (bx_first + j) * g.block;
         T.wcol0 = j * g.block;
@@ -713,7 +739,8 @@ static RingPlan ring_plan(const Geometry& g, int nct, int qt, int waves, int nbx
     p.off_rel = rup(p.off_v + vb, 16);
     p.off_scr = rup(p.off_rel + rb, 16);
     p.off_kn = rup(p.off_scr + sb, 16);
-    p.lds_bytes = p.off_kn + 2 * 16 * 4 + g.d * 4;          // key-chunk norm maxima (2 sets), table maxima
+    p.off_qt = rup(p.off_kn + 2 * 16 * 4 + g.d * 4, 16);    // key-chunk norm maxima (2 sets), table maxima
+    p.lds_bytes = p.off_qt + p.groups * qt * 16 * 16;       // query geometry of a full block
     return p;
 }
 
