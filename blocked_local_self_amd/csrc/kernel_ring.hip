@@ -485,6 +485,20 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             rh0[u] = scr0 + u * scr_u + 4u * kScrStride * (NCT == 1 ? sh : 1);
         }
         auto rhv = [&](int u, int t) { return lds_ld<float>(smem, rh0[u] + 4u * kScrStride * t); };
+        // One column tile: row pairs start at even ring slots, so the second
+        // row of a pair is always the next slot (the ring has an even number
+        // of rows, the window advances by an even number of rows).  The pair
+        // may then begin one row above tlo and end one row past thi-1; those
+        // rows get a height term of -inf (weight 0).  Their scratch rows are
+        // not otherwise in use once the width terms have been read.
+        const int ts = NCT == 1 ? tlo - ((base + tlo) & 1) : tlo;
+        if constexpr (NCT == 1) {
+#pragma unroll
+            for (int u = 0; u < QT; ++u) {
+                if (ts < tlo) lds_st<float>(smem, rh0[u] + 4u * kScrStride * ts, -INFINITY);
+                if ((thi - ts) & 1) lds_st<float>(smem, rh0[u] + 4u * kScrStride * thi, -INFINITY);
+            }
+        }
 
         // lane-constant LDS byte offsets of this lane's K and V^T fragments
         // (column tile ct adds 16 columns; the K swizzle repeats every 16)
@@ -505,8 +519,8 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 
         // ---- weighted sum: P = exp2(alpha*S + (alpha*rh - mb)) in bf16;
         // O^T += V^T . P^T and L += 1 . P^T, one K=32 step per two score
-        // tiles: rows t and t+1 (one column tile; a missing second row has
-        // zero weights) or both column tiles of row t.  Operands of the next
+        // tiles: rows t and t+1 (one column tile, pairs aligned as above)
+        // or both column tiles of row t.  Operands of the next
         // step are loaded one step ahead (clamped to the last row).
         constexpr int STEP = NCT == 1 ? 2 : 1;
         f32x4 O[QT][D / 16], L[QT];
@@ -517,19 +531,32 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         };
         auto fetch = [&](int t0) {
             Ops o;
-            const int t1 = NCT == 1 ? min(t0 + 1, thi - 1) : t0;
-            const int c1 = NCT == 1 ? 0 : 1;
-            o.a0 = kload(t0, 0);
-            o.a1 = kload(t1, c1);
+            if constexpr (NCT == 1) {                 // rows t0, t0+1: slots s, s+1
+                const unsigned ko = kl + rslot(t0) * rowb_k;
+                o.a0 = lds_ld<FragT>(smem, ko);
+                o.a1 = lds_ld<FragT>(smem, ko + rowb_k);
 #pragma unroll
-            for (int mt = 0; mt < D / 16; ++mt) {
-                const u32x2 x0 = vload(mt, t0, 0), x1 = vload(mt, t1, c1);
-                o.vw[mt] = u32x4{x0[0], x0[1], x1[0], x1[1]};
-            }
+                for (int mt = 0; mt < D / 16; ++mt) {
+                    const unsigned vo = vl + 2u * ((unsigned)(mt * 16 * CP) + rslot(t0) * SWv);
+                    const u32x2 x0 = lds_ld<u32x2>(smem, vo), x1 = lds_ld<u32x2>(smem, vo + 2u * SWv);
+                    o.vw[mt] = u32x4{x0[0], x0[1], x1[0], x1[1]};
+                }
 #pragma unroll
-            for (int u = 0; u < QT; ++u) {
-                o.c0[u] = rhv(u, t0);
-                o.c1[u] = NCT == 1 ? rhv(u, t1) : o.c0[u];
+                for (int u = 0; u < QT; ++u) {
+                    const unsigned ro = rh0[u] + 4u * kScrStride * t0;
+                    o.c0[u] = lds_ld<float>(smem, ro);
+                    o.c1[u] = lds_ld<float>(smem, ro + 4u * kScrStride);
+                }
+            } else {                                  // row t0, column tiles 0 and 1
+                o.a0 = kload(t0, 0);
+                o.a1 = kload(t0, 1);
+#pragma unroll
+                for (int mt = 0; mt < D / 16; ++mt) {
+                    const u32x2 x0 = vload(mt, t0, 0), x1 = vload(mt, t0, 1);
+                    o.vw[mt] = u32x4{x0[0], x0[1], x1[0], x1[1]};
+                }
+#pragma unroll
+                for (int u = 0; u < QT; ++u) o.c0[u] = o.c1[u] = rhv(u, t0);
             }
             return o;
         };
@@ -543,12 +570,11 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             // double-buffered: the operands of the next step are issued before
             // the current step is computed; scheduling barriers keep the
             // compiler from sinking those loads back to their uses
-            auto compute = [&](const Ops& c, int t) {
-                const bool two = NCT == 2 || t + 1 < thi;   // uniform
+            auto compute = [&](const Ops& c) {
 #pragma unroll
                 for (int u = 0; u < QT; ++u) {
                     const u32x2 p0 = probs(Frag<D>::mma(c.a0, qf[u], cinit[u][0]), c.c0[u]);
-                    const u32x2 p1 = probs(Frag<D>::mma(c.a1, qf[u], cinit[u][NCT - 1]), two ? c.c1[u] : -3.0e38f);
+                    const u32x2 p1 = probs(Frag<D>::mma(c.a1, qf[u], cinit[u][NCT - 1]), c.c1[u]);
                     const s16x8 pf = __builtin_bit_cast(s16x8, u32x4{p0[0], p0[1], p1[0], p1[1]});
 #pragma unroll
                     for (int mt = 0; mt < D / 16; ++mt)
@@ -582,17 +608,17 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
                 }
             };
-            Ops A = fetch(tlo), B;
-            for (int t = tlo;;) {
-                B = fetch(min(t + STEP, thi - 1));
+            Ops A = fetch(ts), B;
+            for (int t = ts;;) {
+                B = fetch(t + STEP < thi ? t + STEP : t);
                 __builtin_amdgcn_sched_barrier(0);
-                compute(A, t);
+                compute(A);
                 __builtin_amdgcn_sched_barrier(0);
                 t += STEP;
                 if (t >= thi) break;
-                A = fetch(min(t + STEP, thi - 1));
+                A = fetch(t + STEP < thi ? t + STEP : t);
                 __builtin_amdgcn_sched_barrier(0);
-                compute(B, t);
+                compute(B);
                 __builtin_amdgcn_sched_barrier(0);
                 t += STEP;
                 if (t >= thi) break;
