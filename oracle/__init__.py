@@ -12,7 +12,9 @@ heads), 2.2 with Figures 1 and 2 (blocking, haloing, padding at the border,
 no centred mask, strided queries keep stride-1 neighbourhoods), appendix A
 (per-axis factorisation), and the HaloAttention module on the pswp.cn blog
 page (scale applied to q before both terms; table row (key - query) + r-1+h;
-off-image window positions masked).  This module only marshals numpy arrays.
+off-image window positions masked).  The backward (``halo_attn_bwd_ref``) is
+the exact derivative of that definition.  This module only marshals numpy
+arrays.
 """
 from __future__ import annotations
 
@@ -41,6 +43,12 @@ def _load():
         ctypes.c_int, ctypes.c_int, dp, ctypes.POINTER(dp), dp, ctypes.POINTER(dp),
         ctypes.c_double, dp, dp]
     lib.halo_ref_set_attention.restype = None
+    lib.halo_ref_bwd.argtypes = [dp] * 11 + [ctypes.c_int] * 8 + [ctypes.c_double, ctypes.c_int]
+    lib.halo_ref_bwd.restype = ctypes.c_int
+    lib.halo_ref_set_attention_bwd.argtypes = [
+        ctypes.c_int, ctypes.c_int, dp, ctypes.POINTER(dp), dp, ctypes.POINTER(dp),
+        ctypes.c_double, dp, dp, ctypes.POINTER(dp), ctypes.POINTER(dp), dp, dp]
+    lib.halo_ref_set_attention_bwd.restype = None
     lib.halo_ref_max_threads.argtypes = []
     lib.halo_ref_max_threads.restype = ctypes.c_int
     _lib = lib
@@ -71,6 +79,20 @@ def halo_attn_ref(q, k, v, rel_h, rel_w, block: int, halo: int,
     ``scale=None`` means d**-0.5, the value the HaloAttention module uses.
     """
     q, k, v, rel_h, rel_w = (_f64(t) for t in (q, k, v, rel_h, rel_w))
+    _check(q, k, v, rel_h, rel_w, block, halo, query_stride)
+    B, heads, H, W, d = q.shape
+    s = query_stride
+    if scale is None:
+        scale = float(d) ** -0.5
+    out = np.zeros((B, heads, H // s, W // s, d), dtype=np.float64)
+    rc = _load().halo_ref_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(rel_h), _ptr(rel_w), _ptr(out),
+                              B, heads, H, W, d, block, halo, s, float(scale), int(threads))
+    if rc != 0:
+        raise ValueError(f"halo_ref_fwd failed with status {rc}")
+    return out
+
+
+def _check(q, k, v, rel_h, rel_w, block, halo, query_stride):
     if q.ndim != 5 or k.shape != q.shape or v.shape != q.shape:
         raise ValueError(f"q, k, v must share one 5-D shape, got {q.shape} {k.shape} {v.shape}")
     B, heads, H, W, d = q.shape
@@ -80,14 +102,59 @@ def halo_attn_ref(q, k, v, rel_h, rel_w, block: int, halo: int,
     s = query_stride
     if s < 1 or block % s or H % s or W % s:
         raise ValueError("query_stride must divide block, H and W")
+
+
+def halo_attn_bwd_ref(q, k, v, rel_h, rel_w, dout, block: int, halo: int,
+                      query_stride: int = 1, scale: float | None = None,
+                      threads: int = 0):
+    """Backward pass, fp64: gradients of a scalar loss given d loss / d out.
+
+    Same arguments as ``halo_attn_ref`` plus ``dout`` [B, heads, H/s, W/s, d].
+    Returns (dq, dk, dv, drel_h, drel_w) as float64 arrays shaped like
+    (q, k, v, rel_h, rel_w).  Pixels that are not queries (stride > 1) get a
+    zero dq.  The exact derivative of the forward definition (chain rule
+    through each query's softmax); see halo_ref.c.
+    """
+    q, k, v, rel_h, rel_w, dout = (_f64(t) for t in (q, k, v, rel_h, rel_w, dout))
+    _check(q, k, v, rel_h, rel_w, block, halo, query_stride)
+    B, heads, H, W, d = q.shape
+    s = query_stride
+    if dout.shape != (B, heads, H // s, W // s, d):
+        raise ValueError(f"dout must be {(B, heads, H // s, W // s, d)}, got {dout.shape}")
     if scale is None:
         scale = float(d) ** -0.5
-    out = np.zeros((B, heads, H // s, W // s, d), dtype=np.float64)
-    rc = _load().halo_ref_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(rel_h), _ptr(rel_w), _ptr(out),
+    dq, dk, dv = (np.zeros(q.shape) for _ in range(3))
+    drh, drw = np.zeros(rel_h.shape), np.zeros(rel_w.shape)
+    rc = _load().halo_ref_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(rel_h), _ptr(rel_w), _ptr(dout),
+                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(drh), _ptr(drw),
                               B, heads, H, W, d, block, halo, s, float(scale), int(threads))
     if rc != 0:
-        raise ValueError(f"halo_ref_fwd failed with status {rc}")
-    return out
+        raise ValueError(f"halo_ref_bwd failed with status {rc}")
+    return dq, dk, dv, drh, drw
+
+
+def set_attention_bwd(q, keys, bias, vals, scale: float, g):
+    """Gradients of sum(g * set_attention(q, keys, bias, vals, scale)).
+
+    Returns (dq [d], dkeys [n, d], dbias [n], dvals [n, d]); dq covers the
+    path through q . keys_j only (bias is an independent input here).
+    """
+    q, g = _f64(q), _f64(g)
+    keys, vals, bias = _f64(keys), _f64(vals), _f64(bias)
+    n, d = keys.shape
+    if n < 1:
+        raise ValueError("need at least one key")
+    dp = ctypes.POINTER(ctypes.c_double)
+    dkeys, dvals = np.zeros((n, d)), np.zeros((n, d))
+    kp = (dp * n)(*[_ptr(keys[j]) for j in range(n)])
+    vp = (dp * n)(*[_ptr(vals[j]) for j in range(n)])
+    dkp = (dp * n)(*[_ptr(dkeys[j]) for j in range(n)])
+    dvp = (dp * n)(*[_ptr(dvals[j]) for j in range(n)])
+    dq, dbias = np.zeros(d), np.zeros(n)
+    scratch = np.zeros(2 * n)
+    _load().halo_ref_set_attention_bwd(d, n, _ptr(q), kp, _ptr(bias), vp, float(scale), _ptr(g),
+                                       _ptr(dq), dkp, dvp, _ptr(dbias), _ptr(scratch))
+    return dq, dkeys, dbias, dvals
 
 
 def set_attention(q, keys, bias, vals, scale: float) -> np.ndarray:

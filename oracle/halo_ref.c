@@ -38,6 +38,10 @@
  * partial and keeps the full window geometry); strided queries sit at
  * (s*y', s*x'), displacements measured at full resolution; b % s == 0.
  *
+ * Backward (halo_ref_bwd): the gradient of a scalar loss with respect to
+ * q, k, v and both tables, given its gradient with respect to out; the
+ * chain rule through the softmax of each query, nothing else.
+ *
  * Layouts: q, k, v are [B][heads][H][W][d] row-major; rel_h, rel_w are
  * [2r-1][d]; out is [B][heads][H/s][W/s][d].  All fp64.
  */
@@ -179,6 +183,191 @@ int halo_ref_fwd(const double* q, const double* k, const double* v,
     free(vals);
     free(bias);
     free(logits);
+    return 0;
+}
+
+/*
+ * Backward of halo_ref_set_attention: the exact gradient of the scalar
+ * sum_c g[c] * out[c] with respect to every input, by the chain rule through
+ * the softmax.  The pages print no backward pass; HaloNet's models are
+ * trained by gradient descent (section 4.1, Nesterov momentum on ImageNet),
+ * so this is the derivative of the definition above, written out:
+ *   P_j    = softmax(l)_j,  o = sum_j P_j val_j
+ *   dl_j   = P_j * (g . val_j - g . o)          (softmax Jacobian)
+ *   dq     = scale * sum_j dl_j key_j           (through q . key_j only)
+ *   dkey_j = scale * dl_j * q
+ *   dval_j = P_j * g
+ *   dbias_j = scale * dl_j
+ * dq[d], dbias[nkeys] are written; dkeys_j and dvals_j (arrays of nkeys
+ * pointers to d-vectors) are ACCUMULATED into (+=), so a key seen by several
+ * queries collects every contribution.  scratch holds 2*nkeys doubles.
+ */
+void halo_ref_set_attention_bwd(int d, int nkeys, const double* q,
+                                const double* const* keys, const double* bias,
+                                const double* const* vals, double scale,
+                                const double* g, double* dq,
+                                double* const* dkeys, double* const* dvals,
+                                double* dbias, double* scratch)
+{
+    double* p = scratch;            /* softmax weights */
+    double* gv = scratch + nkeys;   /* g . val_j */
+    double m = -INFINITY;
+    for (int j = 0; j < nkeys; ++j) {
+        p[j] = scale * (dot(q, keys[j], d) + bias[j]);
+        if (p[j] > m) m = p[j];
+    }
+    double z = 0.0;
+    for (int j = 0; j < nkeys; ++j) {
+        p[j] = exp(p[j] - m);
+        z += p[j];
+    }
+    double go = 0.0;                /* g . o = sum_j P_j (g . val_j) */
+    for (int j = 0; j < nkeys; ++j) {
+        p[j] /= z;
+        gv[j] = dot(g, vals[j], d);
+        go += p[j] * gv[j];
+    }
+    for (int c = 0; c < d; ++c) dq[c] = 0.0;
+    for (int j = 0; j < nkeys; ++j) {
+        const double dl = p[j] * (gv[j] - go);
+        dbias[j] = scale * dl;
+        for (int c = 0; c < d; ++c) {
+            dq[c] += scale * dl * keys[j][c];
+            dkeys[j][c] += scale * dl * q[c];
+            dvals[j][c] += p[j] * g[c];
+        }
+    }
+}
+
+/*
+ * Whole backward pass: given dout (the gradient of a scalar loss with
+ * respect to out, same layout as out), the gradients with respect to q, k,
+ * v (layouts of the inputs) and to the two tables ([2r-1][d]).  Per query it
+ * forms the same key set, biases and table rows as halo_ref_fwd, calls
+ * halo_ref_set_attention_bwd, and sends the bias gradient of key j to both
+ * tables and to q:  bias_j = q . rel_h[row_j] + q . rel_w[col_j], so
+ *   dq += sum_j dbias_j (rel_h[row_j] + rel_w[col_j]),
+ *   drel_h[row_j] += dbias_j q,  drel_w[col_j] += dbias_j q.
+ * Queries of other (batch, head) slices never share keys, so slices run in
+ * parallel; the tables' gradients are summed per slice and then over slices
+ * in slice order (results do not depend on the thread count).
+ * Returns 0, -1 (null pointer), -2 (bad shape) or -3 (no memory).
+ */
+int halo_ref_bwd(const double* q, const double* k, const double* v,
+                 const double* rel_h, const double* rel_w, const double* dout,
+                 double* dq, double* dk, double* dv, double* drel_h, double* drel_w,
+                 int B, int heads, int H, int W, int d,
+                 int block, int halo, int stride, double scale, int nthreads)
+{
+    if (check_shape(B, heads, H, W, d, block, halo, stride)) return -2;
+    const int r = block + 2 * halo;
+    const int c0 = r - 1 + halo;
+    const long nrel = (long)(2 * r - 1) * d;
+    if (!drel_h || !drel_w) return -1;
+    for (long e = 0; e < nrel; ++e) drel_h[e] = drel_w[e] = 0.0;
+    const long slices = (long)B * heads;
+    if (slices == 0 || H == 0 || W == 0) return 0;
+    if (!q || !k || !v || !rel_h || !rel_w || !dout || !dq || !dk || !dv) return -1;
+
+    const int Ho = H / stride, Wo = W / stride;
+    const long plane = (long)H * W * d;
+    const long oplane = (long)Ho * Wo * d;
+#ifdef _OPENMP
+    const int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#else
+    const int nt = 1;
+    (void)nthreads;
+#endif
+    const size_t nk = (size_t)r * r;
+    const double** keys = malloc(sizeof(double*) * nk * nt);
+    const double** vals = malloc(sizeof(double*) * nk * nt);
+    double** dkeys = malloc(sizeof(double*) * nk * nt);
+    double** dvals = malloc(sizeof(double*) * nk * nt);
+    int* rows = malloc(sizeof(int) * 2 * nk * nt);
+    double* bias = malloc(sizeof(double) * nk * nt);
+    double* dbias = malloc(sizeof(double) * nk * nt);
+    double* scratch = malloc(sizeof(double) * 2 * nk * nt);
+    double* qgrad = malloc(sizeof(double) * (size_t)d * nt);
+    double* part = calloc((size_t)slices * 2 * nrel, sizeof(double));   /* per-slice table grads */
+    if (!keys || !vals || !dkeys || !dvals || !rows || !bias || !dbias || !scratch || !qgrad || !part) {
+        free(keys); free(vals); free(dkeys); free(dvals); free(rows);
+        free(bias); free(dbias); free(scratch); free(qgrad); free(part);
+        return -3;
+    }
+    for (long e = 0; e < slices * plane; ++e) dq[e] = dk[e] = dv[e] = 0.0;
+
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+#endif
+    for (long sl = 0; sl < slices; ++sl) {
+#ifdef _OPENMP
+        const size_t t = (size_t)omp_get_thread_num();
+#else
+        const size_t t = 0;
+#endif
+        const double** tk = keys + t * nk;
+        const double** tv = vals + t * nk;
+        double** tdk = dkeys + t * nk;
+        double** tdv = dvals + t * nk;
+        int* trow = rows + t * 2 * nk;
+        double* tb = bias + t * nk;
+        double* tdb = dbias + t * nk;
+        double* ts = scratch + t * 2 * nk;
+        double* tq = qgrad + t * d;
+        double* ph = part + sl * 2 * nrel;     /* this slice's d rel_h */
+        double* pw = ph + nrel;                /* and d rel_w */
+        const long so = sl * plane;
+        for (int yo = 0; yo < Ho; ++yo) {
+            for (int xo = 0; xo < Wo; ++xo) {
+                const int y = yo * stride, x = xo * stride;
+                const int y0 = (y / block) * block - halo;
+                const int x0 = (x / block) * block - halo;
+                const double* qv = q + so + ((long)y * W + x) * d;
+                int n = 0;
+                for (int ky = y0; ky < y0 + r; ++ky) {
+                    if (ky < 0 || ky >= H) continue;
+                    const int rowh = ky - y + c0;
+                    const double rh = dot(qv, rel_h + (long)rowh * d, d);
+                    for (int kx = x0; kx < x0 + r; ++kx) {
+                        if (kx < 0 || kx >= W) continue;
+                        const int roww = kx - x + c0;
+                        const long off = so + ((long)ky * W + kx) * d;
+                        tk[n] = k + off;
+                        tv[n] = v + off;
+                        tdk[n] = dk + off;
+                        tdv[n] = dv + off;
+                        tb[n] = rh + dot(qv, rel_w + (long)roww * d, d);
+                        trow[2 * n] = rowh;
+                        trow[2 * n + 1] = roww;
+                        ++n;
+                    }
+                }
+                halo_ref_set_attention_bwd(d, n, qv, tk, tb, tv, scale,
+                                           dout + sl * oplane + ((long)yo * Wo + xo) * d,
+                                           tq, tdk, tdv, tdb, ts);
+                double* dqv = dq + so + ((long)y * W + x) * d;
+                for (int c = 0; c < d; ++c) dqv[c] = tq[c];
+                for (int j = 0; j < n; ++j) {
+                    const double* rhr = rel_h + (long)trow[2 * j] * d;
+                    const double* rwr = rel_w + (long)trow[2 * j + 1] * d;
+                    double* ghr = ph + (long)trow[2 * j] * d;
+                    double* gwr = pw + (long)trow[2 * j + 1] * d;
+                    for (int c = 0; c < d; ++c) {
+                        dqv[c] += tdb[j] * (rhr[c] + rwr[c]);
+                        ghr[c] += tdb[j] * qv[c];
+                        gwr[c] += tdb[j] * qv[c];
+                    }
+                }
+            }
+        }
+    }
+    for (long sl = 0; sl < slices; ++sl)
+        for (long e = 0; e < nrel; ++e) {
+            drel_h[e] += part[sl * 2 * nrel + e];
+            drel_w[e] += part[sl * 2 * nrel + nrel + e];
+        }
+    free(keys); free(vals); free(dkeys); free(dvals); free(rows);
+    free(bias); free(dbias); free(scratch); free(qgrad); free(part);
     return 0;
 }
 

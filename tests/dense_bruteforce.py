@@ -62,3 +62,38 @@ def halo_attn_dense(q, k, v, rel_h, rel_w, block, halo, stride=1, scale=None):
             w = w / w.sum(axis=1, keepdims=True)
             out[n, hd] = (w @ Vs).reshape(H // stride, W // stride, d)
     return out
+
+
+def halo_attn_dense_torch(q, k, v, rel_h, rel_w, block, halo, stride=1, scale=None):
+    """The same dense formulation in torch float64, differentiable.
+
+    Used to pin the oracle's backward against torch autograd: the gradient
+    comes from autograd through this dense route, not from any hand-written
+    derivative.
+    """
+    import torch
+    B, heads, H, W, d = q.shape
+    if scale is None:
+        scale = d ** -0.5
+    member, row_h, row_w, qy, qx = window_mask_and_index(H, W, block, halo, stride)
+    nrows = rel_h.shape[0]
+    member = torch.as_tensor(member)
+    safe_h = torch.as_tensor(np.clip(row_h, 0, nrows - 1))
+    safe_w = torch.as_tensor(np.clip(row_w, 0, nrows - 1))
+    qy, qx = torch.as_tensor(qy), torch.as_tensor(qx)
+    outs = []
+    for n in range(B):
+        per_head = []
+        for hd in range(heads):
+            Qs = q[n, hd][qy, qx]
+            Ks = k[n, hd].reshape(-1, d)
+            Vs = v[n, hd].reshape(-1, d)
+            lh = Qs @ rel_h.T
+            lw = Qs @ rel_w.T
+            bias = torch.gather(lh, 1, safe_h) + torch.gather(lw, 1, safe_w)
+            logits = scale * (Qs @ Ks.T + bias)
+            logits = logits.masked_fill(~member, float("-inf"))
+            w = torch.softmax(logits, dim=1)
+            per_head.append((w @ Vs).reshape(H // stride, W // stride, d))
+        outs.append(torch.stack(per_head))
+    return torch.stack(outs)
