@@ -11,12 +11,15 @@ module on the pswp.cn blog page, section 4): for every query pixel, softmax
 over the in-image keys of its block's (block+2*halo)^2 window of
 scale * (q.k + q.rel_h[dy + c0] + q.rel_w[dx + c0]), c0 = block+3*halo-1,
 then the weighted sum of v; queries at multiples of ``query_stride``.
+``halo_attn_bwd`` is its exact gradient (recomputing every softmax), and
+``halo_attention`` joins the two as a differentiable torch function.
 """
 from __future__ import annotations
 
 from . import _native
 
-__all__ = ["halo_attn_fwd", "select_kernel", "HaloError", "KERNELS"]
+__all__ = ["halo_attn_fwd", "halo_attn_bwd", "bwd_workspace_bytes", "halo_attention",
+           "select_kernel", "HaloError", "KERNELS"]
 
 HaloError = _native.HaloError
 KERNELS = {"auto": _native.HALO_KERNEL_AUTO, "generic": _native.HALO_KERNEL_GENERIC,
@@ -41,18 +44,9 @@ def select_kernel(d: int, block: int, halo: int, query_stride: int = 1, dtype: s
     return {v: k for k, v in KERNELS.items()}[st]
 
 
-def halo_attn_fwd(q, k, v, rel_h, rel_w, block: int, halo: int, query_stride: int = 1,
-                  scale: float | None = None, out=None, kernel: str = "auto", stream=None):
-    """Halo attention forward.
-
-    q, k, v: [B, heads, H, W, d] contiguous CUDA(HIP) tensors, float32 or bfloat16.
-    rel_h, rel_w: [2*(block+2*halo)-1, d], same dtype and device.
-    Returns out [B, heads, H/s, W/s, d] (allocated unless ``out`` is given).
-    ``scale=None`` means d**-0.5.  ``kernel`` in {"auto", "generic", "mfma", "mfma_strip"}.
-    ``stream``: a torch.cuda.Stream (default: the current stream).
-    """
+def _check_inputs(q, k, v, rel_h, rel_w, block, halo, query_stride, **extra):
     import torch
-    tensors = {"q": q, "k": k, "v": v, "rel_h": rel_h, "rel_w": rel_w}
+    tensors = {"q": q, "k": k, "v": v, "rel_h": rel_h, "rel_w": rel_w, **extra}
     for name, t in tensors.items():
         if not isinstance(t, torch.Tensor):
             raise TypeError(f"{name} must be a torch.Tensor")
@@ -73,6 +67,22 @@ def halo_attn_fwd(q, k, v, rel_h, rel_w, block: int, halo: int, query_stride: in
     s = query_stride
     if s < 1 or H % s or W % s:
         raise ValueError(f"query_stride={s} must divide H={H} and W={W}")
+    return B, heads, H, W, d
+
+
+def halo_attn_fwd(q, k, v, rel_h, rel_w, block: int, halo: int, query_stride: int = 1,
+                  scale: float | None = None, out=None, kernel: str = "auto", stream=None):
+    """Halo attention forward.
+
+    q, k, v: [B, heads, H, W, d] contiguous CUDA(HIP) tensors, float32 or bfloat16.
+    rel_h, rel_w: [2*(block+2*halo)-1, d], same dtype and device.
+    Returns out [B, heads, H/s, W/s, d] (allocated unless ``out`` is given).
+    ``scale=None`` means d**-0.5.  ``kernel`` in {"auto", "generic", "mfma", "mfma_strip"}.
+    ``stream``: a torch.cuda.Stream (default: the current stream).
+    """
+    import torch
+    B, heads, H, W, d = _check_inputs(q, k, v, rel_h, rel_w, block, halo, query_stride)
+    s = query_stride
     if scale is None:
         scale = float(d) ** -0.5
     oshape = (B, heads, H // s, W // s, d)
@@ -93,3 +103,95 @@ def halo_attn_fwd(q, k, v, rel_h, rel_w, block: int, halo: int, query_stride: in
                                       stream.cuda_stream)
     _native.check(st)
     return out
+
+
+def bwd_workspace_bytes(B: int, heads: int, H: int, W: int, d: int, block: int, halo: int,
+                        query_stride: int = 1, dtype: str = "bf16") -> int:
+    """Workspace bytes ``halo_attn_bwd`` needs for these sizes (host-only)."""
+    code = {"fp32": _native.HALO_F32, "bf16": _native.HALO_BF16}[dtype]
+    n = _native.load().halo_attn_bwd_workspace_bytes(B, heads, H, W, d, block, halo, query_stride, code)
+    if n < 0:
+        _native.check(int(n))
+    return int(n)
+
+
+def halo_attn_bwd(q, k, v, rel_h, rel_w, dout, block: int, halo: int, query_stride: int = 1,
+                  scale: float | None = None, kernel: str = "auto", workspace=None, stream=None):
+    """Halo attention backward: gradients given dout = d loss / d out.
+
+    Same tensors and arguments as ``halo_attn_fwd`` plus ``dout``
+    [B, heads, H/s, W/s, d] (same dtype).  Returns (dq, dk, dv, drel_h, drel_w):
+    dq, dk, dv in q's dtype and layout, drel_h and drel_w float32 [2r-1, d].
+    ``workspace``: optional uint8 CUDA tensor of at least
+    ``bwd_workspace_bytes(...)`` bytes (allocated here when None).
+    """
+    import torch
+    B, heads, H, W, d = _check_inputs(q, k, v, rel_h, rel_w, block, halo, query_stride, dout=dout)
+    s = query_stride
+    oshape = (B, heads, H // s, W // s, d)
+    if tuple(dout.shape) != oshape:
+        raise ValueError(f"dout must be {oshape}; got {tuple(dout.shape)}")
+    if scale is None:
+        scale = float(d) ** -0.5
+    if kernel not in KERNELS:
+        raise ValueError(f"kernel must be one of {sorted(KERNELS)}")
+    dtype = "bf16" if q.dtype == torch.bfloat16 else "fp32"
+    need = bwd_workspace_bytes(B, heads, H, W, d, block, halo, s, dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    elif (workspace.device != q.device or not workspace.is_contiguous()
+          or workspace.numel() * workspace.element_size() < need):
+        raise ValueError(f"workspace must be a contiguous tensor of >= {need} bytes on {q.device}")
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    r = block + 2 * halo
+    drh = torch.empty((2 * r - 1, d), dtype=torch.float32, device=q.device)
+    drw = torch.empty_like(drh)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    lib = _native.load()
+    with torch.cuda.device(q.device):
+        st = lib.halo_attn_bwd_kernel(q.data_ptr(), k.data_ptr(), v.data_ptr(), rel_h.data_ptr(),
+                                      rel_w.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                      dv.data_ptr(), drh.data_ptr(), drw.data_ptr(), workspace.data_ptr(),
+                                      workspace.numel() * workspace.element_size(), B, heads, H, W, d,
+                                      block, halo, s, float(scale), _dtype_code(q), KERNELS[kernel],
+                                      stream.cuda_stream)
+    _native.check(st)
+    return dq, dk, dv, drh, drw
+
+
+def _make_function():
+    import torch
+
+    class HaloAttentionFunction(torch.autograd.Function):
+        """out = halo_attn_fwd(...); its backward calls halo_attn_bwd."""
+
+        @staticmethod
+        def forward(ctx, q, k, v, rel_h, rel_w, block, halo, query_stride, scale):
+            ctx.save_for_backward(q, k, v, rel_h, rel_w)
+            ctx.cfg = (block, halo, query_stride, scale)
+            return halo_attn_fwd(q, k, v, rel_h, rel_w, block, halo, query_stride, scale=scale)
+
+        @staticmethod
+        def backward(ctx, dout):
+            q, k, v, rel_h, rel_w = ctx.saved_tensors
+            block, halo, s, scale = ctx.cfg
+            dq, dk, dv, drh, drw = halo_attn_bwd(q, k, v, rel_h, rel_w, dout.contiguous(), block, halo,
+                                                 s, scale=scale)
+            return dq, dk, dv, drh.to(rel_h.dtype), drw.to(rel_w.dtype), None, None, None, None
+
+    return HaloAttentionFunction
+
+
+_FUNCTION = None
+
+
+def halo_attention(q, k, v, rel_h, rel_w, block: int, halo: int, query_stride: int = 1,
+                   scale: float | None = None):
+    """Differentiable halo attention (torch autograd) on the library's kernels."""
+    global _FUNCTION
+    if _FUNCTION is None:
+        _FUNCTION = _make_function()
+    if scale is None:
+        scale = float(q.shape[-1]) ** -0.5
+    return _FUNCTION.apply(q, k, v, rel_h, rel_w, block, halo, query_stride, scale)

@@ -16,7 +16,8 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "halo_attn.h")
 HALO_F32, HALO_BF16 = 0, 1
 HALO_KERNEL_AUTO, HALO_KERNEL_GENERIC, HALO_KERNEL_MFMA, HALO_KERNEL_MFMA_STRIP = 0, 1, 2, 3
 STATUS = {0: "HALO_OK", -1: "HALO_ERR_NULL", -2: "HALO_ERR_SHAPE", -3: "HALO_ERR_DTYPE",
-          -4: "HALO_ERR_UNSUPPORTED", -5: "HALO_ERR_HIP", -6: "HALO_ERR_ALIAS"}
+          -4: "HALO_ERR_UNSUPPORTED", -5: "HALO_ERR_HIP", -6: "HALO_ERR_ALIAS",
+          -7: "HALO_ERR_WORKSPACE"}
 
 _lib = None
 
@@ -41,6 +42,13 @@ def load() -> ctypes.CDLL:
     lib.halo_attn_fwd.restype = i
     lib.halo_attn_fwd_kernel.argtypes = [vp] * 6 + [i] * 8 + [f, i, i, vp]
     lib.halo_attn_fwd_kernel.restype = i
+    sz = ctypes.c_size_t
+    lib.halo_attn_bwd_kernel.argtypes = [vp] * 12 + [sz] + [i] * 8 + [f, i, i, vp]
+    lib.halo_attn_bwd_kernel.restype = i
+    lib.halo_attn_bwd.argtypes = [vp] * 12 + [sz] + [i] * 8 + [f, i, vp]
+    lib.halo_attn_bwd.restype = i
+    lib.halo_attn_bwd_workspace_bytes.argtypes = [i] * 9
+    lib.halo_attn_bwd_workspace_bytes.restype = ctypes.c_longlong
     lib.halo_attn_select_kernel.argtypes = [i] * 5
     lib.halo_attn_select_kernel.restype = i
     lib.halo_attn_last_error.argtypes = []
@@ -64,4 +72,4 @@ def declared_functions() -> list[str]:
     """Function names declared in include/halo_attn.h."""
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(halo_attn_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*[\w\s]+?\*?\s*(halo_attn_\w+)\s*\(", text, flags=re.M)))

@@ -15,6 +15,11 @@ hipError_t launch_generic(const void* q, const void* k, const void* v, const voi
 bool mfma_supported(int d, int r, int block, int stride, bool bf16);
 hipError_t launch_mfma(const void* q, const void* k, const void* v, const void* rh,
                        const void* rw, void* out, const Geometry& g, bool force_strip, hipStream_t st);
+int64_t bwd_generic_workspace_floats(const Geometry& g);
+hipError_t launch_bwd_generic(const void* q, const void* k, const void* v, const void* rh, const void* rw,
+                              const void* dout, void* dq, void* dk, void* dv, float* drh, float* drw,
+                              void* ws, const Geometry& g, bool bf16, hipStream_t st);
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t st);
 }  // namespace halo
 
 namespace {
@@ -70,25 +75,28 @@ int halo_attn_select_kernel(int d, int block, int halo, int query_stride, int dt
                ? HALO_KERNEL_MFMA : HALO_KERNEL_GENERIC;
 }
 
-int halo_attn_fwd_kernel(const void* q, const void* k, const void* v,
-                         const void* rel_h, const void* rel_w, void* out,
-                         int B, int heads, int H, int W, int d,
-                         int block, int halo, int query_stride,
-                         float scale, int dtype, int kernel, void* stream)
+}  // extern "C"
+
+namespace {
+
+// Checks shared by every entry point that takes tensors.  Fills g; sets
+// empty when a size is zero (the call then has nothing to compute).
+int check_sizes(int B, int heads, int H, int W, int d, int block, int halo, int query_stride,
+                float scale, int dtype, halo::Geometry& g, bool& empty)
 {
-    g_err[0] = 0;
     int st = check_config(d, block, halo, query_stride, dtype);
     if (st) return st;
-    if (kernel != HALO_KERNEL_AUTO && kernel != HALO_KERNEL_GENERIC && kernel != HALO_KERNEL_MFMA &&
-        kernel != HALO_KERNEL_MFMA_STRIP)
-        return fail(HALO_ERR_SHAPE, "kernel=%d is not a halo_kernel value", kernel);
     if (B < 0 || heads < 0 || H < 0 || W < 0)
         return fail(HALO_ERR_SHAPE, "negative size: B=%d heads=%d H=%d W=%d", B, heads, H, W);
     if (H % query_stride || W % query_stride)
         return fail(HALO_ERR_SHAPE, "query_stride=%d must divide H=%d and W=%d", query_stride, H, W);
     if (!std::isfinite(scale)) return fail(HALO_ERR_SHAPE, "scale must be finite");
-    if (B == 0 || heads == 0 || H == 0 || W == 0) return HALO_OK;   // empty: nothing to do
-
+    const int r = block + 2 * halo;
+    g = halo::Geometry{};
+    g.d = d; g.block = block; g.halo = halo; g.stride = query_stride;
+    g.r = r; g.c0 = r - 1 + halo; g.scale = scale;
+    empty = B == 0 || heads == 0 || H == 0 || W == 0;
+    if (empty) return HALO_OK;
     // magnitude checks in double first, so the int64 products below cannot overflow
     const double nelem = (double)B * heads * H * W * d;
     const int nbh = (H + block - 1) / block, nbw = (W + block - 1) / block;
@@ -97,18 +105,40 @@ int halo_attn_fwd_kernel(const void* q, const void* k, const void* v,
         return fail(HALO_ERR_SHAPE, "tensor too large (%.3g elements, limit 1e18)", nelem);
     if (nblk >= 2147483648.0)
         return fail(HALO_ERR_SHAPE, "%.0f blocks exceed the 2^31 grid limit", nblk);
-    const int64_t BH = (int64_t)B * heads;
-    const int64_t elems = BH * H * W * d;
+    g.BH = (int64_t)B * heads; g.H = H; g.W = W;
+    g.Ho = H / query_stride; g.Wo = W / query_stride;
+    g.nbh = nbh; g.nbw = nbw;
+    return HALO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int halo_attn_fwd_kernel(const void* q, const void* k, const void* v,
+                         const void* rel_h, const void* rel_w, void* out,
+                         int B, int heads, int H, int W, int d,
+                         int block, int halo, int query_stride,
+                         float scale, int dtype, int kernel, void* stream)
+{
+    g_err[0] = 0;
+    if (kernel != HALO_KERNEL_AUTO && kernel != HALO_KERNEL_GENERIC && kernel != HALO_KERNEL_MFMA &&
+        kernel != HALO_KERNEL_MFMA_STRIP)
+        return fail(HALO_ERR_SHAPE, "kernel=%d is not a halo_kernel value", kernel);
+    halo::Geometry g;
+    bool empty = false;
+    int st = check_sizes(B, heads, H, W, d, block, halo, query_stride, scale, dtype, g, empty);
+    if (st) return st;
+    if (empty) return HALO_OK;   // nothing to do
 
     if (!q || !k || !v || !rel_h || !rel_w || !out)
         return fail(HALO_ERR_NULL, "null pointer among q, k, v, rel_h, rel_w, out");
 
-    const int r = block + 2 * halo;
+    const int r = g.r;
     const size_t esz = dtype == HALO_BF16 ? 2 : 4;
-    const size_t in_bytes = (size_t)elems * esz;
+    const size_t in_bytes = (size_t)(g.BH * H * W * d) * esz;
     const size_t tab_bytes = (size_t)(2 * r - 1) * d * esz;
-    const int Ho = H / query_stride, Wo = W / query_stride;
-    const size_t out_bytes = (size_t)(BH * Ho * Wo * d) * esz;
+    const size_t out_bytes = (size_t)(g.BH * g.Ho * g.Wo * d) * esz;
     if (overlaps(out, out_bytes, q, in_bytes) || overlaps(out, out_bytes, k, in_bytes) ||
         overlaps(out, out_bytes, v, in_bytes) || overlaps(out, out_bytes, rel_h, tab_bytes) ||
         overlaps(out, out_bytes, rel_w, tab_bytes))
@@ -120,12 +150,6 @@ int halo_attn_fwd_kernel(const void* q, const void* k, const void* v,
         return fail(HALO_ERR_UNSUPPORTED,
                     "matrix-core kernel needs bf16, d in {16,32}, window side <= 32 "
                     "(got dtype=%d d=%d r=%d)", dtype, d, r);
-
-    halo::Geometry g;
-    g.BH = BH; g.H = H; g.W = W; g.d = d;
-    g.block = block; g.halo = halo; g.stride = query_stride;
-    g.r = r; g.c0 = r - 1 + halo; g.Ho = Ho; g.Wo = Wo;
-    g.nbh = nbh; g.nbw = nbw; g.scale = scale;
 
     hipStream_t s = (hipStream_t)stream;
     const bool use_mfma = kernel == HALO_KERNEL_MFMA || kernel == HALO_KERNEL_MFMA_STRIP ||
@@ -146,6 +170,94 @@ int halo_attn_fwd(const void* q, const void* k, const void* v,
 {
     return halo_attn_fwd_kernel(q, k, v, rel_h, rel_w, out, B, heads, H, W, d, block, halo,
                                 query_stride, scale, dtype, HALO_KERNEL_AUTO, stream);
+}
+
+long long halo_attn_bwd_workspace_bytes(int B, int heads, int H, int W, int d,
+                                        int block, int halo, int query_stride, int dtype)
+{
+    g_err[0] = 0;
+    halo::Geometry g;
+    bool empty = false;
+    const int st = check_sizes(B, heads, H, W, d, block, halo, query_stride, 1.0f, dtype, g, empty);
+    if (st) return st;
+    if (empty) return 0;
+    return (long long)halo::bwd_generic_workspace_floats(g) * 4;
+}
+
+int halo_attn_bwd_kernel(const void* q, const void* k, const void* v,
+                         const void* rel_h, const void* rel_w, const void* dout,
+                         void* dq, void* dk, void* dv, float* drel_h, float* drel_w,
+                         void* workspace, size_t workspace_bytes,
+                         int B, int heads, int H, int W, int d,
+                         int block, int halo, int query_stride,
+                         float scale, int dtype, int kernel, void* stream)
+{
+    g_err[0] = 0;
+    if (kernel != HALO_KERNEL_AUTO && kernel != HALO_KERNEL_GENERIC && kernel != HALO_KERNEL_MFMA &&
+        kernel != HALO_KERNEL_MFMA_STRIP)
+        return fail(HALO_ERR_SHAPE, "kernel=%d is not a halo_kernel value", kernel);
+    halo::Geometry g;
+    bool empty = false;
+    int st = check_sizes(B, heads, H, W, d, block, halo, query_stride, scale, dtype, g, empty);
+    if (st) return st;
+    if (!drel_h || !drel_w) return fail(HALO_ERR_NULL, "null drel_h or drel_w");
+    const int r = g.r;
+    const size_t tabf = (size_t)(2 * r - 1) * d;
+    if (overlaps(drel_h, tabf * 4, drel_w, tabf * 4))
+        return fail(HALO_ERR_ALIAS, "drel_h overlaps drel_w");
+    hipStream_t s = (hipStream_t)stream;
+    if (empty) {   // the gradient of an empty sum: zero tables, nothing else
+        hipError_t e = halo::launch_zero_f32(drel_h, (int64_t)tabf, s);
+        if (e == hipSuccess) e = halo::launch_zero_f32(drel_w, (int64_t)tabf, s);
+        if (e != hipSuccess) return fail(HALO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+        return HALO_OK;
+    }
+    if (!q || !k || !v || !rel_h || !rel_w || !dout || !dq || !dk || !dv || !workspace)
+        return fail(HALO_ERR_NULL, "null pointer among q, k, v, rel_h, rel_w, dout, dq, dk, dv, workspace");
+    const size_t need = (size_t)halo::bwd_generic_workspace_floats(g) * 4;
+    if (workspace_bytes < need)
+        return fail(HALO_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu this call needs",
+                    workspace_bytes, need);
+    if ((uintptr_t)workspace % 16)
+        return fail(HALO_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+
+    const size_t esz = dtype == HALO_BF16 ? 2 : 4;
+    const size_t in_bytes = (size_t)(g.BH * H * W * d) * esz;
+    const size_t tab_bytes = tabf * esz;
+    const size_t out_bytes = (size_t)(g.BH * g.Ho * g.Wo * d) * esz;
+    const void* ins[6] = {q, k, v, rel_h, rel_w, dout};
+    const size_t insz[6] = {in_bytes, in_bytes, in_bytes, tab_bytes, tab_bytes, out_bytes};
+    const void* outs[6] = {dq, dk, dv, drel_h, drel_w, workspace};
+    const size_t outsz[6] = {in_bytes, in_bytes, in_bytes, tabf * 4, tabf * 4, need};
+    for (int a = 0; a < 6; ++a) {
+        for (int b = 0; b < 6; ++b)
+            if (overlaps(outs[a], outsz[a], ins[b], insz[b]))
+                return fail(HALO_ERR_ALIAS, "an output or the workspace overlaps an input tensor");
+        for (int b = a + 1; b < 6; ++b)
+            if (overlaps(outs[a], outsz[a], outs[b], outsz[b]))
+                return fail(HALO_ERR_ALIAS, "two outputs (or an output and the workspace) overlap");
+    }
+    if (kernel == HALO_KERNEL_MFMA || kernel == HALO_KERNEL_MFMA_STRIP)
+        return fail(HALO_ERR_UNSUPPORTED, "no matrix-core backward kernel for these arguments");
+
+    const hipError_t e = halo::launch_bwd_generic(q, k, v, rel_h, rel_w, dout, dq, dk, dv, drel_h, drel_w,
+                                                  workspace, g, dtype == HALO_BF16, s);
+    if (e != hipSuccess)
+        return fail(HALO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return HALO_OK;
+}
+
+int halo_attn_bwd(const void* q, const void* k, const void* v,
+                  const void* rel_h, const void* rel_w, const void* dout,
+                  void* dq, void* dk, void* dv, float* drel_h, float* drel_w,
+                  void* workspace, size_t workspace_bytes,
+                  int B, int heads, int H, int W, int d,
+                  int block, int halo, int query_stride,
+                  float scale, int dtype, void* stream)
+{
+    return halo_attn_bwd_kernel(q, k, v, rel_h, rel_w, dout, dq, dk, dv, drel_h, drel_w, workspace,
+                                workspace_bytes, B, heads, H, W, d, block, halo, query_stride, scale,
+                                dtype, HALO_KERNEL_AUTO, stream);
 }
 
 }  // extern "C"

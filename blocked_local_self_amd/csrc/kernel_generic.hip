@@ -12,6 +12,11 @@
 //     scale * (q.k + q.rel_h[ky - y + c0] + q.rel_w[kx - x + c0]).
 // This is the path for fp32 inputs, for shapes the matrix-core kernel does
 // not cover, and a second implementation to cross-check that kernel.
+//
+// With STATS set the same kernel serves the backward pass: instead of the
+// output it writes, per query, the log of the softmax normaliser in logit
+// units (lse = m + log l) and dout . out, the two numbers every later
+// gradient kernel needs.
 #include "halo_common.h"
 
 namespace halo {
@@ -19,11 +24,12 @@ namespace halo {
 constexpr int kGenericKC = 64;        // keys per LDS chunk
 constexpr int kGenericThreads = 256;  // upper bound on workgroup size
 
-template <int DMAX, typename T>
+template <int DMAX, typename T, bool STATS>
 __global__ __launch_bounds__(kGenericThreads)
 void generic_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                     const T* __restrict__ rel_h, const T* __restrict__ rel_w,
-                    T* __restrict__ out, Geometry g)
+                    T* __restrict__ out, Geometry g,
+                    const T* __restrict__ dout, float* __restrict__ lse, float* __restrict__ dsum)
 {
     __shared__ float Ks[kGenericKC][DMAX];
     __shared__ float Vs[kGenericKC][DMAX];
@@ -117,23 +123,36 @@ void generic_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
         }
         if (active) {
             const float inv = 1.f / l;
-            T* op = os + ((int64_t)((y / g.stride) * g.Wo + x / g.stride)) * d;
+            const int64_t opix = (int64_t)((y / g.stride) * g.Wo + x / g.stride);
+            if constexpr (STATS) {
+                const T* gp = dout + bh * (int64_t)g.Ho * g.Wo * d + opix * d;
+                float acc = 0.f;
 #pragma unroll
-            for (int c = 0; c < DMAX; ++c) if (c < d) op[c] = from_f32<T>(o[c] * inv);
+                for (int c = 0; c < DMAX; ++c) if (c < d) acc += to_f32(gp[c]) * o[c];
+                const int64_t qo = bh * (int64_t)g.Ho * g.Wo + opix;
+                lse[qo] = m + __logf(l);
+                dsum[qo] = acc * inv;
+            } else {
+                T* op = os + opix * d;
+#pragma unroll
+                for (int c = 0; c < DMAX; ++c) if (c < d) op[c] = from_f32<T>(o[c] * inv);
+            }
         }
     }
 }
 
-template <int DMAX, typename T>
+template <int DMAX, typename T, bool STATS = false>
 static hipError_t launch_generic_t(const void* q, const void* k, const void* v, const void* rh,
-                                   const void* rw, void* out, const Geometry& g, hipStream_t st)
+                                   const void* rw, void* out, const Geometry& g, hipStream_t st,
+                                   const void* dout = nullptr, float* lse = nullptr, float* dsum = nullptr)
 {
     const int64_t nblocks = g.BH * g.nbh * g.nbw;
     const int qmax = ((g.block + g.stride - 1) / g.stride) * ((g.block + g.stride - 1) / g.stride);
     int threads = ((qmax + 63) / 64) * 64;
     if (threads > kGenericThreads) threads = kGenericThreads;
-    hipLaunchKernelGGL((generic_kernel<DMAX, T>), dim3((unsigned)nblocks), dim3(threads), 0, st,
-                       (const T*)q, (const T*)k, (const T*)v, (const T*)rh, (const T*)rw, (T*)out, g);
+    hipLaunchKernelGGL((generic_kernel<DMAX, T, STATS>), dim3((unsigned)nblocks), dim3(threads), 0, st,
+                       (const T*)q, (const T*)k, (const T*)v, (const T*)rh, (const T*)rw, (T*)out, g,
+                       (const T*)dout, lse, dsum);
     return hipGetLastError();
 }
 
@@ -145,6 +164,26 @@ static hipError_t launch_generic_dt(const void* q, const void* k, const void* v,
     if (g.d <= 32) return launch_generic_t<32, T>(q, k, v, rh, rw, out, g, st);
     if (g.d <= 64) return launch_generic_t<64, T>(q, k, v, rh, rw, out, g, st);
     return launch_generic_t<128, T>(q, k, v, rh, rw, out, g, st);
+}
+
+// Softmax statistics for the backward pass (lse, dout . out per query).
+template <typename T>
+static hipError_t launch_stats_dt(const void* q, const void* k, const void* v, const void* rh,
+                                  const void* rw, const void* dout, float* lse, float* dsum,
+                                  const Geometry& g, hipStream_t st)
+{
+    if (g.d <= 16) return launch_generic_t<16, T, true>(q, k, v, rh, rw, nullptr, g, st, dout, lse, dsum);
+    if (g.d <= 32) return launch_generic_t<32, T, true>(q, k, v, rh, rw, nullptr, g, st, dout, lse, dsum);
+    if (g.d <= 64) return launch_generic_t<64, T, true>(q, k, v, rh, rw, nullptr, g, st, dout, lse, dsum);
+    return launch_generic_t<128, T, true>(q, k, v, rh, rw, nullptr, g, st, dout, lse, dsum);
+}
+
+hipError_t launch_softmax_stats(const void* q, const void* k, const void* v, const void* rh,
+                                const void* rw, const void* dout, float* lse, float* dsum,
+                                const Geometry& g, bool bf16, hipStream_t st)
+{
+    return bf16 ? launch_stats_dt<__bf16>(q, k, v, rh, rw, dout, lse, dsum, g, st)
+                : launch_stats_dt<float>(q, k, v, rh, rw, dout, lse, dsum, g, st);
 }
 
 // Host entry used by the dispatcher; d <= 128 is checked by the caller.

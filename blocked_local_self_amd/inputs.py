@@ -10,6 +10,10 @@ rel_w, each [2r-1, d] with r = block + 2*halo, drawn N(0, 1) and multiplied by
 d**-0.5 (the initialisation of the relative tables in the HaloAttention module
 on the pswp.cn blog page, section 4).  Every tensor is then rounded to the
 workload dtype (round-to-nearest-even for bf16), tables included.
+
+For the backward pass, the gradient of the loss with respect to out is drawn
+by ``make_grad_output`` from its own seeded generator: N(0, 1) float32 of the
+output's shape, rounded to the workload dtype.
 """
 from __future__ import annotations
 
@@ -45,3 +49,12 @@ def make_workload_inputs(wl, seed: int = 0, device: str | torch.device = "cpu"):
     """Inputs for a :class:`blocked_local_self_amd.workloads.Workload`."""
     return make_inputs(wl.B, wl.heads, wl.H, wl.W, wl.d, wl.block, wl.halo,
                        dtype=wl.dtype, seed=seed, device=device)
+
+
+def make_grad_output(B: int, heads: int, Ho: int, Wo: int, d: int, dtype: str = "bf16",
+                     seed: int = 0, device: str | torch.device = "cpu"):
+    """d loss / d out, [B, heads, Ho, Wo, d], drawn N(0, 1) and rounded to ``dtype``."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed) + 0x5EED)
+    t = torch.randn((B, heads, Ho, Wo, d), dtype=torch.float32, generator=g)
+    return t.to(dtype=torch_dtype(dtype)).to(device).contiguous()

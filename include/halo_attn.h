@@ -44,11 +44,13 @@
 #ifndef HALO_ATTN_H
 #define HALO_ATTN_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define HALO_ATTN_ABI_VERSION 1
+#define HALO_ATTN_ABI_VERSION 2
 
 typedef enum halo_dtype {
     HALO_F32 = 0,
@@ -77,7 +79,8 @@ typedef enum halo_status {
     HALO_ERR_DTYPE = -3,        /* dtype not HALO_F32 / HALO_BF16 */
     HALO_ERR_UNSUPPORTED = -4,  /* valid, but no kernel handles it */
     HALO_ERR_HIP = -5,          /* the HIP runtime reported an error */
-    HALO_ERR_ALIAS = -6         /* out overlaps an input */
+    HALO_ERR_ALIAS = -6,        /* an output overlaps an input or another output */
+    HALO_ERR_WORKSPACE = -7     /* workspace too small or misaligned */
 } halo_status;
 
 /*
@@ -103,6 +106,67 @@ int halo_attn_fwd(const void* q, const void* k, const void* v,
                   int B, int heads, int H, int W, int d,
                   int block, int halo, int query_stride,
                   float scale, int dtype, void* stream);
+
+/*
+ * Backward pass: gradients of a scalar loss with respect to q, k, v and both
+ * relative tables, given dout = d loss / d out.  The pages print no backward;
+ * HaloNet's models are trained by gradient descent (section 4.1), so this is
+ * the exact derivative of the forward definition above, with
+ * P = softmax(l) over the query's in-image window keys:
+ *   dl_j      = P_j (dout . v_j - dout . out)
+ *   dq        = scale * sum_j dl_j (k_j + rel_h[row_j] + rel_w[col_j])
+ *   dk_j, dv_j = sums over every query whose window holds key j of
+ *               scale * dl_j * q and P_j * dout
+ *   drel_h[R] = scale * sum of dl_j * q over all (query, key) pairs of all
+ *               batches and heads whose row displacement selects row R;
+ *               drel_w likewise for columns.
+ * The forward output is not an input: the softmax of every query is
+ * recomputed.
+ *
+ * Layouts and dtype: q, k, v, rel_h, rel_w as in the forward; dout has out's
+ * layout [B][heads][H/s][W/s][d]; dq, dk, dv have q's layout; all of these
+ * share `dtype`.  drel_h and drel_w are fp32 [2r-1][d] whatever the dtype
+ * (sums over the whole batch).  With query_stride s > 1, dq is zero at the
+ * pixels that are not queries.  Table rows no displacement selects get 0.
+ * All arithmetic is fp32; bf16 gradients are rounded to nearest even.
+ *
+ * Workspace: a device buffer of at least halo_attn_bwd_workspace_bytes()
+ * bytes, 16-byte aligned, owned by the caller, contents irrelevant on entry
+ * and undefined on return (per-query softmax statistics, per-block partial
+ * table gradients).  The library allocates nothing.
+ *
+ * Determinism: no floating-point atomics; every sum runs in a fixed order,
+ * so repeated calls give bitwise identical results.
+ *
+ * Errors as for the forward, plus HALO_ERR_WORKSPACE (workspace too small or
+ * misaligned) and HALO_ERR_ALIAS when any output or the workspace overlaps
+ * an input or another output.  drel_h and drel_w must be non-NULL; if a size
+ * is zero they are set to zero (the gradient of an empty sum) and no other
+ * pointer is inspected.  kernel: a halo_kernel value; only the generic
+ * kernels exist for the backward, so HALO_KERNEL_MFMA and MFMA_STRIP return
+ * HALO_ERR_UNSUPPORTED.
+ */
+int halo_attn_bwd_kernel(const void* q, const void* k, const void* v,
+                         const void* rel_h, const void* rel_w, const void* dout,
+                         void* dq, void* dk, void* dv, float* drel_h, float* drel_w,
+                         void* workspace, size_t workspace_bytes,
+                         int B, int heads, int H, int W, int d,
+                         int block, int halo, int query_stride,
+                         float scale, int dtype, int kernel, void* stream);
+
+/* halo_attn_bwd_kernel with kernel = HALO_KERNEL_AUTO. */
+int halo_attn_bwd(const void* q, const void* k, const void* v,
+                  const void* rel_h, const void* rel_w, const void* dout,
+                  void* dq, void* dk, void* dv, float* drel_h, float* drel_w,
+                  void* workspace, size_t workspace_bytes,
+                  int B, int heads, int H, int W, int d,
+                  int block, int halo, int query_stride,
+                  float scale, int dtype, void* stream);
+
+/* Host-only query: workspace bytes halo_attn_bwd needs for these sizes
+ * (0 when a size is zero), or a negative status for invalid arguments. */
+long long halo_attn_bwd_workspace_bytes(int B, int heads, int H, int W, int d,
+                                        int block, int halo, int query_stride, int dtype);
 
 /* Host-only query: the halo_kernel value AUTO would run for these
  * arguments (HALO_KERNEL_GENERIC or HALO_KERNEL_MFMA), or a negative

@@ -1,0 +1,160 @@
+"""GPU parity of the backward pass: the HIP kernels (through the C ABI)
+against the fp64 oracle's backward, on the same seeded inputs.
+
+The pages print no backward; HaloNet's models are trained by gradient
+descent ("Scaling Local Self-Attention for Parameter Efficient Visual
+Backbones", section 4.1), and the oracle's backward is pinned to finite
+differences of the forward definition.  Each gradient tensor is compared
+element by element, relative to its own largest magnitude:
+
+    max |gpu - oracle| <= TOL[dtype] * max |oracle|
+
+fp32 inputs: 1e-4 (fp32 sums of up to a few hundred terms, fast exp and
+log).  bf16 inputs: 1.5e-2, from the rounding of dq, dk, dv to bf16 (half an
+ulp, 2^-9 of the value) on top of fp32 arithmetic, with headroom for the
+cancellation in dl = P (dout.v - dout.out).  The table gradients are fp32
+for both dtypes but sum over every query of the batch; they are held to the
+same relative bound.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from blocked_local_self_amd import halo_attn_bwd, halo_attention, halo_attn_fwd, HaloError, workloads
+from blocked_local_self_amd.inputs import make_inputs, make_workload_inputs, make_grad_output
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-4, "bf16": 1.5e-2}
+DEV = "cuda"
+NAMES = ["dq", "dk", "dv", "drel_h", "drel_w"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def case(B, heads, H, W, d, block, halo, stride, dtype, seed):
+    ins = make_inputs(B, heads, H, W, d, block, halo, dtype=dtype, seed=seed)
+    g = make_grad_output(B, heads, H // stride, W // stride, d, dtype=dtype, seed=seed)
+    return ins, g
+
+
+def gpu_bwd(ins, g, block, halo, stride, kernel="auto"):
+    q, k, v, rh, rw = (t.to(DEV) for t in ins)
+    res = halo_attn_bwd(q, k, v, rh, rw, g.to(DEV), block, halo, stride, kernel=kernel)
+    torch.cuda.synchronize()
+    return [f64(t) for t in res]
+
+
+def ref_bwd(ins, g, block, halo, stride):
+    return oracle.halo_attn_bwd_ref(*(f64(t) for t in ins), f64(g), block, halo, stride)
+
+
+def compare(got, want, dtype, label=""):
+    worst = 0.0
+    for name, a, b in zip(NAMES, got, want):
+        assert a.shape == b.shape, name
+        assert np.isfinite(a).all(), f"{name}: non-finite"
+        scale = max(float(np.abs(b).max()), 1e-6)
+        rel = float(np.abs(a - b).max()) / scale
+        worst = max(worst, rel)
+        assert rel <= TOL[dtype], f"{label} {name}: max err {rel:.3e} of max |ref| {scale:.3e}"
+    return worst
+
+
+SMALL = [
+    # (B, heads, H, W, d, block, halo, stride)
+    (2, 3, 24, 24, 16, 8, 3, 1),
+    (1, 2, 24, 24, 32, 8, 3, 1),
+    (1, 2, 20, 28, 16, 8, 3, 1),    # ragged last block row and column
+    (2, 2, 24, 24, 16, 8, 3, 2),    # strided queries
+    (1, 2, 36, 36, 32, 12, 3, 1),   # 18x18 window
+    (1, 2, 32, 40, 16, 12, 3, 2),   # ragged + strided + wide window
+    (1, 2, 16, 16, 16, 4, 1, 1),
+    (1, 1, 16, 16, 16, 8, 0, 1),    # h = 0
+    (1, 2, 12, 12, 16, 16, 1, 1),   # block larger than the image
+    (1, 1, 20, 20, 16, 2, 5, 1),    # halo wider than a block: keys seen by 5x5 blocks
+    (1, 2, 9, 7, 24, 3, 1, 1),      # odd d and block
+    (1, 1, 10, 10, 64, 4, 2, 2),
+    (1, 1, 6, 6, 128, 2, 1, 1),
+]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_small_shapes_match_oracle(shape, dtype):
+    B, heads, H, W, d, block, halo, stride = shape
+    say(f"bwd case {shape} {dtype}")
+    ins, g = case(*shape, dtype, seed=sum(shape))
+    got = gpu_bwd(ins, g, block, halo, stride)
+    compare(got, ref_bwd(ins, g, block, halo, stride), dtype, str(shape))
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_workload_full_size(name):
+    wl = workloads.get(name)
+    say(f"bwd workload {name}")
+    ins = make_workload_inputs(wl, seed=0)
+    g = make_grad_output(wl.B, wl.heads, wl.Ho, wl.Wo, wl.d, dtype=wl.dtype, seed=0)
+    got = gpu_bwd(ins, g, wl.block, wl.halo, wl.stride)
+    want = ref_bwd(ins, g, wl.block, wl.halo, wl.stride)
+    worst = compare(got, want, wl.dtype, name)
+    say(f"  worst relative error {worst:.3e}")
+
+
+def test_deterministic():
+    ins, g = case(2, 4, 32, 32, 16, 8, 3, 1, "bf16", seed=21)
+    a = gpu_bwd(ins, g, 8, 3, 1)
+    b = gpu_bwd(ins, g, 8, 3, 1)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_autograd_function_matches_direct_call():
+    ins, g = case(1, 2, 24, 24, 16, 8, 3, 1, "fp32", seed=22)
+    ts = [t.to(DEV).requires_grad_(True) for t in ins]
+    out = halo_attention(*ts, 8, 3)
+    ref_out = halo_attn_fwd(*(t.detach() for t in ts), 8, 3)
+    assert torch.equal(out.detach(), ref_out)
+    out.backward(g.to(DEV))
+    direct = gpu_bwd(ins, g, 8, 3, 1)
+    for t, want in zip(ts, direct):
+        assert np.array_equal(f64(t.grad), want)
+
+
+def test_zero_output_gradient_and_constant_values():
+    ins, g = case(1, 2, 24, 24, 16, 8, 3, 1, "fp32", seed=23)
+    for x in gpu_bwd(ins, torch.zeros_like(g), 8, 3, 1):
+        assert not x.any()
+    q, k, v, rh, rw = ins
+    got = gpu_bwd((q, k, torch.full_like(v, 0.5), rh, rw), g, 8, 3, 1)
+    for name, x in zip(NAMES, got):
+        if name != "dv":
+            assert np.abs(x).max() < 1e-5, name
+
+
+def test_empty_and_errors_on_gpu():
+    q = torch.zeros(0, 2, 8, 8, 16, dtype=torch.bfloat16, device=DEV)
+    t = torch.zeros(11, 16, dtype=torch.bfloat16, device=DEV)
+    dq, dk, dv, drh, drw = halo_attn_bwd(q, q, q, t, t, q, 4, 1)
+    torch.cuda.synchronize()
+    assert dq.shape == q.shape and not drh.any() and not drw.any()
+    x = torch.zeros(1, 1, 8, 8, 16, dtype=torch.bfloat16, device=DEV)
+    small = torch.zeros(16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(ValueError):
+        halo_attn_bwd(x, x, x, t, t, x, 4, 1, workspace=small)
