@@ -36,13 +36,13 @@ def _load():
         _build()
     lib = ctypes.CDLL(LIB_PATH)
     dp = ctypes.POINTER(ctypes.c_double)
-    lib.halo_ref_fwd.argtypes = [dp, dp, dp, dp, dp, dp] + [ctypes.c_int] * 8 + [
+    lib.halo_ref_fwd.argtypes = [dp, dp, dp, dp, dp, dp, dp] + [ctypes.c_int] * 8 + [
         ctypes.c_double, ctypes.c_int]
     lib.halo_ref_fwd.restype = ctypes.c_int
     lib.halo_ref_set_attention.argtypes = [
         ctypes.c_int, ctypes.c_int, dp, ctypes.POINTER(dp), dp, ctypes.POINTER(dp),
         ctypes.c_double, dp, dp]
-    lib.halo_ref_set_attention.restype = None
+    lib.halo_ref_set_attention.restype = ctypes.c_double
     lib.halo_ref_bwd.argtypes = [dp] * 11 + [ctypes.c_int] * 8 + [ctypes.c_double, ctypes.c_int]
     lib.halo_ref_bwd.restype = ctypes.c_int
     lib.halo_ref_set_attention_bwd.argtypes = [
@@ -70,13 +70,15 @@ def max_threads() -> int:
 
 def halo_attn_ref(q, k, v, rel_h, rel_w, block: int, halo: int,
                   query_stride: int = 1, scale: float | None = None,
-                  threads: int = 0) -> np.ndarray:
+                  threads: int = 0, return_lse: bool = False):
     """Forward pass, fp64.
 
     q, k, v: [B, heads, H, W, d]; rel_h, rel_w: [2*(block+2*halo)-1, d].
     Inputs are converted exactly to float64 (fp32 and bf16 values are exact
     in fp64).  Returns [B, heads, H/s, W/s, d] float64.
     ``scale=None`` means d**-0.5, the value the HaloAttention module uses.
+    With ``return_lse`` also returns lse [B, heads, H/s, W/s]: per query,
+    log sum_j exp(l_j) over its window keys (the log softmax normaliser).
     """
     q, k, v, rel_h, rel_w = (_f64(t) for t in (q, k, v, rel_h, rel_w))
     _check(q, k, v, rel_h, rel_w, block, halo, query_stride)
@@ -85,11 +87,13 @@ def halo_attn_ref(q, k, v, rel_h, rel_w, block: int, halo: int,
     if scale is None:
         scale = float(d) ** -0.5
     out = np.zeros((B, heads, H // s, W // s, d), dtype=np.float64)
+    lse = np.zeros((B, heads, H // s, W // s), dtype=np.float64) if return_lse else None
     rc = _load().halo_ref_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(rel_h), _ptr(rel_w), _ptr(out),
+                              _ptr(lse) if return_lse else None,
                               B, heads, H, W, d, block, halo, s, float(scale), int(threads))
     if rc != 0:
         raise ValueError(f"halo_ref_fwd failed with status {rc}")
-    return out
+    return (out, lse) if return_lse else out
 
 
 def _check(q, k, v, rel_h, rel_w, block, halo, query_stride):

@@ -66,8 +66,9 @@ static double dot(const double* a, const double* b, int d)
  * keys/vals are arrays of nkeys pointers to d-vectors; bias has nkeys
  * entries; logits is caller scratch of nkeys doubles.  The max is subtracted
  * before exponentiation (the result is unchanged by it).  nkeys must be >= 1.
+ * Returns log(sum_j exp(l_j)), the log of the softmax normaliser.
  */
-void halo_ref_set_attention(int d, int nkeys, const double* q,
+double halo_ref_set_attention(int d, int nkeys, const double* q,
                             const double* const* keys, const double* bias,
                             const double* const* vals, double scale,
                             double* out, double* logits)
@@ -87,6 +88,7 @@ void halo_ref_set_attention(int d, int nkeys, const double* q,
         const double p = logits[j] / z;
         for (int c = 0; c < d; ++c) out[c] += p * vals[j][c];
     }
+    return m + log(z);
 }
 
 /* Same argument checks as the library's entry point; returns 0 or -2. */
@@ -100,12 +102,14 @@ static int check_shape(int B, int heads, int H, int W, int d, int block,
 }
 
 /*
- * Whole forward pass.  nthreads <= 0 means the OpenMP default.
+ * Whole forward pass.  nthreads <= 0 means the OpenMP default.  lse may be
+ * NULL; otherwise it receives, per query ([B][heads][H/s][W/s]), the log of
+ * its softmax normaliser, log sum_j exp(l_j) over its window keys.
  * Returns 0 on success, -1 on a null pointer, -2 on a bad shape,
  * -3 when scratch memory cannot be allocated.
  */
 int halo_ref_fwd(const double* q, const double* k, const double* v,
-                 const double* rel_h, const double* rel_w, double* out,
+                 const double* rel_h, const double* rel_w, double* out, double* lse,
                  int B, int heads, int H, int W, int d,
                  int block, int halo, int stride, double scale, int nthreads)
 {
@@ -174,8 +178,9 @@ int halo_ref_fwd(const double* q, const double* k, const double* v,
                     }
                 }
                 /* n >= 1: the query pixel lies inside its own window */
-                halo_ref_set_attention(d, n, qv, tk, tb, tv, scale,
-                                       os + ((long)yo * Wo + xo) * d, tl);
+                const double z = halo_ref_set_attention(d, n, qv, tk, tb, tv, scale,
+                                                        os + ((long)yo * Wo + xo) * d, tl);
+                if (lse) lse[sl * (long)Ho * Wo + (long)yo * Wo + xo] = z;
             }
         }
     }

@@ -97,3 +97,27 @@ def halo_attn_dense_torch(q, k, v, rel_h, rel_w, block, halo, stride=1, scale=No
             per_head.append((w @ Vs).reshape(H // stride, W // stride, d))
         outs.append(torch.stack(per_head))
     return torch.stack(outs)
+
+
+def halo_lse_dense(q, k, rel_h, rel_w, block, halo, stride=1, scale=None):
+    """Per-query log softmax normaliser, dense formulation (float64)."""
+    q, k, rel_h, rel_w = (np.asarray(t, dtype=np.float64) for t in (q, k, rel_h, rel_w))
+    B, heads, H, W, d = q.shape
+    if scale is None:
+        scale = d ** -0.5
+    member, row_h, row_w, qy, qx = window_mask_and_index(H, W, block, halo, stride)
+    nrows = rel_h.shape[0]
+    safe_h = np.clip(row_h, 0, nrows - 1)
+    safe_w = np.clip(row_w, 0, nrows - 1)
+    out = np.zeros((B, heads, H // stride, W // stride))
+    for n in range(B):
+        for hd in range(heads):
+            Qs = q[n, hd][qy, qx]
+            Ks = k[n, hd].reshape(-1, d)
+            pidx = np.arange(Qs.shape[0])[:, None]
+            bias = (Qs @ rel_h.T)[pidx, safe_h] + (Qs @ rel_w.T)[pidx, safe_w]
+            logits = np.where(member, scale * (Qs @ Ks.T + bias), -np.inf)
+            m = logits.max(axis=1, keepdims=True)
+            lse = m[:, 0] + np.log(np.exp(logits - m).sum(axis=1))
+            out[n, hd] = lse.reshape(H // stride, W // stride)
+    return out

@@ -16,7 +16,7 @@ import pytest
 import torch
 
 import oracle
-from tests.dense_bruteforce import halo_attn_dense
+from tests.dense_bruteforce import halo_attn_dense, halo_lse_dense
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -61,6 +61,27 @@ def test_p1_oracle_matches_dense_bruteforce(H, W, d, block, halo, stride):
     want = halo_attn_dense(q, k, v, rh, rw, block, halo, stride)
     assert got.shape == want.shape == (2, 2, H // stride, W // stride, d)
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("H,W,d,block,halo,stride", P1_CASES[:8])
+def test_p1_lse_matches_dense_bruteforce(H, W, d, block, halo, stride):
+    q, k, v, rh, rw = case(2, 2, H, W, d, block, halo, seed=H * 10 + W)
+    out, lse = oracle.halo_attn_ref(q, k, v, rh, rw, block, halo, stride, return_lse=True)
+    np.testing.assert_allclose(lse, halo_lse_dense(q, k, rh, rw, block, halo, stride), rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(out, oracle.halo_attn_ref(q, k, v, rh, rw, block, halo, stride))
+
+
+def test_p1_lse_of_zero_logits_counts_the_in_image_window():
+    # q = 0: every logit is 0, so exp(lse) is the number of in-image window keys
+    H = W = 10; block, halo = 4, 2
+    q, k, v, rh, rw = case(1, 1, H, W, 3, block, halo, seed=4)
+    _, lse = oracle.halo_attn_ref(np.zeros_like(q), k, v, rh, rw, block, halo, return_lse=True)
+    r = block + 2 * halo
+    for y in range(H):
+        for x in range(W):
+            y0, x0 = (y // block) * block - halo, (x // block) * block - halo
+            n = (min(H, y0 + r) - max(0, y0)) * (min(W, x0 + r) - max(0, x0))
+            assert abs(lse[0, 0, y, x] - np.log(n)) < 1e-13
 
 
 def test_p1_negative_control_wrong_offset_is_detected():
