@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
-"""Benchmark: halo-attention forward on one MI355X.
+"""Benchmark: halo-attention forward (default) or backward on one MI355X.
 
 One step = one halo_attn_fwd launch over one full batch of the workload (all
-of the method's steps run inside that launch).  Inputs are seeded synthetic
+of the method's steps run inside that launch); with --pass bwd, one
+halo_attn_bwd call (all of its kernels) over one full batch.  Inputs are seeded synthetic
 tensors already resident in HBM; several independent input/output sets are
 rotated so the working set exceeds the 256 MB Infinity Cache and every step
 reads HBM.  Prints ONE JSON line (rank 0):
@@ -13,6 +14,12 @@ reads HBM.  Prints ONE JSON line (rank 0):
              measured with HIP events on the launch stream
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
              workload on this host (reported, not a target)
+
+Backward accounting (--pass bwd): F = 10*d*r^2 per (query, head), the five
+window contractions q.k (recomputed), dout.v, dl.k, dl.q, p.dout; algorithmic
+bytes = e*d*B*heads*(2*(H/s)*(W/s) + 5*H*W): q and dout once at query
+pixels, k and v once, dq, dk, dv written once.  The roofline entry then
+covers the whole backward call (its mean time over the timed region).
 """
 from __future__ import annotations
 
@@ -26,6 +33,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
 METRIC = "halo-attn fwd TFLOP/s + tokens/s per MI355X; % of MFMA/HBM roofline"
+METRIC_BWD = "halo-attn bwd TFLOP/s + tokens/s per MI355X; % of MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MALL_BYTES = 256 * 2 ** 20     # Infinity Cache
 
@@ -66,6 +74,8 @@ def parse():
                     help="untimed launches first (the GPU clocks need ~0.1 s of load to ramp up)")
     ap.add_argument("--workload", default=None, help="workload name (default: the early-stage shape)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "generic", "mfma"])
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
+                    help="forward (the headline) or backward pass")
     ap.add_argument("--sets", type=int, default=0, help="rotated input sets (0: enough to exceed the MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU-oracle sample time")
@@ -87,7 +97,15 @@ def copy_calibration(mib, steps):
                                            "copies": steps}}), flush=True)
 
 
-def cpu_baseline(wl, inputs_cpu, target_s):
+def bwd_flops(wl):
+    return 10 * wl.d * wl.r * wl.r * wl.B * wl.heads * wl.Ho * wl.Wo
+
+
+def bwd_alg_bytes(wl):
+    return wl.elem_bytes * wl.d * wl.B * wl.heads * (2 * wl.Ho * wl.Wo + 5 * wl.H * wl.W)
+
+
+def cpu_baseline(wl, inputs_cpu, target_s, dout_cpu=None):
     """Time the fp64 oracle on whole (batch, head) slices of the workload.
 
     The sample grows (more slices, then repeated passes over all of them)
@@ -95,16 +113,21 @@ def cpu_baseline(wl, inputs_cpu, target_s):
     """
     import numpy as np
     import oracle
-    q, k, v, rh, rw = (t.to(dtype=__import__("torch").float64).numpy() for t in inputs_cpu)
+    f64 = lambda t: t.to(dtype=__import__("torch").float64).numpy()
+    q, k, v, rh, rw = (f64(t) for t in inputs_cpu)
+    g = f64(dout_cpu) if dout_cpu is not None else None
     threads = oracle.max_threads()
     nslices = wl.B * wl.heads
-    per_slice_flops = wl.flops / nslices
+    per_slice_flops = (wl.flops if g is None else bwd_flops(wl)) / nslices
 
     def run(nsl):
         sl = lambda a: np.ascontiguousarray(a.reshape(nslices, 1, *a.shape[2:])[:nsl])
         args = [sl(q), sl(k), sl(v)]
         t0 = time.perf_counter()
-        oracle.halo_attn_ref(*args, rh, rw, wl.block, wl.halo, wl.stride, threads=threads)
+        if g is None:
+            oracle.halo_attn_ref(*args, rh, rw, wl.block, wl.halo, wl.stride, threads=threads)
+        else:
+            oracle.halo_attn_bwd_ref(*args, rh, rw, sl(g), wl.block, wl.halo, wl.stride, threads=threads)
         return time.perf_counter() - t0
 
     n = min(threads, nslices)
@@ -122,7 +145,8 @@ def cpu_baseline(wl, inputs_cpu, target_s):
     tokens = wl.tokens * n * passes / nslices   # token = output position with all heads
     what = f"{n} of {nslices} (batch, head) slices" if n < nslices else f"all {nslices} (batch, head) slices"
     return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{what} of {wl.name} x {passes} pass(es), fp64, {t:.2f} s",
+            "sample": f"{what} of {wl.name} x {passes} pass(es), {'backward' if g is not None else 'forward'}, "
+                      f"fp64, {t:.2f} s",
             "seconds": round(t, 3), "tokens_per_s": round(tokens / t, 1)}
 
 
@@ -136,30 +160,47 @@ def main():
         copy_calibration(args.copy_calibration, args.steps)
         return
     import torch
-    from blocked_local_self_amd import halo_attn_fwd, workloads
-    from blocked_local_self_amd.inputs import make_workload_inputs
+    from blocked_local_self_amd import halo_attn_fwd, halo_attn_bwd, bwd_workspace_bytes, workloads
+    from blocked_local_self_amd.inputs import make_workload_inputs, make_grad_output
 
     wl = workloads.get(args.workload or workloads.BENCH_WORKLOAD)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     in_bytes = 3 * wl.elem_bytes * wl.B * wl.heads * wl.H * wl.W * wl.d
     out_bytes = wl.elem_bytes * wl.B * wl.heads * wl.Ho * wl.Wo * wl.d
-    nsets = args.sets or max(2, -(-2 * MALL_BYTES // (in_bytes + out_bytes)))
+    bwd = args.which == "bwd"
+    per_set = in_bytes + out_bytes if not bwd else 2 * in_bytes + 2 * out_bytes
+    nsets = args.sets or max(2, -(-2 * MALL_BYTES // per_set))
     sets = []
-    inputs0_cpu = None
+    inputs0_cpu = dout0_cpu = None
     for s in range(nsets):
         cpu = make_workload_inputs(wl, seed=s)
         if s == 0:
             inputs0_cpu = cpu
         dev_t = tuple(t.to(dev) for t in cpu)
-        out = torch.empty(wl.out_shape(), dtype=dev_t[0].dtype, device=dev)
-        sets.append((dev_t, out))
+        if bwd:
+            g_cpu = make_grad_output(wl.B, wl.heads, wl.Ho, wl.Wo, wl.d, dtype=wl.dtype, seed=s)
+            if s == 0:
+                dout0_cpu = g_cpu
+            sets.append((dev_t, g_cpu.to(dev)))
+        else:
+            sets.append((dev_t, torch.empty(wl.out_shape(), dtype=dev_t[0].dtype, device=dev)))
     stream = torch.cuda.current_stream(dev)
+    ws = None
+    if bwd:
+        nws = bwd_workspace_bytes(wl.B, wl.heads, wl.H, wl.W, wl.d, wl.block, wl.halo, wl.stride, wl.dtype)
+        ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
+        grads = tuple(torch.empty(wl.shape(), dtype=sets[0][0][0].dtype, device=dev) for _ in range(3)) + \
+            tuple(torch.empty((2 * wl.r - 1, wl.d), dtype=torch.float32, device=dev) for _ in range(2))
 
     def step(i):
-        (q, k, v, rh, rw), out = sets[i % nsets]
-        halo_attn_fwd(q, k, v, rh, rw, wl.block, wl.halo, wl.stride, out=out, kernel=args.kernel,
-                      stream=stream)
+        (q, k, v, rh, rw), x = sets[i % nsets]
+        if bwd:
+            halo_attn_bwd(q, k, v, rh, rw, x, wl.block, wl.halo, wl.stride, kernel=args.kernel,
+                          workspace=ws, grads=grads, stream=stream)
+        else:
+            halo_attn_fwd(q, k, v, rh, rw, wl.block, wl.halo, wl.stride, out=x, kernel=args.kernel,
+                          stream=stream)
 
     for i in range(args.warmup):
         step(i)
@@ -175,15 +216,17 @@ def main():
     wall = time.perf_counter() - t0
     gpu_ms = ev0.elapsed_time(ev1)
     ms = gpu_ms / args.steps
-    tflops = wl.flops / (ms * 1e-3) / 1e12
-    achieved_gbs = wl.alg_bytes / (ms * 1e-3) / 1e9
+    flops = bwd_flops(wl) if bwd else wl.flops
+    alg_bytes = bwd_alg_bytes(wl) if bwd else wl.alg_bytes
+    tflops = flops / (ms * 1e-3) / 1e12
+    achieved_gbs = alg_bytes / (ms * 1e-3) / 1e9
 
     src_hash = kernel_source_hash()
-    rec = MEASURED_TRAFFIC.get(wl.name)
+    rec = None if bwd else MEASURED_TRAFFIC.get(wl.name)
     traffic = rec["bytes_per_launch"] if rec and rec["sources"] == src_hash else None
 
     line = {
-        "metric": METRIC,
+        "metric": METRIC_BWD if bwd else METRIC,
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -195,7 +238,7 @@ def main():
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic",
-        "config": {**wl.describe(), "kernel": args.kernel, "rotated_input_sets": nsets},
+        "config": {**wl.describe(), "pass": args.which, "kernel": args.kernel, "rotated_input_sets": nsets},
         "tokens_per_s": round(wl.tokens / (ms * 1e-3), 1),
         "wall_s_timed_region": round(wall, 4),
         "roofline": {
@@ -205,13 +248,13 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "alg_bytes_per_launch": wl.alg_bytes,
+            "alg_bytes_per_launch": alg_bytes,
             "mean_launch_us": round(ms * 1e3, 3),
             "kernel_sources": src_hash,
         },
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, inputs0_cpu, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(wl, inputs0_cpu, args.cpu_seconds, dout0_cpu)
     print(json.dumps(line), flush=True)
 
 

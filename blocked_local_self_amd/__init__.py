@@ -71,7 +71,8 @@ def _check_inputs(q, k, v, rel_h, rel_w, block, halo, query_stride, **extra):
 
 
 def halo_attn_fwd(q, k, v, rel_h, rel_w, block: int, halo: int, query_stride: int = 1,
-                  scale: float | None = None, out=None, kernel: str = "auto", stream=None):
+                  scale: float | None = None, out=None, kernel: str = "auto", stream=None,
+                  return_lse: bool = False):
     """Halo attention forward.
 
     q, k, v: [B, heads, H, W, d] contiguous CUDA(HIP) tensors, float32 or bfloat16.
@@ -79,6 +80,8 @@ def halo_attn_fwd(q, k, v, rel_h, rel_w, block: int, halo: int, query_stride: in
     Returns out [B, heads, H/s, W/s, d] (allocated unless ``out`` is given).
     ``scale=None`` means d**-0.5.  ``kernel`` in {"auto", "generic", "mfma", "mfma_strip"}.
     ``stream``: a torch.cuda.Stream (default: the current stream).
+    ``return_lse``: also return lse [B, heads, H/s, W/s] float32, the natural
+    log of each query's softmax normaliser (what ``halo_attn_bwd`` reuses).
     """
     import torch
     B, heads, H, W, d = _check_inputs(q, k, v, rel_h, rel_w, block, halo, query_stride)
@@ -95,14 +98,15 @@ def halo_attn_fwd(q, k, v, rel_h, rel_w, block: int, halo: int, query_stride: in
         raise ValueError(f"kernel must be one of {sorted(KERNELS)}")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    lse = torch.empty(oshape[:4], dtype=torch.float32, device=q.device) if return_lse else None
     lib = _native.load()
     with torch.cuda.device(q.device):
-        st = lib.halo_attn_fwd_kernel(q.data_ptr(), k.data_ptr(), v.data_ptr(), rel_h.data_ptr(),
-                                      rel_w.data_ptr(), out.data_ptr(), B, heads, H, W, d, block,
-                                      halo, s, float(scale), _dtype_code(q), KERNELS[kernel],
-                                      stream.cuda_stream)
+        st = lib.halo_attn_fwd_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), rel_h.data_ptr(),
+                                   rel_w.data_ptr(), out.data_ptr(), lse.data_ptr() if return_lse else None,
+                                   B, heads, H, W, d, block, halo, s, float(scale), _dtype_code(q),
+                                   KERNELS[kernel], stream.cuda_stream)
     _native.check(st)
-    return out
+    return (out, lse) if return_lse else out
 
 
 def bwd_workspace_bytes(B: int, heads: int, H: int, W: int, d: int, block: int, halo: int,
@@ -116,7 +120,8 @@ def bwd_workspace_bytes(B: int, heads: int, H: int, W: int, d: int, block: int, 
 
 
 def halo_attn_bwd(q, k, v, rel_h, rel_w, dout, block: int, halo: int, query_stride: int = 1,
-                  scale: float | None = None, kernel: str = "auto", workspace=None, stream=None):
+                  scale: float | None = None, out=None, lse=None, kernel: str = "auto",
+                  workspace=None, grads=None, stream=None):
     """Halo attention backward: gradients given dout = d loss / d out.
 
     Same tensors and arguments as ``halo_attn_fwd`` plus ``dout``
@@ -124,6 +129,9 @@ def halo_attn_bwd(q, k, v, rel_h, rel_w, dout, block: int, halo: int, query_stri
     dq, dk, dv in q's dtype and layout, drel_h and drel_w float32 [2r-1, d].
     ``workspace``: optional uint8 CUDA tensor of at least
     ``bwd_workspace_bytes(...)`` bytes (allocated here when None).
+    ``out``, ``lse``: the forward's output and log normalisers
+    (``halo_attn_fwd(..., return_lse=True)``), or both None to recompute them.
+    ``grads``: optional preallocated (dq, dk, dv, drel_h, drel_w) to write into.
     """
     import torch
     B, heads, H, W, d = _check_inputs(q, k, v, rel_h, rel_w, block, halo, query_stride, dout=dout)
@@ -131,6 +139,15 @@ def halo_attn_bwd(q, k, v, rel_h, rel_w, dout, block: int, halo: int, query_stri
     oshape = (B, heads, H // s, W // s, d)
     if tuple(dout.shape) != oshape:
         raise ValueError(f"dout must be {oshape}; got {tuple(dout.shape)}")
+    if (out is None) != (lse is None):
+        raise ValueError("pass both out and lse from the forward, or neither")
+    if out is not None:
+        if (tuple(out.shape) != oshape or out.dtype != q.dtype or out.device != q.device
+                or not out.is_contiguous()):
+            raise ValueError(f"out must be a contiguous {oshape} {q.dtype} tensor on {q.device}")
+        if (tuple(lse.shape) != oshape[:4] or lse.dtype != torch.float32 or lse.device != q.device
+                or not lse.is_contiguous()):
+            raise ValueError(f"lse must be a contiguous float32 {oshape[:4]} tensor on {q.device}")
     if scale is None:
         scale = float(d) ** -0.5
     if kernel not in KERNELS:
@@ -142,16 +159,28 @@ def halo_attn_bwd(q, k, v, rel_h, rel_w, dout, block: int, halo: int, query_stri
     elif (workspace.device != q.device or not workspace.is_contiguous()
           or workspace.numel() * workspace.element_size() < need):
         raise ValueError(f"workspace must be a contiguous tensor of >= {need} bytes on {q.device}")
-    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     r = block + 2 * halo
-    drh = torch.empty((2 * r - 1, d), dtype=torch.float32, device=q.device)
-    drw = torch.empty_like(drh)
+    if grads is None:
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        drh = torch.empty((2 * r - 1, d), dtype=torch.float32, device=q.device)
+        drw = torch.empty_like(drh)
+    else:
+        dq, dk, dv, drh, drw = grads
+        for t, like in ((dq, q), (dk, q), (dv, q)):
+            if t.shape != like.shape or t.dtype != like.dtype or t.device != q.device or not t.is_contiguous():
+                raise ValueError("dq, dk, dv must be contiguous tensors like q")
+        for t in (drh, drw):
+            if (tuple(t.shape) != (2 * r - 1, d) or t.dtype != torch.float32 or t.device != q.device
+                    or not t.is_contiguous()):
+                raise ValueError(f"drel_h, drel_w must be contiguous float32 {(2 * r - 1, d)} tensors")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     lib = _native.load()
     with torch.cuda.device(q.device):
         st = lib.halo_attn_bwd_kernel(q.data_ptr(), k.data_ptr(), v.data_ptr(), rel_h.data_ptr(),
-                                      rel_w.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                      rel_w.data_ptr(), out.data_ptr() if out is not None else None,
+                                      dout.data_ptr(), lse.data_ptr() if lse is not None else None,
+                                      dq.data_ptr(), dk.data_ptr(),
                                       dv.data_ptr(), drh.data_ptr(), drw.data_ptr(), workspace.data_ptr(),
                                       workspace.numel() * workspace.element_size(), B, heads, H, W, d,
                                       block, halo, s, float(scale), _dtype_code(q), KERNELS[kernel],
@@ -168,16 +197,18 @@ def _make_function():
 
         @staticmethod
         def forward(ctx, q, k, v, rel_h, rel_w, block, halo, query_stride, scale):
-            ctx.save_for_backward(q, k, v, rel_h, rel_w)
+            out, lse = halo_attn_fwd(q, k, v, rel_h, rel_w, block, halo, query_stride, scale=scale,
+                                     return_lse=True)
+            ctx.save_for_backward(q, k, v, rel_h, rel_w, out, lse)
             ctx.cfg = (block, halo, query_stride, scale)
-            return halo_attn_fwd(q, k, v, rel_h, rel_w, block, halo, query_stride, scale=scale)
+            return out
 
         @staticmethod
         def backward(ctx, dout):
-            q, k, v, rel_h, rel_w = ctx.saved_tensors
+            q, k, v, rel_h, rel_w, out, lse = ctx.saved_tensors
             block, halo, s, scale = ctx.cfg
             dq, dk, dv, drh, drw = halo_attn_bwd(q, k, v, rel_h, rel_w, dout.contiguous(), block, halo,
-                                                 s, scale=scale)
+                                                 s, scale=scale, out=out, lse=lse)
             return dq, dk, dv, drh.to(rel_h.dtype), drw.to(rel_w.dtype), None, None, None, None
 
     return HaloAttentionFunction

@@ -43,9 +43,11 @@ def load() -> ctypes.CDLL:
     lib.halo_attn_fwd_kernel.argtypes = [vp] * 6 + [i] * 8 + [f, i, i, vp]
     lib.halo_attn_fwd_kernel.restype = i
     sz = ctypes.c_size_t
-    lib.halo_attn_bwd_kernel.argtypes = [vp] * 12 + [sz] + [i] * 8 + [f, i, i, vp]
+    lib.halo_attn_fwd_lse.argtypes = [vp] * 7 + [i] * 8 + [f, i, i, vp]
+    lib.halo_attn_fwd_lse.restype = i
+    lib.halo_attn_bwd_kernel.argtypes = [vp] * 14 + [sz] + [i] * 8 + [f, i, i, vp]
     lib.halo_attn_bwd_kernel.restype = i
-    lib.halo_attn_bwd.argtypes = [vp] * 12 + [sz] + [i] * 8 + [f, i, vp]
+    lib.halo_attn_bwd.argtypes = [vp] * 14 + [sz] + [i] * 8 + [f, i, vp]
     lib.halo_attn_bwd.restype = i
     lib.halo_attn_bwd_workspace_bytes.argtypes = [i] * 9
     lib.halo_attn_bwd_workspace_bytes.restype = ctypes.c_longlong

@@ -11,13 +11,15 @@
 
 namespace halo {
 hipError_t launch_generic(const void* q, const void* k, const void* v, const void* rh,
-                          const void* rw, void* out, const Geometry& g, bool bf16, hipStream_t st);
+                          const void* rw, void* out, float* lse, const Geometry& g, bool bf16, hipStream_t st);
 bool mfma_supported(int d, int r, int block, int stride, bool bf16);
 hipError_t launch_mfma(const void* q, const void* k, const void* v, const void* rh,
-                       const void* rw, void* out, const Geometry& g, bool force_strip, hipStream_t st);
+                       const void* rw, void* out, float* lse, const Geometry& g, bool force_strip,
+                       hipStream_t st);
 int64_t bwd_generic_workspace_floats(const Geometry& g);
 hipError_t launch_bwd_generic(const void* q, const void* k, const void* v, const void* rh, const void* rw,
-                              const void* dout, void* dq, void* dk, void* dv, float* drh, float* drw,
+                              const void* out, const void* dout, const float* lse,
+                              void* dq, void* dk, void* dv, float* drh, float* drw,
                               void* ws, const Geometry& g, bool bf16, hipStream_t st);
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t st);
 }  // namespace halo
@@ -115,11 +117,11 @@ int check_sizes(int B, int heads, int H, int W, int d, int block, int halo, int 
 
 extern "C" {
 
-int halo_attn_fwd_kernel(const void* q, const void* k, const void* v,
-                         const void* rel_h, const void* rel_w, void* out,
-                         int B, int heads, int H, int W, int d,
-                         int block, int halo, int query_stride,
-                         float scale, int dtype, int kernel, void* stream)
+int halo_attn_fwd_lse(const void* q, const void* k, const void* v,
+                      const void* rel_h, const void* rel_w, void* out, float* lse,
+                      int B, int heads, int H, int W, int d,
+                      int block, int halo, int query_stride,
+                      float scale, int dtype, int kernel, void* stream)
 {
     g_err[0] = 0;
     if (kernel != HALO_KERNEL_AUTO && kernel != HALO_KERNEL_GENERIC && kernel != HALO_KERNEL_MFMA &&
@@ -133,6 +135,7 @@ int halo_attn_fwd_kernel(const void* q, const void* k, const void* v,
 
     if (!q || !k || !v || !rel_h || !rel_w || !out)
         return fail(HALO_ERR_NULL, "null pointer among q, k, v, rel_h, rel_w, out");
+    const size_t nq = (size_t)(g.BH * g.Ho * g.Wo);
 
     const int r = g.r;
     const size_t esz = dtype == HALO_BF16 ? 2 : 4;
@@ -143,6 +146,10 @@ int halo_attn_fwd_kernel(const void* q, const void* k, const void* v,
         overlaps(out, out_bytes, v, in_bytes) || overlaps(out, out_bytes, rel_h, tab_bytes) ||
         overlaps(out, out_bytes, rel_w, tab_bytes))
         return fail(HALO_ERR_ALIAS, "out overlaps an input tensor");
+    if (lse && (overlaps(lse, nq * 4, q, in_bytes) || overlaps(lse, nq * 4, k, in_bytes) ||
+                overlaps(lse, nq * 4, v, in_bytes) || overlaps(lse, nq * 4, rel_h, tab_bytes) ||
+                overlaps(lse, nq * 4, rel_w, tab_bytes) || overlaps(lse, nq * 4, out, out_bytes)))
+        return fail(HALO_ERR_ALIAS, "lse overlaps an input tensor or out");
 
     const bool bf16 = dtype == HALO_BF16;
     const bool mfma_ok = halo::mfma_supported(d, r, block, query_stride, bf16);
@@ -154,12 +161,22 @@ int halo_attn_fwd_kernel(const void* q, const void* k, const void* v,
     hipStream_t s = (hipStream_t)stream;
     const bool use_mfma = kernel == HALO_KERNEL_MFMA || kernel == HALO_KERNEL_MFMA_STRIP ||
                           (kernel == HALO_KERNEL_AUTO && mfma_ok);
-    const hipError_t e = use_mfma ? halo::launch_mfma(q, k, v, rel_h, rel_w, out, g,
+    const hipError_t e = use_mfma ? halo::launch_mfma(q, k, v, rel_h, rel_w, out, lse, g,
                                                       kernel == HALO_KERNEL_MFMA_STRIP, s)
-                                  : halo::launch_generic(q, k, v, rel_h, rel_w, out, g, bf16, s);
+                                  : halo::launch_generic(q, k, v, rel_h, rel_w, out, lse, g, bf16, s);
     if (e != hipSuccess)
         return fail(HALO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return HALO_OK;
+}
+
+int halo_attn_fwd_kernel(const void* q, const void* k, const void* v,
+                         const void* rel_h, const void* rel_w, void* out,
+                         int B, int heads, int H, int W, int d,
+                         int block, int halo, int query_stride,
+                         float scale, int dtype, int kernel, void* stream)
+{
+    return halo_attn_fwd_lse(q, k, v, rel_h, rel_w, out, nullptr, B, heads, H, W, d, block, halo,
+                             query_stride, scale, dtype, kernel, stream);
 }
 
 int halo_attn_fwd(const void* q, const void* k, const void* v,
@@ -185,7 +202,8 @@ long long halo_attn_bwd_workspace_bytes(int B, int heads, int H, int W, int d,
 }
 
 int halo_attn_bwd_kernel(const void* q, const void* k, const void* v,
-                         const void* rel_h, const void* rel_w, const void* dout,
+                         const void* rel_h, const void* rel_w,
+                         const void* out, const void* dout, const float* lse,
                          void* dq, void* dk, void* dv, float* drel_h, float* drel_w,
                          void* workspace, size_t workspace_bytes,
                          int B, int heads, int H, int W, int d,
@@ -214,6 +232,8 @@ int halo_attn_bwd_kernel(const void* q, const void* k, const void* v,
     }
     if (!q || !k || !v || !rel_h || !rel_w || !dout || !dq || !dk || !dv || !workspace)
         return fail(HALO_ERR_NULL, "null pointer among q, k, v, rel_h, rel_w, dout, dq, dk, dv, workspace");
+    if ((out == nullptr) != (lse == nullptr))
+        return fail(HALO_ERR_NULL, "pass both out and lse from the forward, or neither");
     const size_t need = (size_t)halo::bwd_generic_workspace_floats(g) * 4;
     if (workspace_bytes < need)
         return fail(HALO_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu this call needs",
@@ -225,12 +245,14 @@ int halo_attn_bwd_kernel(const void* q, const void* k, const void* v,
     const size_t in_bytes = (size_t)(g.BH * H * W * d) * esz;
     const size_t tab_bytes = tabf * esz;
     const size_t out_bytes = (size_t)(g.BH * g.Ho * g.Wo * d) * esz;
-    const void* ins[6] = {q, k, v, rel_h, rel_w, dout};
-    const size_t insz[6] = {in_bytes, in_bytes, in_bytes, tab_bytes, tab_bytes, out_bytes};
+    const size_t nq = (size_t)(g.BH * g.Ho * g.Wo);
+    const void* ins[8] = {q, k, v, rel_h, rel_w, dout, out, lse};
+    const size_t insz[8] = {in_bytes, in_bytes, in_bytes, tab_bytes, tab_bytes, out_bytes,
+                            out ? out_bytes : 0, lse ? nq * 4 : 0};
     const void* outs[6] = {dq, dk, dv, drel_h, drel_w, workspace};
     const size_t outsz[6] = {in_bytes, in_bytes, in_bytes, tabf * 4, tabf * 4, need};
     for (int a = 0; a < 6; ++a) {
-        for (int b = 0; b < 6; ++b)
+        for (int b = 0; b < 8; ++b)
             if (overlaps(outs[a], outsz[a], ins[b], insz[b]))
                 return fail(HALO_ERR_ALIAS, "an output or the workspace overlaps an input tensor");
         for (int b = a + 1; b < 6; ++b)
@@ -240,22 +262,23 @@ int halo_attn_bwd_kernel(const void* q, const void* k, const void* v,
     if (kernel == HALO_KERNEL_MFMA || kernel == HALO_KERNEL_MFMA_STRIP)
         return fail(HALO_ERR_UNSUPPORTED, "no matrix-core backward kernel for these arguments");
 
-    const hipError_t e = halo::launch_bwd_generic(q, k, v, rel_h, rel_w, dout, dq, dk, dv, drel_h, drel_w,
-                                                  workspace, g, dtype == HALO_BF16, s);
+    const hipError_t e = halo::launch_bwd_generic(q, k, v, rel_h, rel_w, out, dout, lse, dq, dk, dv, drel_h,
+                                                  drel_w, workspace, g, dtype == HALO_BF16, s);
     if (e != hipSuccess)
         return fail(HALO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return HALO_OK;
 }
 
 int halo_attn_bwd(const void* q, const void* k, const void* v,
-                  const void* rel_h, const void* rel_w, const void* dout,
+                  const void* rel_h, const void* rel_w,
+                  const void* out, const void* dout, const float* lse,
                   void* dq, void* dk, void* dv, float* drel_h, float* drel_w,
                   void* workspace, size_t workspace_bytes,
                   int B, int heads, int H, int W, int d,
                   int block, int halo, int query_stride,
                   float scale, int dtype, void* stream)
 {
-    return halo_attn_bwd_kernel(q, k, v, rel_h, rel_w, dout, dq, dk, dv, drel_h, drel_w, workspace,
+    return halo_attn_bwd_kernel(q, k, v, rel_h, rel_w, out, dout, lse, dq, dk, dv, drel_h, drel_w, workspace,
                                 workspace_bytes, B, heads, H, W, d, block, halo, query_stride, scale,
                                 dtype, HALO_KERNEL_AUTO, stream);
 }

@@ -355,6 +355,32 @@ void bwd_rel_final_kernel(const float* __restrict__ in, float* __restrict__ drh,
     else drw[e - half] = acc;
 }
 
+// D = dout . out per query, from the forward's output (n queries of d channels).
+template <typename T>
+__global__ __launch_bounds__(256)
+void bwd_dsum_kernel(const T* __restrict__ out, const T* __restrict__ dout, float* __restrict__ dsum,
+                     int64_t n, int d)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        float acc = 0.f;
+        for (int c = 0; c < d; ++c) acc += to_f32(out[i * d + c]) * to_f32(dout[i * d + c]);
+        dsum[i] = acc;
+    }
+}
+
+hipError_t launch_dsum(const void* out, const void* dout, float* dsum, const Geometry& g, bool bf16, hipStream_t st)
+{
+    const int64_t n = g.BH * g.Ho * g.Wo;
+    const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 65536));
+    if (bf16)
+        hipLaunchKernelGGL(bwd_dsum_kernel<__bf16>, dim3((unsigned)blocks), dim3(256), 0, st,
+                           (const __bf16*)out, (const __bf16*)dout, dsum, n, g.d);
+    else
+        hipLaunchKernelGGL(bwd_dsum_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, st,
+                           (const float*)out, (const float*)dout, dsum, n, g.d);
+    return hipGetLastError();
+}
+
 // Zero a buffer of `n` elements of T (the dq pixels strided queries never write).
 template <typename T>
 __global__ __launch_bounds__(256)
@@ -415,12 +441,21 @@ static hipError_t bwd_launch_dt(const void* q, const void* k, const void* v, con
 
 // Whole generic backward on `st`: statistics, dq + table partials, dk/dv,
 // table reduction.  `ws` holds bwd_generic_workspace_floats(g) floats.
+// With the forward's out and lse given, the statistics are lse itself and
+// dout . out; otherwise both come from a recomputation of the softmax.
 hipError_t launch_bwd_generic(const void* q, const void* k, const void* v, const void* rh, const void* rw,
-                              const void* dout, void* dq, void* dk, void* dv, float* drh, float* drw,
+                              const void* out, const void* dout, const float* lse,
+                              void* dq, void* dk, void* dv, float* drh, float* drw,
                               void* ws, const Geometry& g, bool bf16, hipStream_t st)
 {
-    const BwdWork w = bwd_carve(g, ws);
-    hipError_t e = launch_softmax_stats(q, k, v, rh, rw, dout, w.lse, w.dsum, g, bf16, st);
+    BwdWork w = bwd_carve(g, ws);
+    hipError_t e;
+    if (lse != nullptr) {
+        w.lse = const_cast<float*>(lse);   // read only
+        e = launch_dsum(out, dout, w.dsum, g, bf16, st);
+    } else {
+        e = launch_softmax_stats(q, k, v, rh, rw, dout, w.lse, w.dsum, g, bf16, st);
+    }
     if (e != hipSuccess) return e;
     return bf16 ? bwd_launch_dt<__bf16>(q, k, v, rh, rw, dout, dq, dk, dv, drh, drw, g, w, st)
                 : bwd_launch_dt<float>(q, k, v, rh, rw, dout, dq, dk, dv, drh, drw, g, w, st);

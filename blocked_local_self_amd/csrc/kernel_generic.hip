@@ -24,6 +24,8 @@ namespace halo {
 constexpr int kGenericKC = 64;        // keys per LDS chunk
 constexpr int kGenericThreads = 256;  // upper bound on workgroup size
 
+// lse (may be null in the forward): natural log of each query's softmax
+// normaliser, [B*heads][Ho][Wo].
 template <int DMAX, typename T, bool STATS>
 __global__ __launch_bounds__(kGenericThreads)
 void generic_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
@@ -136,6 +138,7 @@ void generic_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
                 T* op = os + opix * d;
 #pragma unroll
                 for (int c = 0; c < DMAX; ++c) if (c < d) op[c] = from_f32<T>(o[c] * inv);
+                if (lse != nullptr) lse[bh * (int64_t)g.Ho * g.Wo + opix] = m + __logf(l);
             }
         }
     }
@@ -158,12 +161,12 @@ static hipError_t launch_generic_t(const void* q, const void* k, const void* v, 
 
 template <typename T>
 static hipError_t launch_generic_dt(const void* q, const void* k, const void* v, const void* rh,
-                                    const void* rw, void* out, const Geometry& g, hipStream_t st)
+                                    const void* rw, void* out, float* lse, const Geometry& g, hipStream_t st)
 {
-    if (g.d <= 16) return launch_generic_t<16, T>(q, k, v, rh, rw, out, g, st);
-    if (g.d <= 32) return launch_generic_t<32, T>(q, k, v, rh, rw, out, g, st);
-    if (g.d <= 64) return launch_generic_t<64, T>(q, k, v, rh, rw, out, g, st);
-    return launch_generic_t<128, T>(q, k, v, rh, rw, out, g, st);
+    if (g.d <= 16) return launch_generic_t<16, T>(q, k, v, rh, rw, out, g, st, nullptr, lse);
+    if (g.d <= 32) return launch_generic_t<32, T>(q, k, v, rh, rw, out, g, st, nullptr, lse);
+    if (g.d <= 64) return launch_generic_t<64, T>(q, k, v, rh, rw, out, g, st, nullptr, lse);
+    return launch_generic_t<128, T>(q, k, v, rh, rw, out, g, st, nullptr, lse);
 }
 
 // Softmax statistics for the backward pass (lse, dout . out per query).
@@ -188,10 +191,10 @@ hipError_t launch_softmax_stats(const void* q, const void* k, const void* v, con
 
 // Host entry used by the dispatcher; d <= 128 is checked by the caller.
 hipError_t launch_generic(const void* q, const void* k, const void* v, const void* rh,
-                          const void* rw, void* out, const Geometry& g, bool bf16, hipStream_t st)
+                          const void* rw, void* out, float* lse, const Geometry& g, bool bf16, hipStream_t st)
 {
-    return bf16 ? launch_generic_dt<__bf16>(q, k, v, rh, rw, out, g, st)
-                : launch_generic_dt<float>(q, k, v, rh, rw, out, g, st);
+    return bf16 ? launch_generic_dt<__bf16>(q, k, v, rh, rw, out, lse, g, st)
+                : launch_generic_dt<float>(q, k, v, rh, rw, out, lse, g, st);
 }
 
 }  // namespace halo

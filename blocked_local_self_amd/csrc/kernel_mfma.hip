@@ -70,7 +70,7 @@ __global__ __launch_bounds__(kMaxThreads)
 void mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                  const __bf16* __restrict__ v, const __bf16* __restrict__ rel_h,
                  const __bf16* __restrict__ rel_w, __bf16* __restrict__ out,
-                 Geometry g, MfmaPlan p)
+                 float* __restrict__ lse, Geometry g, MfmaPlan p)
 {
     constexpr int KPL = D / 4;                 // channels per lane in a QK fragment
     typedef typename Frag<D>::T FragT;
@@ -328,8 +328,10 @@ void mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 if (!qvalid[u]) continue;
                 const float inv = 1.0f / L[u][0];
                 const int yq = qpix[u] / g.W, xq = qpix[u] - yq * g.W;
-                __bf16* op = out + bh * (int64_t)g.Ho * g.Wo * D +
-                             ((int64_t)(yq / g.stride) * g.Wo + xq / g.stride) * D + gq * 4;
+                const int64_t opix = bh * (int64_t)g.Ho * g.Wo + (int64_t)(yq / g.stride) * g.Wo + xq / g.stride;
+                __bf16* op = out + opix * D + gq * 4;
+                if (lse != nullptr && gq == 0)   // natural log of the normaliser: (shift + log2 L) ln 2
+                    lse[opix] = (mb[u] + __builtin_amdgcn_logf(L[u][0])) * 0.6931471805599453f;
 #pragma unroll
                 for (int mt = 0; mt < D / 16; ++mt) {
                     const u32x2 w = {pack_bf16x2(O[u][mt][0] * inv, O[u][mt][1] * inv),
@@ -400,7 +402,7 @@ static int choose_qt(const Geometry& g)
 
 template <int D, int NCH, int QT>
 static hipError_t launch_t(const void* q, const void* k, const void* v, const void* rh,
-                           const void* rw, void* out, const Geometry& g, hipStream_t st)
+                           const void* rw, void* out, float* lse, const Geometry& g, hipStream_t st)
 {
     // Strip width: widest strip within the preferred LDS budget; narrower
     // only when even one block needs more.  One wave per QT-tile group of
@@ -426,37 +428,38 @@ static hipError_t launch_t(const void* q, const void* k, const void* v, const vo
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)p.nwg), dim3(64 * p.waves), p.lds_bytes, st,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
-                       (const __bf16*)rh, (const __bf16*)rw, (__bf16*)out, g, p);
+                       (const __bf16*)rh, (const __bf16*)rw, (__bf16*)out, lse, g, p);
     return hipGetLastError();
 }
 
 template <int D, int NCH>
 static hipError_t launch_dn(const void* q, const void* k, const void* v, const void* rh,
-                            const void* rw, void* out, const Geometry& g, hipStream_t st)
+                            const void* rw, void* out, float* lse, const Geometry& g, hipStream_t st)
 {
     switch (choose_qt(g)) {
-    case 1: return launch_t<D, NCH, 1>(q, k, v, rh, rw, out, g, st);
-    case 3: return launch_t<D, NCH, 3>(q, k, v, rh, rw, out, g, st);
-    case 4: return launch_t<D, NCH, 4>(q, k, v, rh, rw, out, g, st);
-    default: return launch_t<D, NCH, 2>(q, k, v, rh, rw, out, g, st);
+    case 1: return launch_t<D, NCH, 1>(q, k, v, rh, rw, out, lse, g, st);
+    case 3: return launch_t<D, NCH, 3>(q, k, v, rh, rw, out, lse, g, st);
+    case 4: return launch_t<D, NCH, 4>(q, k, v, rh, rw, out, lse, g, st);
+    default: return launch_t<D, NCH, 2>(q, k, v, rh, rw, out, lse, g, st);
     }
 }
 
 bool ring_supported(const Geometry& g);
 hipError_t launch_ring(const void* q, const void* k, const void* v, const void* rh,
-                       const void* rw, void* out, const Geometry& g, hipStream_t st);
+                       const void* rw, void* out, float* lse, const Geometry& g, hipStream_t st);
 
 // Matrix-core launch: the persistent ring kernel when it covers the shape,
 // else the strip kernel.  force_strip selects the strip kernel regardless.
 hipError_t launch_mfma(const void* q, const void* k, const void* v, const void* rh,
-                       const void* rw, void* out, const Geometry& g, bool force_strip, hipStream_t st)
+                       const void* rw, void* out, float* lse, const Geometry& g, bool force_strip,
+                       hipStream_t st)
 {
-    if (!force_strip && ring_supported(g)) return launch_ring(q, k, v, rh, rw, out, g, st);
+    if (!force_strip && ring_supported(g)) return launch_ring(q, k, v, rh, rw, out, lse, g, st);
     const bool wide = g.r > 16;
-    if (g.d == 16) return wide ? launch_dn<16, 2>(q, k, v, rh, rw, out, g, st)
-                               : launch_dn<16, 1>(q, k, v, rh, rw, out, g, st);
-    return wide ? launch_dn<32, 2>(q, k, v, rh, rw, out, g, st)
-                : launch_dn<32, 1>(q, k, v, rh, rw, out, g, st);
+    if (g.d == 16) return wide ? launch_dn<16, 2>(q, k, v, rh, rw, out, lse, g, st)
+                               : launch_dn<16, 1>(q, k, v, rh, rw, out, lse, g, st);
+    return wide ? launch_dn<32, 2>(q, k, v, rh, rw, out, lse, g, st)
+                : launch_dn<32, 1>(q, k, v, rh, rw, out, lse, g, st);
 }
 
 }  // namespace halo

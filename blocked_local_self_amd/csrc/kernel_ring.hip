@@ -110,7 +110,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2)))
 void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                  const __bf16* __restrict__ v, const __bf16* __restrict__ rel_h,
                  const __bf16* __restrict__ rel_w, __bf16* __restrict__ out,
-                 Geometry g, RingPlan p)
+                 float* __restrict__ lse, Geometry g, RingPlan p)
 {
     static_assert(NCT == 1 || NCT == 2, "windows of up to 32 columns");
     const int R = g.r;                         // window side, <= 16 * NCT
@@ -368,8 +368,11 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 
     // Output of one group: lane (n, g) holds channels 16*mt + 4g + i of
     // query n of tile u, packed bf16.
+    // lse2: the softmax shift plus log2 of the weight sum (base-2 log of
+    // the normaliser), when the caller asks for the log normalisers.
     struct Result {
         u32x2 w[QT][D / 16];
+        float lse2[QT];
     };
     auto store_result = [&](const Tile& T, const Result& res) {
 #pragma unroll
@@ -378,6 +381,8 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             __bf16* op = out + bh * (int64_t)g.Ho * g.Wo * D + (int64_t)T.opix[u] * D + gq * 4;
 #pragma unroll
             for (int mt = 0; mt < D / 16; ++mt) *reinterpret_cast<u32x2*>(op + mt * 16) = res.w[u][mt];
+            if (lse != nullptr && gq == 0)
+                lse[bh * (int64_t)g.Ho * g.Wo + T.opix[u]] = res.lse2[u] * 0.6931471805599453f;
         }
     };
 
@@ -626,6 +631,9 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         };
 
         weighted_sum();
+        float shift[QT];                              // base-2 shift the weights carry
+#pragma unroll
+        for (int u = 0; u < QT; ++u) shift[u] = mb[u];
         bool redo = false;
 #pragma unroll
         for (int u = 0; u < QT; ++u) redo |= !(L[u][0] >= 0x1p-60f);
@@ -646,6 +654,7 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
             for (int u = 0; u < QT; ++u) {
                 const float m = max_over_rows(M[u]);
+                shift[u] += m;
 #pragma unroll
                 for (int k2 = 0; k2 < NCT; ++k2)
 #pragma unroll
@@ -660,6 +669,7 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         // ---- normalise and pack
 #pragma unroll
         for (int u = 0; u < QT; ++u) {
+            if (lse != nullptr) res.lse2[u] = shift[u] + __builtin_amdgcn_logf(L[u][0]);
             const float inv = __builtin_amdgcn_rcpf(L[u][0]);
 #pragma unroll
             for (int mt = 0; mt < D / 16; ++mt)
@@ -864,7 +874,7 @@ static int ring_qt(const Geometry& g)
 
 template <int D, int NCT, int QT, int W>
 static hipError_t ring_launch_t(const void* q, const void* k, const void* v, const void* rh,
-                                const void* rw, void* out, const Geometry& g, hipStream_t st)
+                                const void* rw, void* out, float* lse, const Geometry& g, hipStream_t st)
 {
     RingPlan p = W == 4 ? ring_choose(g, NCT, QT, 4, ring_min_strips4(g)) : ring_choose(g, NCT, QT, 8);
     if (p.nbx == 0) return hipErrorInvalidConfiguration;
@@ -879,27 +889,27 @@ static hipError_t ring_launch_t(const void* q, const void* k, const void* v, con
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)p.nwg), dim3(64 * W), p.lds_bytes, st,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
-                       (const __bf16*)rh, (const __bf16*)rw, (__bf16*)out, g, p);
+                       (const __bf16*)rh, (const __bf16*)rw, (__bf16*)out, lse, g, p);
     return hipGetLastError();
 }
 
 template <int D, int NCT, int QT>
 static hipError_t ring_launch_w(const void* q, const void* k, const void* v, const void* rh,
-                                const void* rw, void* out, const Geometry& g, hipStream_t st)
+                                const void* rw, void* out, float* lse, const Geometry& g, hipStream_t st)
 {
     const int w = ring_waves(g, NCT, QT);
-    if (w == 4) return ring_launch_t<D, NCT, QT, 4>(q, k, v, rh, rw, out, g, st);
-    if (w == 8) return ring_launch_t<D, NCT, QT, 8>(q, k, v, rh, rw, out, g, st);
+    if (w == 4) return ring_launch_t<D, NCT, QT, 4>(q, k, v, rh, rw, out, lse, g, st);
+    if (w == 8) return ring_launch_t<D, NCT, QT, 8>(q, k, v, rh, rw, out, lse, g, st);
     return hipErrorInvalidConfiguration;
 }
 
 template <int D>
 static hipError_t ring_launch_d(const void* q, const void* k, const void* v, const void* rh,
-                                const void* rw, void* out, const Geometry& g, hipStream_t st)
+                                const void* rw, void* out, float* lse, const Geometry& g, hipStream_t st)
 {
-    if (ring_nct(g) == 2) return ring_launch_w<D, 2, 1>(q, k, v, rh, rw, out, g, st);
-    if (ring_qt(g) > 1) return ring_launch_w<D, 1, HALO_RING_QT>(q, k, v, rh, rw, out, g, st);
-    return ring_launch_w<D, 1, 1>(q, k, v, rh, rw, out, g, st);
+    if (ring_nct(g) == 2) return ring_launch_w<D, 2, 1>(q, k, v, rh, rw, out, lse, g, st);
+    if (ring_qt(g) > 1) return ring_launch_w<D, 1, HALO_RING_QT>(q, k, v, rh, rw, out, lse, g, st);
+    return ring_launch_w<D, 1, 1>(q, k, v, rh, rw, out, lse, g, st);
 }
 
 bool ring_supported(const Geometry& g)
@@ -910,10 +920,10 @@ bool ring_supported(const Geometry& g)
 }
 
 hipError_t launch_ring(const void* q, const void* k, const void* v, const void* rh,
-                       const void* rw, void* out, const Geometry& g, hipStream_t st)
+                       const void* rw, void* out, float* lse, const Geometry& g, hipStream_t st)
 {
-    return g.d == 16 ? ring_launch_d<16>(q, k, v, rh, rw, out, g, st)
-                     : ring_launch_d<32>(q, k, v, rh, rw, out, g, st);
+    return g.d == 16 ? ring_launch_d<16>(q, k, v, rh, rw, out, lse, g, st)
+                     : ring_launch_d<32>(q, k, v, rh, rw, out, lse, g, st);
 }
 
 }  // namespace halo

@@ -2,8 +2,8 @@
  * halo_attn.h -- C ABI of the MI355X (gfx950) halo-attention library.
  *
  * The operation: HaloNet's blocked local self-attention with haloing, forward
- * pass, on already projected queries, keys and values ("Scaling Local
- * Self-Attention for Parameter Efficient Visual Backbones").
+ * and backward pass, on already projected queries, keys and values ("Scaling
+ * Local Self-Attention for Parameter Efficient Visual Backbones").
  *
  *  - Section 2.2, Figure 1: the H x W map is cut into non-overlapping
  *    block x block query blocks, tiled from the top-left (a last block row or
@@ -100,6 +100,20 @@ int halo_attn_fwd_kernel(const void* q, const void* k, const void* v,
                          int block, int halo, int query_stride,
                          float scale, int dtype, int kernel, void* stream);
 
+/*
+ * halo_attn_fwd_kernel that also writes, per query, the natural log of its
+ * softmax normaliser: lse[n][head][y'][x'] = log sum_j exp(l_j) over the
+ * query's in-image window keys (fp32, [B][heads][H/s][W/s], caller-owned
+ * device memory that must not overlap any other tensor).  lse may be NULL
+ * (then this is halo_attn_fwd_kernel).  A training step keeps out and lse
+ * for halo_attn_bwd, which then skips recomputing the softmax statistics.
+ */
+int halo_attn_fwd_lse(const void* q, const void* k, const void* v,
+                      const void* rel_h, const void* rel_w, void* out, float* lse,
+                      int B, int heads, int H, int W, int d,
+                      int block, int halo, int query_stride,
+                      float scale, int dtype, int kernel, void* stream);
+
 /* halo_attn_fwd_kernel with kernel = HALO_KERNEL_AUTO. */
 int halo_attn_fwd(const void* q, const void* k, const void* v,
                   const void* rel_h, const void* rel_w, void* out,
@@ -120,8 +134,10 @@ int halo_attn_fwd(const void* q, const void* k, const void* v,
  *   drel_h[R] = scale * sum of dl_j * q over all (query, key) pairs of all
  *               batches and heads whose row displacement selects row R;
  *               drel_w likewise for columns.
- * The forward output is not an input: the softmax of every query is
- * recomputed.
+ * out and lse: the forward's output and log normalisers
+ * (halo_attn_fwd_lse) for these inputs, or both NULL.  Given, the softmax
+ * weights are exp(l - lse) and dout . out comes from out; NULL, both are
+ * recomputed from q, k and the tables (an extra pass).
  *
  * Layouts and dtype: q, k, v, rel_h, rel_w as in the forward; dout has out's
  * layout [B][heads][H/s][W/s][d]; dq, dk, dv have q's layout; all of these
@@ -139,15 +155,17 @@ int halo_attn_fwd(const void* q, const void* k, const void* v,
  * so repeated calls give bitwise identical results.
  *
  * Errors as for the forward, plus HALO_ERR_WORKSPACE (workspace too small or
- * misaligned) and HALO_ERR_ALIAS when any output or the workspace overlaps
- * an input or another output.  drel_h and drel_w must be non-NULL; if a size
+ * misaligned), HALO_ERR_ALIAS when any output or the workspace overlaps an
+ * input or another output, and HALO_ERR_NULL when only one of out and lse
+ * is given.  drel_h and drel_w must be non-NULL; if a size
  * is zero they are set to zero (the gradient of an empty sum) and no other
  * pointer is inspected.  kernel: a halo_kernel value; only the generic
  * kernels exist for the backward, so HALO_KERNEL_MFMA and MFMA_STRIP return
  * HALO_ERR_UNSUPPORTED.
  */
 int halo_attn_bwd_kernel(const void* q, const void* k, const void* v,
-                         const void* rel_h, const void* rel_w, const void* dout,
+                         const void* rel_h, const void* rel_w,
+                         const void* out, const void* dout, const float* lse,
                          void* dq, void* dk, void* dv, float* drel_h, float* drel_w,
                          void* workspace, size_t workspace_bytes,
                          int B, int heads, int H, int W, int d,
@@ -156,7 +174,8 @@ int halo_attn_bwd_kernel(const void* q, const void* k, const void* v,
 
 /* halo_attn_bwd_kernel with kernel = HALO_KERNEL_AUTO. */
 int halo_attn_bwd(const void* q, const void* k, const void* v,
-                  const void* rel_h, const void* rel_w, const void* dout,
+                  const void* rel_h, const void* rel_w,
+                  const void* out, const void* dout, const float* lse,
                   void* dq, void* dk, void* dv, float* drel_h, float* drel_w,
                   void* workspace, size_t workspace_bytes,
                   int B, int heads, int H, int W, int d,

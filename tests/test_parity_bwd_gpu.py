@@ -54,9 +54,15 @@ def case(B, heads, H, W, d, block, halo, stride, dtype, seed):
     return ins, g
 
 
-def gpu_bwd(ins, g, block, halo, stride, kernel="auto"):
+def gpu_bwd(ins, g, block, halo, stride, kernel="auto", use_fwd=False):
+    """Backward through the C ABI; with use_fwd the forward's out and lse
+    (halo_attn_fwd with return_lse) are passed in instead of recomputed."""
     q, k, v, rh, rw = (t.to(DEV) for t in ins)
-    res = halo_attn_bwd(q, k, v, rh, rw, g.to(DEV), block, halo, stride, kernel=kernel)
+    extra = {}
+    if use_fwd:
+        out, lse = halo_attn_fwd(q, k, v, rh, rw, block, halo, stride, return_lse=True)
+        extra = {"out": out, "lse": lse}
+    res = halo_attn_bwd(q, k, v, rh, rw, g.to(DEV), block, halo, stride, kernel=kernel, **extra)
     torch.cuda.synchronize()
     return [f64(t) for t in res]
 
@@ -95,13 +101,14 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("use_fwd", [False, True], ids=["recompute", "fwd_lse"])
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
-def test_small_shapes_match_oracle(shape, dtype):
+def test_small_shapes_match_oracle(shape, dtype, use_fwd):
     B, heads, H, W, d, block, halo, stride = shape
-    say(f"bwd case {shape} {dtype}")
+    say(f"bwd case {shape} {dtype} use_fwd={use_fwd}")
     ins, g = case(*shape, dtype, seed=sum(shape))
-    got = gpu_bwd(ins, g, block, halo, stride)
+    got = gpu_bwd(ins, g, block, halo, stride, use_fwd=use_fwd)
     compare(got, ref_bwd(ins, g, block, halo, stride), dtype, str(shape))
 
 
@@ -111,7 +118,7 @@ def test_workload_full_size(name):
     say(f"bwd workload {name}")
     ins = make_workload_inputs(wl, seed=0)
     g = make_grad_output(wl.B, wl.heads, wl.Ho, wl.Wo, wl.d, dtype=wl.dtype, seed=0)
-    got = gpu_bwd(ins, g, wl.block, wl.halo, wl.stride)
+    got = gpu_bwd(ins, g, wl.block, wl.halo, wl.stride, use_fwd=True)
     want = ref_bwd(ins, g, wl.block, wl.halo, wl.stride)
     worst = compare(got, want, wl.dtype, name)
     say(f"  worst relative error {worst:.3e}")
@@ -132,7 +139,7 @@ def test_autograd_function_matches_direct_call():
     ref_out = halo_attn_fwd(*(t.detach() for t in ts), 8, 3)
     assert torch.equal(out.detach(), ref_out)
     out.backward(g.to(DEV))
-    direct = gpu_bwd(ins, g, 8, 3, 1)
+    direct = gpu_bwd(ins, g, 8, 3, 1, use_fwd=True)   # the function keeps the forward's out and lse
     for t, want in zip(ts, direct):
         assert np.array_equal(f64(t.grad), want)
 

@@ -89,6 +89,45 @@ def test_small_shapes_match_oracle(shape, kernel, dtype):
     assert err <= TOL[dtype], err
 
 
+# lse (log softmax normaliser per query): the matrix-core kernels sum the
+# bf16-rounded weights (relative error <= 2^-9 of the sum, so <= 2^-9 in the
+# log) after fp32 logits; the generic kernel sums fp32 weights.
+LSE_TOL = {"fp32": 1e-4, "bf16": 4e-3}
+
+
+@pytest.mark.parametrize("kernel", ["auto", "generic", "mfma_strip"])
+@pytest.mark.parametrize("shape", [s for s in SMALL if s[4] in (16, 32) and s[5] % 4 == 0][:8],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_lse_matches_oracle(shape, kernel):
+    B, heads, H, W, d, block, halo, stride = shape
+    dtype = "fp32" if kernel == "generic" else "bf16"
+    say(f"lse case {shape} kernel={kernel}")
+    inp = make_inputs(B, heads, H, W, d, block, halo, dtype=dtype, seed=5 + sum(shape))
+    q, k, v, rh, rw = (t.to(DEV) for t in inp)
+    out, lse = halo_attn_fwd(q, k, v, rh, rw, block, halo, stride, kernel=kernel, return_lse=True)
+    plain = halo_attn_fwd(q, k, v, rh, rw, block, halo, stride, kernel=kernel)
+    torch.cuda.synchronize()
+    assert torch.equal(out, plain)                      # asking for lse changes nothing else
+    want_out, want_lse = oracle.halo_attn_ref(*(f64(t) for t in inp), block, halo, stride, return_lse=True)
+    assert np.abs(f64(out) - want_out).max() <= TOL[dtype]
+    assert np.abs(f64(lse) - want_lse).max() <= LSE_TOL[dtype]
+
+
+@pytest.mark.parametrize("name", ["early_stage_bf16_64x64_d16_b8h3", "large_bf16_128x128_d32_b12h3"])
+def test_lse_full_workload(name):
+    wl = workloads.get(name)
+    inp = make_workload_inputs(wl, seed=2)
+    q, k, v, rh, rw = (t.to(DEV) for t in inp)
+    out, lse = halo_attn_fwd(q, k, v, rh, rw, wl.block, wl.halo, wl.stride, return_lse=True)
+    torch.cuda.synchronize()
+    slices = sampled_slices(wl, 3)
+    pick = lambda t: np.stack([f64(t[n, hd]) for n, hd in slices])[:, None]
+    _, want = oracle.halo_attn_ref(pick(q), pick(k), pick(v), f64(rh), f64(rw), wl.block, wl.halo,
+                                   wl.stride, return_lse=True)
+    have = np.stack([f64(lse)[n, hd] for n, hd in slices])[:, None]
+    assert np.abs(have - want).max() <= LSE_TOL["bf16"]
+
+
 @pytest.mark.parametrize("shape", [s for s in SMALL if s[4] in (16, 32) and s[5] % 4 == 0],
                          ids=lambda s: "x".join(map(str, s)))
 def test_matrix_core_kernel_matches_oracle(shape):
