@@ -1,5 +1,6 @@
 // C ABI of the halo-attention library: argument checks, kernel choice, launch.
 // The operation and every convention are documented in include/halo_attn.h.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -22,6 +23,14 @@ hipError_t launch_bwd_generic(const void* q, const void* k, const void* v, const
                               void* dq, void* dk, void* dv, float* drh, float* drw,
                               void* ws, const Geometry& g, bool bf16, hipStream_t st);
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t st);
+bool bwd_mfma_supported(const Geometry& g, bool bf16);
+int64_t bwd_mfma_workspace_floats(const Geometry& g, int64_t nchunks);
+int64_t bwd_rel_chunks(const Geometry& g);
+hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const void* rh, const void* rw,
+                           const void* out, const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           float* part_kv, float* part_rel, const Geometry& g, hipStream_t st);
+hipError_t launch_rel_reduce(const float* part, float* part2, float* drh, float* drw, const Geometry& g,
+                             hipStream_t st);
 }  // namespace halo
 
 namespace {
@@ -113,6 +122,37 @@ int check_sizes(int B, int heads, int H, int W, int d, int block, int halo, int 
     return HALO_OK;
 }
 
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace of the matrix-core backward, carved in this order (256-byte
+// aligned pieces): per-block dk/dv shares, per-block table partials, the
+// table reduction's first level, then the forward's lse and out when the
+// caller does not pass them.
+struct MfmaWs {
+    size_t kv, rel, rel2, lse, out, total;
+};
+MfmaWs mfma_ws(const halo::Geometry& g)
+{
+    MfmaWs w;
+    const int64_t nblocks = g.BH * g.nbh * g.nbw;
+    const int64_t e2 = 2 * (int64_t)(2 * g.r - 1) * g.d;
+    const int64_t nq = g.BH * g.Ho * g.Wo;
+    w.kv = 0;
+    w.rel = align256(w.kv + (size_t)(nblocks * g.r * g.r * 2 * g.d) * 4);
+    w.rel2 = align256(w.rel + (size_t)(nblocks * e2) * 4);
+    w.lse = align256(w.rel2 + (size_t)(halo::bwd_rel_chunks(g) * e2) * 4);
+    w.out = align256(w.lse + (size_t)nq * 4);
+    w.total = align256(w.out + (size_t)(nq * g.d) * 2);
+    return w;
+}
+
+size_t bwd_ws_bytes(const halo::Geometry& g, bool bf16)
+{
+    const size_t gen = (size_t)halo::bwd_generic_workspace_floats(g) * 4;
+    if (!halo::bwd_mfma_supported(g, bf16)) return gen;
+    return std::max(gen, mfma_ws(g).total);
+}
+
 }  // namespace
 
 extern "C" {
@@ -198,7 +238,7 @@ long long halo_attn_bwd_workspace_bytes(int B, int heads, int H, int W, int d,
     const int st = check_sizes(B, heads, H, W, d, block, halo, query_stride, 1.0f, dtype, g, empty);
     if (st) return st;
     if (empty) return 0;
-    return (long long)halo::bwd_generic_workspace_floats(g) * 4;
+    return (long long)bwd_ws_bytes(g, dtype == HALO_BF16);
 }
 
 int halo_attn_bwd_kernel(const void* q, const void* k, const void* v,
@@ -234,7 +274,8 @@ int halo_attn_bwd_kernel(const void* q, const void* k, const void* v,
         return fail(HALO_ERR_NULL, "null pointer among q, k, v, rel_h, rel_w, dout, dq, dk, dv, workspace");
     if ((out == nullptr) != (lse == nullptr))
         return fail(HALO_ERR_NULL, "pass both out and lse from the forward, or neither");
-    const size_t need = (size_t)halo::bwd_generic_workspace_floats(g) * 4;
+    const bool bf16 = dtype == HALO_BF16;
+    const size_t need = bwd_ws_bytes(g, bf16);
     if (workspace_bytes < need)
         return fail(HALO_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu this call needs",
                     workspace_bytes, need);
@@ -259,11 +300,36 @@ int halo_attn_bwd_kernel(const void* q, const void* k, const void* v,
             if (overlaps(outs[a], outsz[a], outs[b], outsz[b]))
                 return fail(HALO_ERR_ALIAS, "two outputs (or an output and the workspace) overlap");
     }
-    if (kernel == HALO_KERNEL_MFMA || kernel == HALO_KERNEL_MFMA_STRIP)
-        return fail(HALO_ERR_UNSUPPORTED, "no matrix-core backward kernel for these arguments");
-
-    const hipError_t e = halo::launch_bwd_generic(q, k, v, rel_h, rel_w, out, dout, lse, dq, dk, dv, drel_h,
-                                                  drel_w, workspace, g, dtype == HALO_BF16, s);
+    const bool mfma_ok = halo::bwd_mfma_supported(g, bf16);
+    if ((kernel == HALO_KERNEL_MFMA || kernel == HALO_KERNEL_MFMA_STRIP) && !mfma_ok)
+        return fail(HALO_ERR_UNSUPPORTED,
+                    "matrix-core backward needs bf16, d in {16,32}, window side <= 16, blocks that tile "
+                    "the image, and (block/stride)^2 in {16, 64} (got dtype=%d d=%d r=%d block=%d H=%d W=%d)",
+                    dtype, d, r, block, H, W);
+    hipError_t e;
+    if (kernel == HALO_KERNEL_GENERIC || !mfma_ok) {
+        e = halo::launch_bwd_generic(q, k, v, rel_h, rel_w, out, dout, lse, dq, dk, dv, drel_h, drel_w,
+                                     workspace, g, bf16, s);
+    } else {
+        const MfmaWs w = mfma_ws(g);
+        unsigned char* base = static_cast<unsigned char*>(workspace);
+        const void* fo = out;
+        const float* fl = lse;
+        e = hipSuccess;
+        if (lse == nullptr) {   // the forward's out and lse, recomputed into the workspace
+            fo = base + w.out;
+            fl = reinterpret_cast<float*>(base + w.lse);
+            e = halo::launch_mfma(q, k, v, rel_h, rel_w, base + w.out, reinterpret_cast<float*>(base + w.lse),
+                                  g, false, s);
+        }
+        if (e == hipSuccess)
+            e = halo::launch_bwd_mfma(q, k, v, rel_h, rel_w, fo, dout, fl, dq, dk, dv,
+                                      reinterpret_cast<float*>(base + w.kv), reinterpret_cast<float*>(base + w.rel),
+                                      g, s);
+        if (e == hipSuccess)
+            e = halo::launch_rel_reduce(reinterpret_cast<const float*>(base + w.rel),
+                                        reinterpret_cast<float*>(base + w.rel2), drel_h, drel_w, g, s);
+    }
     if (e != hipSuccess)
         return fail(HALO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return HALO_OK;

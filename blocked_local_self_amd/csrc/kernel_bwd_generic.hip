@@ -29,8 +29,8 @@
 //     query data (q, dout, lse, D) stream through LDS, and each thread sums
 //     dk and dv over the queries whose window holds its key.  Keys are
 //     owned by exactly one workgroup, so dk and dv need no atomics.
-//  4. bwd_rel_reduce_kernel, then bwd_rel_final_kernel: the partial table
-//     gradients summed over blocks in two fixed-order levels, written fp32.
+//  4. bwd_rel_reduce_kernel (levels of 32-row sums), then bwd_rel_final_kernel:
+//     the partial table gradients summed over blocks in a fixed order, fp32.
 #include <algorithm>
 
 #include "halo_common.h"
@@ -44,7 +44,7 @@ hipError_t launch_softmax_stats(const void* q, const void* k, const void* v, con
 constexpr int kBwdKC = 64;           // keys per LDS chunk (bwd_q_kernel)
 constexpr int kBwdQC = 64;           // queries per LDS chunk (bwd_kv_kernel)
 constexpr int kBwdThreads = 256;     // upper bound on workgroup size
-constexpr int kRelChunk = 128;       // blocks per first-level reduction chunk
+constexpr int kRelChunk = 32;        // rows summed per thread at each reduction level
 
 // Workspace carve-up of the generic backward, in floats.
 struct BwdWork {
@@ -55,7 +55,9 @@ struct BwdWork {
     float* part2;    // [nchunks][2][(2r-1)*d]
 };
 
-static int64_t bwd_nchunks(int64_t nblocks) { return (nblocks + kRelChunk - 1) / kRelChunk; }
+// Rows of reduction scratch for nblocks partial rows: every level divides
+// the row count by kRelChunk, so twice the first level's rows hold them all.
+static int64_t bwd_nchunks(int64_t nblocks) { return 2 * ((nblocks + kRelChunk - 1) / kRelChunk) + 1; }
 
 // Floats of workspace the generic backward needs.
 int64_t bwd_generic_workspace_floats(const Geometry& g)
@@ -326,18 +328,20 @@ void bwd_kv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
 }
 
 // out[y][e] = sum of in[n][e] over the rows n of chunk y = blockIdx.x
-// (rows y*per .. min((y+1)*per, nin) - 1, in increasing order), e < E.
+// (rows y*per .. min((y+1)*per, nin) - 1, in increasing order); entry
+// e = blockIdx.y * blockDim.x + threadIdx.x < E.
 __global__ __launch_bounds__(256)
 void bwd_rel_reduce_kernel(const float* __restrict__ in, float* __restrict__ out,
                            int64_t E, int64_t nin, int64_t per)
 {
+    const int64_t e = (int64_t)blockIdx.y * blockDim.x + threadIdx.x;
+    if (e >= E) return;
     const int64_t n0 = (int64_t)blockIdx.x * per;
     const int64_t n1 = min(n0 + per, nin);
-    for (int64_t e = threadIdx.x; e < E; e += blockDim.x) {
-        float acc = 0.f;
-        for (int64_t n = n0; n < n1; ++n) acc += in[n * E + e];
-        out[(int64_t)blockIdx.x * E + e] = acc;
-    }
+    float acc = 0.f;
+#pragma unroll 8
+    for (int64_t n = n0; n < n1; ++n) acc += in[n * E + e];
+    out[(int64_t)blockIdx.x * E + e] = acc;
 }
 
 // The two tables' gradients: entry e of the concatenated (rel_h, rel_w) row
@@ -349,6 +353,7 @@ void bwd_rel_final_kernel(const float* __restrict__ in, float* __restrict__ drh,
     const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (e >= E) return;
     float acc = 0.f;
+#pragma unroll 8
     for (int64_t n = 0; n < nin; ++n) acc += in[n * E + e];
     const int64_t half = E / 2;
     if (e < half) drh[e] = acc;
@@ -390,12 +395,22 @@ void zero_kernel(T* __restrict__ p, int64_t n)
         p[i] = from_f32<T>(0.f);
 }
 
+hipError_t launch_zero_bf16(void* p, int64_t n, hipStream_t st)
+{
+    const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 65536));
+    hipLaunchKernelGGL(zero_kernel<__bf16>, dim3((unsigned)blocks), dim3(256), 0, st, (__bf16*)p, n);
+    return hipGetLastError();
+}
+
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t st)
 {
     const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 65536));
     hipLaunchKernelGGL(zero_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, st, p, n);
     return hipGetLastError();
 }
+
+hipError_t launch_rel_reduce(const float* part, float* part2, float* drh, float* drw, const Geometry& g,
+                             hipStream_t st);
 
 template <int DMAX, typename T>
 static hipError_t bwd_launch_t(const void* q, const void* k, const void* v, const void* rh, const void* rw,
@@ -417,16 +432,34 @@ static hipError_t bwd_launch_t(const void* q, const void* k, const void* v, cons
     hipLaunchKernelGGL((bwd_kv_kernel<DMAX, T>), dim3((unsigned)nblocks), dim3(kthreads), 0, st,
                        (const T*)q, (const T*)k, (const T*)v, (const T*)rh, (const T*)rw, (const T*)dout,
                        (T*)dk, (T*)dv, g, w);
-    // table gradients: blocks -> chunks of kRelChunk blocks -> the two tables
+    return launch_rel_reduce(w.part, w.part2, drh, drw, g, st);
+}
+
+// Table gradients from per-block partials [nblocks][2][(2r-1)*d]: rows are
+// summed kRelChunk at a time, level after level (scratch rows in part2),
+// until at most kRelChunk remain; the last level writes the two tables.
+// Every sum runs in a fixed order.
+hipError_t launch_rel_reduce(const float* part, float* part2, float* drh, float* drw, const Geometry& g,
+                             hipStream_t st)
+{
     const int64_t E = (int64_t)(2 * g.r - 1) * g.d * 2;
-    const int64_t nch = bwd_nchunks(nblocks);
-    const unsigned ex = (unsigned)((E + 255) / 256);
-    hipLaunchKernelGGL(bwd_rel_reduce_kernel, dim3((unsigned)nch), dim3(256), 0, st,
-                       (const float*)w.part, w.part2, E, nblocks, (int64_t)kRelChunk);
-    hipLaunchKernelGGL(bwd_rel_final_kernel, dim3(ex), dim3(256), 0, st,
-                       (const float*)w.part2, drh, drw, E, nch);
+    const unsigned ey = (unsigned)((E + 255) / 256);
+    const float* in = part;
+    int64_t rows = g.BH * g.nbh * g.nbw;
+    float* dst = part2;
+    while (rows > kRelChunk) {
+        const int64_t nch = (rows + kRelChunk - 1) / kRelChunk;
+        hipLaunchKernelGGL(bwd_rel_reduce_kernel, dim3((unsigned)nch, ey), dim3(256), 0, st, in, dst, E, rows,
+                           (int64_t)kRelChunk);
+        in = dst;
+        dst += nch * E;
+        rows = nch;
+    }
+    hipLaunchKernelGGL(bwd_rel_final_kernel, dim3(ey), dim3(256), 0, st, in, drh, drw, E, rows);
     return hipGetLastError();
 }
+
+int64_t bwd_rel_chunks(const Geometry& g) { return bwd_nchunks(g.BH * g.nbh * g.nbw); }
 
 template <typename T>
 static hipError_t bwd_launch_dt(const void* q, const void* k, const void* v, const void* rh, const void* rw,

@@ -1,0 +1,638 @@
+// Backward pass of halo attention on gfx950 matrix cores (bf16 in, fp32
+// accumulate), for windows of at most 16 columns and full blocks.
+//
+// The pages print no backward; HaloNet's models are trained by gradient
+// descent ("Scaling Local Self-Attention for Parameter Efficient Visual
+// Backbones", section 4.1), so this is the exact derivative of the forward
+// definition (sections 2.1-2.2; logit
+//   l = scale * (q.k + q.rel_h[ky - y + c0] + q.rel_w[kx - x + c0])
+// as in the HaloAttention module of the pswp.cn blog page, section 4), with
+// the forward's per-query log normaliser lse:
+//   P = exp(l - lse),  dl = P (dout.v - dout.out),
+//   dq = scale sum_keys dl (k + rel_h[row] + rel_w[col]),
+//   dk = scale sum_queries dl q,  dv = sum_queries P dout,
+//   d rel_h[R] = scale sum dl q over the pairs at row displacement R (d rel_w alike).
+//
+// One workgroup (4 waves) per query block:
+//  * stages the block's window (K and V as MFMA fragments, K also transposed),
+//    both tables, Q^T and dout^T of its queries, and dout.out per query;
+//  * relative logits of every query against both tables on MFMA, re-indexed
+//    per query into a width table (window column -> q.rel_w, masked -1e30
+//    off the image or past the window) and a height table (window row ->
+//    alpha q.rel_h - lse2, alpha = scale log2 e, lse2 = lse log2 e);
+//  * query path (wave per 16-query tile, scores transposed, S^T = K Q^T, so
+//    lane (n, g) holds query n and window columns 4g..4g+3 of one row):
+//    P = exp2(alpha S^T + height), dP^T = V dout^T, dl = P (dP - D);
+//    dq^T += K^T dl^T and, on two more MFMAs against 0/1 operands, the sums
+//    of dl over each window row and each window column of the query.  Those
+//    sums, re-indexed by table row, give the tables' share of dq (tables^T
+//    times sums) and the block's table gradients (Q^T times sums), both on
+//    MFMA with the sums split into bf16 high and low parts;
+//  * key path (wave per window row, scores in the other orientation,
+//    S = Q K^T, so lane (n, g) holds window column n and queries 4g..4g+3):
+//    the same P and dl, then dV^T += dout^T P and dK^T += Q^T dl over pairs
+//    of query tiles.  The window's dk and dv are this block's share only;
+//    they go to a workspace, and a gather kernel sums, for every key, the
+//    shares of the (at most four, for halo < block) windows holding it in a
+//    fixed order.
+// No floating-point atomics anywhere: results are bitwise reproducible.
+#include <algorithm>
+#include <type_traits>
+
+#include "mfma_util.h"
+
+namespace halo {
+
+constexpr int kBRows = 16;             // LDS window rows (r <= 16)
+constexpr int kBCols = 16;             // window columns per row (one MFMA tile, r <= 16)
+constexpr int kKtPitch = 264;          // K^T channel pitch (elements, >= 16*16): 132 dwords = 4 (mod 64)
+constexpr int kScrStrideB = 20;        // floats per per-wave scratch row
+constexpr int kTabRows = 32;           // relative tables padded to 32 rows (2r-1 <= 31)
+
+struct BwdMfmaPlan {
+    int nq;                // queries per block (16 * NT)
+    int qpitch;            // Q^T / dout^T channel pitch (elements)
+    int off_v, off_kt, off_tab, off_tabt, off_qt, off_dot, off_rw, off_rh, off_d, off_scr, lds_bytes;
+    int remap_xcd;
+    int64_t nwg;
+    float alpha;           // scale * log2(e)
+};
+
+template <int D>
+__device__ inline unsigned bk_chunk(int c, int col)   // same swizzle as the forward ring
+{
+    if (D == 16) return (unsigned)((c ^ ((col >> 3) & 1)) * 16);
+    return (unsigned)((c ^ ((col >> 2) & 3)) * 16);
+}
+
+template <typename T>
+__device__ inline T bld(const unsigned char* base, unsigned off) { return *reinterpret_cast<const T*>(base + off); }
+template <typename T>
+__device__ inline void bst(unsigned char* base, unsigned off, T v) { *reinterpret_cast<T*>(base + off) = v; }
+
+// fp32 -> (bf16 high part, bf16 low part) packed pairs: x ~ hi + lo to 2^-16.
+__device__ inline void split2(float a, float b, unsigned& hi, unsigned& lo)
+{
+    hi = pack_bf16x2(a, b);
+    const float ah = __builtin_bit_cast(float, hi << 16), bh = __builtin_bit_cast(float, hi & 0xffff0000u);
+    lo = pack_bf16x2(a - ah, b - bh);
+}
+
+// NT: 16-query tiles per block (1: 4 x 4 queries, 4: 8 x 8 queries).
+template <int D, int NT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_block_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                      const __bf16* __restrict__ v, const __bf16* __restrict__ rel_h,
+                      const __bf16* __restrict__ rel_w, const __bf16* __restrict__ out,
+                      const __bf16* __restrict__ dout, const float* __restrict__ lse,
+                      __bf16* __restrict__ dq, float* __restrict__ part_kv, float* __restrict__ part_rel,
+                      Geometry g, BwdMfmaPlan p)
+{
+    constexpr int KPL = D / 4;
+    constexpr int CPP = D / 8;                  // 16-byte chunks per pixel
+    constexpr unsigned PIXB = D * 2;
+    constexpr unsigned ROWB = kBCols * PIXB;    // bytes per K / V row
+    constexpr int NQ = 16 * NT;
+    typedef typename Frag<D>::T FragT;
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15, gq = lane >> 4;
+    const int r = g.r;
+    const float alpha = p.alpha;
+
+    int64_t wg = blockIdx.x;
+    if (p.remap_xcd) {
+        const int64_t per = p.nwg >> 3;
+        wg = (wg & 7) * per + (wg >> 3);
+    }
+    const int64_t nblk_img = (int64_t)g.nbh * g.nbw;
+    const int64_t bh = wg / nblk_img;
+    const int rem = (int)(wg - bh * nblk_img);
+    const int by = rem / g.nbw, bx = rem - by * g.nbw;
+    const int yb = by * g.block, xb = bx * g.block;
+    const int wy0 = yb - g.halo, wx0 = xb - g.halo;            // window origin
+    const int tlo = max(0, -wy0), thi = min(r, g.H - wy0);     // in-image window rows
+    const int clo = max(0, -wx0), chi = min(r, g.W - wx0);     // in-image window columns
+    const int64_t plane = (int64_t)g.H * g.W * D;
+    const int64_t oplane = (int64_t)g.Ho * g.Wo;
+    constexpr int SIDE = NT == 1 ? 4 : 8;       // queries per block row / column
+
+    // query position of block-local query index qi (row-major over the block's query grid)
+    auto qpos = [&](int qi, int& yl, int& xl) {
+        const int iy = qi / SIDE;
+        yl = iy * g.stride;
+        xl = (qi - iy * SIDE) * g.stride;
+    };
+    auto qpix = [&](int qi) -> int64_t {      // query pixel in the image
+        int yl, xl;
+        qpos(qi, yl, xl);
+        return (int64_t)(yb + yl) * g.W + xb + xl;
+    };
+    auto opix = [&](int qi) -> int64_t {      // output pixel
+        int yl, xl;
+        qpos(qi, yl, xl);
+        return (int64_t)((yb + yl) / g.stride) * g.Wo + (xb + xl) / g.stride;
+    };
+
+    // query and dout fragments of every query tile (lane n: query 16u+n,
+    // channels gq*KPL..), issued first so they arrive during the staging
+    FragT qfa[NT], gfa[NT];
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+        qfa[u] = *reinterpret_cast<const FragT*>(q + bh * plane + qpix(16 * u + n) * D + gq * KPL);
+        gfa[u] = *reinterpret_cast<const FragT*>(dout + (bh * oplane + opix(16 * u + n)) * D + gq * KPL);
+    }
+    // the tile this wave owns in the relative and query phases (NT is 1 or 4:
+    // at most one per wave), loaded separately so no array is indexed at run time
+    const int uown = NT == 4 ? wave : 0;
+    const FragT qown = *reinterpret_cast<const FragT*>(q + bh * plane + qpix(16 * uown + n) * D + gq * KPL);
+    const FragT gown = *reinterpret_cast<const FragT*>(dout + (bh * oplane + opix(16 * uown + n)) * D + gq * KPL);
+
+    // ---------------------------------------------------------------- staging
+    {
+        // K, V (swizzled fragment layout) and K^T for window rows 0..kBRows-1,
+        // columns 0..15; everything outside the image or the window is zero
+        const __bf16* kb = k + bh * plane;
+        const __bf16* vb = v + bh * plane;
+        for (int e = tid; e < kBRows * 4 * CPP; e += 256) {
+            const int ch = e % CPP, rest = e / CPP;
+            const int t = rest >> 2, c4 = rest & 3;
+            const int iy = wy0 + t;
+            u32x4 kk[4], vv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int c = 4 * c4 + j, ix = wx0 + c;
+                kk[j] = u32x4{0u, 0u, 0u, 0u};
+                vv[j] = u32x4{0u, 0u, 0u, 0u};
+                if (t < r && c < r && iy >= 0 && iy < g.H && ix >= 0 && ix < g.W) {
+                    const int64_t off = ((int64_t)iy * g.W + ix) * D + ch * 8;
+                    kk[j] = *reinterpret_cast<const u32x4*>(kb + off);
+                    vv[j] = *reinterpret_cast<const u32x4*>(vb + off);
+                }
+                bst<u32x4>(smem, (unsigned)t * ROWB + c * PIXB + bk_chunk<D>(ch, c), kk[j]);
+                bst<u32x4>(smem, p.off_v + (unsigned)t * ROWB + c * PIXB + bk_chunk<D>(ch, c), vv[j]);
+            }
+            // K^T: channel ch*8 + 2w (+1) of the 4 columns, 8-byte rows
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                if (t >= 16) break;
+                const u32x2 lo = {__builtin_amdgcn_perm(kk[1][w], kk[0][w], 0x05040100u),
+                                  __builtin_amdgcn_perm(kk[3][w], kk[2][w], 0x05040100u)};
+                const u32x2 hi = {__builtin_amdgcn_perm(kk[1][w], kk[0][w], 0x07060302u),
+                                  __builtin_amdgcn_perm(kk[3][w], kk[2][w], 0x07060302u)};
+                const unsigned base = p.off_kt + 2u * ((unsigned)t * kBCols + 4 * c4);
+                bst<u32x2>(smem, base + 2u * (unsigned)((ch * 8 + 2 * w) * kKtPitch), lo);
+                bst<u32x2>(smem, base + 2u * (unsigned)((ch * 8 + 2 * w + 1) * kKtPitch), hi);
+            }
+        }
+        // tables: [32][D] (A operands of table . Q^T) and [D][32] (A operands of tables^T . sums)
+        const unsigned short* rhs = reinterpret_cast<const unsigned short*>(rel_h);
+        const unsigned short* rws = reinterpret_cast<const unsigned short*>(rel_w);
+        const int nrel = 2 * r - 1;
+        for (int e = tid; e < kTabRows * D; e += 256) {
+            const int row = e / D, c = e - row * D;
+            const unsigned short hv = row < nrel ? rhs[row * D + c] : (unsigned short)0;
+            const unsigned short wv = row < nrel ? rws[row * D + c] : (unsigned short)0;
+            bst<unsigned short>(smem, p.off_tab + 2u * e, hv);
+            bst<unsigned short>(smem, p.off_tab + 2u * (kTabRows * D + e), wv);
+            bst<unsigned short>(smem, p.off_tabt + 2u * (c * kTabRows + row), hv);
+            bst<unsigned short>(smem, p.off_tabt + 2u * (D * kTabRows + c * kTabRows + row), wv);
+        }
+        // Q^T and dout^T of the block's queries; D = dout . out per query
+        const unsigned short* qs = reinterpret_cast<const unsigned short*>(q + bh * plane);
+        const unsigned short* gs = reinterpret_cast<const unsigned short*>(dout + bh * oplane * D);
+        for (int e = tid; e < NQ * D; e += 256) {
+            const int qi = e / D, c = e - qi * D;
+            bst<unsigned short>(smem, p.off_qt + 2u * (c * p.qpitch + qi), qs[qpix(qi) * D + c]);
+            bst<unsigned short>(smem, p.off_dot + 2u * (c * p.qpitch + qi), gs[opix(qi) * D + c]);
+        }
+        if (tid < NQ) {
+            const __bf16* op = out + (bh * oplane + opix(tid)) * D;
+            const __bf16* gp = dout + (bh * oplane + opix(tid)) * D;
+            float acc = 0.f;
+#pragma unroll
+            for (int c = 0; c < D; ++c) acc += (float)op[c] * (float)gp[c];
+            bst<float>(smem, p.off_d + 4u * tid, acc);
+        }
+    }
+    __syncthreads();
+
+    const unsigned kl = (unsigned)n * PIXB + (D == 16 ? bk_chunk<D>(gq >> 1, n) + (gq & 1) * 8
+                                                      : bk_chunk<D>(gq, n));
+    auto kfrag = [&](int t) { return bld<FragT>(smem, kl + (unsigned)t * ROWB); };
+    auto vfrag = [&](int t) { return bld<FragT>(smem, p.off_v + kl + (unsigned)t * ROWB); };
+    const unsigned scr0 = p.off_scr + wave * (kTabRows * kScrStrideB * 4) + 4u * n;
+    auto scr = [&](int row) { return scr0 + 4u * kScrStrideB * row; };
+
+    // --------------------------------------- relative tables per query tile
+    if (wave < NT) {
+        const int u = uown;
+        const FragT qf = qown;
+        int yl, xl;
+        qpos(16 * u + n, yl, xl);
+        const float lse2 = lse[bh * oplane + opix(16 * u + n)] * 1.4426950408889634f;
+        for (int tab = 0; tab < 2; ++tab) {          // 0: rel_w -> width table, 1: rel_h -> height
+            f32x4 gv[2];
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                const FragT a = bld<FragT>(smem, p.off_tab + 2u * ((tab == 0 ? kTabRows * D : 0) +
+                                                                     (rt * 16 + n) * D + gq * KPL));
+                gv[rt] = Frag<D>::mma(a, qf, f32x4{0.f, 0.f, 0.f, 0.f});
+            }
+            // scratch row j = table row j, column n = query n
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) bst<float>(smem, scr(rt * 16 + 4 * gq + i), gv[rt][i]);
+            // window position w = 4g+i <- table row w - (yl or xl) + r - 1
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int w = 4 * gq + i;
+                const int row = w - (tab == 0 ? xl : yl) + r - 1;   // in [0, 31) for w < 16
+                const float gval = bld<float>(smem, scr(row));
+                if (tab == 0) {
+                    const bool in = w >= clo && w < chi;
+                    bst<float>(smem, p.off_rw + 4u * (w * NQ + 16 * u + n), in ? gval : kMaskLogit);
+                } else {
+                    const bool in = w >= tlo && w < thi;
+                    bst<float>(smem, p.off_rh + 4u * (w * NQ + 16 * u + n), in ? alpha * gval - lse2 : -INFINITY);
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ------------------------------------------------------------ query path
+    f32x4 drelT[2][2][D / 16];                     // [table][R tile][channel tile], this wave's queries
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int mt = 0; mt < D / 16; ++mt) drelT[a][b][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // column-indicator operand: A[m][8g+j] = 1 if window column 4g + (j%4) == m
+    u32x4 ecol;
+    {
+        const unsigned one = (unsigned)0x3F80;
+        unsigned w01 = 0, w23 = 0;
+        if (n == 4 * gq + 0) w01 |= one;
+        if (n == 4 * gq + 1) w01 |= one << 16;
+        if (n == 4 * gq + 2) w23 |= one;
+        if (n == 4 * gq + 3) w23 |= one << 16;
+        ecol = u32x4{w01, w23, w01, w23};
+    }
+
+    if (wave < NT) {
+        const int u = uown;
+        const FragT qf = qown, gf = gown;
+        const float Dn = bld<float>(smem, p.off_d + 4u * (16 * u + n));
+        f32x4 cinit;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cinit[i] = bld<float>(smem, p.off_rw + 4u * ((4 * gq + i) * NQ + 16 * u + n));
+        f32x4 dqT[D / 16], ghT = {0.f, 0.f, 0.f, 0.f}, gwT = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int mt = 0; mt < D / 16; ++mt) dqT[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const unsigned ktl = p.off_kt + 2u * ((unsigned)n * kKtPitch + 4 * gq);
+        // one K=32 step per two window rows; a last odd row goes alone (its
+        // partner's weights and K^T operand are zero)
+        auto step = [&](auto two_c, int t0) {
+            constexpr bool two = decltype(two_c)::value;
+            const int t1 = two ? t0 + 1 : t0;
+            const float c0 = bld<float>(smem, p.off_rh + 4u * (t0 * NQ + 16 * u + n));
+            const f32x4 s0 = Frag<D>::mma(kfrag(t0), qf, cinit);
+            const f32x4 d0 = Frag<D>::mma(vfrag(t0), gf, f32x4{0.f, 0.f, 0.f, 0.f});
+            float l0[4], l1[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) l0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], alpha, c0)) * (d0[i] - Dn);
+            if (two) {
+                const float c1 = bld<float>(smem, p.off_rh + 4u * (t1 * NQ + 16 * u + n));
+                const f32x4 s1 = Frag<D>::mma(kfrag(t1), qf, cinit);
+                const f32x4 d1 = Frag<D>::mma(vfrag(t1), gf, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int i = 0; i < 4; ++i) l1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], alpha, c1)) * (d1[i] - Dn);
+            }
+            const s16x8 lp = __builtin_bit_cast(s16x8, u32x4{pack_bf16x2(l0[0], l0[1]), pack_bf16x2(l0[2], l0[3]),
+                                                             pack_bf16x2(l1[0], l1[1]), pack_bf16x2(l1[2], l1[3])});
+#pragma unroll
+            for (int mt = 0; mt < D / 16; ++mt) {
+                const unsigned a = ktl + 2u * (unsigned)(mt * 16 * kKtPitch);
+                const u32x2 x0 = bld<u32x2>(smem, a + 2u * (unsigned)(t0 * kBCols));
+                const u32x2 x1 = two ? bld<u32x2>(smem, a + 2u * (unsigned)(t1 * kBCols)) : u32x2{0u, 0u};
+                dqT[mt] = mma_k32(__builtin_bit_cast(s16x8, u32x4{x0[0], x0[1], x1[0], x1[1]}), lp, dqT[mt]);
+            }
+            const unsigned e0 = n == t0 ? 0x3F803F80u : 0u, e1 = (two && n == t1) ? 0x3F803F80u : 0u;
+            ghT = mma_k32(__builtin_bit_cast(s16x8, u32x4{e0, e0, e1, e1}), lp, ghT);
+            gwT = mma_k32(__builtin_bit_cast(s16x8, ecol), lp, gwT);
+        };
+        int t0 = tlo;
+        for (; t0 + 1 < thi; t0 += 2) step(std::true_type{}, t0);
+        if (t0 < thi) step(std::false_type{}, t0);
+
+        // sums re-indexed by table row (R = w - yl + r - 1 for rows, - xl for
+        // columns), zero elsewhere, in this wave's scratch; then
+        //   dq^T += table^T . sums  and  drel^T += Q^T . sums^T
+        int yl, xl;
+        qpos(16 * u + n, yl, xl);
+#pragma unroll
+        for (int tab = 0; tab < 2; ++tab) {            // 0: rows -> rel_h, 1: columns -> rel_w
+            const f32x4 gs = tab == 0 ? ghT : gwT;
+            const int sh = (tab == 0 ? yl : xl);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) bst<float>(smem, scr(8 * gq + j), 0.f);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int w = 4 * gq + i;
+                if (w < r) bst<float>(smem, scr(w - sh + r - 1), gs[i]);
+            }
+            // B operand of table^T . sums: lane (n, g) = query n, table rows 8g..8g+7
+            float sv[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sv[j] = bld<float>(smem, scr(8 * gq + j));
+            unsigned hw[4], lw[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) split2(sv[2 * j], sv[2 * j + 1], hw[j], lw[j]);
+            const u32x4 bh4 = {hw[0], hw[1], hw[2], hw[3]}, bl4 = {lw[0], lw[1], lw[2], lw[3]};
+            const unsigned tt = p.off_tabt + 2u * ((tab == 0 ? 0 : D * kTabRows) + gq * 8);
+#pragma unroll
+            for (int mt = 0; mt < D / 16; ++mt) {
+                const s16x8 at = bld<s16x8>(smem, tt + 2u * (unsigned)((mt * 16 + n) * kTabRows));
+                dqT[mt] = mma_k32(at, __builtin_bit_cast(s16x8, bh4), dqT[mt]);
+                dqT[mt] = mma_k32(at, __builtin_bit_cast(s16x8, bl4), dqT[mt]);
+            }
+            // table gradient: drel^T[c][R] += sum_q Q^T[c][q] sums[R][q]:
+            // A = Q^T (lane n': channel, queries 4g'..4g'+3 of tile u),
+            // B = sums^T (lane n: table row 16 rt + n, queries 4g..4g+3)
+            wave_lds_sync();   // the scratch column reads above are done before the row reads below
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                const f32x4 sr = bld<f32x4>(smem, p.off_scr + wave * (kTabRows * kScrStrideB * 4) +
+                                                      4u * (kScrStrideB * (rt * 16 + n) + 4 * gq));
+                unsigned h01, l01, h23, l23;
+                split2(sr[0], sr[1], h01, l01);
+                split2(sr[2], sr[3], h23, l23);
+                const s16x4 bhi = __builtin_bit_cast(s16x4, u32x2{h01, h23});
+                const s16x4 blo = __builtin_bit_cast(s16x4, u32x2{l01, l23});
+#pragma unroll
+                for (int mt = 0; mt < D / 16; ++mt) {
+                    const s16x4 aq = bld<s16x4>(smem, p.off_qt + 2u * ((mt * 16 + n) * p.qpitch + 16 * u + 4 * gq));
+                    drelT[tab == 0 ? 0 : 1][rt][mt] =
+                        __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aq, bhi, drelT[tab == 0 ? 0 : 1][rt][mt], 0, 0, 0);
+                    drelT[tab == 0 ? 0 : 1][rt][mt] =
+                        __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aq, blo, drelT[tab == 0 ? 0 : 1][rt][mt], 0, 0, 0);
+                }
+            }
+            wave_lds_sync();   // scratch is rewritten by the next table
+        }
+        // dq = scale * dq^T (lane: query n, channels 16mt + 4g + i)
+        __bf16* dp = dq + bh * plane + qpix(16 * u + n) * D + gq * 4;
+#pragma unroll
+        for (int mt = 0; mt < D / 16; ++mt)
+            *reinterpret_cast<u32x2*>(dp + mt * 16) =
+                u32x2{pack_bf16x2(dqT[mt][0] * g.scale, dqT[mt][1] * g.scale),
+                      pack_bf16x2(dqT[mt][2] * g.scale, dqT[mt][3] * g.scale)};
+    }
+
+    // -------------------------------------------------------------- key path
+    {
+        constexpr int NP = (NT + 1) / 2;             // pairs of query tiles
+        FragT qf[NT], gf[NT];
+        f32x4 cw[NT], Dv[NT];
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+            qf[u] = qfa[u];
+            gf[u] = gfa[u];
+            cw[u] = bld<f32x4>(smem, p.off_rw + 4u * (n * NQ + 16 * u + 4 * gq));   // column n, queries 4g..
+            Dv[u] = bld<f32x4>(smem, p.off_d + 4u * (16 * u + 4 * gq));
+        }
+        // A operands over query pairs: lane n' = channel, queries {4g..4g+3 of u0, of u1}
+        u32x4 qtA[NP][D / 16], gtA[NP][D / 16];
+#pragma unroll
+        for (int pr = 0; pr < NP; ++pr)
+#pragma unroll
+            for (int mt = 0; mt < D / 16; ++mt) {
+                const unsigned rowq = p.off_qt + 2u * ((mt * 16 + n) * p.qpitch + 4 * gq);
+                const unsigned rowg = p.off_dot + 2u * ((mt * 16 + n) * p.qpitch + 4 * gq);
+                const u32x2 a0 = bld<u32x2>(smem, rowq + 2u * (32 * pr)), g0 = bld<u32x2>(smem, rowg + 2u * (32 * pr));
+                u32x2 a1 = {0u, 0u}, g1 = {0u, 0u};
+                if (2 * pr + 1 < NT) {
+                    a1 = bld<u32x2>(smem, rowq + 2u * (32 * pr + 16));
+                    g1 = bld<u32x2>(smem, rowg + 2u * (32 * pr + 16));
+                }
+                qtA[pr][mt] = u32x4{a0[0], a0[1], a1[0], a1[1]};
+                gtA[pr][mt] = u32x4{g0[0], g0[1], g1[0], g1[1]};
+            }
+        const int64_t blk = wg;
+        for (int t = tlo + wave; t < thi; t += 4) {
+            const FragT kf = kfrag(t), vf = vfrag(t);
+            f32x4 dkT[D / 16], dvT[D / 16];
+#pragma unroll
+            for (int mt = 0; mt < D / 16; ++mt) dkT[mt] = dvT[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int pr = 0; pr < NP; ++pr) {
+                unsigned pw[4] = {0u, 0u, 0u, 0u}, lw[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int u = 2 * pr + h;
+                    if (u >= NT) continue;
+                    const f32x4 s = Frag<D>::mma(qf[u], kf, cw[u]);
+                    const f32x4 dpv = Frag<D>::mma(gf[u], vf, f32x4{0.f, 0.f, 0.f, 0.f});
+                    const f32x4 c = bld<f32x4>(smem, p.off_rh + 4u * (t * NQ + 16 * u + 4 * gq));
+                    float pv[4], lv[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        pv[i] = __builtin_amdgcn_exp2f(fmaf(s[i], alpha, c[i]));
+                        lv[i] = pv[i] * (dpv[i] - Dv[u][i]);
+                    }
+                    pw[2 * h] = pack_bf16x2(pv[0], pv[1]);
+                    pw[2 * h + 1] = pack_bf16x2(pv[2], pv[3]);
+                    lw[2 * h] = pack_bf16x2(lv[0], lv[1]);
+                    lw[2 * h + 1] = pack_bf16x2(lv[2], lv[3]);
+                }
+                const s16x8 pp = __builtin_bit_cast(s16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+                const s16x8 lp = __builtin_bit_cast(s16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
+#pragma unroll
+                for (int mt = 0; mt < D / 16; ++mt) {
+                    dvT[mt] = mma_k32(__builtin_bit_cast(s16x8, gtA[pr][mt]), pp, dvT[mt]);
+                    dkT[mt] = mma_k32(__builtin_bit_cast(s16x8, qtA[pr][mt]), lp, dkT[mt]);
+                }
+            }
+            // this block's share for window row t, column n: [dk(D) | dv(D)] fp32
+            if (n < r) {
+                float* dst = part_kv + ((blk * r + t) * r + n) * (2 * D) + 4 * gq;
+#pragma unroll
+                for (int mt = 0; mt < D / 16; ++mt) {
+                    *reinterpret_cast<f32x4*>(dst + 16 * mt) = dkT[mt] * g.scale;
+                    *reinterpret_cast<f32x4*>(dst + D + 16 * mt) = dvT[mt];
+                }
+            }
+        }
+    }
+
+    // ---------------------------------------- the block's table gradients
+    __syncthreads();                   // every wave is done with the K / V region
+    float* red = reinterpret_cast<float*>(smem);   // [wave][tab][32][D]
+#pragma unroll
+    for (int tab = 0; tab < 2; ++tab)
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int mt = 0; mt < D / 16; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)    // lane (n, g): channel 16mt + 4g + i, table row 16rt + n
+                    red[((wave * 2 + tab) * kTabRows + rt * 16 + n) * D + mt * 16 + 4 * gq + i] = drelT[tab][rt][mt][i];
+    __syncthreads();
+    const int E = (2 * r - 1) * D;
+    float* dst = part_rel + wg * 2 * (int64_t)E;
+    for (int e = tid; e < 2 * E; e += 256) {
+        const int tab = e / E, rr = e - tab * E;
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) acc += red[(w * 2 + tab) * kTabRows * D + rr];
+        // part layout: table 0 = rel_h (row sums), 1 = rel_w (column sums)
+        dst[e] = acc * g.scale;
+    }
+}
+
+// dk, dv of every key: the shares of the windows holding it, summed over
+// the blocks (by, bx) in increasing order; one thread per (key, 4 channels).
+template <int D>
+__global__ __launch_bounds__(256)
+void bwd_gather_kernel(const float* __restrict__ part_kv, __bf16* __restrict__ dk, __bf16* __restrict__ dv,
+                       Geometry g)
+{
+    constexpr int G4 = D / 4;
+    const int64_t total = g.BH * g.H * g.W * G4;
+    const int64_t nblk_img = (int64_t)g.nbh * g.nbw;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+        const int c4 = (int)(i % G4);
+        const int64_t pix = i / G4;
+        const int64_t bh = pix / ((int64_t)g.H * g.W);
+        const int rem = (int)(pix - bh * g.H * g.W);
+        const int ky = rem / g.W, kx = rem - ky * g.W;
+        // blocks whose window [by*b - h, by*b + b + h) holds ky lie within
+        // ceil(h/b) block rows of ky's own; likewise for columns
+        const int A = (g.halo + g.block - 1) / g.block;
+        const int by0 = ky / g.block, bx0 = kx / g.block;
+        f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+        for (int by = max(0, by0 - A); by <= min(g.nbh - 1, by0 + A); ++by) {
+            const int t = ky - (by * g.block - g.halo);
+            if (t < 0 || t >= g.r) continue;
+            for (int bx = max(0, bx0 - A); bx <= min(g.nbw - 1, bx0 + A); ++bx) {
+                const int u = kx - (bx * g.block - g.halo);
+                if (u < 0 || u >= g.r) continue;
+                const int64_t blk = bh * nblk_img + (int64_t)by * g.nbw + bx;
+                const float* src = part_kv + ((blk * g.r + t) * g.r + u) * (2 * D) + 4 * c4;
+                sk += *reinterpret_cast<const f32x4*>(src);
+                sv += *reinterpret_cast<const f32x4*>(src + D);
+            }
+        }
+        const int64_t o = pix * D + 4 * c4;
+        *reinterpret_cast<u32x2*>(dk + o) = u32x2{pack_bf16x2(sk[0], sk[1]), pack_bf16x2(sk[2], sk[3])};
+        *reinterpret_cast<u32x2*>(dv + o) = u32x2{pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3])};
+    }
+}
+
+static int brup(int x, int m) { return (x + m - 1) / m * m; }
+
+static BwdMfmaPlan bwd_mfma_plan(const Geometry& g)
+{
+    BwdMfmaPlan p{};
+    const int side = g.block / g.stride;
+    p.nq = side * side;
+    p.qpitch = p.nq + 8;                       // keeps the 8-byte Q^T reads of 16 channels spread
+    const int D = g.d;
+    const int kb = kBRows * kBCols * D * 2;
+    p.off_v = kb;
+    p.off_kt = brup(p.off_v + kb, 16);
+    p.off_tab = brup(p.off_kt + D * kKtPitch * 2, 16);
+    p.off_tabt = brup(p.off_tab + 2 * kTabRows * D * 2, 16);
+    p.off_qt = brup(p.off_tabt + 2 * kTabRows * D * 2, 16);
+    p.off_dot = brup(p.off_qt + D * p.qpitch * 2, 16);
+    p.off_rw = brup(p.off_dot + D * p.qpitch * 2, 16);
+    p.off_rh = brup(p.off_rw + kBCols * p.nq * 4, 16);
+    p.off_d = brup(p.off_rh + kBRows * p.nq * 4, 16);
+    p.off_scr = brup(p.off_d + p.nq * 4, 16);
+    p.lds_bytes = p.off_scr + 4 * kTabRows * kScrStrideB * 4;
+    // the final table reduction reuses the front of LDS: 4 waves x 2 x 32 x D floats
+    p.lds_bytes = std::max(p.lds_bytes, 4 * 2 * kTabRows * D * 4);
+    return p;
+}
+
+bool bwd_mfma_supported(const Geometry& g, bool bf16)
+{
+    if (!bf16 || (g.d != 16 && g.d != 32) || g.r > 16) return false;
+    if (g.H % g.block || g.W % g.block) return false;          // full blocks only
+    const int side = g.block / g.stride;
+    if (side % 4) return false;
+    const int nt = side * side / 16;
+    if (nt != 1 && nt != 4) return false;
+    if ((int64_t)g.H * g.W >= (int64_t(1) << 31)) return false;
+    return true;
+}
+
+// Workspace floats the matrix-core backward needs beyond out / lse:
+// per-block dk/dv shares and table partials (and the table reduction's
+// first level).
+int64_t bwd_mfma_workspace_floats(const Geometry& g, int64_t nchunks)
+{
+    const int64_t nblocks = g.BH * g.nbh * g.nbw;
+    const int64_t e2 = 2 * (int64_t)(2 * g.r - 1) * g.d;
+    return nblocks * g.r * g.r * 2 * g.d + nblocks * e2 + nchunks * e2;
+}
+
+template <int D, int NT>
+static hipError_t bwd_mfma_t(const void* q, const void* k, const void* v, const void* rh, const void* rw,
+                             const void* out, const void* dout, const float* lse, void* dq, float* part_kv,
+                             float* part_rel, const Geometry& g, hipStream_t st)
+{
+    BwdMfmaPlan p = bwd_mfma_plan(g);
+    p.nwg = g.BH * g.nbh * g.nbw;
+    p.remap_xcd = (p.nwg % 8 == 0) ? 1 : 0;
+    p.alpha = (float)((double)g.scale * 1.4426950408889634);
+    auto kern = bwd_block_kernel<D, NT>;
+    if (p.lds_bytes > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)p.nwg), dim3(256), p.lds_bytes, st,
+                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)rh,
+                       (const __bf16*)rw, (const __bf16*)out, (const __bf16*)dout, lse, (__bf16*)dq,
+                       part_kv, part_rel, g, p);
+    return hipGetLastError();
+}
+
+// Block kernel + dk/dv gather.  The table partials land in part_rel
+// ([nblocks][2][2r-1][d], scaled), ready for the fixed-order reduction.
+hipError_t launch_zero_bf16(void* p, int64_t n, hipStream_t st);
+
+hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const void* rh, const void* rw,
+                           const void* out, const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           float* part_kv, float* part_rel, const Geometry& g, hipStream_t st)
+{
+    const int nt = (g.block / g.stride) * (g.block / g.stride) / 16;
+    hipError_t e;
+    if (g.stride > 1) {   // dq is zero at the pixels that are not queries
+        e = launch_zero_bf16(dq, g.BH * g.H * g.W * g.d, st);
+        if (e != hipSuccess) return e;
+    }
+    if (g.d == 16) e = nt == 1 ? bwd_mfma_t<16, 1>(q, k, v, rh, rw, out, dout, lse, dq, part_kv, part_rel, g, st)
+                               : bwd_mfma_t<16, 4>(q, k, v, rh, rw, out, dout, lse, dq, part_kv, part_rel, g, st);
+    else e = nt == 1 ? bwd_mfma_t<32, 1>(q, k, v, rh, rw, out, dout, lse, dq, part_kv, part_rel, g, st)
+                     : bwd_mfma_t<32, 4>(q, k, v, rh, rw, out, dout, lse, dq, part_kv, part_rel, g, st);
+    if (e != hipSuccess) return e;
+    const int64_t total = g.BH * g.H * g.W * (g.d / 4);
+    const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((total + 255) / 256, 1 << 20));
+    if (g.d == 16)
+        hipLaunchKernelGGL(bwd_gather_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, st,
+                           (const float*)part_kv, (__bf16*)dk, (__bf16*)dv, g);
+    else
+        hipLaunchKernelGGL(bwd_gather_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, st,
+                           (const float*)part_kv, (__bf16*)dk, (__bf16*)dv, g);
+    return hipGetLastError();
+}
+
+}  // namespace halo

@@ -159,9 +159,15 @@ int halo_attn_fwd(const void* q, const void* k, const void* v,
  * input or another output, and HALO_ERR_NULL when only one of out and lse
  * is given.  drel_h and drel_w must be non-NULL; if a size
  * is zero they are set to zero (the gradient of an empty sum) and no other
- * pointer is inspected.  kernel: a halo_kernel value; only the generic
- * kernels exist for the backward, so HALO_KERNEL_MFMA and MFMA_STRIP return
- * HALO_ERR_UNSUPPORTED.
+ * pointer is inspected.
+ *
+ * kernel: a halo_kernel value.  GENERIC runs fp32-vector kernels for every
+ * supported shape.  MFMA (and MFMA_STRIP, a synonym here) runs the
+ * matrix-core backward: bf16, d in {16, 32}, window side r <= 16, block
+ * dividing H and W, and (block/query_stride)^2 in {16, 64}; other arguments
+ * return HALO_ERR_UNSUPPORTED.  AUTO takes MFMA when it applies.  The
+ * matrix-core path keeps, per block, its window's share of dk and dv in the
+ * workspace and sums the shares of every key in a fixed order.
  */
 int halo_attn_bwd_kernel(const void* q, const void* k, const void* v,
                          const void* rel_h, const void* rel_w,

@@ -108,8 +108,33 @@ def test_small_shapes_match_oracle(shape, dtype, use_fwd):
     B, heads, H, W, d, block, halo, stride = shape
     say(f"bwd case {shape} {dtype} use_fwd={use_fwd}")
     ins, g = case(*shape, dtype, seed=sum(shape))
-    got = gpu_bwd(ins, g, block, halo, stride, use_fwd=use_fwd)
+    got = gpu_bwd(ins, g, block, halo, stride, use_fwd=use_fwd, kernel="generic")
     compare(got, ref_bwd(ins, g, block, halo, stride), dtype, str(shape))
+
+
+def mfma_ok(shape):
+    B, heads, H, W, d, block, halo, stride = shape
+    side = block // stride
+    return (d in (16, 32) and block + 2 * halo <= 16 and H % block == 0 and W % block == 0
+            and side % 4 == 0 and side * side in (16, 64))
+
+
+MFMA_SHAPES = [s for s in SMALL if mfma_ok(s)] + [
+    (1, 2, 32, 48, 32, 8, 3, 2),   # d = 32, strided
+    (2, 1, 16, 16, 16, 8, 4, 1),   # r = 16, the widest window of the path
+    (1, 1, 8, 8, 16, 4, 6, 1),     # r = 16 with 4x4 blocks and stride 1 (one query tile)
+]
+
+
+@pytest.mark.parametrize("use_fwd", [False, True], ids=["recompute", "fwd_lse"])
+@pytest.mark.parametrize("shape", MFMA_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_matrix_core_backward_matches_oracle(shape, use_fwd):
+    B, heads, H, W, d, block, halo, stride = shape
+    say(f"bwd mfma case {shape} use_fwd={use_fwd}")
+    ins, g = case(*shape, "bf16", seed=3 * sum(shape))
+    got = gpu_bwd(ins, g, block, halo, stride, use_fwd=use_fwd, kernel="mfma")
+    worst = compare(got, ref_bwd(ins, g, block, halo, stride), "bf16", str(shape))
+    say(f"  worst relative error {worst:.3e}")
 
 
 @pytest.mark.parametrize("name", list(workloads.WORKLOADS))
@@ -124,12 +149,19 @@ def test_workload_full_size(name):
     say(f"  worst relative error {worst:.3e}")
 
 
-def test_deterministic():
+@pytest.mark.parametrize("kernel", ["mfma", "generic"])
+def test_deterministic(kernel):
     ins, g = case(2, 4, 32, 32, 16, 8, 3, 1, "bf16", seed=21)
-    a = gpu_bwd(ins, g, 8, 3, 1)
-    b = gpu_bwd(ins, g, 8, 3, 1)
+    a = gpu_bwd(ins, g, 8, 3, 1, kernel=kernel)
+    b = gpu_bwd(ins, g, 8, 3, 1, kernel=kernel)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+def test_matrix_core_backward_refuses_what_it_does_not_cover():
+    ins, g = case(1, 1, 20, 28, 16, 8, 3, 1, "bf16", seed=1)   # ragged blocks
+    with pytest.raises(HaloError):
+        gpu_bwd(ins, g, 8, 3, 1, kernel="mfma")
 
 
 def test_autograd_function_matches_direct_call():
