@@ -15,11 +15,14 @@ reads HBM.  Prints ONE JSON line (rank 0):
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
              workload on this host (reported, not a target)
 
-Backward accounting (--pass bwd): F = 10*d*r^2 per (query, head), the five
-window contractions q.k (recomputed), dout.v, dl.k, dl.q, p.dout; algorithmic
-bytes = e*d*B*heads*(2*(H/s)*(W/s) + 5*H*W): q and dout once at query
-pixels, k and v once, dq, dk, dv written once.  The roofline entry then
-covers the whole backward call (its mean time over the timed region).
+Backward (--pass bwd): one step = one halo_attn_bwd call given the forward's
+out and per-query lse (computed once per input set before the timed region,
+as a training step keeps them from its forward pass).  F = 10*d*r^2 per
+(query, head), the five window contractions q.k (recomputed), dout.v, dl.k,
+dl.q, p.dout; algorithmic bytes = e*d*B*heads*(2*(H/s)*(W/s) + 5*H*W): q and
+dout once at query pixels, k and v once, dq, dk, dv written once (out and
+lse, 1/d of that, not counted).  The roofline entry covers the whole
+backward call (its kernels' mean time per call over the timed region).
 """
 from __future__ import annotations
 
@@ -44,24 +47,42 @@ MALL_BYTES = 256 * 2 ** 20     # Infinity Cache
 # measured on (``sources`` = kernel_source_hash() at the time); otherwise the
 # bench reports traffic as null.
 MEASURED_TRAFFIC = {
-    "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 134535601, "read": 100981169, "write": 33554432,
-                                        "sources": "bdcdc81190e5bc0b"},
-    "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 144211055, "read": 103316591, "write": 40894464,
-                                      "sources": "bdcdc81190e5bc0b"},
-    "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 92508425, "read": 84119817, "write": 8388608,
-                                       "sources": "bdcdc81190e5bc0b"},
-    "large_bf16_128x128_d32_b12h3": {"bytes_per_launch": 273292758, "read": 206183894, "write": 67108864,
-                                     "sources": "bdcdc81190e5bc0b"},
+    "fwd": {
+        "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 134587580, "read": 101033148, "write": 33554432,
+                                            "sources": "5f85d071db4a6551"},
+        "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 146211362, "read": 104268322, "write": 41943040,
+                                          "sources": "5f85d071db4a6551"},
+        "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 92532794, "read": 84144186, "write": 8388608,
+                                           "sources": "5f85d071db4a6551"},
+        "large_bf16_128x128_d32_b12h3": {"bytes_per_launch": 281011610, "read": 213902746, "write": 67108864,
+                                         "sources": "5f85d071db4a6551"},
+    },
+    # backward: summed over the call's kernels (block kernel, dk/dv gather, table reduction)
+    "bwd": {
+        "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 1147056143, "read": 598919823, "write": 548136320,
+                                            "sources": "20cd801b38251cab"},
+        "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 1082461131, "read": 556341451, "write": 526119680,
+                                          "sources": "20cd801b38251cab"},
+        "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 1085189290, "read": 528664362, "write": 556524928,
+                                           "sources": "20cd801b38251cab"},
+    },
 }
 
 
-def kernel_source_hash() -> str:
-    import glob
+# Sources the timed kernels are built from, per pass (the traffic record of
+# a pass holds while these files are unchanged).
+KERNEL_SOURCES = {
+    "fwd": ["halo_common.h", "mfma_util.h", "kernel_ring.hip"],
+    "bwd": ["halo_common.h", "mfma_util.h", "kernel_bwd_mfma.hip", "kernel_bwd_generic.hip"],
+}
+
+
+def kernel_source_hash(which: str = "fwd") -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(HERE, "blocked_local_self_amd", "csrc", "*"))):
-        h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
+    for name in KERNEL_SOURCES[which]:
+        h.update(name.encode())
+        with open(os.path.join(HERE, "blocked_local_self_amd", "csrc", name), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -182,7 +203,10 @@ def main():
             g_cpu = make_grad_output(wl.B, wl.heads, wl.Ho, wl.Wo, wl.d, dtype=wl.dtype, seed=s)
             if s == 0:
                 dout0_cpu = g_cpu
-            sets.append((dev_t, g_cpu.to(dev)))
+            q, k, v, rh, rw = dev_t
+            fwd = halo_attn_fwd(q, k, v, rh, rw, wl.block, wl.halo, wl.stride, kernel=args.kernel,
+                                return_lse=True)
+            sets.append((dev_t, (g_cpu.to(dev),) + fwd))
         else:
             sets.append((dev_t, torch.empty(wl.out_shape(), dtype=dev_t[0].dtype, device=dev)))
     stream = torch.cuda.current_stream(dev)
@@ -196,8 +220,9 @@ def main():
     def step(i):
         (q, k, v, rh, rw), x = sets[i % nsets]
         if bwd:
-            halo_attn_bwd(q, k, v, rh, rw, x, wl.block, wl.halo, wl.stride, kernel=args.kernel,
-                          workspace=ws, grads=grads, stream=stream)
+            g, out, lse = x
+            halo_attn_bwd(q, k, v, rh, rw, g, wl.block, wl.halo, wl.stride, out=out, lse=lse,
+                          kernel=args.kernel, workspace=ws, grads=grads, stream=stream)
         else:
             halo_attn_fwd(q, k, v, rh, rw, wl.block, wl.halo, wl.stride, out=x, kernel=args.kernel,
                           stream=stream)
@@ -221,8 +246,8 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     achieved_gbs = alg_bytes / (ms * 1e-3) / 1e9
 
-    src_hash = kernel_source_hash()
-    rec = None if bwd else MEASURED_TRAFFIC.get(wl.name)
+    src_hash = kernel_source_hash(args.which)
+    rec = MEASURED_TRAFFIC[args.which].get(wl.name)
     traffic = rec["bytes_per_launch"] if rec and rec["sources"] == src_hash else None
 
     line = {
