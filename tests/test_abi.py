@@ -88,3 +88,39 @@ def test_python_wrapper_validates_before_the_library():
     t = torch.zeros(11, 16)
     with pytest.raises(ValueError):
         halo_attn_fwd(x, x, x, t, t, 4, 1)   # CPU tensors are refused
+
+
+# ------------------------------------------------------------------ backward
+def bwd_call(lib, *, q=1, k=2, v=3, rh=4, rw=5, out=0, dout=6, lse=0, dq=7, dk=8, dv=9, drh=10, drw=11,
+             ws=12, ws_bytes=1 << 40, B=1, heads=1, H=8, W=8, d=16, block=4, halo=1, stride=1, scale=0.25,
+             dtype=1, kernel=0):
+    # fake, non-overlapping pointers (i << 36): every call below fails before any HIP call
+    ptr = lambda x: ctypes.c_void_p(x << 36 if x else None)
+    return lib.halo_attn_bwd_kernel(ptr(q), ptr(k), ptr(v), ptr(rh), ptr(rw), ptr(out), ptr(dout), ptr(lse),
+                                    ptr(dq), ptr(dk), ptr(dv), ptr(drh), ptr(drw), ptr(ws), ws_bytes,
+                                    B, heads, H, W, d, block, halo, stride, scale, dtype, kernel, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(drh=0), -1), (dict(q=0), -1), (dict(dq=0), -1), (dict(ws=0), -1), (dict(dout=0), -1),
+    (dict(out=13), -1), (dict(lse=13), -1),                  # only one of out / lse
+    (dict(dtype=5), -3), (dict(d=0), -2), (dict(stride=3), -2), (dict(kernel=7), -2),
+    (dict(scale=float("nan")), -2),
+    (dict(ws_bytes=16), -7),                                 # workspace too small
+    (dict(kernel=2, dtype=0), -4), (dict(kernel=2, H=10), -4), (dict(kernel=2, block=8, halo=5), -4),
+    (dict(dq=1), -6), (dict(dk=7), -6), (dict(ws=1), -6),   # aliasing
+])
+def test_backward_invalid_arguments_rejected_on_host(lib, kw, status):
+    assert bwd_call(lib, **kw) == status, _native.last_error()
+    assert _native.last_error() != ""
+
+
+def test_backward_workspace_query():
+    from blocked_local_self_amd import bwd_workspace_bytes
+    n = bwd_workspace_bytes(32, 8, 64, 64, 16, 8, 3, 1, "bf16")
+    nblocks, r, d = 32 * 8 * 8 * 8, 14, 16
+    assert n >= nblocks * r * r * 2 * d * 4          # per-block dk/dv shares (fp32)
+    assert bwd_workspace_bytes(0, 8, 64, 64, 16, 8, 3, 1, "bf16") == 0
+    assert bwd_workspace_bytes(1, 1, 8, 8, 16, 4, 1, 1, "fp32") > 0
+    with pytest.raises(HaloError):
+        bwd_workspace_bytes(1, 1, 8, 8, 16, 4, 1, 3, "bf16")
