@@ -39,6 +39,9 @@ def _load():
     lib.halo_ref_fwd.argtypes = [dp, dp, dp, dp, dp, dp, dp] + [ctypes.c_int] * 8 + [
         ctypes.c_double, ctypes.c_int]
     lib.halo_ref_fwd.restype = ctypes.c_int
+    lib.halo_ref_fwd_ex.argtypes = [dp, dp, dp, dp, dp, dp, dp] + [ctypes.c_int] * 8 + [
+        ctypes.c_double, ctypes.c_int, ctypes.c_int]
+    lib.halo_ref_fwd_ex.restype = ctypes.c_int
     lib.halo_ref_set_attention.argtypes = [
         ctypes.c_int, ctypes.c_int, dp, ctypes.POINTER(dp), dp, ctypes.POINTER(dp),
         ctypes.c_double, dp, dp]
@@ -68,9 +71,13 @@ def max_threads() -> int:
     return int(_load().halo_ref_max_threads())
 
 
+# Semantic variants (flags of halo_ref_fwd_ex); see halo_ref.c.
+CENTRED_OFFSET, ZERO_PAD, CENTRED_MASK, HALF_SPLIT = 1, 2, 4, 8
+
+
 def halo_attn_ref(q, k, v, rel_h, rel_w, block: int, halo: int,
                   query_stride: int = 1, scale: float | None = None,
-                  threads: int = 0, return_lse: bool = False):
+                  threads: int = 0, return_lse: bool = False, flags: int = 0):
     """Forward pass, fp64.
 
     q, k, v: [B, heads, H, W, d]; rel_h, rel_w: [2*(block+2*halo)-1, d].
@@ -79,6 +86,8 @@ def halo_attn_ref(q, k, v, rel_h, rel_w, block: int, halo: int,
     ``scale=None`` means d**-0.5, the value the HaloAttention module uses.
     With ``return_lse`` also returns lse [B, heads, H/s, W/s]: per query,
     log sum_j exp(l_j) over its window keys (the log softmax normaliser).
+    ``flags``: OR of CENTRED_OFFSET, ZERO_PAD, CENTRED_MASK, HALF_SPLIT
+    (variants of the semantics; 0 = the pages' reading).
     """
     q, k, v, rel_h, rel_w = (_f64(t) for t in (q, k, v, rel_h, rel_w))
     _check(q, k, v, rel_h, rel_w, block, halo, query_stride)
@@ -88,9 +97,9 @@ def halo_attn_ref(q, k, v, rel_h, rel_w, block: int, halo: int,
         scale = float(d) ** -0.5
     out = np.zeros((B, heads, H // s, W // s, d), dtype=np.float64)
     lse = np.zeros((B, heads, H // s, W // s), dtype=np.float64) if return_lse else None
-    rc = _load().halo_ref_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(rel_h), _ptr(rel_w), _ptr(out),
-                              _ptr(lse) if return_lse else None,
-                              B, heads, H, W, d, block, halo, s, float(scale), int(threads))
+    rc = _load().halo_ref_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(rel_h), _ptr(rel_w), _ptr(out),
+                                 _ptr(lse) if return_lse else None,
+                                 B, heads, H, W, d, block, halo, s, float(scale), int(flags), int(threads))
     if rc != 0:
         raise ValueError(f"halo_ref_fwd failed with status {rc}")
     return (out, lse) if return_lse else out

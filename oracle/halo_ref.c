@@ -108,18 +108,38 @@ static int check_shape(int B, int heads, int H, int W, int d, int block,
  * Returns 0 on success, -1 on a null pointer, -2 on a bad shape,
  * -3 when scratch memory cannot be allocated.
  */
-int halo_ref_fwd(const double* q, const double* k, const double* v,
-                 const double* rel_h, const double* rel_w, double* out, double* lse,
-                 int B, int heads, int H, int W, int d,
-                 int block, int halo, int stride, double scale, int nthreads)
+/*
+ * Variants of the semantics (flags, OR-ed), for matching other readings of
+ * the pages:
+ *   HALO_REF_CENTRED_OFFSET (1): table row of displacement D is D + r - 1
+ *     (the table's centre row) instead of D + r - 1 + h;
+ *   HALO_REF_ZERO_PAD (2): window positions outside the image take part as
+ *     zero keys and values (the "padding at image borders" of section 2.2
+ *     read literally) instead of being left out;
+ *   HALO_REF_CENTRED_MASK (4): a query attends only to the keys of its
+ *     window within h rows and h columns of it (the centred (2h+1)^2
+ *     neighbourhood of SASA, which section 2.2 says the blocked form
+ *     drops);
+ *   HALO_REF_HALF_SPLIT (8): the height embedding uses channels [0, d/2) and
+ *     the width embedding channels [d/2, d) only (appendix A's factorised
+ *     embedding, each half of the channels per axis).
+ */
+int halo_ref_fwd_ex(const double* q, const double* k, const double* v,
+                    const double* rel_h, const double* rel_w, double* out, double* lse,
+                    int B, int heads, int H, int W, int d,
+                    int block, int halo, int stride, double scale, int flags, int nthreads)
 {
     if (check_shape(B, heads, H, W, d, block, halo, stride)) return -2;
+    if (flags & ~15) return -2;
     const long slices = (long)B * heads;
     if (slices == 0 || H == 0 || W == 0) return 0;
     if (!q || !k || !v || !rel_h || !rel_w || !out) return -1;
 
     const int r = block + 2 * halo;        /* window side */
-    const int c0 = r - 1 + halo;           /* table row of displacement 0 */
+    const int c0 = (flags & 1) ? r - 1 : r - 1 + halo;   /* table row of displacement 0 */
+    const int zero_pad = (flags & 2) != 0, centred = (flags & 4) != 0;
+    const int hlo = 0, hhi = (flags & 8) ? d / 2 : d;     /* channels of the height term */
+    const int wlo = (flags & 8) ? d / 2 : 0, whi = d;     /* and of the width term */
     const int Ho = H / stride, Wo = W / stride;
     const long plane = (long)H * W * d;    /* one (batch, head) slice */
     const long oplane = (long)Ho * Wo * d;
@@ -135,8 +155,9 @@ int halo_ref_fwd(const double* q, const double* k, const double* v,
     const double** vals = malloc(sizeof(double*) * nk * nt);
     double* bias = malloc(sizeof(double) * nk * nt);
     double* logits = malloc(sizeof(double) * nk * nt);
-    if (!keys || !vals || !bias || !logits) {
-        free(keys); free(vals); free(bias); free(logits);
+    double* zero = calloc((size_t)d, sizeof(double));    /* key and value of a padded position */
+    if (!keys || !vals || !bias || !logits || !zero) {
+        free(keys); free(vals); free(bias); free(logits); free(zero);
         return -3;
     }
 
@@ -166,14 +187,20 @@ int halo_ref_fwd(const double* q, const double* k, const double* v,
                 const double* qv = qs + ((long)y * W + x) * d;
                 int n = 0;
                 for (int ky = y0; ky < y0 + r; ++ky) {
-                    if (ky < 0 || ky >= H) continue;      /* off-image row */
-                    const double rh = dot(qv, rel_h + (long)(ky - y + c0) * d, d);
+                    const int row_in = ky >= 0 && ky < H;
+                    if (!row_in && !zero_pad) continue;              /* off-image row */
+                    if (centred && (ky < y - halo || ky > y + halo)) continue;
+                    const double* rhr = rel_h + (long)(ky - y + c0) * d;
+                    const double rh = dot(qv + hlo, rhr + hlo, hhi - hlo);
                     for (int kx = x0; kx < x0 + r; ++kx) {
-                        if (kx < 0 || kx >= W) continue;  /* off-image column */
+                        const int in = row_in && kx >= 0 && kx < W;
+                        if (!in && !zero_pad) continue;              /* off-image column */
+                        if (centred && (kx < x - halo || kx > x + halo)) continue;
                         const long off = ((long)ky * W + kx) * d;
-                        tk[n] = ks + off;
-                        tv[n] = vs + off;
-                        tb[n] = rh + dot(qv, rel_w + (long)(kx - x + c0) * d, d);
+                        tk[n] = in ? ks + off : zero;
+                        tv[n] = in ? vs + off : zero;
+                        const double* rwr = rel_w + (long)(kx - x + c0) * d;
+                        tb[n] = rh + dot(qv + wlo, rwr + wlo, whi - wlo);
                         ++n;
                     }
                 }
@@ -188,7 +215,18 @@ int halo_ref_fwd(const double* q, const double* k, const double* v,
     free(vals);
     free(bias);
     free(logits);
+    free(zero);
     return 0;
+}
+
+/* The pages' default semantics: halo_ref_fwd_ex with no flags. */
+int halo_ref_fwd(const double* q, const double* k, const double* v,
+                 const double* rel_h, const double* rel_w, double* out, double* lse,
+                 int B, int heads, int H, int W, int d,
+                 int block, int halo, int stride, double scale, int nthreads)
+{
+    return halo_ref_fwd_ex(q, k, v, rel_h, rel_w, out, lse, B, heads, H, W, d, block, halo, stride,
+                           scale, 0, nthreads);
 }
 
 /*
