@@ -19,9 +19,12 @@ from __future__ import annotations
 from . import _native
 
 __all__ = ["halo_attn_fwd", "halo_attn_bwd", "bwd_workspace_bytes", "halo_attention",
-           "select_kernel", "HaloError", "KERNELS"]
+           "select_kernel", "HaloError", "KERNELS", "VARIANTS"]
 
 HaloError = _native.HaloError
+# semantic variants (flags of halo_attn_fwd_ex; see include/halo_attn.h)
+VARIANTS = {"centred_offset": _native.HALO_CENTRED_OFFSET, "zero_pad": _native.HALO_ZERO_PAD,
+            "centred_mask": _native.HALO_CENTRED_MASK, "half_split": _native.HALO_HALF_SPLIT}
 KERNELS = {"auto": _native.HALO_KERNEL_AUTO, "generic": _native.HALO_KERNEL_GENERIC,
            "mfma": _native.HALO_KERNEL_MFMA, "mfma_strip": _native.HALO_KERNEL_MFMA_STRIP}
 
@@ -72,7 +75,7 @@ def _check_inputs(q, k, v, rel_h, rel_w, block, halo, query_stride, **extra):
 
 def halo_attn_fwd(q, k, v, rel_h, rel_w, block: int, halo: int, query_stride: int = 1,
                   scale: float | None = None, out=None, kernel: str = "auto", stream=None,
-                  return_lse: bool = False):
+                  return_lse: bool = False, variants=()):
     """Halo attention forward.
 
     q, k, v: [B, heads, H, W, d] contiguous CUDA(HIP) tensors, float32 or bfloat16.
@@ -82,6 +85,7 @@ def halo_attn_fwd(q, k, v, rel_h, rel_w, block: int, halo: int, query_stride: in
     ``stream``: a torch.cuda.Stream (default: the current stream).
     ``return_lse``: also return lse [B, heads, H/s, W/s] float32, the natural
     log of each query's softmax normaliser (what ``halo_attn_bwd`` reuses).
+    ``variants``: names from VARIANTS (other readings of the pages' semantics).
     """
     import torch
     B, heads, H, W, d = _check_inputs(q, k, v, rel_h, rel_w, block, halo, query_stride)
@@ -96,15 +100,20 @@ def halo_attn_fwd(q, k, v, rel_h, rel_w, block: int, halo: int, query_stride: in
         raise ValueError(f"out must be a contiguous {oshape} {q.dtype} tensor on {q.device}")
     if kernel not in KERNELS:
         raise ValueError(f"kernel must be one of {sorted(KERNELS)}")
+    flags = 0
+    for name in variants:
+        if name not in VARIANTS:
+            raise ValueError(f"unknown variant {name!r}; expected some of {sorted(VARIANTS)}")
+        flags |= VARIANTS[name]
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     lse = torch.empty(oshape[:4], dtype=torch.float32, device=q.device) if return_lse else None
     lib = _native.load()
     with torch.cuda.device(q.device):
-        st = lib.halo_attn_fwd_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), rel_h.data_ptr(),
-                                   rel_w.data_ptr(), out.data_ptr(), lse.data_ptr() if return_lse else None,
-                                   B, heads, H, W, d, block, halo, s, float(scale), _dtype_code(q),
-                                   KERNELS[kernel], stream.cuda_stream)
+        st = lib.halo_attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), rel_h.data_ptr(),
+                                  rel_w.data_ptr(), out.data_ptr(), lse.data_ptr() if return_lse else None,
+                                  B, heads, H, W, d, block, halo, s, float(scale), _dtype_code(q), flags,
+                                  KERNELS[kernel], stream.cuda_stream)
     _native.check(st)
     return (out, lse) if return_lse else out
 

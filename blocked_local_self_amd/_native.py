@@ -15,6 +15,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "halo_attn.h")
 
 HALO_F32, HALO_BF16 = 0, 1
 HALO_KERNEL_AUTO, HALO_KERNEL_GENERIC, HALO_KERNEL_MFMA, HALO_KERNEL_MFMA_STRIP = 0, 1, 2, 3
+HALO_CENTRED_OFFSET, HALO_ZERO_PAD, HALO_CENTRED_MASK, HALO_HALF_SPLIT = 1, 2, 4, 8
 STATUS = {0: "HALO_OK", -1: "HALO_ERR_NULL", -2: "HALO_ERR_SHAPE", -3: "HALO_ERR_DTYPE",
           -4: "HALO_ERR_UNSUPPORTED", -5: "HALO_ERR_HIP", -6: "HALO_ERR_ALIAS",
           -7: "HALO_ERR_WORKSPACE"}
@@ -43,6 +44,8 @@ def load() -> ctypes.CDLL:
     lib.halo_attn_fwd_kernel.argtypes = [vp] * 6 + [i] * 8 + [f, i, i, vp]
     lib.halo_attn_fwd_kernel.restype = i
     sz = ctypes.c_size_t
+    lib.halo_attn_fwd_ex.argtypes = [vp] * 7 + [i] * 8 + [f, i, i, i, vp]
+    lib.halo_attn_fwd_ex.restype = i
     lib.halo_attn_fwd_lse.argtypes = [vp] * 7 + [i] * 8 + [f, i, i, vp]
     lib.halo_attn_fwd_lse.restype = i
     lib.halo_attn_bwd_kernel.argtypes = [vp] * 14 + [sz] + [i] * 8 + [f, i, i, vp]

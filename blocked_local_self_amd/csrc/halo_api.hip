@@ -23,6 +23,7 @@ hipError_t launch_bwd_generic(const void* q, const void* k, const void* v, const
                               void* dq, void* dk, void* dv, float* drh, float* drw,
                               void* ws, const Geometry& g, bool bf16, hipStream_t st);
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t st);
+bool ring_supported(const Geometry& g);
 bool bwd_mfma_supported(const Geometry& g, bool bf16);
 int64_t bwd_mfma_workspace_floats(const Geometry& g, int64_t nchunks);
 int64_t bwd_rel_chunks(const Geometry& g);
@@ -157,20 +158,24 @@ size_t bwd_ws_bytes(const halo::Geometry& g, bool bf16)
 
 extern "C" {
 
-int halo_attn_fwd_lse(const void* q, const void* k, const void* v,
-                      const void* rel_h, const void* rel_w, void* out, float* lse,
-                      int B, int heads, int H, int W, int d,
-                      int block, int halo, int query_stride,
-                      float scale, int dtype, int kernel, void* stream)
+int halo_attn_fwd_ex(const void* q, const void* k, const void* v,
+                     const void* rel_h, const void* rel_w, void* out, float* lse,
+                     int B, int heads, int H, int W, int d,
+                     int block, int halo, int query_stride,
+                     float scale, int dtype, int flags, int kernel, void* stream)
 {
     g_err[0] = 0;
     if (kernel != HALO_KERNEL_AUTO && kernel != HALO_KERNEL_GENERIC && kernel != HALO_KERNEL_MFMA &&
         kernel != HALO_KERNEL_MFMA_STRIP)
         return fail(HALO_ERR_SHAPE, "kernel=%d is not a halo_kernel value", kernel);
+    if (flags & ~(HALO_CENTRED_OFFSET | HALO_ZERO_PAD | HALO_CENTRED_MASK | HALO_HALF_SPLIT))
+        return fail(HALO_ERR_SHAPE, "flags=%d has bits outside the halo_flags values", flags);
     halo::Geometry g;
     bool empty = false;
     int st = check_sizes(B, heads, H, W, d, block, halo, query_stride, scale, dtype, g, empty);
     if (st) return st;
+    g.flags = flags;
+    if (flags & HALO_CENTRED_OFFSET) g.c0 = g.r - 1;
     if (empty) return HALO_OK;   // nothing to do
 
     if (!q || !k || !v || !rel_h || !rel_w || !out)
@@ -192,11 +197,15 @@ int halo_attn_fwd_lse(const void* q, const void* k, const void* v,
         return fail(HALO_ERR_ALIAS, "lse overlaps an input tensor or out");
 
     const bool bf16 = dtype == HALO_BF16;
-    const bool mfma_ok = halo::mfma_supported(d, r, block, query_stride, bf16);
+    // the variants run on the ring kernel and the generic kernel only
+    const bool mfma_ok = halo::mfma_supported(d, r, block, query_stride, bf16) &&
+                         (flags == 0 || halo::ring_supported(g));
     if ((kernel == HALO_KERNEL_MFMA || kernel == HALO_KERNEL_MFMA_STRIP) && !mfma_ok)
         return fail(HALO_ERR_UNSUPPORTED,
                     "matrix-core kernel needs bf16, d in {16,32}, window side <= 32 "
-                    "(got dtype=%d d=%d r=%d)", dtype, d, r);
+                    "(got dtype=%d d=%d r=%d flags=%d)", dtype, d, r, flags);
+    if (kernel == HALO_KERNEL_MFMA_STRIP && flags)
+        return fail(HALO_ERR_UNSUPPORTED, "the strip kernel runs the default semantics only (flags=%d)", flags);
 
     hipStream_t s = (hipStream_t)stream;
     const bool use_mfma = kernel == HALO_KERNEL_MFMA || kernel == HALO_KERNEL_MFMA_STRIP ||
@@ -207,6 +216,16 @@ int halo_attn_fwd_lse(const void* q, const void* k, const void* v,
     if (e != hipSuccess)
         return fail(HALO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return HALO_OK;
+}
+
+int halo_attn_fwd_lse(const void* q, const void* k, const void* v,
+                      const void* rel_h, const void* rel_w, void* out, float* lse,
+                      int B, int heads, int H, int W, int d,
+                      int block, int halo, int query_stride,
+                      float scale, int dtype, int kernel, void* stream)
+{
+    return halo_attn_fwd_ex(q, k, v, rel_h, rel_w, out, lse, B, heads, H, W, d, block, halo, query_stride,
+                            scale, dtype, 0, kernel, stream);
 }
 
 int halo_attn_fwd_kernel(const void* q, const void* k, const void* v,

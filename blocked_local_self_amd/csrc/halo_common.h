@@ -24,7 +24,14 @@ struct Geometry {
     int Ho, Wo;        // output spatial size
     int nbh, nbw;      // blocks per column / row (ceil)
     float scale;       // multiplies q.k and q.rel
+    int flags;         // semantic variants (HALO_CENTRED_OFFSET, ...); 0: the pages' reading
 };
+
+// Semantic variants (bit values as in include/halo_attn.h).
+constexpr int kFlagCentredOffset = 1;   // table row of displacement D is D + r - 1
+constexpr int kFlagZeroPad = 2;         // off-image window positions are zero keys and values
+constexpr int kFlagCentredMask = 4;     // only keys within h rows and columns of the query
+constexpr int kFlagHalfSplit = 8;       // height table on channels [0, d/2), width on [d/2, d)
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(__bf16 x) { return static_cast<float>(x); }

@@ -58,6 +58,11 @@ void generic_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
     const int nq = nqy * nqx;
     const int y0 = ybeg - g.halo, x0 = xbeg - g.halo;   // window origin
     const int r = g.r, nkeys = r * r;
+    // variants: centred mask; half-split embedding (height on channels
+    // [0, d/2), width on [d/2, d))
+    const bool cmask = g.flags & kFlagCentredMask;
+    const int hlo = 0, hhi = (g.flags & kFlagHalfSplit) ? d / 2 : d;
+    const int wlo = (g.flags & kFlagHalfSplit) ? d / 2 : 0;
 
     for (int qbase = 0; qbase < nq; qbase += blockDim.x) {
         const int qi = qbase + threadIdx.x;
@@ -85,7 +90,8 @@ void generic_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
                 const int64_t off = ((int64_t)ky * g.W + kx) * d + c;
                 Ks[j][c] = in ? to_f32(ks[off]) : 0.f;
                 Vs[j][c] = in ? to_f32(vs[off]) : 0.f;
-                if (c == 0) valid[j] = in;
+                // zero padding: off-image window positions are zero keys and values
+                if (c == 0) valid[j] = in || (t < nkeys && (g.flags & kFlagZeroPad));
             }
             __syncthreads();
             if (!active) continue;
@@ -96,18 +102,21 @@ void generic_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
                 if (!valid[j]) continue;
                 const int t = kbase + j;
                 const int ky = y0 + t / r, kx = x0 + t % r;
+                if (cmask && (ky < y - g.halo || ky > y + g.halo || kx < x - g.halo || kx > x + g.halo))
+                    continue;         // centred mask: only keys within h rows and columns
                 if (ky != cur_ky) {   // height term changes once per window row
                     cur_ky = ky;
                     const T* rp = rel_h + (int64_t)(ky - y + g.c0) * d;
                     float acc = 0.f;
 #pragma unroll
-                    for (int c = 0; c < DMAX; ++c) if (c < d) acc += qr[c] * to_f32(rp[c]);
+                    for (int c = 0; c < DMAX; ++c) if (c >= hlo && c < hhi) acc += qr[c] * to_f32(rp[c]);
                     rh = acc;
                 }
                 const T* wp = rel_w + (int64_t)(kx - x + g.c0) * d;
                 float s = rh;
 #pragma unroll
-                for (int c = 0; c < DMAX; ++c) if (c < d) s += qr[c] * (Ks[j][c] + to_f32(wp[c]));
+                for (int c = 0; c < DMAX; ++c)
+                    if (c < d) s += qr[c] * (Ks[j][c] + (c >= wlo ? to_f32(wp[c]) : 0.f));
                 s *= g.scale;
                 // online softmax update
                 if (s > m) {

@@ -105,7 +105,9 @@ __device__ inline unsigned k_chunk(int c, int col)
     return (unsigned)((c ^ ((col >> 2) & 3)) * 16);
 }
 
-template <int D, int NCT, int QT, int W>
+// VAR: the semantic variants of g.flags are honoured (a separate
+// instantiation, so the default semantics carry none of their tests).
+template <int D, int NCT, int QT, int W, bool VAR>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2)))
 void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                  const __bf16* __restrict__ v, const __bf16* __restrict__ rel_h,
@@ -156,10 +158,12 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         const int nrel = 2 * R - 1;
         const unsigned short* rhs = reinterpret_cast<const unsigned short*>(rel_h);
         const unsigned short* rws = reinterpret_cast<const unsigned short*>(rel_w);
+        const bool half = VAR && (g.flags & kFlagHalfSplit);   // height on channels < D/2, width on the rest
         for (int e = tid; e < kRelRows * D; e += kRingThreads) {
             const bool in = e < nrel * D;
-            lds_st<unsigned short>(smem, offrh + 2 * e, in ? rhs[e] : (unsigned short)0);
-            lds_st<unsigned short>(smem, offrw + 2 * e, in ? rws[e] : (unsigned short)0);
+            const int c = e % D;
+            lds_st<unsigned short>(smem, offrh + 2 * e, in && (!half || c < D / 2) ? rhs[e] : (unsigned short)0);
+            lds_st<unsigned short>(smem, offrw + 2 * e, in && (!half || c >= D / 2) ? rws[e] : (unsigned short)0);
         }
     }
 
@@ -390,7 +394,12 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     auto do_item = [&](int byy, const Tile& T, const FragT (&qf)[QT], Result& res) {
         const int yb = byy * g.block;
         const int wy0 = yb - g.halo;
-        const int tlo = max(0, -wy0), thi = min(R, g.H - wy0);
+        // variants: zero padding keeps every window position (off-image ones
+        // are zero rows / columns in LDS); the centred offset moves every
+        // table row by -h; the centred mask keeps rows / columns yl..yl+2h
+        const bool zpad = VAR && (g.flags & kFlagZeroPad), cmask = VAR && (g.flags & kFlagCentredMask);
+        const int coff = VAR ? g.c0 - (R - 1 + g.halo) : 0;
+        const int tlo = zpad ? 0 : max(0, -wy0), thi = zpad ? R : min(R, g.H - wy0);
         const int base = yb % ring;                   // ring slot of window row 0
 
         // ---- relative logits: G = table . Q^T on MFMA (both tables), then
@@ -418,7 +427,7 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         };
 #pragma unroll
         for (int u = 0; u < QT; ++u) {
-            const int sw = R - 1 - T.xl[u];
+            const int sw = R - 1 - T.xl[u] + coff;
 #pragma unroll
             for (int rt = 0; rt < kRelTiles; ++rt)
 #pragma unroll
@@ -427,11 +436,11 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                   gw[u][rt][i]);
         }
         // width term of window column c = 16ct + 4g + i (masked: off-image, c >= R)
-        const int clo = g.halo - T.xb, chi = min(R, g.W - T.xb + g.halo);
+        const int clo = zpad ? 0 : g.halo - T.xb, chi = zpad ? R : min(R, g.W - T.xb + g.halo);
         f32x4 cinit[QT][NCT];
 #pragma unroll
         for (int u = 0; u < QT; ++u) {
-            const int r0 = NCT == 1 ? R - 1 - T.xl[u] : 1;    // scratch row of column 0
+            const int r0 = NCT == 1 ? R - 1 - T.xl[u] + coff : 1;    // scratch row of column 0
             const unsigned a = scr0 + u * scr_u + 4u * kScrStride * (r0 + 4 * gq);
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
@@ -439,7 +448,8 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 for (int i = 0; i < 4; ++i) {
                     const int c = 16 * ct + 4 * gq + i;
                     const float val = lds_ld<float>(smem, a + 4u * kScrStride * (16 * ct + i));
-                    cinit[u][ct][i] = (c >= clo && c < chi) ? val : kMaskLogit;
+                    const bool keep = c >= clo && c < chi && (!cmask || (c >= T.xl[u] && c <= T.xl[u] + 2 * g.halo));
+                    cinit[u][ct][i] = keep ? val : kMaskLogit;
                 }
         }
 
@@ -480,13 +490,16 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         unsigned rh0[QT];                             // scratch byte offset of window row 0
 #pragma unroll
         for (int u = 0; u < QT; ++u) {
-            const int sh = R - 1 - T.yl[u];
+            const int sh = R - 1 - T.yl[u] + coff;
 #pragma unroll
             for (int rt = 0; rt < kRelTiles; ++rt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < 4; ++i) {
+                    const int t = rt * 16 + 4 * gq + i - sh;       // window row of this table row
+                    const bool drop = cmask && (t < T.yl[u] || t > T.yl[u] + 2 * g.halo);
                     lds_st<float>(smem, scr0 + u * scr_u + 4u * kScrStride * wrow(rt * 16 + 4 * gq + i, sh),
-                                  fmaf(gh[u][rt][i], alpha, -mb[u]));
+                                  drop ? -INFINITY : fmaf(gh[u][rt][i], alpha, -mb[u]));
+                }
             rh0[u] = scr0 + u * scr_u + 4u * kScrStride * (NCT == 1 ? sh : 1);
         }
         auto rhv = [&](int u, int t) { return lds_ld<float>(smem, rh0[u] + 4u * kScrStride * t); };
@@ -872,8 +885,8 @@ static int ring_qt(const Geometry& g)
     return (HALO_RING_QT > 1 && ring_nct(g) == 1 && tiles % HALO_RING_QT == 0) ? HALO_RING_QT : 1;
 }
 
-template <int D, int NCT, int QT, int W>
-static hipError_t ring_launch_t(const void* q, const void* k, const void* v, const void* rh,
+template <int D, int NCT, int QT, int W, bool VAR>
+static hipError_t ring_launch_v(const void* q, const void* k, const void* v, const void* rh,
                                 const void* rw, void* out, float* lse, const Geometry& g, hipStream_t st)
 {
     RingPlan p = W == 4 ? ring_choose(g, NCT, QT, 4, ring_min_strips4(g)) : ring_choose(g, NCT, QT, 8);
@@ -881,7 +894,7 @@ static hipError_t ring_launch_t(const void* q, const void* k, const void* v, con
     p.nwg = g.BH * p.nstrips;
     p.remap_xcd = (p.nwg % 8 == 0) ? 1 : 0;
     p.alpha = (float)((double)g.scale * 1.4426950408889634);
-    auto kern = ring_kernel<D, NCT, QT, W>;
+    auto kern = ring_kernel<D, NCT, QT, W, VAR>;
     if (p.lds_bytes > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
@@ -891,6 +904,14 @@ static hipError_t ring_launch_t(const void* q, const void* k, const void* v, con
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
                        (const __bf16*)rh, (const __bf16*)rw, (__bf16*)out, lse, g, p);
     return hipGetLastError();
+}
+
+template <int D, int NCT, int QT, int W>
+static hipError_t ring_launch_t(const void* q, const void* k, const void* v, const void* rh,
+                                const void* rw, void* out, float* lse, const Geometry& g, hipStream_t st)
+{
+    return g.flags ? ring_launch_v<D, NCT, QT, W, true>(q, k, v, rh, rw, out, lse, g, st)
+                   : ring_launch_v<D, NCT, QT, W, false>(q, k, v, rh, rw, out, lse, g, st);
 }
 
 template <int D, int NCT, int QT>

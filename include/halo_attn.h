@@ -72,6 +72,28 @@ typedef enum halo_kernel {
     HALO_KERNEL_MFMA_STRIP = 3
 } halo_kernel;
 
+/* Semantic variants (OR-ed into `flags` of halo_attn_fwd_ex), for matching
+ * other readings of the pages.  0 selects the reading documented above.
+ *  HALO_CENTRED_OFFSET: table row of displacement D is D + r - 1 (the
+ *    table's centre row) instead of D + r - 1 + halo.
+ *  HALO_ZERO_PAD: window positions outside the image take part in the
+ *    softmax as zero keys and values (section 2.2's "padding at image
+ *    borders" read literally) instead of being left out.
+ *  HALO_CENTRED_MASK: a query attends only to the keys of its window within
+ *    `halo` rows and columns of it: the (2*halo+1)^2 neighbourhood centred
+ *    on the query, clipped to the image (SASA; section 2.2 says the blocked
+ *    form drops this mask).
+ *  HALO_HALF_SPLIT: the height table is applied to channels [0, d/2) of q
+ *    and the width table to channels [d/2, d) (appendix A's factorised
+ *    embedding, half the channels per axis); the other channels of the
+ *    tables are ignored. */
+typedef enum halo_flags {
+    HALO_CENTRED_OFFSET = 1,
+    HALO_ZERO_PAD = 2,
+    HALO_CENTRED_MASK = 4,
+    HALO_HALF_SPLIT = 8
+} halo_flags;
+
 typedef enum halo_status {
     HALO_OK = 0,
     HALO_ERR_NULL = -1,         /* a required pointer is NULL */
@@ -113,6 +135,19 @@ int halo_attn_fwd_lse(const void* q, const void* k, const void* v,
                       int B, int heads, int H, int W, int d,
                       int block, int halo, int query_stride,
                       float scale, int dtype, int kernel, void* stream);
+
+/*
+ * halo_attn_fwd_lse with semantic variants: flags is an OR of halo_flags
+ * values (other bits: HALO_ERR_SHAPE).  Variants run on the generic kernel
+ * and on the persistent matrix-core kernel; HALO_KERNEL_MFMA_STRIP with
+ * flags != 0 returns HALO_ERR_UNSUPPORTED.  The backward computes the
+ * default semantics only.
+ */
+int halo_attn_fwd_ex(const void* q, const void* k, const void* v,
+                     const void* rel_h, const void* rel_w, void* out, float* lse,
+                     int B, int heads, int H, int W, int d,
+                     int block, int halo, int query_stride,
+                     float scale, int dtype, int flags, int kernel, void* stream);
 
 /* halo_attn_fwd_kernel with kernel = HALO_KERNEL_AUTO. */
 int halo_attn_fwd(const void* q, const void* k, const void* v,
