@@ -97,6 +97,8 @@ def parse():
     ap.add_argument("--kernel", default="auto", choices=["auto", "generic", "mfma"])
     ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
                     help="forward (the headline) or backward pass")
+    ap.add_argument("--variants", default="", help="comma-separated semantic variants of the forward "
+                    "(centred_offset, zero_pad, centred_mask, half_split); default: none")
     ap.add_argument("--sets", type=int, default=0, help="rotated input sets (0: enough to exceed the MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU-oracle sample time")
@@ -190,6 +192,10 @@ def main():
     in_bytes = 3 * wl.elem_bytes * wl.B * wl.heads * wl.H * wl.W * wl.d
     out_bytes = wl.elem_bytes * wl.B * wl.heads * wl.Ho * wl.Wo * wl.d
     bwd = args.which == "bwd"
+    variants = tuple(v for v in args.variants.split(",") if v)
+    if variants and bwd:
+        print("--variants applies to the forward pass only", file=sys.stderr)
+        sys.exit(2)
     per_set = in_bytes + out_bytes if not bwd else 2 * in_bytes + 2 * out_bytes
     nsets = args.sets or max(2, -(-2 * MALL_BYTES // per_set))
     sets = []
@@ -225,7 +231,7 @@ def main():
                           kernel=args.kernel, workspace=ws, grads=grads, stream=stream)
         else:
             halo_attn_fwd(q, k, v, rh, rw, wl.block, wl.halo, wl.stride, out=x, kernel=args.kernel,
-                          stream=stream)
+                          stream=stream, variants=variants)
 
     for i in range(args.warmup):
         step(i)
@@ -247,7 +253,7 @@ def main():
     achieved_gbs = alg_bytes / (ms * 1e-3) / 1e9
 
     src_hash = kernel_source_hash(args.which)
-    rec = MEASURED_TRAFFIC[args.which].get(wl.name)
+    rec = None if variants else MEASURED_TRAFFIC[args.which].get(wl.name)
     traffic = rec["bytes_per_launch"] if rec and rec["sources"] == src_hash else None
 
     line = {
@@ -263,7 +269,8 @@ def main():
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic",
-        "config": {**wl.describe(), "pass": args.which, "kernel": args.kernel, "rotated_input_sets": nsets},
+        "config": {**wl.describe(), "pass": args.which, "kernel": args.kernel, "rotated_input_sets": nsets,
+                   **({"variants": list(variants)} if variants else {})},
         "tokens_per_s": round(wl.tokens / (ms * 1e-3), 1),
         "wall_s_timed_region": round(wall, 4),
         "roofline": {
