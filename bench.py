@@ -9,9 +9,11 @@ rotated so the working set exceeds the 256 MB Infinity Cache and every step
 reads HBM.  Prints ONE JSON line (rank 0):
 
   value      TFLOP/s, F = 4*d*r^2 per (query, head) over the full window
-  roofline   dominant kernel vs HBM bandwidth: algorithmic bytes per launch
-             (k and v once, q at query pixels, out once) / mean launch time
-             measured with HIP events on the launch stream
+  roofline   dominant kernel vs its binding roof: HBM bandwidth (algorithmic
+             bytes per launch: k and v once, q at query pixels, out once) or,
+             when the flops take longer at the published peaks, the dense
+             matrix peak of the dtype; mean launch time measured with HIP
+             events on the launch stream
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
              workload on this host (reported, not a target)
 
@@ -38,6 +40,7 @@ sys.path.insert(0, HERE)
 METRIC = "halo-attn fwd TFLOP/s + tokens/s per MI355X; % of MFMA/HBM roofline"
 METRIC_BWD = "halo-attn bwd TFLOP/s + tokens/s per MI355X; % of MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}   # MI355X dense matrix peaks, published
 MALL_BYTES = 256 * 2 ** 20     # Infinity Cache
 
 # HBM bytes per launch of the dominant kernel, per workload: rocprofv3 --pmc
@@ -251,6 +254,10 @@ def main():
     alg_bytes = bwd_alg_bytes(wl) if bwd else wl.alg_bytes
     tflops = flops / (ms * 1e-3) / 1e12
     achieved_gbs = alg_bytes / (ms * 1e-3) / 1e9
+    # the binding roof: whichever of HBM bytes and matrix flops takes longer
+    # at the published peaks
+    mfma_peak = MFMA_PEAK_TFLOPS[wl.dtype]
+    mfma_bound = flops / (mfma_peak * 1e12) > alg_bytes / (HBM_PEAK_GBS * 1e9)
 
     src_hash = kernel_source_hash(args.which)
     rec = None if variants else MEASURED_TRAFFIC[args.which].get(wl.name)
@@ -274,11 +281,11 @@ def main():
         "tokens_per_s": round(wl.tokens / (ms * 1e-3), 1),
         "wall_s_timed_region": round(wall, 4),
         "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved_gbs, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+            "bound": "mfma" if mfma_bound else "hbm",
+            "achieved": round(tflops, 2) if mfma_bound else round(achieved_gbs, 1),
+            "peak": mfma_peak if mfma_bound else HBM_PEAK_GBS,
+            "unit": "TFLOP/s" if mfma_bound else "GB/s",
+            "frac": round(tflops / mfma_peak if mfma_bound else achieved_gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "alg_bytes_per_launch": alg_bytes,
             "mean_launch_us": round(ms * 1e3, 3),

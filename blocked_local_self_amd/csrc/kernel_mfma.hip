@@ -318,8 +318,16 @@ void mfma_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 int t = tlo;
                 for (; t + 1 < thi; t += 2) step(std::true_type{}, t, 0, t + 1, 0);
                 if (t < thi) step(std::false_type{}, t, 0, t, 0);
-            } else {
+            } else if (NCH == 2) {
                 for (int t = tlo; t < thi; ++t) step(std::true_type{}, t, 0, t, NCH - 1);
+            } else {
+                // consecutive score tiles of the row-major (row, column chunk)
+                // sequence, two per step; a pair may span two rows
+                const int ntiles = (thi - tlo) * NCH;
+                int tau = 0;
+                for (; tau + 1 < ntiles; tau += 2)
+                    step(std::true_type{}, tlo + tau / NCH, tau % NCH, tlo + (tau + 1) / NCH, (tau + 1) % NCH);
+                if (tau < ntiles) step(std::false_type{}, tlo + tau / NCH, tau % NCH, tlo + tau / NCH, tau % NCH);
             }
 
             // ---- normalise and store: lane (n, g) holds channels 16*mt + 4g + i of query n
@@ -368,10 +376,13 @@ static MfmaPlan make_plan(const Geometry& g, int nch, int qt, int nbx, int waves
     return p;
 }
 
+// Windows up to 32 columns for d in {16, 32}; up to 40 (three column
+// chunks, the strip kernel only) for d = 16: a one-block strip's K and V^T
+// (r x 48 columns) plus one query tile of scratch per wave stay within LDS.
 bool mfma_supported(int d, int r, int block, int stride, bool bf16)
 {
     (void)stride;
-    return bf16 && (d == 16 || d == 32) && r <= 32 && block % 4 == 0;
+    return bf16 && block % 4 == 0 && (((d == 16 || d == 32) && r <= 32) || (d == 16 && r <= 40));
 }
 
 // Largest dynamic LDS one workgroup may use on the current device.
@@ -436,12 +447,16 @@ template <int D, int NCH>
 static hipError_t launch_dn(const void* q, const void* k, const void* v, const void* rh,
                             const void* rw, void* out, float* lse, const Geometry& g, hipStream_t st)
 {
+    hipError_t e;
     switch (choose_qt(g)) {
     case 1: return launch_t<D, NCH, 1>(q, k, v, rh, rw, out, lse, g, st);
-    case 3: return launch_t<D, NCH, 3>(q, k, v, rh, rw, out, lse, g, st);
-    case 4: return launch_t<D, NCH, 4>(q, k, v, rh, rw, out, lse, g, st);
-    default: return launch_t<D, NCH, 2>(q, k, v, rh, rw, out, lse, g, st);
+    case 3: e = launch_t<D, NCH, 3>(q, k, v, rh, rw, out, lse, g, st); break;
+    case 4: e = launch_t<D, NCH, 4>(q, k, v, rh, rw, out, lse, g, st); break;
+    default: e = launch_t<D, NCH, 2>(q, k, v, rh, rw, out, lse, g, st); break;
     }
+    // a window too large for several query tiles' scratch: one tile per wave
+    if (e == hipErrorInvalidConfiguration) e = launch_t<D, NCH, 1>(q, k, v, rh, rw, out, lse, g, st);
+    return e;
 }
 
 bool ring_supported(const Geometry& g);
@@ -456,6 +471,7 @@ hipError_t launch_mfma(const void* q, const void* k, const void* v, const void* 
 {
     if (!force_strip && ring_supported(g)) return launch_ring(q, k, v, rh, rw, out, lse, g, st);
     const bool wide = g.r > 16;
+    if (g.d == 16 && g.r > 32) return launch_dn<16, 3>(q, k, v, rh, rw, out, lse, g, st);
     if (g.d == 16) return wide ? launch_dn<16, 2>(q, k, v, rh, rw, out, lse, g, st)
                                : launch_dn<16, 1>(q, k, v, rh, rw, out, lse, g, st);
     return wide ? launch_dn<32, 2>(q, k, v, rh, rw, out, lse, g, st)

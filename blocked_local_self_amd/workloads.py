@@ -5,7 +5,9 @@ for Parameter Efficient Visual Backbones": 16 channels per head and 8 heads in
 the later stages (section 2.3, appendix C.1), b=8/h=3 giving 14x14 windows
 (sections 2.3 and 4.6), windows up to 18x18 (section 2.3; b=12 as in the
 384-pixel transfer setting of appendix E), 64x64 and 32x32 maps from 256-pixel
-inputs, and stride-2 attention downsampling (section 2.2, Figure 2).
+inputs, and stride-2 attention downsampling (section 2.2, Figure 2); plus the
+larger-window settings: b=32/h=3 from the detection study (section 4.6) and
+global attention over a 16x16 map (section 2.2).
 
 Accounting conventions (per launch):
   flops     = 4 * d * r^2 per (query, head): q.k and p.v over the full
@@ -86,6 +88,11 @@ WORKLOADS = {
         Workload("mid_stage_bf16_32x32_d32_b8h3", "bf16", 64, 8, 32, 32, 32, 8, 3, 1),
         Workload("strided_bf16_64x64_d16_b8h3_s2", "bf16", 32, 8, 64, 64, 16, 8, 3, 2),
         Workload("large_bf16_128x128_d32_b12h3", "bf16", 8, 8, 128, 128, 32, 12, 3, 1),
+        # larger windows: the detection setting with b=32, h=3 (section 4.6;
+        # 38x38 windows, 1444 keys), and whole-map attention at the smallest
+        # resolution (section 2.2, last paragraph: one block covers the map)
+        Workload("detection_bf16_64x64_d16_b32h3", "bf16", 8, 8, 64, 64, 16, 32, 3, 1),
+        Workload("global_bf16_16x16_d16_b16h0", "bf16", 64, 8, 16, 16, 16, 16, 0, 1),
     )
 }
 

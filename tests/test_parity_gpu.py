@@ -74,6 +74,9 @@ SMALL = [
     (1, 2, 12, 12, 16, 16, 1, 1),   # block larger than the image
     (1, 1, 40, 40, 16, 20, 6, 1),   # largest matrix-core window side, r = 32
     (1, 1, 40, 40, 16, 4, 14, 4),   # r = 32 with tiny blocks, stride = block
+    (1, 2, 64, 64, 16, 32, 3, 1),   # r = 38: three column chunks (strip kernel, d = 16)
+    (1, 1, 40, 44, 16, 8, 13, 1),   # r = 34, ragged
+    (1, 1, 24, 40, 16, 12, 14, 2),  # r = 40, the largest three-chunk window, strided
 ]
 
 
