@@ -51,23 +51,27 @@ MALL_BYTES = 256 * 2 ** 20     # Infinity Cache
 # bench reports traffic as null.
 MEASURED_TRAFFIC = {
     "fwd": {
-        "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 134587580, "read": 101033148, "write": 33554432,
-                                            "sources": "5f85d071db4a6551"},
-        "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 146211362, "read": 104268322, "write": 41943040,
-                                          "sources": "5f85d071db4a6551"},
-        "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 92532794, "read": 84144186, "write": 8388608,
-                                           "sources": "5f85d071db4a6551"},
-        "large_bf16_128x128_d32_b12h3": {"bytes_per_launch": 281011610, "read": 213902746, "write": 67108864,
-                                         "sources": "5f85d071db4a6551"},
+        "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 134575124, "read": 101020692, "write": 33554432,
+            "sources": "fef9af93e1c3c5e3"},
+        "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 146210145, "read": 104267105, "write": 41943040,
+            "sources": "fef9af93e1c3c5e3"},
+        "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 92519052, "read": 84130444, "write": 8388608,
+            "sources": "fef9af93e1c3c5e3"},
+        "large_bf16_128x128_d32_b12h3": {"bytes_per_launch": 281791968, "read": 214683104, "write": 67108864,
+            "sources": "fef9af93e1c3c5e3"},
+        "detection_bf16_64x64_d16_b32h3": {"bytes_per_launch": 33755071, "read": 25366463, "write": 8388608,
+            "sources": "fef9af93e1c3c5e3"},
+        "global_bf16_16x16_d16_b16h0": {"bytes_per_launch": 17137550, "read": 12943246, "write": 4194304,
+            "sources": "fef9af93e1c3c5e3"},
     },
     # backward: summed over the call's kernels (block kernel, dk/dv gather, table reduction)
     "bwd": {
-        "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 1147056143, "read": 598919823, "write": 548136320,
-                                            "sources": "20cd801b38251cab"},
-        "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 1082461131, "read": 556341451, "write": 526119680,
-                                          "sources": "20cd801b38251cab"},
-        "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 1085189290, "read": 528664362, "write": 556524928,
-                                           "sources": "20cd801b38251cab"},
+        "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 1147083147, "read": 598946827, "write": 548136320,
+            "sources": "c921ba62421b8c2a"},
+        "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 1082528532, "read": 556408852, "write": 526119680,
+            "sources": "c921ba62421b8c2a"},
+        "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 1085221069, "read": 528696141, "write": 556524928,
+            "sources": "c921ba62421b8c2a"},
     },
 }
 
@@ -75,7 +79,7 @@ MEASURED_TRAFFIC = {
 # Sources the timed kernels are built from, per pass (the traffic record of
 # a pass holds while these files are unchanged).
 KERNEL_SOURCES = {
-    "fwd": ["halo_common.h", "mfma_util.h", "kernel_ring.hip"],
+    "fwd": ["halo_common.h", "mfma_util.h", "kernel_ring.hip", "kernel_mfma.hip"],
     "bwd": ["halo_common.h", "mfma_util.h", "kernel_bwd_mfma.hip", "kernel_bwd_generic.hip"],
 }
 
@@ -226,15 +230,39 @@ def main():
         grads = tuple(torch.empty(wl.shape(), dtype=sets[0][0][0].dtype, device=dev) for _ in range(3)) + \
             tuple(torch.empty((2 * wl.r - 1, wl.d), dtype=torch.float32, device=dev) for _ in range(2))
 
-    def step(i):
-        (q, k, v, rh, rw), x = sets[i % nsets]
+    # Every input set goes once through the checked torch-level wrapper; the
+    # timed steps then call the same C entry point with the argument tuples
+    # prepared here, so host-side argument checking does not pace the GPU
+    # (it would for the smallest workloads).
+    from blocked_local_self_amd import _native, KERNELS, VARIANTS
+    lib = _native.load()
+    dcode = _native.HALO_BF16 if wl.dtype == "bf16" else _native.HALO_F32
+    flags = sum(VARIANTS[v] for v in variants)
+    scale = float(wl.d) ** -0.5
+    calls = []
+    for (q, k, v, rh, rw), x in sets:
         if bwd:
             g, out, lse = x
             halo_attn_bwd(q, k, v, rh, rw, g, wl.block, wl.halo, wl.stride, out=out, lse=lse,
                           kernel=args.kernel, workspace=ws, grads=grads, stream=stream)
+            calls.append((lib.halo_attn_bwd_kernel,
+                          (q.data_ptr(), k.data_ptr(), v.data_ptr(), rh.data_ptr(), rw.data_ptr(), out.data_ptr(),
+                           g.data_ptr(), lse.data_ptr(), *[t.data_ptr() for t in grads], ws.data_ptr(),
+                           ws.numel(), wl.B, wl.heads, wl.H, wl.W, wl.d, wl.block, wl.halo, wl.stride, scale,
+                           dcode, KERNELS[args.kernel], stream.cuda_stream)))
         else:
             halo_attn_fwd(q, k, v, rh, rw, wl.block, wl.halo, wl.stride, out=x, kernel=args.kernel,
                           stream=stream, variants=variants)
+            calls.append((lib.halo_attn_fwd_ex,
+                          (q.data_ptr(), k.data_ptr(), v.data_ptr(), rh.data_ptr(), rw.data_ptr(), x.data_ptr(),
+                           None, wl.B, wl.heads, wl.H, wl.W, wl.d, wl.block, wl.halo, wl.stride, scale, dcode,
+                           flags, KERNELS[args.kernel], stream.cuda_stream)))
+
+    def step(i):
+        fn, a = calls[i % nsets]
+        st = fn(*a)
+        if st:
+            _native.check(st)
 
     for i in range(args.warmup):
         step(i)

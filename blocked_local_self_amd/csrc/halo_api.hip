@@ -1,7 +1,11 @@
 // C ABI of the halo-attention library: argument checks, kernel choice, launch.
 // The operation and every convention are documented in include/halo_attn.h.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
+#include <mutex>
+#include <utility>
+#include <vector>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -11,6 +15,46 @@
 #include "halo_common.h"
 
 namespace halo {
+
+DeviceInfo device_info()
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static std::atomic<int> ready[kMaxDevices];
+    static DeviceInfo info[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DeviceInfo{64 * 1024, 256};
+    if (!ready[dev].load(std::memory_order_acquire)) {
+        std::lock_guard<std::mutex> lock(mu);
+        if (!ready[dev].load(std::memory_order_relaxed)) {
+            int lds = 0, cus = 0;
+            if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || lds <= 0)
+                lds = 64 * 1024;
+            if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+                cus = 256;
+            info[dev] = DeviceInfo{lds, cus};
+            ready[dev].store(1, std::memory_order_release);
+        }
+    }
+    return info[dev];
+}
+
+hipError_t ensure_lds_limit(const void* kernel, int bytes)
+{
+    if (bytes <= 64 * 1024) return hipSuccess;
+    // (kernel, device) pairs already raised; the attribute is per device
+    static std::mutex mu;
+    static std::vector<std::pair<const void*, int>> done;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    std::lock_guard<std::mutex> lock(mu);
+    for (const auto& d : done)
+        if (d.first == kernel && d.second == dev) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess) done.emplace_back(kernel, dev);
+    return e;
+}
+
 hipError_t launch_generic(const void* q, const void* k, const void* v, const void* rh,
                           const void* rw, void* out, float* lse, const Geometry& g, bool bf16, hipStream_t st);
 bool mfma_supported(int d, int r, int block, int stride, bool bf16);

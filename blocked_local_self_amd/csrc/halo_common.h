@@ -33,6 +33,18 @@ constexpr int kFlagZeroPad = 2;         // off-image window positions are zero k
 constexpr int kFlagCentredMask = 4;     // only keys within h rows and columns of the query
 constexpr int kFlagHalfSplit = 8;       // height table on channels [0, d/2), width on [d/2, d)
 
+// Attributes of the current device, queried through HIP once per device and
+// cached (kernel planning runs on every call and must not pay for API calls).
+struct DeviceInfo {
+    int lds_per_block;   // bytes of dynamic LDS one workgroup may use
+    int cus;             // compute units
+};
+DeviceInfo device_info();
+
+// Raise a kernel's dynamic-LDS limit to `bytes` once per device (a no-op at
+// or below the 64 KiB default).
+hipError_t ensure_lds_limit(const void* kernel, int bytes);
+
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(__bf16 x) { return static_cast<float>(x); }
 

@@ -149,6 +149,7 @@ void bwd_block_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
     const int uown = NT == 4 ? wave : 0;
     const FragT qown = *reinterpret_cast<const FragT*>(q + bh * plane + qpix(16 * uown + n) * D + gq * KPL);
     const FragT gown = *reinterpret_cast<const FragT*>(dout + (bh * oplane + opix(16 * uown + n)) * D + gq * KPL);
+    const float lse2own = lse[bh * oplane + opix(16 * uown + n)] * 1.4426950408889634f;   // base-2
 
     // ---------------------------------------------------------------- staging
     {
@@ -200,21 +201,46 @@ void bwd_block_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
             bst<unsigned short>(smem, p.off_tabt + 2u * (c * kTabRows + row), hv);
             bst<unsigned short>(smem, p.off_tabt + 2u * (D * kTabRows + c * kTabRows + row), wv);
         }
-        // Q^T and dout^T of the block's queries; D = dout . out per query
-        const unsigned short* qs = reinterpret_cast<const unsigned short*>(q + bh * plane);
-        const unsigned short* gs = reinterpret_cast<const unsigned short*>(dout + bh * oplane * D);
-        for (int e = tid; e < NQ * D; e += 256) {
-            const int qi = e / D, c = e - qi * D;
-            bst<unsigned short>(smem, p.off_qt + 2u * (c * p.qpitch + qi), qs[qpix(qi) * D + c]);
-            bst<unsigned short>(smem, p.off_dot + 2u * (c * p.qpitch + qi), gs[opix(qi) * D + c]);
-        }
-        if (tid < NQ) {
-            const __bf16* op = out + (bh * oplane + opix(tid)) * D;
-            const __bf16* gp = dout + (bh * oplane + opix(tid)) * D;
-            float acc = 0.f;
+        // Q^T and dout^T of the block's queries, and D = dout . out per
+        // query.  Item: 4 consecutive queries (one block-row of queries holds
+        // 4 or 8 of them) x all channels, loaded 16 bytes at a time and
+        // transposed in registers into 8-byte rows (4 queries of a channel).
+        if (tid < NQ / 4) {
+            const int qi0 = 4 * tid;
+            const __bf16* qp = q + bh * plane + qpix(qi0) * D;
+            const int64_t o0 = (bh * oplane + opix(qi0)) * D;
+            float dacc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int c = 0; c < D; ++c) acc += (float)op[c] * (float)gp[c];
-            bst<float>(smem, p.off_d + 4u * tid, acc);
+            for (int ch = 0; ch < CPP; ++ch) {
+                u32x4 qq[4], gg[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    qq[j] = *reinterpret_cast<const u32x4*>(qp + (int64_t)j * g.stride * D + ch * 8);
+                    gg[j] = *reinterpret_cast<const u32x4*>(dout + o0 + j * D + ch * 8);
+                    const u32x4 oo = *reinterpret_cast<const u32x4*>(out + o0 + j * D + ch * 8);
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        dacc[j] = fmaf(__builtin_bit_cast(float, oo[w] << 16), __builtin_bit_cast(float, gg[j][w] << 16), dacc[j]);
+                        dacc[j] = fmaf(__builtin_bit_cast(float, oo[w] & 0xffff0000u),
+                                       __builtin_bit_cast(float, gg[j][w] & 0xffff0000u), dacc[j]);
+                    }
+                }
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {          // channels ch*8 + 2w (low halves), + 2w + 1 (high)
+                    const unsigned c = ch * 8 + 2 * w;
+                    const unsigned bq = p.off_qt + 2u * (c * p.qpitch + qi0);
+                    const unsigned bg = p.off_dot + 2u * (c * p.qpitch + qi0);
+                    bst<u32x2>(smem, bq, u32x2{__builtin_amdgcn_perm(qq[1][w], qq[0][w], 0x05040100u),
+                                               __builtin_amdgcn_perm(qq[3][w], qq[2][w], 0x05040100u)});
+                    bst<u32x2>(smem, bq + 2u * p.qpitch, u32x2{__builtin_amdgcn_perm(qq[1][w], qq[0][w], 0x07060302u),
+                                                               __builtin_amdgcn_perm(qq[3][w], qq[2][w], 0x07060302u)});
+                    bst<u32x2>(smem, bg, u32x2{__builtin_amdgcn_perm(gg[1][w], gg[0][w], 0x05040100u),
+                                               __builtin_amdgcn_perm(gg[3][w], gg[2][w], 0x05040100u)});
+                    bst<u32x2>(smem, bg + 2u * p.qpitch, u32x2{__builtin_amdgcn_perm(gg[1][w], gg[0][w], 0x07060302u),
+                                                               __builtin_amdgcn_perm(gg[3][w], gg[2][w], 0x07060302u)});
+                }
+            }
+            bst<f32x4>(smem, p.off_d + 16u * tid, f32x4{dacc[0], dacc[1], dacc[2], dacc[3]});
         }
     }
     __syncthreads();
@@ -232,7 +258,7 @@ void bwd_block_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
         const FragT qf = qown;
         int yl, xl;
         qpos(16 * u + n, yl, xl);
-        const float lse2 = lse[bh * oplane + opix(16 * u + n)] * 1.4426950408889634f;
+        const float lse2 = lse2own;
         for (int tab = 0; tab < 2; ++tab) {          // 0: rel_w -> width table, 1: rel_h -> height
             f32x4 gv[2];
 #pragma unroll
@@ -593,9 +619,8 @@ static hipError_t bwd_mfma_t(const void* q, const void* k, const void* v, const 
     p.remap_xcd = (p.nwg % 8 == 0) ? 1 : 0;
     p.alpha = (float)((double)g.scale * 1.4426950408889634);
     auto kern = bwd_block_kernel<D, NT>;
-    if (p.lds_bytes > 64 * 1024) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
+    {
+        const hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), p.lds_bytes);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)p.nwg), dim3(256), p.lds_bytes, st,

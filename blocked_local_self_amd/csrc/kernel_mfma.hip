@@ -386,14 +386,7 @@ bool mfma_supported(int d, int r, int block, int stride, bool bf16)
 }
 
 // Largest dynamic LDS one workgroup may use on the current device.
-static int device_lds_limit()
-{
-    int dev = 0, bytes = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 64 * 1024;
-    if (hipDeviceGetAttribute(&bytes, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-        return 64 * 1024;
-    return bytes;
-}
+static int device_lds_limit() { return device_info().lds_per_block; }
 
 // 16-query tiles per block, and how many of them a wave carries at once.
 static int tiles_per_block(const Geometry& g)
@@ -432,9 +425,8 @@ static hipError_t launch_t(const void* q, const void* k, const void* v, const vo
     p.remap_xcd = (p.nwg % 8 == 0) ? 1 : 0;
     p.alpha = (float)((double)g.scale * 1.4426950408889634);
     auto kern = mfma_kernel<D, NCH, QT>;
-    if (p.lds_bytes > 64 * 1024) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
+    {
+        const hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), p.lds_bytes);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)p.nwg), dim3(64 * p.waves), p.lds_bytes, st,

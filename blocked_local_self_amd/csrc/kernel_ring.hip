@@ -797,21 +797,10 @@ static RingPlan ring_plan(const Geometry& g, int nct, int qt, int waves, int nbx
 // a CU (the device limit per workgroup caps it too).
 static int ring_lds_limit(int waves)
 {
-    int dev = 0, bytes = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 64 * 1024;
-    if (hipDeviceGetAttribute(&bytes, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-        return 64 * 1024;
-    return std::min(bytes, kLdsPerCU * waves / 8);
+    return std::min(device_info().lds_per_block, kLdsPerCU * waves / 8);
 }
 
-static int device_cus()
-{
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        return 256;
-    return cus;
-}
+static int device_cus() { return device_info().cus; }
 
 // Widest plan that fits in LDS with at least `min_strips` strips per image
 // and at most ring_maxi groups per wave per block row, for one ring size, or
@@ -895,9 +884,8 @@ static hipError_t ring_launch_v(const void* q, const void* k, const void* v, con
     p.remap_xcd = (p.nwg % 8 == 0) ? 1 : 0;
     p.alpha = (float)((double)g.scale * 1.4426950408889634);
     auto kern = ring_kernel<D, NCT, QT, W, VAR>;
-    if (p.lds_bytes > 64 * 1024) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
+    {
+        const hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), p.lds_bytes);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)p.nwg), dim3(64 * W), p.lds_bytes, st,
