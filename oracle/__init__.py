@@ -48,6 +48,8 @@ def _load():
     lib.halo_ref_set_attention.restype = ctypes.c_double
     lib.halo_ref_bwd.argtypes = [dp] * 11 + [ctypes.c_int] * 8 + [ctypes.c_double, ctypes.c_int]
     lib.halo_ref_bwd.restype = ctypes.c_int
+    lib.halo_ref_bwd_ex.argtypes = [dp] * 11 + [ctypes.c_int] * 8 + [ctypes.c_double, ctypes.c_int, ctypes.c_int]
+    lib.halo_ref_bwd_ex.restype = ctypes.c_int
     lib.halo_ref_set_attention_bwd.argtypes = [
         ctypes.c_int, ctypes.c_int, dp, ctypes.POINTER(dp), dp, ctypes.POINTER(dp),
         ctypes.c_double, dp, dp, ctypes.POINTER(dp), ctypes.POINTER(dp), dp, dp]
@@ -119,14 +121,15 @@ def _check(q, k, v, rel_h, rel_w, block, halo, query_stride):
 
 def halo_attn_bwd_ref(q, k, v, rel_h, rel_w, dout, block: int, halo: int,
                       query_stride: int = 1, scale: float | None = None,
-                      threads: int = 0):
+                      threads: int = 0, flags: int = 0):
     """Backward pass, fp64: gradients of a scalar loss given d loss / d out.
 
     Same arguments as ``halo_attn_ref`` plus ``dout`` [B, heads, H/s, W/s, d].
     Returns (dq, dk, dv, drel_h, drel_w) as float64 arrays shaped like
     (q, k, v, rel_h, rel_w).  Pixels that are not queries (stride > 1) get a
     zero dq.  The exact derivative of the forward definition (chain rule
-    through each query's softmax); see halo_ref.c.
+    through each query's softmax); see halo_ref.c.  ``flags``: the variants
+    of ``halo_attn_ref`` (CENTRED_OFFSET, ZERO_PAD, CENTRED_MASK, HALF_SPLIT).
     """
     q, k, v, rel_h, rel_w, dout = (_f64(t) for t in (q, k, v, rel_h, rel_w, dout))
     _check(q, k, v, rel_h, rel_w, block, halo, query_stride)
@@ -138,9 +141,9 @@ def halo_attn_bwd_ref(q, k, v, rel_h, rel_w, dout, block: int, halo: int,
         scale = float(d) ** -0.5
     dq, dk, dv = (np.zeros(q.shape) for _ in range(3))
     drh, drw = np.zeros(rel_h.shape), np.zeros(rel_w.shape)
-    rc = _load().halo_ref_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(rel_h), _ptr(rel_w), _ptr(dout),
-                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(drh), _ptr(drw),
-                              B, heads, H, W, d, block, halo, s, float(scale), int(threads))
+    rc = _load().halo_ref_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(rel_h), _ptr(rel_w), _ptr(dout),
+                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(drh), _ptr(drw),
+                                 B, heads, H, W, d, block, halo, s, float(scale), int(flags), int(threads))
     if rc != 0:
         raise ValueError(f"halo_ref_bwd failed with status {rc}")
     return dq, dk, dv, drh, drw

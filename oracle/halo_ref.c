@@ -296,15 +296,20 @@ void halo_ref_set_attention_bwd(int d, int nkeys, const double* q,
  * in slice order (results do not depend on the thread count).
  * Returns 0, -1 (null pointer), -2 (bad shape) or -3 (no memory).
  */
-int halo_ref_bwd(const double* q, const double* k, const double* v,
-                 const double* rel_h, const double* rel_w, const double* dout,
-                 double* dq, double* dk, double* dv, double* drel_h, double* drel_w,
-                 int B, int heads, int H, int W, int d,
-                 int block, int halo, int stride, double scale, int nthreads)
+int halo_ref_bwd_ex(const double* q, const double* k, const double* v,
+                    const double* rel_h, const double* rel_w, const double* dout,
+                    double* dq, double* dk, double* dv, double* drel_h, double* drel_w,
+                    int B, int heads, int H, int W, int d,
+                    int block, int halo, int stride, double scale, int flags, int nthreads)
 {
     if (check_shape(B, heads, H, W, d, block, halo, stride)) return -2;
+    if (flags & ~15) return -2;
     const int r = block + 2 * halo;
-    const int c0 = r - 1 + halo;
+    /* the variants of halo_ref_fwd_ex: same key sets and biases */
+    const int c0 = (flags & 1) ? r - 1 : r - 1 + halo;
+    const int zero_pad = (flags & 2) != 0, centred = (flags & 4) != 0;
+    const int hlo = 0, hhi = (flags & 8) ? d / 2 : d;
+    const int wlo = (flags & 8) ? d / 2 : 0, whi = d;
     const long nrel = (long)(2 * r - 1) * d;
     if (!drel_h || !drel_w) return -1;
     for (long e = 0; e < nrel; ++e) drel_h[e] = drel_w[e] = 0.0;
@@ -332,9 +337,12 @@ int halo_ref_bwd(const double* q, const double* k, const double* v,
     double* scratch = malloc(sizeof(double) * 2 * nk * nt);
     double* qgrad = malloc(sizeof(double) * (size_t)d * nt);
     double* part = calloc((size_t)slices * 2 * nrel, sizeof(double));   /* per-slice table grads */
-    if (!keys || !vals || !dkeys || !dvals || !rows || !bias || !dbias || !scratch || !qgrad || !part) {
+    double* zero = calloc((size_t)d, sizeof(double));             /* key / value of a padded position */
+    double* sink = calloc((size_t)2 * d * nt, sizeof(double));    /* their (discarded) gradients */
+    if (!keys || !vals || !dkeys || !dvals || !rows || !bias || !dbias || !scratch || !qgrad || !part ||
+        !zero || !sink) {
         free(keys); free(vals); free(dkeys); free(dvals); free(rows);
-        free(bias); free(dbias); free(scratch); free(qgrad); free(part);
+        free(bias); free(dbias); free(scratch); free(qgrad); free(part); free(zero); free(sink);
         return -3;
     }
     for (long e = 0; e < slices * plane; ++e) dq[e] = dk[e] = dv[e] = 0.0;
@@ -367,19 +375,24 @@ int halo_ref_bwd(const double* q, const double* k, const double* v,
                 const int x0 = (x / block) * block - halo;
                 const double* qv = q + so + ((long)y * W + x) * d;
                 int n = 0;
+                double* tsink = sink + t * 2 * d;
                 for (int ky = y0; ky < y0 + r; ++ky) {
-                    if (ky < 0 || ky >= H) continue;
+                    const int row_in = ky >= 0 && ky < H;
+                    if (!row_in && !zero_pad) continue;
+                    if (centred && (ky < y - halo || ky > y + halo)) continue;
                     const int rowh = ky - y + c0;
-                    const double rh = dot(qv, rel_h + (long)rowh * d, d);
+                    const double rh = dot(qv + hlo, rel_h + (long)rowh * d + hlo, hhi - hlo);
                     for (int kx = x0; kx < x0 + r; ++kx) {
-                        if (kx < 0 || kx >= W) continue;
+                        const int in = row_in && kx >= 0 && kx < W;
+                        if (!in && !zero_pad) continue;
+                        if (centred && (kx < x - halo || kx > x + halo)) continue;
                         const int roww = kx - x + c0;
                         const long off = so + ((long)ky * W + kx) * d;
-                        tk[n] = k + off;
-                        tv[n] = v + off;
-                        tdk[n] = dk + off;
-                        tdv[n] = dv + off;
-                        tb[n] = rh + dot(qv, rel_w + (long)roww * d, d);
+                        tk[n] = in ? k + off : zero;
+                        tv[n] = in ? v + off : zero;
+                        tdk[n] = in ? dk + off : tsink;
+                        tdv[n] = in ? dv + off : tsink + d;
+                        tb[n] = rh + dot(qv + wlo, rel_w + (long)roww * d + wlo, whi - wlo);
                         trow[2 * n] = rowh;
                         trow[2 * n + 1] = roww;
                         ++n;
@@ -395,9 +408,12 @@ int halo_ref_bwd(const double* q, const double* k, const double* v,
                     const double* rwr = rel_w + (long)trow[2 * j + 1] * d;
                     double* ghr = ph + (long)trow[2 * j] * d;
                     double* gwr = pw + (long)trow[2 * j + 1] * d;
-                    for (int c = 0; c < d; ++c) {
-                        dqv[c] += tdb[j] * (rhr[c] + rwr[c]);
+                    for (int c = hlo; c < hhi; ++c) {
+                        dqv[c] += tdb[j] * rhr[c];
                         ghr[c] += tdb[j] * qv[c];
+                    }
+                    for (int c = wlo; c < whi; ++c) {
+                        dqv[c] += tdb[j] * rwr[c];
                         gwr[c] += tdb[j] * qv[c];
                     }
                 }
@@ -410,8 +426,19 @@ int halo_ref_bwd(const double* q, const double* k, const double* v,
             drel_w[e] += part[sl * 2 * nrel + nrel + e];
         }
     free(keys); free(vals); free(dkeys); free(dvals); free(rows);
-    free(bias); free(dbias); free(scratch); free(qgrad); free(part);
+    free(bias); free(dbias); free(scratch); free(qgrad); free(part); free(zero); free(sink);
     return 0;
+}
+
+/* The backward of the pages' default semantics: halo_ref_bwd_ex with no flags. */
+int halo_ref_bwd(const double* q, const double* k, const double* v,
+                 const double* rel_h, const double* rel_w, const double* dout,
+                 double* dq, double* dk, double* dv, double* drel_h, double* drel_w,
+                 int B, int heads, int H, int W, int d,
+                 int block, int halo, int stride, double scale, int nthreads)
+{
+    return halo_ref_bwd_ex(q, k, v, rel_h, rel_w, dout, dq, dk, dv, drel_h, drel_w, B, heads, H, W, d,
+                           block, halo, stride, scale, 0, nthreads);
 }
 
 /* Number of OpenMP threads a parallel region would use (1 without OpenMP). */

@@ -114,3 +114,29 @@ def test_combined_flags_and_bad_flags():
     np.testing.assert_allclose(got, oracle.halo_attn_ref(q, k, v, rh2, rw2, block, halo), rtol=0, atol=1e-13)
     with pytest.raises(ValueError):
         oracle.halo_attn_ref(q, k, v, rh, rw, block, halo, flags=16)
+
+
+# ------------------------------------------------ backward of the variants
+@pytest.mark.parametrize("flags", [CENTRED_OFFSET, ZERO_PAD, CENTRED_MASK, HALF_SPLIT,
+                                   ZERO_PAD | CENTRED_MASK | HALF_SPLIT])
+@pytest.mark.parametrize("H,W,d,block,halo,stride", [(6, 5, 2, 4, 1, 1), (8, 8, 2, 4, 2, 2)])
+def test_variant_backward_matches_central_differences(H, W, d, block, halo, stride, flags):
+    ins = list(case(1, 2, H, W, d, block, halo, seed=7 * H + flags))
+    g = rnd((1, 2, H // stride, W // stride, d), 99)
+    grads = oracle.halo_attn_bwd_ref(*ins, g, block, halo, stride, flags=flags)
+    eps = 1e-5
+
+    def loss(a):
+        return float((oracle.halo_attn_ref(*a, block, halo, stride, flags=flags) * g).sum())
+
+    for t in range(5):
+        fd = np.zeros_like(ins[t])
+        for idx in np.ndindex(*ins[t].shape):
+            a = [x.copy() for x in ins]
+            a[t][idx] += eps
+            lp = loss(a)
+            a[t][idx] -= 2 * eps
+            fd[idx] = (lp - loss(a)) / (2 * eps)
+        np.testing.assert_allclose(grads[t], fd, rtol=1e-6, atol=1e-7)
+    if flags & HALF_SPLIT:   # unused table channels get no gradient
+        assert not grads[3][:, d // 2:].any() and not grads[4][:, :d // 2].any()
