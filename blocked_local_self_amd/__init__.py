@@ -47,6 +47,15 @@ def select_kernel(d: int, block: int, halo: int, query_stride: int = 1, dtype: s
     return {v: k for k, v in KERNELS.items()}[st]
 
 
+def _flags(variants) -> int:
+    flags = 0
+    for name in variants:
+        if name not in VARIANTS:
+            raise ValueError(f"unknown variant {name!r}; expected some of {sorted(VARIANTS)}")
+        flags |= VARIANTS[name]
+    return flags
+
+
 def _check_inputs(q, k, v, rel_h, rel_w, block, halo, query_stride, **extra):
     import torch
     tensors = {"q": q, "k": k, "v": v, "rel_h": rel_h, "rel_w": rel_w, **extra}
@@ -100,11 +109,7 @@ def halo_attn_fwd(q, k, v, rel_h, rel_w, block: int, halo: int, query_stride: in
         raise ValueError(f"out must be a contiguous {oshape} {q.dtype} tensor on {q.device}")
     if kernel not in KERNELS:
         raise ValueError(f"kernel must be one of {sorted(KERNELS)}")
-    flags = 0
-    for name in variants:
-        if name not in VARIANTS:
-            raise ValueError(f"unknown variant {name!r}; expected some of {sorted(VARIANTS)}")
-        flags |= VARIANTS[name]
+    flags = _flags(variants)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     lse = torch.empty(oshape[:4], dtype=torch.float32, device=q.device) if return_lse else None
@@ -130,7 +135,7 @@ def bwd_workspace_bytes(B: int, heads: int, H: int, W: int, d: int, block: int, 
 
 def halo_attn_bwd(q, k, v, rel_h, rel_w, dout, block: int, halo: int, query_stride: int = 1,
                   scale: float | None = None, out=None, lse=None, kernel: str = "auto",
-                  workspace=None, grads=None, stream=None):
+                  workspace=None, grads=None, stream=None, variants=()):
     """Halo attention backward: gradients given dout = d loss / d out.
 
     Same tensors and arguments as ``halo_attn_fwd`` plus ``dout``
@@ -141,6 +146,8 @@ def halo_attn_bwd(q, k, v, rel_h, rel_w, dout, block: int, halo: int, query_stri
     ``out``, ``lse``: the forward's output and log normalisers
     (``halo_attn_fwd(..., return_lse=True)``), or both None to recompute them.
     ``grads``: optional preallocated (dq, dk, dv, drel_h, drel_w) to write into.
+    ``variants``: as in ``halo_attn_fwd`` (out and lse must come from a
+    forward with the same variants).
     """
     import torch
     B, heads, H, W, d = _check_inputs(q, k, v, rel_h, rel_w, block, halo, query_stride, dout=dout)
@@ -186,14 +193,14 @@ def halo_attn_bwd(q, k, v, rel_h, rel_w, dout, block: int, halo: int, query_stri
         stream = torch.cuda.current_stream(q.device)
     lib = _native.load()
     with torch.cuda.device(q.device):
-        st = lib.halo_attn_bwd_kernel(q.data_ptr(), k.data_ptr(), v.data_ptr(), rel_h.data_ptr(),
-                                      rel_w.data_ptr(), out.data_ptr() if out is not None else None,
-                                      dout.data_ptr(), lse.data_ptr() if lse is not None else None,
-                                      dq.data_ptr(), dk.data_ptr(),
-                                      dv.data_ptr(), drh.data_ptr(), drw.data_ptr(), workspace.data_ptr(),
-                                      workspace.numel() * workspace.element_size(), B, heads, H, W, d,
-                                      block, halo, s, float(scale), _dtype_code(q), KERNELS[kernel],
-                                      stream.cuda_stream)
+        st = lib.halo_attn_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), rel_h.data_ptr(),
+                                  rel_w.data_ptr(), out.data_ptr() if out is not None else None,
+                                  dout.data_ptr(), lse.data_ptr() if lse is not None else None,
+                                  dq.data_ptr(), dk.data_ptr(),
+                                  dv.data_ptr(), drh.data_ptr(), drw.data_ptr(), workspace.data_ptr(),
+                                  workspace.numel() * workspace.element_size(), B, heads, H, W, d,
+                                  block, halo, s, float(scale), _dtype_code(q), _flags(variants),
+                                  KERNELS[kernel], stream.cuda_stream)
     _native.check(st)
     return dq, dk, dv, drh, drw
 
@@ -205,20 +212,20 @@ def _make_function():
         """out = halo_attn_fwd(...); its backward calls halo_attn_bwd."""
 
         @staticmethod
-        def forward(ctx, q, k, v, rel_h, rel_w, block, halo, query_stride, scale):
+        def forward(ctx, q, k, v, rel_h, rel_w, block, halo, query_stride, scale, variants):
             out, lse = halo_attn_fwd(q, k, v, rel_h, rel_w, block, halo, query_stride, scale=scale,
-                                     return_lse=True)
+                                     return_lse=True, variants=variants)
             ctx.save_for_backward(q, k, v, rel_h, rel_w, out, lse)
-            ctx.cfg = (block, halo, query_stride, scale)
+            ctx.cfg = (block, halo, query_stride, scale, variants)
             return out
 
         @staticmethod
         def backward(ctx, dout):
             q, k, v, rel_h, rel_w, out, lse = ctx.saved_tensors
-            block, halo, s, scale = ctx.cfg
+            block, halo, s, scale, variants = ctx.cfg
             dq, dk, dv, drh, drw = halo_attn_bwd(q, k, v, rel_h, rel_w, dout.contiguous(), block, halo,
-                                                 s, scale=scale, out=out, lse=lse)
-            return dq, dk, dv, drh.to(rel_h.dtype), drw.to(rel_w.dtype), None, None, None, None
+                                                 s, scale=scale, out=out, lse=lse, variants=variants)
+            return dq, dk, dv, drh.to(rel_h.dtype), drw.to(rel_w.dtype), None, None, None, None, None
 
     return HaloAttentionFunction
 
@@ -227,11 +234,14 @@ _FUNCTION = None
 
 
 def halo_attention(q, k, v, rel_h, rel_w, block: int, halo: int, query_stride: int = 1,
-                   scale: float | None = None):
-    """Differentiable halo attention (torch autograd) on the library's kernels."""
+                   scale: float | None = None, variants=()):
+    """Differentiable halo attention (torch autograd) on the library's kernels.
+
+    ``variants``: semantic variants (names from VARIANTS), forward and backward.
+    """
     global _FUNCTION
     if _FUNCTION is None:
         _FUNCTION = _make_function()
     if scale is None:
         scale = float(q.shape[-1]) ** -0.5
-    return _FUNCTION.apply(q, k, v, rel_h, rel_w, block, halo, query_stride, scale)
+    return _FUNCTION.apply(q, k, v, rel_h, rel_w, block, halo, query_stride, scale, tuple(variants))

@@ -48,6 +48,8 @@ def load() -> ctypes.CDLL:
     lib.halo_attn_fwd_ex.restype = i
     lib.halo_attn_fwd_lse.argtypes = [vp] * 7 + [i] * 8 + [f, i, i, vp]
     lib.halo_attn_fwd_lse.restype = i
+    lib.halo_attn_bwd_ex.argtypes = [vp] * 14 + [sz] + [i] * 8 + [f, i, i, i, vp]
+    lib.halo_attn_bwd_ex.restype = i
     lib.halo_attn_bwd_kernel.argtypes = [vp] * 14 + [sz] + [i] * 8 + [f, i, i, vp]
     lib.halo_attn_bwd_kernel.restype = i
     lib.halo_attn_bwd.argtypes = [vp] * 14 + [sz] + [i] * 8 + [f, i, vp]

@@ -304,16 +304,18 @@ long long halo_attn_bwd_workspace_bytes(int B, int heads, int H, int W, int d,
     return (long long)bwd_ws_bytes(g, dtype == HALO_BF16);
 }
 
-int halo_attn_bwd_kernel(const void* q, const void* k, const void* v,
-                         const void* rel_h, const void* rel_w,
-                         const void* out, const void* dout, const float* lse,
-                         void* dq, void* dk, void* dv, float* drel_h, float* drel_w,
-                         void* workspace, size_t workspace_bytes,
-                         int B, int heads, int H, int W, int d,
-                         int block, int halo, int query_stride,
-                         float scale, int dtype, int kernel, void* stream)
+int halo_attn_bwd_ex(const void* q, const void* k, const void* v,
+                     const void* rel_h, const void* rel_w,
+                     const void* out, const void* dout, const float* lse,
+                     void* dq, void* dk, void* dv, float* drel_h, float* drel_w,
+                     void* workspace, size_t workspace_bytes,
+                     int B, int heads, int H, int W, int d,
+                     int block, int halo, int query_stride,
+                     float scale, int dtype, int flags, int kernel, void* stream)
 {
     g_err[0] = 0;
+    if (flags & ~(HALO_CENTRED_OFFSET | HALO_ZERO_PAD | HALO_CENTRED_MASK | HALO_HALF_SPLIT))
+        return fail(HALO_ERR_SHAPE, "flags=%d has bits outside the halo_flags values", flags);
     if (kernel != HALO_KERNEL_AUTO && kernel != HALO_KERNEL_GENERIC && kernel != HALO_KERNEL_MFMA &&
         kernel != HALO_KERNEL_MFMA_STRIP)
         return fail(HALO_ERR_SHAPE, "kernel=%d is not a halo_kernel value", kernel);
@@ -321,6 +323,8 @@ int halo_attn_bwd_kernel(const void* q, const void* k, const void* v,
     bool empty = false;
     int st = check_sizes(B, heads, H, W, d, block, halo, query_stride, scale, dtype, g, empty);
     if (st) return st;
+    g.flags = flags;
+    if (flags & HALO_CENTRED_OFFSET) g.c0 = g.r - 1;
     if (!drel_h || !drel_w) return fail(HALO_ERR_NULL, "null drel_h or drel_w");
     const int r = g.r;
     const size_t tabf = (size_t)(2 * r - 1) * d;
@@ -382,8 +386,11 @@ int halo_attn_bwd_kernel(const void* q, const void* k, const void* v,
         if (lse == nullptr) {   // the forward's out and lse, recomputed into the workspace
             fo = base + w.out;
             fl = reinterpret_cast<float*>(base + w.lse);
-            e = halo::launch_mfma(q, k, v, rel_h, rel_w, base + w.out, reinterpret_cast<float*>(base + w.lse),
-                                  g, false, s);
+            float* wl = reinterpret_cast<float*>(base + w.lse);
+            // the variants run on the persistent kernel or the generic one
+            e = (flags == 0 || halo::ring_supported(g))
+                    ? halo::launch_mfma(q, k, v, rel_h, rel_w, base + w.out, wl, g, false, s)
+                    : halo::launch_generic(q, k, v, rel_h, rel_w, base + w.out, wl, g, bf16, s);
         }
         if (e == hipSuccess)
             e = halo::launch_bwd_mfma(q, k, v, rel_h, rel_w, fo, dout, fl, dq, dk, dv,
@@ -396,6 +403,20 @@ int halo_attn_bwd_kernel(const void* q, const void* k, const void* v,
     if (e != hipSuccess)
         return fail(HALO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return HALO_OK;
+}
+
+int halo_attn_bwd_kernel(const void* q, const void* k, const void* v,
+                         const void* rel_h, const void* rel_w,
+                         const void* out, const void* dout, const float* lse,
+                         void* dq, void* dk, void* dv, float* drel_h, float* drel_w,
+                         void* workspace, size_t workspace_bytes,
+                         int B, int heads, int H, int W, int d,
+                         int block, int halo, int query_stride,
+                         float scale, int dtype, int kernel, void* stream)
+{
+    return halo_attn_bwd_ex(q, k, v, rel_h, rel_w, out, dout, lse, dq, dk, dv, drel_h, drel_w, workspace,
+                            workspace_bytes, B, heads, H, W, d, block, halo, query_stride, scale, dtype, 0,
+                            kernel, stream);
 }
 
 int halo_attn_bwd(const void* q, const void* k, const void* v,

@@ -121,6 +121,11 @@ void bwd_q_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
     const T* vs = v + qb.bh * plane;
     const int nq = qb.nqy * qb.nqx;
     const int y0 = qb.ybeg - g.halo, x0 = qb.xbeg - g.halo;
+    // semantic variants (the forward's flags): zero padding, centred mask,
+    // half-split embedding (height on channels < hhi, width on >= wlo)
+    const bool zpad = g.flags & kFlagZeroPad, cmask = g.flags & kFlagCentredMask;
+    const int hhi = (g.flags & kFlagHalfSplit) ? d / 2 : d;
+    const int wlo = (g.flags & kFlagHalfSplit) ? d / 2 : 0;
 
     for (int qbase = 0; qbase < nq; qbase += blockDim.x) {
         const int qi = qbase + threadIdx.x;
@@ -161,7 +166,7 @@ void bwd_q_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
                 const int64_t off = ((int64_t)ky * g.W + kx) * d + c;
                 Ks[j][c] = in ? to_f32(ks[off]) : 0.f;
                 Vs[j][c] = in ? to_f32(vs[off]) : 0.f;
-                if (c == 0) valid[j] = in;
+                if (c == 0) valid[j] = in || (zpad && t < nkeys);
             }
             __syncthreads();
             if (!active) continue;
@@ -170,6 +175,9 @@ void bwd_q_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
                 if (!valid[j]) continue;
                 const int idx = kbase + j;
                 const int t = idx / r, u = idx - t * r;
+                if (cmask && (y0 + t < y - g.halo || y0 + t > y + g.halo || x0 + u < x - g.halo ||
+                              x0 + u > x + g.halo))
+                    continue;
                 if (t != cur_t) {            // window row changes: flush its sum
                     if (cur_t >= 0) gs[cur_t] = grow;
                     cur_t = t;
@@ -177,7 +185,7 @@ void bwd_q_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
                     rhp = rel_h + (int64_t)(y0 + t - y + g.c0) * d;
                     float a = 0.f;
 #pragma unroll
-                    for (int c = 0; c < DMAX; ++c) if (c < d) a += qr[c] * to_f32(rhp[c]);
+                    for (int c = 0; c < DMAX; ++c) if (c < hhi) a += qr[c] * to_f32(rhp[c]);
                     rh = a;
                 }
                 const T* wp = rel_w + (int64_t)(x0 + u - x + g.c0) * d;
@@ -185,14 +193,15 @@ void bwd_q_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
 #pragma unroll
                 for (int c = 0; c < DMAX; ++c)
                     if (c < d) {
-                        sc += qr[c] * (Ks[j][c] + to_f32(wp[c]));
+                        sc += qr[c] * (Ks[j][c] + (c >= wlo ? to_f32(wp[c]) : 0.f));
                         gv += gr[c] * Vs[j][c];
                     }
                 const float p = __expf(sc * g.scale - lse);
                 const float sdl = g.scale * p * (gv - D);
 #pragma unroll
                 for (int c = 0; c < DMAX; ++c)
-                    if (c < d) acc[c] += sdl * (Ks[j][c] + to_f32(wp[c]) + to_f32(rhp[c]));
+                    if (c < d)
+                        acc[c] += sdl * (Ks[j][c] + (c >= wlo ? to_f32(wp[c]) : 0.f) + (c < hhi ? to_f32(rhp[c]) : 0.f));
                 grow += sdl;
                 gs[r + u] += sdl;            // this thread's own entry
             }
@@ -218,7 +227,8 @@ void bwd_q_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
         for (int qi = 0; qi < nq; ++qi) {
             const int iy = qi / qb.nqx, ix = qi - iy * qb.nqx;
             const int yl = iy * g.stride, xl = ix * g.stride;
-            const int t = R - (r - 1) + (tab == 0 ? yl : xl);
+            // window row (column) whose table row is R for this query
+            const int t = R + (tab == 0 ? yl : xl) + g.halo - g.c0;
             if (t < 0 || t >= r) continue;
             const int64_t opix = qb.bh * qplane + (int64_t)(qb.ybeg / g.stride + iy) * g.Wo +
                                  qb.xbeg / g.stride + ix;
@@ -226,7 +236,7 @@ void bwd_q_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
             const int64_t qoff = ((int64_t)(qb.ybeg + yl) * g.W + qb.xbeg + xl) * d + c;
             acc += gsum * to_f32(qs[qoff]);
         }
-        part[e] = acc;
+        part[e] = (tab == 0 ? c < hhi : c >= wlo) ? acc : 0.f;   // unused half-split channels: 0
     }
 }
 
@@ -255,6 +265,9 @@ void bwd_kv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     const T* qs = q + bh * plane;
     const T* gsrc = dout + bh * qplane * d;
     const int A = (g.halo + g.block - 1) / g.block;   // block positions a key's viewers reach
+    const bool cmask = g.flags & kFlagCentredMask;
+    const int hhi = (g.flags & kFlagHalfSplit) ? d / 2 : d;
+    const int wlo = (g.flags & kFlagHalfSplit) ? d / 2 : 0;
 
     for (int kbase = 0; kbase < nk; kbase += blockDim.x) {
         const int ki = kbase + threadIdx.x;
@@ -297,13 +310,17 @@ void bwd_kv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
                     __syncthreads();
                     if (!mine) continue;
                     for (int j = 0; j < qn; ++j) {
+                        if (cmask && (ky < Ys[j] - g.halo || ky > Ys[j] + g.halo || kx < Xs[j] - g.halo ||
+                                      kx > Xs[j] + g.halo))
+                            continue;
                         const T* rhp = rel_h + (int64_t)(ky - Ys[j] + g.c0) * d;
                         const T* rwp = rel_w + (int64_t)(kx - Xs[j] + g.c0) * d;
                         float sc = 0.f, gv = 0.f;
 #pragma unroll
                         for (int c = 0; c < DMAX; ++c)
                             if (c < d) {
-                                sc += Qs[j][c] * (kr[c] + to_f32(rhp[c]) + to_f32(rwp[c]));
+                                sc += Qs[j][c] * (kr[c] + (c < hhi ? to_f32(rhp[c]) : 0.f) +
+                                                  (c >= wlo ? to_f32(rwp[c]) : 0.f));
                                 gv += Gs[j][c] * vr[c];
                             }
                         const float p = __expf(sc * g.scale - Ls[j]);

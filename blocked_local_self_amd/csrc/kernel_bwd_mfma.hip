@@ -115,6 +115,14 @@ void bwd_block_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
     const int wy0 = yb - g.halo, wx0 = xb - g.halo;            // window origin
     const int tlo = max(0, -wy0), thi = min(r, g.H - wy0);     // in-image window rows
     const int clo = max(0, -wx0), chi = min(r, g.W - wx0);     // in-image window columns
+    // semantic variants (the forward's flags): zero padding keeps every
+    // window position in the softmax (off-image ones are zero in LDS); the
+    // centred mask keeps rows / columns yl..yl+2h; the centred offset moves
+    // every table row by -h; the half split zeroes table channels
+    const bool zpad = g.flags & kFlagZeroPad, cmask = g.flags & kFlagCentredMask;
+    const bool half = g.flags & kFlagHalfSplit;
+    const int coff = g.c0 - (r - 1 + g.halo);
+    const int qtlo = zpad ? 0 : tlo, qthi = zpad ? r : thi;   // rows in the softmax
     const int64_t plane = (int64_t)g.H * g.W * D;
     const int64_t oplane = (int64_t)g.Ho * g.Wo;
     constexpr int SIDE = NT == 1 ? 4 : 8;       // queries per block row / column
@@ -194,8 +202,8 @@ void bwd_block_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
         const int nrel = 2 * r - 1;
         for (int e = tid; e < kTabRows * D; e += 256) {
             const int row = e / D, c = e - row * D;
-            const unsigned short hv = row < nrel ? rhs[row * D + c] : (unsigned short)0;
-            const unsigned short wv = row < nrel ? rws[row * D + c] : (unsigned short)0;
+            const unsigned short hv = row < nrel && (!half || c < D / 2) ? rhs[row * D + c] : (unsigned short)0;
+            const unsigned short wv = row < nrel && (!half || c >= D / 2) ? rws[row * D + c] : (unsigned short)0;
             bst<unsigned short>(smem, p.off_tab + 2u * e, hv);
             bst<unsigned short>(smem, p.off_tab + 2u * (kTabRows * D + e), wv);
             bst<unsigned short>(smem, p.off_tabt + 2u * (c * kTabRows + row), hv);
@@ -276,13 +284,15 @@ void bwd_block_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int w = 4 * gq + i;
-                const int row = w - (tab == 0 ? xl : yl) + r - 1;   // in [0, 31) for w < 16
+                const int row = w - (tab == 0 ? xl : yl) + r - 1 + coff;   // in [0, 31) for w < 16
                 const float gval = bld<float>(smem, scr(row));
+                const int lo = tab == 0 ? xl : yl;
+                const bool near = !cmask || (w >= lo && w <= lo + 2 * g.halo);
                 if (tab == 0) {
-                    const bool in = w >= clo && w < chi;
+                    const bool in = (zpad ? w < r : (w >= clo && w < chi)) && near;
                     bst<float>(smem, p.off_rw + 4u * (w * NQ + 16 * u + n), in ? gval : kMaskLogit);
                 } else {
-                    const bool in = w >= tlo && w < thi;
+                    const bool in = (zpad ? w < r : (w >= tlo && w < thi)) && near;
                     bst<float>(smem, p.off_rh + 4u * (w * NQ + 16 * u + n), in ? alpha * gval - lse2 : -INFINITY);
                 }
             }
@@ -353,9 +363,9 @@ void bwd_block_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
             ghT = mma_k32(__builtin_bit_cast(s16x8, u32x4{e0, e0, e1, e1}), lp, ghT);
             gwT = mma_k32(__builtin_bit_cast(s16x8, ecol), lp, gwT);
         };
-        int t0 = tlo;
-        for (; t0 + 1 < thi; t0 += 2) step(std::true_type{}, t0);
-        if (t0 < thi) step(std::false_type{}, t0);
+        int t0 = qtlo;
+        for (; t0 + 1 < qthi; t0 += 2) step(std::true_type{}, t0);
+        if (t0 < qthi) step(std::false_type{}, t0);
 
         // sums re-indexed by table row (R = w - yl + r - 1 for rows, - xl for
         // columns), zero elsewhere, in this wave's scratch; then
@@ -371,7 +381,7 @@ void bwd_block_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int w = 4 * gq + i;
-                if (w < r) bst<float>(smem, scr(w - sh + r - 1), gs[i]);
+                if (w < r) bst<float>(smem, scr(w - sh + r - 1 + coff), gs[i]);
             }
             // B operand of table^T . sums: lane (n, g) = query n, table rows 8g..8g+7
             float sv[8];
@@ -517,8 +527,11 @@ void bwd_block_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
         float acc = 0.f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) acc += red[(w * 2 + tab) * kTabRows * D + rr];
-        // part layout: table 0 = rel_h (row sums), 1 = rel_w (column sums)
-        dst[e] = acc * g.scale;
+        // part layout: table 0 = rel_h (row sums), 1 = rel_w (column sums);
+        // half split: the channels a table does not use get no gradient
+        const int c = rr % D;
+        const bool used = !half || (tab == 0 ? c < D / 2 : c >= D / 2);
+        dst[e] = used ? acc * g.scale : 0.f;
     }
 }
 

@@ -140,8 +140,8 @@ int halo_attn_fwd_lse(const void* q, const void* k, const void* v,
  * halo_attn_fwd_lse with semantic variants: flags is an OR of halo_flags
  * values (other bits: HALO_ERR_SHAPE).  Variants run on the generic kernel
  * and on the persistent matrix-core kernel; HALO_KERNEL_MFMA_STRIP with
- * flags != 0 returns HALO_ERR_UNSUPPORTED.  The backward computes the
- * default semantics only.
+ * flags != 0 returns HALO_ERR_UNSUPPORTED.  halo_attn_bwd_ex is the
+ * matching backward.
  */
 int halo_attn_fwd_ex(const void* q, const void* k, const void* v,
                      const void* rel_h, const void* rel_w, void* out, float* lse,
@@ -212,6 +212,19 @@ int halo_attn_bwd_kernel(const void* q, const void* k, const void* v,
                          int B, int heads, int H, int W, int d,
                          int block, int halo, int query_stride,
                          float scale, int dtype, int kernel, void* stream);
+
+/* halo_attn_bwd_kernel for the semantic variants: flags as in
+ * halo_attn_fwd_ex (the out and lse passed in must come from the forward
+ * with the same flags).  With HALO_HALF_SPLIT the channels a table does not
+ * use get a zero gradient. */
+int halo_attn_bwd_ex(const void* q, const void* k, const void* v,
+                     const void* rel_h, const void* rel_w,
+                     const void* out, const void* dout, const float* lse,
+                     void* dq, void* dk, void* dv, float* drel_h, float* drel_w,
+                     void* workspace, size_t workspace_bytes,
+                     int B, int heads, int H, int W, int d,
+                     int block, int halo, int query_stride,
+                     float scale, int dtype, int flags, int kernel, void* stream);
 
 /* halo_attn_bwd_kernel with kernel = HALO_KERNEL_AUTO. */
 int halo_attn_bwd(const void* q, const void* k, const void* v,

@@ -66,3 +66,35 @@ def test_variants_refused_where_not_supported():
         halo_attn_fwd(q, k, v, rh, rw, 8, 3, kernel="mfma_strip", variants=("zero_pad",))
     with pytest.raises(ValueError):
         halo_attn_fwd(q, k, v, rh, rw, 8, 3, variants=("no_such_variant",))
+
+
+# ------------------------------------------------------ backward of the variants
+BWD_TOL = {"fp32": 1e-4, "bf16": 1.5e-2}   # as for the default backward, relative to max |oracle|
+
+
+@pytest.mark.parametrize("kernel,dtype", [("mfma", "bf16"), ("generic", "fp32")])
+@pytest.mark.parametrize("variants", VARIANT_SETS, ids=lambda v: "+".join(v))
+@pytest.mark.parametrize("shape", [(2, 2, 24, 24, 16, 8, 3, 1), (1, 2, 32, 48, 32, 8, 3, 2)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_variant_backward_matches_oracle(shape, variants, kernel, dtype):
+    from blocked_local_self_amd import halo_attn_bwd
+    from blocked_local_self_amd.inputs import make_grad_output
+    B, heads, H, W, d, block, halo, stride = shape
+    print(f"variant bwd case {shape} {variants} {kernel} {dtype}", flush=True)
+    inp = make_inputs(B, heads, H, W, d, block, halo, dtype=dtype, seed=3 * sum(shape) + len(variants))
+    g = make_grad_output(B, heads, H // stride, W // stride, d, dtype=dtype, seed=sum(shape))
+    q, k, v, rh, rw = (t.to(DEV) for t in inp)
+    out, lse = halo_attn_fwd(q, k, v, rh, rw, block, halo, stride, variants=variants, return_lse=True)
+    got = halo_attn_bwd(q, k, v, rh, rw, g.to(DEV), block, halo, stride, out=out, lse=lse, kernel=kernel,
+                        variants=variants)
+    torch.cuda.synchronize()
+    flags = sum(ORACLE_FLAG[n] for n in variants)
+    want = oracle.halo_attn_bwd_ref(*(f64(t) for t in inp), f64(g), block, halo, stride, flags=flags)
+    for name, a, b in zip(["dq", "dk", "dv", "drel_h", "drel_w"], got, want):
+        a = f64(a)
+        scale = max(float(np.abs(b).max()), 1e-6)
+        assert np.abs(a - b).max() <= BWD_TOL[dtype] * scale, name
+        if "half_split" in variants and name == "drel_h":
+            assert not a[:, d // 2:].any()
+        if "half_split" in variants and name == "drel_w":
+            assert not a[:, :d // 2].any()
