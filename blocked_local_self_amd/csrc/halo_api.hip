@@ -69,13 +69,14 @@ hipError_t launch_bwd_generic(const void* q, const void* k, const void* v, const
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t st);
 bool ring_supported(const Geometry& g);
 bool bwd_mfma_supported(const Geometry& g, bool bf16);
-int64_t bwd_mfma_workspace_floats(const Geometry& g, int64_t nchunks);
-int64_t bwd_rel_chunks(const Geometry& g);
+int64_t bwd_mfma_rel_rows(const Geometry& g);
+int64_t bwd_mfma_kv_floats(const Geometry& g);
+int64_t bwd_rel_chunks(int64_t nrows);
 hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const void* rh, const void* rw,
                            const void* out, const void* dout, const float* lse, void* dq, void* dk, void* dv,
                            float* part_kv, float* part_rel, const Geometry& g, hipStream_t st);
-hipError_t launch_rel_reduce(const float* part, float* part2, float* drh, float* drw, const Geometry& g,
-                             hipStream_t st);
+hipError_t launch_rel_reduce(const float* part, int64_t nrows, float* part2, float* drh, float* drw,
+                             const Geometry& g, hipStream_t st);
 }  // namespace halo
 
 namespace {
@@ -170,8 +171,8 @@ int check_sizes(int B, int heads, int H, int W, int d, int block, int halo, int 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Workspace of the matrix-core backward, carved in this order (256-byte
-// aligned pieces): per-block dk/dv shares, per-block table partials, the
-// table reduction's first level, then the forward's lse and out when the
+// aligned pieces): per-column dk/dv shares, per-workgroup table partials,
+// the table reduction's first level, then the forward's lse and out when the
 // caller does not pass them.
 struct MfmaWs {
     size_t kv, rel, rel2, lse, out, total;
@@ -179,13 +180,13 @@ struct MfmaWs {
 MfmaWs mfma_ws(const halo::Geometry& g)
 {
     MfmaWs w;
-    const int64_t nblocks = g.BH * g.nbh * g.nbw;
+    const int64_t rows = halo::bwd_mfma_rel_rows(g);
     const int64_t e2 = 2 * (int64_t)(2 * g.r - 1) * g.d;
     const int64_t nq = g.BH * g.Ho * g.Wo;
     w.kv = 0;
-    w.rel = align256(w.kv + (size_t)(nblocks * g.r * g.r * 2 * g.d) * 4);
-    w.rel2 = align256(w.rel + (size_t)(nblocks * e2) * 4);
-    w.lse = align256(w.rel2 + (size_t)(halo::bwd_rel_chunks(g) * e2) * 4);
+    w.rel = align256(w.kv + (size_t)halo::bwd_mfma_kv_floats(g) * 4);
+    w.rel2 = align256(w.rel + (size_t)(rows * e2) * 4);
+    w.lse = align256(w.rel2 + (size_t)(halo::bwd_rel_chunks(rows) * e2) * 4);
     w.out = align256(w.lse + (size_t)nq * 4);
     w.total = align256(w.out + (size_t)(nq * g.d) * 2);
     return w;
@@ -397,7 +398,7 @@ int halo_attn_bwd_ex(const void* q, const void* k, const void* v,
                                       reinterpret_cast<float*>(base + w.kv), reinterpret_cast<float*>(base + w.rel),
                                       g, s);
         if (e == hipSuccess)
-            e = halo::launch_rel_reduce(reinterpret_cast<const float*>(base + w.rel),
+            e = halo::launch_rel_reduce(reinterpret_cast<const float*>(base + w.rel), halo::bwd_mfma_rel_rows(g),
                                         reinterpret_cast<float*>(base + w.rel2), drel_h, drel_w, g, s);
     }
     if (e != hipSuccess)

@@ -426,8 +426,8 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t st)
     return hipGetLastError();
 }
 
-hipError_t launch_rel_reduce(const float* part, float* part2, float* drh, float* drw, const Geometry& g,
-                             hipStream_t st);
+hipError_t launch_rel_reduce(const float* part, int64_t nrows, float* part2, float* drh, float* drw,
+                             const Geometry& g, hipStream_t st);
 
 template <int DMAX, typename T>
 static hipError_t bwd_launch_t(const void* q, const void* k, const void* v, const void* rh, const void* rw,
@@ -449,20 +449,21 @@ static hipError_t bwd_launch_t(const void* q, const void* k, const void* v, cons
     hipLaunchKernelGGL((bwd_kv_kernel<DMAX, T>), dim3((unsigned)nblocks), dim3(kthreads), 0, st,
                        (const T*)q, (const T*)k, (const T*)v, (const T*)rh, (const T*)rw, (const T*)dout,
                        (T*)dk, (T*)dv, g, w);
-    return launch_rel_reduce(w.part, w.part2, drh, drw, g, st);
+    return launch_rel_reduce(w.part, g.BH * g.nbh * g.nbw, w.part2, drh, drw, g, st);
 }
 
-// Table gradients from per-block partials [nblocks][2][(2r-1)*d]: rows are
-// summed kRelChunk at a time, level after level (scratch rows in part2),
-// until at most kRelChunk remain; the last level writes the two tables.
-// Every sum runs in a fixed order.
-hipError_t launch_rel_reduce(const float* part, float* part2, float* drh, float* drw, const Geometry& g,
-                             hipStream_t st)
+// Table gradients from partials [nrows][2][(2r-1)*d] (one row per block or
+// per workgroup): rows are summed kRelChunk at a time, level after level
+// (scratch rows in part2, bwd_rel_chunks(nrows) of them), until at most
+// kRelChunk remain; the last level writes the two tables.  Every sum runs in
+// a fixed order.
+hipError_t launch_rel_reduce(const float* part, int64_t nrows, float* part2, float* drh, float* drw,
+                             const Geometry& g, hipStream_t st)
 {
     const int64_t E = (int64_t)(2 * g.r - 1) * g.d * 2;
     const unsigned ey = (unsigned)((E + 255) / 256);
     const float* in = part;
-    int64_t rows = g.BH * g.nbh * g.nbw;
+    int64_t rows = nrows;
     float* dst = part2;
     while (rows > kRelChunk) {
         const int64_t nch = (rows + kRelChunk - 1) / kRelChunk;
@@ -476,7 +477,7 @@ hipError_t launch_rel_reduce(const float* part, float* part2, float* drh, float*
     return hipGetLastError();
 }
 
-int64_t bwd_rel_chunks(const Geometry& g) { return bwd_nchunks(g.BH * g.nbh * g.nbw); }
+int64_t bwd_rel_chunks(int64_t nrows) { return bwd_nchunks(nrows); }
 
 template <typename T>
 static hipError_t bwd_launch_dt(const void* q, const void* k, const void* v, const void* rh, const void* rw,

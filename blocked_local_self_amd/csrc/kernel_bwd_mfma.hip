@@ -13,9 +13,11 @@
 //   dk = scale sum_queries dl q,  dv = sum_queries P dout,
 //   d rel_h[R] = scale sum dl q over the pairs at row displacement R (d rel_w alike).
 //
-// One workgroup (4 waves) per query block:
-//  * stages the block's window (K and V as MFMA fragments, K also transposed),
-//    both tables, Q^T and dout^T of its queries, and dout.out per query;
+// One workgroup (4 waves) per (batch, head, block column) walks down the
+// column's block rows.  Both tables are staged once.  Per block row:
+//  * staging from registers that were loaded during the previous block row:
+//    the block's window (K and V as MFMA fragments, K also transposed), Q^T
+//    and dout^T of its queries, and dout.out per query;
 //  * relative logits of every query against both tables on MFMA, re-indexed
 //    per query into a width table (window column -> q.rel_w, masked -1e30
 //    off the image or past the window) and a height table (window row ->
@@ -26,15 +28,18 @@
 //    dq^T += K^T dl^T and, on two more MFMAs against 0/1 operands, the sums
 //    of dl over each window row and each window column of the query.  Those
 //    sums, re-indexed by table row, give the tables' share of dq (tables^T
-//    times sums) and the block's table gradients (Q^T times sums), both on
-//    MFMA with the sums split into bf16 high and low parts;
+//    times sums) and the table gradients (Q^T times sums), both on MFMA with
+//    the sums split into bf16 high and low parts; the table gradients stay
+//    in registers for the whole walk;
 //  * key path (wave per window row, scores in the other orientation,
 //    S = Q K^T, so lane (n, g) holds window column n and queries 4g..4g+3):
 //    the same P and dl, then dV^T += dout^T P and dK^T += Q^T dl over pairs
-//    of query tiles.  The window's dk and dv are this block's share only;
-//    they go to a workspace, and a gather kernel sums, for every key, the
-//    shares of the (at most four, for halo < block) windows holding it in a
-//    fixed order.
+//    of query tiles.  The wave owning window row t keeps its sums in
+//    registers: row t of one window is row t - block of the next, and block
+//    is a multiple of 4, so the same wave owns it.  A row leaves once no
+//    later window holds it, as this column's share of that key row; a
+//    gather kernel sums, for every key, the shares of the (at most two, for
+//    halo < block) block columns whose windows hold it in a fixed order.
 // No floating-point atomics anywhere: results are bitwise reproducible.
 #include <algorithm>
 #include <type_traits>
@@ -80,8 +85,8 @@ __device__ inline void split2(float a, float b, unsigned& hi, unsigned& lo)
 
 // NT: 16-query tiles per block (1: 4 x 4 queries, 4: 8 x 8 queries).
 template <int D, int NT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
-void bwd_block_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 16 ? 2 : 1)))
+void bwd_strip_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                       const __bf16* __restrict__ v, const __bf16* __restrict__ rel_h,
                       const __bf16* __restrict__ rel_w, const __bf16* __restrict__ out,
                       const __bf16* __restrict__ dout, const float* __restrict__ lse,
@@ -93,6 +98,11 @@ void bwd_block_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
     constexpr unsigned PIXB = D * 2;
     constexpr unsigned ROWB = kBCols * PIXB;    // bytes per K / V row
     constexpr int NQ = 16 * NT;
+    constexpr int PX = D == 16 ? 2 : 4;         // pixels per staging item (register budget)
+    constexpr int NGX = kBCols / PX;            // items per window row and chunk
+    constexpr int KV_ITEMS = kBRows * NGX * CPP;   // staging items (PX pixels x 8 channels): one per thread
+    static_assert(KV_ITEMS == 256, "one staging item per thread");
+    constexpr int NSLOT = kBRows / 4;           // window rows per wave in the key path
     typedef typename Frag<D>::T FragT;
     extern __shared__ __align__(16) unsigned char smem[];
 
@@ -107,13 +117,10 @@ void bwd_block_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
         const int64_t per = p.nwg >> 3;
         wg = (wg & 7) * per + (wg >> 3);
     }
-    const int64_t nblk_img = (int64_t)g.nbh * g.nbw;
-    const int64_t bh = wg / nblk_img;
-    const int rem = (int)(wg - bh * nblk_img);
-    const int by = rem / g.nbw, bx = rem - by * g.nbw;
-    const int yb = by * g.block, xb = bx * g.block;
-    const int wy0 = yb - g.halo, wx0 = xb - g.halo;            // window origin
-    const int tlo = max(0, -wy0), thi = min(r, g.H - wy0);     // in-image window rows
+    const int64_t bh = wg / g.nbw;                             // (batch, head)
+    const int bx = (int)(wg - bh * g.nbw);                     // block column
+    const int xb = bx * g.block;
+    const int wx0 = xb - g.halo;                               // window column origin
     const int clo = max(0, -wx0), chi = min(r, g.W - wx0);     // in-image window columns
     // semantic variants (the forward's flags): zero padding keeps every
     // window position in the softmax (off-image ones are zero in LDS); the
@@ -122,10 +129,12 @@ void bwd_block_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
     const bool zpad = g.flags & kFlagZeroPad, cmask = g.flags & kFlagCentredMask;
     const bool half = g.flags & kFlagHalfSplit;
     const int coff = g.c0 - (r - 1 + g.halo);
-    const int qtlo = zpad ? 0 : tlo, qthi = zpad ? r : thi;   // rows in the softmax
     const int64_t plane = (int64_t)g.H * g.W * D;
     const int64_t oplane = (int64_t)g.Ho * g.Wo;
     constexpr int SIDE = NT == 1 ? 4 : 8;       // queries per block row / column
+    // the query tile this wave owns in the relative and query phases (NT is
+    // 1 or 4: at most one per wave)
+    const int uown = NT == 4 ? wave : 0;
 
     // query position of block-local query index qi (row-major over the block's query grid)
     auto qpos = [&](int qi, int& yl, int& xl) {
@@ -133,70 +142,20 @@ void bwd_block_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
         yl = iy * g.stride;
         xl = (qi - iy * SIDE) * g.stride;
     };
-    auto qpix = [&](int qi) -> int64_t {      // query pixel in the image
+    auto qpix = [&](int yb, int qi) -> int64_t {      // query pixel in the image
         int yl, xl;
         qpos(qi, yl, xl);
         return (int64_t)(yb + yl) * g.W + xb + xl;
     };
-    auto opix = [&](int qi) -> int64_t {      // output pixel
+    auto opix = [&](int yb, int qi) -> int64_t {      // output pixel
         int yl, xl;
         qpos(qi, yl, xl);
         return (int64_t)((yb + yl) / g.stride) * g.Wo + (xb + xl) / g.stride;
     };
 
-    // query and dout fragments of every query tile (lane n: query 16u+n,
-    // channels gq*KPL..), issued first so they arrive during the staging
-    FragT qfa[NT], gfa[NT];
-#pragma unroll
-    for (int u = 0; u < NT; ++u) {
-        qfa[u] = *reinterpret_cast<const FragT*>(q + bh * plane + qpix(16 * u + n) * D + gq * KPL);
-        gfa[u] = *reinterpret_cast<const FragT*>(dout + (bh * oplane + opix(16 * u + n)) * D + gq * KPL);
-    }
-    // the tile this wave owns in the relative and query phases (NT is 1 or 4:
-    // at most one per wave), loaded separately so no array is indexed at run time
-    const int uown = NT == 4 ? wave : 0;
-    const FragT qown = *reinterpret_cast<const FragT*>(q + bh * plane + qpix(16 * uown + n) * D + gq * KPL);
-    const FragT gown = *reinterpret_cast<const FragT*>(dout + (bh * oplane + opix(16 * uown + n)) * D + gq * KPL);
-    const float lse2own = lse[bh * oplane + opix(16 * uown + n)] * 1.4426950408889634f;   // base-2
-
-    // ---------------------------------------------------------------- staging
+    // ------------------------------------------- tables, once per workgroup
+    // [32][D] (A operands of table . Q^T) and [D][32] (A operands of tables^T . sums)
     {
-        // K, V (swizzled fragment layout) and K^T for window rows 0..kBRows-1,
-        // columns 0..15; everything outside the image or the window is zero
-        const __bf16* kb = k + bh * plane;
-        const __bf16* vb = v + bh * plane;
-        for (int e = tid; e < kBRows * 4 * CPP; e += 256) {
-            const int ch = e % CPP, rest = e / CPP;
-            const int t = rest >> 2, c4 = rest & 3;
-            const int iy = wy0 + t;
-            u32x4 kk[4], vv[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int c = 4 * c4 + j, ix = wx0 + c;
-                kk[j] = u32x4{0u, 0u, 0u, 0u};
-                vv[j] = u32x4{0u, 0u, 0u, 0u};
-                if (t < r && c < r && iy >= 0 && iy < g.H && ix >= 0 && ix < g.W) {
-                    const int64_t off = ((int64_t)iy * g.W + ix) * D + ch * 8;
-                    kk[j] = *reinterpret_cast<const u32x4*>(kb + off);
-                    vv[j] = *reinterpret_cast<const u32x4*>(vb + off);
-                }
-                bst<u32x4>(smem, (unsigned)t * ROWB + c * PIXB + bk_chunk<D>(ch, c), kk[j]);
-                bst<u32x4>(smem, p.off_v + (unsigned)t * ROWB + c * PIXB + bk_chunk<D>(ch, c), vv[j]);
-            }
-            // K^T: channel ch*8 + 2w (+1) of the 4 columns, 8-byte rows
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                if (t >= 16) break;
-                const u32x2 lo = {__builtin_amdgcn_perm(kk[1][w], kk[0][w], 0x05040100u),
-                                  __builtin_amdgcn_perm(kk[3][w], kk[2][w], 0x05040100u)};
-                const u32x2 hi = {__builtin_amdgcn_perm(kk[1][w], kk[0][w], 0x07060302u),
-                                  __builtin_amdgcn_perm(kk[3][w], kk[2][w], 0x07060302u)};
-                const unsigned base = p.off_kt + 2u * ((unsigned)t * kBCols + 4 * c4);
-                bst<u32x2>(smem, base + 2u * (unsigned)((ch * 8 + 2 * w) * kKtPitch), lo);
-                bst<u32x2>(smem, base + 2u * (unsigned)((ch * 8 + 2 * w + 1) * kKtPitch), hi);
-            }
-        }
-        // tables: [32][D] (A operands of table . Q^T) and [D][32] (A operands of tables^T . sums)
         const unsigned short* rhs = reinterpret_cast<const unsigned short*>(rel_h);
         const unsigned short* rws = reinterpret_cast<const unsigned short*>(rel_w);
         const int nrel = 2 * r - 1;
@@ -209,49 +168,48 @@ void bwd_block_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
             bst<unsigned short>(smem, p.off_tabt + 2u * (c * kTabRows + row), hv);
             bst<unsigned short>(smem, p.off_tabt + 2u * (D * kTabRows + c * kTabRows + row), wv);
         }
-        // Q^T and dout^T of the block's queries, and D = dout . out per
-        // query.  Item: 4 consecutive queries (one block-row of queries holds
-        // 4 or 8 of them) x all channels, loaded 16 bytes at a time and
-        // transposed in registers into 8-byte rows (4 queries of a channel).
-        if (tid < NQ / 4) {
-            const int qi0 = 4 * tid;
-            const __bf16* qp = q + bh * plane + qpix(qi0) * D;
-            const int64_t o0 = (bh * oplane + opix(qi0)) * D;
-            float dacc[4] = {0.f, 0.f, 0.f, 0.f};
+    }
+
+    // ------------------------------- inputs of a block row, held in registers
+    // K / V: this thread's staging item (window row kv_t, columns
+    // PX kv_cx .. +PX-1, channels 8 kv_ch .. +7); queries: the fragments of
+    // every query tile (lane n: query 16u+n, channels gq*KPL..) and of the
+    // own tile.
+    struct Pre {
+        u32x4 kk[PX], vv[PX];
+        FragT qf[NT], gf[NT], qo, go, oo;
+        float lse2;
+    };
+    const int kv_ch = tid % CPP, kv_t = (tid / CPP) / NGX, kv_cx = (tid / CPP) % NGX;
+    auto prefetch = [&](int byy, Pre& P) {
+        const int yb = byy * g.block, wy0 = yb - g.halo;
+        {
+            const int iy = wy0 + kv_t;
+            const __bf16* kb = k + bh * plane;
+            const __bf16* vb = v + bh * plane;
 #pragma unroll
-            for (int ch = 0; ch < CPP; ++ch) {
-                u32x4 qq[4], gg[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    qq[j] = *reinterpret_cast<const u32x4*>(qp + (int64_t)j * g.stride * D + ch * 8);
-                    gg[j] = *reinterpret_cast<const u32x4*>(dout + o0 + j * D + ch * 8);
-                    const u32x4 oo = *reinterpret_cast<const u32x4*>(out + o0 + j * D + ch * 8);
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        dacc[j] = fmaf(__builtin_bit_cast(float, oo[w] << 16), __builtin_bit_cast(float, gg[j][w] << 16), dacc[j]);
-                        dacc[j] = fmaf(__builtin_bit_cast(float, oo[w] & 0xffff0000u),
-                                       __builtin_bit_cast(float, gg[j][w] & 0xffff0000u), dacc[j]);
-                    }
-                }
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {          // channels ch*8 + 2w (low halves), + 2w + 1 (high)
-                    const unsigned c = ch * 8 + 2 * w;
-                    const unsigned bq = p.off_qt + 2u * (c * p.qpitch + qi0);
-                    const unsigned bg = p.off_dot + 2u * (c * p.qpitch + qi0);
-                    bst<u32x2>(smem, bq, u32x2{__builtin_amdgcn_perm(qq[1][w], qq[0][w], 0x05040100u),
-                                               __builtin_amdgcn_perm(qq[3][w], qq[2][w], 0x05040100u)});
-                    bst<u32x2>(smem, bq + 2u * p.qpitch, u32x2{__builtin_amdgcn_perm(qq[1][w], qq[0][w], 0x07060302u),
-                                                               __builtin_amdgcn_perm(qq[3][w], qq[2][w], 0x07060302u)});
-                    bst<u32x2>(smem, bg, u32x2{__builtin_amdgcn_perm(gg[1][w], gg[0][w], 0x05040100u),
-                                               __builtin_amdgcn_perm(gg[3][w], gg[2][w], 0x05040100u)});
-                    bst<u32x2>(smem, bg + 2u * p.qpitch, u32x2{__builtin_amdgcn_perm(gg[1][w], gg[0][w], 0x07060302u),
-                                                               __builtin_amdgcn_perm(gg[3][w], gg[2][w], 0x07060302u)});
+            for (int j = 0; j < PX; ++j) {
+                const int c = PX * kv_cx + j, ix = wx0 + c;
+                P.kk[j] = u32x4{0u, 0u, 0u, 0u};
+                P.vv[j] = u32x4{0u, 0u, 0u, 0u};
+                if (kv_t < r && c < r && iy >= 0 && iy < g.H && ix >= 0 && ix < g.W) {
+                    const int64_t off = ((int64_t)iy * g.W + ix) * D + kv_ch * 8;
+                    P.kk[j] = *reinterpret_cast<const u32x4*>(kb + off);
+                    P.vv[j] = *reinterpret_cast<const u32x4*>(vb + off);
                 }
             }
-            bst<f32x4>(smem, p.off_d + 16u * tid, f32x4{dacc[0], dacc[1], dacc[2], dacc[3]});
         }
-    }
-    __syncthreads();
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+            P.qf[u] = *reinterpret_cast<const FragT*>(q + bh * plane + qpix(yb, 16 * u + n) * D + gq * KPL);
+            P.gf[u] = *reinterpret_cast<const FragT*>(dout + (bh * oplane + opix(yb, 16 * u + n)) * D + gq * KPL);
+        }
+        const int64_t oown = bh * oplane + opix(yb, 16 * uown + n);
+        P.qo = *reinterpret_cast<const FragT*>(q + bh * plane + qpix(yb, 16 * uown + n) * D + gq * KPL);
+        P.go = *reinterpret_cast<const FragT*>(dout + oown * D + gq * KPL);
+        P.oo = *reinterpret_cast<const FragT*>(out + oown * D + gq * KPL);
+        P.lse2 = lse[oown] * 1.4426950408889634f;   // base-2
+    };
 
     const unsigned kl = (unsigned)n * PIXB + (D == 16 ? bk_chunk<D>(gq >> 1, n) + (gq & 1) * 8
                                                       : bk_chunk<D>(gq, n));
@@ -259,55 +217,6 @@ void bwd_block_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
     auto vfrag = [&](int t) { return bld<FragT>(smem, p.off_v + kl + (unsigned)t * ROWB); };
     const unsigned scr0 = p.off_scr + wave * (kTabRows * kScrStrideB * 4) + 4u * n;
     auto scr = [&](int row) { return scr0 + 4u * kScrStrideB * row; };
-
-    // --------------------------------------- relative tables per query tile
-    if (wave < NT) {
-        const int u = uown;
-        const FragT qf = qown;
-        int yl, xl;
-        qpos(16 * u + n, yl, xl);
-        const float lse2 = lse2own;
-        for (int tab = 0; tab < 2; ++tab) {          // 0: rel_w -> width table, 1: rel_h -> height
-            f32x4 gv[2];
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                const FragT a = bld<FragT>(smem, p.off_tab + 2u * ((tab == 0 ? kTabRows * D : 0) +
-                                                                     (rt * 16 + n) * D + gq * KPL));
-                gv[rt] = Frag<D>::mma(a, qf, f32x4{0.f, 0.f, 0.f, 0.f});
-            }
-            // scratch row j = table row j, column n = query n
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) bst<float>(smem, scr(rt * 16 + 4 * gq + i), gv[rt][i]);
-            // window position w = 4g+i <- table row w - (yl or xl) + r - 1
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int w = 4 * gq + i;
-                const int row = w - (tab == 0 ? xl : yl) + r - 1 + coff;   // in [0, 31) for w < 16
-                const float gval = bld<float>(smem, scr(row));
-                const int lo = tab == 0 ? xl : yl;
-                const bool near = !cmask || (w >= lo && w <= lo + 2 * g.halo);
-                if (tab == 0) {
-                    const bool in = (zpad ? w < r : (w >= clo && w < chi)) && near;
-                    bst<float>(smem, p.off_rw + 4u * (w * NQ + 16 * u + n), in ? gval : kMaskLogit);
-                } else {
-                    const bool in = (zpad ? w < r : (w >= tlo && w < thi)) && near;
-                    bst<float>(smem, p.off_rh + 4u * (w * NQ + 16 * u + n), in ? alpha * gval - lse2 : -INFINITY);
-                }
-            }
-        }
-    }
-    __syncthreads();
-
-    // ------------------------------------------------------------ query path
-    f32x4 drelT[2][2][D / 16];                     // [table][R tile][channel tile], this wave's queries
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int mt = 0; mt < D / 16; ++mt) drelT[a][b][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // column-indicator operand: A[m][8g+j] = 1 if window column 4g + (j%4) == m
     u32x4 ecol;
@@ -321,193 +230,342 @@ void bwd_block_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
         ecol = u32x4{w01, w23, w01, w23};
     }
 
-    if (wave < NT) {
-        const int u = uown;
-        const FragT qf = qown, gf = gown;
-        const float Dn = bld<float>(smem, p.off_d + 4u * (16 * u + n));
-        f32x4 cinit;
+    // table gradients of this wave's queries over the walk: [table][R tile][channel tile]
+    f32x4 drelT[2][2][D / 16];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) cinit[i] = bld<float>(smem, p.off_rw + 4u * ((4 * gq + i) * NQ + 16 * u + n));
-        f32x4 dqT[D / 16], ghT = {0.f, 0.f, 0.f, 0.f}, gwT = {0.f, 0.f, 0.f, 0.f};
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int mt = 0; mt < D / 16; ++mt) dqT[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const unsigned ktl = p.off_kt + 2u * ((unsigned)n * kKtPitch + 4 * gq);
-        // one K=32 step per two window rows; a last odd row goes alone (its
-        // partner's weights and K^T operand are zero)
-        auto step = [&](auto two_c, int t0) {
-            constexpr bool two = decltype(two_c)::value;
-            const int t1 = two ? t0 + 1 : t0;
-            const float c0 = bld<float>(smem, p.off_rh + 4u * (t0 * NQ + 16 * u + n));
-            const f32x4 s0 = Frag<D>::mma(kfrag(t0), qf, cinit);
-            const f32x4 d0 = Frag<D>::mma(vfrag(t0), gf, f32x4{0.f, 0.f, 0.f, 0.f});
-            float l0[4], l1[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) l0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], alpha, c0)) * (d0[i] - Dn);
-            if (two) {
-                const float c1 = bld<float>(smem, p.off_rh + 4u * (t1 * NQ + 16 * u + n));
-                const f32x4 s1 = Frag<D>::mma(kfrag(t1), qf, cinit);
-                const f32x4 d1 = Frag<D>::mma(vfrag(t1), gf, f32x4{0.f, 0.f, 0.f, 0.f});
+            for (int mt = 0; mt < D / 16; ++mt) drelT[a][b][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // dk^T / dv^T of window rows wave + 4j (lane (n, g): column n, channels
+    // 16mt + 4g + i), carried from one block row to the next
+    f32x4 akT[NSLOT][D / 16], avT[NSLOT][D / 16];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) l1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], alpha, c1)) * (d1[i] - Dn);
-            }
-            const s16x8 lp = __builtin_bit_cast(s16x8, u32x4{pack_bf16x2(l0[0], l0[1]), pack_bf16x2(l0[2], l0[3]),
-                                                             pack_bf16x2(l1[0], l1[1]), pack_bf16x2(l1[2], l1[3])});
+    for (int j = 0; j < NSLOT; ++j)
 #pragma unroll
-            for (int mt = 0; mt < D / 16; ++mt) {
-                const unsigned a = ktl + 2u * (unsigned)(mt * 16 * kKtPitch);
-                const u32x2 x0 = bld<u32x2>(smem, a + 2u * (unsigned)(t0 * kBCols));
-                const u32x2 x1 = two ? bld<u32x2>(smem, a + 2u * (unsigned)(t1 * kBCols)) : u32x2{0u, 0u};
-                dqT[mt] = mma_k32(__builtin_bit_cast(s16x8, u32x4{x0[0], x0[1], x1[0], x1[1]}), lp, dqT[mt]);
-            }
-            const unsigned e0 = n == t0 ? 0x3F803F80u : 0u, e1 = (two && n == t1) ? 0x3F803F80u : 0u;
-            ghT = mma_k32(__builtin_bit_cast(s16x8, u32x4{e0, e0, e1, e1}), lp, ghT);
-            gwT = mma_k32(__builtin_bit_cast(s16x8, ecol), lp, gwT);
-        };
-        int t0 = qtlo;
-        for (; t0 + 1 < qthi; t0 += 2) step(std::true_type{}, t0);
-        if (t0 < qthi) step(std::false_type{}, t0);
+        for (int mt = 0; mt < D / 16; ++mt) akT[j][mt] = avT[j][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        // sums re-indexed by table row (R = w - yl + r - 1 for rows, - xl for
-        // columns), zero elsewhere, in this wave's scratch; then
-        //   dq^T += table^T . sums  and  drel^T += Q^T . sums^T
-        int yl, xl;
-        qpos(16 * u + n, yl, xl);
+    Pre P;
+    prefetch(0, P);
+
+    for (int by = 0; by < g.nbh; ++by) {
+        const int yb = by * g.block;
+        const int wy0 = yb - g.halo;                               // window row origin
+        const int tlo = max(0, -wy0), thi = min(r, g.H - wy0);     // in-image window rows
+        const int qtlo = zpad ? 0 : tlo, qthi = zpad ? r : thi;   // rows in the softmax
+
+        __syncthreads();               // the previous block row is done with LDS
+
+        // ------------------------------------------------------------ staging
+        {
+            // K, V (swizzled fragment layout) and K^T for window rows 0..kBRows-1,
+            // columns 0..15; everything outside the image or the window is zero
+            const int t = kv_t, ch = kv_ch;
 #pragma unroll
-        for (int tab = 0; tab < 2; ++tab) {            // 0: rows -> rel_h, 1: columns -> rel_w
-            const f32x4 gs = tab == 0 ? ghT : gwT;
-            const int sh = (tab == 0 ? yl : xl);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) bst<float>(smem, scr(8 * gq + j), 0.f);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int w = 4 * gq + i;
-                if (w < r) bst<float>(smem, scr(w - sh + r - 1 + coff), gs[i]);
+            for (int j = 0; j < PX; ++j) {
+                const int c = PX * kv_cx + j;
+                bst<u32x4>(smem, (unsigned)t * ROWB + c * PIXB + bk_chunk<D>(ch, c), P.kk[j]);
+                bst<u32x4>(smem, p.off_v + (unsigned)t * ROWB + c * PIXB + bk_chunk<D>(ch, c), P.vv[j]);
             }
-            // B operand of table^T . sums: lane (n, g) = query n, table rows 8g..8g+7
-            float sv[8];
+            // K^T: channel ch*8 + 2w (+1) of the PX columns (PX * 2-byte rows)
+            const unsigned base = p.off_kt + 2u * ((unsigned)t * kBCols + PX * kv_cx);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) sv[j] = bld<float>(smem, scr(8 * gq + j));
-            unsigned hw[4], lw[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) split2(sv[2 * j], sv[2 * j + 1], hw[j], lw[j]);
-            const u32x4 bh4 = {hw[0], hw[1], hw[2], hw[3]}, bl4 = {lw[0], lw[1], lw[2], lw[3]};
-            const unsigned tt = p.off_tabt + 2u * ((tab == 0 ? 0 : D * kTabRows) + gq * 8);
-#pragma unroll
-            for (int mt = 0; mt < D / 16; ++mt) {
-                const s16x8 at = bld<s16x8>(smem, tt + 2u * (unsigned)((mt * 16 + n) * kTabRows));
-                dqT[mt] = mma_k32(at, __builtin_bit_cast(s16x8, bh4), dqT[mt]);
-                dqT[mt] = mma_k32(at, __builtin_bit_cast(s16x8, bl4), dqT[mt]);
-            }
-            // table gradient: drel^T[c][R] += sum_q Q^T[c][q] sums[R][q]:
-            // A = Q^T (lane n': channel, queries 4g'..4g'+3 of tile u),
-            // B = sums^T (lane n: table row 16 rt + n, queries 4g..4g+3)
-            wave_lds_sync();   // the scratch column reads above are done before the row reads below
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                const f32x4 sr = bld<f32x4>(smem, p.off_scr + wave * (kTabRows * kScrStrideB * 4) +
-                                                      4u * (kScrStrideB * (rt * 16 + n) + 4 * gq));
-                unsigned h01, l01, h23, l23;
-                split2(sr[0], sr[1], h01, l01);
-                split2(sr[2], sr[3], h23, l23);
-                const s16x4 bhi = __builtin_bit_cast(s16x4, u32x2{h01, h23});
-                const s16x4 blo = __builtin_bit_cast(s16x4, u32x2{l01, l23});
-#pragma unroll
-                for (int mt = 0; mt < D / 16; ++mt) {
-                    const s16x4 aq = bld<s16x4>(smem, p.off_qt + 2u * ((mt * 16 + n) * p.qpitch + 16 * u + 4 * gq));
-                    drelT[tab == 0 ? 0 : 1][rt][mt] =
-                        __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aq, bhi, drelT[tab == 0 ? 0 : 1][rt][mt], 0, 0, 0);
-                    drelT[tab == 0 ? 0 : 1][rt][mt] =
-                        __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aq, blo, drelT[tab == 0 ? 0 : 1][rt][mt], 0, 0, 0);
+            for (int w = 0; w < 4; ++w) {
+                if constexpr (PX == 4) {
+                    const u32x2 lo = {__builtin_amdgcn_perm(P.kk[1][w], P.kk[0][w], 0x05040100u),
+                                      __builtin_amdgcn_perm(P.kk[3][w], P.kk[2][w], 0x05040100u)};
+                    const u32x2 hi = {__builtin_amdgcn_perm(P.kk[1][w], P.kk[0][w], 0x07060302u),
+                                      __builtin_amdgcn_perm(P.kk[3][w], P.kk[2][w], 0x07060302u)};
+                    bst<u32x2>(smem, base + 2u * (unsigned)((ch * 8 + 2 * w) * kKtPitch), lo);
+                    bst<u32x2>(smem, base + 2u * (unsigned)((ch * 8 + 2 * w + 1) * kKtPitch), hi);
+                } else {
+                    bst<unsigned>(smem, base + 2u * (unsigned)((ch * 8 + 2 * w) * kKtPitch),
+                                  __builtin_amdgcn_perm(P.kk[1][w], P.kk[0][w], 0x05040100u));
+                    bst<unsigned>(smem, base + 2u * (unsigned)((ch * 8 + 2 * w + 1) * kKtPitch),
+                                  __builtin_amdgcn_perm(P.kk[1][w], P.kk[0][w], 0x07060302u));
                 }
             }
-            wave_lds_sync();   // scratch is rewritten by the next table
         }
-        // dq = scale * dq^T (lane: query n, channels 16mt + 4g + i)
-        __bf16* dp = dq + bh * plane + qpix(16 * u + n) * D + gq * 4;
-#pragma unroll
-        for (int mt = 0; mt < D / 16; ++mt)
-            *reinterpret_cast<u32x2*>(dp + mt * 16) =
-                u32x2{pack_bf16x2(dqT[mt][0] * g.scale, dqT[mt][1] * g.scale),
-                      pack_bf16x2(dqT[mt][2] * g.scale, dqT[mt][3] * g.scale)};
-    }
-
-    // -------------------------------------------------------------- key path
-    {
-        constexpr int NP = (NT + 1) / 2;             // pairs of query tiles
-        FragT qf[NT], gf[NT];
-        f32x4 cw[NT], Dv[NT];
+        FragT qfa[NT], gfa[NT];
 #pragma unroll
         for (int u = 0; u < NT; ++u) {
-            qf[u] = qfa[u];
-            gf[u] = gfa[u];
-            cw[u] = bld<f32x4>(smem, p.off_rw + 4u * (n * NQ + 16 * u + 4 * gq));   // column n, queries 4g..
-            Dv[u] = bld<f32x4>(smem, p.off_d + 4u * (16 * u + 4 * gq));
+            qfa[u] = P.qf[u];
+            gfa[u] = P.gf[u];
         }
-        // A operands over query pairs: lane n' = channel, queries {4g..4g+3 of u0, of u1}
-        u32x4 qtA[NP][D / 16], gtA[NP][D / 16];
+        const FragT qown = P.qo, gown = P.go;
+        const float lse2own = P.lse2;
+        if (wave < NT) {
+            // Q^T and dout^T of the own tile (channel gq*KPL + e, query 16u + n),
+            // and D = dout . out of its queries (the four lanes of a query hold
+            // a quarter of the channels each)
+            float dpart = 0.f;
 #pragma unroll
-        for (int pr = 0; pr < NP; ++pr)
-#pragma unroll
-            for (int mt = 0; mt < D / 16; ++mt) {
-                const unsigned rowq = p.off_qt + 2u * ((mt * 16 + n) * p.qpitch + 4 * gq);
-                const unsigned rowg = p.off_dot + 2u * ((mt * 16 + n) * p.qpitch + 4 * gq);
-                const u32x2 a0 = bld<u32x2>(smem, rowq + 2u * (32 * pr)), g0 = bld<u32x2>(smem, rowg + 2u * (32 * pr));
-                u32x2 a1 = {0u, 0u}, g1 = {0u, 0u};
-                if (2 * pr + 1 < NT) {
-                    a1 = bld<u32x2>(smem, rowq + 2u * (32 * pr + 16));
-                    g1 = bld<u32x2>(smem, rowg + 2u * (32 * pr + 16));
-                }
-                qtA[pr][mt] = u32x4{a0[0], a0[1], a1[0], a1[1]};
-                gtA[pr][mt] = u32x4{g0[0], g0[1], g1[0], g1[1]};
+            for (int e = 0; e < KPL; ++e) {
+                const unsigned c = gq * KPL + e;
+                bst<short>(smem, p.off_qt + 2u * (c * p.qpitch + 16 * uown + n), qown[e]);
+                bst<short>(smem, p.off_dot + 2u * (c * p.qpitch + 16 * uown + n), gown[e]);
+                dpart = fmaf(__builtin_bit_cast(float, (unsigned)(unsigned short)gown[e] << 16),
+                             __builtin_bit_cast(float, (unsigned)(unsigned short)P.oo[e] << 16), dpart);
             }
-        const int64_t blk = wg;
-        for (int t = tlo + wave; t < thi; t += 4) {
-            const FragT kf = kfrag(t), vf = vfrag(t);
-            f32x4 dkT[D / 16], dvT[D / 16];
+            const float dsum = sum_over_rows(dpart);
+            if (gq == 0) bst<float>(smem, p.off_d + 4u * (16 * uown + n), dsum);
+        }
+
+        // the next block row's inputs, in flight during this one's compute
+        if (by + 1 < g.nbh) prefetch(by + 1, P);
+
+        // ----------------------------------- relative tables per query tile
+        if (wave < NT) {
+            const int u = uown;
+            const FragT qf = qown;
+            int yl, xl;
+            qpos(16 * u + n, yl, xl);
+            const float lse2 = lse2own;
+            for (int tab = 0; tab < 2; ++tab) {          // 0: rel_w -> width table, 1: rel_h -> height
+                f32x4 gv[2];
 #pragma unroll
-            for (int mt = 0; mt < D / 16; ++mt) dkT[mt] = dvT[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int rt = 0; rt < 2; ++rt) {
+                    const FragT a = bld<FragT>(smem, p.off_tab + 2u * ((tab == 0 ? kTabRows * D : 0) +
+                                                                         (rt * 16 + n) * D + gq * KPL));
+                    gv[rt] = Frag<D>::mma(a, qf, f32x4{0.f, 0.f, 0.f, 0.f});
+                }
+                // scratch row j = table row j, column n = query n
 #pragma unroll
-            for (int pr = 0; pr < NP; ++pr) {
-                unsigned pw[4] = {0u, 0u, 0u, 0u}, lw[4] = {0u, 0u, 0u, 0u};
+                for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int u = 2 * pr + h;
-                    if (u >= NT) continue;
-                    const f32x4 s = Frag<D>::mma(qf[u], kf, cw[u]);
-                    const f32x4 dpv = Frag<D>::mma(gf[u], vf, f32x4{0.f, 0.f, 0.f, 0.f});
-                    const f32x4 c = bld<f32x4>(smem, p.off_rh + 4u * (t * NQ + 16 * u + 4 * gq));
-                    float pv[4], lv[4];
+                    for (int i = 0; i < 4; ++i) bst<float>(smem, scr(rt * 16 + 4 * gq + i), gv[rt][i]);
+                // window position w = 4g+i <- table row w - (yl or xl) + r - 1
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        pv[i] = __builtin_amdgcn_exp2f(fmaf(s[i], alpha, c[i]));
-                        lv[i] = pv[i] * (dpv[i] - Dv[u][i]);
+                for (int i = 0; i < 4; ++i) {
+                    const int w = 4 * gq + i;
+                    const int row = w - (tab == 0 ? xl : yl) + r - 1 + coff;   // in [0, 31) for w < 16
+                    const float gval = bld<float>(smem, scr(row));
+                    const int lo = tab == 0 ? xl : yl;
+                    const bool near = !cmask || (w >= lo && w <= lo + 2 * g.halo);
+                    if (tab == 0) {
+                        const bool in = (zpad ? w < r : (w >= clo && w < chi)) && near;
+                        bst<float>(smem, p.off_rw + 4u * (w * NQ + 16 * u + n), in ? gval : kMaskLogit);
+                    } else {
+                        const bool in = (zpad ? w < r : (w >= tlo && w < thi)) && near;
+                        bst<float>(smem, p.off_rh + 4u * (w * NQ + 16 * u + n),
+                                   in ? alpha * gval - lse2 : -INFINITY);
                     }
-                    pw[2 * h] = pack_bf16x2(pv[0], pv[1]);
-                    pw[2 * h + 1] = pack_bf16x2(pv[2], pv[3]);
-                    lw[2 * h] = pack_bf16x2(lv[0], lv[1]);
-                    lw[2 * h + 1] = pack_bf16x2(lv[2], lv[3]);
-                }
-                const s16x8 pp = __builtin_bit_cast(s16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
-                const s16x8 lp = __builtin_bit_cast(s16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
-#pragma unroll
-                for (int mt = 0; mt < D / 16; ++mt) {
-                    dvT[mt] = mma_k32(__builtin_bit_cast(s16x8, gtA[pr][mt]), pp, dvT[mt]);
-                    dkT[mt] = mma_k32(__builtin_bit_cast(s16x8, qtA[pr][mt]), lp, dkT[mt]);
                 }
             }
-            // this block's share for window row t, column n: [dk(D) | dv(D)] fp32
-            if (n < r) {
-                float* dst = part_kv + ((blk * r + t) * r + n) * (2 * D) + 4 * gq;
+        }
+        __syncthreads();
+
+        // ------------------------------------------------------------ query path
+        if (wave < NT) {
+            const int u = uown;
+            const FragT qf = qown, gf = gown;
+            const float Dn = bld<float>(smem, p.off_d + 4u * (16 * u + n));
+            f32x4 cinit;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cinit[i] = bld<float>(smem, p.off_rw + 4u * ((4 * gq + i) * NQ + 16 * u + n));
+            f32x4 dqT[D / 16], ghT = {0.f, 0.f, 0.f, 0.f}, gwT = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int mt = 0; mt < D / 16; ++mt) dqT[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const unsigned ktl = p.off_kt + 2u * ((unsigned)n * kKtPitch + 4 * gq);
+            // one K=32 step per two window rows; a last odd row goes alone (its
+            // partner's weights and K^T operand are zero)
+            auto step = [&](auto two_c, int t0) {
+                constexpr bool two = decltype(two_c)::value;
+                const int t1 = two ? t0 + 1 : t0;
+                const float c0 = bld<float>(smem, p.off_rh + 4u * (t0 * NQ + 16 * u + n));
+                const f32x4 s0 = Frag<D>::mma(kfrag(t0), qf, cinit);
+                const f32x4 d0 = Frag<D>::mma(vfrag(t0), gf, f32x4{0.f, 0.f, 0.f, 0.f});
+                float l0[4], l1[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) l0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], alpha, c0)) * (d0[i] - Dn);
+                if (two) {
+                    const float c1 = bld<float>(smem, p.off_rh + 4u * (t1 * NQ + 16 * u + n));
+                    const f32x4 s1 = Frag<D>::mma(kfrag(t1), qf, cinit);
+                    const f32x4 d1 = Frag<D>::mma(vfrag(t1), gf, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) l1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], alpha, c1)) * (d1[i] - Dn);
+                }
+                const s16x8 lp = __builtin_bit_cast(s16x8, u32x4{pack_bf16x2(l0[0], l0[1]), pack_bf16x2(l0[2], l0[3]),
+                                                                 pack_bf16x2(l1[0], l1[1]), pack_bf16x2(l1[2], l1[3])});
 #pragma unroll
                 for (int mt = 0; mt < D / 16; ++mt) {
-                    *reinterpret_cast<f32x4*>(dst + 16 * mt) = dkT[mt] * g.scale;
-                    *reinterpret_cast<f32x4*>(dst + D + 16 * mt) = dvT[mt];
+                    const unsigned a = ktl + 2u * (unsigned)(mt * 16 * kKtPitch);
+                    const u32x2 x0 = bld<u32x2>(smem, a + 2u * (unsigned)(t0 * kBCols));
+                    const u32x2 x1 = two ? bld<u32x2>(smem, a + 2u * (unsigned)(t1 * kBCols)) : u32x2{0u, 0u};
+                    dqT[mt] = mma_k32(__builtin_bit_cast(s16x8, u32x4{x0[0], x0[1], x1[0], x1[1]}), lp, dqT[mt]);
+                }
+                const unsigned e0 = n == t0 ? 0x3F803F80u : 0u, e1 = (two && n == t1) ? 0x3F803F80u : 0u;
+                ghT = mma_k32(__builtin_bit_cast(s16x8, u32x4{e0, e0, e1, e1}), lp, ghT);
+                gwT = mma_k32(__builtin_bit_cast(s16x8, ecol), lp, gwT);
+            };
+            int t0 = qtlo;
+            for (; t0 + 1 < qthi; t0 += 2) step(std::true_type{}, t0);
+            if (t0 < qthi) step(std::false_type{}, t0);
+
+            // sums re-indexed by table row (R = w - yl + r - 1 for rows, - xl for
+            // columns), zero elsewhere, in this wave's scratch; then
+            //   dq^T += table^T . sums  and  drel^T += Q^T . sums^T
+            int yl, xl;
+            qpos(16 * u + n, yl, xl);
+#pragma unroll
+            for (int tab = 0; tab < 2; ++tab) {            // 0: rows -> rel_h, 1: columns -> rel_w
+                const f32x4 gs = tab == 0 ? ghT : gwT;
+                const int sh = (tab == 0 ? yl : xl);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) bst<float>(smem, scr(8 * gq + j), 0.f);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int w = 4 * gq + i;
+                    if (w < r) bst<float>(smem, scr(w - sh + r - 1 + coff), gs[i]);
+                }
+                // B operand of table^T . sums: lane (n, g) = query n, table rows 8g..8g+7
+                float sv[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) sv[j] = bld<float>(smem, scr(8 * gq + j));
+                unsigned hw[4], lw[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) split2(sv[2 * j], sv[2 * j + 1], hw[j], lw[j]);
+                const u32x4 bh4 = {hw[0], hw[1], hw[2], hw[3]}, bl4 = {lw[0], lw[1], lw[2], lw[3]};
+                const unsigned tt = p.off_tabt + 2u * ((tab == 0 ? 0 : D * kTabRows) + gq * 8);
+#pragma unroll
+                for (int mt = 0; mt < D / 16; ++mt) {
+                    const s16x8 at = bld<s16x8>(smem, tt + 2u * (unsigned)((mt * 16 + n) * kTabRows));
+                    dqT[mt] = mma_k32(at, __builtin_bit_cast(s16x8, bh4), dqT[mt]);
+                    dqT[mt] = mma_k32(at, __builtin_bit_cast(s16x8, bl4), dqT[mt]);
+                }
+                // table gradient: drel^T[c][R] += sum_q Q^T[c][q] sums[R][q]:
+                // A = Q^T (lane n': channel, queries 4g'..4g'+3 of tile u),
+                // B = sums^T (lane n: table row 16 rt + n, queries 4g..4g+3)
+                wave_lds_sync();   // the scratch column reads above are done before the row reads below
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+                    const f32x4 sr = bld<f32x4>(smem, p.off_scr + wave * (kTabRows * kScrStrideB * 4) +
+                                                          4u * (kScrStrideB * (rt * 16 + n) + 4 * gq));
+                    unsigned h01, l01, h23, l23;
+                    split2(sr[0], sr[1], h01, l01);
+                    split2(sr[2], sr[3], h23, l23);
+                    const s16x4 bhi = __builtin_bit_cast(s16x4, u32x2{h01, h23});
+                    const s16x4 blo = __builtin_bit_cast(s16x4, u32x2{l01, l23});
+#pragma unroll
+                    for (int mt = 0; mt < D / 16; ++mt) {
+                        const s16x4 aq = bld<s16x4>(smem, p.off_qt + 2u * ((mt * 16 + n) * p.qpitch + 16 * u + 4 * gq));
+                        drelT[tab][rt][mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aq, bhi, drelT[tab][rt][mt], 0, 0, 0);
+                        drelT[tab][rt][mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aq, blo, drelT[tab][rt][mt], 0, 0, 0);
+                    }
+                }
+                wave_lds_sync();   // scratch is rewritten by the next table
+            }
+            // dq = scale * dq^T (lane: query n, channels 16mt + 4g + i)
+            __bf16* dp = dq + bh * plane + qpix(yb, 16 * u + n) * D + gq * 4;
+#pragma unroll
+            for (int mt = 0; mt < D / 16; ++mt)
+                *reinterpret_cast<u32x2*>(dp + mt * 16) =
+                    u32x2{pack_bf16x2(dqT[mt][0] * g.scale, dqT[mt][1] * g.scale),
+                          pack_bf16x2(dqT[mt][2] * g.scale, dqT[mt][3] * g.scale)};
+        }
+
+        // -------------------------------------------------------------- key path
+        {
+            constexpr int NP = (NT + 1) / 2;             // pairs of query tiles
+            // width terms (column n, queries 4g..4g+3 of tile u) and D of those
+            // queries, read from LDS per use (register budget)
+            auto cw = [&](int u) { return bld<f32x4>(smem, p.off_rw + 4u * (n * NQ + 16 * u + 4 * gq)); };
+            auto Dv = [&](int u) { return bld<f32x4>(smem, p.off_d + 4u * (16 * u + 4 * gq)); };
+            // A operands over query pairs: lane n' = channel, queries {4g..4g+3 of u0, of u1}
+            u32x4 qtA[NP][D / 16], gtA[NP][D / 16];
+#pragma unroll
+            for (int pr = 0; pr < NP; ++pr)
+#pragma unroll
+                for (int mt = 0; mt < D / 16; ++mt) {
+                    const unsigned rowq = p.off_qt + 2u * ((mt * 16 + n) * p.qpitch + 4 * gq);
+                    const unsigned rowg = p.off_dot + 2u * ((mt * 16 + n) * p.qpitch + 4 * gq);
+                    const u32x2 a0 = bld<u32x2>(smem, rowq + 2u * (32 * pr)), g0 = bld<u32x2>(smem, rowg + 2u * (32 * pr));
+                    u32x2 a1 = {0u, 0u}, g1 = {0u, 0u};
+                    if (2 * pr + 1 < NT) {
+                        a1 = bld<u32x2>(smem, rowq + 2u * (32 * pr + 16));
+                        g1 = bld<u32x2>(smem, rowg + 2u * (32 * pr + 16));
+                    }
+                    qtA[pr][mt] = u32x4{a0[0], a0[1], a1[0], a1[1]};
+                    gtA[pr][mt] = u32x4{g0[0], g0[1], g1[0], g1[1]};
+                }
+#pragma unroll
+            for (int j = 0; j < NSLOT; ++j) {
+                const int t = wave + 4 * j;
+                if (t < tlo || t >= thi) continue;       // wave-uniform
+                const FragT kf = kfrag(t), vf = vfrag(t);
+#pragma unroll
+                for (int pr = 0; pr < NP; ++pr) {
+                    unsigned pw[4] = {0u, 0u, 0u, 0u}, lw[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int u = 2 * pr + h;
+                        if (u >= NT) continue;
+                        const f32x4 s = Frag<D>::mma(qfa[u], kf, cw(u));
+                        const f32x4 dvu = Dv(u);
+                        const f32x4 dpv = Frag<D>::mma(gfa[u], vf, f32x4{0.f, 0.f, 0.f, 0.f});
+                        const f32x4 c = bld<f32x4>(smem, p.off_rh + 4u * (t * NQ + 16 * u + 4 * gq));
+                        float pv[4], lv[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            pv[i] = __builtin_amdgcn_exp2f(fmaf(s[i], alpha, c[i]));
+                            lv[i] = pv[i] * (dpv[i] - dvu[i]);
+                        }
+                        pw[2 * h] = pack_bf16x2(pv[0], pv[1]);
+                        pw[2 * h + 1] = pack_bf16x2(pv[2], pv[3]);
+                        lw[2 * h] = pack_bf16x2(lv[0], lv[1]);
+                        lw[2 * h + 1] = pack_bf16x2(lv[2], lv[3]);
+                    }
+                    const s16x8 pp = __builtin_bit_cast(s16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+                    const s16x8 lp = __builtin_bit_cast(s16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
+#pragma unroll
+                    for (int mt = 0; mt < D / 16; ++mt) {
+                        avT[j][mt] = mma_k32(__builtin_bit_cast(s16x8, gtA[pr][mt]), pp, avT[j][mt]);
+                        akT[j][mt] = mma_k32(__builtin_bit_cast(s16x8, qtA[pr][mt]), lp, akT[j][mt]);
+                    }
                 }
             }
+        }
+
+        // ------------------------- finished key rows out, the others carried
+        // Window row t is in no later window when t < block (the next window
+        // starts block rows lower), or in the last block row.  Such a row is
+        // this column's share of key row wy0 + t: [dk(D) | dv(D)] fp32 per
+        // window column, for the in-image columns.
+        {
+            const bool last = by + 1 == g.nbh;
+#pragma unroll
+            for (int j = 0; j < NSLOT; ++j) {
+                const int t = wave + 4 * j;
+                if ((t < g.block || last) && t >= tlo && t < thi && n >= clo && n < chi) {
+                    float* dst = part_kv + ((wg * g.H + (wy0 + t)) * r + n) * (2 * D) + 4 * gq;
+#pragma unroll
+                    for (int mt = 0; mt < D / 16; ++mt) {
+                        *reinterpret_cast<f32x4*>(dst + 16 * mt) = akT[j][mt] * g.scale;
+                        *reinterpret_cast<f32x4*>(dst + D + 16 * mt) = avT[j][mt];
+                    }
+                }
+            }
+            // row t becomes row t - block of the next window: slot j <- j + block/4
+            const int m = g.block >> 2;
+#pragma unroll
+            for (int j = 0; j < NSLOT; ++j)
+#pragma unroll
+                for (int mt = 0; mt < D / 16; ++mt) {
+                    f32x4 nk = {0.f, 0.f, 0.f, 0.f}, nv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 1; s < NSLOT; ++s)
+                        if (j + s < NSLOT && s == m) {
+                            nk = akT[j + s][mt];
+                            nv = avT[j + s][mt];
+                        }
+                    akT[j][mt] = nk;
+                    avT[j][mt] = nv;
+                }
         }
     }
 
-    // ---------------------------------------- the block's table gradients
+    // ----------------------------------- the walk's table gradients, once
     __syncthreads();                   // every wave is done with the K / V region
     float* red = reinterpret_cast<float*>(smem);   // [wave][tab][32][D]
 #pragma unroll
@@ -535,8 +593,8 @@ void bwd_block_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
     }
 }
 
-// dk, dv of every key: the shares of the windows holding it, summed over
-// the blocks (by, bx) in increasing order; one thread per (key, 4 channels).
+// dk, dv of every key: the shares of the block columns whose windows hold
+// it, summed in increasing column order; one thread per (key, 4 channels).
 template <int D>
 __global__ __launch_bounds__(256)
 void bwd_gather_kernel(const float* __restrict__ part_kv, __bf16* __restrict__ dk, __bf16* __restrict__ dv,
@@ -544,29 +602,24 @@ void bwd_gather_kernel(const float* __restrict__ part_kv, __bf16* __restrict__ d
 {
     constexpr int G4 = D / 4;
     const int64_t total = g.BH * g.H * g.W * G4;
-    const int64_t nblk_img = (int64_t)g.nbh * g.nbw;
+    // block columns whose window [bx*b - h, bx*b + b + h) holds kx lie
+    // within ceil(h/b) columns of kx's own
+    const int A = (g.halo + g.block - 1) / g.block;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
         const int c4 = (int)(i % G4);
         const int64_t pix = i / G4;
-        const int64_t bh = pix / ((int64_t)g.H * g.W);
-        const int rem = (int)(pix - bh * g.H * g.W);
-        const int ky = rem / g.W, kx = rem - ky * g.W;
-        // blocks whose window [by*b - h, by*b + b + h) holds ky lie within
-        // ceil(h/b) block rows of ky's own; likewise for columns
-        const int A = (g.halo + g.block - 1) / g.block;
-        const int by0 = ky / g.block, bx0 = kx / g.block;
+        const int64_t row = pix / g.W;                 // bh * H + ky
+        const int kx = (int)(pix - row * g.W);
+        const int64_t bh = row / g.H;
+        const int ky = (int)(row - bh * g.H);
+        const int bx0 = kx / g.block;
         f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
-        for (int by = max(0, by0 - A); by <= min(g.nbh - 1, by0 + A); ++by) {
-            const int t = ky - (by * g.block - g.halo);
-            if (t < 0 || t >= g.r) continue;
-            for (int bx = max(0, bx0 - A); bx <= min(g.nbw - 1, bx0 + A); ++bx) {
-                const int u = kx - (bx * g.block - g.halo);
-                if (u < 0 || u >= g.r) continue;
-                const int64_t blk = bh * nblk_img + (int64_t)by * g.nbw + bx;
-                const float* src = part_kv + ((blk * g.r + t) * g.r + u) * (2 * D) + 4 * c4;
-                sk += *reinterpret_cast<const f32x4*>(src);
-                sv += *reinterpret_cast<const f32x4*>(src + D);
-            }
+        for (int bx = max(0, bx0 - A); bx <= min(g.nbw - 1, bx0 + A); ++bx) {
+            const int u = kx - (bx * g.block - g.halo);
+            if (u < 0 || u >= g.r) continue;
+            const float* src = part_kv + (((bh * g.nbw + bx) * g.H + ky) * g.r + u) * (2 * D) + 4 * c4;
+            sk += *reinterpret_cast<const f32x4*>(src);
+            sv += *reinterpret_cast<const f32x4*>(src + D);
         }
         const int64_t o = pix * D + 4 * c4;
         *reinterpret_cast<u32x2*>(dk + o) = u32x2{pack_bf16x2(sk[0], sk[1]), pack_bf16x2(sk[2], sk[3])};
@@ -595,7 +648,8 @@ static BwdMfmaPlan bwd_mfma_plan(const Geometry& g)
     p.off_d = brup(p.off_rh + kBRows * p.nq * 4, 16);
     p.off_scr = brup(p.off_d + p.nq * 4, 16);
     p.lds_bytes = p.off_scr + 4 * kTabRows * kScrStrideB * 4;
-    // the final table reduction reuses the front of LDS: 4 waves x 2 x 32 x D floats
+    // the final table reduction reuses the front of LDS (K and V):
+    // 4 waves x 2 x 32 x D floats
     p.lds_bytes = std::max(p.lds_bytes, 4 * 2 * kTabRows * D * 4);
     return p;
 }
@@ -605,22 +659,18 @@ bool bwd_mfma_supported(const Geometry& g, bool bf16)
     if (!bf16 || (g.d != 16 && g.d != 32) || g.r > 16) return false;
     if (g.H % g.block || g.W % g.block) return false;          // full blocks only
     const int side = g.block / g.stride;
-    if (side % 4) return false;
+    if (side % 4) return false;                                // also makes block a multiple of 4
     const int nt = side * side / 16;
     if (nt != 1 && nt != 4) return false;
     if ((int64_t)g.H * g.W >= (int64_t(1) << 31)) return false;
     return true;
 }
 
-// Workspace floats the matrix-core backward needs beyond out / lse:
-// per-block dk/dv shares and table partials (and the table reduction's
-// first level).
-int64_t bwd_mfma_workspace_floats(const Geometry& g, int64_t nchunks)
-{
-    const int64_t nblocks = g.BH * g.nbh * g.nbw;
-    const int64_t e2 = 2 * (int64_t)(2 * g.r - 1) * g.d;
-    return nblocks * g.r * g.r * 2 * g.d + nblocks * e2 + nchunks * e2;
-}
+// Rows of table-gradient partials the matrix-core backward writes (one per workgroup).
+int64_t bwd_mfma_rel_rows(const Geometry& g) { return g.BH * g.nbw; }
+
+// Floats of the per-column dk/dv shares: [BH][nbw][H][r][2d].
+int64_t bwd_mfma_kv_floats(const Geometry& g) { return g.BH * g.nbw * (int64_t)g.H * g.r * 2 * g.d; }
 
 template <int D, int NT>
 static hipError_t bwd_mfma_t(const void* q, const void* k, const void* v, const void* rh, const void* rw,
@@ -628,10 +678,10 @@ static hipError_t bwd_mfma_t(const void* q, const void* k, const void* v, const 
                              float* part_rel, const Geometry& g, hipStream_t st)
 {
     BwdMfmaPlan p = bwd_mfma_plan(g);
-    p.nwg = g.BH * g.nbh * g.nbw;
+    p.nwg = bwd_mfma_rel_rows(g);
     p.remap_xcd = (p.nwg % 8 == 0) ? 1 : 0;
     p.alpha = (float)((double)g.scale * 1.4426950408889634);
-    auto kern = bwd_block_kernel<D, NT>;
+    auto kern = bwd_strip_kernel<D, NT>;
     {
         const hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), p.lds_bytes);
         if (e != hipSuccess) return e;
@@ -643,8 +693,8 @@ static hipError_t bwd_mfma_t(const void* q, const void* k, const void* v, const 
     return hipGetLastError();
 }
 
-// Block kernel + dk/dv gather.  The table partials land in part_rel
-// ([nblocks][2][2r-1][d], scaled), ready for the fixed-order reduction.
+// Strip kernel + dk/dv gather.  The table partials land in part_rel
+// ([BH*nbw][2][2r-1][d], scaled), ready for the fixed-order reduction.
 hipError_t launch_zero_bf16(void* p, int64_t n, hipStream_t st);
 
 hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const void* rh, const void* rw,

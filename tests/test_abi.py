@@ -120,8 +120,8 @@ def test_backward_invalid_arguments_rejected_on_host(lib, kw, status):
 def test_backward_workspace_query():
     from blocked_local_self_amd import bwd_workspace_bytes
     n = bwd_workspace_bytes(32, 8, 64, 64, 16, 8, 3, 1, "bf16")
-    nblocks, r, d = 32 * 8 * 8 * 8, 14, 16
-    assert n >= nblocks * r * r * 2 * d * 4          # per-block dk/dv shares (fp32)
+    strips, H, r, d = 32 * 8 * 8, 64, 14, 16
+    assert n >= strips * H * r * 2 * d * 4           # per-block-column dk/dv shares (fp32)
     assert bwd_workspace_bytes(0, 8, 64, 64, 16, 8, 3, 1, "bf16") == 0
     assert bwd_workspace_bytes(1, 1, 8, 8, 16, 4, 1, 1, "fp32") > 0
     with pytest.raises(HaloError):
