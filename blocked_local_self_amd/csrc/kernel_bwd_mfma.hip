@@ -142,16 +142,16 @@ void bwd_strip_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
         yl = iy * g.stride;
         xl = (qi - iy * SIDE) * g.stride;
     };
-    auto qpix = [&](int yb, int qi) -> int64_t {      // query pixel in the image
-        int yl, xl;
-        qpos(qi, yl, xl);
-        return (int64_t)(yb + yl) * g.W + xb + xl;
-    };
-    auto opix = [&](int yb, int qi) -> int64_t {      // output pixel
-        int yl, xl;
-        qpos(qi, yl, xl);
-        return (int64_t)((yb + yl) / g.stride) * g.Wo + (xb + xl) / g.stride;
-    };
+    // Pixel offsets of query n of tile 0 from the block's first query pixel
+    // (lane_q, input resolution) and output pixel (lane_o); tile u lies
+    // 16/SIDE query rows further (tile_q, tile_o).  Blocks start at multiples
+    // of the stride, so the output pixel of block-local query (iy, ix) is the
+    // block's first output pixel + (iy, ix): no division.
+    const int lane_q = (n / SIDE) * g.stride * g.W + (n % SIDE) * g.stride;
+    const int lane_o = (n / SIDE) * g.Wo + (n % SIDE);
+    const int tile_q = (16 / SIDE) * g.stride * g.W, tile_o = (16 / SIDE) * g.Wo;
+    auto qpix0 = [&](int byy) -> int64_t { return (int64_t)byy * g.block * g.W + xb; };        // block's first query pixel
+    auto opix0 = [&](int byy) -> int64_t { return (int64_t)byy * SIDE * g.Wo + bx * SIDE; };   // its output pixel
 
     // ------------------------------------------- tables, once per workgroup
     // [32][D] (A operands of table . Q^T) and [D][32] (A operands of tables^T . sums)
@@ -177,7 +177,7 @@ void bwd_strip_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
     // own tile.
     struct Pre {
         u32x4 kk[PX], vv[PX];
-        FragT qf[NT], gf[NT], qo, go, oo;
+        FragT qf[NT], gf[NT], oo;
         float lse2;
     };
     const int kv_ch = tid % CPP, kv_t = (tid / CPP) / NGX, kv_cx = (tid / CPP) % NGX;
@@ -199,16 +199,19 @@ void bwd_strip_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
                 }
             }
         }
+        // uniform block bases plus 32-bit lane offsets
+        const __bf16* qb = q + (bh * g.H * g.W + qpix0(byy)) * D;
+        const int64_t ob = bh * oplane + opix0(byy);
+        const __bf16* gb = dout + ob * D;
+        const __bf16* obp = out + ob * D;
 #pragma unroll
         for (int u = 0; u < NT; ++u) {
-            P.qf[u] = *reinterpret_cast<const FragT*>(q + bh * plane + qpix(yb, 16 * u + n) * D + gq * KPL);
-            P.gf[u] = *reinterpret_cast<const FragT*>(dout + (bh * oplane + opix(yb, 16 * u + n)) * D + gq * KPL);
+            P.qf[u] = *reinterpret_cast<const FragT*>(qb + ((unsigned)(lane_q + u * tile_q) * D + gq * KPL));
+            P.gf[u] = *reinterpret_cast<const FragT*>(gb + ((unsigned)(lane_o + u * tile_o) * D + gq * KPL));
         }
-        const int64_t oown = bh * oplane + opix(yb, 16 * uown + n);
-        P.qo = *reinterpret_cast<const FragT*>(q + bh * plane + qpix(yb, 16 * uown + n) * D + gq * KPL);
-        P.go = *reinterpret_cast<const FragT*>(dout + oown * D + gq * KPL);
-        P.oo = *reinterpret_cast<const FragT*>(out + oown * D + gq * KPL);
-        P.lse2 = lse[oown] * 1.4426950408889634f;   // base-2
+        const unsigned oo = (unsigned)(lane_o + uown * tile_o);
+        P.oo = *reinterpret_cast<const FragT*>(obp + (oo * D + gq * KPL));
+        P.lse2 = lse[ob + oo] * 1.4426950408889634f;   // base-2
     };
 
     const unsigned kl = (unsigned)n * PIXB + (D == 16 ? bk_chunk<D>(gq >> 1, n) + (gq & 1) * 8
@@ -293,7 +296,15 @@ void bwd_strip_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
             qfa[u] = P.qf[u];
             gfa[u] = P.gf[u];
         }
-        const FragT qown = P.qo, gown = P.go;
+        // the own tile's fragments, picked with wave-uniform selects (no
+        // run-time array index)
+        FragT qown = P.qf[0], gown = P.gf[0];
+#pragma unroll
+        for (int u = 1; u < NT; ++u)
+            if (uown == u) {
+                qown = P.qf[u];
+                gown = P.gf[u];
+            }
         const float lse2own = P.lse2;
         if (wave < NT) {
             // Q^T and dout^T of the own tile (channel gq*KPL + e, query 16u + n),
@@ -309,7 +320,7 @@ void bwd_strip_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
                              __builtin_bit_cast(float, (unsigned)(unsigned short)P.oo[e] << 16), dpart);
             }
             const float dsum = sum_over_rows(dpart);
-            if (gq == 0) bst<float>(smem, p.off_d + 4u * (16 * uown + n), dsum);
+            if (gq == 0) bst<float>(smem, p.off_d + 4u * (16 * uown + n), -dsum);   // stored negated
         }
 
         // the next block row's inputs, in flight during this one's compute
@@ -322,6 +333,7 @@ void bwd_strip_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
             int yl, xl;
             qpos(16 * u + n, yl, xl);
             const float lse2 = lse2own;
+#pragma unroll
             for (int tab = 0; tab < 2; ++tab) {          // 0: rel_w -> width table, 1: rel_h -> height
                 f32x4 gv[2];
 #pragma unroll
@@ -335,22 +347,22 @@ void bwd_strip_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
                 for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) bst<float>(smem, scr(rt * 16 + 4 * gq + i), gv[rt][i]);
-                // window position w = 4g+i <- table row w - (yl or xl) + r - 1
+                // window position w = 4g+i <- table row w - (yl or xl) + r - 1;
+                // kept when inside [blo, bhi) (the image, or the whole window
+                // under zero padding) and, under the centred mask, within 2h
+                // of the query's own position (bitwise tests: no branches)
+                const int lo = tab == 0 ? xl : yl;
+                const int blo = tab == 0 ? (zpad ? 0 : clo) : qtlo, bhi = tab == 0 ? (zpad ? r : chi) : qthi;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int w = 4 * gq + i;
-                    const int row = w - (tab == 0 ? xl : yl) + r - 1 + coff;   // in [0, 31) for w < 16
+                    const int row = w - lo + r - 1 + coff;   // in [0, 31) for w < 16
                     const float gval = bld<float>(smem, scr(row));
-                    const int lo = tab == 0 ? xl : yl;
-                    const bool near = !cmask || (w >= lo && w <= lo + 2 * g.halo);
-                    if (tab == 0) {
-                        const bool in = (zpad ? w < r : (w >= clo && w < chi)) && near;
-                        bst<float>(smem, p.off_rw + 4u * (w * NQ + 16 * u + n), in ? gval : kMaskLogit);
-                    } else {
-                        const bool in = (zpad ? w < r : (w >= tlo && w < thi)) && near;
-                        bst<float>(smem, p.off_rh + 4u * (w * NQ + 16 * u + n),
-                                   in ? alpha * gval - lse2 : -INFINITY);
-                    }
+                    const int keep = (w >= blo) & (w < bhi) & ((int)!cmask | ((w >= lo) & (w <= lo + 2 * g.halo)));
+                    if (tab == 0)
+                        bst<float>(smem, p.off_rw + 4u * (w * NQ + 16 * u + n), keep ? gval : kMaskLogit);
+                    else
+                        bst<float>(smem, p.off_rh + 4u * (w * NQ + 16 * u + n), keep ? alpha * gval - lse2 : -INFINITY);
                 }
             }
         }
@@ -360,7 +372,8 @@ void bwd_strip_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
         if (wave < NT) {
             const int u = uown;
             const FragT qf = qown, gf = gown;
-            const float Dn = bld<float>(smem, p.off_d + 4u * (16 * u + n));
+            const float mD = bld<float>(smem, p.off_d + 4u * (16 * u + n));   // -D
+            const f32x4 mDn = {mD, mD, mD, mD};         // accumulator start of dP^T: dP - D directly
             f32x4 cinit;
 #pragma unroll
             for (int i = 0; i < 4; ++i) cinit[i] = bld<float>(smem, p.off_rw + 4u * ((4 * gq + i) * NQ + 16 * u + n));
@@ -375,16 +388,16 @@ void bwd_strip_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
                 const int t1 = two ? t0 + 1 : t0;
                 const float c0 = bld<float>(smem, p.off_rh + 4u * (t0 * NQ + 16 * u + n));
                 const f32x4 s0 = Frag<D>::mma(kfrag(t0), qf, cinit);
-                const f32x4 d0 = Frag<D>::mma(vfrag(t0), gf, f32x4{0.f, 0.f, 0.f, 0.f});
+                const f32x4 d0 = Frag<D>::mma(vfrag(t0), gf, mDn);     // dP - D
                 float l0[4], l1[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) l0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], alpha, c0)) * (d0[i] - Dn);
+                for (int i = 0; i < 4; ++i) l0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], alpha, c0)) * d0[i];
                 if (two) {
                     const float c1 = bld<float>(smem, p.off_rh + 4u * (t1 * NQ + 16 * u + n));
                     const f32x4 s1 = Frag<D>::mma(kfrag(t1), qf, cinit);
-                    const f32x4 d1 = Frag<D>::mma(vfrag(t1), gf, f32x4{0.f, 0.f, 0.f, 0.f});
+                    const f32x4 d1 = Frag<D>::mma(vfrag(t1), gf, mDn);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) l1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], alpha, c1)) * (d1[i] - Dn);
+                    for (int i = 0; i < 4; ++i) l1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], alpha, c1)) * d1[i];
                 }
                 const s16x8 lp = __builtin_bit_cast(s16x8, u32x4{pack_bf16x2(l0[0], l0[1]), pack_bf16x2(l0[2], l0[3]),
                                                                  pack_bf16x2(l1[0], l1[1]), pack_bf16x2(l1[2], l1[3])});
@@ -457,7 +470,7 @@ void bwd_strip_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
                 wave_lds_sync();   // scratch is rewritten by the next table
             }
             // dq = scale * dq^T (lane: query n, channels 16mt + 4g + i)
-            __bf16* dp = dq + bh * plane + qpix(yb, 16 * u + n) * D + gq * 4;
+            __bf16* dp = dq + (bh * g.H * g.W + qpix0(by)) * D + ((unsigned)(lane_q + u * tile_q) * D + gq * 4);
 #pragma unroll
             for (int mt = 0; mt < D / 16; ++mt)
                 *reinterpret_cast<u32x2*>(dp + mt * 16) =
@@ -471,7 +484,7 @@ void bwd_strip_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
             // width terms (column n, queries 4g..4g+3 of tile u) and D of those
             // queries, read from LDS per use (register budget)
             auto cw = [&](int u) { return bld<f32x4>(smem, p.off_rw + 4u * (n * NQ + 16 * u + 4 * gq)); };
-            auto Dv = [&](int u) { return bld<f32x4>(smem, p.off_d + 4u * (16 * u + 4 * gq)); };
+            auto mDv = [&](int u) { return bld<f32x4>(smem, p.off_d + 4u * (16 * u + 4 * gq)); };   // -D
             // A operands over query pairs: lane n' = channel, queries {4g..4g+3 of u0, of u1}
             u32x4 qtA[NP][D / 16], gtA[NP][D / 16];
 #pragma unroll
@@ -489,10 +502,12 @@ void bwd_strip_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
                     qtA[pr][mt] = u32x4{a0[0], a0[1], a1[0], a1[1]};
                     gtA[pr][mt] = u32x4{g0[0], g0[1], g1[0], g1[1]};
                 }
+            // every slot is computed: rows past the window or, without zero
+            // padding, off the image have a height term of -inf (weights 0);
+            // rows that are neither finished nor carried are never written
 #pragma unroll
             for (int j = 0; j < NSLOT; ++j) {
                 const int t = wave + 4 * j;
-                if (t < tlo || t >= thi) continue;       // wave-uniform
                 const FragT kf = kfrag(t), vf = vfrag(t);
 #pragma unroll
                 for (int pr = 0; pr < NP; ++pr) {
@@ -502,14 +517,13 @@ void bwd_strip_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
                         const int u = 2 * pr + h;
                         if (u >= NT) continue;
                         const f32x4 s = Frag<D>::mma(qfa[u], kf, cw(u));
-                        const f32x4 dvu = Dv(u);
-                        const f32x4 dpv = Frag<D>::mma(gfa[u], vf, f32x4{0.f, 0.f, 0.f, 0.f});
+                        const f32x4 dpv = Frag<D>::mma(gfa[u], vf, mDv(u));   // dP - D
                         const f32x4 c = bld<f32x4>(smem, p.off_rh + 4u * (t * NQ + 16 * u + 4 * gq));
                         float pv[4], lv[4];
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             pv[i] = __builtin_amdgcn_exp2f(fmaf(s[i], alpha, c[i]));
-                            lv[i] = pv[i] * (dpv[i] - dvu[i]);
+                            lv[i] = pv[i] * dpv[i];
                         }
                         pw[2 * h] = pack_bf16x2(pv[0], pv[1]);
                         pw[2 * h + 1] = pack_bf16x2(pv[2], pv[3]);
@@ -548,6 +562,16 @@ void bwd_strip_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
             }
             // row t becomes row t - block of the next window: slot j <- j + block/4
             const int m = g.block >> 2;
+            if (m == 2) {                  // block 8: plain moves
+#pragma unroll
+                for (int mt = 0; mt < D / 16; ++mt) {
+                    akT[0][mt] = akT[2][mt];
+                    avT[0][mt] = avT[2][mt];
+                    akT[1][mt] = akT[3][mt];
+                    avT[1][mt] = avT[3][mt];
+                    akT[2][mt] = avT[2][mt] = akT[3][mt] = avT[3][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            } else
 #pragma unroll
             for (int j = 0; j < NSLOT; ++j)
 #pragma unroll
@@ -662,7 +686,7 @@ bool bwd_mfma_supported(const Geometry& g, bool bf16)
     if (side % 4) return false;                                // also makes block a multiple of 4
     const int nt = side * side / 16;
     if (nt != 1 && nt != 4) return false;
-    if ((int64_t)g.H * g.W >= (int64_t(1) << 31)) return false;
+    if ((int64_t)g.H * g.W * g.d >= (int64_t(1) << 31)) return false;   // 32-bit lane offsets
     return true;
 }
 
