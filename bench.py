@@ -64,14 +64,14 @@ MEASURED_TRAFFIC = {
         "global_bf16_16x16_d16_b16h0": {"bytes_per_launch": 17137550, "read": 12943246, "write": 4194304,
             "sources": "fef9af93e1c3c5e3"},
     },
-    # backward: summed over the call's kernels (block kernel, dk/dv gather, table reduction)
+    # backward: summed over the call's kernels (strip kernel, dk/dv gather, table reduction)
     "bwd": {
-        "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 1147083147, "read": 598946827, "write": 548136320,
-            "sources": "c921ba62421b8c2a"},
-        "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 1082528532, "read": 556408852, "write": 526119680,
-            "sources": "c921ba62421b8c2a"},
-        "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 1085221069, "read": 528696141, "write": 556524928,
-            "sources": "c921ba62421b8c2a"},
+        "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 738464990, "read": 403999838, "write": 334465152,
+            "sources": "a7dee07ddb8e074d"},
+        "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 719827550, "read": 394830174, "write": 324997376,
+            "sources": "a7dee07ddb8e074d"},
+        "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 670355761, "read": 331696305, "write": 338659456,
+            "sources": "a7dee07ddb8e074d"},
     },
 }
 
