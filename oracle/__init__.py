@@ -192,3 +192,87 @@ def set_attention(q, keys, bias, vals, scale: float) -> np.ndarray:
     _load().halo_ref_set_attention(d, n, _ptr(q), kp, _ptr(bias), vp, float(scale),
                                    _ptr(out), _ptr(scratch))
     return out
+
+
+# ---------------------------------------------------------------- the layer
+# The attention layer around the op: the HaloAttention module on the pswp.cn
+# blog page (section 4) projects every pixel with to_q and to_kv (linear maps
+# without bias; to_kv's output is k then v), splits the heads, runs the
+# blocked attention, merges the heads (head-major: channel h*d + c) and
+# applies to_out (a linear map with bias).  Activations stay in one of two
+# pixel-major layouts:
+#   "nhwc":    [B, H, W, C]
+#   "blocked": [B, H/b, W/b, b*b, C], pixel (i*b + p1, j*b + p2) at
+#              [., i, j, p1*b + p2, .]: the persistent blocking of appendix D
+#              of "Scaling Local Self-Attention for Parameter Efficient Visual
+#              Backbones" (blocks flattened row-major, as in the module's
+#              rearrange into (p1 p2)).
+LAYOUTS = ("nhwc", "blocked")
+
+
+def to_nhwc(x, layout: str, side: int) -> np.ndarray:
+    """Layer activations in `layout` (block side `side`) -> [B, H, W, C]."""
+    x = np.asarray(x)
+    if layout == "nhwc":
+        return x
+    if layout != "blocked":
+        raise ValueError(f"unknown layout {layout!r}")
+    B, nby, nbx, bb, C = x.shape
+    if bb != side * side:
+        raise ValueError(f"blocked layout needs {side * side} pixels per block, got {bb}")
+    return x.reshape(B, nby, nbx, side, side, C).transpose(0, 1, 3, 2, 4, 5).reshape(B, nby * side, nbx * side, C)
+
+
+def from_nhwc(x, layout: str, side: int) -> np.ndarray:
+    """[B, H, W, C] -> layer activations in `layout` (block side `side`)."""
+    x = np.asarray(x)
+    if layout == "nhwc":
+        return x
+    if layout != "blocked":
+        raise ValueError(f"unknown layout {layout!r}")
+    B, H, W, C = x.shape
+    if H % side or W % side:
+        raise ValueError("the blocked layout needs H and W divisible by the block side")
+    return x.reshape(B, H // side, side, W // side, side, C).transpose(0, 1, 3, 2, 4, 5).reshape(
+        B, H // side, W // side, side * side, C)
+
+
+def halo_proj_in_ref(x, w_q, w_kv, heads: int, layout: str = "nhwc", block: int = 1):
+    """to_q and to_kv of every pixel, fp64: x (layer layout, C channels),
+    w_q [inner, C], w_kv [2*inner, C] -> q, k, v [B, heads, H, W, inner/heads]."""
+    xn = _f64(to_nhwc(x, layout, block))
+    w_q, w_kv = _f64(w_q), _f64(w_kv)
+    B, H, W, C = xn.shape
+    inner = w_q.shape[0]
+    if w_q.shape != (inner, C) or w_kv.shape != (2 * inner, C) or inner % heads:
+        raise ValueError(f"weights {w_q.shape} {w_kv.shape} do not fit C={C}, heads={heads}")
+    d = inner // heads
+
+    def split(t):   # [B, H, W, inner] -> [B, heads, H, W, d]
+        return np.ascontiguousarray(t.reshape(B, H, W, heads, d).transpose(0, 3, 1, 2, 4))
+
+    kv = xn @ w_kv.T
+    return split(xn @ w_q.T), split(kv[..., :inner]), split(kv[..., inner:])
+
+
+def halo_proj_out_ref(attn, w_o, b_o, layout: str = "nhwc", block: int = 1):
+    """Head merge and to_out, fp64: attn [B, heads, Ho, Wo, d], w_o [C, heads*d],
+    b_o [C] -> y in the layer layout (block side `block` for "blocked")."""
+    attn, w_o, b_o = _f64(attn), _f64(w_o), _f64(b_o)
+    B, heads, Ho, Wo, d = attn.shape
+    merged = attn.transpose(0, 2, 3, 1, 4).reshape(B, Ho, Wo, heads * d)
+    if w_o.shape[1] != heads * d or b_o.shape != (w_o.shape[0],):
+        raise ValueError(f"to_out weight {w_o.shape} / bias {b_o.shape} do not fit {heads}x{d} channels")
+    return from_nhwc(merged @ w_o.T + b_o, layout, block)
+
+
+def halo_layer_ref(x, w_q, w_kv, w_o, b_o, rel_h, rel_w, block: int, halo: int, heads: int,
+                   query_stride: int = 1, scale: float | None = None, layout: str = "nhwc",
+                   threads: int = 0, flags: int = 0) -> np.ndarray:
+    """The whole layer, fp64: to_q / to_kv, blocked attention, head merge,
+    to_out.  x: [B, H, W, C] ("nhwc") or [B, H/b, W/b, b*b, C] ("blocked");
+    returns y in the same layout at the output resolution (blocks of side
+    block/query_stride)."""
+    q, k, v = halo_proj_in_ref(x, w_q, w_kv, heads, layout, block)
+    attn = halo_attn_ref(q, k, v, rel_h, rel_w, block, halo, query_stride, scale, threads, flags=flags)
+    return halo_proj_out_ref(attn, w_o, b_o, layout, block // query_stride)

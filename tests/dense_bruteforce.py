@@ -121,3 +121,60 @@ def halo_lse_dense(q, k, rel_h, rel_w, block, halo, stride=1, scale=None):
             lse = m[:, 0] + np.log(np.exp(logits - m).sum(axis=1))
             out[n, hd] = lse.reshape(H // stride, W // stride)
     return out
+
+
+def halo_layer_module_torch(x, w_q, w_kv, w_o, b_o, rel_h, rel_w, block, halo, heads, scale=None):
+    """The HaloAttention layer computed the way the module on the pswp.cn page
+    (section 4) orders its steps, in torch float64 on the CPU:
+      x [N, C, H, W] is cut into blocks of b*b query pixels; the key/value
+      inputs are the (b+2h)^2 windows extracted by a zero-padded unfold; both
+      go through the projections (so k, v are projected per window position,
+      padded positions included, instead of once per pixel); heads are split;
+      logits = (scale q) . k + relative terms; padded window positions are
+      masked; softmax; weighted sum of v; heads merged; to_out with its bias;
+      blocks put back into [N, C, H, W].
+    The relative term of block-local query (y, x) and window position (ty, tx)
+    is q . rel_h[ty - y + r - 1] + q . rel_w[tx - x + r - 1] with ty, tx
+    counted from the window corner (the same row as (key - query) + r-1+h).
+    Stride 1 only, as in the module."""
+    import torch
+    import torch.nn.functional as F
+    t = lambda a: torch.as_tensor(np.asarray(a, dtype=np.float64))
+    x, w_q, w_kv, w_o, b_o, rel_h, rel_w = (t(a) for a in (x, w_q, w_kv, w_o, b_o, rel_h, rel_w))
+    N, C, H, W = x.shape
+    b, r = block, block + 2 * halo
+    nby, nbx = H // b, W // b
+    inner = w_q.shape[0]
+    d = inner // heads
+    if scale is None:
+        scale = d ** -0.5
+    # queries: [N*nby*nbx, b*b, C], block-local pixel p1*b + p2
+    q_in = x.reshape(N, C, nby, b, nbx, b).permute(0, 2, 4, 3, 5, 1).reshape(N * nby * nbx, b * b, C)
+    # key/value inputs: the zero-padded windows, [N*nblocks, r*r, C]
+    win = F.unfold(x, kernel_size=r, stride=b, padding=halo)             # [N, C*r*r, nblocks]
+    kv_in = win.reshape(N, C, r * r, nby * nbx).permute(0, 3, 2, 1).reshape(N * nby * nbx, r * r, C)
+    inside = F.unfold(torch.ones(1, 1, H, W, dtype=torch.float64), kernel_size=r, stride=b, padding=halo)
+    inside = inside.reshape(r * r, nby * nbx).T.repeat(N, 1)             # [N*nblocks, r*r], 1 = in the image
+    q = q_in @ w_q.T
+    kv = kv_in @ w_kv.T
+    k, v = kv[..., :inner], kv[..., inner:]
+    heads_first = lambda a: a.reshape(a.shape[0], a.shape[1], heads, d).permute(0, 2, 1, 3)
+    q, k, v = heads_first(q) * scale, heads_first(k), heads_first(v)      # [nb, heads, n, d]
+    qy = torch.arange(b).repeat_interleave(b)                            # query rows / columns in the block
+    qx = torch.arange(b).repeat(b)
+    ty = torch.arange(r).repeat_interleave(r)                            # window rows / columns
+    tx = torch.arange(r).repeat(r)
+    rows_h = ty[None, :] - qy[:, None] + r - 1                           # [b*b, r*r]
+    rows_w = tx[None, :] - qx[:, None] + r - 1
+    lh = q @ rel_h.T                                                     # [nb, heads, b*b, 2r-1]
+    lw = q @ rel_w.T
+    rel = (torch.gather(lh, 3, rows_h.expand(lh.shape[0], heads, -1, -1)) +
+           torch.gather(lw, 3, rows_w.expand(lw.shape[0], heads, -1, -1)))
+    sim = q @ k.transpose(-1, -2) + rel
+    sim = sim.masked_fill(inside[:, None, None, :] == 0, float("-inf"))
+    out = torch.softmax(sim, dim=-1) @ v                                 # [nb, heads, b*b, d]
+    out = out.permute(0, 2, 1, 3).reshape(out.shape[0], b * b, inner)
+    y = out @ w_o.T + b_o                                                # [nb, b*b, C_out]
+    Co = y.shape[-1]
+    y = y.reshape(N, nby, nbx, b, b, Co).permute(0, 5, 1, 3, 2, 4).reshape(N, Co, H, W)
+    return y.numpy()
