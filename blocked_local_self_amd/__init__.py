@@ -13,18 +13,24 @@ scale * (q.k + q.rel_h[dy + c0] + q.rel_w[dx + c0]), c0 = block+3*halo-1,
 then the weighted sum of v; queries at multiples of ``query_stride``.
 ``halo_attn_bwd`` is its exact gradient (recomputing every softmax), and
 ``halo_attention`` joins the two as a differentiable torch function.
+``halo_layer_fwd`` is the whole attention layer of that module (to_q, to_kv,
+the attention, to_out) on activations kept in a pixel-major, channels-last
+layout (image order or the paper's persistent blocks, appendix D), with the
+head split / merge and the (un)blocking done inside the projection kernels.
 """
 from __future__ import annotations
 
 from . import _native
 
 __all__ = ["halo_attn_fwd", "halo_attn_bwd", "bwd_workspace_bytes", "halo_attention",
-           "select_kernel", "HaloError", "KERNELS", "VARIANTS"]
+           "halo_layer_proj_in", "halo_layer_proj_out", "halo_layer_fwd", "layer_workspace_bytes",
+           "select_kernel", "HaloError", "KERNELS", "VARIANTS", "LAYOUTS"]
 
 HaloError = _native.HaloError
 # semantic variants (flags of halo_attn_fwd_ex; see include/halo_attn.h)
 VARIANTS = {"centred_offset": _native.HALO_CENTRED_OFFSET, "zero_pad": _native.HALO_ZERO_PAD,
             "centred_mask": _native.HALO_CENTRED_MASK, "half_split": _native.HALO_HALF_SPLIT}
+LAYOUTS = {"nhwc": _native.HALO_LAYOUT_NHWC, "blocked": _native.HALO_LAYOUT_BLOCKED}
 KERNELS = {"auto": _native.HALO_KERNEL_AUTO, "generic": _native.HALO_KERNEL_GENERIC,
            "mfma": _native.HALO_KERNEL_MFMA, "mfma_strip": _native.HALO_KERNEL_MFMA_STRIP}
 
@@ -245,3 +251,141 @@ def halo_attention(q, k, v, rel_h, rel_w, block: int, halo: int, query_stride: i
     if scale is None:
         scale = float(q.shape[-1]) ** -0.5
     return _FUNCTION.apply(q, k, v, rel_h, rel_w, block, halo, query_stride, scale, tuple(variants))
+
+
+# ---------------------------------------------------------------- the layer
+
+def _check_device_tensors(ref, **tensors):
+    import torch
+    for name, t in tensors.items():
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device.type != "cuda" or t.device != ref.device:
+            raise ValueError(f"{name} must live on {ref.device} (got {t.device})")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dtype != ref.dtype:
+            raise ValueError(f"{name} must have dtype {ref.dtype} (got {t.dtype})")
+
+
+def _layer_pixels(x, layout: str, block: int):
+    """(B, H, W, C) of activations x in `layout` (block side `block`)."""
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
+    if layout == "nhwc":
+        if x.dim() != 4:
+            raise ValueError(f"nhwc activations are [B, H, W, C]; got {tuple(x.shape)}")
+        return tuple(x.shape)
+    if x.dim() != 5 or x.shape[3] != block * block:
+        raise ValueError(f"blocked activations are [B, H/b, W/b, b*b, C] with b={block}; got {tuple(x.shape)}")
+    B, nby, nbx, _, C = x.shape
+    return B, nby * block, nbx * block, C
+
+
+def _layer_shape(B, H, W, C, layout, block):
+    if layout == "nhwc":
+        return (B, H, W, C)
+    return (B, H // block, W // block, block * block, C)
+
+
+def halo_layer_proj_in(x, w_q, w_kv, heads: int, block: int = 1, layout: str = "nhwc", stream=None):
+    """to_q and to_kv of every pixel: x in `layout` ([B, H, W, C], or
+    [B, H/b, W/b, b*b, C] with b = ``block``), w_q [inner, C], w_kv
+    [2*inner, C] -> q, k, v [B, heads, H, W, inner/heads]."""
+    import torch
+    _check_device_tensors(x, x=x, w_q=w_q, w_kv=w_kv)
+    B, H, W, C = _layer_pixels(x, layout, block)
+    inner = w_q.shape[0]
+    if w_q.dim() != 2 or tuple(w_q.shape) != (inner, C) or tuple(w_kv.shape) != (2 * inner, C) or inner % heads:
+        raise ValueError(f"w_q {tuple(w_q.shape)} / w_kv {tuple(w_kv.shape)} do not fit C={C}, heads={heads}")
+    d = inner // heads
+    q, k, v = (torch.empty((B, heads, H, W, d), dtype=x.dtype, device=x.device) for _ in range(3))
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    with torch.cuda.device(x.device):
+        st = _native.load().halo_attn_layer_proj_in(x.data_ptr(), w_q.data_ptr(), w_kv.data_ptr(), q.data_ptr(),
+                                                    k.data_ptr(), v.data_ptr(), B, H, W, C, heads, d, block,
+                                                    LAYOUTS[layout], _dtype_code(x), stream.cuda_stream)
+    _native.check(st)
+    return q, k, v
+
+
+def halo_layer_proj_out(attn, w_o, b_o, block_out: int = 1, layout: str = "nhwc", stream=None):
+    """Head merge and to_out: attn [B, heads, Ho, Wo, d], w_o [C_out, heads*d],
+    b_o [C_out] -> y in `layout` (blocks of side ``block_out``)."""
+    import torch
+    _check_device_tensors(attn, attn=attn, w_o=w_o, b_o=b_o)
+    if attn.dim() != 5:
+        raise ValueError(f"attn must be [B, heads, Ho, Wo, d]; got {tuple(attn.shape)}")
+    B, heads, Ho, Wo, d = attn.shape
+    Co = w_o.shape[0]
+    if w_o.dim() != 2 or w_o.shape[1] != heads * d or tuple(b_o.shape) != (Co,):
+        raise ValueError(f"w_o {tuple(w_o.shape)} / b_o {tuple(b_o.shape)} do not fit {heads}x{d} channels")
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
+    y = torch.empty(_layer_shape(B, Ho, Wo, Co, layout, block_out), dtype=attn.dtype, device=attn.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(attn.device)
+    with torch.cuda.device(attn.device):
+        st = _native.load().halo_attn_layer_proj_out(attn.data_ptr(), w_o.data_ptr(), b_o.data_ptr(), y.data_ptr(),
+                                                     B, Ho, Wo, Co, heads, d, block_out, LAYOUTS[layout],
+                                                     _dtype_code(attn), stream.cuda_stream)
+    _native.check(st)
+    return y
+
+
+def layer_workspace_bytes(B: int, H: int, W: int, heads: int, d: int, query_stride: int = 1,
+                          dtype: str = "bf16") -> int:
+    """Workspace bytes ``halo_layer_fwd`` needs (host-only query)."""
+    code = {"fp32": _native.HALO_F32, "bf16": _native.HALO_BF16}[dtype]
+    n = _native.load().halo_attn_layer_workspace_bytes(B, H, W, heads, d, query_stride, code)
+    if n < 0:
+        _native.check(int(n))
+    return int(n)
+
+
+def halo_layer_fwd(x, w_q, w_kv, w_o, b_o, rel_h, rel_w, block: int, halo: int, heads: int,
+                   query_stride: int = 1, scale: float | None = None, layout: str = "nhwc",
+                   workspace=None, out=None, stream=None):
+    """The attention layer: to_q / to_kv, halo attention, head merge, to_out.
+
+    x: [B, H, W, C] ("nhwc") or [B, H/b, W/b, b*b, C] ("blocked", b = block);
+    w_q [inner, C], w_kv [2*inner, C], w_o [C_out, inner], b_o [C_out];
+    rel_h, rel_w [2*(block+2*halo)-1, inner/heads]; all one dtype on one GPU.
+    Returns y in the same layout at the output resolution (H/s x W/s pixels,
+    blocks of side block/s).  ``workspace``: an optional uint8 device tensor
+    of at least ``layer_workspace_bytes`` bytes (allocated if None).
+    """
+    import torch
+    _check_device_tensors(x, x=x, w_q=w_q, w_kv=w_kv, w_o=w_o, b_o=b_o, rel_h=rel_h, rel_w=rel_w)
+    B, H, W, C = _layer_pixels(x, layout, block)
+    inner = w_q.shape[0]
+    if tuple(w_q.shape) != (inner, C) or tuple(w_kv.shape) != (2 * inner, C) or inner % heads:
+        raise ValueError(f"w_q {tuple(w_q.shape)} / w_kv {tuple(w_kv.shape)} do not fit C={C}, heads={heads}")
+    d = inner // heads
+    Co = w_o.shape[0]
+    if w_o.dim() != 2 or w_o.shape[1] != inner or tuple(b_o.shape) != (Co,):
+        raise ValueError(f"w_o {tuple(w_o.shape)} / b_o {tuple(b_o.shape)} do not fit inner={inner}")
+    s = query_stride
+    if s < 1 or block % s or H % s or W % s:
+        raise ValueError(f"query_stride={s} must divide block, H and W")
+    if scale is None:
+        scale = float(d) ** -0.5
+    oshape = _layer_shape(B, H // s, W // s, Co, layout, block // s)
+    if out is None:
+        out = torch.empty(oshape, dtype=x.dtype, device=x.device)
+    elif tuple(out.shape) != oshape or out.dtype != x.dtype or out.device != x.device or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous {oshape} {x.dtype} tensor on {x.device}")
+    need = layer_workspace_bytes(B, H, W, heads, d, s, "bf16" if x.dtype == torch.bfloat16 else "fp32")
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    with torch.cuda.device(x.device):
+        st = _native.load().halo_attn_layer_fwd(
+            x.data_ptr(), w_q.data_ptr(), w_kv.data_ptr(), w_o.data_ptr(), b_o.data_ptr(), rel_h.data_ptr(),
+            rel_w.data_ptr(), out.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            B, H, W, C, Co, heads, d, block, halo, s, float(scale), LAYOUTS[layout], _dtype_code(x),
+            stream.cuda_stream)
+    _native.check(st)
+    return out

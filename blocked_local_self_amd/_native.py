@@ -16,6 +16,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "halo_attn.h")
 HALO_F32, HALO_BF16 = 0, 1
 HALO_KERNEL_AUTO, HALO_KERNEL_GENERIC, HALO_KERNEL_MFMA, HALO_KERNEL_MFMA_STRIP = 0, 1, 2, 3
 HALO_CENTRED_OFFSET, HALO_ZERO_PAD, HALO_CENTRED_MASK, HALO_HALF_SPLIT = 1, 2, 4, 8
+HALO_LAYOUT_NHWC, HALO_LAYOUT_BLOCKED = 0, 1
 STATUS = {0: "HALO_OK", -1: "HALO_ERR_NULL", -2: "HALO_ERR_SHAPE", -3: "HALO_ERR_DTYPE",
           -4: "HALO_ERR_UNSUPPORTED", -5: "HALO_ERR_HIP", -6: "HALO_ERR_ALIAS",
           -7: "HALO_ERR_WORKSPACE"}
@@ -56,6 +57,14 @@ def load() -> ctypes.CDLL:
     lib.halo_attn_bwd.restype = i
     lib.halo_attn_bwd_workspace_bytes.argtypes = [i] * 9
     lib.halo_attn_bwd_workspace_bytes.restype = ctypes.c_longlong
+    lib.halo_attn_layer_proj_in.argtypes = [vp] * 6 + [i] * 9 + [vp]
+    lib.halo_attn_layer_proj_in.restype = i
+    lib.halo_attn_layer_proj_out.argtypes = [vp] * 4 + [i] * 9 + [vp]
+    lib.halo_attn_layer_proj_out.restype = i
+    lib.halo_attn_layer_workspace_bytes.argtypes = [i] * 7
+    lib.halo_attn_layer_workspace_bytes.restype = ctypes.c_longlong
+    lib.halo_attn_layer_fwd.argtypes = [vp] * 9 + [sz] + [i] * 10 + [f, i, i, vp]
+    lib.halo_attn_layer_fwd.restype = i
     lib.halo_attn_select_kernel.argtypes = [i] * 5
     lib.halo_attn_select_kernel.restype = i
     lib.halo_attn_last_error.argtypes = []

@@ -13,6 +13,7 @@
 
 #include "../../include/halo_attn.h"
 #include "halo_common.h"
+#include "proj.h"
 
 namespace halo {
 
@@ -432,6 +433,182 @@ int halo_attn_bwd(const void* q, const void* k, const void* v,
     return halo_attn_bwd_kernel(q, k, v, rel_h, rel_w, out, dout, lse, dq, dk, dv, drel_h, drel_w, workspace,
                                 workspace_bytes, B, heads, H, W, d, block, halo, query_stride, scale,
                                 dtype, HALO_KERNEL_AUTO, stream);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ the layer
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Checks of the layer's sizes; fills L (input and output grids).  empty: a
+// size is zero, nothing to compute.
+int check_layer(int B, int H, int W, int C, int Cout, int heads, int d, int side, int stride, int layout,
+                int dtype, halo::LayerGeom& L, bool& empty)
+{
+    if (dtype != HALO_F32 && dtype != HALO_BF16)
+        return fail(HALO_ERR_DTYPE, "dtype %d is neither HALO_F32 (0) nor HALO_BF16 (1)", dtype);
+    if (layout != HALO_LAYOUT_NHWC && layout != HALO_LAYOUT_BLOCKED)
+        return fail(HALO_ERR_SHAPE, "layout=%d is not a halo_layout value", layout);
+    if (B < 0 || H < 0 || W < 0 || C < 0 || Cout < 0 || heads < 0 || d < 0)
+        return fail(HALO_ERR_SHAPE, "negative size: B=%d H=%d W=%d C=%d C_out=%d heads=%d d=%d",
+                    B, H, W, C, Cout, heads, d);
+    if (C > 65536 || Cout > 65536 || (int64_t)heads * d > 4096)
+        return fail(HALO_ERR_SHAPE, "channels out of range: C=%d C_out=%d heads*d=%lld (limits 65536, 4096)",
+                    C, Cout, (long long)heads * d);
+    if (stride < 1 || H % stride || W % stride)
+        return fail(HALO_ERR_SHAPE, "query_stride=%d must be >= 1 and divide H=%d, W=%d", stride, H, W);
+    L = halo::LayerGeom{};
+    L.B = B; L.H = H; L.W = W; L.Ho = H / stride; L.Wo = W / stride;
+    L.C = C; L.Cout = Cout; L.heads = heads; L.d = d; L.layout = layout;
+    L.side = side; L.side_out = side;
+    empty = B == 0 || H == 0 || W == 0 || C == 0 || Cout == 0 || heads == 0 || d == 0;
+    if (layout == HALO_LAYOUT_BLOCKED) {
+        if (side < 1) return fail(HALO_ERR_SHAPE, "the blocked layout needs block >= 1 (got %d)", side);
+        if (H % side || W % side)
+            return fail(HALO_ERR_SHAPE, "the blocked layout needs block=%d to divide H=%d and W=%d", side, H, W);
+    }
+    const double big = (double)B * H * W * std::max(std::max(C, Cout), heads * d);
+    if (big >= 1e15) return fail(HALO_ERR_SHAPE, "tensor too large (%.3g elements)", big);
+    L.NP = (int64_t)B * H * W;
+    L.NPo = (int64_t)B * L.Ho * L.Wo;
+    return HALO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int halo_attn_layer_proj_in(const void* x, const void* w_q, const void* w_kv, void* q, void* k, void* v,
+                            int B, int H, int W, int C, int heads, int d, int block, int layout, int dtype,
+                            void* stream)
+{
+    g_err[0] = 0;
+    halo::LayerGeom L;
+    bool empty = false;
+    int st = check_layer(B, H, W, C, C, heads, d, layout == HALO_LAYOUT_BLOCKED ? block : 1, 1, layout, dtype, L,
+                         empty);
+    if (st) return st;
+    if (empty) return HALO_OK;
+    if (!x || !w_q || !w_kv || !q || !k || !v) return fail(HALO_ERR_NULL, "null pointer among x, w_q, w_kv, q, k, v");
+    const size_t esz = dtype == HALO_BF16 ? 2 : 4;
+    const size_t inner = (size_t)heads * d;
+    const size_t xb = (size_t)L.NP * C * esz, wqb = inner * C * esz, wkvb = 2 * inner * C * esz;
+    const size_t ob = (size_t)L.NP * inner * esz;
+    const void* outs[3] = {q, k, v};
+    for (int i = 0; i < 3; ++i) {
+        if (overlaps(outs[i], ob, x, xb) || overlaps(outs[i], ob, w_q, wqb) || overlaps(outs[i], ob, w_kv, wkvb))
+            return fail(HALO_ERR_ALIAS, "q, k or v overlaps an input");
+        for (int j = 0; j < i; ++j)
+            if (overlaps(outs[i], ob, outs[j], ob)) return fail(HALO_ERR_ALIAS, "q, k and v overlap each other");
+    }
+    const bool bf16 = dtype == HALO_BF16;
+    const bool mfma = halo::proj_in_mfma_supported(L, bf16) && aligned16(x) && aligned16(w_q) && aligned16(w_kv) &&
+                      aligned16(q) && aligned16(k) && aligned16(v);
+    const hipError_t e = halo::launch_proj_in(x, w_q, w_kv, q, k, v, L, bf16, mfma, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(HALO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return HALO_OK;
+}
+
+int halo_attn_layer_proj_out(const void* attn, const void* w_o, const void* b_o, void* y,
+                             int B, int Ho, int Wo, int C_out, int heads, int d, int block_out, int layout, int dtype,
+                             void* stream)
+{
+    g_err[0] = 0;
+    halo::LayerGeom L;
+    bool empty = false;
+    // the output grid is the layer geometry at stride 1 (Ho x Wo pixels)
+    int st = check_layer(B, Ho, Wo, C_out, C_out, heads, d, layout == HALO_LAYOUT_BLOCKED ? block_out : 1, 1, layout,
+                         dtype, L, empty);
+    if (st) return st;
+    if (empty) return HALO_OK;
+    if (!attn || !w_o || !b_o || !y) return fail(HALO_ERR_NULL, "null pointer among attn, w_o, b_o, y");
+    const size_t esz = dtype == HALO_BF16 ? 2 : 4;
+    const size_t inner = (size_t)heads * d;
+    const size_t ab = (size_t)L.NPo * inner * esz, wb = (size_t)C_out * inner * esz, bb = (size_t)C_out * esz;
+    const size_t yb = (size_t)L.NPo * C_out * esz;
+    if (overlaps(y, yb, attn, ab) || overlaps(y, yb, w_o, wb) || overlaps(y, yb, b_o, bb))
+        return fail(HALO_ERR_ALIAS, "y overlaps an input");
+    const bool bf16 = dtype == HALO_BF16;
+    const bool mfma = halo::proj_out_mfma_supported(L, bf16) && aligned16(attn) && aligned16(w_o) &&
+                      aligned16(b_o) && aligned16(y);
+    const hipError_t e = halo::launch_proj_out(attn, w_o, b_o, y, L, bf16, mfma, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(HALO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return HALO_OK;
+}
+
+long long halo_attn_layer_workspace_bytes(int B, int H, int W, int heads, int d, int query_stride, int dtype)
+{
+    g_err[0] = 0;
+    halo::LayerGeom L;
+    bool empty = false;
+    int st = check_layer(B, H, W, 1, 1, heads, d, 1, query_stride, HALO_LAYOUT_NHWC, dtype, L, empty);
+    if (st) return st;
+    if (empty) return 0;
+    const size_t esz = dtype == HALO_BF16 ? 2 : 4;
+    const size_t qkv = align256((size_t)L.NP * heads * d * esz);
+    return (long long)(3 * qkv + align256((size_t)L.NPo * heads * d * esz));
+}
+
+int halo_attn_layer_fwd(const void* x, const void* w_q, const void* w_kv, const void* w_o, const void* b_o,
+                        const void* rel_h, const void* rel_w, void* y, void* workspace, size_t workspace_bytes,
+                        int B, int H, int W, int C, int C_out, int heads, int d, int block, int halo,
+                        int query_stride, float scale, int layout, int dtype, void* stream)
+{
+    g_err[0] = 0;
+    halo::LayerGeom L;
+    bool empty = false;
+    if (block < 1) return fail(HALO_ERR_SHAPE, "block=%d must be >= 1", block);
+    if (query_stride < 1 || block % query_stride)
+        return fail(HALO_ERR_SHAPE, "query_stride=%d must be >= 1 and divide block=%d", query_stride, block);
+    int st = check_layer(B, H, W, C, C_out, heads, d, block, query_stride, layout, dtype, L, empty);
+    if (st) return st;
+    L.side_out = block / query_stride;
+    {   // the attention's own checks, before any launch
+        halo::Geometry g;
+        bool e2 = false;
+        st = check_sizes(B, heads, H, W, d, block, halo, query_stride, scale, dtype, g, e2);
+        if (st) return st;
+    }
+    if (empty) return HALO_OK;
+    if (!x || !w_q || !w_kv || !w_o || !b_o || !rel_h || !rel_w || !y)
+        return fail(HALO_ERR_NULL, "null pointer among x, w_q, w_kv, w_o, b_o, rel_h, rel_w, y");
+    if (!workspace) return fail(HALO_ERR_NULL, "null workspace");
+    const size_t esz = dtype == HALO_BF16 ? 2 : 4;
+    const size_t inner = (size_t)heads * d;
+    const size_t qkv = align256((size_t)L.NP * inner * esz), ab = align256((size_t)L.NPo * inner * esz);
+    const size_t need = 3 * qkv + ab;
+    if (workspace_bytes < need || ((uintptr_t)workspace & 255u))
+        return fail(HALO_ERR_WORKSPACE, "workspace of %zu bytes at %p: need %zu bytes, 256-byte aligned",
+                    workspace_bytes, workspace, need);
+    const int r = block + 2 * halo;
+    const size_t xb = (size_t)L.NP * C * esz, yb = (size_t)L.NPo * C_out * esz;
+    const size_t wqb = inner * C * esz, wkvb = 2 * inner * C * esz, wob = (size_t)C_out * inner * esz,
+                 bb = (size_t)C_out * esz, tb = (size_t)(2 * r - 1) * d * esz;
+    const void* ins[7] = {x, w_q, w_kv, w_o, b_o, rel_h, rel_w};
+    const size_t insz[7] = {xb, wqb, wkvb, wob, bb, tb, tb};
+    for (int i = 0; i < 7; ++i) {
+        if (overlaps(y, yb, ins[i], insz[i])) return fail(HALO_ERR_ALIAS, "y overlaps an input");
+        if (overlaps(workspace, need, ins[i], insz[i])) return fail(HALO_ERR_ALIAS, "workspace overlaps an input");
+    }
+    if (overlaps(workspace, need, y, yb)) return fail(HALO_ERR_ALIAS, "workspace overlaps y");
+
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    void *q = ws, *k = ws + qkv, *v = ws + 2 * qkv, *attn = ws + 3 * qkv;
+    const bool bf16 = dtype == HALO_BF16;
+    hipStream_t s = (hipStream_t)stream;
+    const bool mi = halo::proj_in_mfma_supported(L, bf16) && aligned16(x) && aligned16(w_q) && aligned16(w_kv);
+    hipError_t e = halo::launch_proj_in(x, w_q, w_kv, q, k, v, L, bf16, mi, s);
+    if (e != hipSuccess) return fail(HALO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    st = halo_attn_fwd_ex(q, k, v, rel_h, rel_w, attn, nullptr, B, heads, H, W, d, block, halo, query_stride, scale,
+                          dtype, 0, HALO_KERNEL_AUTO, stream);
+    if (st) return st;
+    const bool mo = halo::proj_out_mfma_supported(L, bf16) && aligned16(w_o) && aligned16(b_o) && aligned16(y);
+    e = halo::launch_proj_out(attn, w_o, b_o, y, L, bf16, mo, s);
+    if (e != hipSuccess) return fail(HALO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return HALO_OK;
 }
 
 }  // extern "C"

@@ -58,3 +58,32 @@ def make_grad_output(B: int, heads: int, Ho: int, Wo: int, d: int, dtype: str = 
     g.manual_seed(int(seed) + 0x5EED)
     t = torch.randn((B, heads, Ho, Wo, d), dtype=torch.float32, generator=g)
     return t.to(dtype=torch_dtype(dtype)).to(device).contiguous()
+
+
+def make_layer_inputs(B: int, H: int, W: int, C: int, heads: int, d: int, block: int, halo: int,
+                      C_out: int | None = None, dtype: str = "bf16", seed: int = 0,
+                      device: str | torch.device = "cpu"):
+    """Inputs of the attention layer: (x, w_q, w_kv, w_o, b_o, rel_h, rel_w).
+
+    One seeded CPU generator; drawn in that order as N(0, 1) float32: x
+    [B, H, W, C] (pixel-major, channels last), w_q [inner, C] and w_kv
+    [2*inner, C] times C**-0.5, w_o [C_out, inner] times inner**-0.5, b_o
+    [C_out] times 0.1, rel_h and rel_w [2r-1, d] times d**-0.5 (inner =
+    heads*d, r = block + 2*halo; C_out defaults to C, as in the module); then
+    each is rounded to ``dtype``.  The weight scales keep the projections'
+    outputs near unit variance.
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed) + 0x1A7E)
+    inner = heads * d
+    Co = C if C_out is None else C_out
+    r = block + 2 * halo
+    x = torch.randn((B, H, W, C), dtype=torch.float32, generator=g)
+    w_q = torch.randn((inner, C), dtype=torch.float32, generator=g) * C ** -0.5
+    w_kv = torch.randn((2 * inner, C), dtype=torch.float32, generator=g) * C ** -0.5
+    w_o = torch.randn((Co, inner), dtype=torch.float32, generator=g) * inner ** -0.5
+    b_o = torch.randn((Co,), dtype=torch.float32, generator=g) * 0.1
+    rel_h = torch.randn((2 * r - 1, d), dtype=torch.float32, generator=g) * d ** -0.5
+    rel_w = torch.randn((2 * r - 1, d), dtype=torch.float32, generator=g) * d ** -0.5
+    dt = torch_dtype(dtype)
+    return tuple(t.to(dtype=dt).to(device).contiguous() for t in (x, w_q, w_kv, w_o, b_o, rel_h, rel_w))

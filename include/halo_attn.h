@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define HALO_ATTN_ABI_VERSION 2
+#define HALO_ATTN_ABI_VERSION 3
 
 typedef enum halo_dtype {
     HALO_F32 = 0,
@@ -201,8 +201,9 @@ int halo_attn_fwd(const void* q, const void* k, const void* v,
  * matrix-core backward: bf16, d in {16, 32}, window side r <= 16, block
  * dividing H and W, and (block/query_stride)^2 in {16, 64}; other arguments
  * return HALO_ERR_UNSUPPORTED.  AUTO takes MFMA when it applies.  The
- * matrix-core path keeps, per block, its window's share of dk and dv in the
- * workspace and sums the shares of every key in a fixed order.
+ * matrix-core path keeps, per block column and key row, that column's share
+ * of dk and dv in the workspace and sums the shares of every key in a fixed
+ * order.
  */
 int halo_attn_bwd_kernel(const void* q, const void* k, const void* v,
                          const void* rel_h, const void* rel_w,
@@ -240,6 +241,74 @@ int halo_attn_bwd(const void* q, const void* k, const void* v,
  * (0 when a size is zero), or a negative status for invalid arguments. */
 long long halo_attn_bwd_workspace_bytes(int B, int heads, int H, int W, int d,
                                         int block, int halo, int query_stride, int dtype);
+
+/*
+ * The attention layer around the op: the HaloAttention module on the pswp.cn
+ * blog page (section 4).  With inner = heads * d:
+ *   q = x W_q^T, [k | v] = x W_kv^T   (to_q, to_kv: no bias; k is the first
+ *                                      inner outputs of to_kv, v the rest)
+ *   heads split off the channel axis: channel h*d + c is channel c of head h
+ *   attn = the blocked attention above (scale, tables, block, halo, stride)
+ *   y = merge_heads(attn) W_o^T + b_o (to_out), merged head-major as split.
+ * Activations (x, y) stay in a persistent pixel-major layout with channels
+ * last (appendix D of the paper keeps the network's activations blocked and
+ * avoids formatting operations):
+ *   HALO_LAYOUT_NHWC:    [B][H][W][C]
+ *   HALO_LAYOUT_BLOCKED: [B][H/s][W/s][s*s][C] with s the block side: pixel
+ *                        (i*s + p1, j*s + p2) at [.][i][j][p1*s + p2][.]
+ *                        (the blocks flattened row-major).
+ * The projections read and write the attention's [B][heads][H][W][d]
+ * tensors directly; the head split / merge and the (un)blocking are index
+ * arithmetic inside the projection kernels.
+ * Weights use the linear-layer layout [out][in]: w_q [inner][C], w_kv
+ * [2*inner][C], w_o [C_out][inner], b_o [C_out]; all tensors share `dtype`;
+ * accumulation is fp32.  Pointers are device pointers owned by the caller;
+ * outputs must not overlap inputs (else HALO_ERR_ALIAS).
+ */
+typedef enum halo_layout {
+    HALO_LAYOUT_NHWC = 0,
+    HALO_LAYOUT_BLOCKED = 1
+} halo_layout;
+
+/* to_q and to_kv of every pixel of x (layout `layout`, block side `block`
+ * for HALO_LAYOUT_BLOCKED) into q, k, v [B][heads][H][W][d].
+ * Preconditions: B, H, W, C, heads, d >= 0 (a zero makes the call a no-op);
+ * heads*d <= 4096, C <= 65536; for the blocked layout block >= 1 divides H
+ * and W.  bf16 with C % 32 == 0, C <= 512, d % 4 == 0 and heads*d % 16 == 0
+ * (16-byte aligned pointers) runs on matrix cores, anything else on a plain
+ * fp32-accumulating kernel. */
+int halo_attn_layer_proj_in(const void* x, const void* w_q, const void* w_kv,
+                            void* q, void* k, void* v,
+                            int B, int H, int W, int C, int heads, int d,
+                            int block, int layout, int dtype, void* stream);
+
+/* Head merge and to_out: attn [B][heads][Ho][Wo][d] -> y [.][C_out] in
+ * `layout` (block side `block_out` for HALO_LAYOUT_BLOCKED, which must divide
+ * Ho and Wo).  bf16 with heads*d % 32 == 0, heads*d <= 512, d % 8 == 0 and
+ * C_out % 16 == 0 (16-byte aligned pointers) runs on matrix cores. */
+int halo_attn_layer_proj_out(const void* attn, const void* w_o, const void* b_o, void* y,
+                             int B, int Ho, int Wo, int C_out, int heads, int d,
+                             int block_out, int layout, int dtype, void* stream);
+
+/* Host-only query: workspace bytes halo_attn_layer_fwd needs (q, k, v and
+ * the attention output), 0 when a size is zero, or a negative status. */
+long long halo_attn_layer_workspace_bytes(int B, int H, int W, int heads, int d,
+                                          int query_stride, int dtype);
+
+/* The whole layer: proj_in, the attention (halo_attn_fwd, kernel AUTO) and
+ * proj_out, on `stream`, with q, k, v and the attention output in the
+ * caller's workspace (at least halo_attn_layer_workspace_bytes(), 256-byte
+ * aligned; contents undefined on return).  x has B x H x W pixels of C
+ * channels, y has B x H/s x W/s pixels of C_out channels (s = query_stride;
+ * blocks of side block/s in the blocked layout).  Errors as for the parts,
+ * plus HALO_ERR_WORKSPACE. */
+int halo_attn_layer_fwd(const void* x, const void* w_q, const void* w_kv,
+                        const void* w_o, const void* b_o,
+                        const void* rel_h, const void* rel_w, void* y,
+                        void* workspace, size_t workspace_bytes,
+                        int B, int H, int W, int C, int C_out, int heads, int d,
+                        int block, int halo, int query_stride, float scale,
+                        int layout, int dtype, void* stream);
 
 /* Host-only query: the halo_kernel value AUTO would run for these
  * arguments (HALO_KERNEL_GENERIC or HALO_KERNEL_MFMA), or a negative

@@ -126,3 +126,51 @@ def test_backward_workspace_query():
     assert bwd_workspace_bytes(1, 1, 8, 8, 16, 4, 1, 1, "fp32") > 0
     with pytest.raises(HaloError):
         bwd_workspace_bytes(1, 1, 8, 8, 16, 4, 1, 3, "bf16")
+
+
+# ------------------------------------------------------------------ the layer
+
+def layer_call(lib, *, x=1, wq=2, wkv=3, wo=4, bo=5, rh=6, rw=7, y=8, ws=9, ws_bytes=1 << 40, B=1, H=8, W=8,
+               C=32, Co=32, heads=2, d=16, block=4, halo=1, stride=1, scale=0.25, layout=0, dtype=1):
+    # fake pointers 2^36 apart: every call below must fail before any launch
+    ptr = lambda v: ctypes.c_void_p(v << 36 if v else None)
+    return lib.halo_attn_layer_fwd(ptr(x), ptr(wq), ptr(wkv), ptr(wo), ptr(bo), ptr(rh), ptr(rw), ptr(y), ptr(ws),
+                                   ws_bytes, B, H, W, C, Co, heads, d, block, halo, stride, scale, layout, dtype,
+                                   None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=0), -1), (dict(bo=0), -1), (dict(y=0), -1), (dict(ws=0), -1),
+    (dict(dtype=4), -3), (dict(layout=2), -2), (dict(C=-1), -2), (dict(heads=300, d=16), -2),
+    (dict(stride=3), -2), (dict(stride=2, block=5), -2), (dict(layout=1, block=3), -2),
+    (dict(d=0, heads=2, block=0), -2), (dict(scale=float("nan")), -2), (dict(d=200), -2),
+    (dict(ws_bytes=1024), -7),
+    (dict(y=1), -6), (dict(ws=8), -6),                     # y / workspace overlap
+])
+def test_layer_invalid_arguments_rejected_on_host(lib, kw, status):
+    assert layer_call(lib, **kw) == status, _native.last_error()
+    assert _native.last_error() != ""
+
+
+def test_layer_parts_reject_on_host(lib):
+    p = lambda v: ctypes.c_void_p(v << 36 if v else None)
+    # proj_in: q overlaps x; unknown layout; blocked layout not dividing H
+    assert lib.halo_attn_layer_proj_in(p(1), p(2), p(3), p(1), p(5), p(6), 1, 8, 8, 32, 2, 16, 4, 0, 1, None) == -6
+    assert lib.halo_attn_layer_proj_in(p(1), p(2), p(3), p(4), p(5), p(6), 1, 8, 8, 32, 2, 16, 4, 3, 1, None) == -2
+    assert lib.halo_attn_layer_proj_in(p(1), p(2), p(3), p(4), p(5), p(6), 1, 9, 8, 32, 2, 16, 4, 1, 1, None) == -2
+    assert lib.halo_attn_layer_proj_in(p(1), p(0), p(3), p(4), p(5), p(6), 1, 8, 8, 32, 2, 16, 4, 0, 1, None) == -1
+    # proj_out: y overlaps w_o; bad dtype
+    assert lib.halo_attn_layer_proj_out(p(1), p(2), p(3), p(2), 1, 8, 8, 32, 2, 16, 4, 0, 1, None) == -6
+    assert lib.halo_attn_layer_proj_out(p(1), p(2), p(3), p(4), 1, 8, 8, 32, 2, 16, 4, 0, 9, None) == -3
+    # zero sizes are no-ops even with null pointers
+    assert lib.halo_attn_layer_proj_in(p(0), p(0), p(0), p(0), p(0), p(0), 0, 8, 8, 32, 2, 16, 4, 0, 1, None) == 0
+
+
+def test_layer_workspace_query():
+    from blocked_local_self_amd import layer_workspace_bytes
+    n = layer_workspace_bytes(32, 64, 64, 8, 16)
+    assert n == 4 * 32 * 8 * 64 * 64 * 16 * 2          # q, k, v and the attention output, bf16
+    assert layer_workspace_bytes(32, 64, 64, 8, 16, 2) == 3 * 32 * 8 * 64 * 64 * 16 * 2 + 32 * 8 * 32 * 32 * 16 * 2
+    assert layer_workspace_bytes(0, 64, 64, 8, 16) == 0
+    with pytest.raises(HaloError):
+        layer_workspace_bytes(1, 8, 8, 2, 16, 3)
