@@ -25,6 +25,16 @@ dl.q, p.dout; algorithmic bytes = e*d*B*heads*(2*(H/s)*(W/s) + 5*H*W): q and
 dout once at query pixels, k and v once, dq, dk, dv written once (out and
 lse, 1/d of that, not counted).  The roofline entry covers the whole
 backward call (its kernels' mean time per call over the timed region).
+
+Layer (--pass layer): one step = one halo_attn_layer_fwd call: to_q / to_kv
+of every pixel, the attention, head merge and to_out, on activations kept in
+a pixel-major channels-last layout (--layout nhwc or blocked), with C = C_out
+= heads*d channels.  F = attention flops + 2*pixels*C*3*inner (to_q, to_kv) +
+2*out_pixels*inner*C_out (to_out); algorithmic bytes = x read once and y
+written once (the intermediates q, k, v and the attention output are not
+counted: a layer that never leaves the chip needs none of them).  The
+roofline entry covers the whole call; ``parts_us`` times each of its three
+kernels on its own.
 """
 from __future__ import annotations
 
@@ -39,6 +49,7 @@ sys.path.insert(0, HERE)
 
 METRIC = "halo-attn fwd TFLOP/s + tokens/s per MI355X; % of MFMA/HBM roofline"
 METRIC_BWD = "halo-attn bwd TFLOP/s + tokens/s per MI355X; % of MFMA/HBM roofline"
+METRIC_LAYER = "halo-attn layer fwd (projections + attention) TFLOP/s + tokens/s per MI355X; % of MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}   # MI355X dense matrix peaks, published
 MALL_BYTES = 256 * 2 ** 20     # Infinity Cache
@@ -64,6 +75,8 @@ MEASURED_TRAFFIC = {
         "global_bf16_16x16_d16_b16h0": {"bytes_per_launch": 17137550, "read": 12943246, "write": 4194304,
             "sources": "fef9af93e1c3c5e3"},
     },
+    # layer: summed over the call's kernels (to_q/to_kv, attention, to_out)
+    "layer": {},
     # backward: summed over the call's kernels (strip kernel, dk/dv gather, table reduction)
     "bwd": {
         "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 738464990, "read": 403999838, "write": 334465152,
@@ -80,6 +93,7 @@ MEASURED_TRAFFIC = {
 # a pass holds while these files are unchanged).
 KERNEL_SOURCES = {
     "fwd": ["halo_common.h", "mfma_util.h", "kernel_ring.hip", "kernel_mfma.hip"],
+    "layer": ["halo_common.h", "mfma_util.h", "kernel_ring.hip", "kernel_mfma.hip", "proj.h", "kernel_proj.hip"],
     "bwd": ["halo_common.h", "mfma_util.h", "kernel_bwd_mfma.hip", "kernel_bwd_generic.hip"],
 }
 
@@ -102,8 +116,10 @@ def parse():
                     help="untimed launches first (the GPU clocks need ~0.1 s of load to ramp up)")
     ap.add_argument("--workload", default=None, help="workload name (default: the early-stage shape)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "generic", "mfma"])
-    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
-                    help="forward (the headline) or backward pass")
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd", "layer"],
+                    help="forward (the headline), backward pass, or the whole layer with its projections")
+    ap.add_argument("--layout", default="nhwc", choices=["nhwc", "blocked"],
+                    help="activation layout of --pass layer")
     ap.add_argument("--variants", default="", help="comma-separated semantic variants of the forward "
                     "(centred_offset, zero_pad, centred_mask, half_split); default: none")
     ap.add_argument("--sets", type=int, default=0, help="rotated input sets (0: enough to exceed the MALL)")
@@ -180,6 +196,146 @@ def cpu_baseline(wl, inputs_cpu, target_s, dout_cpu=None):
             "seconds": round(t, 3), "tokens_per_s": round(tokens / t, 1)}
 
 
+def layer_flops(wl, C, Co):
+    inner = wl.heads * wl.d
+    return wl.flops + 2 * wl.B * wl.H * wl.W * C * 3 * inner + 2 * wl.B * wl.Ho * wl.Wo * inner * Co
+
+
+def layer_alg_bytes(wl, C, Co):
+    return wl.elem_bytes * (wl.B * wl.H * wl.W * C + wl.B * wl.Ho * wl.Wo * Co)
+
+
+def cpu_baseline_layer(wl, xs, target_s):
+    """Time the fp64 oracle layer on whole images of the workload."""
+    import oracle
+    f64 = lambda t: t.to(dtype=__import__("torch").float64).numpy()
+    x, w_q, w_kv, w_o, b_o, rh, rw = (f64(t) for t in xs)
+    C = x.shape[-1]
+    Co = w_o.shape[0]
+    threads = oracle.max_threads()
+    per_image = layer_flops(wl, C, Co) / wl.B
+    n, t, images = 1, 0.0, 0
+    while t < target_s and images < 64 * wl.B:
+        sl = x[(images % wl.B):(images % wl.B) + n]
+        t0 = time.perf_counter()
+        oracle.halo_layer_ref(sl, w_q, w_kv, w_o, b_o, rh, rw, wl.block, wl.halo, wl.heads, wl.stride,
+                              threads=threads)
+        t += time.perf_counter() - t0
+        images += sl.shape[0]
+        n = min(wl.B, 2 * n)
+    return {"value": round(per_image * images / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{images} images of {wl.name} (layer: projections + attention, C={C}), fp64, {t:.2f} s",
+            "seconds": round(t, 3), "tokens_per_s": round(wl.tokens / wl.B * images / t, 1)}
+
+
+def run_layer(args):
+    import torch
+    from blocked_local_self_amd import (halo_layer_fwd, halo_layer_proj_in, halo_layer_proj_out, halo_attn_fwd,
+                                        layer_workspace_bytes, workloads, _native, LAYOUTS)
+    from blocked_local_self_amd.inputs import make_layer_inputs, nhwc_to_layout
+
+    wl = workloads.get(args.workload or workloads.BENCH_WORKLOAD)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    C = Co = wl.heads * wl.d
+    inner = wl.heads * wl.d
+    lay = args.layout
+    side, side_o = wl.block, wl.block // wl.stride
+    e = wl.elem_bytes
+    per_set = e * (wl.B * wl.H * wl.W * C + wl.B * wl.Ho * wl.Wo * Co)
+    nsets = args.sets or max(2, -(-2 * MALL_BYTES // per_set))
+    sets = []
+    xs0 = None
+    for s_ in range(nsets):
+        xs = make_layer_inputs(wl.B, wl.H, wl.W, C, wl.heads, wl.d, wl.block, wl.halo, dtype=wl.dtype, seed=s_)
+        if s_ == 0:
+            xs0 = xs
+        dt = [nhwc_to_layout(xs[0], lay, side).to(dev)] + [t.to(dev) for t in xs[1:]]
+        ys = (wl.B, wl.Ho, wl.Wo, Co) if lay == "nhwc" else (wl.B, wl.Ho // side_o, wl.Wo // side_o, side_o ** 2, Co)
+        sets.append((dt, torch.empty(ys, dtype=dt[0].dtype, device=dev)))
+    nws = layer_workspace_bytes(wl.B, wl.H, wl.W, wl.heads, wl.d, wl.stride, wl.dtype)
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    lib = _native.load()
+    dcode = _native.HALO_BF16 if wl.dtype == "bf16" else _native.HALO_F32
+    scale = float(wl.d) ** -0.5
+    calls = []
+    for (x, w_q, w_kv, w_o, b_o, rh, rw), y in sets:
+        halo_layer_fwd(x, w_q, w_kv, w_o, b_o, rh, rw, wl.block, wl.halo, wl.heads, wl.stride, layout=lay,
+                       workspace=ws, out=y, stream=stream)
+        calls.append((x.data_ptr(), w_q.data_ptr(), w_kv.data_ptr(), w_o.data_ptr(), b_o.data_ptr(), rh.data_ptr(),
+                      rw.data_ptr(), y.data_ptr(), ws.data_ptr(), ws.numel(), wl.B, wl.H, wl.W, C, Co, wl.heads,
+                      wl.d, wl.block, wl.halo, wl.stride, scale, LAYOUTS[lay], dcode, stream.cuda_stream))
+
+    def timed(fn, steps, warmup):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for i in range(steps):
+            fn(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / steps, time.perf_counter() - t0
+
+    def step(i):
+        st = lib.halo_attn_layer_fwd(*calls[i % nsets])
+        if st:
+            _native.check(st)
+
+    ms, wall = timed(step, args.steps, args.warmup)
+    # the three kernels on their own (same shapes and layout)
+    (x, w_q, w_kv, w_o, b_o, rh, rw), y = sets[0]
+    q, k, v = halo_layer_proj_in(x, w_q, w_kv, wl.heads, side, lay, stream=stream)
+    attn = halo_attn_fwd(q, k, v, rh, rw, wl.block, wl.halo, wl.stride, stream=stream)
+    parts = {}
+    nsteps = max(10, args.steps // 4)
+    parts["proj_in"] = timed(lambda i: halo_layer_proj_in(sets[i % nsets][0][0], w_q, w_kv, wl.heads, side, lay,
+                                                          stream=stream), nsteps, 20)[0]
+    parts["attention"] = timed(lambda i: halo_attn_fwd(q, k, v, rh, rw, wl.block, wl.halo, wl.stride, out=attn,
+                                                       stream=stream), nsteps, 20)[0]
+    parts["proj_out"] = timed(lambda i: halo_layer_proj_out(attn, w_o, b_o, side_o, lay, stream=stream),
+                              nsteps, 20)[0]
+
+    flops = layer_flops(wl, C, Co)
+    alg_bytes = layer_alg_bytes(wl, C, Co)
+    tflops = flops / (ms * 1e-3) / 1e12
+    achieved_gbs = alg_bytes / (ms * 1e-3) / 1e9
+    mfma_peak = MFMA_PEAK_TFLOPS[wl.dtype]
+    mfma_bound = flops / (mfma_peak * 1e12) > alg_bytes / (HBM_PEAK_GBS * 1e9)
+    src_hash = kernel_source_hash("layer")
+    rec = MEASURED_TRAFFIC["layer"].get(f"{wl.name}/{lay}")
+    traffic = rec["bytes_per_launch"] if rec and rec["sources"] == src_hash else None
+    line = {
+        "metric": METRIC_LAYER, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {**wl.describe(), "pass": "layer", "layout": lay, "C": C, "C_out": Co,
+                   "rotated_input_sets": nsets},
+        "tokens_per_s": round(wl.tokens / (ms * 1e-3), 1),
+        "wall_s_timed_region": round(wall, 4),
+        "roofline": {
+            "bound": "mfma" if mfma_bound else "hbm",
+            "achieved": round(tflops, 2) if mfma_bound else round(achieved_gbs, 1),
+            "peak": mfma_peak if mfma_bound else HBM_PEAK_GBS,
+            "unit": "TFLOP/s" if mfma_bound else "GB/s",
+            "frac": round(tflops / mfma_peak if mfma_bound else achieved_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "alg_bytes_per_launch": alg_bytes,
+            "flops_per_launch": flops,
+            "mean_launch_us": round(ms * 1e3, 3),
+            "kernel_sources": src_hash,
+        },
+        "parts_us": {k_: round(v_ * 1e3, 2) for k_, v_ in parts.items()},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_layer(wl, xs0, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -188,6 +344,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, args.steps)
+        return
+    if args.which == "layer":
+        run_layer(args)
         return
     import torch
     from blocked_local_self_amd import halo_attn_fwd, halo_attn_bwd, bwd_workspace_bytes, workloads

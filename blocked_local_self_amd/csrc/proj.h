@@ -5,6 +5,22 @@
 
 namespace halo {
 
+// Division by a run-time constant d >= 1 for dividends below 2^31, by
+// multiplication (Granlund and Montgomery, "Division by invariant integers
+// using multiplication", 1994): with l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1, n / d = (mulhi(n, m) + n) >> l.
+struct FastDiv {
+    uint32_t d, m, l;
+    FastDiv() = default;
+    explicit FastDiv(uint32_t dv) : d(dv)
+    {
+        l = 0;
+        while ((1ull << l) < dv) ++l;
+        m = (uint32_t)((((1ull << l) - dv) << 32) / dv + 1);
+    }
+    __device__ __forceinline__ uint32_t div(uint32_t n) const { return (__umulhi(n, m) + n) >> l; }
+};
+
 struct LayerGeom {
     int64_t NP, NPo;      // pixels in / out: B*H*W, B*Ho*Wo
     int B, H, W, Ho, Wo;
@@ -12,7 +28,13 @@ struct LayerGeom {
     int heads, d;         // attention heads and channels per head
     int side, side_out;   // block side of the blocked layout, in / out (block, block/stride)
     int layout;           // 0 NHWC, 1 blocked
+    // dividers for the pixel and channel index arithmetic of the
+    // matrix-core kernels (pixel counts below 2^31)
+    FastDiv fW, fH, fWo, fHo, fbb, fside, fnbx, fnby, fbbo, fsideo, fnbxo, fnbyo, finner, fd;
 };
+
+// Fills the dividers of L's sizes (the launchers call it).
+void layer_fastdiv(LayerGeom& L);
 
 struct ProjPlan {
     int ns;               // weight rows (output channels) per workgroup

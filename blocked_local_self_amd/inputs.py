@@ -87,3 +87,16 @@ def make_layer_inputs(B: int, H: int, W: int, C: int, heads: int, d: int, block:
     rel_w = torch.randn((2 * r - 1, d), dtype=torch.float32, generator=g) * d ** -0.5
     dt = torch_dtype(dtype)
     return tuple(t.to(dtype=dt).to(device).contiguous() for t in (x, w_q, w_kv, w_o, b_o, rel_h, rel_w))
+
+
+def nhwc_to_layout(x: torch.Tensor, layout: str, side: int) -> torch.Tensor:
+    """Seeded [B, H, W, C] activations rearranged into the layer's `layout`:
+    "nhwc" (unchanged) or "blocked" ([B, H/s, W/s, s*s, C], blocks flattened
+    row-major).  Data arrangement only."""
+    if layout == "nhwc":
+        return x
+    if layout != "blocked":
+        raise ValueError(f"unknown layout {layout!r}")
+    B, H, W, C = x.shape
+    return x.reshape(B, H // side, side, W // side, side, C).permute(0, 1, 3, 2, 4, 5).reshape(
+        B, H // side, W // side, side * side, C).contiguous()

@@ -50,3 +50,13 @@ def test_fp32_workload_inputs():
     w = workloads.get("tiny_fp32_16x16_d16_b4h1")
     q, k, v, rh, rw = make_workload_inputs(w)
     assert q.dtype == torch.float32 and q.shape == w.shape() and rh.shape == (11, 16)
+
+
+def test_layer_input_layout_matches_oracle_layout():
+    import numpy as np
+    import torch
+    import oracle
+    from blocked_local_self_amd.inputs import make_layer_inputs, nhwc_to_layout
+    x = make_layer_inputs(2, 8, 12, 8, 2, 4, 4, 1, dtype="fp32", seed=1)[0]
+    for lay in ("nhwc", "blocked"):
+        np.testing.assert_array_equal(nhwc_to_layout(x, lay, 4).numpy(), oracle.from_nhwc(x.numpy(), lay, 4))
