@@ -76,7 +76,10 @@ MEASURED_TRAFFIC = {
             "sources": "fef9af93e1c3c5e3"},
     },
     # layer: summed over the call's kernels (to_q/to_kv, attention, to_out)
-    "layer": {},
+    "layer": {
+        "early_stage_bf16_64x64_d16_b8h3/nhwc": {"bytes_per_launch": 337304332, "read": 169532170,
+            "write": 167772162, "sources": "4dc2b6aef7a3d0b1"},
+    },
     # backward: summed over the call's kernels (strip kernel, dk/dv gather, table reduction)
     "bwd": {
         "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 738464990, "read": 403999838, "write": 334465152,
