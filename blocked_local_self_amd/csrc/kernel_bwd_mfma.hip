@@ -56,6 +56,9 @@ constexpr int kTabRows = 32;           // relative tables padded to 32 rows (2r-
 
 struct BwdMfmaPlan {
     int nq;                // queries per block (16 * NT)
+    int two_phase;         // block columns in two launches: even (phase 0), then odd
+    int phase;
+    int ncols;             // block columns this launch walks per image
     int qpitch;            // Q^T / dout^T channel pitch (elements)
     int off_v, off_kt, off_tab, off_tabt, off_qt, off_dot, off_rw, off_rh, off_d, off_scr, lds_bytes;
     int remap_xcd;
@@ -90,8 +93,8 @@ void bwd_strip_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
                       const __bf16* __restrict__ v, const __bf16* __restrict__ rel_h,
                       const __bf16* __restrict__ rel_w, const __bf16* __restrict__ out,
                       const __bf16* __restrict__ dout, const float* __restrict__ lse,
-                      __bf16* __restrict__ dq, float* __restrict__ part_kv, float* __restrict__ part_rel,
-                      Geometry g, BwdMfmaPlan p)
+                      __bf16* __restrict__ dq, __bf16* __restrict__ dk, __bf16* __restrict__ dv,
+                      float* __restrict__ part_kv, float* __restrict__ part_rel, Geometry g, BwdMfmaPlan p)
 {
     constexpr int KPL = D / 4;
     constexpr int CPP = D / 8;                  // 16-byte chunks per pixel
@@ -117,8 +120,10 @@ void bwd_strip_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
         const int64_t per = p.nwg >> 3;
         wg = (wg & 7) * per + (wg >> 3);
     }
-    const int64_t bh = wg / g.nbw;                             // (batch, head)
-    const int bx = (int)(wg - bh * g.nbw);                     // block column
+    const int64_t bh = wg / p.ncols;                           // (batch, head)
+    const int kcol = (int)(wg - bh * p.ncols);
+    const int bx = p.two_phase ? 2 * kcol + p.phase : kcol;     // block column
+    const int64_t strip = bh * g.nbw + bx;                     // its share / partial slot
     const int xb = bx * g.block;
     const int wx0 = xb - g.halo;                               // window column origin
     const int clo = max(0, -wx0), chi = min(r, g.W - wx0);     // in-image window columns
@@ -478,6 +483,33 @@ void bwd_strip_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
                           pack_bf16x2(dqT[mt][2] * g.scale, dqT[mt][3] * g.scale)};
         }
 
+        // the even neighbours' shares of the rows this block row finishes in
+        // window slots 0 and 1 (second launch only), in flight during the key
+        // path; not where registers are scarcest (d = 16 with 64 queries),
+        // which reads them when it needs them
+        constexpr bool PRE = !(D == 16 && NT == 4);
+        const bool shl = bx >= 1 && n < 2 * g.halo, shr = bx + 1 < g.nbw && n >= g.block;
+        f32x4 pk[2][D / 16], pv[2][D / 16];
+        auto share_src = [&](int t) {
+            const int64_t nb = shl ? strip - 1 : strip + 1;
+            const int cn = shl ? n + g.block : n - g.block;
+            return part_kv + ((nb * g.H + (wy0 + t)) * r + cn) * (2 * D) + 4 * gq;
+        };
+        if (PRE && p.phase == 1) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int t = wave + 4 * j;
+                if (t < g.block && t >= tlo && t < thi && n >= clo && n < chi && (shl || shr)) {
+                    const float* src = share_src(t);
+#pragma unroll
+                    for (int mt = 0; mt < D / 16; ++mt) {
+                        pk[j][mt] = *reinterpret_cast<const f32x4*>(src + 16 * mt);
+                        pv[j][mt] = *reinterpret_cast<const f32x4*>(src + D + 16 * mt);
+                    }
+                }
+            }
+        }
+
         // -------------------------------------------------------------- key path
         {
             constexpr int NP = (NT + 1) / 2;             // pairs of query tiles
@@ -485,23 +517,26 @@ void bwd_strip_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
             // queries, read from LDS per use (register budget)
             auto cw = [&](int u) { return bld<f32x4>(smem, p.off_rw + 4u * (n * NQ + 16 * u + 4 * gq)); };
             auto mDv = [&](int u) { return bld<f32x4>(smem, p.off_d + 4u * (16 * u + 4 * gq)); };   // -D
-            // A operands over query pairs: lane n' = channel, queries {4g..4g+3 of u0, of u1}
-            u32x4 qtA[NP][D / 16], gtA[NP][D / 16];
+            // A operands over query pairs: lane n' = channel, queries
+            // {4g..4g+3 of u0, of u1}; held in registers, or read from LDS per
+            // use where the shares are prefetched (register budget)
+            auto pairA = [&](unsigned base, int pr, int mt) {
+                const unsigned row = base + 2u * ((mt * 16 + n) * p.qpitch + 4 * gq);
+                const u32x2 a0 = bld<u32x2>(smem, row + 2u * (32 * pr));
+                u32x2 a1 = {0u, 0u};
+                if (2 * pr + 1 < NT) a1 = bld<u32x2>(smem, row + 2u * (32 * pr + 16));
+                return __builtin_bit_cast(s16x8, u32x4{a0[0], a0[1], a1[0], a1[1]});
+            };
+            s16x8 qtA[PRE ? 1 : NP][D / 16], gtA[PRE ? 1 : NP][D / 16];
+            if constexpr (!PRE) {
 #pragma unroll
-            for (int pr = 0; pr < NP; ++pr)
+                for (int pr = 0; pr < NP; ++pr)
 #pragma unroll
-                for (int mt = 0; mt < D / 16; ++mt) {
-                    const unsigned rowq = p.off_qt + 2u * ((mt * 16 + n) * p.qpitch + 4 * gq);
-                    const unsigned rowg = p.off_dot + 2u * ((mt * 16 + n) * p.qpitch + 4 * gq);
-                    const u32x2 a0 = bld<u32x2>(smem, rowq + 2u * (32 * pr)), g0 = bld<u32x2>(smem, rowg + 2u * (32 * pr));
-                    u32x2 a1 = {0u, 0u}, g1 = {0u, 0u};
-                    if (2 * pr + 1 < NT) {
-                        a1 = bld<u32x2>(smem, rowq + 2u * (32 * pr + 16));
-                        g1 = bld<u32x2>(smem, rowg + 2u * (32 * pr + 16));
+                    for (int mt = 0; mt < D / 16; ++mt) {
+                        qtA[pr][mt] = pairA(p.off_qt, pr, mt);
+                        gtA[pr][mt] = pairA(p.off_dot, pr, mt);
                     }
-                    qtA[pr][mt] = u32x4{a0[0], a0[1], a1[0], a1[1]};
-                    gtA[pr][mt] = u32x4{g0[0], g0[1], g1[0], g1[1]};
-                }
+            }
             // every slot is computed: rows past the window or, without zero
             // padding, off the image have a height term of -inf (weights 0);
             // rows that are neither finished nor carried are never written
@@ -534,8 +569,8 @@ void bwd_strip_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
                     const s16x8 lp = __builtin_bit_cast(s16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
 #pragma unroll
                     for (int mt = 0; mt < D / 16; ++mt) {
-                        avT[j][mt] = mma_k32(__builtin_bit_cast(s16x8, gtA[pr][mt]), pp, avT[j][mt]);
-                        akT[j][mt] = mma_k32(__builtin_bit_cast(s16x8, qtA[pr][mt]), lp, akT[j][mt]);
+                        avT[j][mt] = mma_k32(PRE ? pairA(p.off_dot, pr, mt) : gtA[PRE ? 0 : pr][mt], pp, avT[j][mt]);
+                        akT[j][mt] = mma_k32(PRE ? pairA(p.off_qt, pr, mt) : qtA[PRE ? 0 : pr][mt], lp, akT[j][mt]);
                     }
                 }
             }
@@ -544,19 +579,59 @@ void bwd_strip_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
         // ------------------------- finished key rows out, the others carried
         // Window row t is in no later window when t < block (the next window
         // starts block rows lower), or in the last block row.  Such a row is
-        // this column's share of key row wy0 + t: [dk(D) | dv(D)] fp32 per
-        // window column, for the in-image columns.
+        // this column's sum for key row wy0 + t, for the in-image columns.
+        // One launch: every column writes it as its share ([dk(D) | dv(D)]
+        // fp32 per window column) for the gather kernel.  Two launches
+        // (2 halo <= block, so a key lies in at most two adjacent windows):
+        // an even column writes shares only for the window columns an odd
+        // neighbour also holds (n < 2h on the left, n >= block on the right)
+        // and final dk, dv for the rest; an odd column then adds those
+        // shares to its own sums and writes final dk, dv for its whole window.
         {
             const bool last = by + 1 == g.nbh;
 #pragma unroll
             for (int j = 0; j < NSLOT; ++j) {
                 const int t = wave + 4 * j;
                 if ((t < g.block || last) && t >= tlo && t < thi && n >= clo && n < chi) {
-                    float* dst = part_kv + ((wg * g.H + (wy0 + t)) * r + n) * (2 * D) + 4 * gq;
+                    const int64_t ky = wy0 + t;
+                    if (!p.two_phase || (p.phase == 0 && (shl || shr))) {
+                        float* dst = part_kv + ((strip * g.H + ky) * r + n) * (2 * D) + 4 * gq;
 #pragma unroll
-                    for (int mt = 0; mt < D / 16; ++mt) {
-                        *reinterpret_cast<f32x4*>(dst + 16 * mt) = akT[j][mt] * g.scale;
-                        *reinterpret_cast<f32x4*>(dst + D + 16 * mt) = avT[j][mt];
+                        for (int mt = 0; mt < D / 16; ++mt) {
+                            *reinterpret_cast<f32x4*>(dst + 16 * mt) = akT[j][mt] * g.scale;
+                            *reinterpret_cast<f32x4*>(dst + D + 16 * mt) = avT[j][mt];
+                        }
+                    } else {
+                        f32x4 kk4[D / 16], vv4[D / 16];
+#pragma unroll
+                        for (int mt = 0; mt < D / 16; ++mt) {
+                            kk4[mt] = akT[j][mt] * g.scale;
+                            vv4[mt] = avT[j][mt];
+                        }
+                        if (p.phase == 1 && (shl || shr)) {     // the even neighbour's share
+                            if (PRE && j < 2 && t < g.block) {   // prefetched
+#pragma unroll
+                                for (int mt = 0; mt < D / 16; ++mt) {
+                                    kk4[mt] += pk[j < 2 ? j : 0][mt];
+                                    vv4[mt] += pv[j < 2 ? j : 0][mt];
+                                }
+                            } else {
+                                const float* src = share_src(t);
+#pragma unroll
+                                for (int mt = 0; mt < D / 16; ++mt) {
+                                    kk4[mt] += *reinterpret_cast<const f32x4*>(src + 16 * mt);
+                                    vv4[mt] += *reinterpret_cast<const f32x4*>(src + D + 16 * mt);
+                                }
+                            }
+                        }
+                        const int64_t o = ((bh * g.H + ky) * g.W + wx0 + n) * D + 4 * gq;
+#pragma unroll
+                        for (int mt = 0; mt < D / 16; ++mt) {
+                            *reinterpret_cast<u32x2*>(dk + o + 16 * mt) =
+                                u32x2{pack_bf16x2(kk4[mt][0], kk4[mt][1]), pack_bf16x2(kk4[mt][2], kk4[mt][3])};
+                            *reinterpret_cast<u32x2*>(dv + o + 16 * mt) =
+                                u32x2{pack_bf16x2(vv4[mt][0], vv4[mt][1]), pack_bf16x2(vv4[mt][2], vv4[mt][3])};
+                        }
                     }
                 }
             }
@@ -603,7 +678,7 @@ void bwd_strip_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
                     red[((wave * 2 + tab) * kTabRows + rt * 16 + n) * D + mt * 16 + 4 * gq + i] = drelT[tab][rt][mt][i];
     __syncthreads();
     const int E = (2 * r - 1) * D;
-    float* dst = part_rel + wg * 2 * (int64_t)E;
+    float* dst = part_rel + strip * 2 * (int64_t)E;
     for (int e = tid; e < 2 * E; e += 256) {
         const int tab = e / E, rr = e - tab * E;
         float acc = 0.f;
@@ -698,11 +773,16 @@ int64_t bwd_mfma_kv_floats(const Geometry& g) { return g.BH * g.nbw * (int64_t)g
 
 template <int D, int NT>
 static hipError_t bwd_mfma_t(const void* q, const void* k, const void* v, const void* rh, const void* rw,
-                             const void* out, const void* dout, const float* lse, void* dq, float* part_kv,
-                             float* part_rel, const Geometry& g, hipStream_t st)
+                             const void* out, const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                             float* part_kv, float* part_rel, const Geometry& g, bool two_phase, int phase,
+                             hipStream_t st)
 {
     BwdMfmaPlan p = bwd_mfma_plan(g);
-    p.nwg = bwd_mfma_rel_rows(g);
+    p.two_phase = two_phase ? 1 : 0;
+    p.phase = phase;
+    p.ncols = two_phase ? (g.nbw - phase + 1) / 2 : g.nbw;
+    p.nwg = g.BH * p.ncols;
+    if (p.nwg == 0) return hipSuccess;
     p.remap_xcd = (p.nwg % 8 == 0) ? 1 : 0;
     p.alpha = (float)((double)g.scale * 1.4426950408889634);
     auto kern = bwd_strip_kernel<D, NT>;
@@ -713,12 +793,15 @@ static hipError_t bwd_mfma_t(const void* q, const void* k, const void* v, const 
     hipLaunchKernelGGL(kern, dim3((unsigned)p.nwg), dim3(256), p.lds_bytes, st,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)rh,
                        (const __bf16*)rw, (const __bf16*)out, (const __bf16*)dout, lse, (__bf16*)dq,
-                       part_kv, part_rel, g, p);
+                       (__bf16*)dk, (__bf16*)dv, part_kv, part_rel, g, p);
     return hipGetLastError();
 }
 
-// Strip kernel + dk/dv gather.  The table partials land in part_rel
-// ([BH*nbw][2][2r-1][d], scaled), ready for the fixed-order reduction.
+// The strip kernel, then the dk/dv shares combined: with 2*halo <= block in
+// two launches of the strip kernel (even block columns, then odd ones, which
+// add the even columns' shares), otherwise in one launch and a gather.  The
+// table partials land in part_rel ([BH*nbw][2][2r-1][d], scaled), ready for
+// the fixed-order reduction.
 hipError_t launch_zero_bf16(void* p, int64_t n, hipStream_t st);
 
 hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const void* rh, const void* rw,
@@ -731,11 +814,21 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
         e = launch_zero_bf16(dq, g.BH * g.H * g.W * g.d, st);
         if (e != hipSuccess) return e;
     }
-    if (g.d == 16) e = nt == 1 ? bwd_mfma_t<16, 1>(q, k, v, rh, rw, out, dout, lse, dq, part_kv, part_rel, g, st)
-                               : bwd_mfma_t<16, 4>(q, k, v, rh, rw, out, dout, lse, dq, part_kv, part_rel, g, st);
-    else e = nt == 1 ? bwd_mfma_t<32, 1>(q, k, v, rh, rw, out, dout, lse, dq, part_kv, part_rel, g, st)
-                     : bwd_mfma_t<32, 4>(q, k, v, rh, rw, out, dout, lse, dq, part_kv, part_rel, g, st);
+    const bool two = 2 * g.halo <= g.block;
+    auto strip = [&](int phase) {
+        if (g.d == 16)
+            return nt == 1 ? bwd_mfma_t<16, 1>(q, k, v, rh, rw, out, dout, lse, dq, dk, dv, part_kv, part_rel, g, two,
+                                               phase, st)
+                           : bwd_mfma_t<16, 4>(q, k, v, rh, rw, out, dout, lse, dq, dk, dv, part_kv, part_rel, g, two,
+                                               phase, st);
+        return nt == 1 ? bwd_mfma_t<32, 1>(q, k, v, rh, rw, out, dout, lse, dq, dk, dv, part_kv, part_rel, g, two,
+                                           phase, st)
+                       : bwd_mfma_t<32, 4>(q, k, v, rh, rw, out, dout, lse, dq, dk, dv, part_kv, part_rel, g, two,
+                                           phase, st);
+    };
+    e = strip(0);
     if (e != hipSuccess) return e;
+    if (two) return strip(1);
     const int64_t total = g.BH * g.H * g.W * (g.d / 4);
     const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((total + 255) / 256, 1 << 20));
     if (g.d == 16)
