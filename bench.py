@@ -80,14 +80,14 @@ MEASURED_TRAFFIC = {
         "early_stage_bf16_64x64_d16_b8h3/nhwc": {"bytes_per_launch": 337304332, "read": 169532170,
             "write": 167772162, "sources": "4dc2b6aef7a3d0b1"},
     },
-    # backward: summed over the call's kernels (strip kernel, dk/dv gather, table reduction)
+    # backward: summed over the call's kernels (strip kernel launches, table reduction)
     "bwd": {
-        "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 738464990, "read": 403999838, "write": 334465152,
-            "sources": "a7dee07ddb8e074d"},
-        "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 719827550, "read": 394830174, "write": 324997376,
-            "sources": "a7dee07ddb8e074d"},
-        "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 670355761, "read": 331696305, "write": 338659456,
-            "sources": "a7dee07ddb8e074d"},
+        "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 590617115, "read": 373592475, "write": 217024640,
+            "sources": "6479a114b5641871"},
+        "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 504387837, "read": 313608189, "write": 190779648,
+            "sources": "6479a114b5641871"},
+        "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 464386157, "read": 259944419, "write": 204441737,
+            "sources": "6479a114b5641871"},
     },
 }
 
