@@ -454,14 +454,19 @@ static hipError_t launch_dn(const void* q, const void* k, const void* v, const v
 bool ring_supported(const Geometry& g);
 hipError_t launch_ring(const void* q, const void* k, const void* v, const void* rh,
                        const void* rw, void* out, float* lse, const Geometry& g, hipStream_t st);
+bool wide_supported(const Geometry& g, bool bf16);
+hipError_t launch_wide(const void* q, const void* k, const void* v, const void* rh, const void* rw, void* out,
+                       float* lse, const Geometry& g, hipStream_t st);
 
 // Matrix-core launch: the persistent ring kernel when it covers the shape,
-// else the strip kernel.  force_strip selects the strip kernel regardless.
+// the streaming kernel for windows wider than 32 columns, else the strip
+// kernel.  force_strip selects the strip kernel regardless.
 hipError_t launch_mfma(const void* q, const void* k, const void* v, const void* rh,
                        const void* rw, void* out, float* lse, const Geometry& g, bool force_strip,
                        hipStream_t st)
 {
     if (!force_strip && ring_supported(g)) return launch_ring(q, k, v, rh, rw, out, lse, g, st);
+    if (!force_strip && g.flags == 0 && wide_supported(g, true)) return launch_wide(q, k, v, rh, rw, out, lse, g, st);
     const bool wide = g.r > 16;
     if (g.d == 16 && g.r > 32) return launch_dn<16, 3>(q, k, v, rh, rw, out, lse, g, st);
     if (g.d == 16) return wide ? launch_dn<16, 2>(q, k, v, rh, rw, out, lse, g, st)
