@@ -60,7 +60,7 @@ struct BwdMfmaPlan {
     int phase;
     int ncols;             // block columns this launch walks per image
     int qpitch;            // Q^T / dout^T channel pitch (elements)
-    int off_v, off_kt, off_tab, off_tabt, off_qt, off_dot, off_rw, off_rh, off_d, off_scr, lds_bytes;
+    int off_v, off_kt, off_tab, off_tabt, off_qt, off_dot, off_rw, off_rh, off_d, off_scr, off_red, lds_bytes;
     int remap_xcd;
     int64_t nwg;
     float alpha;           // scale * log2(e)
@@ -374,7 +374,11 @@ void bwd_strip_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
         __syncthreads();
 
         // ------------------------------------------------------------ query path
-        if (wave < NT) {
+        // With one query tile (NT = 1) its row pairs are spread over the four
+        // waves and their partial sums added in wave order through LDS;
+        // wave 0 then finishes the tile.
+        constexpr bool SPLIT = NT == 1;
+        if (SPLIT || wave < NT) {
             const int u = uown;
             const FragT qf = qown, gf = gown;
             const float mD = bld<float>(smem, p.off_d + 4u * (16 * u + n));   // -D
@@ -417,9 +421,36 @@ void bwd_strip_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
                 ghT = mma_k32(__builtin_bit_cast(s16x8, u32x4{e0, e0, e1, e1}), lp, ghT);
                 gwT = mma_k32(__builtin_bit_cast(s16x8, ecol), lp, gwT);
             };
-            int t0 = qtlo;
-            for (; t0 + 1 < qthi; t0 += 2) step(std::true_type{}, t0);
-            if (t0 < qthi) step(std::false_type{}, t0);
+            if constexpr (SPLIT) {
+                for (int t0 = qtlo + 2 * wave; t0 < qthi; t0 += 8) {
+                    if (t0 + 1 < qthi) step(std::true_type{}, t0);
+                    else step(std::false_type{}, t0);
+                }
+                // lane-major [wave][lane][dq^T tiles, row sums, column sums]
+                constexpr int NV = D / 16 + 2;
+                const unsigned rbase = p.off_red + 16u * (unsigned)(lane * NV);
+#pragma unroll
+                for (int mt = 0; mt < D / 16; ++mt)
+                    bst<f32x4>(smem, rbase + 16u * (unsigned)(wave * 64 * NV + mt), dqT[mt]);
+                bst<f32x4>(smem, rbase + 16u * (unsigned)(wave * 64 * NV + D / 16), ghT);
+                bst<f32x4>(smem, rbase + 16u * (unsigned)(wave * 64 * NV + D / 16 + 1), gwT);
+                __syncthreads();
+                if (wave == 0) {
+#pragma unroll
+                    for (int w = 1; w < 4; ++w) {
+#pragma unroll
+                        for (int mt = 0; mt < D / 16; ++mt)
+                            dqT[mt] += bld<f32x4>(smem, rbase + 16u * (unsigned)(w * 64 * NV + mt));
+                        ghT += bld<f32x4>(smem, rbase + 16u * (unsigned)(w * 64 * NV + D / 16));
+                        gwT += bld<f32x4>(smem, rbase + 16u * (unsigned)(w * 64 * NV + D / 16 + 1));
+                    }
+                }
+            } else {
+                int t0 = qtlo;
+                for (; t0 + 1 < qthi; t0 += 2) step(std::true_type{}, t0);
+                if (t0 < qthi) step(std::false_type{}, t0);
+            }
+          if (!SPLIT || wave == 0) {
 
             // sums re-indexed by table row (R = w - yl + r - 1 for rows, - xl for
             // columns), zero elsewhere, in this wave's scratch; then
@@ -481,6 +512,7 @@ void bwd_strip_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
                 *reinterpret_cast<u32x2*>(dp + mt * 16) =
                     u32x2{pack_bf16x2(dqT[mt][0] * g.scale, dqT[mt][1] * g.scale),
                           pack_bf16x2(dqT[mt][2] * g.scale, dqT[mt][3] * g.scale)};
+          }
         }
 
         // the even neighbours' shares of the rows this block row finishes in
@@ -747,6 +779,9 @@ static BwdMfmaPlan bwd_mfma_plan(const Geometry& g)
     p.off_d = brup(p.off_rh + kBRows * p.nq * 4, 16);
     p.off_scr = brup(p.off_d + p.nq * 4, 16);
     p.lds_bytes = p.off_scr + 4 * kTabRows * kScrStrideB * 4;
+    // one query tile: the four waves' partial query-path sums
+    p.off_red = brup(p.lds_bytes, 16);
+    if (p.nq == 16) p.lds_bytes = p.off_red + 4 * 64 * (D / 16 + 2) * 16;
     // the final table reduction reuses the front of LDS (K and V):
     // 4 waves x 2 x 32 x D floats
     p.lds_bytes = std::max(p.lds_bytes, 4 * 2 * kTabRows * D * 4);
