@@ -331,6 +331,20 @@ void bwd_strip_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
         // the next block row's inputs, in flight during this one's compute
         if (by + 1 < g.nbh) prefetch(by + 1, P);
 
+        // strided queries, one tile per block: dq is zero at the block's
+        // other pixels (the blocks tile the image, so every such pixel is
+        // written once; with more tiles a separate pass clears dq first)
+        if (NT == 1 && g.stride > 1) {
+            constexpr int C4 = D / 4;                       // 8-byte pieces per pixel
+            for (int e = tid; e < g.block * g.block * C4; e += 256) {
+                const int pix = e / C4, c4 = e - pix * C4;
+                const int yy = pix / g.block, xx = pix - yy * g.block;
+                if (yy % g.stride || xx % g.stride)
+                    *reinterpret_cast<u32x2*>(dq + (bh * g.H * g.W + (int64_t)(yb + yy) * g.W + xb + xx) * D + 4 * c4) =
+                        u32x2{0u, 0u};
+            }
+        }
+
         // ----------------------------------- relative tables per query tile
         if (wave < NT) {
             const int u = uown;
@@ -845,7 +859,7 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
 {
     const int nt = (g.block / g.stride) * (g.block / g.stride) / 16;
     hipError_t e;
-    if (g.stride > 1) {   // dq is zero at the pixels that are not queries
+    if (g.stride > 1 && nt != 1) {   // dq is zero at the pixels that are not queries
         e = launch_zero_bf16(dq, g.BH * g.H * g.W * g.d, st);
         if (e != hipSuccess) return e;
     }
