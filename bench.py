@@ -82,12 +82,12 @@ MEASURED_TRAFFIC = {
     },
     # backward: summed over the call's kernels (strip kernel launches, table reduction)
     "bwd": {
-        "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 590617115, "read": 373592475, "write": 217024640,
-            "sources": "6479a114b5641871"},
-        "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 504387837, "read": 313608189, "write": 190779648,
-            "sources": "6479a114b5641871"},
-        "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 464386157, "read": 259944419, "write": 204441737,
-            "sources": "6479a114b5641871"},
+        "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 590653110, "read": 373628470, "write": 217024640,
+            "sources": "0c842c555e88797f"},
+        "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 504399861, "read": 313620213, "write": 190779648,
+            "sources": "0c842c555e88797f"},
+        "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 456748711, "read": 260247435, "write": 196501275,
+            "sources": "0c842c555e88797f"},
     },
 }
 
