@@ -135,6 +135,13 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, gq = lane >> 4;
+    // One column tile, 16 channels, two query tiles: the group's 32 queries
+    // go through 32x32 MFMAs (lane = query lane & 31, K half lane >> 5).
+    // A K = 16 score tile of 32 keys x 32 queries then costs what a 16x16
+    // one does, and one 32x32 P.V MFMA with bf16 ones in rows 16-31 gives
+    // the weighted sum and the weight sum together.
+    constexpr bool G32 = D == 16 && NCT == 1 && QT == 2 && !VAR;
+    const int n32 = lane & 31, g2 = lane >> 5;
     constexpr unsigned scr_u = (unsigned)kScrRows * kScrStride * 4;   // bytes per query tile
     const unsigned scr0 = p.off_scr + wave * QT * scr_u + 4u * n;     // column n of tile 0
 
@@ -189,6 +196,8 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     // sees is therefore independent of wave timing.
     unsigned* kmax_bits = reinterpret_cast<unsigned*>(smem + p.off_kn);
     if (tid < 32) kmax_bits[tid] = 0u;
+    const unsigned off_one = p.off_kn + 2 * 16 * 4 + D * 4;     // 32 bytes of bf16 ones
+    if (G32 && tid < 8) lds_st<unsigned>(smem, off_one + 4u * tid, 0x3F803F80u);
     __syncthreads();
     auto load_item = [&](const Item& it, int row0, u32x4 (&kk)[4], u32x4 (&vv)[4]) {
         const int iy = row0 + it.dr;
@@ -254,7 +263,11 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     auto tab_frag = [&](unsigned off, int rt) {
         return lds_ld<FragT>(smem, off + 2u * ((rt * 16 + n) * D + gq * KPL));
     };
-    if constexpr (NCT == 1) {
+    s16x8 tab32w, tab32h;                       // 32x32 A operands: row n32, channels 8*g2..+7
+    if constexpr (G32) {
+        tab32w = lds_ld<s16x8>(smem, offrw + 2u * (n32 * D + 8 * g2));
+        tab32h = lds_ld<s16x8>(smem, offrh + 2u * (n32 * D + 8 * g2));
+    } else if constexpr (NCT == 1) {
 #pragma unroll
         for (int rt = 0; rt < kRelTiles; ++rt) {
             tabw[rt] = tab_frag(offrw, rt);
@@ -309,6 +322,10 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     // small non-negative integer quotient a / b through an fp32 reciprocal
     // (exact for a < 2^16: (a + 0.5) / b stays > 0.5/b away from integers)
     auto qdiv = [](int a, float rb) { return (int)(((float)a + 0.5f) * rb); };
+    // query of this lane in tile u of group grp (block-local index); the
+    // 32-query layout has one query per lane (entries [0] of a Tile)
+    constexpr int QU = G32 ? 1 : QT;
+    auto qindex = [&](int grp, int u) { return G32 ? grp * 32 + n32 : (grp * QT + u) * 16 + n; };
     auto tile_of = [&](int byy, int it) {
         Tile T;
         const int j = it / p.groups, grp = it - j * p.groups;
@@ -318,8 +335,8 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             T.wcol0 = j * g.block;
             const int qbase0 = yb * g.W + T.xb, obase0 = byy * side * g.Wo + (bx_first + j) * side;
 #pragma unroll
-            for (int u = 0; u < QT; ++u) {
-                const i32x4 e = lds_ld<i32x4>(smem, p.off_qt + 16u * ((grp * QT + u) * 16 + n));
+            for (int u = 0; u < QU; ++u) {
+                const i32x4 e = lds_ld<i32x4>(smem, p.off_qt + 16u * qindex(grp, u));
                 T.qvalid[u] = e[0] >= 0;
                 T.yl[u] = T.qvalid[u] ? e[0] : 0;
                 T.xl[u] = e[1];
@@ -336,8 +353,8 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         const float rnqx = __builtin_amdgcn_rcpf((float)nqx);   // 1 ulp: ample for qdiv
         const int opix0 = (yb / g.stride) * g.Wo + T.xb / g.stride;   // block % stride == 0
 #pragma unroll
-        for (int u = 0; u < QT; ++u) {
-            const int qi = (grp * QT + u) * 16 + n;
+        for (int u = 0; u < QU; ++u) {
+            const int qi = qindex(grp, u);
             T.qvalid[u] = qi < nq;
             const int qq = T.qvalid[u] ? qi : 0;
             const int iy = qdiv(qq, rnqx), ix = qq - iy * nqx;
@@ -355,10 +372,16 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             const int it = f + ii * kRingWaves;
             if (byy < g.nbh && it < items) {
                 const Tile T = tile_of(byy, it);
+                if constexpr (G32) {                  // channels 8*g2..+7 of the lane's query
+                    const u32x4 w = *reinterpret_cast<const u32x4*>(q + qbase + (int64_t)T.qpix[0] * D + 8 * g2);
+                    qf[ii][0] = __builtin_bit_cast(FragT, u32x2{w[0], w[1]});
+                    qf[ii][1] = __builtin_bit_cast(FragT, u32x2{w[2], w[3]});
+                } else {
 #pragma unroll
                 for (int u = 0; u < QT; ++u)
                     qf[ii][u] = *reinterpret_cast<const FragT*>(
                         q + qbase + (int64_t)T.qpix[u] * D + gq * KPL);
+                }
             }
         }
     };
@@ -379,6 +402,15 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         float lse2[QT];
     };
     auto store_result = [&](const Tile& T, const Result& res) {
+        if constexpr (G32) {                          // channels 4*g2.. and 8+4*g2.. of the lane's query
+            if (!T.qvalid[0]) return;
+            __bf16* op = out + bh * (int64_t)g.Ho * g.Wo * D + (int64_t)T.opix[0] * D + 4 * g2;
+            *reinterpret_cast<u32x2*>(op) = res.w[0][0];
+            *reinterpret_cast<u32x2*>(op + 8) = res.w[1][0];
+            if (lse != nullptr && g2 == 0)
+                lse[bh * (int64_t)g.Ho * g.Wo + T.opix[0]] = res.lse2[0] * 0.6931471805599453f;
+            return;
+        }
 #pragma unroll
         for (int u = 0; u < QT; ++u) {
             if (!T.qvalid[u]) continue;
@@ -390,8 +422,191 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         }
     };
 
+    // One group of 32 queries of block row byy in the 32x32 layout (one
+    // column tile, 16 channels, no variants).  The steps are those of the
+    // 16x16 path below; lane l holds query l & 31 and, of every 32-row
+    // operand or result, the rows 8j + 4(l >> 5) + i.
+    auto do_item32 = [&](int byy, const Tile& T, const FragT (&qf)[QT], Result& res) {
+      if constexpr (G32) {
+            const int yb = byy * g.block;
+            const int wy0 = yb - g.halo;
+            const int tlo = max(0, -wy0), thi = min(R, g.H - wy0);
+            const int base = yb % ring;                   // ring slot of window row 0
+            auto rslot = [&](int t) -> unsigned {
+                const int s2 = base + t;
+                return (unsigned)(s2 >= ring ? s2 - ring : s2);
+            };
+            const u32x2 qa = __builtin_bit_cast(u32x2, qf[0]), qb = __builtin_bit_cast(u32x2, qf[1]);
+            const s16x8 q32 = __builtin_bit_cast(s16x8, u32x4{qa[0], qa[1], qb[0], qb[1]});
+            const f32x16 zero16 = {};
+            const unsigned scr32 = p.off_scr + wave * QT * scr_u + (unsigned)(n32 >> 4) * scr_u + 4u * (n32 & 15);
+            constexpr unsigned RS = 4u * kScrStride;      // bytes per scratch row
+
+            // ---- relative logits of the 32 table rows, then the width terms
+            const f32x16 gw = mma32_k16(tab32w, q32, zero16);
+            const f32x16 gh = mma32_k16(tab32h, q32, zero16);
+    #pragma unroll
+            for (int j = 0; j < 4; ++j)
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) lds_st<float>(smem, scr32 + RS * (8 * j + 4 * g2 + i), gw[4 * j + i]);
+            // width term of window column c = 8j + 4*g2 + i (j = 0, 1); rows
+            // 16-31 of a score tile are the second window row: same columns
+            const int clo = g.halo - T.xb, chi = min(R, g.W - T.xb + g.halo);
+            f32x16 cinit;
+            {
+                const unsigned a = scr32 + RS * (R - 1 - T.xl[0] + 4 * g2);
+    #pragma unroll
+                for (int j = 0; j < 2; ++j)
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int c = 8 * j + 4 * g2 + i;
+                        const float val = lds_ld<float>(smem, a + RS * (8 * j + i));
+                        cinit[4 * j + i] = cinit[8 + 4 * j + i] = (c >= clo && c < chi) ? val : kMaskLogit;
+                    }
+            }
+
+            // ---- softmax shift: the bound of the 16x16 path, for 32 queries in
+            // one MFMA (a_c in all 32 rows, |q| as B; channels 8*g2..+7 lie in chunk g2)
+            float mb;
+            {
+                const float kn = __builtin_sqrtf(__builtin_bit_cast(float, kmax_bits[16 * (byy & 1) + g2])) *
+                                 (1.f + 0x1p-20f);
+                s16x8 abound, aq;
+    #pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float a = kn + tmax[8 * g2 + e];
+                    abound[e] = (short)((__builtin_bit_cast(unsigned, a) + 0xffffu) >> 16);   // round up
+                    aq[e] = (short)(q32[e] & 0x7fff);
+                }
+                const float bound = mma32_k16(abound, aq, zero16)[0];
+                mb = alpha * (bound + 1e-3f * (1.f + bound));
+            }
+            // height terms alpha*G - mb -> scratch (after the width reads)
+            const int sh = R - 1 - T.yl[0];
+    #pragma unroll
+            for (int j = 0; j < 4; ++j)
+    #pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    lds_st<float>(smem, scr32 + RS * (8 * j + 4 * g2 + i), fmaf(gh[4 * j + i], alpha, -mb));
+            const unsigned rh = scr32 + RS * sh;          // scratch of window row 0
+            // row pairs start at even ring slots (see the 16x16 path); the rows
+            // a pair adds before tlo or at thi get a height term of -inf
+            const int ts = tlo - ((base + tlo) & 1);
+            if (ts < tlo) lds_st<float>(smem, rh + RS * ts, -INFINITY);
+            if ((thi - ts) & 1) lds_st<float>(smem, rh + RS * thi, -INFINITY);
+
+            // ---- operands: K rows t, t+1 (keys 0-15, 16-31: 16 bytes of chunk
+            // g2 per lane); V^T of channel n32 for n32 < 16 and bf16 ones for the
+            // weight-sum rows 16-31 (stride 0: the same 32 bytes every row)
+            const int kcol = T.wcol0 + (n32 & 15);
+            const unsigned kl = (unsigned)kcol * PIXB + k_chunk<D>(g2, kcol) + (unsigned)(n32 >> 4) * rowb_k;
+            const bool vlane = n32 < 16;
+            const unsigned vl = vlane ? offv + 2u * ((unsigned)n32 * CP + T.wcol0 + 4 * g2) : off_one;
+            const unsigned vrow = vlane ? 2u * SWv : 0u;
+            struct Ops32 {
+                s16x8 a;
+                u32x4 v0, v1;
+                float c0, c1;
+            };
+            auto fetch = [&](int t0) {
+                Ops32 o;
+                const unsigned sl = rslot(t0);
+                o.a = lds_ld<s16x8>(smem, kl + sl * rowb_k);
+                const unsigned vo = vl + sl * vrow;
+                const u32x2 x0 = lds_ld<u32x2>(smem, vo), x1 = lds_ld<u32x2>(smem, vo + 16);
+                const u32x2 y0 = lds_ld<u32x2>(smem, vo + vrow), y1 = lds_ld<u32x2>(smem, vo + vrow + 16);
+                o.v0 = u32x4{x0[0], x0[1], x1[0], x1[1]};
+                o.v1 = u32x4{y0[0], y0[1], y1[0], y1[1]};
+                o.c0 = lds_ld<float>(smem, rh + RS * t0);
+                o.c1 = lds_ld<float>(smem, rh + RS * (t0 + 1));
+                return o;
+            };
+            f32x16 O, O2;                             // rows t and t+1 of each pair
+            auto weighted_sum = [&]() {
+                O = zero16;
+                O2 = zero16;
+                auto compute = [&](const Ops32& c) {
+                    const f32x16 sc = mma32_k16(c.a, q32, cinit);
+                    unsigned pw[8];
+    #pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float e = j < 2 ? c.c0 : c.c1;
+                        pw[2 * j] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sc[4 * j], alpha, e)),
+                                                __builtin_amdgcn_exp2f(fmaf(sc[4 * j + 1], alpha, e)));
+                        pw[2 * j + 1] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sc[4 * j + 2], alpha, e)),
+                                                    __builtin_amdgcn_exp2f(fmaf(sc[4 * j + 3], alpha, e)));
+                    }
+                    // K order of B (per lane half): columns 4*g2+i, then 8+4*g2+i;
+                    // the V^T operand was read in the same order
+                    O = mma32_k16(__builtin_bit_cast(s16x8, c.v0),
+                                  __builtin_bit_cast(s16x8, u32x4{pw[0], pw[1], pw[2], pw[3]}), O);
+                    O2 = mma32_k16(__builtin_bit_cast(s16x8, c.v1),
+                                   __builtin_bit_cast(s16x8, u32x4{pw[4], pw[5], pw[6], pw[7]}), O2);
+                };
+                Ops32 A = fetch(ts), B;
+                for (int t = ts;;) {
+                    B = fetch(t + 2 < thi ? t + 2 : t);
+                    __builtin_amdgcn_sched_barrier(0);
+                    compute(A);
+                    __builtin_amdgcn_sched_barrier(0);
+                    t += 2;
+                    if (t >= thi) break;
+                    A = fetch(t + 2 < thi ? t + 2 : t);
+                    __builtin_amdgcn_sched_barrier(0);
+                    compute(B);
+                    __builtin_amdgcn_sched_barrier(0);
+                    t += 2;
+                    if (t >= thi) break;
+                }
+                O += O2;
+            };
+
+            weighted_sum();
+            float shift = mb;
+            if (__any(!(O[8] >= 0x1p-60f))) {
+                // exact maximum of the shifted base-2 logits, then shift the
+                // stored height terms by it and redo
+                float M = -3.0e38f;
+                for (int t = ts; t < thi; t += 2) {
+                    const f32x16 sc = mma32_k16(lds_ld<s16x8>(smem, kl + rslot(t) * rowb_k), q32, cinit);
+                    float m0 = sc[0], m1 = sc[8];
+    #pragma unroll
+                    for (int e = 1; e < 8; ++e) {
+                        m0 = fmaxf(m0, sc[e]);
+                        m1 = fmaxf(m1, sc[8 + e]);
+                    }
+                    M = fmaxf(M, fmaxf(fmaf(m0, alpha, lds_ld<float>(smem, rh + RS * t)),
+                                       fmaf(m1, alpha, lds_ld<float>(smem, rh + RS * (t + 1)))));
+                }
+                {
+                    float a = M, b = M;
+                    swap32(a, b);                         // the query's other lane half
+                    M = fmaxf(a, b);
+                }
+                shift += M;
+    #pragma unroll
+                for (int r2 = 0; r2 < 8; ++r2) {          // window rows 8*g2 .. +7 of the query
+                    const unsigned a = rh + RS * (8 * g2 + r2);
+                    lds_st<float>(smem, a, lds_ld<float>(smem, a) - M);
+                }
+                weighted_sum();
+            }
+
+            // ---- normalise and pack: rows 0-15 are channels, 16-31 the weight sum
+            const float L = O[8];
+            if (lse != nullptr) res.lse2[0] = shift + __builtin_amdgcn_logf(L);
+            const float inv = __builtin_amdgcn_rcpf(L);
+            res.w[0][0] = u32x2{pack_bf16x2(O[0] * inv, O[1] * inv), pack_bf16x2(O[2] * inv, O[3] * inv)};
+            res.w[1][0] = u32x2{pack_bf16x2(O[4] * inv, O[5] * inv), pack_bf16x2(O[6] * inv, O[7] * inv)};
+      }
+    };
+
     // One group of QT query tiles of block row byy.
     auto do_item = [&](int byy, const Tile& T, const FragT (&qf)[QT], Result& res) {
+        if constexpr (G32) {
+            do_item32(byy, T, qf, res);
+            return;
+        }
         const int yb = byy * g.block;
         const int wy0 = yb - g.halo;
         // variants: zero padding keeps every window position (off-image ones
@@ -788,7 +1003,8 @@ static RingPlan ring_plan(const Geometry& g, int nct, int qt, int waves, int nbx
     p.off_rel = rup(p.off_v + vb, 16);
     p.off_scr = rup(p.off_rel + rb, 16);
     p.off_kn = rup(p.off_scr + sb, 16);
-    p.off_qt = rup(p.off_kn + 2 * 16 * 4 + g.d * 4, 16);    // key-chunk norm maxima (2 sets), table maxima
+    // key-chunk norm maxima (2 sets), table maxima, 32 bytes of bf16 ones
+    p.off_qt = rup(p.off_kn + 2 * 16 * 4 + g.d * 4 + 32, 16);
     p.lds_bytes = p.off_qt + p.groups * qt * 16 * 16;       // query geometry of a full block
     return p;
 }

@@ -12,6 +12,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr float kMaskLogit = -1.0e30f;       // exp2 of (alpha * this) is exactly 0
 
@@ -35,6 +36,14 @@ template <> struct Frag<32> {
 __device__ inline f32x4 mma_k32(s16x8 a, s16x8 b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16((bf16x8)a, (bf16x8)b, c, 0, 0, 0);
+}
+
+// 32x32 output tile, K = 16 (8 bf16 per lane: lanes 0-31 and 32-63 hold the
+// two halves of K for row / column lane & 31).  Lane l holds rows
+// 8j + 4(l >> 5) + i (j, i = 0..3) of column l & 31, element 4j + i.
+__device__ inline f32x16 mma32_k16(s16x8 a, s16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16((bf16x8)a, (bf16x8)b, c, 0, 0, 0);
 }
 
 __device__ inline unsigned pack_bf16x2(float lo, float hi)

@@ -92,6 +92,37 @@ def test_small_shapes_match_oracle(shape, kernel, dtype):
     assert err <= TOL[dtype], err
 
 
+# Queries 40x larger than the recipe's: the matrix-core kernels' softmax
+# shift (a Cauchy-Schwarz bound on the logits) then exceeds the largest logit
+# by several hundred in base-2 units, every weight underflows, and the group is
+# recomputed with the exact maximum.  Softmax is shift-invariant, so the result
+# must still match the oracle (and the log normaliser too).
+REDO = [
+    (2, 3, 24, 24, 16, 8, 3, 1),    # 32-query groups (one column tile, d = 16)
+    (1, 2, 20, 28, 16, 8, 3, 1),    # the same, ragged
+    (2, 3, 24, 24, 32, 8, 3, 1),    # d = 32
+    (2, 2, 24, 24, 16, 8, 3, 2),    # strided: 16-query groups
+    (1, 2, 36, 36, 32, 12, 3, 1),   # two column tiles
+    (1, 2, 64, 64, 16, 32, 3, 1),   # window wider than 32 columns
+]
+
+
+@pytest.mark.parametrize("shape", REDO, ids=lambda s: "x".join(map(str, s)))
+def test_shift_bound_overshoot_recomputes(shape):
+    B, heads, H, W, d, block, halo, stride = shape
+    say(f"case {shape} queries x40")
+    q, k, v, rh, rw = make_inputs(B, heads, H, W, d, block, halo, dtype="bf16", seed=7 + sum(shape))
+    q = (q.float() * 40.0).to(torch.bfloat16)
+    inp = (q, k, v, rh, rw)
+    dq, dk, dv, drh, drw = (t.to(DEV) for t in inp)
+    out, lse = halo_attn_fwd(dq, dk, dv, drh, drw, block, halo, stride, return_lse=True)
+    torch.cuda.synchronize()
+    want, want_lse = oracle.halo_attn_ref(*(f64(t) for t in inp), block, halo, stride, return_lse=True)
+    assert max_err(out, want) <= TOL["bf16"]
+    rel = np.abs(f64(lse) - want_lse) / np.maximum(1.0, np.abs(want_lse))
+    assert float(rel.max()) <= 4e-3
+
+
 # lse (log softmax normaliser per query): the matrix-core kernels sum the
 # bf16-rounded weights (relative error <= 2^-9 of the sum, so <= 2^-9 in the
 # log) after fp32 logits; the generic kernel sums fp32 weights.
