@@ -445,9 +445,9 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             // ---- relative logits of the 32 table rows, then the width terms
             const f32x16 gw = mma32_k16(tab32w, q32, zero16);
             const f32x16 gh = mma32_k16(tab32h, q32, zero16);
-    #pragma unroll
+#pragma unroll
             for (int j = 0; j < 4; ++j)
-    #pragma unroll
+#pragma unroll
                 for (int i = 0; i < 4; ++i) lds_st<float>(smem, scr32 + RS * (8 * j + 4 * g2 + i), gw[4 * j + i]);
             // width term of window column c = 8j + 4*g2 + i (j = 0, 1); rows
             // 16-31 of a score tile are the second window row: same columns
@@ -455,9 +455,9 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             f32x16 cinit;
             {
                 const unsigned a = scr32 + RS * (R - 1 - T.xl[0] + 4 * g2);
-    #pragma unroll
+#pragma unroll
                 for (int j = 0; j < 2; ++j)
-    #pragma unroll
+#pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int c = 8 * j + 4 * g2 + i;
                         const float val = lds_ld<float>(smem, a + RS * (8 * j + i));
@@ -472,7 +472,7 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 const float kn = __builtin_sqrtf(__builtin_bit_cast(float, kmax_bits[16 * (byy & 1) + g2])) *
                                  (1.f + 0x1p-20f);
                 s16x8 abound, aq;
-    #pragma unroll
+#pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float a = kn + tmax[8 * g2 + e];
                     abound[e] = (short)((__builtin_bit_cast(unsigned, a) + 0xffffu) >> 16);   // round up
@@ -483,9 +483,9 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             }
             // height terms alpha*G - mb -> scratch (after the width reads)
             const int sh = R - 1 - T.yl[0];
-    #pragma unroll
+#pragma unroll
             for (int j = 0; j < 4; ++j)
-    #pragma unroll
+#pragma unroll
                 for (int i = 0; i < 4; ++i)
                     lds_st<float>(smem, scr32 + RS * (8 * j + 4 * g2 + i), fmaf(gh[4 * j + i], alpha, -mb));
             const unsigned rh = scr32 + RS * sh;          // scratch of window row 0
@@ -528,7 +528,7 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 auto compute = [&](const Ops32& c) {
                     const f32x16 sc = mma32_k16(c.a, q32, cinit);
                     unsigned pw[8];
-    #pragma unroll
+#pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const float e = j < 2 ? c.c0 : c.c1;
                         pw[2 * j] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sc[4 * j], alpha, e)),
@@ -570,7 +570,7 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 for (int t = ts; t < thi; t += 2) {
                     const f32x16 sc = mma32_k16(lds_ld<s16x8>(smem, kl + rslot(t) * rowb_k), q32, cinit);
                     float m0 = sc[0], m1 = sc[8];
-    #pragma unroll
+#pragma unroll
                     for (int e = 1; e < 8; ++e) {
                         m0 = fmaxf(m0, sc[e]);
                         m1 = fmaxf(m1, sc[8 + e]);
@@ -584,7 +584,7 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                     M = fmaxf(a, b);
                 }
                 shift += M;
-    #pragma unroll
+#pragma unroll
                 for (int r2 = 0; r2 < 8; ++r2) {          // window rows 8*g2 .. +7 of the query
                     const unsigned a = rh + RS * (8 * g2 + r2);
                     lds_st<float>(smem, a, lds_ld<float>(smem, a) - M);
