@@ -62,32 +62,32 @@ MALL_BYTES = 256 * 2 ** 20     # Infinity Cache
 # bench reports traffic as null.
 MEASURED_TRAFFIC = {
     "fwd": {
-        "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 134575136, "read": 101020704, "write": 33554432,
-            "sources": "d9dedbfb07a9d3df"},
-        "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 146249950, "read": 104306910, "write": 41943040,
-            "sources": "d9dedbfb07a9d3df"},
-        "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 92518995, "read": 84130387, "write": 8388608,
-            "sources": "d9dedbfb07a9d3df"},
-        "large_bf16_128x128_d32_b12h3": {"bytes_per_launch": 280898145, "read": 213789281, "write": 67108864,
-            "sources": "d9dedbfb07a9d3df"},
-        "detection_bf16_64x64_d16_b32h3": {"bytes_per_launch": 33730035, "read": 25341427, "write": 8388608,
-            "sources": "d9dedbfb07a9d3df"},
-        "global_bf16_16x16_d16_b16h0": {"bytes_per_launch": 17137567, "read": 12943263, "write": 4194304,
-            "sources": "d9dedbfb07a9d3df"},
+        "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 134556787, "read": 101002355, "write": 33554432,
+            "sources": "4ff4300b2442fcc6"},
+        "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 146198277, "read": 104255237, "write": 41943040,
+            "sources": "4ff4300b2442fcc6"},
+        "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 92523239, "read": 84134631, "write": 8388608,
+            "sources": "4ff4300b2442fcc6"},
+        "large_bf16_128x128_d32_b12h3": {"bytes_per_launch": 280822198, "read": 213713334, "write": 67108864,
+            "sources": "4ff4300b2442fcc6"},
+        "detection_bf16_64x64_d16_b32h3": {"bytes_per_launch": 33730175, "read": 25341567, "write": 8388608,
+            "sources": "4ff4300b2442fcc6"},
+        "global_bf16_16x16_d16_b16h0": {"bytes_per_launch": 17119086, "read": 12924782, "write": 4194304,
+            "sources": "4ff4300b2442fcc6"},
     },
     # layer: summed over the call's kernels (to_q/to_kv, attention, to_out)
     "layer": {
-        "early_stage_bf16_64x64_d16_b8h3/nhwc": {"bytes_per_launch": 337295287, "read": 169523127,
-            "write": 167772160, "sources": "0356e31e946e3b5d"}
+        "early_stage_bf16_64x64_d16_b8h3/nhwc": {"bytes_per_launch": 337281703, "read": 169509494, "write": 167772209,
+            "sources": "4668607b6f28c8b6"},
     },
     # backward: summed over the call's kernels (strip kernel launches, table reduction)
     "bwd": {
-        "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 590653110, "read": 373628470, "write": 217024640,
-            "sources": "0c842c555e88797f"},
-        "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 504399861, "read": 313620213, "write": 190779648,
-            "sources": "0c842c555e88797f"},
-        "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 456748711, "read": 260247435, "write": 196501275,
-            "sources": "0c842c555e88797f"},
+        "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 590635834, "read": 373611194, "write": 217024640,
+            "sources": "0b600c6971720264"},
+        "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 504392789, "read": 313613141, "write": 190779648,
+            "sources": "0b600c6971720264"},
+        "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 456787748, "read": 260288730, "write": 196499017,
+            "sources": "0b600c6971720264"},
     },
 }
 
