@@ -71,8 +71,21 @@ def load() -> ctypes.CDLL:
     lib.halo_attn_last_error.restype = ctypes.c_char_p
     lib.halo_attn_abi_version.argtypes = []
     lib.halo_attn_abi_version.restype = i
+    lib.halo_attn_build_id.argtypes = []
+    lib.halo_attn_build_id.restype = ctypes.c_char_p
+    _check_build_id(lib)
     _lib = lib
     return lib
+
+
+def _check_build_id(lib) -> None:
+    """Warn when the library was built from other sources than those in csrc/."""
+    from . import build
+    built, here = lib.halo_attn_build_id().decode(), build.source_id()
+    if built != here:
+        import warnings
+        warnings.warn(f"{LIB_PATH} was built from sources {built}, csrc/ now holds {here}: rebuild "
+                      "(__graft_entry__.build())", RuntimeWarning, stacklevel=3)
 
 
 def last_error() -> str:

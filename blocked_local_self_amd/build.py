@@ -28,6 +28,19 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+def source_id() -> str:
+    """First 16 hex digits of SHA-256 over csrc/'s file names and contents
+    (name order): the identifier compiled into the library."""
+    import hashlib
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        if os.path.isfile(path):
+            h.update(os.path.basename(path).encode())
+            with open(path, "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 # Extra flags per source.  The matrix-core kernel keeps MFMA results in
 # ordinary VGPRs (no accumulator-register copies) and, having no NaN
 # semantics to preserve in its max reductions, skips NaN canonicalisation.
@@ -51,10 +64,11 @@ def build(verbose: bool = False, defines: tuple = (), out: str | None = None) ->
     os.makedirs(bdir, exist_ok=True)
     objs, logs = [], []
     procs = []
+    build_id = source_id()
     for src in sources():
         obj = os.path.join(bdir, os.path.basename(src) + ".o")
         cmd = [hipcc(), f"--offload-arch={ARCH}", *COMMON, "-I", INCLUDE, *[f"-D{d}" for d in defines],
-               *PER_FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
+               f'-DHALO_BUILD_ID="{build_id}"', *PER_FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
         procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
         objs.append(obj)
     for cmd, pr in procs:

@@ -124,6 +124,11 @@ const char* halo_attn_last_error(void) { return g_err; }
 
 int halo_attn_abi_version(void) { return HALO_ATTN_ABI_VERSION; }
 
+#ifndef HALO_BUILD_ID
+#define HALO_BUILD_ID "unknown"
+#endif
+const char* halo_attn_build_id(void) { return HALO_BUILD_ID; }
+
 int halo_attn_select_kernel(int d, int block, int halo, int query_stride, int dtype)
 {
     g_err[0] = 0;

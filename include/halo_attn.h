@@ -322,6 +322,14 @@ const char* halo_attn_last_error(void);
 /* HALO_ATTN_ABI_VERSION of the built library. */
 int halo_attn_abi_version(void);
 
+/* Identifier of the sources the library was built from: the first 16 hex
+ * digits of the SHA-256 over the names and contents of every file in the
+ * package's csrc/ directory, in name order ("unknown" when built without it).
+ * The Python binding compares it with the sources next to the library and
+ * warns when they differ (a library older than its sources).  Static string,
+ * owned by the library. */
+const char* halo_attn_build_id(void);
+
 #ifdef __cplusplus
 }
 #endif

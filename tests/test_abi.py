@@ -31,6 +31,13 @@ def test_abi_version(lib):
     assert f"#define HALO_ATTN_ABI_VERSION {lib.halo_attn_abi_version()}" in text
 
 
+def test_library_built_from_these_sources(lib):
+    """The identifier compiled into the library is the hash of csrc/ as it is
+    now: the library is not older than its sources."""
+    from blocked_local_self_amd import build
+    assert lib.halo_attn_build_id().decode() == build.source_id()
+
+
 def call(lib, *, q=1, k=1, v=1, rh=1, rw=1, out=1 << 40, B=1, heads=1, H=8, W=8, d=16, block=4,
          halo=1, stride=1, scale=0.25, dtype=1, kernel=0):
     # Fake, non-overlapping pointers: every call below must fail before the
