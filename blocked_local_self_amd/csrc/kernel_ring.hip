@@ -451,19 +451,19 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 for (int i = 0; i < 4; ++i) lds_st<float>(smem, scr32 + RS * (8 * j + 4 * g2 + i), gw[4 * j + i]);
             // width term of window column c = 8j + 4*g2 + i (j = 0, 1); rows
             // 16-31 of a score tile are the second window row: same columns
+            // Masked columns (off the image, c < clo or c >= chi, or past the
+            // window, c >= R) get the mask value in their scratch rows, which
+            // no other column of the query reads: the reads need no selects
             const int clo = g.halo - T.xb, chi = min(R, g.W - T.xb + g.halo);
+            const unsigned a0 = scr32 + RS * (R - 1 - T.xl[0]);     // row of column 0
+            for (int c = 0; c < clo; ++c) lds_st<float>(smem, a0 + RS * c, kMaskLogit);
+            for (int c = chi; c < 16; ++c) lds_st<float>(smem, a0 + RS * c, kMaskLogit);
             f32x16 cinit;
-            {
-                const unsigned a = scr32 + RS * (R - 1 - T.xl[0] + 4 * g2);
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int c = 8 * j + 4 * g2 + i;
-                        const float val = lds_ld<float>(smem, a + RS * (8 * j + i));
-                        cinit[4 * j + i] = cinit[8 + 4 * j + i] = (c >= clo && c < chi) ? val : kMaskLogit;
-                    }
-            }
+                for (int i = 0; i < 4; ++i)
+                    cinit[4 * j + i] = cinit[8 + 4 * j + i] = lds_ld<float>(smem, a0 + RS * (8 * j + 4 * g2 + i));
 
             // ---- softmax shift: the bound of the 16x16 path, for 32 queries in
             // one MFMA (a_c in all 32 rows, |q| as B; channels 8*g2..+7 lie in chunk g2)
@@ -523,9 +523,8 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             };
             f32x16 O, O2;                             // rows t and t+1 of each pair
             auto weighted_sum = [&]() {
-                O = zero16;
-                O2 = zero16;
-                auto compute = [&](const Ops32& c) {
+                // first: the pair's P.V products start the sums (no zeroed accumulators)
+                auto compute = [&](const Ops32& c, auto first) {
                     const f32x16 sc = mma32_k16(c.a, q32, cinit);
                     unsigned pw[8];
 #pragma unroll
@@ -538,25 +537,29 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                     }
                     // K order of B (per lane half): columns 4*g2+i, then 8+4*g2+i;
                     // the V^T operand was read in the same order
+                    constexpr bool F = decltype(first)::value;
                     O = mma32_k16(__builtin_bit_cast(s16x8, c.v0),
-                                  __builtin_bit_cast(s16x8, u32x4{pw[0], pw[1], pw[2], pw[3]}), O);
+                                  __builtin_bit_cast(s16x8, u32x4{pw[0], pw[1], pw[2], pw[3]}), F ? zero16 : O);
                     O2 = mma32_k16(__builtin_bit_cast(s16x8, c.v1),
-                                   __builtin_bit_cast(s16x8, u32x4{pw[4], pw[5], pw[6], pw[7]}), O2);
+                                   __builtin_bit_cast(s16x8, u32x4{pw[4], pw[5], pw[6], pw[7]}), F ? zero16 : O2);
                 };
-                Ops32 A = fetch(ts), B;
-                for (int t = ts;;) {
-                    B = fetch(t + 2 < thi ? t + 2 : t);
-                    __builtin_amdgcn_sched_barrier(0);
-                    compute(A);
-                    __builtin_amdgcn_sched_barrier(0);
-                    t += 2;
-                    if (t >= thi) break;
+                // pair ts always exists (the block's own rows are in the image)
+                Ops32 A = fetch(ts), B = fetch(ts + 2 < thi ? ts + 2 : ts);
+                __builtin_amdgcn_sched_barrier(0);
+                compute(A, std::true_type{});
+                __builtin_amdgcn_sched_barrier(0);
+                for (int t = ts + 2; t < thi;) {
                     A = fetch(t + 2 < thi ? t + 2 : t);
                     __builtin_amdgcn_sched_barrier(0);
-                    compute(B);
+                    compute(B, std::false_type{});
                     __builtin_amdgcn_sched_barrier(0);
                     t += 2;
                     if (t >= thi) break;
+                    B = fetch(t + 2 < thi ? t + 2 : t);
+                    __builtin_amdgcn_sched_barrier(0);
+                    compute(A, std::false_type{});
+                    __builtin_amdgcn_sched_barrier(0);
+                    t += 2;
                 }
                 O += O2;
             };
