@@ -239,6 +239,12 @@ void proj_out_kernel(const __bf16* __restrict__ attn, const __bf16* __restrict__
     const int o0 = slice * p.ns;
     const int ns = min(p.ns, Co - o0);                   // multiple of 16
     const unsigned pitch = (unsigned)p.pitch * 2;
+    // output staging (p.stage != 0): this wave's 32 x ns tile, row pitch spitch bytes
+    const unsigned spitch = 2u * ns + 16u;
+    const unsigned sbase = (unsigned)p.stage + (unsigned)wave * 32u * (2u * (unsigned)p.ns + 16u);
+    const int cpr = ns / 8;                              // 16-byte chunks per row (divides 64)
+    const int lrow = p.stage ? lane / cpr : 0, lchunk = p.stage ? lane - lrow * cpr : 0;
+    const int rstep = p.stage ? 64 / cpr : 1;
 
     stage_rows(smem, pitch, ns, inner, tid, [&](int row) { return w_o + (int64_t)(o0 + row) * inner; });
     __syncthreads();
@@ -284,9 +290,22 @@ void proj_out_kernel(const __bf16* __restrict__ attn, const __bf16* __restrict__
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 const int64_t pix = pb + 16 * tt + n;
+                const u32x2 w = u32x2{pack_bf16x2(acc[tt][0] + b0, acc[tt][1] + b1),
+                                      pack_bf16x2(acc[tt][2] + b2, acc[tt][3] + b3)};
+                if (p.stage)        // row 16 tt + n of the wave's tile, channels 16 ot + 4 g ..
+                    *reinterpret_cast<u32x2*>(smem + sbase + (16 * tt + n) * spitch + 2u * (16 * ot + 4 * g)) = w;
+                else if (pix < L.NPo)
+                    *reinterpret_cast<u32x2*>(y + pix * Co + o) = w;
+            }
+        }
+        if (p.stage) {
+            // whole rows out: lane -> (row lrow + rstep * it, 16-byte chunk lchunk).
+            // The tile was written by this wave; LDS runs one wave's accesses in order.
+            for (int r = lrow; r < 32; r += rstep) {
+                const int64_t pix = pb + r;
                 if (pix < L.NPo)
-                    *reinterpret_cast<u32x2*>(y + pix * Co + o) =
-                        u32x2{pack_bf16x2(acc[tt][0] + b0, acc[tt][1] + b1), pack_bf16x2(acc[tt][2] + b2, acc[tt][3] + b3)};
+                    *reinterpret_cast<u32x4*>(y + pix * Co + o0 + 8 * lchunk) =
+                        *reinterpret_cast<const u32x4*>(smem + sbase + r * spitch + 16u * lchunk);
             }
         }
 #pragma unroll
@@ -364,7 +383,10 @@ bool proj_out_mfma_supported(const LayerGeom& L, bool bf16)
 // chunk of 256 pixels, as many workgroups as the CUs hold at once (the
 // slices of one chunk sit next to each other in the XCD-grouped order, so
 // they share the chunk's pixels through one L2).
-static ProjPlan proj_plan(int nout, int kdim, int64_t npix)
+// out_stage: the output projection stages each wave's 32 x ns output tile in
+// LDS (row pitch ns*2 + 16 bytes) and writes whole pixel rows with 16-byte
+// stores, when a row's 16-byte chunks divide 64 lanes.
+static ProjPlan proj_plan(int nout, int kdim, int64_t npix, bool out_stage = false)
 {
     ProjPlan p{};
     p.pitch = kdim + 8;                                // 16 bytes of padding per row
@@ -375,6 +397,10 @@ static ProjPlan proj_plan(int nout, int kdim, int64_t npix)
     p.nslices = (nout + p.ns - 1) / p.ns;
     p.chunk = 256;                                     // pixels per chunk: 4 waves x 2 passes x 32
     p.lds_bytes = p.ns * p.pitch * 2;
+    if (out_stage && 64 % (p.ns / 8) == 0) {
+        p.stage = p.lds_bytes;                          // a multiple of 16: pitch*2 = 2*kdim + 16
+        p.lds_bytes += 4 * 32 * (p.ns * 2 + 16);
+    }
     const int64_t nchunks = (npix + p.chunk - 1) / p.chunk;
     const int per_cu = std::max(1, std::min(8, 160 * 1024 / std::max(p.lds_bytes, 1)));
     const int64_t slots = std::max<int64_t>(1, (int64_t)per_cu * device_info().cus / p.nslices);
@@ -449,7 +475,7 @@ hipError_t launch_proj_out(const void* attn, const void* w_o, const void* b_o, v
     LayerGeom L = L0;
     layer_fastdiv(L);
     if (mfma) {
-        const ProjPlan p = proj_plan(L.Cout, L.heads * L.d, L.NPo);
+        const ProjPlan p = proj_plan(L.Cout, L.heads * L.d, L.NPo, true);
         auto kern = pick_kc(L.heads * L.d / 32, [](auto kc) { return proj_out_kernel<decltype(kc)::value>; });
         const hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), p.lds_bytes);
         if (e != hipSuccess) return e;

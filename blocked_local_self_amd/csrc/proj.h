@@ -42,6 +42,7 @@ struct ProjPlan {
     int pitch;            // LDS weight row pitch, elements
     int chunk;            // pixels per workgroup
     int lds_bytes;
+    int stage;            // output projection: byte offset of the per-wave row staging (0: direct stores)
     int remap_xcd;
     int64_t nwg;
 };
