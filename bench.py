@@ -62,23 +62,23 @@ MALL_BYTES = 256 * 2 ** 20     # Infinity Cache
 # bench reports traffic as null.
 MEASURED_TRAFFIC = {
     "fwd": {
-        "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 134556787, "read": 101002355, "write": 33554432,
-            "sources": "4ff4300b2442fcc6"},
-        "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 146198277, "read": 104255237, "write": 41943040,
-            "sources": "4ff4300b2442fcc6"},
-        "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 92523239, "read": 84134631, "write": 8388608,
-            "sources": "4ff4300b2442fcc6"},
-        "large_bf16_128x128_d32_b12h3": {"bytes_per_launch": 280822198, "read": 213713334, "write": 67108864,
-            "sources": "4ff4300b2442fcc6"},
-        "detection_bf16_64x64_d16_b32h3": {"bytes_per_launch": 33730175, "read": 25341567, "write": 8388608,
-            "sources": "4ff4300b2442fcc6"},
-        "global_bf16_16x16_d16_b16h0": {"bytes_per_launch": 17119086, "read": 12924782, "write": 4194304,
-            "sources": "4ff4300b2442fcc6"},
+        "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 134553832, "read": 100999400, "write": 33554432,
+            "sources": "d57d55aa5ed9f9d1"},
+        "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 146213465, "read": 104270425, "write": 41943040,
+            "sources": "d57d55aa5ed9f9d1"},
+        "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 92521142, "read": 84132534, "write": 8388608,
+            "sources": "d57d55aa5ed9f9d1"},
+        "large_bf16_128x128_d32_b12h3": {"bytes_per_launch": 280846577, "read": 213737713, "write": 67108864,
+            "sources": "d57d55aa5ed9f9d1"},
+        "detection_bf16_64x64_d16_b32h3": {"bytes_per_launch": 33730206, "read": 25341598, "write": 8388608,
+            "sources": "d57d55aa5ed9f9d1"},
+        "global_bf16_16x16_d16_b16h0": {"bytes_per_launch": 17116085, "read": 12921781, "write": 4194304,
+            "sources": "d57d55aa5ed9f9d1"},
     },
     # layer: summed over the call's kernels (to_q/to_kv, attention, to_out)
     "layer": {
-        "early_stage_bf16_64x64_d16_b8h3/nhwc": {"bytes_per_launch": 337281703, "read": 169509494, "write": 167772209,
-            "sources": "4668607b6f28c8b6"},
+        "early_stage_bf16_64x64_d16_b8h3/nhwc": {"bytes_per_launch": 337282790, "read": 169510630, "write": 167772160,
+            "sources": "45b208855654c55d"},
     },
     # backward: summed over the call's kernels (strip kernel launches, table reduction)
     "bwd": {
