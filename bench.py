@@ -62,23 +62,23 @@ MALL_BYTES = 256 * 2 ** 20     # Infinity Cache
 # bench reports traffic as null.
 MEASURED_TRAFFIC = {
     "fwd": {
-        "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 134553832, "read": 100999400, "write": 33554432,
-            "sources": "d57d55aa5ed9f9d1"},
-        "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 146213465, "read": 104270425, "write": 41943040,
-            "sources": "d57d55aa5ed9f9d1"},
-        "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 92521142, "read": 84132534, "write": 8388608,
-            "sources": "d57d55aa5ed9f9d1"},
-        "large_bf16_128x128_d32_b12h3": {"bytes_per_launch": 280846577, "read": 213737713, "write": 67108864,
-            "sources": "d57d55aa5ed9f9d1"},
-        "detection_bf16_64x64_d16_b32h3": {"bytes_per_launch": 33730206, "read": 25341598, "write": 8388608,
-            "sources": "d57d55aa5ed9f9d1"},
-        "global_bf16_16x16_d16_b16h0": {"bytes_per_launch": 17116085, "read": 12921781, "write": 4194304,
-            "sources": "d57d55aa5ed9f9d1"},
+        "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 134553679, "read": 100999221, "write": 33554458,
+            "sources": "d13ee25021d0373b"},
+        "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 135613825, "read": 101010817, "write": 34603008,
+            "sources": "d13ee25021d0373b"},
+        "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 92520909, "read": 84132301, "write": 8388608,
+            "sources": "d13ee25021d0373b"},
+        "large_bf16_128x128_d32_b12h3": {"bytes_per_launch": 284424717, "read": 217315853, "write": 67108864,
+            "sources": "d13ee25021d0373b"},
+        "detection_bf16_64x64_d16_b32h3": {"bytes_per_launch": 33730060, "read": 25341452, "write": 8388608,
+            "sources": "d13ee25021d0373b"},
+        "global_bf16_16x16_d16_b16h0": {"bytes_per_launch": 17116037, "read": 12921733, "write": 4194304,
+            "sources": "d13ee25021d0373b"},
     },
     # layer: summed over the call's kernels (to_q/to_kv, attention, to_out)
     "layer": {
-        "early_stage_bf16_64x64_d16_b8h3/nhwc": {"bytes_per_launch": 337282790, "read": 169510630, "write": 167772160,
-            "sources": "45b208855654c55d"},
+        "early_stage_bf16_64x64_d16_b8h3/nhwc": {"bytes_per_launch": 337289341, "read": 169517178, "write": 167772163,
+            "sources": "b8e9245d8f3c28f3"},
     },
     # backward: summed over the call's kernels (strip kernel launches, table reduction)
     "bwd": {
