@@ -38,6 +38,15 @@ def test_library_built_from_these_sources(lib):
     assert lib.halo_attn_build_id().decode() == build.source_id()
 
 
+def test_stale_library_warns(lib, monkeypatch):
+    """A library built from other sources than csrc/ holds draws a warning
+    when the binding loads it."""
+    from blocked_local_self_amd import build
+    monkeypatch.setattr(build, "source_id", lambda: "0" * 16)
+    with pytest.warns(RuntimeWarning, match="rebuild"):
+        _native._check_build_id(lib)
+
+
 def call(lib, *, q=1, k=1, v=1, rh=1, rw=1, out=1 << 40, B=1, heads=1, H=8, W=8, d=16, block=4,
          halo=1, stride=1, scale=0.25, dtype=1, kernel=0):
     # Fake, non-overlapping pointers: every call below must fail before the
