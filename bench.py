@@ -62,23 +62,23 @@ MALL_BYTES = 256 * 2 ** 20     # Infinity Cache
 # bench reports traffic as null.
 MEASURED_TRAFFIC = {
     "fwd": {
-        "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 134553679, "read": 100999221, "write": 33554458,
-            "sources": "d13ee25021d0373b"},
-        "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 135613825, "read": 101010817, "write": 34603008,
-            "sources": "d13ee25021d0373b"},
-        "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 92520909, "read": 84132301, "write": 8388608,
-            "sources": "d13ee25021d0373b"},
-        "large_bf16_128x128_d32_b12h3": {"bytes_per_launch": 284424717, "read": 217315853, "write": 67108864,
-            "sources": "d13ee25021d0373b"},
-        "detection_bf16_64x64_d16_b32h3": {"bytes_per_launch": 33730060, "read": 25341452, "write": 8388608,
-            "sources": "d13ee25021d0373b"},
-        "global_bf16_16x16_d16_b16h0": {"bytes_per_launch": 17116037, "read": 12921733, "write": 4194304,
-            "sources": "d13ee25021d0373b"},
+        "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 134553827, "read": 100999395, "write": 33554432,
+            "sources": "d32fed82af16fc17"},
+        "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 135619439, "read": 101016431, "write": 34603008,
+            "sources": "d32fed82af16fc17"},
+        "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 92521159, "read": 84132551, "write": 8388608,
+            "sources": "d32fed82af16fc17"},
+        "large_bf16_128x128_d32_b12h3": {"bytes_per_launch": 280842865, "read": 213734001, "write": 67108864,
+            "sources": "d32fed82af16fc17"},
+        "detection_bf16_64x64_d16_b32h3": {"bytes_per_launch": 33730126, "read": 25341518, "write": 8388608,
+            "sources": "d32fed82af16fc17"},
+        "global_bf16_16x16_d16_b16h0": {"bytes_per_launch": 17116113, "read": 12921809, "write": 4194304,
+            "sources": "d32fed82af16fc17"},
     },
     # layer: summed over the call's kernels (to_q/to_kv, attention, to_out)
     "layer": {
-        "early_stage_bf16_64x64_d16_b8h3/nhwc": {"bytes_per_launch": 337289341, "read": 169517178, "write": 167772163,
-            "sources": "b8e9245d8f3c28f3"},
+        "early_stage_bf16_64x64_d16_b8h3/nhwc": {"bytes_per_launch": 337276140, "read": 169503980, "write": 167772160,
+            "sources": "db3f598f16960393"},
     },
     # backward: summed over the call's kernels (strip kernel launches, table reduction)
     "bwd": {
