@@ -95,8 +95,10 @@ MEASURED_TRAFFIC = {
 # Sources the timed kernels are built from, per pass (the traffic record of
 # a pass holds while these files are unchanged).
 KERNEL_SOURCES = {
-    "fwd": ["halo_common.h", "mfma_util.h", "kernel_ring.hip", "kernel_mfma.hip", "kernel_wide.hip"],
-    "layer": ["halo_common.h", "mfma_util.h", "kernel_ring.hip", "kernel_mfma.hip", "kernel_wide.hip", "proj.h",
+    "fwd": ["halo_common.h", "mfma_util.h", "kernel_tile.hip", "kernel_ring.hip", "kernel_mfma.hip",
+            "kernel_wide.hip"],
+    "layer": ["halo_common.h", "mfma_util.h", "kernel_tile.hip", "kernel_ring.hip", "kernel_mfma.hip",
+              "kernel_wide.hip", "proj.h",
               "kernel_proj.hip"],
     "bwd": ["halo_common.h", "mfma_util.h", "kernel_bwd_mfma.hip", "kernel_bwd_generic.hip"],
 }

@@ -32,7 +32,8 @@ VARIANTS = {"centred_offset": _native.HALO_CENTRED_OFFSET, "zero_pad": _native.H
             "centred_mask": _native.HALO_CENTRED_MASK, "half_split": _native.HALO_HALF_SPLIT}
 LAYOUTS = {"nhwc": _native.HALO_LAYOUT_NHWC, "blocked": _native.HALO_LAYOUT_BLOCKED}
 KERNELS = {"auto": _native.HALO_KERNEL_AUTO, "generic": _native.HALO_KERNEL_GENERIC,
-           "mfma": _native.HALO_KERNEL_MFMA, "mfma_strip": _native.HALO_KERNEL_MFMA_STRIP}
+           "mfma": _native.HALO_KERNEL_MFMA, "mfma_strip": _native.HALO_KERNEL_MFMA_STRIP,
+           "mfma_ring": _native.HALO_KERNEL_MFMA_RING}
 
 
 def _dtype_code(t) -> int:

@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(HERE, "libhaloattn.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "halo_attn.h")
 
 HALO_F32, HALO_BF16 = 0, 1
-HALO_KERNEL_AUTO, HALO_KERNEL_GENERIC, HALO_KERNEL_MFMA, HALO_KERNEL_MFMA_STRIP = 0, 1, 2, 3
+HALO_KERNEL_AUTO, HALO_KERNEL_GENERIC, HALO_KERNEL_MFMA, HALO_KERNEL_MFMA_STRIP, HALO_KERNEL_MFMA_RING = 0, 1, 2, 3, 4
 HALO_CENTRED_OFFSET, HALO_ZERO_PAD, HALO_CENTRED_MASK, HALO_HALF_SPLIT = 1, 2, 4, 8
 HALO_LAYOUT_NHWC, HALO_LAYOUT_BLOCKED = 0, 1
 STATUS = {0: "HALO_OK", -1: "HALO_ERR_NULL", -2: "HALO_ERR_SHAPE", -3: "HALO_ERR_DTYPE",

@@ -47,6 +47,7 @@ def source_id() -> str:
 PER_FILE_FLAGS = {
     "kernel_mfma.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
     "kernel_ring.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "kernel_tile.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
     "kernel_bwd_mfma.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
     "kernel_wide.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
 }

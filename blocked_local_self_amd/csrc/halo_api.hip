@@ -60,7 +60,7 @@ hipError_t launch_generic(const void* q, const void* k, const void* v, const voi
                           const void* rw, void* out, float* lse, const Geometry& g, bool bf16, hipStream_t st);
 bool mfma_supported(int d, int r, int block, int stride, bool bf16);
 hipError_t launch_mfma(const void* q, const void* k, const void* v, const void* rh,
-                       const void* rw, void* out, float* lse, const Geometry& g, bool force_strip,
+                       const void* rw, void* out, float* lse, const Geometry& g, int mode,
                        hipStream_t st);
 int64_t bwd_generic_workspace_floats(const Geometry& g);
 hipError_t launch_bwd_generic(const void* q, const void* k, const void* v, const void* rh, const void* rw,
@@ -217,7 +217,7 @@ int halo_attn_fwd_ex(const void* q, const void* k, const void* v,
 {
     g_err[0] = 0;
     if (kernel != HALO_KERNEL_AUTO && kernel != HALO_KERNEL_GENERIC && kernel != HALO_KERNEL_MFMA &&
-        kernel != HALO_KERNEL_MFMA_STRIP)
+        kernel != HALO_KERNEL_MFMA_STRIP && kernel != HALO_KERNEL_MFMA_RING)
         return fail(HALO_ERR_SHAPE, "kernel=%d is not a halo_kernel value", kernel);
     if (flags & ~(HALO_CENTRED_OFFSET | HALO_ZERO_PAD | HALO_CENTRED_MASK | HALO_HALF_SPLIT))
         return fail(HALO_ERR_SHAPE, "flags=%d has bits outside the halo_flags values", flags);
@@ -251,18 +251,20 @@ int halo_attn_fwd_ex(const void* q, const void* k, const void* v,
     // the variants run on the ring kernel and the generic kernel only
     const bool mfma_ok = halo::mfma_supported(d, r, block, query_stride, bf16) &&
                          (flags == 0 || halo::ring_supported(g));
-    if ((kernel == HALO_KERNEL_MFMA || kernel == HALO_KERNEL_MFMA_STRIP) && !mfma_ok)
+    const bool forced = kernel == HALO_KERNEL_MFMA || kernel == HALO_KERNEL_MFMA_STRIP ||
+                        kernel == HALO_KERNEL_MFMA_RING;
+    if (forced && !mfma_ok)
         return fail(HALO_ERR_UNSUPPORTED,
-                    "matrix-core kernel needs bf16, d in {16,32}, window side <= 32 "
-                    "(got dtype=%d d=%d r=%d flags=%d)", dtype, d, r, flags);
+                    "matrix-core kernel needs bf16, block %% 4 == 0, d in {16,32} with window side <= 32 "
+                    "or d = 16 with window side <= 40 (got dtype=%d d=%d block=%d r=%d flags=%d)",
+                    dtype, d, block, r, flags);
     if (kernel == HALO_KERNEL_MFMA_STRIP && flags)
         return fail(HALO_ERR_UNSUPPORTED, "the strip kernel runs the default semantics only (flags=%d)", flags);
 
     hipStream_t s = (hipStream_t)stream;
-    const bool use_mfma = kernel == HALO_KERNEL_MFMA || kernel == HALO_KERNEL_MFMA_STRIP ||
-                          (kernel == HALO_KERNEL_AUTO && mfma_ok);
-    const hipError_t e = use_mfma ? halo::launch_mfma(q, k, v, rel_h, rel_w, out, lse, g,
-                                                      kernel == HALO_KERNEL_MFMA_STRIP, s)
+    const bool use_mfma = forced || (kernel == HALO_KERNEL_AUTO && mfma_ok);
+    const int mode = kernel == HALO_KERNEL_MFMA_STRIP ? 1 : kernel == HALO_KERNEL_MFMA_RING ? 2 : 0;
+    const hipError_t e = use_mfma ? halo::launch_mfma(q, k, v, rel_h, rel_w, out, lse, g, mode, s)
                                   : halo::launch_generic(q, k, v, rel_h, rel_w, out, lse, g, bf16, s);
     if (e != hipSuccess)
         return fail(HALO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -324,7 +326,7 @@ int halo_attn_bwd_ex(const void* q, const void* k, const void* v,
     if (flags & ~(HALO_CENTRED_OFFSET | HALO_ZERO_PAD | HALO_CENTRED_MASK | HALO_HALF_SPLIT))
         return fail(HALO_ERR_SHAPE, "flags=%d has bits outside the halo_flags values", flags);
     if (kernel != HALO_KERNEL_AUTO && kernel != HALO_KERNEL_GENERIC && kernel != HALO_KERNEL_MFMA &&
-        kernel != HALO_KERNEL_MFMA_STRIP)
+        kernel != HALO_KERNEL_MFMA_STRIP && kernel != HALO_KERNEL_MFMA_RING)
         return fail(HALO_ERR_SHAPE, "kernel=%d is not a halo_kernel value", kernel);
     halo::Geometry g;
     bool empty = false;
@@ -375,7 +377,8 @@ int halo_attn_bwd_ex(const void* q, const void* k, const void* v,
                 return fail(HALO_ERR_ALIAS, "two outputs (or an output and the workspace) overlap");
     }
     const bool mfma_ok = halo::bwd_mfma_supported(g, bf16);
-    if ((kernel == HALO_KERNEL_MFMA || kernel == HALO_KERNEL_MFMA_STRIP) && !mfma_ok)
+    if ((kernel == HALO_KERNEL_MFMA || kernel == HALO_KERNEL_MFMA_STRIP || kernel == HALO_KERNEL_MFMA_RING) &&
+        !mfma_ok)
         return fail(HALO_ERR_UNSUPPORTED,
                     "matrix-core backward needs bf16, d in {16,32}, window side <= 16, blocks that tile "
                     "the image, and (block/stride)^2 in {16, 64} (got dtype=%d d=%d r=%d block=%d H=%d W=%d)",
@@ -396,7 +399,7 @@ int halo_attn_bwd_ex(const void* q, const void* k, const void* v,
             float* wl = reinterpret_cast<float*>(base + w.lse);
             // the variants run on the persistent kernel or the generic one
             e = (flags == 0 || halo::ring_supported(g))
-                    ? halo::launch_mfma(q, k, v, rel_h, rel_w, base + w.out, wl, g, false, s)
+                    ? halo::launch_mfma(q, k, v, rel_h, rel_w, base + w.out, wl, g, 0, s)
                     : halo::launch_generic(q, k, v, rel_h, rel_w, base + w.out, wl, g, bf16, s);
         }
         if (e == hipSuccess)

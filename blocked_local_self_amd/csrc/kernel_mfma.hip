@@ -461,10 +461,20 @@ hipError_t launch_wide(const void* q, const void* k, const void* v, const void* 
 // Matrix-core launch: the persistent ring kernel when it covers the shape,
 // the streaming kernel for windows wider than 32 columns, else the strip
 // kernel.  force_strip selects the strip kernel regardless.
+bool tile_supported(const Geometry& g);
+hipError_t launch_tile(const void* q, const void* k, const void* v, const void* rh, const void* rw,
+                       void* out, float* lse, const Geometry& g, hipStream_t st);
+
+// mode: 0 the fastest matrix-core kernel for the shape (16-query tile
+// kernel, else the persistent ring kernel, the streaming wide kernel, the
+// strip kernel); 1 the strip kernel; 2 the ring kernel where it applies
+// (else as 0 without the tile kernel).
 hipError_t launch_mfma(const void* q, const void* k, const void* v, const void* rh,
-                       const void* rw, void* out, float* lse, const Geometry& g, bool force_strip,
+                       const void* rw, void* out, float* lse, const Geometry& g, int mode,
                        hipStream_t st)
 {
+    const bool force_strip = mode == 1;
+    if (mode == 0 && tile_supported(g)) return launch_tile(q, k, v, rh, rw, out, lse, g, st);
     if (!force_strip && ring_supported(g)) return launch_ring(q, k, v, rh, rw, out, lse, g, st);
     if (!force_strip && g.flags == 0 && wide_supported(g, true)) return launch_wide(q, k, v, rh, rw, out, lse, g, st);
     const bool wide = g.r > 16;

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define HALO_ATTN_ABI_VERSION 3
+#define HALO_ATTN_ABI_VERSION 4
 
 typedef enum halo_dtype {
     HALO_F32 = 0,
@@ -59,17 +59,23 @@ typedef enum halo_dtype {
 
 /* Which implementation runs.  AUTO picks the fastest one that supports the
  * arguments.  GENERIC is the fp32-vector kernel for every supported shape.
- * MFMA is the fused matrix-core path (bf16, d in {16, 32}, block % 4 == 0,
- * window side r <= 32): a persistent kernel that walks each image down its
- * block rows with the window rows in an LDS ring when the ring fits in LDS,
- * else a kernel that stages each strip of blocks separately.  MFMA_STRIP
- * forces the latter (for cross-checking).  Asking for an MFMA path with other
+ * MFMA is the fused matrix-core path: bf16, block % 4 == 0, and either
+ * d in {16, 32} with window side r <= 32 or d == 16 with r <= 40.  Inside
+ * it the forward picks, by shape: a persistent kernel of 16-query groups
+ * (d in {16, 32} with r <= 16, d == 32 with r <= 20; default semantics); a
+ * persistent kernel that walks each image down its block rows with the
+ * window rows in an LDS ring (r <= 32, and every semantic variant); a
+ * streaming kernel for windows of 33..40 columns (d == 16); or a kernel that
+ * stages each strip of blocks separately.  MFMA_STRIP forces the last one
+ * and MFMA_RING the ring kernel where it applies (for cross-checking; the
+ * backward treats both as MFMA).  Asking for a matrix-core path with other
  * arguments returns HALO_ERR_UNSUPPORTED. */
 typedef enum halo_kernel {
     HALO_KERNEL_AUTO = 0,
     HALO_KERNEL_GENERIC = 1,
     HALO_KERNEL_MFMA = 2,
-    HALO_KERNEL_MFMA_STRIP = 3
+    HALO_KERNEL_MFMA_STRIP = 3,
+    HALO_KERNEL_MFMA_RING = 4
 } halo_kernel;
 
 /* Semantic variants (OR-ed into `flags` of halo_attn_fwd_ex), for matching
