@@ -3,7 +3,12 @@
 
 One step = one halo_attn_fwd launch over one full batch of the workload (all
 of the method's steps run inside that launch); with --pass bwd, one
-halo_attn_bwd call (all of its kernels) over one full batch.  Inputs are seeded synthetic
+halo_attn_bwd call (all of its kernels) over one full batch.  Without
+--workload the forward line is the headline: the large shape (B=8, 8 heads,
+128x128, d=32, block 12, halo 3: 18x18 windows), the largest that fits one
+GPU, timed with --steps/--warmup, plus a ``per_config`` block with the same
+fields for the other HaloNet-stage shapes (early, mid, strided), measured
+first with --per-config-steps launches each.  Inputs are seeded synthetic
 tensors already resident in HBM; several independent input/output sets are
 rotated so the working set exceeds the 256 MB Infinity Cache and every step
 reads HBM.  Prints ONE JSON line (rank 0):
@@ -120,8 +125,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=2000,
                     help="untimed launches first (the GPU clocks need ~0.1 s of load to ramp up)")
-    ap.add_argument("--workload", default=None, help="workload name (default: the early-stage shape)")
-    ap.add_argument("--kernel", default="auto", choices=["auto", "generic", "mfma"])
+    ap.add_argument("--workload", default=None,
+                    help="workload name (default: the forward headline is the large 18x18-window shape, "
+                         "reported with every HaloNet-stage shape; the backward and layer passes default "
+                         "to the early-stage shape)")
+    ap.add_argument("--kernel", default="auto", choices=["auto", "generic", "mfma", "mfma_ring", "mfma_strip"])
     ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd", "layer"],
                     help="forward (the headline), backward pass, or the whole layer with its projections")
     ap.add_argument("--layout", default="nhwc", choices=["nhwc", "blocked"],
@@ -131,6 +139,8 @@ def parse():
     ap.add_argument("--sets", type=int, default=0, help="rotated input sets (0: enough to exceed the MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU-oracle sample time")
+    ap.add_argument("--per-config-steps", type=int, default=500,
+                    help="timed launches per stage shape in the per_config block (after as many warm-up launches)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run --steps plain device copies of MIB MiB each "
                          "(the reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -155,6 +165,17 @@ def bwd_flops(wl):
 
 def bwd_alg_bytes(wl):
     return wl.elem_bytes * wl.d * wl.B * wl.heads * (2 * wl.Ho * wl.Wo + 5 * wl.H * wl.W)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(wl, inputs_cpu, target_s, dout_cpu=None):
@@ -199,7 +220,7 @@ def cpu_baseline(wl, inputs_cpu, target_s, dout_cpu=None):
     return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{what} of {wl.name} x {passes} pass(es), {'backward' if g is not None else 'forward'}, "
                       f"fp64, {t:.2f} s",
-            "seconds": round(t, 3), "tokens_per_s": round(tokens / t, 1)}
+            "seconds": round(t, 3), "tokens_per_s": round(tokens / t, 1), "cpu_model": cpu_model()}
 
 
 def layer_flops(wl, C, Co):
@@ -230,7 +251,7 @@ def cpu_baseline_layer(wl, xs, target_s):
         images += sl.shape[0]
         n = min(wl.B, 2 * n)
     return {"value": round(per_image * images / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{images} images of {wl.name} (layer: projections + attention, C={C}), fp64, {t:.2f} s",
             "seconds": round(t, 3), "tokens_per_s": round(wl.tokens / wl.B * images / t, 1)}
 
@@ -241,7 +262,7 @@ def run_layer(args):
                                         layer_workspace_bytes, workloads, _native, LAYOUTS)
     from blocked_local_self_amd.inputs import make_layer_inputs, nhwc_to_layout
 
-    wl = workloads.get(args.workload or workloads.BENCH_WORKLOAD)
+    wl = workloads.get(args.workload or workloads.PASS_WORKLOAD)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     C = Co = wl.heads * wl.d
@@ -355,10 +376,35 @@ def main():
         run_layer(args)
         return
     import torch
+    from blocked_local_self_amd import workloads
+    if args.which == "bwd" or args.workload or args.variants:
+        wl = workloads.get(args.workload or (workloads.PASS_WORKLOAD if args.which == "bwd"
+                                             else workloads.BENCH_WORKLOAD))
+        print(json.dumps(run_op(args, wl, args.steps, args.warmup, args.cpu_seconds)), flush=True)
+        return
+    # the forward headline: every HaloNet-stage shape first (each with its
+    # own warm-up), then the headline shape with the requested steps
+    per_config = {}
+    for name in workloads.STAGE_WORKLOADS:
+        if name == workloads.BENCH_WORKLOAD:
+            continue
+        e = run_op(args, workloads.get(name), args.per_config_steps, args.per_config_steps,
+                   min(5.0, args.cpu_seconds))
+        per_config[name] = {k_: e[k_] for k_ in ("value", "unit", "ms_per_step", "tokens_per_s", "dtype", "steps",
+                                                  "warmup", "roofline", "cpu_baseline", "config") if k_ in e}
+        torch.cuda.empty_cache()
+    line = run_op(args, workloads.get(workloads.BENCH_WORKLOAD), args.steps, args.warmup, args.cpu_seconds)
+    line["per_config"] = per_config
+    print(json.dumps(line), flush=True)
+
+
+def run_op(args, wl, steps, warmup, cpu_seconds):
+    """Time `steps` launches of the forward (or backward) on workload wl after
+    `warmup` untimed ones; returns the JSON line's fields."""
+    import torch
     from blocked_local_self_amd import halo_attn_fwd, halo_attn_bwd, bwd_workspace_bytes, workloads
     from blocked_local_self_amd.inputs import make_workload_inputs, make_grad_output
 
-    wl = workloads.get(args.workload or workloads.BENCH_WORKLOAD)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     in_bytes = 3 * wl.elem_bytes * wl.B * wl.heads * wl.H * wl.W * wl.d
@@ -429,20 +475,20 @@ def main():
         if st:
             _native.check(st)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = ev0.elapsed_time(ev1)
-    ms = gpu_ms / args.steps
+    ms = gpu_ms / steps
     flops = bwd_flops(wl) if bwd else wl.flops
     alg_bytes = bwd_alg_bytes(wl) if bwd else wl.alg_bytes
     tflops = flops / (ms * 1e-3) / 1e12
@@ -461,8 +507,8 @@ def main():
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -486,8 +532,10 @@ def main():
         },
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, inputs0_cpu, args.cpu_seconds, dout0_cpu)
-    print(json.dumps(line), flush=True)
+        line["cpu_baseline"] = cpu_baseline(wl, inputs0_cpu, cpu_seconds, dout0_cpu)
+    return line
+
+
 
 
 if __name__ == "__main__":

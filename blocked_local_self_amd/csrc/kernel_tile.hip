@@ -582,24 +582,36 @@ void tile_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             };
             constexpr int NT = NQ * NCT;               // tiles
             constexpr int NS = (NT + 1) / 2;           // P.V steps
-            struct Ops {
-                FragT a0, a1;
-                u32x4 vw[D / 16];
+            // software pipeline over the fully unrolled steps: the K
+            // fragments of step s+2 and the V fragments of step s+1 are
+            // loaded, and the scores of step s+1 computed, before step s's
+            // exponentials, so a wave overlaps its own MFMA and LDS latency
+            FragT kf[NS][2];
+            u32x4 vf[NS][D / 16];
+            f32x4 sc[NS][QT][2];
+            auto kfetch = [&](int st) {
+                const int t0 = 2 * st, t1 = 2 * st + 1 < NT ? 2 * st + 1 : 2 * st;
+                kf[st][0] = lds_load<FragT>(smem, kl + qslot(t0 / NCT) * rowb + 4u * (t0 % NCT) * PIXB);
+                kf[st][1] = lds_load<FragT>(smem, kl + qslot(t1 / NCT) * rowb + 4u * (t1 % NCT) * PIXB);
             };
-            auto fetch = [&](int s) {
-                Ops o;
-                const int t0 = 2 * s, t1 = 2 * s + 1 < NT ? 2 * s + 1 : 2 * s;
-                const int q0 = t0 / NCT, c0 = t0 % NCT, q1 = t1 / NCT, c1 = t1 % NCT;
-                const unsigned s0 = qslot(q0), s1 = qslot(q1);
-                o.a0 = lds_load<FragT>(smem, kl + s0 * rowb + 4u * c0 * PIXB);
-                o.a1 = lds_load<FragT>(smem, kl + s1 * rowb + 4u * c1 * PIXB);
+            auto vfetch = [&](int st) {
+                const int t0 = 2 * st, t1 = 2 * st + 1 < NT ? 2 * st + 1 : 2 * st;
+                const unsigned s0 = qslot(t0 / NCT), s1 = qslot(t1 / NCT);
 #pragma unroll
                 for (int mt = 0; mt < D / 16; ++mt) {
-                    const u32x2 x0 = lds_load<u32x2>(smem, vl + 2u * (s0 * SWv + (unsigned)(mt * 16 * CP + 4 * c0)));
-                    const u32x2 x1 = lds_load<u32x2>(smem, vl + 2u * (s1 * SWv + (unsigned)(mt * 16 * CP + 4 * c1)));
-                    o.vw[mt] = u32x4{x0[0], x0[1], x1[0], x1[1]};
+                    const u32x2 x0 = lds_load<u32x2>(smem, vl + 2u * (s0 * SWv + (unsigned)(mt * 16 * CP + 4 * (t0 % NCT))));
+                    const u32x2 x1 = lds_load<u32x2>(smem, vl + 2u * (s1 * SWv + (unsigned)(mt * 16 * CP + 4 * (t1 % NCT))));
+                    vf[st][mt] = u32x4{x0[0], x0[1], x1[0], x1[1]};
                 }
-                return o;
+            };
+            auto scores = [&](int st) {
+                const int t0 = 2 * st, t1 = 2 * st + 1;
+#pragma unroll
+                for (int u = 0; u < QT; ++u) {
+                    if (u == 1 && !G.two) continue;
+                    sc[st][u][0] = Frag<D>::mma(kf[st][0], qf[u], cinit[u][t0 % NCT]);
+                    if (t1 < NT) sc[st][u][1] = Frag<D>::mma(kf[st][1], qf[u], cinit[u][t1 % NCT]);
+                }
             };
             auto weighted_sum = [&]() {
 #pragma unroll
@@ -608,26 +620,30 @@ void tile_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
                     for (int mt = 0; mt < D / 16; ++mt) O[u][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
-                Ops A = fetch(0), B;
+                kfetch(0);
+                if (NS > 1) kfetch(1);
+                vfetch(0);
+                scores(0);
 #pragma unroll
-                for (int s = 0; s < NS; ++s) {
-                    if (s + 1 < NS) B = fetch(s + 1);
+                for (int st = 0; st < NS; ++st) {
+                    if (st + 2 < NS) kfetch(st + 2);
+                    if (st + 1 < NS) vfetch(st + 1);
+                    if (st + 1 < NS) scores(st + 1);
                     __builtin_amdgcn_sched_barrier(0);
-                    const int t0 = 2 * s, t1 = 2 * s + 1;
+                    const int t0 = 2 * st, t1 = 2 * st + 1;
 #pragma unroll
                     for (int u = 0; u < QT; ++u) {
                         if (u == 1 && !G.two) continue;
-                        const u32x2 p0 = probs(Frag<D>::mma(A.a0, qf[u], cinit[u][t0 % NCT]), hq[u][t0 / NCT]);
+                        const u32x2 p0 = probs(sc[st][u][0], hq[u][t0 / NCT]);
                         u32x2 p1 = u32x2{0u, 0u};
-                        if (t1 < NT) p1 = probs(Frag<D>::mma(A.a1, qf[u], cinit[u][t1 % NCT]), hq[u][t1 / NCT]);
+                        if (t1 < NT) p1 = probs(sc[st][u][1], hq[u][t1 / NCT]);
                         const s16x8 pf = __builtin_bit_cast(s16x8, u32x4{p0[0], p0[1], p1[0], p1[1]});
 #pragma unroll
                         for (int mt = 0; mt < D / 16; ++mt)
-                            O[u][mt] = mma_k32(__builtin_bit_cast(s16x8, A.vw[mt]), pf, O[u][mt]);
+                            O[u][mt] = mma_k32(__builtin_bit_cast(s16x8, vf[st][mt]), pf, O[u][mt]);
                         L[u] = mma_k32(ones, pf, L[u]);
                     }
                     __builtin_amdgcn_sched_barrier(0);
-                    A = B;
                 }
             };
             auto exact_shift = [&]() {

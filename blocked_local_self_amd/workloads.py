@@ -96,8 +96,14 @@ WORKLOADS = {
     )
 }
 
-# Workload timed by the benchmark: the HaloNet early-stage shape.
-BENCH_WORKLOAD = "early_stage_bf16_64x64_d16_b8h3"
+# Workload of the benchmark's headline line: the largest single-GPU shape
+# (18x18 windows on 128x128 maps).
+BENCH_WORKLOAD = "large_bf16_128x128_d32_b12h3"
+# The HaloNet-stage shapes the headline line also reports, one entry each.
+STAGE_WORKLOADS = ("early_stage_bf16_64x64_d16_b8h3", "mid_stage_bf16_32x32_d32_b8h3",
+                   "strided_bf16_64x64_d16_b8h3_s2", "large_bf16_128x128_d32_b12h3")
+# Default workload of the backward and whole-layer passes.
+PASS_WORKLOAD = "early_stage_bf16_64x64_d16_b8h3"
 
 
 def get(name: str) -> Workload:
