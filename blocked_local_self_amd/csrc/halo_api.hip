@@ -168,6 +168,9 @@ int check_sizes(int B, int heads, int H, int W, int d, int block, int halo, int 
         return fail(HALO_ERR_SHAPE, "tensor too large (%.3g elements, limit 1e18)", nelem);
     if (nblk >= 2147483648.0)
         return fail(HALO_ERR_SHAPE, "%.0f blocks exceed the 2^31 grid limit", nblk);
+    // pixel indices inside one (batch, head) image are 32-bit in the kernels
+    if ((double)H * W >= 2147483648.0)
+        return fail(HALO_ERR_SHAPE, "H*W=%.0f pixels per image reach the 2^31 limit", (double)H * W);
     g.BH = (int64_t)B * heads; g.H = H; g.W = W;
     g.Ho = H / query_stride; g.Wo = W / query_stride;
     g.nbh = nbh; g.nbw = nbw;

@@ -236,11 +236,16 @@ void tile_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     {
         const int lo = -g.halo;
         const int total = R * ng2 * CPP;
-        for (int e = tid; e < total; e += kThreads) {
-            u32x4 kk[2], vv[2];
+        // two items per thread in flight: both loads issued before the stores
+        for (int e = tid; e < total; e += 2 * kThreads) {
+            u32x4 kk[2], vv[2], kk2[2], vv2[2];
             const Item it = item_of(e);
+            const bool second = e + kThreads < total;
+            const Item it2 = item_of(second ? e + kThreads : e);
             load_item(it, lo, kk, vv);
+            if (second) load_item(it2, lo, kk2, vv2);
             store_item(it, lo, kk, vv, kmax_bits);
+            if (second) store_item(it2, lo, kk2, vv2, kmax_bits);
         }
     }
     __syncthreads();
@@ -783,10 +788,12 @@ static TilePlan tile_plan(const Geometry& g, int pc, int nct, int qt, int waves,
     p.midstage = mid ? 1 : 0;
     p.ring = rup(mid ? g.r + g.block : g.r, pc == 4 ? 4 : 2);
     const int over = std::max(0, (nbx - 1) * g.block + nct * pc - p.SWv);   // pixels read past a row
-    // V^T channel pitch: >= ring*SWv + over-read, = 4 (mod 64) dwords so the
-    // 16 channels of a fragment read land in distinct banks
+    // V^T channel pitch: >= ring*SWv + over-read, = 4 (mod 8) dwords: the 16
+    // channels of a fragment read then start 4*odd dwords apart, i.e. in 16
+    // distinct 4-dword bank groups of the 64 banks, and the two lane halves
+    // (rows one slot = SWv/2 = 2 mod 4 dwords apart) take the other halves
     p.CP = rup(p.ring * p.SWv + over, 2);
-    while ((p.CP / 2) % 64 != 4 || p.CP % 2) ++p.CP;
+    while ((p.CP / 2) % 8 != 4 || p.CP % 2) ++p.CP;
     const int side = g.block / g.stride;
     p.tiles = (side * side + 15) / 16;
     p.groups = (p.tiles + qt - 1) / qt;

@@ -117,8 +117,9 @@ typedef enum halo_status {
  *   pointers are then not inspected); 1 <= d <= 128; block >= 1;
  *   0 <= halo; r = block + 2*halo <= 256; query_stride >= 1 with
  *   block % query_stride == 0, H % query_stride == 0, W % query_stride == 0;
- *   B*heads*H*W*d < 10^18 and the number of blocks B*heads*ceil(H/block)*
- *   ceil(W/block) < 2^31.  scale must be finite (else HALO_ERR_SHAPE); pass
+ *   B*heads*H*W*d < 10^18, H*W < 2^31 (pixel indices inside one image are
+ *   32-bit) and the number of blocks B*heads*ceil(H/block)*ceil(W/block)
+ *   < 2^31.  scale must be finite (else HALO_ERR_SHAPE); pass
  *   d^-0.5 to follow the HaloAttention module.
  * kernel: a halo_kernel value (else HALO_ERR_SHAPE).
  */

@@ -67,6 +67,9 @@ def call(lib, *, q=1, k=1, v=1, rh=1, rw=1, out=1 << 40, B=1, heads=1, H=8, W=8,
     (dict(kernel=2, dtype=0), -4), (dict(kernel=2, d=64), -4), (dict(kernel=2, block=6), -4),
     (dict(kernel=2, block=8, halo=17), -4), (dict(kernel=2, block=8, halo=13, d=32), -4),
     (dict(B=1 << 30, heads=1 << 30, H=1 << 15, W=1 << 15), -2),
+    # 46341^2 >= 2^31 pixels in one image: the kernels' 32-bit pixel indices
+    # would wrap (d = 1 keeps every other size check satisfied)
+    (dict(H=46341, W=46341, d=1), -2),
 ])
 def test_invalid_arguments_rejected_on_host(lib, kw, status):
     assert call(lib, **kw) == status

@@ -48,7 +48,7 @@ P1_CASES = [
     (7, 11, 4, 2, 1, 1),
     (12, 8, 4, 4, 1, 4),    # stride = block
     (4, 4, 2, 3, 2, 1),     # ragged, window covers image
-    (11, 12, 6, 3, 0, 3),
+    (12, 12, 6, 3, 0, 3),   # h = 0 with stride 3 (= block): one query per block
 ]
 
 

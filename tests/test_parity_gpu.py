@@ -212,9 +212,14 @@ def test_workload_full_size(name):
     assert np.abs(g).max() <= float(v.abs().max()) + TOL[wl.dtype]
 
 
-@pytest.mark.parametrize("name", ["early_stage_bf16_64x64_d16_b8h3", "tiny_fp32_16x16_d16_b4h1"])
+@pytest.mark.parametrize("name", ["early_stage_bf16_64x64_d16_b8h3", "mid_stage_bf16_32x32_d32_b8h3",
+                                  "strided_bf16_64x64_d16_b8h3_s2", "large_bf16_128x128_d32_b12h3",
+                                  "tiny_fp32_16x16_d16_b4h1"])
 def test_workload_generic_kernel_agrees(name):
+    # every slice of the full-size workload against the independent fp32
+    # vector kernel (the oracle checks only sampled slices at this size)
     wl = workloads.get(name)
+    say(f"workload {name}: generic kernel vs default")
     inp = make_workload_inputs(wl, seed=1)
     a = f64(run(inp, wl.block, wl.halo, wl.stride, "generic"))
     b = f64(run(inp, wl.block, wl.halo, wl.stride, "auto"))
