@@ -55,6 +55,10 @@ def load() -> ctypes.CDLL:
     lib.halo_attn_bwd_kernel.restype = i
     lib.halo_attn_bwd.argtypes = [vp] * 14 + [sz] + [i] * 8 + [f, i, vp]
     lib.halo_attn_bwd.restype = i
+    lib.halo_attn_bwd_noalloc.argtypes = [vp] * 13 + [i] * 8 + [f, i, vp]
+    lib.halo_attn_bwd_noalloc.restype = i
+    lib.halo_attn_noalloc_scratch_bytes.argtypes = []
+    lib.halo_attn_noalloc_scratch_bytes.restype = ctypes.c_longlong
     lib.halo_attn_bwd_workspace_bytes.argtypes = [i] * 9
     lib.halo_attn_bwd_workspace_bytes.restype = ctypes.c_longlong
     lib.halo_attn_layer_proj_in.argtypes = [vp] * 6 + [i] * 9 + [vp]

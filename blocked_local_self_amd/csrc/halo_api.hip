@@ -448,6 +448,77 @@ int halo_attn_bwd(const void* q, const void* k, const void* v,
 
 }  // extern "C"
 
+// ------------------------------------------------- allocation-free backward
+
+// The backward's workspace for callers that cannot allocate: one array per
+// GPU, held for the life of the process.  Its device address is taken once
+// per device (hipGetSymbolAddress, with that device current) and cached;
+// host code never passes the array's own name to a kernel.
+static constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+// Address of `scratch` on the current device, or nullptr with the HIP error
+// in `err`.
+void* scratch_ptr(int& dev, hipError_t& err)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* ptrs[kMaxDevices] = {};
+    err = hipGetDevice(&dev);
+    if (err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) {
+        err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (ptrs[dev] == nullptr) {
+        void* p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return nullptr;
+        ptrs[dev] = p;
+    }
+    err = hipSuccess;
+    return ptrs[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+long long halo_attn_noalloc_scratch_bytes(void) { return (long long)kNoAllocScratchBytes; }
+
+int halo_attn_bwd_noalloc(const void* q, const void* k, const void* v,
+                          const void* rel_h, const void* rel_w,
+                          const void* out, const void* dout, const float* lse,
+                          void* dq, void* dk, void* dv, float* drel_h, float* drel_w,
+                          int B, int heads, int H, int W, int d,
+                          int block, int halo, int query_stride,
+                          float scale, int dtype, void* stream)
+{
+    g_err[0] = 0;
+    halo::Geometry g;
+    bool empty = false;
+    int st = check_sizes(B, heads, H, W, d, block, halo, query_stride, scale, dtype, g, empty);
+    if (st) return st;
+    const size_t need = empty ? 0 : bwd_ws_bytes(g, dtype == HALO_BF16);
+    if (need > kNoAllocScratchBytes)
+        return fail(HALO_ERR_WORKSPACE,
+                    "this call needs %zu bytes of workspace; the library's static scratch holds %zu "
+                    "(use halo_attn_bwd with a caller workspace, or split the batch)",
+                    need, kNoAllocScratchBytes);
+    int dev = 0;
+    hipError_t e = hipSuccess;
+    void* ws = scratch_ptr(dev, e);
+    if (ws == nullptr) return fail(HALO_ERR_HIP, "static scratch of device %d: %s", dev, hipGetErrorString(e));
+    return halo_attn_bwd_ex(q, k, v, rel_h, rel_w, out, dout, lse, dq, dk, dv, drel_h, drel_w, ws,
+                            kNoAllocScratchBytes, B, heads, H, W, d, block, halo, query_stride, scale, dtype, 0,
+                            HALO_KERNEL_AUTO, stream);
+}
+
+}  // extern "C"
+
 // ------------------------------------------------------------------ the layer
 
 namespace {

@@ -244,6 +244,32 @@ int halo_attn_bwd(const void* q, const void* k, const void* v,
                   int block, int halo, int query_stride,
                   float scale, int dtype, void* stream);
 
+/*
+ * halo_attn_bwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight training loops, harnesses that forbid hipMalloc):
+ * the same operation, arguments and results as halo_attn_bwd without the
+ * workspace arguments.  The workspace is a static array the library holds on
+ * every GPU it runs on, halo_attn_noalloc_scratch_bytes() bytes (64 MiB),
+ * kept until the process ends; its address is looked up once per device.
+ * A call whose workspace (halo_attn_bwd_workspace_bytes) exceeds it returns
+ * HALO_ERR_WORKSPACE before any launch (split the batch, or use
+ * halo_attn_bwd).  The call allocates nothing and calls no allocating
+ * routine.  Every call on one GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (other streams, other host threads) race and
+ * must be serialised by the caller.  The array keeps the last call's
+ * contents; the backward reads none of it before writing it.
+ */
+int halo_attn_bwd_noalloc(const void* q, const void* k, const void* v,
+                          const void* rel_h, const void* rel_w,
+                          const void* out, const void* dout, const float* lse,
+                          void* dq, void* dk, void* dv, float* drel_h, float* drel_w,
+                          int B, int heads, int H, int W, int d,
+                          int block, int halo, int query_stride,
+                          float scale, int dtype, void* stream);
+
+/* Bytes of the static workspace halo_attn_bwd_noalloc uses (host-only). */
+long long halo_attn_noalloc_scratch_bytes(void);
+
 /* Host-only query: workspace bytes halo_attn_bwd needs for these sizes
  * (0 when a size is zero), or a negative status for invalid arguments. */
 long long halo_attn_bwd_workspace_bytes(int B, int heads, int H, int W, int d,

@@ -193,3 +193,13 @@ def test_layer_workspace_query():
     assert layer_workspace_bytes(0, 64, 64, 8, 16) == 0
     with pytest.raises(HaloError):
         layer_workspace_bytes(1, 8, 8, 2, 16, 3)
+
+
+def test_noalloc_backward_rejects_oversized_calls_on_host(lib):
+    # the early-stage shape needs ~270 MB of workspace, more than the static
+    # scratch: refused before any HIP call (fake pointers are never touched)
+    fake = [ctypes.c_void_p((i + 1) << 32) for i in range(13)]
+    assert lib.halo_attn_noalloc_scratch_bytes() == 64 << 20
+    st = lib.halo_attn_bwd_noalloc(*fake, 32, 8, 64, 64, 16, 8, 3, 1, 0.25, 1, None)
+    assert st == -7
+    assert "static scratch" in _native.last_error()
