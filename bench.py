@@ -62,23 +62,20 @@ MALL_BYTES = 256 * 2 ** 20     # Infinity Cache
 # HBM bytes per launch of the dominant kernel, per workload: rocprofv3 --pmc
 # FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by the ratio of
 # known bytes to the same counter's reading for a plain device copy
-# (--copy-calibration).  A record holds only for the kernel sources it was
-# measured on (``sources`` = kernel_source_hash() at the time); otherwise the
+# (--copy-calibration).  A record holds only for the kernel it was measured
+# on (forward: ``kernel`` = the launched kernel's name) and that kernel's
+# sources at the time (``sources`` = kernel_source_hash()); otherwise the
 # bench reports traffic as null.
 MEASURED_TRAFFIC = {
     "fwd": {
-        "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 134553827, "read": 100999395, "write": 33554432,
-            "sources": "d32fed82af16fc17"},
-        "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 135619439, "read": 101016431, "write": 34603008,
-            "sources": "d32fed82af16fc17"},
-        "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 92521159, "read": 84132551, "write": 8388608,
-            "sources": "d32fed82af16fc17"},
-        "large_bf16_128x128_d32_b12h3": {"bytes_per_launch": 280842865, "read": 213734001, "write": 67108864,
-            "sources": "d32fed82af16fc17"},
-        "detection_bf16_64x64_d16_b32h3": {"bytes_per_launch": 33730126, "read": 25341518, "write": 8388608,
-            "sources": "d32fed82af16fc17"},
-        "global_bf16_16x16_d16_b16h0": {"bytes_per_launch": 17116113, "read": 12921809, "write": 4194304,
-            "sources": "d32fed82af16fc17"},
+        "large_bf16_128x128_d32_b12h3": {"bytes_per_launch": 273837727, "read": 206728863, "write": 67108864,
+            "kernel": "tile", "sources": "009aae16d7d0099b"},
+        "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 92519208, "read": 84130600, "write": 8388608,
+            "kernel": "ring", "sources": "30cafffd6e32feaa"},
+        "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 134551698, "read": 100997215, "write": 33554483,
+            "kernel": "ring", "sources": "30cafffd6e32feaa"},
+        "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 135619038, "read": 101016030, "write": 34603008,
+            "kernel": "ring", "sources": "30cafffd6e32feaa"},
     },
     # layer: summed over the call's kernels (to_q/to_kv, attention, to_out)
     "layer": {
@@ -100,8 +97,13 @@ MEASURED_TRAFFIC = {
 # Sources the timed kernels are built from, per pass (the traffic record of
 # a pass holds while these files are unchanged).
 KERNEL_SOURCES = {
-    "fwd": ["halo_common.h", "mfma_util.h", "kernel_tile.hip", "kernel_ring.hip", "kernel_mfma.hip",
-            "kernel_wide.hip"],
+    # forward: per kernel (the record also names the kernel, so a change of
+    # kernel selection voids it too)
+    "fwd:tile": ["halo_common.h", "mfma_util.h", "kernel_tile.hip"],
+    "fwd:ring": ["halo_common.h", "mfma_util.h", "kernel_ring.hip"],
+    "fwd:wide": ["halo_common.h", "mfma_util.h", "kernel_wide.hip"],
+    "fwd:strip": ["halo_common.h", "mfma_util.h", "kernel_mfma.hip"],
+    "fwd:generic": ["halo_common.h", "kernel_generic.hip"],
     "layer": ["halo_common.h", "mfma_util.h", "kernel_tile.hip", "kernel_ring.hip", "kernel_mfma.hip",
               "kernel_wide.hip", "proj.h",
               "kernel_proj.hip"],
@@ -498,9 +500,16 @@ def run_op(args, wl, steps, warmup, cpu_seconds):
     mfma_peak = MFMA_PEAK_TFLOPS[wl.dtype]
     mfma_bound = flops / (mfma_peak * 1e12) > alg_bytes / (HBM_PEAK_GBS * 1e9)
 
-    src_hash = kernel_source_hash(args.which)
+    if bwd:
+        used = None
+        src_hash = kernel_source_hash("bwd")
+    else:
+        used = _native.fwd_kernel_name(wl.B, wl.heads, wl.H, wl.W, wl.d, wl.block, wl.halo, wl.stride, dcode,
+                                       flags, KERNELS[args.kernel])
+        src_hash = kernel_source_hash(f"fwd:{used}")
     rec = None if variants else MEASURED_TRAFFIC[args.which].get(wl.name)
-    traffic = rec["bytes_per_launch"] if rec and rec["sources"] == src_hash else None
+    valid = rec is not None and rec["sources"] == src_hash and rec.get("kernel") == used
+    traffic = rec["bytes_per_launch"] if valid else None
 
     line = {
         "metric": METRIC_BWD if bwd else METRIC,
@@ -515,7 +524,8 @@ def run_op(args, wl, steps, warmup, cpu_seconds):
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic",
-        "config": {**wl.describe(), "pass": args.which, "kernel": args.kernel, "rotated_input_sets": nsets,
+        "config": {**wl.describe(), "pass": args.which, "kernel": args.kernel,
+                   **({"kernel_used": used} if used else {}), "rotated_input_sets": nsets,
                    **({"variants": list(variants)} if variants else {})},
         "tokens_per_s": round(wl.tokens / (ms * 1e-3), 1),
         "wall_s_timed_region": round(wall, 4),

@@ -69,6 +69,8 @@ def load() -> ctypes.CDLL:
     lib.halo_attn_layer_workspace_bytes.restype = ctypes.c_longlong
     lib.halo_attn_layer_fwd.argtypes = [vp] * 9 + [sz] + [i] * 10 + [f, i, i, vp]
     lib.halo_attn_layer_fwd.restype = i
+    lib.halo_attn_fwd_kernel_name.argtypes = [i] * 11
+    lib.halo_attn_fwd_kernel_name.restype = ctypes.c_char_p
     lib.halo_attn_select_kernel.argtypes = [i] * 5
     lib.halo_attn_select_kernel.restype = i
     lib.halo_attn_last_error.argtypes = []
@@ -90,6 +92,14 @@ def _check_build_id(lib) -> None:
         import warnings
         warnings.warn(f"{LIB_PATH} was built from sources {built}, csrc/ now holds {here}: rebuild "
                       "(__graft_entry__.build())", RuntimeWarning, stacklevel=3)
+
+
+def fwd_kernel_name(B, heads, H, W, d, block, halo, stride, dtype, flags=0, kernel=HALO_KERNEL_AUTO) -> str:
+    """The forward kernel halo_attn_fwd_ex runs for these arguments (queries the device)."""
+    name = load().halo_attn_fwd_kernel_name(B, heads, H, W, d, block, halo, stride, dtype, flags, kernel)
+    if name is None:
+        raise ValueError(f"halo_attn_fwd_kernel_name: {last_error()}")
+    return name.decode()
 
 
 def last_error() -> str:

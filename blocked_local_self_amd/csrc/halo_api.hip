@@ -62,6 +62,7 @@ bool mfma_supported(int d, int r, int block, int stride, bool bf16);
 hipError_t launch_mfma(const void* q, const void* k, const void* v, const void* rh,
                        const void* rw, void* out, float* lse, const Geometry& g, int mode,
                        hipStream_t st);
+MfmaKernel mfma_select(const Geometry& g, int mode);
 int64_t bwd_generic_workspace_floats(const Geometry& g);
 hipError_t launch_bwd_generic(const void* q, const void* k, const void* v, const void* rh, const void* rw,
                               const void* out, const void* dout, const float* lse,
@@ -208,9 +209,68 @@ size_t bwd_ws_bytes(const halo::Geometry& g, bool bf16)
     return std::max(gen, mfma_ws(g).total);
 }
 
+// Validates a forward call's kernel, flags and sizes into g.
+int fwd_geometry(int B, int heads, int H, int W, int d, int block, int halo, int query_stride, float scale,
+                 int dtype, int flags, int kernel, halo::Geometry& g, bool& empty)
+{
+    if (kernel != HALO_KERNEL_AUTO && kernel != HALO_KERNEL_GENERIC && kernel != HALO_KERNEL_MFMA &&
+        kernel != HALO_KERNEL_MFMA_STRIP && kernel != HALO_KERNEL_MFMA_RING)
+        return fail(HALO_ERR_SHAPE, "kernel=%d is not a halo_kernel value", kernel);
+    if (flags & ~(HALO_CENTRED_OFFSET | HALO_ZERO_PAD | HALO_CENTRED_MASK | HALO_HALF_SPLIT))
+        return fail(HALO_ERR_SHAPE, "flags=%d has bits outside the halo_flags values", flags);
+    const int st = check_sizes(B, heads, H, W, d, block, halo, query_stride, scale, dtype, g, empty);
+    if (st) return st;
+    g.flags = flags;
+    if (flags & HALO_CENTRED_OFFSET) g.c0 = g.r - 1;
+    return HALO_OK;
+}
+
+// The forward kernel of a call: mode >= 0 runs the matrix-core launcher in
+// that mode (0 the fastest kernel for the shape, 1 the strip kernel, 2 the
+// ring kernel), -1 the generic kernel.
+int fwd_choice(const halo::Geometry& g, bool bf16, int kernel, int& mode)
+{
+    // the variants run on the ring kernel and the generic kernel only
+    const bool mfma_ok = halo::mfma_supported(g.d, g.r, g.block, g.stride, bf16) &&
+                         (g.flags == 0 || halo::ring_supported(g));
+    const bool forced = kernel == HALO_KERNEL_MFMA || kernel == HALO_KERNEL_MFMA_STRIP ||
+                        kernel == HALO_KERNEL_MFMA_RING;
+    if (forced && !mfma_ok)
+        return fail(HALO_ERR_UNSUPPORTED,
+                    "matrix-core kernel needs bf16, block %% 4 == 0, d in {16,32} with window side <= 32 "
+                    "or d = 16 with window side <= 40 (got bf16=%d d=%d block=%d r=%d flags=%d)",
+                    (int)bf16, g.d, g.block, g.r, g.flags);
+    if (kernel == HALO_KERNEL_MFMA_STRIP && g.flags)
+        return fail(HALO_ERR_UNSUPPORTED, "the strip kernel runs the default semantics only (flags=%d)", g.flags);
+    const bool use_mfma = forced || (kernel == HALO_KERNEL_AUTO && mfma_ok);
+    mode = !use_mfma ? -1 : kernel == HALO_KERNEL_MFMA_STRIP ? 1 : kernel == HALO_KERNEL_MFMA_RING ? 2 : 0;
+    return HALO_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+const char* halo_attn_fwd_kernel_name(int B, int heads, int H, int W, int d, int block, int halo,
+                                      int query_stride, int dtype, int flags, int kernel)
+{
+    g_err[0] = 0;
+    halo::Geometry g;
+    bool empty = false;
+    if (fwd_geometry(B, heads, H, W, d, block, halo, query_stride, 1.0f, dtype, flags, kernel, g, empty))
+        return nullptr;
+    if (empty) return "none";
+    int mode = 0;
+    if (fwd_choice(g, dtype == HALO_BF16, kernel, mode)) return nullptr;
+    if (mode < 0) return "generic";
+    switch (halo::mfma_select(g, mode)) {
+    case halo::MfmaKernel::tile: return "tile";
+    case halo::MfmaKernel::ring: return "ring";
+    case halo::MfmaKernel::wide: return "wide";
+    case halo::MfmaKernel::strip: return "strip";
+    }
+    return "strip";
+}
 
 int halo_attn_fwd_ex(const void* q, const void* k, const void* v,
                      const void* rel_h, const void* rel_w, void* out, float* lse,
@@ -219,17 +279,10 @@ int halo_attn_fwd_ex(const void* q, const void* k, const void* v,
                      float scale, int dtype, int flags, int kernel, void* stream)
 {
     g_err[0] = 0;
-    if (kernel != HALO_KERNEL_AUTO && kernel != HALO_KERNEL_GENERIC && kernel != HALO_KERNEL_MFMA &&
-        kernel != HALO_KERNEL_MFMA_STRIP && kernel != HALO_KERNEL_MFMA_RING)
-        return fail(HALO_ERR_SHAPE, "kernel=%d is not a halo_kernel value", kernel);
-    if (flags & ~(HALO_CENTRED_OFFSET | HALO_ZERO_PAD | HALO_CENTRED_MASK | HALO_HALF_SPLIT))
-        return fail(HALO_ERR_SHAPE, "flags=%d has bits outside the halo_flags values", flags);
     halo::Geometry g;
     bool empty = false;
-    int st = check_sizes(B, heads, H, W, d, block, halo, query_stride, scale, dtype, g, empty);
+    int st = fwd_geometry(B, heads, H, W, d, block, halo, query_stride, scale, dtype, flags, kernel, g, empty);
     if (st) return st;
-    g.flags = flags;
-    if (flags & HALO_CENTRED_OFFSET) g.c0 = g.r - 1;
     if (empty) return HALO_OK;   // nothing to do
 
     if (!q || !k || !v || !rel_h || !rel_w || !out)
@@ -251,24 +304,12 @@ int halo_attn_fwd_ex(const void* q, const void* k, const void* v,
         return fail(HALO_ERR_ALIAS, "lse overlaps an input tensor or out");
 
     const bool bf16 = dtype == HALO_BF16;
-    // the variants run on the ring kernel and the generic kernel only
-    const bool mfma_ok = halo::mfma_supported(d, r, block, query_stride, bf16) &&
-                         (flags == 0 || halo::ring_supported(g));
-    const bool forced = kernel == HALO_KERNEL_MFMA || kernel == HALO_KERNEL_MFMA_STRIP ||
-                        kernel == HALO_KERNEL_MFMA_RING;
-    if (forced && !mfma_ok)
-        return fail(HALO_ERR_UNSUPPORTED,
-                    "matrix-core kernel needs bf16, block %% 4 == 0, d in {16,32} with window side <= 32 "
-                    "or d = 16 with window side <= 40 (got dtype=%d d=%d block=%d r=%d flags=%d)",
-                    dtype, d, block, r, flags);
-    if (kernel == HALO_KERNEL_MFMA_STRIP && flags)
-        return fail(HALO_ERR_UNSUPPORTED, "the strip kernel runs the default semantics only (flags=%d)", flags);
-
+    int mode = 0;
+    st = fwd_choice(g, bf16, kernel, mode);
+    if (st) return st;
     hipStream_t s = (hipStream_t)stream;
-    const bool use_mfma = forced || (kernel == HALO_KERNEL_AUTO && mfma_ok);
-    const int mode = kernel == HALO_KERNEL_MFMA_STRIP ? 1 : kernel == HALO_KERNEL_MFMA_RING ? 2 : 0;
-    const hipError_t e = use_mfma ? halo::launch_mfma(q, k, v, rel_h, rel_w, out, lse, g, mode, s)
-                                  : halo::launch_generic(q, k, v, rel_h, rel_w, out, lse, g, bf16, s);
+    const hipError_t e = mode >= 0 ? halo::launch_mfma(q, k, v, rel_h, rel_w, out, lse, g, mode, s)
+                                   : halo::launch_generic(q, k, v, rel_h, rel_w, out, lse, g, bf16, s);
     if (e != hipSuccess)
         return fail(HALO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return HALO_OK;

@@ -33,6 +33,11 @@ constexpr int kFlagZeroPad = 2;         // off-image window positions are zero k
 constexpr int kFlagCentredMask = 4;     // only keys within h rows and columns of the query
 constexpr int kFlagHalfSplit = 8;       // height table on channels [0, d/2), width on [d/2, d)
 
+// The matrix-core forward kernels (selection in kernel_mfma.hip): the
+// 16-query tile kernel, the persistent ring kernel, the streaming kernel for
+// windows wider than 32 columns, the strip kernel.
+enum class MfmaKernel { tile, ring, wide, strip };
+
 // Attributes of the current device, queried through HIP once per device and
 // cached (kernel planning runs on every call and must not pay for API calls).
 struct DeviceInfo {

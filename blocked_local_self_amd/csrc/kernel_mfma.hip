@@ -469,14 +469,25 @@ hipError_t launch_tile(const void* q, const void* k, const void* v, const void* 
 // kernel, else the persistent ring kernel, the streaming wide kernel, the
 // strip kernel); 1 the strip kernel; 2 the ring kernel where it applies
 // (else as 0 without the tile kernel).
+MfmaKernel mfma_select(const Geometry& g, int mode)
+{
+    const bool force_strip = mode == 1;
+    if (mode == 0 && tile_supported(g)) return MfmaKernel::tile;
+    if (!force_strip && ring_supported(g)) return MfmaKernel::ring;
+    if (!force_strip && g.flags == 0 && wide_supported(g, true)) return MfmaKernel::wide;
+    return MfmaKernel::strip;
+}
+
 hipError_t launch_mfma(const void* q, const void* k, const void* v, const void* rh,
                        const void* rw, void* out, float* lse, const Geometry& g, int mode,
                        hipStream_t st)
 {
-    const bool force_strip = mode == 1;
-    if (mode == 0 && tile_supported(g)) return launch_tile(q, k, v, rh, rw, out, lse, g, st);
-    if (!force_strip && ring_supported(g)) return launch_ring(q, k, v, rh, rw, out, lse, g, st);
-    if (!force_strip && g.flags == 0 && wide_supported(g, true)) return launch_wide(q, k, v, rh, rw, out, lse, g, st);
+    switch (mfma_select(g, mode)) {
+    case MfmaKernel::tile: return launch_tile(q, k, v, rh, rw, out, lse, g, st);
+    case MfmaKernel::ring: return launch_ring(q, k, v, rh, rw, out, lse, g, st);
+    case MfmaKernel::wide: return launch_wide(q, k, v, rh, rw, out, lse, g, st);
+    case MfmaKernel::strip: break;
+    }
     const bool wide = g.r > 16;
     if (g.d == 16 && g.r > 32) return launch_dn<16, 3>(q, k, v, rh, rw, out, lse, g, st);
     if (g.d == 16) return wide ? launch_dn<16, 2>(q, k, v, rh, rw, out, lse, g, st)

@@ -348,6 +348,20 @@ int halo_attn_layer_fwd(const void* x, const void* w_q, const void* w_kv,
  * status if the arguments are invalid.  Touches no device. */
 int halo_attn_select_kernel(int d, int block, int halo, int query_stride, int dtype);
 
+/*
+ * Which forward kernel halo_attn_fwd_ex would run for these arguments:
+ * "generic", "tile" (16-query tiles of 4x4 key patches), "ring" (the
+ * persistent block-row ring), "wide" (windows wider than 32 columns),
+ * "strip", or "none" when a size is zero (nothing to compute).  The
+ * arguments mean what they mean there (the scale plays no part).  Queries
+ * the current device's compute-unit count and LDS limit, which the
+ * matrix-core plans depend on; launches nothing.  The string is static.
+ * Invalid arguments: NULL, with halo_attn_last_error() telling why.
+ */
+const char* halo_attn_fwd_kernel_name(int B, int heads, int H, int W, int d,
+                                      int block, int halo, int query_stride,
+                                      int dtype, int flags, int kernel);
+
 /* Message for the last non-zero status returned on this thread ("" if none).
  * The pointer stays valid until the next call on this thread. */
 const char* halo_attn_last_error(void);

@@ -102,6 +102,20 @@ def test_kernel_selection():
         select_kernel(16, 4, 1, 3, "bf16")
 
 
+def test_kernel_name_query_on_the_host():
+    # answers that need no device: the generic kernel (fp32), nothing to compute, invalid arguments
+    assert _native.fwd_kernel_name(1, 2, 16, 16, 16, 4, 1, 1, _native.HALO_F32) == "generic"
+    assert _native.fwd_kernel_name(1, 2, 16, 16, 16, 4, 1, 1, _native.HALO_BF16,
+                                   kernel=_native.HALO_KERNEL_GENERIC) == "generic"
+    assert _native.fwd_kernel_name(0, 2, 16, 16, 16, 4, 1, 1, _native.HALO_BF16) == "none"
+    with pytest.raises(ValueError, match="query_stride"):
+        _native.fwd_kernel_name(1, 2, 16, 16, 16, 4, 1, 3, _native.HALO_BF16)
+    with pytest.raises(ValueError, match="matrix-core"):
+        _native.fwd_kernel_name(1, 2, 16, 16, 16, 4, 1, 1, _native.HALO_F32, kernel=_native.HALO_KERNEL_MFMA)
+    with pytest.raises(ValueError, match="halo_kernel"):
+        _native.fwd_kernel_name(1, 2, 16, 16, 16, 4, 1, 1, _native.HALO_BF16, kernel=9)
+
+
 def test_python_wrapper_validates_before_the_library():
     import torch
     from blocked_local_self_amd import halo_attn_fwd

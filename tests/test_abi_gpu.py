@@ -58,3 +58,22 @@ def test_halo_attn_fwd_symbol_matches_oracle(case):
     want = oracle.halo_attn_ref(*(t.double().numpy() for t in inp), block, halo, stride)
     err = float(np.abs(got - want).max())
     assert err <= tol, err
+
+
+@pytest.mark.gpu
+def test_kernel_name_query_names_the_launched_kernels():
+    """The kernels the query names for the stage shapes (the benchmark reports
+    them and keys its traffic records on them)."""
+    from blocked_local_self_amd import workloads
+    name = lambda wl, kernel=_native.HALO_KERNEL_AUTO: _native.fwd_kernel_name(
+        wl.B, wl.heads, wl.H, wl.W, wl.d, wl.block, wl.halo, wl.stride,
+        _native.HALO_BF16 if wl.dtype == "bf16" else _native.HALO_F32, kernel=kernel)
+    get = workloads.get
+    assert name(get("large_bf16_128x128_d32_b12h3")) == "tile"
+    assert name(get("large_bf16_128x128_d32_b12h3"), _native.HALO_KERNEL_MFMA_RING) == "ring"
+    assert name(get("large_bf16_128x128_d32_b12h3"), _native.HALO_KERNEL_MFMA_STRIP) == "strip"
+    for wl in ("early_stage_bf16_64x64_d16_b8h3", "mid_stage_bf16_32x32_d32_b8h3",
+               "strided_bf16_64x64_d16_b8h3_s2"):
+        assert name(get(wl)) == "ring", wl
+    assert name(get("detection_bf16_64x64_d16_b32h3")) == "wide"
+    assert name(get("tiny_fp32_16x16_d16_b4h1")) == "generic"
