@@ -79,6 +79,11 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
                            float* part_kv, float* part_rel, const Geometry& g, hipStream_t st);
 hipError_t launch_rel_reduce(const float* part, int64_t nrows, float* part2, float* drh, float* drw,
                              const Geometry& g, hipStream_t st);
+bool bwd_tile_supported(const Geometry& g, bool bf16);
+int64_t bwd_tile_rel_rows(const Geometry& g);
+hipError_t launch_bwd_tile(const void* q, const void* k, const void* v, const void* rh, const void* rw,
+                           const void* out, const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           float* dsum, float* part_rel, const Geometry& g, hipStream_t st);
 }  // namespace halo
 
 namespace {
@@ -202,11 +207,44 @@ MfmaWs mfma_ws(const halo::Geometry& g)
     return w;
 }
 
+// Workspace of the 16-query tile backward: D = dout.out per query, one
+// table-gradient partial per block, the reduction's first level, then the
+// forward's lse and out when the caller does not pass them.
+struct TileWs {
+    size_t dsum, rel, rel2, lse, out, total;
+};
+TileWs tile_ws(const halo::Geometry& g)
+{
+    TileWs w;
+    const int64_t rows = halo::bwd_tile_rel_rows(g);
+    const int64_t e2 = 2 * (int64_t)(2 * g.r - 1) * g.d;
+    const int64_t nq = g.BH * g.Ho * g.Wo;
+    w.dsum = 0;
+    w.rel = align256(w.dsum + (size_t)nq * 4);
+    w.rel2 = align256(w.rel + (size_t)(rows * e2) * 4);
+    w.lse = align256(w.rel2 + (size_t)(halo::bwd_rel_chunks(rows) * e2) * 4);
+    w.out = align256(w.lse + (size_t)nq * 4);
+    w.total = align256(w.out + (size_t)(nq * g.d) * 2);
+    return w;
+}
+
+// The matrix-core backward of a shape: 1 the strip kernel (windows of at
+// most 16 columns over whole blocks), 2 the 16-query tile kernels, 0 none.
+int bwd_mfma_path(const halo::Geometry& g, bool bf16)
+{
+    if (halo::bwd_mfma_supported(g, bf16)) return 1;
+    if (halo::bwd_tile_supported(g, bf16)) return 2;
+    return 0;
+}
+
 size_t bwd_ws_bytes(const halo::Geometry& g, bool bf16)
 {
     const size_t gen = (size_t)halo::bwd_generic_workspace_floats(g) * 4;
-    if (!halo::bwd_mfma_supported(g, bf16)) return gen;
-    return std::max(gen, mfma_ws(g).total);
+    switch (bwd_mfma_path(g, bf16)) {
+    case 1: return std::max(gen, mfma_ws(g).total);
+    case 2: return std::max(gen, tile_ws(g).total);
+    default: return gen;
+    }
 }
 
 // Validates a forward call's kernel, flags and sizes into g.
@@ -420,17 +458,40 @@ int halo_attn_bwd_ex(const void* q, const void* k, const void* v,
             if (overlaps(outs[a], outsz[a], outs[b], outsz[b]))
                 return fail(HALO_ERR_ALIAS, "two outputs (or an output and the workspace) overlap");
     }
-    const bool mfma_ok = halo::bwd_mfma_supported(g, bf16);
+    const bool aligned = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)dout | (uintptr_t)dq |
+                          (uintptr_t)dk | (uintptr_t)dv | (uintptr_t)(out ? out : q)) % 16 == 0;
+    const int path = aligned ? bwd_mfma_path(g, bf16) : 0;
     if ((kernel == HALO_KERNEL_MFMA || kernel == HALO_KERNEL_MFMA_STRIP || kernel == HALO_KERNEL_MFMA_RING) &&
-        !mfma_ok)
+        path == 0)
         return fail(HALO_ERR_UNSUPPORTED,
-                    "matrix-core backward needs bf16, d in {16,32}, window side <= 16, blocks that tile "
-                    "the image, and (block/stride)^2 in {16, 64} (got dtype=%d d=%d r=%d block=%d H=%d W=%d)",
-                    dtype, d, r, block, H, W);
+                    "matrix-core backward needs bf16, the default semantics, d in {16,32}, 16-byte aligned "
+                    "tensors, and a window side <= 32 with block <= 16 (got dtype=%d d=%d r=%d block=%d "
+                    "flags=%d)", dtype, d, r, block, flags);
     hipError_t e;
-    if (kernel == HALO_KERNEL_GENERIC || !mfma_ok) {
+    if (kernel == HALO_KERNEL_GENERIC || path == 0) {
         e = halo::launch_bwd_generic(q, k, v, rel_h, rel_w, out, dout, lse, dq, dk, dv, drel_h, drel_w,
                                      workspace, g, bf16, s);
+    } else if (path == 2) {
+        const TileWs w = tile_ws(g);
+        unsigned char* base = static_cast<unsigned char*>(workspace);
+        const void* fo = out;
+        const float* fl = lse;
+        e = hipSuccess;
+        if (lse == nullptr) {   // the forward's out and lse, recomputed into the workspace
+            fo = base + w.out;
+            fl = reinterpret_cast<float*>(base + w.lse);
+            float* wl = reinterpret_cast<float*>(base + w.lse);
+            e = halo::mfma_supported(d, r, block, query_stride, bf16)
+                    ? halo::launch_mfma(q, k, v, rel_h, rel_w, base + w.out, wl, g, 0, s)
+                    : halo::launch_generic(q, k, v, rel_h, rel_w, base + w.out, wl, g, bf16, s);
+        }
+        float* rel = reinterpret_cast<float*>(base + w.rel);
+        if (e == hipSuccess)
+            e = halo::launch_bwd_tile(q, k, v, rel_h, rel_w, fo, dout, fl, dq, dk, dv,
+                                      reinterpret_cast<float*>(base + w.dsum), rel, g, s);
+        if (e == hipSuccess)
+            e = halo::launch_rel_reduce(rel, halo::bwd_tile_rel_rows(g), reinterpret_cast<float*>(base + w.rel2),
+                                        drel_h, drel_w, g, s);
     } else {
         const MfmaWs w = mfma_ws(g);
         unsigned char* base = static_cast<unsigned char*>(workspace);

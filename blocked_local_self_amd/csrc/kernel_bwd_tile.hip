@@ -1,0 +1,753 @@
+// Backward pass of halo attention on gfx950 matrix cores for windows of up
+// to 32 columns and any block tiling (partial edge blocks included): bf16
+// in, fp32 accumulate, the pages' default semantics.
+//
+// The pages print no backward; HaloNet's models are trained by gradient
+// descent ("Scaling Local Self-Attention for Parameter Efficient Visual
+// Backbones", section 4.1), so this is the exact derivative of the forward
+// definition (sections 2.1-2.2; logit
+//   l = scale * (q.k + q.rel_h[ky - y + c0] + q.rel_w[kx - x + c0])
+// as in the HaloAttention module of the pswp.cn blog page, section 4), with
+// the forward's per-query log normaliser lse and D = dout.out:
+//   P = exp(l - lse),  dl = P (dout.v - D),
+//   dq = scale sum_keys dl (k + rel_h[row] + rel_w[col]),
+//   dk = scale sum_queries dl q,  dv = sum_queries P dout,
+//   d rel_h[R] = scale sum dl q over the pairs at row displacement R (d rel_w alike).
+//
+// Two kernels, then the table reduction shared with the other backward paths:
+//  * bwd_query_kernel: one workgroup per block.  The block's window (K and V,
+//    zero off the image) is staged in LDS; waves take 16-query tiles.  Scores
+//    are transposed, S^T = K Q^T over 4x4 key patches (lane (n, g): query n,
+//    window row 4rq+g, columns 4ct..4ct+3), the width term entering as the
+//    MFMA accumulator and the height term (minus lse) as the exponent's
+//    addend, as in the forward tile kernel.  dP^T = V dout^T, dl = P (dP - D),
+//    dq^T += K^T dl^T on a 16x16x16 MFMA per patch (K^T fragments gathered
+//    from the key-major window).  Per query, the sums of dl over each window
+//    column and each window row, placed at their table rows, give the
+//    tables' share of dq (tables^T times sums) and the table gradients (Q^T
+//    times sums), on MFMA with the sums split into bf16 high and low parts.
+//    Writes dq, D per query, and one table-gradient partial per workgroup
+//    (the waves' partials summed in a fixed order).
+//  * bwd_key_kernel: one workgroup per key block.  Waves own 4x4 key patches
+//    of the block (their K and V fragments in registers) and walk the query
+//    blocks whose windows reach them, scores in the other orientation
+//    (S = Q K^T, lane (n, g): key n, queries 4g..4g+3; relative terms
+//    gathered per pair from the tile's table products): P and dl are
+//    recomputed, dv^T += dout^T P and dk^T += Q^T dl.  Every key belongs to
+//    one workgroup: dk and dv are written once, with no atomics.
+// Every sum runs in a fixed order: results are bitwise reproducible.
+#include <algorithm>
+
+#include "mfma_util.h"
+
+namespace halo {
+
+constexpr int kBtWaves = 4;          // waves per workgroup (both kernels)
+
+struct BwdTilePlan {
+    // query kernel
+    int rp;            // staged window rows and columns (4 * NP)
+    int cw;            // staged row pitch in pixels (>= rp, = 4 mod 8)
+    int jr;            // table rows in LDS and scratch (16 * JT >= 2r - 1)
+    int jp;            // scratch pitch per query (floats)
+    int q_off_v, q_off_tab, q_off_scr, q_lds;
+    int64_t q_nwg;
+    // key kernel
+    int qp;            // Q^T / dout^T channel pitch (elements)
+    int nqpad;         // queries per block rounded up to tiles
+    int k_off_dot, k_off_l, k_off_d, k_off_tab, k_off_scr, k_lds;
+    int64_t k_nwg;
+    float alpha;       // scale * log2(e)
+};
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ inline f32x4 mma16(s16x4_t a, s16x4_t b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+template <typename T>
+__device__ inline T bt_ld(const unsigned char* base, unsigned off) { return *reinterpret_cast<const T*>(base + off); }
+template <typename T>
+__device__ inline void bt_st(unsigned char* base, unsigned off, T v) { *reinterpret_cast<T*>(base + off) = v; }
+
+// four bf16 values (16-bit patterns) into one MFMA operand
+__device__ inline s16x4_t pack4(unsigned short a, unsigned short b, unsigned short c, unsigned short d)
+{
+    return s16x4_t{(short)a, (short)b, (short)c, (short)d};
+}
+
+__device__ inline s16x4_t bf16x4_of(float a, float b, float c, float d)
+{
+    const u32x2 w{pack_bf16x2(a, b), pack_bf16x2(c, d)};
+    return __builtin_bit_cast(s16x4_t, w);
+}
+
+// x ~ hi + lo (bf16 each) to 2^-16 relative
+__device__ inline void split4(f32x4 x, s16x4_t& hi, s16x4_t& lo)
+{
+    hi = bf16x4_of(x[0], x[1], x[2], x[3]);
+    const u32x2 h = __builtin_bit_cast(u32x2, hi);
+    const float h0 = __builtin_bit_cast(float, h[0] << 16), h1 = __builtin_bit_cast(float, h[0] & 0xffff0000u);
+    const float h2 = __builtin_bit_cast(float, h[1] << 16), h3 = __builtin_bit_cast(float, h[1] & 0xffff0000u);
+    lo = bf16x4_of(x[0] - h0, x[1] - h1, x[2] - h2, x[3] - h3);
+}
+
+// Byte offset of channel chunk `c` (16 bytes) of the staged window pixel in
+// row t: chunks rotate with the row so the four rows of a patch spread over
+// the banks.
+template <int D>
+__device__ inline unsigned bt_chunk(int c, int t)
+{
+    constexpr int CPP = D / 8;
+    return (unsigned)((c ^ (t & (CPP - 1))) * 16);
+}
+
+// ------------------------------------------------------------------ queries
+template <int D, int NP>
+__global__ __launch_bounds__(64 * kBtWaves) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_query_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                      const __bf16* __restrict__ v, const __bf16* __restrict__ rel_h,
+                      const __bf16* __restrict__ rel_w, const __bf16* __restrict__ out,
+                      const __bf16* __restrict__ dout, const float* __restrict__ lse,
+                      __bf16* __restrict__ dq, float* __restrict__ dsum, float* __restrict__ part_rel,
+                      Geometry g, BwdTilePlan p)
+{
+    constexpr int KPL = D / 4;                  // channels per lane in a Frag<D> operand
+    constexpr int CPP = D / 8;                  // 16-byte chunks per pixel
+    constexpr unsigned PIXB = D * 2;
+    constexpr int MT = D / 16;                  // 16-channel output tiles
+    constexpr int JT = NP <= 4 ? 2 : NP <= 6 ? 3 : 4;   // 16-row table tiles (2r - 1 <= 16 JT)
+    typedef typename Frag<D>::T FragT;
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15, gq = lane >> 4;
+    const int r = g.r;
+    const float alpha = p.alpha;
+    const float log2e = 1.4426950408889634f;
+
+    const int64_t nblk = (int64_t)g.nbh * g.nbw;
+    const int64_t bh = blockIdx.x / nblk;
+    const int rem = (int)(blockIdx.x - bh * nblk);
+    const int by = rem / g.nbw, bx = rem - by * g.nbw;
+    const int ybeg = by * g.block, xbeg = bx * g.block;
+    const int wy0 = ybeg - g.halo, wx0 = xbeg - g.halo;
+    const int nqy = (min(ybeg + g.block, g.H) - ybeg + g.stride - 1) / g.stride;
+    const int nqx = (min(xbeg + g.block, g.W) - xbeg + g.stride - 1) / g.stride;
+    const int nq = nqy * nqx;
+    const int tiles = (nq + 15) / 16;
+    const int64_t plane = (int64_t)g.H * g.W * D;
+    const int64_t oplane = (int64_t)g.Ho * g.Wo;
+    const __bf16* qs = q + bh * plane;
+    const int cw = p.cw, rp = p.rp, jr = p.jr, jp = p.jp;
+    const unsigned rowb = (unsigned)cw * PIXB;
+    const unsigned offv = (unsigned)p.q_off_v, offth = (unsigned)p.q_off_tab;
+    const unsigned offtw = offth + (unsigned)jr * D * 2;
+    const unsigned scr = (unsigned)p.q_off_scr + (unsigned)wave * (unsigned)(16 * jp * 4 + 16 * D * 2);
+    const unsigned qtl = scr + (unsigned)(16 * jp * 4);     // this wave's tile of Q, [16][D] bf16
+
+    // ---- stage the window (K and V, zero outside the image or the window)
+    // and both tables (zero rows past 2r - 1)
+    {
+        const int items = rp * rp * CPP;
+        for (int e = tid; e < items; e += 64 * kBtWaves) {
+            const int t = e / (rp * CPP), rr = e - t * (rp * CPP);
+            const int c = rr / CPP, ch = rr - c * CPP;
+            const int y = wy0 + t, x = wx0 + c;
+            u32x4 kk{0u, 0u, 0u, 0u}, vv{0u, 0u, 0u, 0u};
+            if (t < r && c < r && y >= 0 && y < g.H && x >= 0 && x < g.W) {
+                const int64_t off = bh * plane + ((int64_t)y * g.W + x) * D + ch * 8;
+                kk = *reinterpret_cast<const u32x4*>(k + off);
+                vv = *reinterpret_cast<const u32x4*>(v + off);
+            }
+            const unsigned a = (unsigned)t * rowb + (unsigned)c * PIXB + bt_chunk<D>(ch, t);
+            bt_st<u32x4>(smem, a, kk);
+            bt_st<u32x4>(smem, offv + a, vv);
+        }
+        const int titems = jr * CPP;
+        for (int e = tid; e < 2 * titems; e += 64 * kBtWaves) {
+            const int tab = e / titems, rr = e - tab * titems;
+            const int j = rr / CPP, ch = rr - j * CPP;
+            u32x4 x{0u, 0u, 0u, 0u};
+            if (j < 2 * r - 1) x = *reinterpret_cast<const u32x4*>((tab ? rel_w : rel_h) + (int64_t)j * D + ch * 8);
+            bt_st<u32x4>(smem, (tab ? offtw : offth) + (unsigned)(j * D + ch * 8) * 2, x);
+        }
+    }
+    __syncthreads();
+
+    // table-gradient partials of this wave: lane (n, g) holds
+    // d rel^T[channel 16 mt + 4g + i][table row 16 jt + n]
+    f32x4 dRh[MT][JT], dRw[MT][JT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) {
+            dRh[mt][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            dRw[mt][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+
+    for (int u = wave; u < tiles; u += kBtWaves) {
+        // ---- the tile's queries (lane n: query 16u + n)
+        const int qi = 16 * u + n;
+        const bool valid = qi < nq;
+        const int qc = valid ? qi : 0;
+        const int iy = qc / nqx, ix = qc - iy * nqx;
+        const int y = ybeg + iy * g.stride, x = xbeg + ix * g.stride;
+        const int yl = y - wy0, xl = x - wx0;
+        const int64_t opix = bh * oplane + (int64_t)(y / g.stride) * g.Wo + x / g.stride;
+        FragT qf = *reinterpret_cast<const FragT*>(qs + ((int64_t)y * g.W + x) * D + gq * KPL);
+        FragT df = *reinterpret_cast<const FragT*>(dout + opix * D + gq * KPL);
+        const FragT of = *reinterpret_cast<const FragT*>(out + opix * D + gq * KPL);
+        if (!valid) {
+#pragma unroll
+            for (int e = 0; e < KPL; ++e) { qf[e] = 0; df[e] = 0; }
+        }
+        float dpart = 0.f;
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) {
+            const float a = __builtin_bit_cast(float, (unsigned)(unsigned short)df[e] << 16);
+            const float b = __builtin_bit_cast(float, (unsigned)(unsigned short)of[e] << 16);
+            dpart = fmaf(a, b, dpart);
+        }
+        const float Dq = sum_over_rows(dpart);
+        const float lse2 = lse[opix] * log2e;
+        if (valid && gq == 0) dsum[opix] = Dq;
+        bt_st<FragT>(smem, qtl + (unsigned)(n * D + gq * KPL) * 2, qf);
+
+        // ---- width terms: scratch[query][j] = q.rel_w[j], read back per
+        // window column as the score MFMA's accumulator (mask value off the
+        // image or past the window)
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) {
+            const FragT a = bt_ld<FragT>(smem, offtw + (unsigned)((16 * jt + n) * D + gq * KPL) * 2);
+            bt_st<f32x4>(smem, scr + (unsigned)(n * jp + 16 * jt + 4 * gq) * 4,
+                         Frag<D>::mma(a, qf, f32x4{0.f, 0.f, 0.f, 0.f}));
+        }
+        f32x4 cinit[NP];
+#pragma unroll
+        for (int ct = 0; ct < NP; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = 4 * ct + i, kx = wx0 + c;
+                const bool ok = c < r && kx >= 0 && kx < g.W;
+                const int j = ok ? c - xl + g.c0 : 0;
+                const float w = bt_ld<float>(smem, scr + (unsigned)(n * jp + j) * 4);
+                cinit[ct][i] = ok ? w : kMaskLogit;
+            }
+        // ---- height terms: alpha q.rel_h[row] - lse2 (-inf off the image,
+        // past the window, or for lanes without a query)
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) {
+            const FragT a = bt_ld<FragT>(smem, offth + (unsigned)((16 * jt + n) * D + gq * KPL) * 2);
+            bt_st<f32x4>(smem, scr + (unsigned)(n * jp + 16 * jt + 4 * gq) * 4,
+                         Frag<D>::mma(a, qf, f32x4{0.f, 0.f, 0.f, 0.f}));
+        }
+        float hq[NP];
+#pragma unroll
+        for (int rq = 0; rq < NP; ++rq) {
+            const int t = 4 * rq + gq, ky = wy0 + t;
+            const bool ok = valid && t < r && ky >= 0 && ky < g.H;
+            const int j = ok ? t - yl + g.c0 : 0;
+            const float h = bt_ld<float>(smem, scr + (unsigned)(n * jp + j) * 4);
+            hq[rq] = ok ? fmaf(h, alpha, -lse2) : -INFINITY;
+        }
+
+        // ---- the window, patch by patch
+        f32x4 dQt[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) dQt[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float rowsum[NP];
+        f32x4 colsum[NP];
+#pragma unroll
+        for (int ct = 0; ct < NP; ++ct) colsum[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // A-operand lane (m, kg): key m of the patch = (row m >> 2, column
+        // m & 3), channels kg*KPL..; K^T gather lane (channel n, kg): patch
+        // row kg, columns 0..3
+        const unsigned kA = (unsigned)(n >> 2) * rowb + (unsigned)(n & 3) * PIXB;
+#pragma unroll
+        for (int rq = 0; rq < NP; ++rq) {
+            rowsum[rq] = 0.f;
+            const int ta = 4 * rq + (n >> 2);          // row of this lane's A-operand key
+            const int tg = 4 * rq + gq;                // row of this lane's K^T gather
+            const unsigned chA = D == 32 ? bt_chunk<D>(gq, ta) : bt_chunk<D>(gq >> 1, ta) + (gq & 1) * 8;
+#pragma unroll
+            for (int ct = 0; ct < NP; ++ct) {
+                const unsigned a = (unsigned)(4 * rq) * rowb + kA + (unsigned)(4 * ct) * PIXB + chA;
+                const FragT kf = bt_ld<FragT>(smem, a);
+                const FragT vf = bt_ld<FragT>(smem, offv + a);
+                const f32x4 s = Frag<D>::mma(kf, qf, cinit[ct]);
+                const f32x4 dp = Frag<D>::mma(vf, df, f32x4{0.f, 0.f, 0.f, 0.f});
+                f32x4 ds;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float pr = __builtin_amdgcn_exp2f(fmaf(s[i], alpha, hq[rq]));
+                    ds[i] = pr * (dp[i] - Dq);
+                }
+                rowsum[rq] += (ds[0] + ds[1]) + (ds[2] + ds[3]);
+                colsum[ct] += ds;
+                const s16x4_t dsb = bf16x4_of(ds[0], ds[1], ds[2], ds[3]);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const int ch = 16 * mt + n;
+                    const unsigned base = (unsigned)tg * rowb + (unsigned)(4 * ct) * PIXB +
+                                          bt_chunk<D>(ch >> 3, tg) + (unsigned)(ch & 7) * 2;
+                    const s16x4_t kt = pack4(bt_ld<unsigned short>(smem, base),
+                                             bt_ld<unsigned short>(smem, base + PIXB),
+                                             bt_ld<unsigned short>(smem, base + 2 * PIXB),
+                                             bt_ld<unsigned short>(smem, base + 3 * PIXB));
+                    dQt[mt] = mma16(kt, dsb, dQt[mt]);
+                }
+            }
+        }
+
+        // ---- column sums over the four lanes of a query, then the width
+        // table's share: scratch[query][table row of column c] = column sum
+#pragma unroll
+        for (int ct = 0; ct < NP; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) colsum[ct][i] = sum_over_rows(colsum[ct][i]);
+        for (int jj = gq; jj < jr / 4; jj += 4)
+            bt_st<f32x4>(smem, scr + (unsigned)(n * jp + 4 * jj) * 4, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int ct = 0; ct < NP; ++ct) {
+            const int c = 4 * ct + gq, kx = wx0 + c;
+            const float val = gq == 0 ? colsum[ct][0] : gq == 1 ? colsum[ct][1] : gq == 2 ? colsum[ct][2] : colsum[ct][3];
+            if (valid && c < r && kx >= 0 && kx < g.W) bt_st<float>(smem, scr + (unsigned)(n * jp + c - xl + g.c0) * 4, val);
+        }
+        auto table_terms = [&](unsigned offt, f32x4 (&dR)[MT][JT]) {
+            // Q^T of the tile: lane (channel 16 mt + n, kg) holds queries 4kg..4kg+3
+            s16x4_t qt[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const unsigned b = qtl + (unsigned)((4 * gq) * D + 16 * mt + n) * 2;
+                qt[mt] = pack4(bt_ld<unsigned short>(smem, b), bt_ld<unsigned short>(smem, b + D * 2),
+                               bt_ld<unsigned short>(smem, b + 2 * D * 2), bt_ld<unsigned short>(smem, b + 3 * D * 2));
+            }
+#pragma unroll
+            for (int jt = 0; jt < JT; ++jt) {
+                // dq^T += table^T sums: B lane (query n, kg) = sums at rows 16jt+4kg..
+                s16x4_t hi, lo;
+                split4(bt_ld<f32x4>(smem, scr + (unsigned)(n * jp + 16 * jt + 4 * gq) * 4), hi, lo);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const unsigned b = offt + (unsigned)((16 * jt + 4 * gq) * D + 16 * mt + n) * 2;
+                    const s16x4_t tt = pack4(bt_ld<unsigned short>(smem, b), bt_ld<unsigned short>(smem, b + D * 2),
+                                             bt_ld<unsigned short>(smem, b + 2 * D * 2),
+                                             bt_ld<unsigned short>(smem, b + 3 * D * 2));
+                    dQt[mt] = mma16(tt, lo, mma16(tt, hi, dQt[mt]));
+                }
+                // d table^T += Q^T sums^T: B lane (table row 16jt+n, kg) = sums of queries 4kg..4kg+3
+                f32x4 st;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) st[e] = bt_ld<float>(smem, scr + (unsigned)((4 * gq + e) * jp + 16 * jt + n) * 4);
+                split4(st, hi, lo);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) dR[mt][jt] = mma16(qt[mt], lo, mma16(qt[mt], hi, dR[mt][jt]));
+            }
+        };
+        table_terms(offtw, dRw);
+        // ---- the height table likewise (row sums are whole per lane)
+        for (int jj = gq; jj < jr / 4; jj += 4)
+            bt_st<f32x4>(smem, scr + (unsigned)(n * jp + 4 * jj) * 4, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int rq = 0; rq < NP; ++rq) {
+            const int t = 4 * rq + gq, ky = wy0 + t;
+            if (valid && t < r && ky >= 0 && ky < g.H)
+                bt_st<float>(smem, scr + (unsigned)(n * jp + t - yl + g.c0) * 4, rowsum[rq]);
+        }
+        table_terms(offth, dRh);
+
+        if (valid) {
+            __bf16* dp = dq + bh * plane + ((int64_t)y * g.W + x) * D + 4 * gq;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                *reinterpret_cast<u32x2*>(dp + 16 * mt) =
+                    u32x2{pack_bf16x2(g.scale * dQt[mt][0], g.scale * dQt[mt][1]),
+                          pack_bf16x2(g.scale * dQt[mt][2], g.scale * dQt[mt][3])};
+        }
+    }
+
+    // ---- the workgroup's table-gradient partial: waves' partials through
+    // LDS (the window's space), summed in wave order
+    __syncthreads();
+    const int E = (2 * r - 1) * D;
+    float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int tab = 0; tab < 2; ++tab)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int jt = 0; jt < JT; ++jt) {
+                const f32x4 x = tab ? dRw[mt][jt] : dRh[mt][jt];
+                const int j = 16 * jt + n;
+                *reinterpret_cast<f32x4*>(red + ((wave * 2 + tab) * jr + j) * D + 16 * mt + 4 * gq) = x;
+            }
+    __syncthreads();
+    float* part = part_rel + (int64_t)blockIdx.x * 2 * E;
+    for (int e = tid; e < 2 * E; e += 64 * kBtWaves) {
+        const int tab = e / E, rr = e - tab * E;
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < kBtWaves; ++w) s += red[(w * 2 + tab) * jr * D + rr];
+        part[e] = g.scale * s;
+    }
+}
+
+// --------------------------------------------------------------------- keys
+template <int D, int KP>
+__global__ __launch_bounds__(64 * kBtWaves) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_key_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                    const __bf16* __restrict__ v, const __bf16* __restrict__ rel_h,
+                    const __bf16* __restrict__ rel_w, const __bf16* __restrict__ dout,
+                    const float* __restrict__ lse, const float* __restrict__ dsum,
+                    __bf16* __restrict__ dk, __bf16* __restrict__ dv, Geometry g, BwdTilePlan p)
+{
+    constexpr int KPL = D / 4;
+    constexpr int CPP = D / 8;
+    constexpr int MT = D / 16;
+    typedef typename Frag<D>::T FragT;
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15, gq = lane >> 4;
+    const int r = g.r;
+    const float alpha = p.alpha;
+    const float log2e = 1.4426950408889634f;
+
+    const int64_t nblk = (int64_t)g.nbh * g.nbw;
+    const int64_t bh = blockIdx.x / nblk;
+    const int rem = (int)(blockIdx.x - bh * nblk);
+    const int kby = rem / g.nbw, kbx = rem - kby * g.nbw;
+    const int kyb = kby * g.block, kxb = kbx * g.block;
+    const int nky = min(g.block, g.H - kyb), nkx = min(g.block, g.W - kxb);
+    const int pb = (g.block + 3) / 4;                   // patches per block side
+    const int64_t plane = (int64_t)g.H * g.W * D;
+    const int64_t oplane = (int64_t)g.Ho * g.Wo;
+    const __bf16* qs = q + bh * plane;
+    const int jr = p.jr, jp = p.jp, qp = p.qp;
+    const int JT = jr / 16;
+    const unsigned offqt = 0, offdt = (unsigned)p.k_off_dot;
+    const unsigned offl = (unsigned)p.k_off_l, offd = (unsigned)p.k_off_d;
+    const unsigned offth = (unsigned)p.k_off_tab, offtw = offth + (unsigned)jr * D * 2;
+    const unsigned scrh = (unsigned)p.k_off_scr + (unsigned)wave * (unsigned)(2 * 16 * jp * 4);
+    const unsigned scrw = scrh + (unsigned)(16 * jp * 4);
+
+    // ---- this wave's patches: key (row n >> 2, column n & 3) of patch
+    // wave + 4 kp; K and V as B operands (lane (key n, kg): channels kg*KPL..)
+    FragT kb[KP], vb[KP];
+    f32x4 dKt[KP][MT], dVt[KP][MT];
+    int ky[KP], kx[KP];
+    bool kok[KP], pown[KP];
+#pragma unroll
+    for (int kp = 0; kp < KP; ++kp) {
+        const int pw = wave + kBtWaves * kp;
+        pown[kp] = pw < pb * pb;
+        const int py = pw / pb, px = pw - py * pb;
+        const int ly = 4 * py + (n >> 2), lx = 4 * px + (n & 3);
+        ky[kp] = kyb + ly;
+        kx[kp] = kxb + lx;
+        kok[kp] = pown[kp] && ly < nky && lx < nkx;
+        const int64_t off = bh * plane + ((int64_t)(kok[kp] ? ky[kp] : kyb) * g.W + (kok[kp] ? kx[kp] : kxb)) * D + gq * KPL;
+        kb[kp] = *reinterpret_cast<const FragT*>(k + off);
+        vb[kp] = *reinterpret_cast<const FragT*>(v + off);
+        if (!kok[kp]) {
+#pragma unroll
+            for (int e = 0; e < KPL; ++e) { kb[kp][e] = 0; vb[kp][e] = 0; }
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            dKt[kp][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            dVt[kp][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+
+    // ---- tables (zero rows past 2r - 1)
+    {
+        const int titems = jr * CPP;
+        for (int e = tid; e < 2 * titems; e += 64 * kBtWaves) {
+            const int tab = e / titems, rr = e - tab * titems;
+            const int j = rr / CPP, ch = rr - j * CPP;
+            u32x4 x{0u, 0u, 0u, 0u};
+            if (j < 2 * r - 1) x = *reinterpret_cast<const u32x4*>((tab ? rel_w : rel_h) + (int64_t)j * D + ch * 8);
+            bt_st<u32x4>(smem, (tab ? offtw : offth) + (unsigned)(j * D + ch * 8) * 2, x);
+        }
+    }
+
+    // ---- the query blocks whose windows reach this key block
+    const int A = (g.halo + g.block - 1) / g.block;
+    for (int nby = max(0, kby - A); nby <= min(g.nbh - 1, kby + A); ++nby)
+        for (int nbx = max(0, kbx - A); nbx <= min(g.nbw - 1, kbx + A); ++nbx) {
+            const int wy0 = nby * g.block - g.halo, wx0 = nbx * g.block - g.halo;
+            if (max(kyb, wy0) >= min(kyb + nky, wy0 + r) || max(kxb, wx0) >= min(kxb + nkx, wx0 + r)) continue;
+            const int ybeg = nby * g.block, xbeg = nbx * g.block;
+            const int nqy = (min(ybeg + g.block, g.H) - ybeg + g.stride - 1) / g.stride;
+            const int nqx = (min(xbeg + g.block, g.W) - xbeg + g.stride - 1) / g.stride;
+            const int nq = nqy * nqx;
+            const int tiles = (nq + 15) / 16;
+            __syncthreads();
+            // Q^T and dout^T [channel][query] (zero past nq), lse2 (+inf past
+            // nq: zero weights) and D per query
+            for (int e = tid; e < tiles * 16 * CPP; e += 64 * kBtWaves) {
+                const int qi = e / CPP, ch = e - qi * CPP;
+                u32x4 a{0u, 0u, 0u, 0u}, b{0u, 0u, 0u, 0u};
+                if (qi < nq) {
+                    const int iy = qi / nqx, ix = qi - iy * nqx;
+                    const int y = ybeg + iy * g.stride, x = xbeg + ix * g.stride;
+                    const int64_t opix = bh * oplane + (int64_t)(y / g.stride) * g.Wo + x / g.stride;
+                    a = *reinterpret_cast<const u32x4*>(qs + ((int64_t)y * g.W + x) * D + ch * 8);
+                    b = *reinterpret_cast<const u32x4*>(dout + opix * D + ch * 8);
+                    if (ch == 0) {
+                        bt_st<float>(smem, offl + (unsigned)qi * 4, lse[opix] * log2e);
+                        bt_st<float>(smem, offd + (unsigned)qi * 4, dsum[opix]);
+                    }
+                } else if (ch == 0) {
+                    bt_st<float>(smem, offl + (unsigned)qi * 4, INFINITY);
+                    bt_st<float>(smem, offd + (unsigned)qi * 4, 0.f);
+                }
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const unsigned c0 = (unsigned)(ch * 8 + 2 * w);
+                    bt_st<unsigned short>(smem, offqt + (c0 * qp + qi) * 2, (unsigned short)(a[w] & 0xffffu));
+                    bt_st<unsigned short>(smem, offqt + ((c0 + 1) * qp + qi) * 2, (unsigned short)(a[w] >> 16));
+                    bt_st<unsigned short>(smem, offdt + (c0 * qp + qi) * 2, (unsigned short)(b[w] & 0xffffu));
+                    bt_st<unsigned short>(smem, offdt + ((c0 + 1) * qp + qi) * 2, (unsigned short)(b[w] >> 16));
+                }
+            }
+            __syncthreads();
+
+            // patches of this wave inside the window (uniform per wave)
+            bool pin[KP];
+            bool any = false;
+#pragma unroll
+            for (int kp = 0; kp < KP; ++kp) {
+                const int pw = wave + kBtWaves * kp;
+                const int py = pw / pb, px = pw - py * pb;
+                const int y0 = kyb + 4 * py, x0 = kxb + 4 * px;
+                pin[kp] = pown[kp] && max(y0, wy0) < min(y0 + 4, wy0 + r) && max(x0, wx0) < min(x0 + 4, wx0 + r);
+                any |= pin[kp];
+            }
+            if (!any) continue;
+
+            for (int u = 0; u < tiles; ++u) {
+                // A operands: lane (query n, kg) = channels kg*KPL.. of query 16u+n
+                const int qa_i = min(16 * u + n, nq - 1);
+                int iy = qa_i / nqx, ix = qa_i - iy * nqx;
+                int y = ybeg + iy * g.stride, x = xbeg + ix * g.stride;
+                const int64_t opa = bh * oplane + (int64_t)(y / g.stride) * g.Wo + x / g.stride;
+                FragT qa = *reinterpret_cast<const FragT*>(qs + ((int64_t)y * g.W + x) * D + gq * KPL);
+                const FragT da = *reinterpret_cast<const FragT*>(dout + opa * D + gq * KPL);
+                // q.rel_h[j] and q.rel_w[j] of the tile's queries: scratch[query][j]
+                for (int jt = 0; jt < JT; ++jt) {
+                    const FragT ah = bt_ld<FragT>(smem, offth + (unsigned)((16 * jt + n) * D + gq * KPL) * 2);
+                    const FragT aw = bt_ld<FragT>(smem, offtw + (unsigned)((16 * jt + n) * D + gq * KPL) * 2);
+                    bt_st<f32x4>(smem, scrh + (unsigned)(n * jp + 16 * jt + 4 * gq) * 4,
+                                 Frag<D>::mma(ah, qa, f32x4{0.f, 0.f, 0.f, 0.f}));
+                    bt_st<f32x4>(smem, scrw + (unsigned)(n * jp + 16 * jt + 4 * gq) * 4,
+                                 Frag<D>::mma(aw, qa, f32x4{0.f, 0.f, 0.f, 0.f}));
+                }
+                // this lane's four queries 16u + 4g + i: positions, lse2, D
+                int bhq[4], bwq[4];
+                float l2[4], dd[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int qq = 16 * u + 4 * gq + i;
+                    const int qv = min(qq, nq - 1);
+                    const int jy = qv / nqx, jx = qv - jy * nqx;
+                    const int yq = ybeg + jy * g.stride, xq = xbeg + jx * g.stride;
+                    bhq[i] = (4 * gq + i) * jp + g.c0 - yq;
+                    bwq[i] = (4 * gq + i) * jp + g.c0 - xq;
+                    l2[i] = bt_ld<float>(smem, offl + (unsigned)qq * 4);
+                    dd[i] = bt_ld<float>(smem, offd + (unsigned)qq * 4);
+                }
+                // Q^T and dout^T fragments: lane (channel 16mt + n, kg) = queries 4kg..4kg+3
+                s16x4_t qt[MT], dt[MT];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const unsigned o = (unsigned)((16 * mt + n) * qp + 16 * u + 4 * gq) * 2;
+                    qt[mt] = __builtin_bit_cast(s16x4_t, bt_ld<u32x2>(smem, offqt + o));
+                    dt[mt] = __builtin_bit_cast(s16x4_t, bt_ld<u32x2>(smem, offdt + o));
+                }
+#pragma unroll
+                for (int kp = 0; kp < KP; ++kp) {
+                    if (!pin[kp]) continue;
+                    const bool inw = kok[kp] && ky[kp] >= wy0 && ky[kp] < wy0 + r && kx[kp] >= wx0 && kx[kp] < wx0 + r;
+                    f32x4 cin;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int ih = inw ? bhq[i] + ky[kp] : 0, iw = inw ? bwq[i] + kx[kp] : 0;
+                        const float rel = bt_ld<float>(smem, scrh + (unsigned)ih * 4) + bt_ld<float>(smem, scrw + (unsigned)iw * 4);
+                        cin[i] = inw ? rel : kMaskLogit;
+                    }
+                    const f32x4 s = Frag<D>::mma(qa, kb[kp], cin);
+                    const f32x4 dp = Frag<D>::mma(da, vb[kp], f32x4{0.f, 0.f, 0.f, 0.f});
+                    f32x4 pr, ds;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        pr[i] = __builtin_amdgcn_exp2f(fmaf(s[i], alpha, -l2[i]));
+                        ds[i] = pr[i] * (dp[i] - dd[i]);
+                    }
+                    const s16x4_t pb4 = bf16x4_of(pr[0], pr[1], pr[2], pr[3]);
+                    const s16x4_t db4 = bf16x4_of(ds[0], ds[1], ds[2], ds[3]);
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) {
+                        dVt[kp][mt] = mma16(dt[mt], pb4, dVt[kp][mt]);
+                        dKt[kp][mt] = mma16(qt[mt], db4, dKt[kp][mt]);
+                    }
+                }
+            }
+        }
+
+    // ---- dk, dv of this wave's keys: lane (key n, g) holds channels 16mt + 4g..
+#pragma unroll
+    for (int kp = 0; kp < KP; ++kp) {
+        if (!kok[kp]) continue;
+        const int64_t off = bh * plane + ((int64_t)ky[kp] * g.W + kx[kp]) * D + 4 * gq;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            *reinterpret_cast<u32x2*>(dk + off + 16 * mt) =
+                u32x2{pack_bf16x2(g.scale * dKt[kp][mt][0], g.scale * dKt[kp][mt][1]),
+                      pack_bf16x2(g.scale * dKt[kp][mt][2], g.scale * dKt[kp][mt][3])};
+            *reinterpret_cast<u32x2*>(dv + off + 16 * mt) =
+                u32x2{pack_bf16x2(dVt[kp][mt][0], dVt[kp][mt][1]), pack_bf16x2(dVt[kp][mt][2], dVt[kp][mt][3])};
+        }
+    }
+}
+
+__global__ void bt_zero_u16(unsigned short* __restrict__ p, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
+// ---------------------------------------------------------------- planning
+static int bt_np(int r) { return r <= 16 ? 4 : r <= 20 ? 5 : r <= 24 ? 6 : 8; }
+static int bt_kp(int block)
+{
+    const int pb = (block + 3) / 4;
+    return (pb * pb + kBtWaves - 1) / kBtWaves;
+}
+
+static BwdTilePlan bt_plan(const Geometry& g)
+{
+    BwdTilePlan p{};
+    const int np = bt_np(g.r);
+    const int jt = np <= 4 ? 2 : np <= 6 ? 3 : 4;
+    p.rp = 4 * np;
+    p.cw = p.rp;
+    while (p.cw % 8 != 4) ++p.cw;
+    p.jr = 16 * jt;
+    p.jp = p.jr + 4;
+    const int pix = g.d * 2;
+    const int kvb = p.rp * p.cw * pix;                 // one staged window (bytes)
+    p.q_off_v = kvb;
+    p.q_off_tab = 2 * kvb;
+    p.q_off_scr = p.q_off_tab + 2 * p.jr * g.d * 2;
+    p.q_lds = p.q_off_scr + kBtWaves * (16 * p.jp * 4 + 16 * g.d * 2);
+    const int red = kBtWaves * 2 * p.jr * g.d * 4;     // the partials' reduction reuses the window space
+    if (red > p.q_off_tab) return BwdTilePlan{};       // does not fit under the tables
+    p.q_nwg = g.BH * g.nbh * g.nbw;
+    const int side = (g.block + g.stride - 1) / g.stride;
+    p.nqpad = (side * side + 15) / 16 * 16;
+    p.qp = (p.nqpad + 31) / 32 * 32 + 16;              // qp/2 = 8 (mod 16) dwords
+    p.k_off_dot = g.d * p.qp * 2;
+    p.k_off_l = 2 * p.k_off_dot;
+    p.k_off_d = p.k_off_l + p.nqpad * 4;
+    p.k_off_tab = p.k_off_d + p.nqpad * 4;
+    p.k_off_scr = p.k_off_tab + 2 * p.jr * g.d * 2;
+    p.k_lds = p.k_off_scr + kBtWaves * 2 * 16 * p.jp * 4;
+    p.k_nwg = p.q_nwg;
+    p.alpha = (float)((double)g.scale * 1.4426950408889634);
+    return p;
+}
+
+bool bwd_tile_supported(const Geometry& g, bool bf16)
+{
+    if (!bf16 || g.flags != 0 || (g.d != 16 && g.d != 32) || g.r > 32 || g.block > 16) return false;
+    if ((int64_t)g.H * g.W * g.d >= (int64_t(1) << 31)) return false;   // 32-bit offsets inside an image
+    // LDS of one gfx950 workgroup (160 KiB): the choice depends on the shape
+    // only, so workspace queries need no device
+    const BwdTilePlan p = bt_plan(g);
+    constexpr int kLds = 160 * 1024;
+    return p.q_lds != 0 && p.q_lds <= kLds && p.k_lds <= kLds;
+}
+
+// Rows of table-gradient partials the query kernel writes (one per block).
+int64_t bwd_tile_rel_rows(const Geometry& g) { return g.BH * g.nbh * g.nbw; }
+
+template <int D, int NP>
+static hipError_t bt_query_launch(const void* q, const void* k, const void* v, const void* rh, const void* rw,
+                                  const void* out, const void* dout, const float* lse, void* dq, float* dsum,
+                                  float* part_rel, const Geometry& g, const BwdTilePlan& p, hipStream_t st)
+{
+    auto kern = bwd_query_kernel<D, NP>;
+    const hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), p.q_lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)p.q_nwg), dim3(64 * kBtWaves), p.q_lds, st,
+                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)rh, (const __bf16*)rw,
+                       (const __bf16*)out, (const __bf16*)dout, lse, (__bf16*)dq, dsum, part_rel, g, p);
+    return hipGetLastError();
+}
+
+template <int D, int KP>
+static hipError_t bt_key_launch(const void* q, const void* k, const void* v, const void* rh, const void* rw,
+                                const void* dout, const float* lse, const float* dsum, void* dk, void* dv,
+                                const Geometry& g, const BwdTilePlan& p, hipStream_t st)
+{
+    auto kern = bwd_key_kernel<D, KP>;
+    const hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), p.k_lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)p.k_nwg), dim3(64 * kBtWaves), p.k_lds, st,
+                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)rh, (const __bf16*)rw,
+                       (const __bf16*)dout, lse, dsum, (__bf16*)dk, (__bf16*)dv, g, p);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t bt_query_np(const void* q, const void* k, const void* v, const void* rh, const void* rw,
+                              const void* out, const void* dout, const float* lse, void* dq, float* dsum,
+                              float* part_rel, const Geometry& g, const BwdTilePlan& p, hipStream_t st)
+{
+    switch (bt_np(g.r)) {
+    case 4: return bt_query_launch<D, 4>(q, k, v, rh, rw, out, dout, lse, dq, dsum, part_rel, g, p, st);
+    case 5: return bt_query_launch<D, 5>(q, k, v, rh, rw, out, dout, lse, dq, dsum, part_rel, g, p, st);
+    case 6: return bt_query_launch<D, 6>(q, k, v, rh, rw, out, dout, lse, dq, dsum, part_rel, g, p, st);
+    default: return bt_query_launch<D, 8>(q, k, v, rh, rw, out, dout, lse, dq, dsum, part_rel, g, p, st);
+    }
+}
+
+template <int D>
+static hipError_t bt_key_kp(const void* q, const void* k, const void* v, const void* rh, const void* rw,
+                            const void* dout, const float* lse, const float* dsum, void* dk, void* dv,
+                            const Geometry& g, const BwdTilePlan& p, hipStream_t st)
+{
+    switch (bt_kp(g.block)) {
+    case 1: return bt_key_launch<D, 1>(q, k, v, rh, rw, dout, lse, dsum, dk, dv, g, p, st);
+    case 3: return bt_key_launch<D, 3>(q, k, v, rh, rw, dout, lse, dsum, dk, dv, g, p, st);
+    default: return bt_key_launch<D, 4>(q, k, v, rh, rw, dout, lse, dsum, dk, dv, g, p, st);
+    }
+}
+
+// dq (zeroed first where queries are strided: only query pixels receive a
+// gradient), D per query into dsum, table partials, then dk and dv.
+hipError_t launch_bwd_tile(const void* q, const void* k, const void* v, const void* rh, const void* rw,
+                           const void* out, const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           float* dsum, float* part_rel, const Geometry& g, hipStream_t st)
+{
+    const BwdTilePlan p = bt_plan(g);
+    if (g.stride > 1) {
+        const int64_t nel = g.BH * (int64_t)g.H * g.W * g.d;
+        const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((nel + 255) / 256, 65536));
+        hipLaunchKernelGGL(bt_zero_u16, dim3((unsigned)blocks), dim3(256), 0, st, (unsigned short*)dq, nel);
+    }
+    hipError_t e = g.d == 16 ? bt_query_np<16>(q, k, v, rh, rw, out, dout, lse, dq, dsum, part_rel, g, p, st)
+                             : bt_query_np<32>(q, k, v, rh, rw, out, dout, lse, dq, dsum, part_rel, g, p, st);
+    if (e != hipSuccess) return e;
+    return g.d == 16 ? bt_key_kp<16>(q, k, v, rh, rw, dout, lse, dsum, dk, dv, g, p, st)
+                     : bt_key_kp<32>(q, k, v, rh, rw, dout, lse, dsum, dk, dv, g, p, st);
+}
+
+}  // namespace halo

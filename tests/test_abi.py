@@ -142,7 +142,7 @@ def bwd_call(lib, *, q=1, k=2, v=3, rh=4, rw=5, out=0, dout=6, lse=0, dq=7, dk=8
     (dict(dtype=5), -3), (dict(d=0), -2), (dict(stride=3), -2), (dict(kernel=7), -2),
     (dict(scale=float("nan")), -2),
     (dict(ws_bytes=16), -7),                                 # workspace too small
-    (dict(kernel=2, dtype=0), -4), (dict(kernel=2, H=10), -4), (dict(kernel=2, block=8, halo=5), -4),
+    (dict(kernel=2, dtype=0), -4), (dict(kernel=2, d=24), -4), (dict(kernel=2, block=20, halo=2), -4),
     (dict(dq=1), -6), (dict(dk=7), -6), (dict(ws=1), -6),   # aliasing
 ])
 def test_backward_invalid_arguments_rejected_on_host(lib, kw, status):

@@ -126,6 +126,33 @@ MFMA_SHAPES = [s for s in SMALL if mfma_ok(s)] + [
 ]
 
 
+# Shapes the strip kernel does not take (windows wider than 16 columns,
+# partial edge blocks, other query counts per block): the 16-query tile
+# backward kernels.
+TILE_SHAPES = [
+    (1, 2, 36, 36, 32, 12, 3, 1),    # 18x18 windows, whole blocks
+    (1, 2, 40, 44, 32, 12, 3, 1),    # 18x18 windows, partial last block row and column
+    (1, 2, 20, 28, 16, 8, 3, 1),     # 14x14 windows, partial blocks
+    (1, 2, 32, 40, 16, 12, 3, 2),    # partial + strided + 18x18 windows
+    (1, 1, 20, 20, 16, 2, 5, 1),     # halo wider than a block: keys seen by 7x7 blocks
+    (1, 2, 30, 30, 32, 12, 6, 1),    # r = 24, d = 32
+    (1, 1, 40, 40, 16, 16, 8, 1),    # r = 32, d = 16
+    (1, 2, 24, 21, 16, 6, 3, 3),     # block 6 (patches cross the block edge), partial, stride 3
+    (2, 1, 12, 12, 32, 12, 0, 1),    # h = 0: windows are the blocks
+]
+
+
+@pytest.mark.parametrize("use_fwd", [False, True], ids=["recompute", "fwd_lse"])
+@pytest.mark.parametrize("shape", TILE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_tile_backward_matches_oracle(shape, use_fwd):
+    B, heads, H, W, d, block, halo, stride = shape
+    say(f"bwd tile case {shape} use_fwd={use_fwd}")
+    ins, g = case(*shape, "bf16", seed=5 * sum(shape))
+    got = gpu_bwd(ins, g, block, halo, stride, use_fwd=use_fwd, kernel="mfma")
+    worst = compare(got, ref_bwd(ins, g, block, halo, stride), "bf16", str(shape))
+    say(f"  worst relative error {worst:.3e}")
+
+
 @pytest.mark.parametrize("use_fwd", [False, True], ids=["recompute", "fwd_lse"])
 @pytest.mark.parametrize("shape", MFMA_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_matrix_core_backward_matches_oracle(shape, use_fwd):
@@ -149,19 +176,24 @@ def test_workload_full_size(name):
     say(f"  worst relative error {worst:.3e}")
 
 
-@pytest.mark.parametrize("kernel", ["mfma", "generic"])
-def test_deterministic(kernel):
-    ins, g = case(2, 4, 32, 32, 16, 8, 3, 1, "bf16", seed=21)
-    a = gpu_bwd(ins, g, 8, 3, 1, kernel=kernel)
-    b = gpu_bwd(ins, g, 8, 3, 1, kernel=kernel)
+@pytest.mark.parametrize("kernel,shape", [("mfma", (2, 4, 32, 32, 16, 8, 3, 1)),
+                                          ("mfma", (1, 3, 40, 44, 32, 12, 3, 1)),
+                                          ("generic", (2, 4, 32, 32, 16, 8, 3, 1))])
+def test_deterministic(kernel, shape):
+    ins, g = case(*shape, "bf16", seed=21)
+    a = gpu_bwd(ins, g, *shape[5:], kernel=kernel)
+    b = gpu_bwd(ins, g, *shape[5:], kernel=kernel)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
 
 
-def test_matrix_core_backward_refuses_what_it_does_not_cover():
-    ins, g = case(1, 1, 20, 28, 16, 8, 3, 1, "bf16", seed=1)   # ragged blocks
+@pytest.mark.parametrize("shape", [(1, 1, 40, 40, 16, 20, 6, 1),    # block 20 > 16
+                                   (1, 1, 40, 40, 32, 16, 8, 1),    # r = 32 at d = 32: window past LDS
+                                   (1, 1, 16, 16, 24, 4, 1, 1)])    # d = 24
+def test_matrix_core_backward_refuses_what_it_does_not_cover(shape):
+    ins, g = case(*shape, "bf16", seed=1)
     with pytest.raises(HaloError):
-        gpu_bwd(ins, g, 8, 3, 1, kernel="mfma")
+        gpu_bwd(ins, g, *shape[5:], kernel="mfma")
 
 
 def test_autograd_function_matches_direct_call():
