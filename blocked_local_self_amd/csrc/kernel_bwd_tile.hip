@@ -28,13 +28,16 @@
 //    times sums), on MFMA with the sums split into bf16 high and low parts.
 //    Writes dq, D per query, and one table-gradient partial per workgroup
 //    (the waves' partials summed in a fixed order).
-//  * bwd_key_kernel: one workgroup per key block.  Waves own 4x4 key patches
-//    of the block (their K and V fragments in registers) and walk the query
-//    blocks whose windows reach them, scores in the other orientation
+//  * bwd_key_kernel: one workgroup per key block, its keys staged as 4x4
+//    patches.  The 16-query tiles of the query blocks whose windows reach
+//    the key block are shared out over the waves; for its tile a wave takes
+//    every patch inside the window, scores in the other orientation
 //    (S = Q K^T, lane (n, g): key n, queries 4g..4g+3; relative terms
 //    gathered per pair from the tile's table products): P and dl are
-//    recomputed, dv^T += dout^T P and dk^T += Q^T dl.  Every key belongs to
-//    one workgroup: dk and dv are written once, with no atomics.
+//    recomputed, dv^T += dout^T P and dk^T += Q^T dl (Q^T and dout^T as
+//    MFMA products with a 0/1 operand).  The waves' sums are added in wave
+//    order; every key belongs to one workgroup: dk and dv are written once,
+//    with no atomics.
 // Every sum runs in a fixed order: results are bitwise reproducible.
 #include <algorithm>
 
@@ -53,9 +56,7 @@ struct BwdTilePlan {
     int q_off_v, q_off_tab, q_off_scr, q_lds;
     int64_t q_nwg;
     // key kernel
-    int qp;            // Q^T / dout^T channel pitch (elements)
-    int nqpad;         // queries per block rounded up to tiles
-    int k_off_dot, k_off_l, k_off_d, k_off_tab, k_off_scr, k_lds;
+    int k_off_tab, k_off_scr, k_off_red, k_lds;
     int64_t k_nwg;
     float alpha;       // scale * log2(e)
 };
@@ -397,7 +398,14 @@ void bwd_query_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
 }
 
 // --------------------------------------------------------------------- keys
-template <int D, int KP>
+// One workgroup per key block.  The block's keys, cut into 4x4 patches, are
+// staged once (K and V as B operands: lane (key n, kg) = channels kg*KPL..).
+// The work items are the 16-query tiles of every query block whose window
+// reaches the key block, in a fixed order; wave w takes items w, w+4, ...
+// and, for its tile, every patch inside that window (up to NPP patches per
+// pass; wider blocks take several passes).  The waves' dk^T and dv^T sums are
+// added in wave order through LDS at the end.
+template <int D, int NPP>
 __global__ __launch_bounds__(64 * kBtWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_key_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                     const __bf16* __restrict__ v, const __bf16* __restrict__ rel_h,
@@ -425,47 +433,35 @@ void bwd_key_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const int kyb = kby * g.block, kxb = kbx * g.block;
     const int nky = min(g.block, g.H - kyb), nkx = min(g.block, g.W - kxb);
     const int pb = (g.block + 3) / 4;                   // patches per block side
+    const int npatch = pb * pb;
     const int64_t plane = (int64_t)g.H * g.W * D;
     const int64_t oplane = (int64_t)g.Ho * g.Wo;
     const __bf16* qs = q + bh * plane;
-    const int jr = p.jr, jp = p.jp, qp = p.qp;
+    const int jr = p.jr, jp = p.jp;
     const int JT = jr / 16;
-    const unsigned offqt = 0, offdt = (unsigned)p.k_off_dot;
-    const unsigned offl = (unsigned)p.k_off_l, offd = (unsigned)p.k_off_d;
+    const unsigned offkv = 0;                           // [patch][K, V][16 keys][D] bf16
     const unsigned offth = (unsigned)p.k_off_tab, offtw = offth + (unsigned)jr * D * 2;
     const unsigned scrh = (unsigned)p.k_off_scr + (unsigned)wave * (unsigned)(2 * 16 * jp * 4);
     const unsigned scrw = scrh + (unsigned)(16 * jp * 4);
+    constexpr unsigned PATB = 16 * D * 2;               // one patch of K (or V)
 
-    // ---- this wave's patches: key (row n >> 2, column n & 3) of patch
-    // wave + 4 kp; K and V as B operands (lane (key n, kg): channels kg*KPL..)
-    FragT kb[KP], vb[KP];
-    f32x4 dKt[KP][MT], dVt[KP][MT];
-    int ky[KP], kx[KP];
-    bool kok[KP], pown[KP];
-#pragma unroll
-    for (int kp = 0; kp < KP; ++kp) {
-        const int pw = wave + kBtWaves * kp;
-        pown[kp] = pw < pb * pb;
-        const int py = pw / pb, px = pw - py * pb;
-        const int ly = 4 * py + (n >> 2), lx = 4 * px + (n & 3);
-        ky[kp] = kyb + ly;
-        kx[kp] = kxb + lx;
-        kok[kp] = pown[kp] && ly < nky && lx < nkx;
-        const int64_t off = bh * plane + ((int64_t)(kok[kp] ? ky[kp] : kyb) * g.W + (kok[kp] ? kx[kp] : kxb)) * D + gq * KPL;
-        kb[kp] = *reinterpret_cast<const FragT*>(k + off);
-        vb[kp] = *reinterpret_cast<const FragT*>(v + off);
-        if (!kok[kp]) {
-#pragma unroll
-            for (int e = 0; e < KPL; ++e) { kb[kp][e] = 0; vb[kp][e] = 0; }
+    // ---- the key block's patches and both tables (zero past the image, the
+    // block, or table row 2r - 1)
+    for (int e = tid; e < npatch * 16 * CPP; e += 64 * kBtWaves) {
+        const int pi = e / (16 * CPP), rr = e - pi * (16 * CPP);
+        const int kn = rr / CPP, ch = rr - kn * CPP;
+        const int py = pi / pb, px = pi - py * pb;
+        const int ly = 4 * py + (kn >> 2), lx = 4 * px + (kn & 3);
+        u32x4 kk{0u, 0u, 0u, 0u}, vv{0u, 0u, 0u, 0u};
+        if (ly < nky && lx < nkx) {
+            const int64_t off = bh * plane + ((int64_t)(kyb + ly) * g.W + kxb + lx) * D + ch * 8;
+            kk = *reinterpret_cast<const u32x4*>(k + off);
+            vv = *reinterpret_cast<const u32x4*>(v + off);
         }
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            dKt[kp][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            dVt[kp][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+        const unsigned a = offkv + (unsigned)pi * 2 * PATB + (unsigned)(kn * D + ch * 8) * 2;
+        bt_st<u32x4>(smem, a, kk);
+        bt_st<u32x4>(smem, a + PATB, vv);
     }
-
-    // ---- tables (zero rows past 2r - 1)
     {
         const int titems = jr * CPP;
         for (int e = tid; e < 2 * titems; e += 64 * kBtWaves) {
@@ -476,144 +472,167 @@ void bwd_key_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             bt_st<u32x4>(smem, (tab ? offtw : offth) + (unsigned)(j * D + ch * 8) * 2, x);
         }
     }
+    __syncthreads();
 
-    // ---- the query blocks whose windows reach this key block
+    // 0/1 operands picking channels 16mt..16mt+15: Q . sel^T is Q's channel
+    // block as an MFMA result, lane (n, g) = channel 16mt + n of queries
+    // 4g..4g+3, i.e. the A operand of the contraction over queries
+    FragT sel[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) sel[mt][e] = (gq * KPL + e == 16 * mt + n) ? (short)0x3F80 : (short)0;
+
     const int A = (g.halo + g.block - 1) / g.block;
-    for (int nby = max(0, kby - A); nby <= min(g.nbh - 1, kby + A); ++nby)
-        for (int nbx = max(0, kbx - A); nbx <= min(g.nbw - 1, kbx + A); ++nbx) {
-            const int wy0 = nby * g.block - g.halo, wx0 = nbx * g.block - g.halo;
-            if (max(kyb, wy0) >= min(kyb + nky, wy0 + r) || max(kxb, wx0) >= min(kxb + nkx, wx0 + r)) continue;
-            const int ybeg = nby * g.block, xbeg = nbx * g.block;
-            const int nqy = (min(ybeg + g.block, g.H) - ybeg + g.stride - 1) / g.stride;
-            const int nqx = (min(xbeg + g.block, g.W) - xbeg + g.stride - 1) / g.stride;
-            const int nq = nqy * nqx;
-            const int tiles = (nq + 15) / 16;
-            __syncthreads();
-            // Q^T and dout^T [channel][query] (zero past nq), lse2 (+inf past
-            // nq: zero weights) and D per query
-            for (int e = tid; e < tiles * 16 * CPP; e += 64 * kBtWaves) {
-                const int qi = e / CPP, ch = e - qi * CPP;
-                u32x4 a{0u, 0u, 0u, 0u}, b{0u, 0u, 0u, 0u};
-                if (qi < nq) {
-                    const int iy = qi / nqx, ix = qi - iy * nqx;
+    const int ny0 = max(0, kby - A), ny1 = min(g.nbh - 1, kby + A);
+    const int nx0 = max(0, kbx - A), nx1 = min(g.nbw - 1, kbx + A);
+    const int npass = (npatch + NPP - 1) / NPP;
+    for (int pass = 0; pass < npass; ++pass) {
+        f32x4 dKt[NPP][MT], dVt[NPP][MT];
+#pragma unroll
+        for (int pp = 0; pp < NPP; ++pp)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                dKt[pp][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                dVt[pp][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        int item0 = 0;                                   // items of the query blocks before this one
+        for (int nby = ny0; nby <= ny1; ++nby)
+            for (int nbx = nx0; nbx <= nx1; ++nbx) {
+                const int wy0 = nby * g.block - g.halo, wx0 = nbx * g.block - g.halo;
+                // patches of this pass inside the window (uniform)
+                unsigned pin = 0u;
+#pragma unroll
+                for (int pp = 0; pp < NPP; ++pp) {
+                    const int pi = pass * NPP + pp;
+                    const int py = pi / pb, px = pi - py * pb;
+                    const int y0 = kyb + 4 * py, x0 = kxb + 4 * px;
+                    const int y1 = min(y0 + 4, kyb + nky), x1 = min(x0 + 4, kxb + nkx);
+                    if (pi < npatch && max(y0, wy0) < min(y1, wy0 + r) && max(x0, wx0) < min(x1, wx0 + r))
+                        pin |= 1u << pp;
+                }
+                if (pin == 0u) continue;
+                const int ybeg = nby * g.block, xbeg = nbx * g.block;
+                const int nqy = (min(ybeg + g.block, g.H) - ybeg + g.stride - 1) / g.stride;
+                const int nqx = (min(xbeg + g.block, g.W) - xbeg + g.stride - 1) / g.stride;
+                const int nq = nqy * nqx;
+                const int tiles = (nq + 15) / 16;
+                const int ufirst = ((wave - item0) % kBtWaves + kBtWaves) % kBtWaves;
+                item0 += tiles;
+                for (int u = ufirst; u < tiles; u += kBtWaves) {
+                    // A operands: lane (query n, kg) = channels kg*KPL.. of query 16u+n
+                    const int qa_i = min(16 * u + n, nq - 1);
+                    const int iy = qa_i / nqx, ix = qa_i - iy * nqx;
                     const int y = ybeg + iy * g.stride, x = xbeg + ix * g.stride;
-                    const int64_t opix = bh * oplane + (int64_t)(y / g.stride) * g.Wo + x / g.stride;
-                    a = *reinterpret_cast<const u32x4*>(qs + ((int64_t)y * g.W + x) * D + ch * 8);
-                    b = *reinterpret_cast<const u32x4*>(dout + opix * D + ch * 8);
-                    if (ch == 0) {
-                        bt_st<float>(smem, offl + (unsigned)qi * 4, lse[opix] * log2e);
-                        bt_st<float>(smem, offd + (unsigned)qi * 4, dsum[opix]);
-                    }
-                } else if (ch == 0) {
-                    bt_st<float>(smem, offl + (unsigned)qi * 4, INFINITY);
-                    bt_st<float>(smem, offd + (unsigned)qi * 4, 0.f);
-                }
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const unsigned c0 = (unsigned)(ch * 8 + 2 * w);
-                    bt_st<unsigned short>(smem, offqt + (c0 * qp + qi) * 2, (unsigned short)(a[w] & 0xffffu));
-                    bt_st<unsigned short>(smem, offqt + ((c0 + 1) * qp + qi) * 2, (unsigned short)(a[w] >> 16));
-                    bt_st<unsigned short>(smem, offdt + (c0 * qp + qi) * 2, (unsigned short)(b[w] & 0xffffu));
-                    bt_st<unsigned short>(smem, offdt + ((c0 + 1) * qp + qi) * 2, (unsigned short)(b[w] >> 16));
-                }
-            }
-            __syncthreads();
-
-            // patches of this wave inside the window (uniform per wave)
-            bool pin[KP];
-            bool any = false;
-#pragma unroll
-            for (int kp = 0; kp < KP; ++kp) {
-                const int pw = wave + kBtWaves * kp;
-                const int py = pw / pb, px = pw - py * pb;
-                const int y0 = kyb + 4 * py, x0 = kxb + 4 * px;
-                pin[kp] = pown[kp] && max(y0, wy0) < min(y0 + 4, wy0 + r) && max(x0, wx0) < min(x0 + 4, wx0 + r);
-                any |= pin[kp];
-            }
-            if (!any) continue;
-
-            for (int u = 0; u < tiles; ++u) {
-                // A operands: lane (query n, kg) = channels kg*KPL.. of query 16u+n
-                const int qa_i = min(16 * u + n, nq - 1);
-                int iy = qa_i / nqx, ix = qa_i - iy * nqx;
-                int y = ybeg + iy * g.stride, x = xbeg + ix * g.stride;
-                const int64_t opa = bh * oplane + (int64_t)(y / g.stride) * g.Wo + x / g.stride;
-                FragT qa = *reinterpret_cast<const FragT*>(qs + ((int64_t)y * g.W + x) * D + gq * KPL);
-                const FragT da = *reinterpret_cast<const FragT*>(dout + opa * D + gq * KPL);
-                // q.rel_h[j] and q.rel_w[j] of the tile's queries: scratch[query][j]
-                for (int jt = 0; jt < JT; ++jt) {
-                    const FragT ah = bt_ld<FragT>(smem, offth + (unsigned)((16 * jt + n) * D + gq * KPL) * 2);
-                    const FragT aw = bt_ld<FragT>(smem, offtw + (unsigned)((16 * jt + n) * D + gq * KPL) * 2);
-                    bt_st<f32x4>(smem, scrh + (unsigned)(n * jp + 16 * jt + 4 * gq) * 4,
-                                 Frag<D>::mma(ah, qa, f32x4{0.f, 0.f, 0.f, 0.f}));
-                    bt_st<f32x4>(smem, scrw + (unsigned)(n * jp + 16 * jt + 4 * gq) * 4,
-                                 Frag<D>::mma(aw, qa, f32x4{0.f, 0.f, 0.f, 0.f}));
-                }
-                // this lane's four queries 16u + 4g + i: positions, lse2, D
-                int bhq[4], bwq[4];
-                float l2[4], dd[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int qq = 16 * u + 4 * gq + i;
-                    const int qv = min(qq, nq - 1);
-                    const int jy = qv / nqx, jx = qv - jy * nqx;
-                    const int yq = ybeg + jy * g.stride, xq = xbeg + jx * g.stride;
-                    bhq[i] = (4 * gq + i) * jp + g.c0 - yq;
-                    bwq[i] = (4 * gq + i) * jp + g.c0 - xq;
-                    l2[i] = bt_ld<float>(smem, offl + (unsigned)qq * 4);
-                    dd[i] = bt_ld<float>(smem, offd + (unsigned)qq * 4);
-                }
-                // Q^T and dout^T fragments: lane (channel 16mt + n, kg) = queries 4kg..4kg+3
-                s16x4_t qt[MT], dt[MT];
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const unsigned o = (unsigned)((16 * mt + n) * qp + 16 * u + 4 * gq) * 2;
-                    qt[mt] = __builtin_bit_cast(s16x4_t, bt_ld<u32x2>(smem, offqt + o));
-                    dt[mt] = __builtin_bit_cast(s16x4_t, bt_ld<u32x2>(smem, offdt + o));
-                }
-#pragma unroll
-                for (int kp = 0; kp < KP; ++kp) {
-                    if (!pin[kp]) continue;
-                    const bool inw = kok[kp] && ky[kp] >= wy0 && ky[kp] < wy0 + r && kx[kp] >= wx0 && kx[kp] < wx0 + r;
-                    f32x4 cin;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int ih = inw ? bhq[i] + ky[kp] : 0, iw = inw ? bwq[i] + kx[kp] : 0;
-                        const float rel = bt_ld<float>(smem, scrh + (unsigned)ih * 4) + bt_ld<float>(smem, scrw + (unsigned)iw * 4);
-                        cin[i] = inw ? rel : kMaskLogit;
-                    }
-                    const f32x4 s = Frag<D>::mma(qa, kb[kp], cin);
-                    const f32x4 dp = Frag<D>::mma(da, vb[kp], f32x4{0.f, 0.f, 0.f, 0.f});
-                    f32x4 pr, ds;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        pr[i] = __builtin_amdgcn_exp2f(fmaf(s[i], alpha, -l2[i]));
-                        ds[i] = pr[i] * (dp[i] - dd[i]);
-                    }
-                    const s16x4_t pb4 = bf16x4_of(pr[0], pr[1], pr[2], pr[3]);
-                    const s16x4_t db4 = bf16x4_of(ds[0], ds[1], ds[2], ds[3]);
+                    const int64_t opa = bh * oplane + (int64_t)(y / g.stride) * g.Wo + x / g.stride;
+                    const FragT qa = *reinterpret_cast<const FragT*>(qs + ((int64_t)y * g.W + x) * D + gq * KPL);
+                    const FragT da = *reinterpret_cast<const FragT*>(dout + opa * D + gq * KPL);
+                    // Q^T and dout^T fragments (lane (channel n, kg) = queries 4kg..4kg+3)
+                    s16x4_t qt[MT], dt[MT];
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) {
-                        dVt[kp][mt] = mma16(dt[mt], pb4, dVt[kp][mt]);
-                        dKt[kp][mt] = mma16(qt[mt], db4, dKt[kp][mt]);
+                        const f32x4 a = Frag<D>::mma(qa, sel[mt], f32x4{0.f, 0.f, 0.f, 0.f});
+                        const f32x4 b = Frag<D>::mma(da, sel[mt], f32x4{0.f, 0.f, 0.f, 0.f});
+                        qt[mt] = bf16x4_of(a[0], a[1], a[2], a[3]);
+                        dt[mt] = bf16x4_of(b[0], b[1], b[2], b[3]);
+                    }
+                    // q.rel_h[j] and q.rel_w[j] of the tile's queries: scratch[query][j]
+                    for (int jt = 0; jt < JT; ++jt) {
+                        const FragT ah = bt_ld<FragT>(smem, offth + (unsigned)((16 * jt + n) * D + gq * KPL) * 2);
+                        const FragT aw = bt_ld<FragT>(smem, offtw + (unsigned)((16 * jt + n) * D + gq * KPL) * 2);
+                        bt_st<f32x4>(smem, scrh + (unsigned)(n * jp + 16 * jt + 4 * gq) * 4,
+                                     Frag<D>::mma(ah, qa, f32x4{0.f, 0.f, 0.f, 0.f}));
+                        bt_st<f32x4>(smem, scrw + (unsigned)(n * jp + 16 * jt + 4 * gq) * 4,
+                                     Frag<D>::mma(aw, qa, f32x4{0.f, 0.f, 0.f, 0.f}));
+                    }
+                    // this lane's four queries 16u + 4g + i: scratch bases, lse2, D
+                    // (past nq: +inf, so their weights are 0)
+                    int bhq[4], bwq[4];
+                    float l2[4], dd[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int qq = 16 * u + 4 * gq + i;
+                        const int qv = min(qq, nq - 1);
+                        const int jy = qv / nqx, jx = qv - jy * nqx;
+                        const int yq = ybeg + jy * g.stride, xq = xbeg + jx * g.stride;
+                        const int64_t op = bh * oplane + (int64_t)(yq / g.stride) * g.Wo + xq / g.stride;
+                        bhq[i] = (4 * gq + i) * jp + g.c0 - yq;
+                        bwq[i] = (4 * gq + i) * jp + g.c0 - xq;
+                        l2[i] = qq < nq ? lse[op] * log2e : INFINITY;
+                        dd[i] = dsum[op];
+                    }
+#pragma unroll
+                    for (int pp = 0; pp < NPP; ++pp) {
+                        if (!(pin & (1u << pp))) continue;
+                        const int pi = pass * NPP + pp;
+                        const int py = pi / pb, px = pi - py * pb;
+                        const int ly = 4 * py + (n >> 2), lx = 4 * px + (n & 3);
+                        const int ky = kyb + ly, kx = kxb + lx;
+                        const bool inw = ly < nky && lx < nkx && ky >= wy0 && ky < wy0 + r && kx >= wx0 && kx < wx0 + r;
+                        const unsigned pa = offkv + (unsigned)pi * 2 * PATB + (unsigned)(n * D + gq * KPL) * 2;
+                        const FragT kb = bt_ld<FragT>(smem, pa);
+                        const FragT vb = bt_ld<FragT>(smem, pa + PATB);
+                        f32x4 cin;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int ih = inw ? bhq[i] + ky : 0, iw = inw ? bwq[i] + kx : 0;
+                            const float rel = bt_ld<float>(smem, scrh + (unsigned)ih * 4) +
+                                              bt_ld<float>(smem, scrw + (unsigned)iw * 4);
+                            cin[i] = inw ? rel : kMaskLogit;
+                        }
+                        const f32x4 s = Frag<D>::mma(qa, kb, cin);
+                        const f32x4 dp = Frag<D>::mma(da, vb, f32x4{0.f, 0.f, 0.f, 0.f});
+                        f32x4 pr, ds;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            pr[i] = __builtin_amdgcn_exp2f(fmaf(s[i], alpha, -l2[i]));
+                            ds[i] = pr[i] * (dp[i] - dd[i]);
+                        }
+                        const s16x4_t pb4 = bf16x4_of(pr[0], pr[1], pr[2], pr[3]);
+                        const s16x4_t db4 = bf16x4_of(ds[0], ds[1], ds[2], ds[3]);
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) {
+                            dVt[pp][mt] = mma16(dt[mt], pb4, dVt[pp][mt]);
+                            dKt[pp][mt] = mma16(qt[mt], db4, dKt[pp][mt]);
+                        }
                     }
                 }
             }
-        }
 
-    // ---- dk, dv of this wave's keys: lane (key n, g) holds channels 16mt + 4g..
+        // ---- sums over the waves in wave order (waves 0-2 through LDS, the
+        // last wave adds its own and writes dk, dv); the LDS of the staged
+        // patches is free once every wave is past the first barrier
+        float* red = reinterpret_cast<float*>(smem + p.k_off_red);
+        for (int w = 0; w < kBtWaves; ++w) {
+            __syncthreads();
+            if (wave != w) continue;
 #pragma unroll
-    for (int kp = 0; kp < KP; ++kp) {
-        if (!kok[kp]) continue;
-        const int64_t off = bh * plane + ((int64_t)ky[kp] * g.W + kx[kp]) * D + 4 * gq;
+            for (int pp = 0; pp < NPP; ++pp)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            *reinterpret_cast<u32x2*>(dk + off + 16 * mt) =
-                u32x2{pack_bf16x2(g.scale * dKt[kp][mt][0], g.scale * dKt[kp][mt][1]),
-                      pack_bf16x2(g.scale * dKt[kp][mt][2], g.scale * dKt[kp][mt][3])};
-            *reinterpret_cast<u32x2*>(dv + off + 16 * mt) =
-                u32x2{pack_bf16x2(dVt[kp][mt][0], dVt[kp][mt][1]), pack_bf16x2(dVt[kp][mt][2], dVt[kp][mt][3])};
+                for (int mt = 0; mt < MT; ++mt) {
+                    f32x4* rk = reinterpret_cast<f32x4*>(red) + ((pp * MT + mt) * 2) * 64 + lane;
+                    f32x4* rv = rk + 64;
+                    f32x4 ak = dKt[pp][mt], av = dVt[pp][mt];
+                    if (w > 0) { ak = *rk + ak; av = *rv + av; }
+                    if (w < kBtWaves - 1) {
+                        *rk = ak;
+                        *rv = av;
+                        continue;
+                    }
+                    // dk, dv: lane (key n, g) holds channels 16mt + 4g..4g+3
+                    const int pi = pass * NPP + pp;
+                    if (pi >= npatch) continue;
+                    const int py = pi / pb, px = pi - py * pb;
+                    const int ly = 4 * py + (n >> 2), lx = 4 * px + (n & 3);
+                    if (ly >= nky || lx >= nkx) continue;
+                    const int64_t off = bh * plane + ((int64_t)(kyb + ly) * g.W + kxb + lx) * D + 16 * mt + 4 * gq;
+                    *reinterpret_cast<u32x2*>(dk + off) =
+                        u32x2{pack_bf16x2(g.scale * ak[0], g.scale * ak[1]), pack_bf16x2(g.scale * ak[2], g.scale * ak[3])};
+                    *reinterpret_cast<u32x2*>(dv + off) =
+                        u32x2{pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3])};
+                }
         }
+        __syncthreads();
     }
 }
 
@@ -625,11 +644,8 @@ __global__ void bt_zero_u16(unsigned short* __restrict__ p, int64_t n)
 
 // ---------------------------------------------------------------- planning
 static int bt_np(int r) { return r <= 16 ? 4 : r <= 20 ? 5 : r <= 24 ? 6 : 8; }
-static int bt_kp(int block)
-{
-    const int pb = (block + 3) / 4;
-    return (pb * pb + kBtWaves - 1) / kBtWaves;
-}
+// key patches a wave carries per pass (its dk^T, dv^T sums in registers)
+static int bt_npp(int d) { return d == 16 ? 16 : 9; }
 
 static BwdTilePlan bt_plan(const Geometry& g)
 {
@@ -650,15 +666,16 @@ static BwdTilePlan bt_plan(const Geometry& g)
     const int red = kBtWaves * 2 * p.jr * g.d * 4;     // the partials' reduction reuses the window space
     if (red > p.q_off_tab) return BwdTilePlan{};       // does not fit under the tables
     p.q_nwg = g.BH * g.nbh * g.nbw;
-    const int side = (g.block + g.stride - 1) / g.stride;
-    p.nqpad = (side * side + 15) / 16 * 16;
-    p.qp = (p.nqpad + 31) / 32 * 32 + 16;              // qp/2 = 8 (mod 16) dwords
-    p.k_off_dot = g.d * p.qp * 2;
-    p.k_off_l = 2 * p.k_off_dot;
-    p.k_off_d = p.k_off_l + p.nqpad * 4;
-    p.k_off_tab = p.k_off_d + p.nqpad * 4;
+    // key kernel: the block's patches (K and V), the tables, the waves'
+    // scratch; the wave-order sums of dk^T and dv^T reuse the scratch
+    const int pb = (g.block + 3) / 4;
+    const int npp = bt_npp(g.d);
+    p.k_off_tab = pb * pb * 2 * 16 * g.d * 2;
     p.k_off_scr = p.k_off_tab + 2 * p.jr * g.d * 2;
-    p.k_lds = p.k_off_scr + kBtWaves * 2 * 16 * p.jp * 4;
+    p.k_off_red = p.k_off_scr;
+    const int scr = kBtWaves * 2 * 16 * p.jp * 4;
+    const int redb = npp * (g.d / 16) * 2 * 64 * 16;
+    p.k_lds = p.k_off_scr + std::max(scr, redb);
     p.k_nwg = p.q_nwg;
     p.alpha = (float)((double)g.scale * 1.4426950408889634);
     return p;
@@ -692,12 +709,12 @@ static hipError_t bt_query_launch(const void* q, const void* k, const void* v, c
     return hipGetLastError();
 }
 
-template <int D, int KP>
+template <int D, int NPP>
 static hipError_t bt_key_launch(const void* q, const void* k, const void* v, const void* rh, const void* rw,
                                 const void* dout, const float* lse, const float* dsum, void* dk, void* dv,
                                 const Geometry& g, const BwdTilePlan& p, hipStream_t st)
 {
-    auto kern = bwd_key_kernel<D, KP>;
+    auto kern = bwd_key_kernel<D, NPP>;
     const hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), p.k_lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)p.k_nwg), dim3(64 * kBtWaves), p.k_lds, st,
@@ -719,18 +736,6 @@ static hipError_t bt_query_np(const void* q, const void* k, const void* v, const
     }
 }
 
-template <int D>
-static hipError_t bt_key_kp(const void* q, const void* k, const void* v, const void* rh, const void* rw,
-                            const void* dout, const float* lse, const float* dsum, void* dk, void* dv,
-                            const Geometry& g, const BwdTilePlan& p, hipStream_t st)
-{
-    switch (bt_kp(g.block)) {
-    case 1: return bt_key_launch<D, 1>(q, k, v, rh, rw, dout, lse, dsum, dk, dv, g, p, st);
-    case 3: return bt_key_launch<D, 3>(q, k, v, rh, rw, dout, lse, dsum, dk, dv, g, p, st);
-    default: return bt_key_launch<D, 4>(q, k, v, rh, rw, dout, lse, dsum, dk, dv, g, p, st);
-    }
-}
-
 // dq (zeroed first where queries are strided: only query pixels receive a
 // gradient), D per query into dsum, table partials, then dk and dv.
 hipError_t launch_bwd_tile(const void* q, const void* k, const void* v, const void* rh, const void* rw,
@@ -746,8 +751,8 @@ hipError_t launch_bwd_tile(const void* q, const void* k, const void* v, const vo
     hipError_t e = g.d == 16 ? bt_query_np<16>(q, k, v, rh, rw, out, dout, lse, dq, dsum, part_rel, g, p, st)
                              : bt_query_np<32>(q, k, v, rh, rw, out, dout, lse, dq, dsum, part_rel, g, p, st);
     if (e != hipSuccess) return e;
-    return g.d == 16 ? bt_key_kp<16>(q, k, v, rh, rw, dout, lse, dsum, dk, dv, g, p, st)
-                     : bt_key_kp<32>(q, k, v, rh, rw, dout, lse, dsum, dk, dv, g, p, st);
+    return g.d == 16 ? bt_key_launch<16, 16>(q, k, v, rh, rw, dout, lse, dsum, dk, dv, g, p, st)
+                     : bt_key_launch<32, 9>(q, k, v, rh, rw, dout, lse, dsum, dk, dv, g, p, st);
 }
 
 }  // namespace halo

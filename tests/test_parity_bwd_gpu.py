@@ -139,6 +139,7 @@ TILE_SHAPES = [
     (1, 1, 40, 40, 16, 16, 8, 1),    # r = 32, d = 16
     (1, 2, 24, 21, 16, 6, 3, 3),     # block 6 (patches cross the block edge), partial, stride 3
     (2, 1, 12, 12, 32, 12, 0, 1),    # h = 0: windows are the blocks
+    (1, 2, 40, 36, 32, 16, 4, 1),    # 16 key patches per block at d = 32: two passes of the key kernel
 ]
 
 
