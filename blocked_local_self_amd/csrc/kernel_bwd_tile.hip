@@ -40,6 +40,7 @@
 //    with no atomics.
 // Every sum runs in a fixed order: results are bitwise reproducible.
 #include <algorithm>
+#include <type_traits>
 
 #include "mfma_util.h"
 
@@ -56,7 +57,7 @@ struct BwdTilePlan {
     int q_off_v, q_off_tab, q_off_scr, q_lds;
     int64_t q_nwg;
     // key kernel
-    int k_off_tab, k_off_scr, k_off_red, k_lds;
+    int k_off_tab, k_off_scr, k_off_red, k_off_nb, k_lds;
     int64_t k_nwg;
     float alpha;       // scale * log2(e)
 };
@@ -94,6 +95,10 @@ __device__ inline void split4(f32x4 x, s16x4_t& hi, s16x4_t& lo)
     const float h2 = __builtin_bit_cast(float, h[1] << 16), h3 = __builtin_bit_cast(float, h[1] & 0xffff0000u);
     lo = bf16x4_of(x[0] - h0, x[1] - h1, x[2] - h2, x[3] - h3);
 }
+
+// a / d for 0 <= a < 2^20 from rd = 1/d (one ulp): (a + 1/2)/d is at least
+// 1/(2d) from an integer, far above the rounding error
+__device__ inline int bt_div(int a, float rd) { return (int)(((float)a + 0.5f) * rd); }
 
 // Byte offset of channel chunk `c` (16 bytes) of the staged window pixel in
 // row t: chunks rotate with the row so the four rows of a patch spread over
@@ -140,6 +145,8 @@ void bwd_query_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
     const int nqx = (min(xbeg + g.block, g.W) - xbeg + g.stride - 1) / g.stride;
     const int nq = nqy * nqx;
     const int tiles = (nq + 15) / 16;
+    const float rnqx = __builtin_amdgcn_rcpf((float)nqx);
+    const int bs = g.block / g.stride;                  // query rows / columns of a full block
     const int64_t plane = (int64_t)g.H * g.W * D;
     const int64_t oplane = (int64_t)g.Ho * g.Wo;
     const __bf16* qs = q + bh * plane;
@@ -153,20 +160,35 @@ void bwd_query_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
     // ---- stage the window (K and V, zero outside the image or the window)
     // and both tables (zero rows past 2r - 1)
     {
+        // SB items per thread in flight: every load of a batch is issued
+        // before its stores
+        constexpr int SB = 8;
         const int items = rp * rp * CPP;
-        for (int e = tid; e < items; e += 64 * kBtWaves) {
-            const int t = e / (rp * CPP), rr = e - t * (rp * CPP);
-            const int c = rr / CPP, ch = rr - c * CPP;
-            const int y = wy0 + t, x = wx0 + c;
-            u32x4 kk{0u, 0u, 0u, 0u}, vv{0u, 0u, 0u, 0u};
-            if (t < r && c < r && y >= 0 && y < g.H && x >= 0 && x < g.W) {
-                const int64_t off = bh * plane + ((int64_t)y * g.W + x) * D + ch * 8;
-                kk = *reinterpret_cast<const u32x4*>(k + off);
-                vv = *reinterpret_cast<const u32x4*>(v + off);
+        const float rrow = __builtin_amdgcn_rcpf((float)(rp * CPP));
+        for (int e0 = tid; e0 < items; e0 += SB * 64 * kBtWaves) {
+            u32x4 kk[SB], vv[SB];
+            unsigned a[SB];
+#pragma unroll
+            for (int b = 0; b < SB; ++b) {
+                const int e = e0 + b * 64 * kBtWaves;
+                const int t = bt_div(e, rrow), rr = e - t * (rp * CPP);
+                const int c = rr / CPP, ch = rr - c * CPP;
+                const int y = wy0 + t, x = wx0 + c;
+                kk[b] = u32x4{0u, 0u, 0u, 0u};
+                vv[b] = u32x4{0u, 0u, 0u, 0u};
+                a[b] = (unsigned)t * rowb + (unsigned)c * PIXB + bt_chunk<D>(ch, t);
+                if (e < items && t < r && c < r && y >= 0 && y < g.H && x >= 0 && x < g.W) {
+                    const int64_t off = bh * plane + ((int64_t)y * g.W + x) * D + ch * 8;
+                    kk[b] = *reinterpret_cast<const u32x4*>(k + off);
+                    vv[b] = *reinterpret_cast<const u32x4*>(v + off);
+                }
             }
-            const unsigned a = (unsigned)t * rowb + (unsigned)c * PIXB + bt_chunk<D>(ch, t);
-            bt_st<u32x4>(smem, a, kk);
-            bt_st<u32x4>(smem, offv + a, vv);
+#pragma unroll
+            for (int b = 0; b < SB; ++b) {
+                if (e0 + b * 64 * kBtWaves >= items) break;
+                bt_st<u32x4>(smem, a[b], kk[b]);
+                bt_st<u32x4>(smem, offv + a[b], vv[b]);
+            }
         }
         const int titems = jr * CPP;
         for (int e = tid; e < 2 * titems; e += 64 * kBtWaves) {
@@ -195,10 +217,10 @@ void bwd_query_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
         const int qi = 16 * u + n;
         const bool valid = qi < nq;
         const int qc = valid ? qi : 0;
-        const int iy = qc / nqx, ix = qc - iy * nqx;
+        const int iy = bt_div(qc, rnqx), ix = qc - iy * nqx;
         const int y = ybeg + iy * g.stride, x = xbeg + ix * g.stride;
         const int yl = y - wy0, xl = x - wx0;
-        const int64_t opix = bh * oplane + (int64_t)(y / g.stride) * g.Wo + x / g.stride;
+        const int64_t opix = bh * oplane + (int64_t)(by * bs + iy) * g.Wo + bx * bs + ix;
         FragT qf = *reinterpret_cast<const FragT*>(qs + ((int64_t)y * g.W + x) * D + gq * KPL);
         FragT df = *reinterpret_cast<const FragT*>(dout + opix * D + gq * KPL);
         const FragT of = *reinterpret_cast<const FragT*>(out + opix * D + gq * KPL);
@@ -398,14 +420,16 @@ void bwd_query_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
 }
 
 // --------------------------------------------------------------------- keys
-// One workgroup per key block.  The block's keys, cut into 4x4 patches, are
-// staged once (K and V as B operands: lane (key n, kg) = channels kg*KPL..).
-// The work items are the 16-query tiles of every query block whose window
-// reaches the key block, in a fixed order; wave w takes items w, w+4, ...
-// and, for its tile, every patch inside that window (up to NPP patches per
-// pass; wider blocks take several passes).  The waves' dk^T and dv^T sums are
-// added in wave order through LDS at the end.
-template <int D, int NPP>
+// One workgroup per key block.  The block's keys, cut into PB x PB patches
+// of 4x4, are staged once (K and V as B operands: lane (key n, kg) =
+// channels kg*KPL..).  The work items are the 16-query tiles of every query
+// block whose window reaches the key block, in a fixed order; wave w takes
+// items w, w+4, ... and, for its tile, every patch inside that window (the
+// patches in registers per pass: two passes for 16 patches at d = 32).
+// Patches wholly inside the window and the image take an unmasked path.
+// The waves' dk^T and dv^T sums are added in wave order through LDS at the
+// end.
+template <int D, int PB>
 __global__ __launch_bounds__(64 * kBtWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_key_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                     const __bf16* __restrict__ v, const __bf16* __restrict__ rel_h,
@@ -416,6 +440,9 @@ void bwd_key_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     constexpr int KPL = D / 4;
     constexpr int CPP = D / 8;
     constexpr int MT = D / 16;
+    constexpr int NPATCH = PB * PB;
+    constexpr int NPASS = (D == 32 && NPATCH > 9) ? 2 : 1;
+    constexpr int NPP = (NPATCH + NPASS - 1) / NPASS;
     typedef typename Frag<D>::T FragT;
     extern __shared__ __align__(16) unsigned char smem[];
 
@@ -432,8 +459,7 @@ void bwd_key_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const int kby = rem / g.nbw, kbx = rem - kby * g.nbw;
     const int kyb = kby * g.block, kxb = kbx * g.block;
     const int nky = min(g.block, g.H - kyb), nkx = min(g.block, g.W - kxb);
-    const int pb = (g.block + 3) / 4;                   // patches per block side
-    const int npatch = pb * pb;
+    const int bs = g.block / g.stride;
     const int64_t plane = (int64_t)g.H * g.W * D;
     const int64_t oplane = (int64_t)g.Ho * g.Wo;
     const __bf16* qs = q + bh * plane;
@@ -447,20 +473,33 @@ void bwd_key_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 
     // ---- the key block's patches and both tables (zero past the image, the
     // block, or table row 2r - 1)
-    for (int e = tid; e < npatch * 16 * CPP; e += 64 * kBtWaves) {
-        const int pi = e / (16 * CPP), rr = e - pi * (16 * CPP);
-        const int kn = rr / CPP, ch = rr - kn * CPP;
-        const int py = pi / pb, px = pi - py * pb;
-        const int ly = 4 * py + (kn >> 2), lx = 4 * px + (kn & 3);
-        u32x4 kk{0u, 0u, 0u, 0u}, vv{0u, 0u, 0u, 0u};
-        if (ly < nky && lx < nkx) {
-            const int64_t off = bh * plane + ((int64_t)(kyb + ly) * g.W + kxb + lx) * D + ch * 8;
-            kk = *reinterpret_cast<const u32x4*>(k + off);
-            vv = *reinterpret_cast<const u32x4*>(v + off);
+    {
+        // all of a thread's items in flight at once (loads, then stores)
+        constexpr int SB = (NPATCH * 16 * CPP + 64 * kBtWaves - 1) / (64 * kBtWaves);
+        u32x4 kk[SB], vv[SB];
+        unsigned a[SB];
+#pragma unroll
+        for (int b = 0; b < SB; ++b) {
+            const int e = tid + b * 64 * kBtWaves;
+            const int pi = e / (16 * CPP), rr = e - pi * (16 * CPP);
+            const int kn = rr / CPP, ch = rr - kn * CPP;
+            const int py = pi / PB, px = pi - py * PB;
+            const int ly = 4 * py + (kn >> 2), lx = 4 * px + (kn & 3);
+            kk[b] = u32x4{0u, 0u, 0u, 0u};
+            vv[b] = u32x4{0u, 0u, 0u, 0u};
+            a[b] = offkv + (unsigned)pi * 2 * PATB + (unsigned)(kn * D + ch * 8) * 2;
+            if (e < NPATCH * 16 * CPP && ly < nky && lx < nkx) {
+                const int64_t off = bh * plane + ((int64_t)(kyb + ly) * g.W + kxb + lx) * D + ch * 8;
+                kk[b] = *reinterpret_cast<const u32x4*>(k + off);
+                vv[b] = *reinterpret_cast<const u32x4*>(v + off);
+            }
         }
-        const unsigned a = offkv + (unsigned)pi * 2 * PATB + (unsigned)(kn * D + ch * 8) * 2;
-        bt_st<u32x4>(smem, a, kk);
-        bt_st<u32x4>(smem, a + PATB, vv);
+#pragma unroll
+        for (int b = 0; b < SB; ++b) {
+            if (tid + b * 64 * kBtWaves >= NPATCH * 16 * CPP) break;
+            bt_st<u32x4>(smem, a[b], kk[b]);
+            bt_st<u32x4>(smem, a[b] + PATB, vv[b]);
+        }
     }
     {
         const int titems = jr * CPP;
@@ -486,8 +525,10 @@ void bwd_key_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const int A = (g.halo + g.block - 1) / g.block;
     const int ny0 = max(0, kby - A), ny1 = min(g.nbh - 1, kby + A);
     const int nx0 = max(0, kbx - A), nx1 = min(g.nbw - 1, kbx + A);
-    const int npass = (npatch + NPP - 1) / NPP;
-    for (int pass = 0; pass < npass; ++pass) {
+    const int nnx = nx1 - nx0 + 1, nnb = (ny1 - ny0 + 1) * nnx;
+    i32x4* nbinfo = reinterpret_cast<i32x4*>(smem + p.k_off_nb);
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) {
         f32x4 dKt[NPP][MT], dVt[NPP][MT];
 #pragma unroll
         for (int pp = 0; pp < NPP; ++pp)
@@ -496,112 +537,168 @@ void bwd_key_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 dKt[pp][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
                 dVt[pp][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
-        int item0 = 0;                                   // items of the query blocks before this one
-        for (int nby = ny0; nby <= ny1; ++nby)
-            for (int nbx = nx0; nbx <= nx1; ++nbx) {
-                const int wy0 = nby * g.block - g.halo, wx0 = nbx * g.block - g.halo;
-                // patches of this pass inside the window (uniform)
-                unsigned pin = 0u;
+        // the query blocks whose windows reach this key block, in row-major
+        // order: {query columns, query count (0: no patch of this pass in
+        // the window), patches meeting the window | patches wholly in it
+        // and in the image << 16, 16-query tiles}
+        for (int b = tid; b < nnb; b += 64 * kBtWaves) {
+            const int nby = ny0 + b / nnx, nbx = nx0 + b % nnx;
+            const int wy0 = nby * g.block - g.halo, wx0 = nbx * g.block - g.halo;
+            unsigned pin = 0u, full = 0u;
 #pragma unroll
-                for (int pp = 0; pp < NPP; ++pp) {
-                    const int pi = pass * NPP + pp;
-                    const int py = pi / pb, px = pi - py * pb;
-                    const int y0 = kyb + 4 * py, x0 = kxb + 4 * px;
-                    const int y1 = min(y0 + 4, kyb + nky), x1 = min(x0 + 4, kxb + nkx);
-                    if (pi < npatch && max(y0, wy0) < min(y1, wy0 + r) && max(x0, wx0) < min(x1, wx0 + r))
-                        pin |= 1u << pp;
-                }
-                if (pin == 0u) continue;
-                const int ybeg = nby * g.block, xbeg = nbx * g.block;
-                const int nqy = (min(ybeg + g.block, g.H) - ybeg + g.stride - 1) / g.stride;
-                const int nqx = (min(xbeg + g.block, g.W) - xbeg + g.stride - 1) / g.stride;
-                const int nq = nqy * nqx;
-                const int tiles = (nq + 15) / 16;
-                const int ufirst = ((wave - item0) % kBtWaves + kBtWaves) % kBtWaves;
-                item0 += tiles;
-                for (int u = ufirst; u < tiles; u += kBtWaves) {
-                    // A operands: lane (query n, kg) = channels kg*KPL.. of query 16u+n
-                    const int qa_i = min(16 * u + n, nq - 1);
-                    const int iy = qa_i / nqx, ix = qa_i - iy * nqx;
-                    const int y = ybeg + iy * g.stride, x = xbeg + ix * g.stride;
-                    const int64_t opa = bh * oplane + (int64_t)(y / g.stride) * g.Wo + x / g.stride;
-                    const FragT qa = *reinterpret_cast<const FragT*>(qs + ((int64_t)y * g.W + x) * D + gq * KPL);
-                    const FragT da = *reinterpret_cast<const FragT*>(dout + opa * D + gq * KPL);
-                    // Q^T and dout^T fragments (lane (channel n, kg) = queries 4kg..4kg+3)
-                    s16x4_t qt[MT], dt[MT];
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) {
-                        const f32x4 a = Frag<D>::mma(qa, sel[mt], f32x4{0.f, 0.f, 0.f, 0.f});
-                        const f32x4 b = Frag<D>::mma(da, sel[mt], f32x4{0.f, 0.f, 0.f, 0.f});
-                        qt[mt] = bf16x4_of(a[0], a[1], a[2], a[3]);
-                        dt[mt] = bf16x4_of(b[0], b[1], b[2], b[3]);
-                    }
-                    // q.rel_h[j] and q.rel_w[j] of the tile's queries: scratch[query][j]
-                    for (int jt = 0; jt < JT; ++jt) {
-                        const FragT ah = bt_ld<FragT>(smem, offth + (unsigned)((16 * jt + n) * D + gq * KPL) * 2);
-                        const FragT aw = bt_ld<FragT>(smem, offtw + (unsigned)((16 * jt + n) * D + gq * KPL) * 2);
-                        bt_st<f32x4>(smem, scrh + (unsigned)(n * jp + 16 * jt + 4 * gq) * 4,
-                                     Frag<D>::mma(ah, qa, f32x4{0.f, 0.f, 0.f, 0.f}));
-                        bt_st<f32x4>(smem, scrw + (unsigned)(n * jp + 16 * jt + 4 * gq) * 4,
-                                     Frag<D>::mma(aw, qa, f32x4{0.f, 0.f, 0.f, 0.f}));
-                    }
-                    // this lane's four queries 16u + 4g + i: scratch bases, lse2, D
-                    // (past nq: +inf, so their weights are 0)
-                    int bhq[4], bwq[4];
-                    float l2[4], dd[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int qq = 16 * u + 4 * gq + i;
-                        const int qv = min(qq, nq - 1);
-                        const int jy = qv / nqx, jx = qv - jy * nqx;
-                        const int yq = ybeg + jy * g.stride, xq = xbeg + jx * g.stride;
-                        const int64_t op = bh * oplane + (int64_t)(yq / g.stride) * g.Wo + xq / g.stride;
-                        bhq[i] = (4 * gq + i) * jp + g.c0 - yq;
-                        bwq[i] = (4 * gq + i) * jp + g.c0 - xq;
-                        l2[i] = qq < nq ? lse[op] * log2e : INFINITY;
-                        dd[i] = dsum[op];
-                    }
-#pragma unroll
-                    for (int pp = 0; pp < NPP; ++pp) {
-                        if (!(pin & (1u << pp))) continue;
-                        const int pi = pass * NPP + pp;
-                        const int py = pi / pb, px = pi - py * pb;
-                        const int ly = 4 * py + (n >> 2), lx = 4 * px + (n & 3);
-                        const int ky = kyb + ly, kx = kxb + lx;
-                        const bool inw = ly < nky && lx < nkx && ky >= wy0 && ky < wy0 + r && kx >= wx0 && kx < wx0 + r;
-                        const unsigned pa = offkv + (unsigned)pi * 2 * PATB + (unsigned)(n * D + gq * KPL) * 2;
-                        const FragT kb = bt_ld<FragT>(smem, pa);
-                        const FragT vb = bt_ld<FragT>(smem, pa + PATB);
-                        f32x4 cin;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int ih = inw ? bhq[i] + ky : 0, iw = inw ? bwq[i] + kx : 0;
-                            const float rel = bt_ld<float>(smem, scrh + (unsigned)ih * 4) +
-                                              bt_ld<float>(smem, scrw + (unsigned)iw * 4);
-                            cin[i] = inw ? rel : kMaskLogit;
-                        }
-                        const f32x4 s = Frag<D>::mma(qa, kb, cin);
-                        const f32x4 dp = Frag<D>::mma(da, vb, f32x4{0.f, 0.f, 0.f, 0.f});
-                        f32x4 pr, ds;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            pr[i] = __builtin_amdgcn_exp2f(fmaf(s[i], alpha, -l2[i]));
-                            ds[i] = pr[i] * (dp[i] - dd[i]);
-                        }
-                        const s16x4_t pb4 = bf16x4_of(pr[0], pr[1], pr[2], pr[3]);
-                        const s16x4_t db4 = bf16x4_of(ds[0], ds[1], ds[2], ds[3]);
-#pragma unroll
-                        for (int mt = 0; mt < MT; ++mt) {
-                            dVt[pp][mt] = mma16(dt[mt], pb4, dVt[pp][mt]);
-                            dKt[pp][mt] = mma16(qt[mt], db4, dKt[pp][mt]);
-                        }
-                    }
-                }
+            for (int pp = 0; pp < NPP; ++pp) {
+                const int pi = pass * NPP + pp;
+                if (pi >= NPATCH) continue;
+                const int y0 = kyb + 4 * (pi / PB), x0 = kxb + 4 * (pi % PB);
+                const int y1 = min(y0 + 4, kyb + nky), x1 = min(x0 + 4, kxb + nkx);
+                if (max(y0, wy0) < min(y1, wy0 + r) && max(x0, wx0) < min(x1, wx0 + r)) pin |= 1u << pp;
+                if (y1 == y0 + 4 && x1 == x0 + 4 && y0 >= wy0 && y1 <= wy0 + r && x0 >= wx0 && x1 <= wx0 + r)
+                    full |= 1u << pp;
             }
+            const int ybeg = nby * g.block, xbeg = nbx * g.block;
+            const int nqy = (min(ybeg + g.block, g.H) - ybeg + g.stride - 1) / g.stride;
+            const int nqx = (min(xbeg + g.block, g.W) - xbeg + g.stride - 1) / g.stride;
+            const int nq = pin ? nqy * nqx : 0;
+            nbinfo[b] = i32x4{nqx, nq, (int)(pin | (full << 16)), (nq + 15) / 16};
+        }
+        __syncthreads();
+
+        // this wave's items: tiles wave, wave + 4, ... of the query blocks in order
+        auto settle = [&](int& b, int& u) {
+            while (b < nnb) {
+                const int t = bt_ld<int>(smem, (unsigned)p.k_off_nb + 16u * (unsigned)b + 12u);
+                if (u < t) break;
+                u -= t;
+                ++b;
+            }
+        };
+        // the global operands of item (b, u): Q and dout A fragments of
+        // query 16u + n, its lse2 and D
+        struct ItemIn {
+            FragT qa, da;
+            float l2, dd;
+        };
+        auto fetch = [&](int b, int u) {
+            ItemIn it;
+            const i32x4 info = nbinfo[b];
+            const int nqx = info[0], nq = info[1];
+            const int nby = ny0 + b / nnx, nbx = nx0 + b % nnx;
+            const int qi = min(16 * u + n, nq - 1);
+            const int iy = bt_div(qi, __builtin_amdgcn_rcpf((float)nqx)), ix = qi - iy * nqx;
+            const int y = nby * g.block + iy * g.stride, x = nbx * g.block + ix * g.stride;
+            const int64_t op = bh * oplane + (int64_t)(nby * bs + iy) * g.Wo + nbx * bs + ix;
+            it.qa = *reinterpret_cast<const FragT*>(qs + ((int64_t)y * g.W + x) * D + gq * KPL);
+            it.da = *reinterpret_cast<const FragT*>(dout + op * D + gq * KPL);
+            it.l2 = 16 * u + n < nq ? lse[op] * log2e : INFINITY;
+            it.dd = dsum[op];
+            return it;
+        };
+        int cb = 0, cu = wave;
+        settle(cb, cu);
+        ItemIn cur{};
+        if (cb < nnb) cur = fetch(cb, cu);
+        while (cb < nnb) {
+            int nb2 = cb, nu = cu + kBtWaves;
+            settle(nb2, nu);
+            ItemIn nxt{};
+            if (nb2 < nnb) nxt = fetch(nb2, nu);
+
+            const i32x4 info = nbinfo[cb];
+            const int nqx = info[0], nq = info[1];
+            const unsigned pin = (unsigned)info[2] & 0xffffu, full = (unsigned)info[2] >> 16;
+            const int nby = ny0 + cb / nnx, nbx = nx0 + cb % nnx;
+            const int wy0 = nby * g.block - g.halo, wx0 = nbx * g.block - g.halo;
+            const int ybeg = nby * g.block, xbeg = nbx * g.block;
+            const float rnqx = __builtin_amdgcn_rcpf((float)nqx);
+            const int u = cu;
+            const FragT qa = cur.qa, da = cur.da;
+            // this lane's four queries 16u + 4g + i: lse2 and D (from the
+            // lanes that loaded them), and the scratch addresses of their
+            // table products at this lane's key of patch (0, 0)
+            unsigned hb[4], wb[4];
+            float l2[4], dd[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int src = 4 * gq + i;               // lane holding query 16u + 4g + i
+                l2[i] = __shfl(cur.l2, src);
+                dd[i] = __shfl(cur.dd, src);
+                const int qv = min(16 * u + src, nq - 1);
+                const int jy = bt_div(qv, rnqx), jx = qv - jy * nqx;
+                const int yq = ybeg + jy * g.stride, xq = xbeg + jx * g.stride;
+                hb[i] = scrh + 4u * (unsigned)(src * jp + g.c0 - yq + kyb + (n >> 2));
+                wb[i] = scrw + 4u * (unsigned)(src * jp + g.c0 - xq + kxb + (n & 3));
+            }
+            // Q^T and dout^T fragments (lane (channel n, kg) = queries 4kg..4kg+3)
+            s16x4_t qt[MT], dt[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const f32x4 a = Frag<D>::mma(qa, sel[mt], f32x4{0.f, 0.f, 0.f, 0.f});
+                const f32x4 b = Frag<D>::mma(da, sel[mt], f32x4{0.f, 0.f, 0.f, 0.f});
+                qt[mt] = bf16x4_of(a[0], a[1], a[2], a[3]);
+                dt[mt] = bf16x4_of(b[0], b[1], b[2], b[3]);
+            }
+            // q.rel_h[j] and q.rel_w[j] of the tile's queries: scratch[query][j]
+            for (int jt = 0; jt < JT; ++jt) {
+                const FragT ah = bt_ld<FragT>(smem, offth + (unsigned)((16 * jt + n) * D + gq * KPL) * 2);
+                const FragT aw = bt_ld<FragT>(smem, offtw + (unsigned)((16 * jt + n) * D + gq * KPL) * 2);
+                bt_st<f32x4>(smem, scrh + (unsigned)(n * jp + 16 * jt + 4 * gq) * 4,
+                             Frag<D>::mma(ah, qa, f32x4{0.f, 0.f, 0.f, 0.f}));
+                bt_st<f32x4>(smem, scrw + (unsigned)(n * jp + 16 * jt + 4 * gq) * 4,
+                             Frag<D>::mma(aw, qa, f32x4{0.f, 0.f, 0.f, 0.f}));
+            }
+            // one patch: masked (some of its keys outside the window
+            // or the image) or not
+            auto patch = [&](auto masked, int pp) {
+                constexpr bool M = decltype(masked)::value;
+                const int pi = pass * NPP + pp;
+                const int py = pi / PB, px = pi % PB;
+                const unsigned pa = offkv + (unsigned)pi * 2 * PATB + (unsigned)(n * D + gq * KPL) * 2;
+                const FragT kb = bt_ld<FragT>(smem, pa);
+                const FragT vb = bt_ld<FragT>(smem, pa + PATB);
+                bool inw = true;
+                if (M) {
+                    const int ly = 4 * py + (n >> 2), lx = 4 * px + (n & 3);
+                    const int ky = kyb + ly, kx = kxb + lx;
+                    inw = ly < nky && lx < nkx && ky >= wy0 && ky < wy0 + r && kx >= wx0 && kx < wx0 + r;
+                }
+                f32x4 cin;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const unsigned ah = M ? (inw ? hb[i] + 16u * py : scrh) : hb[i] + 16u * py;
+                    const unsigned aw = M ? (inw ? wb[i] + 16u * px : scrw) : wb[i] + 16u * px;
+                    const float rel = bt_ld<float>(smem, ah) + bt_ld<float>(smem, aw);
+                    cin[i] = (!M || inw) ? rel : kMaskLogit;
+                }
+                const f32x4 s = Frag<D>::mma(qa, kb, cin);
+                const f32x4 dp = Frag<D>::mma(da, vb, f32x4{0.f, 0.f, 0.f, 0.f});
+                f32x4 pr, ds;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pr[i] = __builtin_amdgcn_exp2f(fmaf(s[i], alpha, -l2[i]));
+                    ds[i] = pr[i] * (dp[i] - dd[i]);
+                }
+                const s16x4_t pb4 = bf16x4_of(pr[0], pr[1], pr[2], pr[3]);
+                const s16x4_t db4 = bf16x4_of(ds[0], ds[1], ds[2], ds[3]);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    dVt[pp][mt] = mma16(dt[mt], pb4, dVt[pp][mt]);
+                    dKt[pp][mt] = mma16(qt[mt], db4, dKt[pp][mt]);
+                }
+            };
+#pragma unroll
+            for (int pp = 0; pp < NPP; ++pp) {
+                if (!(pin & (1u << pp))) continue;
+                if (full & (1u << pp)) patch(std::false_type{}, pp);
+                else patch(std::true_type{}, pp);
+            }
+            cb = nb2;
+            cu = nu;
+            cur = nxt;
+        }
 
         // ---- sums over the waves in wave order (waves 0-2 through LDS, the
-        // last wave adds its own and writes dk, dv); the LDS of the staged
-        // patches is free once every wave is past the first barrier
+        // last wave adds its own and writes dk, dv); the LDS holds the
+        // waves' scratch, free once every wave is past the first barrier
         float* red = reinterpret_cast<float*>(smem + p.k_off_red);
         for (int w = 0; w < kBtWaves; ++w) {
             __syncthreads();
@@ -621,9 +718,8 @@ void bwd_key_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                     }
                     // dk, dv: lane (key n, g) holds channels 16mt + 4g..4g+3
                     const int pi = pass * NPP + pp;
-                    if (pi >= npatch) continue;
-                    const int py = pi / pb, px = pi - py * pb;
-                    const int ly = 4 * py + (n >> 2), lx = 4 * px + (n & 3);
+                    if (pi >= NPATCH) continue;
+                    const int ly = 4 * (pi / PB) + (n >> 2), lx = 4 * (pi % PB) + (n & 3);
                     if (ly >= nky || lx >= nkx) continue;
                     const int64_t off = bh * plane + ((int64_t)(kyb + ly) * g.W + kxb + lx) * D + 16 * mt + 4 * gq;
                     *reinterpret_cast<u32x2*>(dk + off) =
@@ -644,8 +740,6 @@ __global__ void bt_zero_u16(unsigned short* __restrict__ p, int64_t n)
 
 // ---------------------------------------------------------------- planning
 static int bt_np(int r) { return r <= 16 ? 4 : r <= 20 ? 5 : r <= 24 ? 6 : 8; }
-// key patches a wave carries per pass (its dk^T, dv^T sums in registers)
-static int bt_npp(int d) { return d == 16 ? 16 : 9; }
 
 static BwdTilePlan bt_plan(const Geometry& g)
 {
@@ -669,13 +763,16 @@ static BwdTilePlan bt_plan(const Geometry& g)
     // key kernel: the block's patches (K and V), the tables, the waves'
     // scratch; the wave-order sums of dk^T and dv^T reuse the scratch
     const int pb = (g.block + 3) / 4;
-    const int npp = bt_npp(g.d);
+    const int npp = g.d == 32 && pb * pb > 9 ? (pb * pb + 1) / 2 : pb * pb;
     p.k_off_tab = pb * pb * 2 * 16 * g.d * 2;
     p.k_off_scr = p.k_off_tab + 2 * p.jr * g.d * 2;
     p.k_off_red = p.k_off_scr;
     const int scr = kBtWaves * 2 * 16 * p.jp * 4;
     const int redb = npp * (g.d / 16) * 2 * 64 * 16;
-    p.k_lds = p.k_off_scr + std::max(scr, redb);
+    p.k_off_nb = p.k_off_scr + std::max(scr, redb);
+    const int A = (g.halo + g.block - 1) / g.block;
+    const int nnb = std::min(2 * A + 1, g.nbh) * std::min(2 * A + 1, g.nbw);
+    p.k_lds = p.k_off_nb + nnb * 16;
     p.k_nwg = p.q_nwg;
     p.alpha = (float)((double)g.scale * 1.4426950408889634);
     return p;
@@ -709,12 +806,12 @@ static hipError_t bt_query_launch(const void* q, const void* k, const void* v, c
     return hipGetLastError();
 }
 
-template <int D, int NPP>
+template <int D, int PB>
 static hipError_t bt_key_launch(const void* q, const void* k, const void* v, const void* rh, const void* rw,
                                 const void* dout, const float* lse, const float* dsum, void* dk, void* dv,
                                 const Geometry& g, const BwdTilePlan& p, hipStream_t st)
 {
-    auto kern = bwd_key_kernel<D, NPP>;
+    auto kern = bwd_key_kernel<D, PB>;
     const hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), p.k_lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)p.k_nwg), dim3(64 * kBtWaves), p.k_lds, st,
@@ -736,6 +833,19 @@ static hipError_t bt_query_np(const void* q, const void* k, const void* v, const
     }
 }
 
+template <int D>
+static hipError_t bt_key_pb(const void* q, const void* k, const void* v, const void* rh, const void* rw,
+                            const void* dout, const float* lse, const float* dsum, void* dk, void* dv,
+                            const Geometry& g, const BwdTilePlan& p, hipStream_t st)
+{
+    switch ((g.block + 3) / 4) {
+    case 1: return bt_key_launch<D, 1>(q, k, v, rh, rw, dout, lse, dsum, dk, dv, g, p, st);
+    case 2: return bt_key_launch<D, 2>(q, k, v, rh, rw, dout, lse, dsum, dk, dv, g, p, st);
+    case 3: return bt_key_launch<D, 3>(q, k, v, rh, rw, dout, lse, dsum, dk, dv, g, p, st);
+    default: return bt_key_launch<D, 4>(q, k, v, rh, rw, dout, lse, dsum, dk, dv, g, p, st);
+    }
+}
+
 // dq (zeroed first where queries are strided: only query pixels receive a
 // gradient), D per query into dsum, table partials, then dk and dv.
 hipError_t launch_bwd_tile(const void* q, const void* k, const void* v, const void* rh, const void* rw,
@@ -751,8 +861,8 @@ hipError_t launch_bwd_tile(const void* q, const void* k, const void* v, const vo
     hipError_t e = g.d == 16 ? bt_query_np<16>(q, k, v, rh, rw, out, dout, lse, dq, dsum, part_rel, g, p, st)
                              : bt_query_np<32>(q, k, v, rh, rw, out, dout, lse, dq, dsum, part_rel, g, p, st);
     if (e != hipSuccess) return e;
-    return g.d == 16 ? bt_key_launch<16, 16>(q, k, v, rh, rw, dout, lse, dsum, dk, dv, g, p, st)
-                     : bt_key_launch<32, 9>(q, k, v, rh, rw, dout, lse, dsum, dk, dv, g, p, st);
+    return g.d == 16 ? bt_key_pb<16>(q, k, v, rh, rw, dout, lse, dsum, dk, dv, g, p, st)
+                     : bt_key_pb<32>(q, k, v, rh, rw, dout, lse, dsum, dk, dv, g, p, st);
 }
 
 }  // namespace halo
