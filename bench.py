@@ -104,10 +104,13 @@ KERNEL_SOURCES = {
     "fwd:wide": ["halo_common.h", "mfma_util.h", "kernel_wide.hip"],
     "fwd:strip": ["halo_common.h", "mfma_util.h", "kernel_mfma.hip"],
     "fwd:generic": ["halo_common.h", "kernel_generic.hip"],
-    "layer": ["halo_common.h", "mfma_util.h", "kernel_tile.hip", "kernel_ring.hip", "kernel_mfma.hip",
-              "kernel_wide.hip", "proj.h",
-              "kernel_proj.hip"],
-    "bwd": ["halo_common.h", "mfma_util.h", "kernel_bwd_mfma.hip", "kernel_bwd_generic.hip"],
+    # layer: the projections plus the attention kernel the call launches
+    "layer:tile": ["halo_common.h", "mfma_util.h", "kernel_tile.hip", "proj.h", "kernel_proj.hip"],
+    "layer:ring": ["halo_common.h", "mfma_util.h", "kernel_ring.hip", "proj.h", "kernel_proj.hip"],
+    # backward: the matrix-core kernels of the path plus the table reduction
+    "bwd:strip": ["halo_common.h", "mfma_util.h", "kernel_bwd_mfma.hip", "kernel_bwd_generic.hip"],
+    "bwd:tile": ["halo_common.h", "mfma_util.h", "kernel_bwd_tile.hip", "kernel_bwd_generic.hip"],
+    "bwd:generic": ["halo_common.h", "kernel_generic.hip", "kernel_bwd_generic.hip"],
 }
 
 
@@ -335,14 +338,17 @@ def run_layer(args):
     achieved_gbs = alg_bytes / (ms * 1e-3) / 1e9
     mfma_peak = MFMA_PEAK_TFLOPS[wl.dtype]
     mfma_bound = flops / (mfma_peak * 1e12) > alg_bytes / (HBM_PEAK_GBS * 1e9)
-    src_hash = kernel_source_hash("layer")
+    used = _native.fwd_kernel_name(wl.B, wl.heads, wl.H, wl.W, wl.d, wl.block, wl.halo, wl.stride,
+                                   _native.HALO_BF16 if wl.dtype == "bf16" else _native.HALO_F32)
+    src_hash = kernel_source_hash(f"layer:{used}") if f"layer:{used}" in KERNEL_SOURCES else None
     rec = MEASURED_TRAFFIC["layer"].get(f"{wl.name}/{lay}")
-    traffic = rec["bytes_per_launch"] if rec and rec["sources"] == src_hash else None
+    valid = rec is not None and src_hash is not None and rec["sources"] == src_hash and rec.get("kernel") == used
+    traffic = rec["bytes_per_launch"] if valid else None
     line = {
         "metric": METRIC_LAYER, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
-        "config": {**wl.describe(), "pass": "layer", "layout": lay, "C": C, "C_out": Co,
+        "config": {**wl.describe(), "pass": "layer", "kernel_used": used, "layout": lay, "C": C, "C_out": Co,
                    "rotated_input_sets": nsets},
         "tokens_per_s": round(wl.tokens / (ms * 1e-3), 1),
         "wall_s_timed_region": round(wall, 4),
@@ -501,8 +507,9 @@ def run_op(args, wl, steps, warmup, cpu_seconds):
     mfma_bound = flops / (mfma_peak * 1e12) > alg_bytes / (HBM_PEAK_GBS * 1e9)
 
     if bwd:
-        used = None
-        src_hash = kernel_source_hash("bwd")
+        used = _native.bwd_kernel_name(wl.B, wl.heads, wl.H, wl.W, wl.d, wl.block, wl.halo, wl.stride, dcode,
+                                       flags, KERNELS[args.kernel])
+        src_hash = kernel_source_hash(f"bwd:{used}")
     else:
         used = _native.fwd_kernel_name(wl.B, wl.heads, wl.H, wl.W, wl.d, wl.block, wl.halo, wl.stride, dcode,
                                        flags, KERNELS[args.kernel])

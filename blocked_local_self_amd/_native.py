@@ -71,6 +71,8 @@ def load() -> ctypes.CDLL:
     lib.halo_attn_layer_fwd.restype = i
     lib.halo_attn_fwd_kernel_name.argtypes = [i] * 11
     lib.halo_attn_fwd_kernel_name.restype = ctypes.c_char_p
+    lib.halo_attn_bwd_kernel_name.argtypes = [i] * 11
+    lib.halo_attn_bwd_kernel_name.restype = ctypes.c_char_p
     lib.halo_attn_select_kernel.argtypes = [i] * 5
     lib.halo_attn_select_kernel.restype = i
     lib.halo_attn_last_error.argtypes = []
@@ -99,6 +101,14 @@ def fwd_kernel_name(B, heads, H, W, d, block, halo, stride, dtype, flags=0, kern
     name = load().halo_attn_fwd_kernel_name(B, heads, H, W, d, block, halo, stride, dtype, flags, kernel)
     if name is None:
         raise ValueError(f"halo_attn_fwd_kernel_name: {last_error()}")
+    return name.decode()
+
+
+def bwd_kernel_name(B, heads, H, W, d, block, halo, stride, dtype, flags=0, kernel=HALO_KERNEL_AUTO) -> str:
+    """The backward kernels halo_attn_bwd_ex runs for these arguments (host only)."""
+    name = load().halo_attn_bwd_kernel_name(B, heads, H, W, d, block, halo, stride, dtype, flags, kernel)
+    if name is None:
+        raise ValueError(f"halo_attn_bwd_kernel_name: {last_error()}")
     return name.decode()
 
 

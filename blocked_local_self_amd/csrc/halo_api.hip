@@ -310,6 +310,35 @@ const char* halo_attn_fwd_kernel_name(int B, int heads, int H, int W, int d, int
     return "strip";
 }
 
+const char* halo_attn_bwd_kernel_name(int B, int heads, int H, int W, int d, int block, int halo,
+                                      int query_stride, int dtype, int flags, int kernel)
+{
+    g_err[0] = 0;
+    if (flags & ~(HALO_CENTRED_OFFSET | HALO_ZERO_PAD | HALO_CENTRED_MASK | HALO_HALF_SPLIT)) {
+        fail(HALO_ERR_SHAPE, "flags=%d has bits outside the halo_flags values", flags);
+        return nullptr;
+    }
+    if (kernel != HALO_KERNEL_AUTO && kernel != HALO_KERNEL_GENERIC && kernel != HALO_KERNEL_MFMA &&
+        kernel != HALO_KERNEL_MFMA_STRIP && kernel != HALO_KERNEL_MFMA_RING) {
+        fail(HALO_ERR_SHAPE, "kernel=%d is not a halo_kernel value", kernel);
+        return nullptr;
+    }
+    halo::Geometry g;
+    bool empty = false;
+    if (check_sizes(B, heads, H, W, d, block, halo, query_stride, 1.0f, dtype, g, empty)) return nullptr;
+    g.flags = flags;
+    if (flags & HALO_CENTRED_OFFSET) g.c0 = g.r - 1;
+    if (empty) return "none";
+    const int path = bwd_mfma_path(g, dtype == HALO_BF16);
+    if (kernel != HALO_KERNEL_AUTO && kernel != HALO_KERNEL_GENERIC && path == 0) {
+        fail(HALO_ERR_UNSUPPORTED, "no matrix-core backward for this shape (d=%d r=%d block=%d flags=%d)",
+             d, g.r, block, flags);
+        return nullptr;
+    }
+    if (kernel == HALO_KERNEL_GENERIC || path == 0) return "generic";
+    return path == 1 ? "strip" : "tile";
+}
+
 int halo_attn_fwd_ex(const void* q, const void* k, const void* v,
                      const void* rel_h, const void* rel_w, void* out, float* lse,
                      int B, int heads, int H, int W, int d,

@@ -100,6 +100,16 @@ __device__ inline void split4(f32x4 x, s16x4_t& hi, s16x4_t& lo)
 // 1/(2d) from an integer, far above the rounding error
 __device__ inline int bt_div(int a, float rd) { return (int)(((float)a + 0.5f) * rd); }
 
+// Workgroup i runs on XCD i mod 8 (the dispatcher deals them round-robin);
+// this bijection gives each XCD one contiguous range of logical blocks, so
+// neighbouring blocks, which read the same halo rows and queries, share an
+// L2.
+__device__ inline int64_t bt_logical(int64_t i, int64_t nwg)
+{
+    const int64_t q8 = nwg >> 3, r8 = nwg & 7, x = i & 7, j = i >> 3;
+    return x * q8 + min(x, r8) + j;
+}
+
 // Byte offset of channel chunk `c` (16 bytes) of the staged window pixel in
 // row t: chunks rotate with the row so the four rows of a patch spread over
 // the banks.
@@ -136,8 +146,9 @@ void bwd_query_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
     const float log2e = 1.4426950408889634f;
 
     const int64_t nblk = (int64_t)g.nbh * g.nbw;
-    const int64_t bh = blockIdx.x / nblk;
-    const int rem = (int)(blockIdx.x - bh * nblk);
+    const int64_t wg = bt_logical(blockIdx.x, p.q_nwg);
+    const int64_t bh = wg / nblk;
+    const int rem = (int)(wg - bh * nblk);
     const int by = rem / g.nbw, bx = rem - by * g.nbw;
     const int ybeg = by * g.block, xbeg = bx * g.block;
     const int wy0 = ybeg - g.halo, wx0 = xbeg - g.halo;
@@ -240,26 +251,6 @@ void bwd_query_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
         if (valid && gq == 0) dsum[opix] = Dq;
         bt_st<FragT>(smem, qtl + (unsigned)(n * D + gq * KPL) * 2, qf);
 
-        // ---- width terms: scratch[query][j] = q.rel_w[j], read back per
-        // window column as the score MFMA's accumulator (mask value off the
-        // image or past the window)
-#pragma unroll
-        for (int jt = 0; jt < JT; ++jt) {
-            const FragT a = bt_ld<FragT>(smem, offtw + (unsigned)((16 * jt + n) * D + gq * KPL) * 2);
-            bt_st<f32x4>(smem, scr + (unsigned)(n * jp + 16 * jt + 4 * gq) * 4,
-                         Frag<D>::mma(a, qf, f32x4{0.f, 0.f, 0.f, 0.f}));
-        }
-        f32x4 cinit[NP];
-#pragma unroll
-        for (int ct = 0; ct < NP; ++ct)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int c = 4 * ct + i, kx = wx0 + c;
-                const bool ok = c < r && kx >= 0 && kx < g.W;
-                const int j = ok ? c - xl + g.c0 : 0;
-                const float w = bt_ld<float>(smem, scr + (unsigned)(n * jp + j) * 4);
-                cinit[ct][i] = ok ? w : kMaskLogit;
-            }
         // ---- height terms: alpha q.rel_h[row] - lse2 (-inf off the image,
         // past the window, or for lanes without a query)
 #pragma unroll
@@ -277,31 +268,52 @@ void bwd_query_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
             const float h = bt_ld<float>(smem, scr + (unsigned)(n * jp + j) * 4);
             hq[rq] = ok ? fmaf(h, alpha, -lse2) : -INFINITY;
         }
+        // ---- width terms: scratch[query][j] = q.rel_w[j], read in the loop
+        // per window column c at entry c - xl + c0 (wbase + 4c) as the score
+        // MFMA's accumulator; columns past the window or off the image get
+        // the mask value in their entries (no other column reads them)
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) {
+            const FragT a = bt_ld<FragT>(smem, offtw + (unsigned)((16 * jt + n) * D + gq * KPL) * 2);
+            bt_st<f32x4>(smem, scr + (unsigned)(n * jp + 16 * jt + 4 * gq) * 4,
+                         Frag<D>::mma(a, qf, f32x4{0.f, 0.f, 0.f, 0.f}));
+        }
+        const unsigned wbase = scr + 4u * (unsigned)(n * jp + g.c0 - xl);
+#pragma unroll
+        for (int ct = 0; ct < NP; ++ct) {
+            const int c = 4 * ct + gq, kx = wx0 + c;
+            if (!(c < r && kx >= 0 && kx < g.W)) bt_st<float>(smem, wbase + 4u * c, kMaskLogit);
+        }
 
         // ---- the window, patch by patch
         f32x4 dQt[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) dQt[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         float rowsum[NP];
-        f32x4 colsum[NP];
 #pragma unroll
-        for (int ct = 0; ct < NP; ++ct) colsum[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int rq = 0; rq < NP; ++rq) rowsum[rq] = 0.f;
         // A-operand lane (m, kg): key m of the patch = (row m >> 2, column
         // m & 3), channels kg*KPL..; K^T gather lane (channel n, kg): patch
-        // row kg, columns 0..3
+        // row kg, columns 0..3.  Column tile by column tile: once a tile's
+        // columns are done, their sums over the window (and over the four
+        // lanes of a query) replace their width terms in the scratch, at the
+        // same entries; every other entry is zeroed after the loop, so the
+        // scratch then holds the width table's sums by table row.
         const unsigned kA = (unsigned)(n >> 2) * rowb + (unsigned)(n & 3) * PIXB;
 #pragma unroll
-        for (int rq = 0; rq < NP; ++rq) {
-            rowsum[rq] = 0.f;
-            const int ta = 4 * rq + (n >> 2);          // row of this lane's A-operand key
-            const int tg = 4 * rq + gq;                // row of this lane's K^T gather
-            const unsigned chA = D == 32 ? bt_chunk<D>(gq, ta) : bt_chunk<D>(gq >> 1, ta) + (gq & 1) * 8;
+        for (int ct = 0; ct < NP; ++ct) {
+            f32x4 colsum{0.f, 0.f, 0.f, 0.f};
+            const f32x4 cin{bt_ld<float>(smem, wbase + 16u * ct), bt_ld<float>(smem, wbase + 16u * ct + 4),
+                            bt_ld<float>(smem, wbase + 16u * ct + 8), bt_ld<float>(smem, wbase + 16u * ct + 12)};
 #pragma unroll
-            for (int ct = 0; ct < NP; ++ct) {
+            for (int rq = 0; rq < NP; ++rq) {
+                const int ta = 4 * rq + (n >> 2);      // row of this lane's A-operand key
+                const int tg = 4 * rq + gq;            // row of this lane's K^T gather
+                const unsigned chA = D == 32 ? bt_chunk<D>(gq, ta) : bt_chunk<D>(gq >> 1, ta) + (gq & 1) * 8;
                 const unsigned a = (unsigned)(4 * rq) * rowb + kA + (unsigned)(4 * ct) * PIXB + chA;
                 const FragT kf = bt_ld<FragT>(smem, a);
                 const FragT vf = bt_ld<FragT>(smem, offv + a);
-                const f32x4 s = Frag<D>::mma(kf, qf, cinit[ct]);
+                const f32x4 s = Frag<D>::mma(kf, qf, cin);
                 const f32x4 dp = Frag<D>::mma(vf, df, f32x4{0.f, 0.f, 0.f, 0.f});
                 f32x4 ds;
 #pragma unroll
@@ -310,7 +322,7 @@ void bwd_query_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
                     ds[i] = pr * (dp[i] - Dq);
                 }
                 rowsum[rq] += (ds[0] + ds[1]) + (ds[2] + ds[3]);
-                colsum[ct] += ds;
+                colsum += ds;
                 const s16x4_t dsb = bf16x4_of(ds[0], ds[1], ds[2], ds[3]);
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
@@ -324,21 +336,32 @@ void bwd_query_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
                     dQt[mt] = mma16(kt, dsb, dQt[mt]);
                 }
             }
+            // this tile's column sums (lane g writes column 4ct + g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) colsum[i] = sum_over_rows(colsum[i]);
+            const float val = gq == 0 ? colsum[0] : gq == 1 ? colsum[1] : gq == 2 ? colsum[2] : colsum[3];
+            bt_st<float>(smem, wbase + 4u * (4 * ct + gq), val);
+            __builtin_amdgcn_sched_barrier(0);   // schedule one column tile at a time (registers)
         }
 
-        // ---- column sums over the four lanes of a query, then the width
-        // table's share: scratch[query][table row of column c] = column sum
-#pragma unroll
-        for (int ct = 0; ct < NP; ++ct)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) colsum[ct][i] = sum_over_rows(colsum[ct][i]);
-        for (int jj = gq; jj < jr / 4; jj += 4)
-            bt_st<f32x4>(smem, scr + (unsigned)(n * jp + 4 * jj) * 4, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int ct = 0; ct < NP; ++ct) {
-            const int c = 4 * ct + gq, kx = wx0 + c;
-            const float val = gq == 0 ? colsum[ct][0] : gq == 1 ? colsum[ct][1] : gq == 2 ? colsum[ct][2] : colsum[ct][3];
-            if (valid && c < r && kx >= 0 && kx < g.W) bt_st<float>(smem, scr + (unsigned)(n * jp + c - xl + g.c0) * 4, val);
+        // ---- the lane's query again, from an opaque copy of the tile index:
+        // recomputed here rather than kept in registers through the loop
+        int uo = u;
+        asm volatile("" : "+s"(uo));
+        const int qi2 = 16 * uo + n;
+        const bool valid2 = qi2 < nq;
+        const int qc2 = valid2 ? qi2 : 0;
+        const int iy2 = bt_div(qc2, rnqx), ix2 = qc2 - iy2 * nqx;
+        const int y2 = ybeg + iy2 * g.stride, x2 = xbeg + ix2 * g.stride;
+        const int yl2 = y2 - wy0, xl2 = x2 - wx0;
+
+        // ---- zero the entries outside the in-image window columns (and all
+        // of a lane without a query): the scratch is the width table's sums
+        {
+            const int clo = max(0, -wx0), chi = min(r, g.W - wx0);
+            const int jlo = valid2 ? clo - xl2 + g.c0 : jr, jhi = valid2 ? chi - xl2 + g.c0 : jr;
+            for (int j = gq; j < jr; j += 4)
+                if (j < jlo || j >= jhi) bt_st<float>(smem, scr + (unsigned)(n * jp + j) * 4, 0.f);
         }
         auto table_terms = [&](unsigned offt, f32x4 (&dR)[MT][JT]) {
             // Q^T of the tile: lane (channel 16 mt + n, kg) holds queries 4kg..4kg+3
@@ -378,13 +401,13 @@ void bwd_query_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
 #pragma unroll
         for (int rq = 0; rq < NP; ++rq) {
             const int t = 4 * rq + gq, ky = wy0 + t;
-            if (valid && t < r && ky >= 0 && ky < g.H)
-                bt_st<float>(smem, scr + (unsigned)(n * jp + t - yl + g.c0) * 4, rowsum[rq]);
+            if (valid2 && t < r && ky >= 0 && ky < g.H)
+                bt_st<float>(smem, scr + (unsigned)(n * jp + t - yl2 + g.c0) * 4, rowsum[rq]);
         }
         table_terms(offth, dRh);
 
-        if (valid) {
-            __bf16* dp = dq + bh * plane + ((int64_t)y * g.W + x) * D + 4 * gq;
+        if (valid2) {
+            __bf16* dp = dq + bh * plane + ((int64_t)y2 * g.W + x2) * D + 4 * gq;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
                 *reinterpret_cast<u32x2*>(dp + 16 * mt) =
@@ -409,7 +432,7 @@ void bwd_query_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
                 *reinterpret_cast<f32x4*>(red + ((wave * 2 + tab) * jr + j) * D + 16 * mt + 4 * gq) = x;
             }
     __syncthreads();
-    float* part = part_rel + (int64_t)blockIdx.x * 2 * E;
+    float* part = part_rel + wg * 2 * E;
     for (int e = tid; e < 2 * E; e += 64 * kBtWaves) {
         const int tab = e / E, rr = e - tab * E;
         float s = 0.f;
@@ -454,8 +477,9 @@ void bwd_key_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const float log2e = 1.4426950408889634f;
 
     const int64_t nblk = (int64_t)g.nbh * g.nbw;
-    const int64_t bh = blockIdx.x / nblk;
-    const int rem = (int)(blockIdx.x - bh * nblk);
+    const int64_t wg = bt_logical(blockIdx.x, p.k_nwg);
+    const int64_t bh = wg / nblk;
+    const int rem = (int)(wg - bh * nblk);
     const int kby = rem / g.nbw, kbx = rem - kby * g.nbw;
     const int kyb = kby * g.block, kxb = kbx * g.block;
     const int nky = min(g.block, g.H - kyb), nkx = min(g.block, g.W - kxb);

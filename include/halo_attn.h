@@ -362,6 +362,19 @@ const char* halo_attn_fwd_kernel_name(int B, int heads, int H, int W, int d,
                                       int block, int halo, int query_stride,
                                       int dtype, int flags, int kernel);
 
+/*
+ * Which backward kernels halo_attn_bwd_ex would run for these arguments
+ * with 16-byte-aligned tensors (unaligned ones take the generic kernels):
+ * "generic", "strip" (matrix cores, windows of at most 16 columns over
+ * whole blocks), "tile" (matrix cores, the 16-query tile kernels), or
+ * "none" when a size is zero.  Host only: touches no device.  The string
+ * is static.  Invalid arguments: NULL, with halo_attn_last_error() telling
+ * why.
+ */
+const char* halo_attn_bwd_kernel_name(int B, int heads, int H, int W, int d,
+                                      int block, int halo, int query_stride,
+                                      int dtype, int flags, int kernel);
+
 /* Message for the last non-zero status returned on this thread ("" if none).
  * The pointer stays valid until the next call on this thread. */
 const char* halo_attn_last_error(void);

@@ -116,6 +116,24 @@ def test_kernel_name_query_on_the_host():
         _native.fwd_kernel_name(1, 2, 16, 16, 16, 4, 1, 1, _native.HALO_BF16, kernel=9)
 
 
+def test_backward_kernel_name_query():
+    bf, f32 = _native.HALO_BF16, _native.HALO_F32
+    name = _native.bwd_kernel_name
+    assert name(32, 8, 64, 64, 16, 8, 3, 1, bf) == "strip"          # 14x14 windows, whole blocks
+    assert name(8, 8, 128, 128, 32, 12, 3, 1, bf) == "tile"         # 18x18 windows, partial blocks
+    assert name(1, 2, 20, 28, 16, 8, 3, 1, bf) == "tile"            # partial blocks
+    assert name(8, 8, 64, 64, 16, 32, 3, 1, bf) == "generic"        # 38x38 windows
+    assert name(1, 2, 16, 16, 16, 4, 1, 1, f32) == "generic"
+    assert name(1, 2, 16, 16, 16, 4, 1, 1, bf, flags=_native.HALO_ZERO_PAD) == "strip"
+    assert name(1, 2, 20, 28, 16, 8, 3, 1, bf, flags=_native.HALO_ZERO_PAD) == "generic"
+    assert name(1, 2, 20, 28, 16, 8, 3, 1, bf, kernel=_native.HALO_KERNEL_GENERIC) == "generic"
+    assert name(0, 2, 20, 28, 16, 8, 3, 1, bf) == "none"
+    with pytest.raises(ValueError, match="matrix-core"):
+        name(8, 8, 64, 64, 16, 32, 3, 1, bf, kernel=_native.HALO_KERNEL_MFMA)
+    with pytest.raises(ValueError, match="query_stride"):
+        name(1, 2, 16, 16, 16, 4, 1, 3, bf)
+
+
 def test_python_wrapper_validates_before_the_library():
     import torch
     from blocked_local_self_amd import halo_attn_fwd
