@@ -76,20 +76,24 @@ MEASURED_TRAFFIC = {
             "kernel": "ring", "sources": "30cafffd6e32feaa"},
         "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 135619038, "read": 101016030, "write": 34603008,
             "kernel": "ring", "sources": "30cafffd6e32feaa"},
+        "detection_bf16_64x64_d16_b32h3": {"bytes_per_launch": 33729508, "read": 25340900, "write": 8388608,
+            "kernel": "wide", "sources": "f57912f258077c20"},
+        "global_bf16_16x16_d16_b16h0": {"bytes_per_launch": 17115897, "read": 12921593, "write": 4194304,
+            "kernel": "ring", "sources": "30cafffd6e32feaa"},
     },
     # layer: summed over the call's kernels (to_q/to_kv, attention, to_out)
     "layer": {
-        "early_stage_bf16_64x64_d16_b8h3/nhwc": {"bytes_per_launch": 337276140, "read": 169503980, "write": 167772160,
-            "sources": "db3f598f16960393"},
+        "early_stage_bf16_64x64_d16_b8h3/nhwc": {"bytes_per_launch": 337291011, "read": 169518851, "write": 167772160,
+            "kernel": "ring", "sources": "94d6e568448027f1"},
     },
-    # backward: summed over the call's kernels (strip kernel launches, table reduction)
+    # backward: summed over the call's kernels (matrix-core kernels, table reduction)
     "bwd": {
-        "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 590635834, "read": 373611194, "write": 217024640,
-            "sources": "0b600c6971720264"},
-        "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 504392789, "read": 313613141, "write": 190779648,
-            "sources": "0b600c6971720264"},
-        "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 456787748, "read": 260288730, "write": 196499017,
-            "sources": "0b600c6971720264"},
+        "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 590464100, "read": 373439460, "write": 217024640,
+            "kernel": "strip", "sources": "9c5d4cb0bea600b2"},
+        "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 504286531, "read": 313506883, "write": 190779648,
+            "kernel": "strip", "sources": "9c5d4cb0bea600b2"},
+        "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 456777508, "read": 260372279, "write": 196405229,
+            "kernel": "strip", "sources": "9c5d4cb0bea600b2"},
     },
 }
 
