@@ -70,21 +70,21 @@ MEASURED_TRAFFIC = {
     "fwd": {
         "large_bf16_128x128_d32_b12h3": {"bytes_per_launch": 273837727, "read": 206728863, "write": 67108864,
             "kernel": "tile", "sources": "009aae16d7d0099b"},
-        "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 92519208, "read": 84130600, "write": 8388608,
-            "kernel": "ring", "sources": "30cafffd6e32feaa"},
-        "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 134551698, "read": 100997215, "write": 33554483,
-            "kernel": "ring", "sources": "30cafffd6e32feaa"},
-        "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 135619038, "read": 101016030, "write": 34603008,
-            "kernel": "ring", "sources": "30cafffd6e32feaa"},
+        "strided_bf16_64x64_d16_b8h3_s2": {"bytes_per_launch": 92520360, "read": 84131752, "write": 8388608,
+            "kernel": "ring", "sources": "aa21a7f49d15e703"},
+        "early_stage_bf16_64x64_d16_b8h3": {"bytes_per_launch": 134551673, "read": 100997241, "write": 33554432,
+            "kernel": "ring", "sources": "aa21a7f49d15e703"},
+        "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 135622814, "read": 101019806, "write": 34603008,
+            "kernel": "ring", "sources": "aa21a7f49d15e703"},
         "detection_bf16_64x64_d16_b32h3": {"bytes_per_launch": 33729508, "read": 25340900, "write": 8388608,
             "kernel": "wide", "sources": "f57912f258077c20"},
-        "global_bf16_16x16_d16_b16h0": {"bytes_per_launch": 17115897, "read": 12921593, "write": 4194304,
-            "kernel": "ring", "sources": "30cafffd6e32feaa"},
+        "global_bf16_16x16_d16_b16h0": {"bytes_per_launch": 17115746, "read": 12921442, "write": 4194304,
+            "kernel": "ring", "sources": "aa21a7f49d15e703"},
     },
     # layer: summed over the call's kernels (to_q/to_kv, attention, to_out)
     "layer": {
-        "early_stage_bf16_64x64_d16_b8h3/nhwc": {"bytes_per_launch": 337291011, "read": 169518851, "write": 167772160,
-            "kernel": "ring", "sources": "94d6e568448027f1"},
+        "early_stage_bf16_64x64_d16_b8h3/nhwc": {"bytes_per_launch": 337280548, "read": 169508388, "write": 167772160,
+            "kernel": "ring", "sources": "8779ba557f649996"},
     },
     # backward: summed over the call's kernels (matrix-core kernels, table reduction)
     "bwd": {

@@ -63,6 +63,15 @@ constexpr int kLdsPerCU = 160 * 1024;   // gfx950
 // Query groups a wave may take per block row (the plan keeps within it).
 constexpr int ring_maxi(int nct) { return nct == 1 ? 2 : 4; }
 constexpr int kScrStride = 20;        // floats per scratch row (conflict-free writes)
+// LDS banks as a 32-bit access sees them: 32 banks of 4 bytes, 32 lanes per
+// pass (SQ_LDS_BANK_CONFLICT on gfx950: padding the 32-query scratch by 32
+// dwords changed nothing, by 16 removed its conflicts).  The 32-query
+// scratch rows hold 16 floats, and a tile's scratch starts 16 banks after
+// the previous tile's: lanes n and n + 16 of a pass (the two query tiles)
+// then fall in different halves of the banks, both for a row shared by the
+// pass and for each query's own height row (row R - 1 - yl, yl = n32 / 8).
+constexpr int kScr32Stride = 16;
+constexpr unsigned scr32_tile_bytes(int rows) { return (unsigned)(rows * kScr32Stride + 16) * 4; }
 
 // Relative-table rows (padded, multiple of 16) for windows of up to 16*nct
 // columns: 2R-1 <= 32*nct - 1 and R-1+16*nct-1 < 32*nct.
@@ -439,8 +448,10 @@ void ring_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             const u32x2 qa = __builtin_bit_cast(u32x2, qf[0]), qb = __builtin_bit_cast(u32x2, qf[1]);
             const s16x8 q32 = __builtin_bit_cast(s16x8, u32x4{qa[0], qa[1], qb[0], qb[1]});
             const f32x16 zero16 = {};
-            const unsigned scr32 = p.off_scr + wave * QT * scr_u + (unsigned)(n32 >> 4) * scr_u + 4u * (n32 & 15);
-            constexpr unsigned RS = 4u * kScrStride;      // bytes per scratch row
+            static_assert(2 * scr32_tile_bytes(kScrRows) <= QT * scr_u, "within the wave's scratch");
+            const unsigned scr32 = p.off_scr + wave * QT * scr_u + (unsigned)(n32 >> 4) * scr32_tile_bytes(kScrRows) +
+                                   4u * (n32 & 15);
+            constexpr unsigned RS = 4u * kScr32Stride;    // bytes per scratch row
 
             // ---- relative logits of the 32 table rows, then the width terms
             const f32x16 gw = mma32_k16(tab32w, q32, zero16);
@@ -1011,9 +1022,17 @@ static RingPlan ring_plan(const Geometry& g, int nct, int qt, int waves, int nbx
     p.midstage = mid ? 1 : 0;
     p.ring = mid ? g.r + g.block : g.r;
     // V^T channel pitch: at least ring*SWv elements, and (pitch/2) = 4 (mod 64)
-    // dwords so the 16 channels of a fragment read land in distinct banks
+    // dwords so the 16 channels of a fragment read land in distinct banks.
+    // The 32-query layout (16 channels, one column tile, two query tiles)
+    // reads 8 bytes of channel n32 in lanes 0-15 (and bf16 ones in 16-31):
+    // pitch/2 = 2 (mod 32) dwords puts those 16 lanes on 32 distinct banks,
+    // and the staging stores of chunks 0 and 1 (channels 8 apart) on
+    // different banks
     p.CP = p.ring * p.SWv;
-    while (p.CP % 2 || (p.CP / 2) % 64 != 4) ++p.CP;
+    if (g.d == 16 && nct == 1 && qt == 2)
+        while (p.CP % 2 || (p.CP / 2) % 32 != 2) ++p.CP;
+    else
+        while (p.CP % 2 || (p.CP / 2) % 64 != 4) ++p.CP;
     const int side = (g.block + g.stride - 1) / g.stride;
     p.groups = ((side * side + 15) / 16 + qt - 1) / qt;
     const int kb = p.ring * p.SWv * g.d * 2;
