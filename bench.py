@@ -38,8 +38,10 @@ a pixel-major channels-last layout (--layout nhwc or blocked), with C = C_out
 2*out_pixels*inner*C_out (to_out); algorithmic bytes = x read once and y
 written once (the intermediates q, k, v and the attention output are not
 counted: a layer that never leaves the chip needs none of them).  The
-roofline entry covers the whole call; ``parts_us`` times each of its three
-kernels on its own.
+roofline entry covers the whole call as AUTO runs it (``config.kernel_used``:
+"fused" for the one-kernel path, else the attention kernel between the
+projections); ``paths_us`` times each path the call can take (split, fused)
+and ``parts_us`` each of the split path's three kernels alone.
 """
 from __future__ import annotations
 
@@ -85,6 +87,9 @@ MEASURED_TRAFFIC = {
     "layer": {
         "early_stage_bf16_64x64_d16_b8h3/nhwc": {"bytes_per_launch": 337280548, "read": 169508388, "write": 167772160,
             "kernel": "ring", "sources": "8779ba557f649996"},
+        # the one-kernel path (--layer-kernel fused)
+        "early_stage_bf16_64x64_d16_b8h3/nhwc/fused": {"bytes_per_launch": 90591270, "read": 57036838,
+            "write": 33554432, "kernel": "fused", "sources": "6889ab74a2b8b934"},
     },
     # backward: summed over the call's kernels (matrix-core kernels, table reduction)
     "bwd": {
@@ -113,6 +118,7 @@ KERNEL_SOURCES = {
     # layer: the projections plus the attention kernel the call launches
     "layer:tile": ["halo_common.h", "mfma_util.h", "kernel_tile.hip", "proj.h", "kernel_proj.hip"],
     "layer:ring": ["halo_common.h", "mfma_util.h", "kernel_ring.hip", "proj.h", "kernel_proj.hip"],
+    "layer:fused": ["halo_common.h", "mfma_util.h", "proj.h", "kernel_layer.hip"],
     # backward: the matrix-core kernels of the path plus the table reduction
     "bwd:strip": ["halo_common.h", "mfma_util.h", "kernel_bwd_mfma.hip", "kernel_bwd_generic.hip"],
     "bwd:tile": ["halo_common.h", "mfma_util.h", "kernel_bwd_tile.hip", "kernel_bwd_generic.hip"],
@@ -145,6 +151,8 @@ def parse():
                     help="forward (the headline), backward pass, or the whole layer with its projections")
     ap.add_argument("--layout", default="nhwc", choices=["nhwc", "blocked"],
                     help="activation layout of --pass layer")
+    ap.add_argument("--layer-kernel", default="auto", choices=["auto", "fused", "split"],
+                    help="path of --pass layer's timed calls (halo_attn_layer_fwd_ex kernel)")
     ap.add_argument("--variants", default="", help="comma-separated semantic variants of the forward "
                     "(centred_offset, zero_pad, centred_mask, half_split); default: none")
     ap.add_argument("--sets", type=int, default=0, help="rotated input sets (0: enough to exceed the MALL)")
@@ -319,13 +327,33 @@ def run_layer(args):
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) / steps, time.perf_counter() - t0
 
+    lk = {"auto": _native.HALO_LAYER_KERNEL_AUTO, "fused": _native.HALO_LAYER_KERNEL_FUSED,
+          "split": _native.HALO_LAYER_KERNEL_SPLIT}[args.layer_kernel]
+
     def step(i):
-        st = lib.halo_attn_layer_fwd(*calls[i % nsets])
+        st = lib.halo_attn_layer_fwd_ex(*calls[i % nsets][:-1], lk, calls[i % nsets][-1])
         if st:
             _native.check(st)
 
     ms, wall = timed(step, args.steps, args.warmup)
-    # the three kernels on their own (same shapes and layout)
+
+    # each path of the call on its own (AUTO above takes one of them)
+    dcode_ = _native.HALO_BF16 if wl.dtype == "bf16" else _native.HALO_F32
+    paths = {}
+    for pname, pcode in (("split", _native.HALO_LAYER_KERNEL_SPLIT), ("fused", _native.HALO_LAYER_KERNEL_FUSED)):
+        try:
+            _native.layer_kernel_name(wl.B, wl.H, wl.W, C, Co, wl.heads, wl.d, wl.block, wl.halo, wl.stride,
+                                      LAYOUTS[lay], dcode_, kernel=pcode)
+        except ValueError:
+            continue
+
+        def step_path(i, pcode=pcode):
+            st = lib.halo_attn_layer_fwd_ex(*calls[i % nsets][:-1], pcode, calls[i % nsets][-1])
+            if st:
+                _native.check(st)
+
+        paths[pname] = timed(step_path, max(10, args.steps // 4), 20)[0]
+    # the three kernels of the split path on their own (same shapes and layout)
     (x, w_q, w_kv, w_o, b_o, rh, rw), y = sets[0]
     q, k, v = halo_layer_proj_in(x, w_q, w_kv, wl.heads, side, lay, stream=stream)
     attn = halo_attn_fwd(q, k, v, rh, rw, wl.block, wl.halo, wl.stride, stream=stream)
@@ -344,10 +372,12 @@ def run_layer(args):
     achieved_gbs = alg_bytes / (ms * 1e-3) / 1e9
     mfma_peak = MFMA_PEAK_TFLOPS[wl.dtype]
     mfma_bound = flops / (mfma_peak * 1e12) > alg_bytes / (HBM_PEAK_GBS * 1e9)
-    used = _native.fwd_kernel_name(wl.B, wl.heads, wl.H, wl.W, wl.d, wl.block, wl.halo, wl.stride,
-                                   _native.HALO_BF16 if wl.dtype == "bf16" else _native.HALO_F32)
+    used = _native.layer_kernel_name(wl.B, wl.H, wl.W, C, Co, wl.heads, wl.d, wl.block, wl.halo, wl.stride,
+                                     LAYOUTS[lay], dcode_, kernel=lk)
+    if used == "split":     # named by the attention kernel between the projections
+        used = _native.fwd_kernel_name(wl.B, wl.heads, wl.H, wl.W, wl.d, wl.block, wl.halo, wl.stride, dcode_)
     src_hash = kernel_source_hash(f"layer:{used}") if f"layer:{used}" in KERNEL_SOURCES else None
-    rec = MEASURED_TRAFFIC["layer"].get(f"{wl.name}/{lay}")
+    rec = MEASURED_TRAFFIC["layer"].get(f"{wl.name}/{lay}" + ("/fused" if used == "fused" else ""))
     valid = rec is not None and src_hash is not None and rec["sources"] == src_hash and rec.get("kernel") == used
     traffic = rec["bytes_per_launch"] if valid else None
     line = {
@@ -370,6 +400,7 @@ def run_layer(args):
             "mean_launch_us": round(ms * 1e3, 3),
             "kernel_sources": src_hash,
         },
+        "paths_us": {k_: round(v_ * 1e3, 3) for k_, v_ in paths.items()},
         "parts_us": {k_: round(v_ * 1e3, 2) for k_, v_ in parts.items()},
     }
     if not args.no_cpu_baseline:

@@ -24,7 +24,7 @@ from . import _native
 
 __all__ = ["halo_attn_fwd", "halo_attn_bwd", "bwd_workspace_bytes", "halo_attention",
            "halo_layer_proj_in", "halo_layer_proj_out", "halo_layer_fwd", "layer_workspace_bytes",
-           "select_kernel", "HaloError", "KERNELS", "VARIANTS", "LAYOUTS"]
+           "select_kernel", "HaloError", "KERNELS", "VARIANTS", "LAYOUTS", "LAYER_KERNELS"]
 
 HaloError = _native.HaloError
 # semantic variants (flags of halo_attn_fwd_ex; see include/halo_attn.h)
@@ -345,9 +345,13 @@ def layer_workspace_bytes(B: int, H: int, W: int, heads: int, d: int, query_stri
     return int(n)
 
 
+LAYER_KERNELS = {"auto": _native.HALO_LAYER_KERNEL_AUTO, "fused": _native.HALO_LAYER_KERNEL_FUSED,
+                 "split": _native.HALO_LAYER_KERNEL_SPLIT}
+
+
 def halo_layer_fwd(x, w_q, w_kv, w_o, b_o, rel_h, rel_w, block: int, halo: int, heads: int,
                    query_stride: int = 1, scale: float | None = None, layout: str = "nhwc",
-                   workspace=None, out=None, stream=None):
+                   workspace=None, out=None, stream=None, kernel: str = "auto"):
     """The attention layer: to_q / to_kv, halo attention, head merge, to_out.
 
     x: [B, H, W, C] ("nhwc") or [B, H/b, W/b, b*b, C] ("blocked", b = block);
@@ -356,8 +360,12 @@ def halo_layer_fwd(x, w_q, w_kv, w_o, b_o, rel_h, rel_w, block: int, halo: int, 
     Returns y in the same layout at the output resolution (H/s x W/s pixels,
     blocks of side block/s).  ``workspace``: an optional uint8 device tensor
     of at least ``layer_workspace_bytes`` bytes (allocated if None).
+    ``kernel``: "auto", "fused" (one kernel, nothing between the steps in
+    HBM) or "split" (projections and attention as three kernels).
     """
     import torch
+    if kernel not in LAYER_KERNELS:
+        raise ValueError(f"kernel must be one of {sorted(LAYER_KERNELS)}, got {kernel!r}")
     _check_device_tensors(x, x=x, w_q=w_q, w_kv=w_kv, w_o=w_o, b_o=b_o, rel_h=rel_h, rel_w=rel_w)
     B, H, W, C = _layer_pixels(x, layout, block)
     inner = w_q.shape[0]
@@ -377,16 +385,26 @@ def halo_layer_fwd(x, w_q, w_kv, w_o, b_o, rel_h, rel_w, block: int, halo: int, 
         out = torch.empty(oshape, dtype=x.dtype, device=x.device)
     elif tuple(out.shape) != oshape or out.dtype != x.dtype or out.device != x.device or not out.is_contiguous():
         raise ValueError(f"out must be a contiguous {oshape} {x.dtype} tensor on {x.device}")
-    need = layer_workspace_bytes(B, H, W, heads, d, s, "bf16" if x.dtype == torch.bfloat16 else "fp32")
+    dname = "bf16" if x.dtype == torch.bfloat16 else "fp32"
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+        # the fused path takes none (it needs 16-byte aligned x and weights,
+        # 8-byte aligned tables, bias and output, which torch's allocations are)
+        aligned = all(t.data_ptr() % 16 == 0 for t in (x, w_q, w_kv)) and \
+            all(t.data_ptr() % 8 == 0 for t in (w_o, b_o, rel_h, rel_w, out))
+        fused = kernel == "fused" or (kernel == "auto" and aligned and _native.layer_kernel_name(
+            B, H, W, C, Co, heads, d, block, halo, s, LAYOUTS[layout], _dtype_code(x)) == "fused")
+        if not fused:
+            workspace = torch.empty(max(layer_workspace_bytes(B, H, W, heads, d, s, dname), 1), dtype=torch.uint8,
+                                    device=x.device)
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     with torch.cuda.device(x.device):
-        st = _native.load().halo_attn_layer_fwd(
+        st = _native.load().halo_attn_layer_fwd_ex(
             x.data_ptr(), w_q.data_ptr(), w_kv.data_ptr(), w_o.data_ptr(), b_o.data_ptr(), rel_h.data_ptr(),
-            rel_w.data_ptr(), out.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            rel_w.data_ptr(), out.data_ptr(), ws_ptr, ws_bytes,
             B, H, W, C, Co, heads, d, block, halo, s, float(scale), LAYOUTS[layout], _dtype_code(x),
-            stream.cuda_stream)
+            LAYER_KERNELS[kernel], stream.cuda_stream)
     _native.check(st)
     return out

@@ -17,6 +17,7 @@ HALO_F32, HALO_BF16 = 0, 1
 HALO_KERNEL_AUTO, HALO_KERNEL_GENERIC, HALO_KERNEL_MFMA, HALO_KERNEL_MFMA_STRIP, HALO_KERNEL_MFMA_RING = 0, 1, 2, 3, 4
 HALO_CENTRED_OFFSET, HALO_ZERO_PAD, HALO_CENTRED_MASK, HALO_HALF_SPLIT = 1, 2, 4, 8
 HALO_LAYOUT_NHWC, HALO_LAYOUT_BLOCKED = 0, 1
+HALO_LAYER_KERNEL_AUTO, HALO_LAYER_KERNEL_FUSED, HALO_LAYER_KERNEL_SPLIT = 0, 1, 2
 STATUS = {0: "HALO_OK", -1: "HALO_ERR_NULL", -2: "HALO_ERR_SHAPE", -3: "HALO_ERR_DTYPE",
           -4: "HALO_ERR_UNSUPPORTED", -5: "HALO_ERR_HIP", -6: "HALO_ERR_ALIAS",
           -7: "HALO_ERR_WORKSPACE"}
@@ -69,6 +70,10 @@ def load() -> ctypes.CDLL:
     lib.halo_attn_layer_workspace_bytes.restype = ctypes.c_longlong
     lib.halo_attn_layer_fwd.argtypes = [vp] * 9 + [sz] + [i] * 10 + [f, i, i, vp]
     lib.halo_attn_layer_fwd.restype = i
+    lib.halo_attn_layer_fwd_ex.argtypes = [vp] * 9 + [sz] + [i] * 10 + [f, i, i, i, vp]
+    lib.halo_attn_layer_fwd_ex.restype = i
+    lib.halo_attn_layer_kernel_name.argtypes = [i] * 13
+    lib.halo_attn_layer_kernel_name.restype = ctypes.c_char_p
     lib.halo_attn_fwd_kernel_name.argtypes = [i] * 11
     lib.halo_attn_fwd_kernel_name.restype = ctypes.c_char_p
     lib.halo_attn_bwd_kernel_name.argtypes = [i] * 11
@@ -109,6 +114,16 @@ def bwd_kernel_name(B, heads, H, W, d, block, halo, stride, dtype, flags=0, kern
     name = load().halo_attn_bwd_kernel_name(B, heads, H, W, d, block, halo, stride, dtype, flags, kernel)
     if name is None:
         raise ValueError(f"halo_attn_bwd_kernel_name: {last_error()}")
+    return name.decode()
+
+
+def layer_kernel_name(B, H, W, C, C_out, heads, d, block, halo, stride, layout, dtype,
+                      kernel=HALO_LAYER_KERNEL_AUTO) -> str:
+    """The path halo_attn_layer_fwd_ex takes for these sizes ("fused" or "split"; host only)."""
+    name = load().halo_attn_layer_kernel_name(B, H, W, C, C_out, heads, d, block, halo, stride, layout, dtype,
+                                              kernel)
+    if name is None:
+        raise ValueError(f"halo_attn_layer_kernel_name: {last_error()}")
     return name.decode()
 
 

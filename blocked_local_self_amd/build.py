@@ -51,6 +51,7 @@ PER_FILE_FLAGS = {
     "kernel_bwd_mfma.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
     "kernel_bwd_tile.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
     "kernel_wide.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "kernel_layer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-command-line-argument"]

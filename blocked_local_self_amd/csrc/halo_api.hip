@@ -655,6 +655,7 @@ int halo_attn_bwd_noalloc(const void* q, const void* k, const void* v,
 namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned8(const void* p) { return ((uintptr_t)p & 7u) == 0; }
 
 // Checks of the layer's sizes; fills L (input and output grids).  empty: a
 // size is zero, nothing to compute.
@@ -765,12 +766,14 @@ long long halo_attn_layer_workspace_bytes(int B, int H, int W, int heads, int d,
     return (long long)(3 * qkv + align256((size_t)L.NPo * heads * d * esz));
 }
 
-int halo_attn_layer_fwd(const void* x, const void* w_q, const void* w_kv, const void* w_o, const void* b_o,
-                        const void* rel_h, const void* rel_w, void* y, void* workspace, size_t workspace_bytes,
-                        int B, int H, int W, int C, int C_out, int heads, int d, int block, int halo,
-                        int query_stride, float scale, int layout, int dtype, void* stream)
+int halo_attn_layer_fwd_ex(const void* x, const void* w_q, const void* w_kv, const void* w_o, const void* b_o,
+                           const void* rel_h, const void* rel_w, void* y, void* workspace, size_t workspace_bytes,
+                           int B, int H, int W, int C, int C_out, int heads, int d, int block, int halo,
+                           int query_stride, float scale, int layout, int dtype, int kernel, void* stream)
 {
     g_err[0] = 0;
+    if (kernel != HALO_LAYER_KERNEL_AUTO && kernel != HALO_LAYER_KERNEL_FUSED && kernel != HALO_LAYER_KERNEL_SPLIT)
+        return fail(HALO_ERR_SHAPE, "kernel=%d is not a halo_layer_kernel value", kernel);
     halo::LayerGeom L;
     bool empty = false;
     if (block < 1) return fail(HALO_ERR_SHAPE, "block=%d must be >= 1", block);
@@ -788,30 +791,44 @@ int halo_attn_layer_fwd(const void* x, const void* w_q, const void* w_kv, const 
     if (empty) return HALO_OK;
     if (!x || !w_q || !w_kv || !w_o || !b_o || !rel_h || !rel_w || !y)
         return fail(HALO_ERR_NULL, "null pointer among x, w_q, w_kv, w_o, b_o, rel_h, rel_w, y");
-    if (!workspace) return fail(HALO_ERR_NULL, "null workspace");
     const size_t esz = dtype == HALO_BF16 ? 2 : 4;
     const size_t inner = (size_t)heads * d;
-    const size_t qkv = align256((size_t)L.NP * inner * esz), ab = align256((size_t)L.NPo * inner * esz);
-    const size_t need = 3 * qkv + ab;
-    if (workspace_bytes < need || ((uintptr_t)workspace & 255u))
-        return fail(HALO_ERR_WORKSPACE, "workspace of %zu bytes at %p: need %zu bytes, 256-byte aligned",
-                    workspace_bytes, workspace, need);
     const int r = block + 2 * halo;
     const size_t xb = (size_t)L.NP * C * esz, yb = (size_t)L.NPo * C_out * esz;
     const size_t wqb = inner * C * esz, wkvb = 2 * inner * C * esz, wob = (size_t)C_out * inner * esz,
                  bb = (size_t)C_out * esz, tb = (size_t)(2 * r - 1) * d * esz;
     const void* ins[7] = {x, w_q, w_kv, w_o, b_o, rel_h, rel_w};
     const size_t insz[7] = {xb, wqb, wkvb, wob, bb, tb, tb};
-    for (int i = 0; i < 7; ++i) {
+    for (int i = 0; i < 7; ++i)
         if (overlaps(y, yb, ins[i], insz[i])) return fail(HALO_ERR_ALIAS, "y overlaps an input");
-        if (overlaps(workspace, need, ins[i], insz[i])) return fail(HALO_ERR_ALIAS, "workspace overlaps an input");
-    }
-    if (overlaps(workspace, need, y, yb)) return fail(HALO_ERR_ALIAS, "workspace overlaps y");
 
-    unsigned char* ws = static_cast<unsigned char*>(workspace);
-    void *q = ws, *k = ws + qkv, *v = ws + 2 * qkv, *attn = ws + 3 * qkv;
     const bool bf16 = dtype == HALO_BF16;
     hipStream_t s = (hipStream_t)stream;
+    const bool fused_ok = halo::layer_fused_supported(L, block, halo, query_stride, bf16) && aligned16(x) &&
+                          aligned16(w_q) && aligned16(w_kv) && aligned8(w_o) && aligned8(b_o) && aligned8(rel_h) &&
+                          aligned8(rel_w) && aligned8(y);
+    if (kernel == HALO_LAYER_KERNEL_FUSED && !fused_ok)
+        return fail(HALO_ERR_UNSUPPORTED, "the fused layer kernel does not take these arguments");
+    if (kernel == HALO_LAYER_KERNEL_FUSED || (kernel == HALO_LAYER_KERNEL_AUTO && fused_ok &&
+                                              halo::layer_fused_preferred(L, block, halo, query_stride))) {
+        const hipError_t e = halo::launch_layer_fused(x, w_q, w_kv, w_o, b_o, rel_h, rel_w, y, L, block, halo,
+                                                      scale, s);
+        if (e != hipSuccess) return fail(HALO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+        return HALO_OK;
+    }
+
+    // the split path: q, k, v and the attention output in the workspace
+    if (!workspace) return fail(HALO_ERR_NULL, "null workspace");
+    const size_t qkv = align256((size_t)L.NP * inner * esz), ab = align256((size_t)L.NPo * inner * esz);
+    const size_t need = 3 * qkv + ab;
+    if (workspace_bytes < need || ((uintptr_t)workspace & 255u))
+        return fail(HALO_ERR_WORKSPACE, "workspace of %zu bytes at %p: need %zu bytes, 256-byte aligned",
+                    workspace_bytes, workspace, need);
+    for (int i = 0; i < 7; ++i)
+        if (overlaps(workspace, need, ins[i], insz[i])) return fail(HALO_ERR_ALIAS, "workspace overlaps an input");
+    if (overlaps(workspace, need, y, yb)) return fail(HALO_ERR_ALIAS, "workspace overlaps y");
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    void *q = ws, *k = ws + qkv, *v = ws + 2 * qkv, *attn = ws + 3 * qkv;
     const bool mi = halo::proj_in_mfma_supported(L, bf16) && aligned16(x) && aligned16(w_q) && aligned16(w_kv);
     hipError_t e = halo::launch_proj_in(x, w_q, w_kv, q, k, v, L, bf16, mi, s);
     if (e != hipSuccess) return fail(HALO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -822,6 +839,51 @@ int halo_attn_layer_fwd(const void* x, const void* w_q, const void* w_kv, const 
     e = halo::launch_proj_out(attn, w_o, b_o, y, L, bf16, mo, s);
     if (e != hipSuccess) return fail(HALO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return HALO_OK;
+}
+
+int halo_attn_layer_fwd(const void* x, const void* w_q, const void* w_kv, const void* w_o, const void* b_o,
+                        const void* rel_h, const void* rel_w, void* y, void* workspace, size_t workspace_bytes,
+                        int B, int H, int W, int C, int C_out, int heads, int d, int block, int halo,
+                        int query_stride, float scale, int layout, int dtype, void* stream)
+{
+    return halo_attn_layer_fwd_ex(x, w_q, w_kv, w_o, b_o, rel_h, rel_w, y, workspace, workspace_bytes, B, H, W, C,
+                                  C_out, heads, d, block, halo, query_stride, scale, layout, dtype,
+                                  HALO_LAYER_KERNEL_AUTO, stream);
+}
+
+const char* halo_attn_layer_kernel_name(int B, int H, int W, int C, int C_out, int heads, int d, int block, int halo,
+                                        int query_stride, int layout, int dtype, int kernel)
+{
+    g_err[0] = 0;
+    if (kernel != HALO_LAYER_KERNEL_AUTO && kernel != HALO_LAYER_KERNEL_FUSED && kernel != HALO_LAYER_KERNEL_SPLIT) {
+        fail(HALO_ERR_SHAPE, "kernel=%d is not a halo_layer_kernel value", kernel);
+        return nullptr;
+    }
+    halo::LayerGeom L;
+    bool empty = false;
+    if (block < 1) {
+        fail(HALO_ERR_SHAPE, "block=%d must be >= 1", block);
+        return nullptr;
+    }
+    if (query_stride < 1 || block % query_stride) {
+        fail(HALO_ERR_SHAPE, "query_stride=%d must be >= 1 and divide block=%d", query_stride, block);
+        return nullptr;
+    }
+    if (check_layer(B, H, W, C, C_out, heads, d, block, query_stride, layout, dtype, L, empty)) return nullptr;
+    {
+        halo::Geometry g;
+        bool e2 = false;
+        if (check_sizes(B, heads, H, W, d, block, halo, query_stride, 1.0f, dtype, g, e2)) return nullptr;
+    }
+    if (empty) return "none";
+    const bool ok = halo::layer_fused_supported(L, block, halo, query_stride, dtype == HALO_BF16);
+    if (kernel == HALO_LAYER_KERNEL_FUSED && !ok) {
+        fail(HALO_ERR_UNSUPPORTED, "the fused layer kernel does not take these arguments");
+        return nullptr;
+    }
+    if (kernel == HALO_LAYER_KERNEL_SPLIT) return "split";
+    if (kernel == HALO_LAYER_KERNEL_FUSED) return "fused";
+    return ok && halo::layer_fused_preferred(L, block, halo, query_stride) ? "fused" : "split";
 }
 
 }  // extern "C"

@@ -57,4 +57,16 @@ hipError_t launch_proj_in(const void* x, const void* w_q, const void* w_kv, void
 hipError_t launch_proj_out(const void* attn, const void* w_o, const void* b_o, void* y, const LayerGeom& L, bool bf16,
                            bool mfma, hipStream_t st);
 
+// The whole layer in one kernel (kernel_layer.hip): bf16, query stride 1,
+// d in {16, 32}, block in {4, 8} dividing H and W, window side <= 16,
+// C % 32 == 0, C_out % 16 == 0 and C_out <= 256, within one workgroup's LDS.
+// The caller checks pointer alignment (16 bytes for x, w_q, w_kv; 8 bytes
+// for w_o, b_o, rel_h, rel_w, y).
+bool layer_fused_supported(const LayerGeom& L, int block, int halo, int stride, bool bf16);
+// Whether AUTO takes the fused kernel where it is supported (by measurement).
+bool layer_fused_preferred(const LayerGeom& L, int block, int halo, int stride);
+hipError_t launch_layer_fused(const void* x, const void* w_q, const void* w_kv, const void* w_o, const void* b_o,
+                              const void* rel_h, const void* rel_w, void* y, const LayerGeom& L, int block, int halo,
+                              float scale, hipStream_t s);
+
 }  // namespace halo

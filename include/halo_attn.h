@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define HALO_ATTN_ABI_VERSION 4
+#define HALO_ATTN_ABI_VERSION 5
 
 typedef enum halo_dtype {
     HALO_F32 = 0,
@@ -331,10 +331,13 @@ long long halo_attn_layer_workspace_bytes(int B, int H, int W, int heads, int d,
 /* The whole layer: proj_in, the attention (halo_attn_fwd, kernel AUTO) and
  * proj_out, on `stream`, with q, k, v and the attention output in the
  * caller's workspace (at least halo_attn_layer_workspace_bytes(), 256-byte
- * aligned; contents undefined on return).  x has B x H x W pixels of C
- * channels, y has B x H/s x W/s pixels of C_out channels (s = query_stride;
- * blocks of side block/s in the blocked layout).  Errors as for the parts,
- * plus HALO_ERR_WORKSPACE. */
+ * aligned; contents undefined on return), or the one-kernel fused path
+ * where it applies and is the faster (halo_attn_layer_kernel_name tells
+ * which; that path uses no workspace and accepts a NULL one; on the shapes
+ * measured AUTO takes the split path).  x has
+ * B x H x W pixels of C channels, y has B x H/s x W/s pixels of C_out
+ * channels (s = query_stride; blocks of side block/s in the blocked
+ * layout).  Errors as for the parts, plus HALO_ERR_WORKSPACE. */
 int halo_attn_layer_fwd(const void* x, const void* w_q, const void* w_kv,
                         const void* w_o, const void* b_o,
                         const void* rel_h, const void* rel_w, void* y,
@@ -342,6 +345,47 @@ int halo_attn_layer_fwd(const void* x, const void* w_q, const void* w_kv,
                         int B, int H, int W, int C, int C_out, int heads, int d,
                         int block, int halo, int query_stride, float scale,
                         int layout, int dtype, void* stream);
+
+/* How halo_attn_layer_fwd_ex computes the layer.  SPLIT: the three steps
+ * above, through the workspace.  FUSED: one kernel per image block that
+ * stages the block's window of x in LDS and, head by head, projects k and v
+ * of the window and q of the block, runs the attention and accumulates
+ * to_out in registers, writing y once (HaloNet appendix D: activations stay
+ * blocked, no formatting passes; the module of the pswp.cn page, section 4).
+ * FUSED takes bf16 with query_stride 1, d in {16, 32}, block in {4, 8}
+ * dividing H and W, block + 2*halo <= 16, C % 32 == 0, C_out % 16 == 0,
+ * C_out <= 256, a window of x that fits one workgroup's LDS, 16-byte
+ * aligned x, w_q, w_kv and 8-byte aligned w_o, b_o, rel_h, rel_w, y.
+ * Storage points are the split path's (q, k, v, the probabilities and the
+ * attention output rounded to bf16); the softmax uses the exact maximum.
+ * It moves about half the split path's HBM bytes but is the slower of the
+ * two on the shapes measured, so AUTO takes SPLIT. */
+typedef enum halo_layer_kernel {
+    HALO_LAYER_KERNEL_AUTO = 0,
+    HALO_LAYER_KERNEL_FUSED = 1,
+    HALO_LAYER_KERNEL_SPLIT = 2
+} halo_layer_kernel;
+
+/* halo_attn_layer_fwd with a halo_layer_kernel value (else HALO_ERR_SHAPE);
+ * FUSED with arguments it does not take returns HALO_ERR_UNSUPPORTED.  Only
+ * the split path uses (and checks) the workspace: the fused one accepts a
+ * NULL workspace. */
+int halo_attn_layer_fwd_ex(const void* x, const void* w_q, const void* w_kv,
+                           const void* w_o, const void* b_o,
+                           const void* rel_h, const void* rel_w, void* y,
+                           void* workspace, size_t workspace_bytes,
+                           int B, int H, int W, int C, int C_out, int heads, int d,
+                           int block, int halo, int query_stride, float scale,
+                           int layout, int dtype, int kernel, void* stream);
+
+/* Which path halo_attn_layer_fwd_ex takes for these sizes, with aligned
+ * pointers, given a halo_layer_kernel value: "fused", "split", or "none"
+ * when a size is zero.  Host only; the string is static.  Invalid arguments,
+ * or FUSED where it does not apply: NULL, with halo_attn_last_error()
+ * telling why. */
+const char* halo_attn_layer_kernel_name(int B, int H, int W, int C, int C_out, int heads, int d,
+                                        int block, int halo, int query_stride, int layout, int dtype,
+                                        int kernel);
 
 /* Host-only query: the halo_kernel value AUTO would run for these
  * arguments (HALO_KERNEL_GENERIC or HALO_KERNEL_MFMA), or a negative

@@ -182,12 +182,14 @@ def test_backward_workspace_query():
 # ------------------------------------------------------------------ the layer
 
 def layer_call(lib, *, x=1, wq=2, wkv=3, wo=4, bo=5, rh=6, rw=7, y=8, ws=9, ws_bytes=1 << 40, B=1, H=8, W=8,
-               C=32, Co=32, heads=2, d=16, block=4, halo=1, stride=1, scale=0.25, layout=0, dtype=1):
+               C=32, Co=32, heads=2, d=16, block=4, halo=1, stride=1, scale=0.25, layout=0, dtype=1,
+               kernel=_native.HALO_LAYER_KERNEL_SPLIT):
     # fake pointers 2^36 apart: every call below must fail before any launch
+    # (the split path, whose checks include the workspace's)
     ptr = lambda v: ctypes.c_void_p(v << 36 if v else None)
-    return lib.halo_attn_layer_fwd(ptr(x), ptr(wq), ptr(wkv), ptr(wo), ptr(bo), ptr(rh), ptr(rw), ptr(y), ptr(ws),
-                                   ws_bytes, B, H, W, C, Co, heads, d, block, halo, stride, scale, layout, dtype,
-                                   None)
+    return lib.halo_attn_layer_fwd_ex(ptr(x), ptr(wq), ptr(wkv), ptr(wo), ptr(bo), ptr(rh), ptr(rw), ptr(y),
+                                      ptr(ws), ws_bytes, B, H, W, C, Co, heads, d, block, halo, stride, scale,
+                                      layout, dtype, kernel, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -201,6 +203,48 @@ def layer_call(lib, *, x=1, wq=2, wkv=3, wo=4, bo=5, rh=6, rw=7, y=8, ws=9, ws_b
 def test_layer_invalid_arguments_rejected_on_host(lib, kw, status):
     assert layer_call(lib, **kw) == status, _native.last_error()
     assert _native.last_error() != ""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=0), -1), (dict(y=1), -6), (dict(stride=2), -4), (dict(dtype=0), -4), (dict(C=48, Co=48), -4),
+])
+def test_fused_layer_invalid_arguments_rejected_on_host(lib, kw, status):
+    """The fused path's own refusals (it takes no workspace: a null one is
+    not an error there)."""
+    assert layer_call(lib, ws=0, kernel=_native.HALO_LAYER_KERNEL_FUSED, **kw) == status, _native.last_error()
+
+
+def test_layer_kernel_query_and_choice_on_host(lib):
+    bf, f32 = _native.HALO_BF16, _native.HALO_F32
+    FUSED = _native.HALO_LAYER_KERNEL_FUSED
+    name = lambda *a: _native.layer_kernel_name(*a, kernel=FUSED)
+    assert name(32, 64, 64, 128, 128, 8, 16, 8, 3, 1, 0, bf) == "fused"     # the bench's layer shape
+    assert name(2, 16, 24, 64, 48, 4, 16, 8, 3, 1, 1, bf) == "fused"        # blocked layout
+    assert name(1, 12, 8, 64, 128, 4, 32, 4, 6, 1, 0, bf) == "fused"        # block 4, 16x16 window
+    for args in [(1, 12, 8, 64, 256, 4, 32, 4, 6, 1, 0, bf),               # W_o of a head beyond the prefetch
+                 (32, 64, 64, 128, 128, 8, 16, 8, 3, 2, 0, bf),             # query stride 2
+                 (32, 64, 64, 128, 128, 8, 16, 8, 3, 1, 0, f32),            # fp32
+                 (1, 24, 24, 128, 128, 8, 16, 12, 3, 1, 0, bf),             # block 12
+                 (1, 16, 16, 128, 128, 4, 32, 8, 5, 1, 0, bf),              # 18x18 window
+                 (1, 16, 16, 48, 48, 3, 16, 8, 3, 1, 0, bf),                # C % 32 != 0
+                 (1, 16, 16, 64, 512, 4, 16, 8, 3, 1, 0, bf),               # C_out > 256
+                 (1, 16, 16, 1024, 64, 4, 16, 8, 4, 1, 0, bf)]:             # window of x beyond the LDS
+        with pytest.raises(ValueError, match="fused"):
+            name(*args)
+        assert _native.layer_kernel_name(*args) == "split"
+    # AUTO takes the split path (the faster where both apply)
+    assert _native.layer_kernel_name(32, 64, 64, 128, 128, 8, 16, 8, 3, 1, 0, bf) == "split"
+    assert name(0, 16, 16, 64, 64, 4, 16, 8, 3, 1, 0, bf) == "none"
+    with pytest.raises(ValueError, match="query_stride"):
+        name(1, 16, 16, 64, 64, 4, 16, 8, 3, 3, 0, bf)
+    with pytest.raises(ValueError, match="kernel"):
+        _native.layer_kernel_name(1, 16, 16, 64, 64, 4, 16, 8, 3, 1, 0, bf, kernel=7)
+    p = lambda v: ctypes.c_void_p(v << 36 if v else None)
+    args = [p(1), p(2), p(3), p(4), p(5), p(6), p(7), p(8), p(9), 1 << 40, 1, 16, 16, 64, 64, 2, 16, 8, 2]
+    # an unknown kernel value; the fused kernel asked for a strided layer (refused before any launch)
+    assert lib.halo_attn_layer_fwd_ex(*args, 1, 0.25, 0, bf, 3, None) == -2
+    assert lib.halo_attn_layer_fwd_ex(*args, 2, 0.25, 0, bf, _native.HALO_LAYER_KERNEL_FUSED, None) == -4
+    assert "fused" in _native.last_error()
 
 
 def test_layer_parts_reject_on_host(lib):

@@ -23,7 +23,7 @@ import torch
 
 import oracle
 from blocked_local_self_amd import (halo_layer_proj_in, halo_layer_proj_out, halo_layer_fwd, halo_attn_fwd,
-                                    HaloError)
+                                    HaloError, _native)
 from blocked_local_self_amd.inputs import make_layer_inputs
 
 pytestmark = pytest.mark.gpu
@@ -123,16 +123,79 @@ LAYER_CASES = [
 ]
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-@pytest.mark.parametrize("case", LAYER_CASES, ids=lambda c: "x".join(map(str, c)))
-def test_layer_matches_oracle(case, dtype):
+# (B, H, W, C, C_out, heads, d, block, halo, stride, layout) the fused
+# kernel takes: both head widths, blocks of 4 and 8 (one query tile, four),
+# windows from 6 to 16 pixels a side (3 to 16 key tiles, padded key tiles
+# masked), halo 0, C != heads*d, C_out from one to sixteen 16-channel tiles,
+# both layouts, non-square images and several images
+FUSED_CASES = [
+    (1, 8, 8, 32, 16, 2, 16, 4, 1, 1, "nhwc"),
+    (2, 16, 24, 64, 48, 4, 16, 8, 3, 1, "blocked"),
+    (1, 16, 16, 96, 64, 3, 32, 8, 4, 1, "nhwc"),
+    (1, 12, 8, 64, 128, 4, 32, 4, 6, 1, "nhwc"),
+    (2, 16, 16, 192, 128, 8, 16, 8, 2, 1, "blocked"),
+    (1, 8, 8, 64, 64, 2, 32, 8, 0, 1, "nhwc"),
+]
+
+
+def run_layer_case(case, dtype, kernel):
     B, H, W, C, Co, heads, d, block, halo, stride, layout = case
-    say("layer", case, dtype)
     x, w_q, w_kv, w_o, b_o, rh, rw = make_layer_inputs(B, H, W, C, heads, d, block, halo, C_out=Co, dtype=dtype,
                                                        seed=11)
     xl = torch.as_tensor(oracle.from_nhwc(x.float().numpy(), layout, block)).to(x.dtype)
     args = [t.to(DEV).contiguous() for t in (xl, w_q, w_kv, w_o, b_o, rh, rw)]
-    y = halo_layer_fwd(*args, block, halo, heads, stride, layout=layout)
+    y = halo_layer_fwd(*args, block, halo, heads, stride, layout=layout, kernel=kernel)
+    torch.cuda.synchronize()
+    return y, [f64(t) for t in (xl, w_q, w_kv, w_o, b_o, rh, rw)]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_fused_layer_matches_oracle(case):
+    """The one-kernel layer against the oracle with the same bf16 storage
+    points, and against the three-kernel path."""
+    B, H, W, C, Co, heads, d, block, halo, stride, layout = case
+    say("fused layer", case)
+    assert _native.layer_kernel_name(B, H, W, C, Co, heads, d, block, halo, stride,
+                                     1 if layout == "blocked" else 0, _native.HALO_BF16,
+                                     kernel=_native.HALO_LAYER_KERNEL_FUSED) == "fused"
+    y, ref_in = run_layer_case(case, "bf16", "fused")
+    exact = oracle.halo_layer_ref(*ref_in, block, halo, heads, stride, layout=layout)
+    rounded = layer_ref_rounded(*ref_in, block, halo, heads, stride, layout)
+    assert tuple(y.shape) == exact.shape
+    g = f64(y)
+    assert np.isfinite(g).all()
+    m = float(np.abs(exact).max())
+    e1, e2 = float(np.abs(g - rounded).max()), float(np.abs(g - exact).max())
+    say(f"  err vs rounded oracle {e1 / m:.3g}, vs fp64 layer {e2 / m:.3g} (of max|ref| {m:.3g})")
+    assert e1 <= 2e-2 * m and e2 <= 5e-2 * m
+    y2, _ = run_layer_case(case, "bf16", "split")
+    e3 = float((y.float() - y2.float()).abs().max())
+    say(f"  fused vs split {e3 / m:.3g}")
+    assert e3 <= 2e-2 * m
+
+
+def test_fused_layer_refuses_what_it_does_not_take():
+    x, w_q, w_kv, w_o, b_o, rh, rw = (t.to(DEV) for t in make_layer_inputs(1, 16, 16, 64, 2, 16, 8, 2, seed=1))
+    with pytest.raises(HaloError):
+        halo_layer_fwd(x, w_q, w_kv, w_o, b_o, rh, rw, 8, 2, 2, 2, kernel="fused")     # query stride 2
+    y = halo_layer_fwd(x, w_q, w_kv, w_o, b_o, rh, rw, 8, 2, 2, 2)                     # auto: the split path
+    torch.cuda.synchronize()
+    assert np.isfinite(f64(y)).all()
+
+
+@pytest.mark.parametrize("kernel", ["auto", "fused"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("case", LAYER_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_layer_matches_oracle(case, dtype, kernel):
+    B, H, W, C, Co, heads, d, block, halo, stride, layout = case
+    if kernel == "fused" and (dtype == "fp32" or stride != 1 or C % 32):
+        pytest.skip("a shape the fused kernel does not take (the split path covers it)")
+    say("layer", case, dtype, kernel)
+    x, w_q, w_kv, w_o, b_o, rh, rw = make_layer_inputs(B, H, W, C, heads, d, block, halo, C_out=Co, dtype=dtype,
+                                                       seed=11)
+    xl = torch.as_tensor(oracle.from_nhwc(x.float().numpy(), layout, block)).to(x.dtype)
+    args = [t.to(DEV).contiguous() for t in (xl, w_q, w_kv, w_o, b_o, rh, rw)]
+    y = halo_layer_fwd(*args, block, halo, heads, stride, layout=layout, kernel=kernel)
     torch.cuda.synchronize()
     ref_in = [f64(t) for t in (xl, w_q, w_kv, w_o, b_o, rh, rw)]
     exact = oracle.halo_layer_ref(*ref_in, block, halo, heads, stride, layout=layout)
@@ -150,11 +213,11 @@ def test_layer_matches_oracle(case, dtype):
 
 
 def test_layer_equals_its_parts():
-    """halo_layer_fwd is proj_in, the attention and proj_out in sequence:
-    bitwise the same as calling the three entry points."""
+    """The split path of halo_layer_fwd is proj_in, the attention and
+    proj_out in sequence: bitwise the same as calling the three entry points."""
     B, H, W, C, heads, d, block, halo = 2, 16, 16, 64, 4, 16, 8, 3
     x, w_q, w_kv, w_o, b_o, rh, rw = (t.to(DEV) for t in make_layer_inputs(B, H, W, C, heads, d, block, halo, seed=2))
-    y = halo_layer_fwd(x, w_q, w_kv, w_o, b_o, rh, rw, block, halo, heads)
+    y = halo_layer_fwd(x, w_q, w_kv, w_o, b_o, rh, rw, block, halo, heads, kernel="split")
     q, k, v = halo_layer_proj_in(x, w_q, w_kv, heads)
     attn = halo_attn_fwd(q, k, v, rh, rw, block, halo)
     y2 = halo_layer_proj_out(attn, w_o, b_o)
@@ -169,7 +232,7 @@ def test_layer_full_size_sampled_images():
     B, H, W, C, heads, d, block, halo = 32, 64, 64, 128, 8, 16, 8, 3
     x, w_q, w_kv, w_o, b_o, rh, rw = make_layer_inputs(B, H, W, C, heads, d, block, halo, seed=0)
     args = [t.to(DEV) for t in (x, w_q, w_kv, w_o, b_o, rh, rw)]
-    say("layer full size")
+    say("layer full size", _native.layer_kernel_name(B, H, W, C, C, heads, d, block, halo, 1, 0, _native.HALO_BF16))
     y = halo_layer_fwd(*args, block, halo, heads)
     torch.cuda.synchronize()
     for b in (0, B - 1):
@@ -187,5 +250,5 @@ def test_layer_errors_raise():
     with pytest.raises(ValueError):
         halo_layer_fwd(x, w_q, w_kv, w_o, b_o, rh, rw, 4, 1, 3)        # heads does not divide inner
     with pytest.raises(HaloError):
-        halo_layer_fwd(x, w_q, w_kv, w_o, b_o, rh, rw, 4, 1, 2, workspace=torch.empty(16, dtype=torch.uint8,
-                                                                                          device=DEV))
+        halo_layer_fwd(x, w_q, w_kv, w_o, b_o, rh, rw, 4, 1, 2, kernel="split",
+                       workspace=torch.empty(16, dtype=torch.uint8, device=DEV))     # too small for the split path
