@@ -85,8 +85,8 @@ MEASURED_TRAFFIC = {
     },
     # layer: summed over the call's kernels (to_q/to_kv, attention, to_out)
     "layer": {
-        "early_stage_bf16_64x64_d16_b8h3/nhwc": {"bytes_per_launch": 337280548, "read": 169508388, "write": 167772160,
-            "kernel": "ring", "sources": "8779ba557f649996"},
+        "early_stage_bf16_64x64_d16_b8h3/nhwc": {"bytes_per_launch": 337275684, "read": 169503524, "write": 167772160,
+            "kernel": "ring", "sources": "9b0d378c69acfb61"},
         # the one-kernel path (--layer-kernel fused)
         "early_stage_bf16_64x64_d16_b8h3/nhwc/fused": {"bytes_per_launch": 90591270, "read": 57036838,
             "write": 33554432, "kernel": "fused", "sources": "6889ab74a2b8b934"},
