@@ -754,8 +754,34 @@ void tile_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         if (p.midstage) {
             if (!staged) stage();
         } else {
+            // the thread's further staging items: loads issued before the
+            // barrier (the compute registers are free here), so their latency
+            // overlaps the wait for the other waves' last items
+            constexpr int kMore = 2;
+            u32x4 mk[kMore][2], mv[kMore][2];
+            Item mit[kMore];
+            bool mh[kMore];
+#pragma unroll
+            for (int j = 0; j < kMore; ++j) {
+                const int e = my_e + (j + 1) * kThreads;
+                mh[j] = e < ntotal;
+                if (mh[j]) {
+                    mit[j] = item_of(e);
+                    load_item(mit[j], nlo, mk[j], mv[j]);
+                }
+            }
             __syncthreads();
-            stage();
+            __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0)
+            if (have) store_item(my_it, nlo, pk, pv, kmax_next);
+#pragma unroll
+            for (int j = 0; j < kMore; ++j)
+                if (mh[j]) store_item(mit[j], nlo, mk[j], mv[j], kmax_next);
+            for (int e = my_e + (kMore + 1) * kThreads; e < ntotal; e += kThreads) {
+                u32x4 kk[2], vv[2];
+                const Item it = item_of(e);
+                load_item(it, nlo, kk, vv);
+                store_item(it, nlo, kk, vv, kmax_next);
+            }
         }
         __syncthreads();
     }
