@@ -814,12 +814,12 @@ static TilePlan tile_plan(const Geometry& g, int pc, int nct, int qt, int waves,
     p.midstage = mid ? 1 : 0;
     p.ring = rup(mid ? g.r + g.block : g.r, pc == 4 ? 4 : 2);
     const int over = std::max(0, (nbx - 1) * g.block + nct * pc - p.SWv);   // pixels read past a row
-    // V^T channel pitch: >= ring*SWv + over-read, = 4 (mod 8) dwords: the 16
-    // channels of a fragment read then start 4*odd dwords apart, i.e. in 16
-    // distinct 4-dword bank groups of the 64 banks, and the two lane halves
-    // (rows one slot = SWv/2 = 2 mod 4 dwords apart) take the other halves
+    // V^T channel pitch: >= ring*SWv + over-read, = 2 (mod 8) dwords.  LDS
+    // serves 8-byte reads 16 lanes per pass over 32 banks of 4 bytes: the 16
+    // channels of a fragment read (lanes 0-15, and 16-31 one slot on) then
+    // start 2*odd dwords apart and cover the 32 banks once
     p.CP = rup(p.ring * p.SWv + over, 2);
-    while ((p.CP / 2) % 8 != 4 || p.CP % 2) ++p.CP;
+    while ((p.CP / 2) % 8 != 2 || p.CP % 2) ++p.CP;
     const int side = g.block / g.stride;
     p.tiles = (side * side + 15) / 16;
     p.groups = (p.tiles + qt - 1) / qt;
