@@ -317,10 +317,11 @@ void wide_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 
 static int wround(int x, int m) { return (x + m - 1) / m * m; }
 
-// Windows of 33..48 columns (three 16-column chunks) for d = 16.
+// Windows of 33..48 columns (three 16-column chunks) for d = 16 and 32
+// (two chunk buffers of 14 rows x 48 columns: 43 KB each at d = 32).
 bool wide_supported(const Geometry& g, bool bf16)
 {
-    return bf16 && g.d == 16 && g.r > 32 && g.r <= 48 && g.block % 4 == 0;
+    return bf16 && (g.d == 16 || g.d == 32) && g.r > 32 && g.r <= 48 && g.block % 4 == 0;
 }
 
 template <int D, int NCH, int QT>
@@ -356,6 +357,7 @@ static hipError_t wide_t(const void* q, const void* k, const void* v, const void
 hipError_t launch_wide(const void* q, const void* k, const void* v, const void* rh, const void* rw, void* out,
                        float* lse, const Geometry& g, hipStream_t st)
 {
+    if (g.d == 32) return wide_t<32, 3, HALO_WIDE_QT>(q, k, v, rh, rw, out, lse, g, st);
     return wide_t<16, 3, HALO_WIDE_QT>(q, k, v, rh, rw, out, lse, g, st);
 }
 

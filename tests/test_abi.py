@@ -65,7 +65,8 @@ def call(lib, *, q=1, k=1, v=1, rh=1, rw=1, out=1 << 40, B=1, heads=1, H=8, W=8,
     (dict(B=-1), -2), (dict(W=-3), -2), (dict(kernel=9), -2),
     (dict(block=200, halo=30), -2), (dict(scale=float("inf")), -2), (dict(scale=float("nan")), -2),
     (dict(kernel=2, dtype=0), -4), (dict(kernel=2, d=64), -4), (dict(kernel=2, block=6), -4),
-    (dict(kernel=2, block=8, halo=17), -4), (dict(kernel=2, block=8, halo=13, d=32), -4),
+    (dict(kernel=2, block=8, halo=17), -4), (dict(kernel=2, block=8, halo=17, d=32), -4),
+    (dict(kernel=3, block=8, halo=13, d=32), -4),          # the strip kernel holds 32 columns at d = 32
     (dict(B=1 << 30, heads=1 << 30, H=1 << 15, W=1 << 15), -2),
     # 46341^2 >= 2^31 pixels in one image: the kernels' 32-bit pixel indices
     # would wrap (d = 1 keeps every other size check satisfied)
@@ -96,7 +97,8 @@ def test_kernel_selection():
     assert select_kernel(64, 8, 3, 1, "bf16") == "generic"
     assert select_kernel(16, 2, 1, 1, "bf16") == "generic"
     assert select_kernel(16, 8, 13, 1, "bf16") == "mfma"      # r = 34: three column chunks (d = 16)
-    assert select_kernel(32, 8, 13, 1, "bf16") == "generic"   # r = 34 with d = 32 does not fit LDS
+    assert select_kernel(32, 8, 13, 1, "bf16") == "mfma"      # r = 34 with d = 32: the streaming kernel
+    assert select_kernel(32, 8, 17, 1, "bf16") == "generic"   # r = 42
     assert select_kernel(16, 8, 17, 1, "bf16") == "generic"   # r = 42
     with pytest.raises(HaloError):
         select_kernel(16, 4, 1, 3, "bf16")

@@ -77,6 +77,9 @@ SMALL = [
     (1, 2, 64, 64, 16, 32, 3, 1),   # r = 38: three column chunks (strip kernel, d = 16)
     (1, 1, 40, 44, 16, 8, 13, 1),   # r = 34, ragged
     (1, 1, 24, 40, 16, 12, 14, 2),  # r = 40, the largest three-chunk window, strided
+    (1, 2, 64, 64, 32, 32, 3, 1),   # r = 38 at d = 32 (streaming kernel)
+    (1, 1, 40, 44, 32, 8, 13, 1),   # r = 34 at d = 32, ragged
+    (1, 1, 24, 40, 32, 12, 14, 2),  # r = 40 at d = 32, strided
 ]
 
 
