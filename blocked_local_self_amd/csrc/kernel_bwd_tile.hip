@@ -286,6 +286,15 @@ void bwd_query_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
         }
 
         // ---- the window, patch by patch
+        // 0/1 operands picking channels 16mt..16mt+15: K . sel^T is the
+        // patch's channel block as an MFMA result, lane (n, g) = channel
+        // 16mt + n of keys 4g..4g+3 (patch row g), i.e. the A operand of
+        // dq^T += K^T dS (exact: the products pick single bf16 values)
+        FragT selk[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int e = 0; e < KPL; ++e) selk[mt][e] = (gq * KPL + e == 16 * mt + n) ? (short)0x3F80 : (short)0;
         f32x4 dQt[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) dQt[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -293,8 +302,8 @@ void bwd_query_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
 #pragma unroll
         for (int rq = 0; rq < NP; ++rq) rowsum[rq] = 0.f;
         // A-operand lane (m, kg): key m of the patch = (row m >> 2, column
-        // m & 3), channels kg*KPL..; K^T gather lane (channel n, kg): patch
-        // row kg, columns 0..3.  Column tile by column tile: once a tile's
+        // m & 3), channels kg*KPL..; its K^T (lane (channel n, kg): patch
+        // row kg, columns 0..3) comes from an MFMA against selk.  Column tile by column tile: once a tile's
         // columns are done, their sums over the window (and over the four
         // lanes of a query) replace their width terms in the scratch, at the
         // same entries; every other entry is zeroed after the loop, so the
@@ -308,7 +317,6 @@ void bwd_query_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
 #pragma unroll
             for (int rq = 0; rq < NP; ++rq) {
                 const int ta = 4 * rq + (n >> 2);      // row of this lane's A-operand key
-                const int tg = 4 * rq + gq;            // row of this lane's K^T gather
                 const unsigned chA = D == 32 ? bt_chunk<D>(gq, ta) : bt_chunk<D>(gq >> 1, ta) + (gq & 1) * 8;
                 const unsigned a = (unsigned)(4 * rq) * rowb + kA + (unsigned)(4 * ct) * PIXB + chA;
                 const FragT kf = bt_ld<FragT>(smem, a);
@@ -326,14 +334,8 @@ void bwd_query_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k
                 const s16x4_t dsb = bf16x4_of(ds[0], ds[1], ds[2], ds[3]);
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    const int ch = 16 * mt + n;
-                    const unsigned base = (unsigned)tg * rowb + (unsigned)(4 * ct) * PIXB +
-                                          bt_chunk<D>(ch >> 3, tg) + (unsigned)(ch & 7) * 2;
-                    const s16x4_t kt = pack4(bt_ld<unsigned short>(smem, base),
-                                             bt_ld<unsigned short>(smem, base + PIXB),
-                                             bt_ld<unsigned short>(smem, base + 2 * PIXB),
-                                             bt_ld<unsigned short>(smem, base + 3 * PIXB));
-                    dQt[mt] = mma16(kt, dsb, dQt[mt]);
+                    const f32x4 kc = Frag<D>::mma(kf, selk[mt], f32x4{0.f, 0.f, 0.f, 0.f});
+                    dQt[mt] = mma16(bf16x4_of(kc[0], kc[1], kc[2], kc[3]), dsb, dQt[mt]);
                 }
             }
             // this tile's column sums (lane g writes column 4ct + g)
