@@ -80,6 +80,9 @@ SMALL = [
     (1, 2, 64, 64, 32, 32, 3, 1),   # r = 38 at d = 32 (streaming kernel)
     (1, 1, 40, 44, 32, 8, 13, 1),   # r = 34 at d = 32, ragged
     (1, 1, 24, 40, 32, 12, 14, 2),  # r = 40 at d = 32, strided
+    (1, 2, 40, 44, 32, 12, 3, 1),   # 18x18 window (4x4 key patches), ragged last block row and column
+    (1, 2, 48, 40, 32, 16, 2, 1),   # 20x20 window, block 16
+    (1, 2, 48, 48, 32, 12, 4, 2),   # 20x20 window, strided
 ]
 
 
