@@ -19,6 +19,10 @@ reads HBM.  Prints ONE JSON line (rank 0):
              when the flops take longer at the published peaks, the dense
              matrix peak of the dtype; mean launch time measured with HIP
              events on the launch stream
+  launch_stats  after the timed region: median, p10 and p90 of single
+             launches (events between consecutive launches, sets rotating)
+             and the mean over as many launches on one input set ("warm":
+             a set that fits the Infinity Cache is read from there)
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
              workload on this host (reported, not a target)
 
@@ -436,7 +440,8 @@ def main():
         e = run_op(args, workloads.get(name), args.per_config_steps, args.per_config_steps,
                    min(5.0, args.cpu_seconds))
         per_config[name] = {k_: e[k_] for k_ in ("value", "unit", "ms_per_step", "tokens_per_s", "dtype", "steps",
-                                                  "warmup", "roofline", "cpu_baseline", "config") if k_ in e}
+                                                  "warmup", "roofline", "launch_stats", "cpu_baseline", "config")
+                             if k_ in e}
         torch.cuda.empty_cache()
     line = run_op(args, workloads.get(workloads.BENCH_WORKLOAD), args.steps, args.warmup, args.cpu_seconds)
     line["per_config"] = per_config
@@ -534,6 +539,28 @@ def run_op(args, wl, steps, warmup, cpu_seconds):
     wall = time.perf_counter() - t0
     gpu_ms = ev0.elapsed_time(ev1)
     ms = gpu_ms / steps
+
+    # Spread of single launches (outside the timed region above): a chain of
+    # events between consecutive launches on the same stream, the input sets
+    # rotating as above; then `steps` launches on input set 0 alone ("warm":
+    # when a set fits the 256 MB Infinity Cache, its reads hit there).
+    nsamp = max(1, min(steps, 200))
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nsamp + 1)]
+    evs[0].record(stream)
+    for i in range(nsamp):
+        step(i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_launch = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(nsamp))
+    pick = lambda f: per_launch[min(nsamp - 1, int(f * (nsamp - 1) + 0.5))]
+    ev0.record(stream)
+    for i in range(steps):
+        step(0)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    launch_stats = {"median_us": round(pick(0.5), 3), "p10_us": round(pick(0.1), 3),
+                    "p90_us": round(pick(0.9), 3), "samples": nsamp,
+                    "warm_mean_us": round(ev0.elapsed_time(ev1) * 1e3 / steps, 3)}
     flops = bwd_flops(wl) if bwd else wl.flops
     alg_bytes = bwd_alg_bytes(wl) if bwd else wl.alg_bytes
     tflops = flops / (ms * 1e-3) / 1e12
@@ -584,6 +611,7 @@ def run_op(args, wl, steps, warmup, cpu_seconds):
             "mean_launch_us": round(ms * 1e3, 3),
             "kernel_sources": src_hash,
         },
+        "launch_stats": launch_stats,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, inputs0_cpu, cpu_seconds, dout0_cpu)
