@@ -19,6 +19,8 @@ reads HBM.  Prints ONE JSON line (rank 0):
              when the flops take longer at the published peaks, the dense
              matrix peak of the dtype; mean launch time measured with HIP
              events on the launch stream
+  achievable_hbm  the same achieved rate over a plain device copy's
+             measured rate (context beside the spec peak)
   launch_stats  after the timed region: median, p10 and p90 of single
              launches (events between consecutive launches, sets rotating)
              and the mean over as many launches on one input set ("warm":
@@ -180,6 +182,38 @@ def copy_calibration(mib, steps):
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration": {"bytes_read_per_copy": n, "bytes_written_per_copy": n,
                                            "copies": steps}}), flush=True)
+
+
+def copy_bandwidth_gbs(mib=512, reps=10):
+    """Achievable HBM bandwidth as context for the spec peak: a plain device
+    copy (torch copy_) of `mib` MiB, event-timed over `reps` copies after two
+    untimed ones; bytes = read + written."""
+    import torch
+    n = mib * 2 ** 20
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    ev1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * n * reps / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbs
+
+
+def with_copy_context(e, copy_gbs):
+    """Add the achieved HBM rate as a fraction of the measured copy rate."""
+    r = e.get("roofline", {})
+    if r.get("bound") == "hbm":
+        e["achievable_hbm"] = {"copy_gbs": round(copy_gbs, 1), "frac_of_copy": round(r["achieved"] / copy_gbs, 4),
+                               "what": "torch copy_ of 512 MiB on the same GPU, read + written bytes"}
+    return e
 
 
 def bwd_flops(wl):
@@ -444,6 +478,10 @@ def main():
                              if k_ in e}
         torch.cuda.empty_cache()
     line = run_op(args, workloads.get(workloads.BENCH_WORKLOAD), args.steps, args.warmup, args.cpu_seconds)
+    copy_gbs = copy_bandwidth_gbs()
+    with_copy_context(line, copy_gbs)
+    for e in per_config.values():
+        with_copy_context(e, copy_gbs)
     line["per_config"] = per_config
     print(json.dumps(line), flush=True)
 
