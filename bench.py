@@ -145,6 +145,8 @@ def kernel_source_hash(which: str = "fwd") -> str:
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--issue-rates", action="store_true",
+                    help="time the library's issue-rate probe (FMA, exp2, MFMA, mixed waves) instead")
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=2000,
                     help="untimed launches first (the GPU clocks need ~0.1 s of load to ramp up)")
@@ -182,6 +184,56 @@ def copy_calibration(mib, steps):
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration": {"bytes_read_per_copy": n, "bytes_written_per_copy": n,
                                            "copies": steps}}), flush=True)
+
+
+def issue_rates(iters=8000):
+    """Per-SIMD issue rates of the instruction kinds the attention kernels
+    are made of, from the library's probe kernel (halo_attn_probe_issue):
+    each mode's launch is timed with HIP events (10 launches after 3), the
+    rate is wave-instructions per SIMD per second, also given as SIMD cycles
+    per wave-instruction at the 2.4 GHz spec clock.  The mixed modes put two
+    instruction kinds in the two halves of every workgroup (waves sharing a
+    SIMD): their time is compared with the sum and the maximum of the two
+    halves' times alone."""
+    import torch
+    from blocked_local_self_amd import _native
+    lib = _native.load()
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    simds = 4 * cus
+    wgs = 4 * cus
+    waves = 8 * wgs
+    out = torch.empty(wgs * 512, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def launch_ms(mode):
+        for _ in range(3):
+            _native.check(lib.halo_attn_probe_issue(mode, iters, wgs, out.data_ptr(), stream.cuda_stream))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(10):
+            lib.halo_attn_probe_issue(mode, iters, wgs, out.data_ptr(), stream.cuda_stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 10
+
+    t = {m: launch_ms(m) for m in range(6)}
+    per_wave = {0: 8 * iters, 1: 8 * iters, 2: 4 * iters, 3: 4 * iters}
+    kinds = {0: "fma_f32", 1: "exp2_f32", 2: "mfma_16x16x32_bf16", 3: "mfma_32x32x16_bf16"}
+    res = {"simds": simds, "waves": waves, "iters": iters}
+    for m, name in kinds.items():
+        per_simd = waves * per_wave[m] / simds
+        rate = per_simd / (t[m] * 1e-3)
+        res[name] = {"launch_ms": round(t[m], 4), "wave_instr_per_simd_per_s": round(rate, 1),
+                     "cycles_per_wave_instr_at_2.4GHz": round(2.4e9 / rate, 2)}
+    res["mfma_16x16x32_bf16"]["tflops"] = round(waves * per_wave[2] * 16384 / (t[2] * 1e-3) / 1e12, 1)
+    res["mfma_32x32x16_bf16"]["tflops"] = round(waves * per_wave[3] * 32768 / (t[3] * 1e-3) / 1e12, 1)
+    res["exp_over_fma_time"] = round(t[1] / t[0], 3)
+    for m, (a, b, name) in {4: (1, 2, "exp_with_mfma_16x16x32"), 5: (1, 0, "exp_with_fma")}.items():
+        res[name] = {"launch_ms": round(t[m], 4), "sum_of_halves_ms": round((t[a] + t[b]) / 2, 4),
+                     "max_of_halves_ms": round(max(t[a], t[b]) / 2, 4)}
+    print(json.dumps({"issue_rates": res}), flush=True)
 
 
 def copy_bandwidth_gbs(mib=512, reps=10):
@@ -454,6 +506,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, args.steps)
+        return
+    if args.issue_rates:
+        issue_rates()
         return
     if args.which == "layer":
         run_layer(args)

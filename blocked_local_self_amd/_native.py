@@ -74,6 +74,8 @@ def load() -> ctypes.CDLL:
     lib.halo_attn_layer_fwd_ex.restype = i
     lib.halo_attn_layer_kernel_name.argtypes = [i] * 13
     lib.halo_attn_layer_kernel_name.restype = ctypes.c_char_p
+    lib.halo_attn_probe_issue.argtypes = [i, i, i, vp, vp]
+    lib.halo_attn_probe_issue.restype = i
     lib.halo_attn_fwd_kernel_name.argtypes = [i] * 11
     lib.halo_attn_fwd_kernel_name.restype = ctypes.c_char_p
     lib.halo_attn_bwd_kernel_name.argtypes = [i] * 11

@@ -435,6 +435,21 @@ int halo_attn_abi_version(void);
  * owned by the library. */
 const char* halo_attn_build_id(void);
 
+/* Measurement aid, not part of the attention path: launches `workgroups`
+ * workgroups of 8 waves on `stream`, every lane running independent chains
+ * of one instruction kind `iters` times, so a launch's duration gives the
+ * rate at which a SIMD issues that kind.  mode: 0 fp32 FMA (8 chains per
+ * lane), 1 exp2 (v_exp_f32, 8 chains), 2 bf16 MFMA 16x16x32 (4 accumulators
+ * per wave), 3 bf16 MFMA 32x32x16 (4 accumulators), 4 waves 0-3 as mode 1
+ * and waves 4-7 as mode 2 (two waves of one SIMD doing different kinds),
+ * 5 waves 0-3 as mode 1 and 4-7 as mode 0.  out: device buffer of
+ * workgroups * 512 floats, overwritten with values that keep the chains
+ * live (meaningless otherwise).  Returns HALO_ERR_SHAPE for a mode outside
+ * 0..5 or non-positive counts, HALO_ERR_NULL for a null out, HALO_ERR_HIP
+ * when the launch fails; asynchronous otherwise.  bench.py --issue-rates
+ * times it. */
+int halo_attn_probe_issue(int mode, int iters, int workgroups, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
