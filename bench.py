@@ -520,19 +520,24 @@ def main():
                                              else workloads.BENCH_WORKLOAD))
         print(json.dumps(run_op(args, wl, args.steps, args.warmup, args.cpu_seconds)), flush=True)
         return
-    # the forward headline: every HaloNet-stage shape first (each with its
-    # own warm-up), then the headline shape with the requested steps
+    # the forward headline: the inputs of every HaloNet-stage shape are put
+    # on the GPU first; then each stage shape is timed (with its own
+    # warm-up) and the headline shape last with the requested steps, back to
+    # back; the CPU baselines follow once the GPU work is done
+    names = [n for n in workloads.STAGE_WORKLOADS if n != workloads.BENCH_WORKLOAD]
+    prepared = {n: prepare_op(args, workloads.get(n)) for n in names + [workloads.BENCH_WORKLOAD]}
     per_config = {}
-    for name in workloads.STAGE_WORKLOADS:
-        if name == workloads.BENCH_WORKLOAD:
-            continue
-        e = run_op(args, workloads.get(name), args.per_config_steps, args.per_config_steps,
-                   min(5.0, args.cpu_seconds))
+    for name in names:
+        e = prepared[name][0](args.per_config_steps, args.per_config_steps)
         per_config[name] = {k_: e[k_] for k_ in ("value", "unit", "ms_per_step", "tokens_per_s", "dtype", "steps",
-                                                  "warmup", "roofline", "launch_stats", "cpu_baseline", "config")
-                             if k_ in e}
-        torch.cuda.empty_cache()
-    line = run_op(args, workloads.get(workloads.BENCH_WORKLOAD), args.steps, args.warmup, args.cpu_seconds)
+                                                  "warmup", "roofline", "launch_stats", "config")}
+    line = prepared[workloads.BENCH_WORKLOAD][0](args.steps, args.warmup)
+    if not args.no_cpu_baseline:
+        for name in names:
+            per_config[name]["cpu_baseline"] = prepared[name][1](min(5.0, args.cpu_seconds))
+        line["cpu_baseline"] = prepared[workloads.BENCH_WORKLOAD][1](args.cpu_seconds)
+    prepared.clear()
+    torch.cuda.empty_cache()
     copy_gbs = copy_bandwidth_gbs()
     with_copy_context(line, copy_gbs)
     for e in per_config.values():
@@ -544,6 +549,19 @@ def main():
 def run_op(args, wl, steps, warmup, cpu_seconds):
     """Time `steps` launches of the forward (or backward) on workload wl after
     `warmup` untimed ones; returns the JSON line's fields."""
+    measure, cpu_job = prepare_op(args, wl)
+    line = measure(steps, warmup)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_job(cpu_seconds)
+    return line
+
+
+def prepare_op(args, wl):
+    """Inputs of workload wl resident on the GPU and the launch arguments;
+    returns (measure(steps, warmup) -> the JSON line's fields without the
+    CPU baseline, cpu_job(seconds) -> the CPU baseline), so that several
+    workloads can be prepared first and timed back to back (the GPU then
+    stays busy, and its clocks up, from one timed region to the next)."""
     import torch
     from blocked_local_self_amd import halo_attn_fwd, halo_attn_bwd, bwd_workspace_bytes, workloads
     from blocked_local_self_amd.inputs import make_workload_inputs, make_grad_output
@@ -618,6 +636,18 @@ def run_op(args, wl, steps, warmup, cpu_seconds):
         if st:
             _native.check(st)
 
+    def measure(steps, warmup):
+        return _measure(args, wl, step, stream, nsets, lib, dcode, flags, variants, bwd, steps, warmup)
+
+    def cpu_job(seconds):
+        return cpu_baseline(wl, inputs0_cpu, seconds, dout0_cpu)
+
+    return measure, cpu_job
+
+
+def _measure(args, wl, step, stream, nsets, lib, dcode, flags, variants, bwd, steps, warmup):
+    import torch
+    from blocked_local_self_amd import _native, KERNELS
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -706,8 +736,6 @@ def run_op(args, wl, steps, warmup, cpu_seconds):
         },
         "launch_stats": launch_stats,
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, inputs0_cpu, cpu_seconds, dout0_cpu)
     return line
 
 
