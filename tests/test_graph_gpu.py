@@ -1,0 +1,57 @@
+"""The forward inside a captured HIP graph (torch.cuda.CUDAGraph): it
+allocates nothing, records no memset and synchronises nothing, so a serving
+loop can capture it once and replay it.  Each replay is compared bitwise
+with the eager result (the kernels are deterministic), with eager work and a
+device synchronisation between the replays, and a replay after the inputs
+change in place must give the new inputs' result."""
+import pytest
+import torch
+
+from blocked_local_self_amd import halo_attn_fwd, _native
+from blocked_local_self_amd.inputs import make_inputs
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [
+    # (B, heads, H, W, d, block, halo, stride, dtype)
+    (2, 3, 24, 24, 16, 8, 3, 1, "bf16"),     # 32-query groups of the ring kernel
+    (1, 2, 36, 36, 32, 12, 3, 1, "bf16"),    # 18x18 window: 4x4-patch tile kernel
+    (2, 2, 24, 24, 16, 8, 3, 2, "bf16"),     # strided queries
+    (1, 2, 64, 64, 16, 32, 3, 1, "bf16"),    # 38x38 window: streaming kernel
+    (1, 2, 16, 16, 16, 4, 1, 1, "fp32"),     # generic kernel
+]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    _native.load()
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_forward_replays_in_a_graph(shape):
+    B, heads, H, W, d, block, halo, stride, dtype = shape
+    print(f"graph case {shape}", flush=True)
+    dev = torch.device("cuda:0")
+    q, k, v, rh, rw = (t.to(dev) for t in make_inputs(B, heads, H, W, d, block, halo, dtype=dtype, seed=11))
+    q2 = make_inputs(B, heads, H, W, d, block, halo, dtype=dtype, seed=12)[0].to(dev)
+    eager = halo_attn_fwd(q, k, v, rh, rw, block, halo, stride)
+    eager2 = halo_attn_fwd(q2, k, v, rh, rw, block, halo, stride)
+    torch.cuda.synchronize()
+
+    out = torch.empty_like(eager)
+    qin = q.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        halo_attn_fwd(qin, k, v, rh, rw, block, halo, stride, out=out)
+    for _ in range(3):
+        out.fill_(float("nan"))                 # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+    qin.copy_(q2)
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out, eager2)
