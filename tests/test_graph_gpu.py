@@ -55,3 +55,41 @@ def test_forward_replays_in_a_graph(shape):
     graph.replay()
     torch.cuda.synchronize()
     assert torch.equal(out, eager2)
+
+
+BWD_SHAPES = [
+    (2, 3, 24, 24, 16, 8, 3, 1),     # column-walk (strip) backward
+    (1, 2, 36, 36, 32, 12, 3, 1),    # 16-query tile backward (18x18 window)
+]
+
+
+@pytest.mark.parametrize("shape", BWD_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_backward_replays_in_a_graph(shape):
+    # with the workspace and the gradients passed in, the backward allocates
+    # nothing either; its sums run in a fixed order, so replays are bitwise
+    from blocked_local_self_amd import halo_attn_bwd, bwd_workspace_bytes
+    from blocked_local_self_amd.inputs import make_grad_output
+    B, heads, H, W, d, block, halo, stride = shape
+    print(f"graph backward case {shape}", flush=True)
+    dev = torch.device("cuda:0")
+    q, k, v, rh, rw = (t.to(dev) for t in make_inputs(B, heads, H, W, d, block, halo, dtype="bf16", seed=13))
+    g = make_grad_output(B, heads, H // stride, W // stride, d, dtype="bf16", seed=14).to(dev)
+    out, lse = halo_attn_fwd(q, k, v, rh, rw, block, halo, stride, return_lse=True)
+    need = bwd_workspace_bytes(B, heads, H, W, d, block, halo, stride, "bf16")
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    eager = halo_attn_bwd(q, k, v, rh, rw, g, block, halo, stride, out=out, lse=lse, workspace=ws)
+    eager = tuple(t.clone() for t in eager)
+    torch.cuda.synchronize()
+
+    grads = tuple(torch.empty_like(t) for t in eager)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        halo_attn_bwd(q, k, v, rh, rw, g, block, halo, stride, out=out, lse=lse, workspace=ws, grads=grads)
+    for _ in range(3):
+        for t in grads:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(grads, eager):
+            assert torch.equal(got, want)
