@@ -93,3 +93,30 @@ def test_backward_replays_in_a_graph(shape):
         torch.cuda.synchronize()
         for got, want in zip(grads, eager):
             assert torch.equal(got, want)
+
+
+@pytest.mark.parametrize("kernel", ["split", "fused"])
+def test_layer_replays_in_a_graph(kernel):
+    # the whole layer (projections, attention, to_out) with its workspace
+    # passed in: the split path's three kernels, or the one-kernel path
+    from blocked_local_self_amd import halo_layer_fwd, layer_workspace_bytes
+    from blocked_local_self_amd.inputs import make_layer_inputs
+    B, H, W, heads, d, block, halo = 2, 32, 32, 4, 16, 8, 3
+    C = heads * d
+    print(f"graph layer case {kernel}", flush=True)
+    dev = torch.device("cuda:0")
+    x, w_q, w_kv, w_o, b_o, rh, rw = (t.to(dev) for t in make_layer_inputs(B, H, W, C, heads, d, block, halo,
+                                                                          dtype="bf16", seed=15))
+    ws = torch.empty(max(layer_workspace_bytes(B, H, W, heads, d), 16), dtype=torch.uint8, device=dev)
+    eager = halo_layer_fwd(x, w_q, w_kv, w_o, b_o, rh, rw, block, halo, heads, workspace=ws, kernel=kernel)
+    torch.cuda.synchronize()
+    out = torch.empty_like(eager)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        halo_layer_fwd(x, w_q, w_kv, w_o, b_o, rh, rw, block, halo, heads, workspace=ws, out=out, kernel=kernel)
+    for _ in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
