@@ -345,6 +345,28 @@ def test_deterministic_and_stream_aware():
     assert torch.equal(a, b)
 
 
+def test_concurrent_streams():
+    # two kernel families on two streams at once, several calls each: the
+    # library keeps no state between forward calls, so each result equals
+    # its eager one
+    say("concurrent streams: ring and tile kernels")
+    a_in = [t.to(DEV) for t in make_inputs(4, 4, 48, 48, 16, 8, 3, "bf16", seed=21)]
+    b_in = [t.to(DEV) for t in make_inputs(2, 4, 48, 48, 32, 12, 3, "bf16", seed=22)]
+    want_a = halo_attn_fwd(*a_in, 8, 3)
+    want_b = halo_attn_fwd(*b_in, 12, 3)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs_a, outs_b = [], []
+    for _ in range(4):
+        with torch.cuda.stream(s1):
+            outs_a.append(halo_attn_fwd(*a_in, 8, 3))
+        with torch.cuda.stream(s2):
+            outs_b.append(halo_attn_fwd(*b_in, 12, 3))
+    torch.cuda.synchronize()
+    assert all(torch.equal(o, want_a) for o in outs_a)
+    assert all(torch.equal(o, want_b) for o in outs_b)
+
+
 @pytest.mark.parametrize("name", ["early_stage_bf16_64x64_d16_b8h3", "mid_stage_bf16_32x32_d32_b8h3"])
 def test_full_workload_is_bitwise_reproducible(name):
     # many workgroups in flight: results must not depend on wave timing
