@@ -276,10 +276,13 @@ int fwd_choice(const halo::Geometry& g, bool bf16, int kernel, int& mode)
     if (forced && !mfma_ok)
         return fail(HALO_ERR_UNSUPPORTED,
                     "matrix-core kernel needs bf16, block %% 4 == 0, d in {16,32} with window side <= 40 "
-                    "(variants: <= 32) (got bf16=%d d=%d block=%d r=%d flags=%d)",
+                    "(variants: <= 32) or d = 64 with window side <= 32 (no variants) "
+                    "(got bf16=%d d=%d block=%d r=%d flags=%d)",
                     (int)bf16, g.d, g.block, g.r, g.flags);
     if (kernel == HALO_KERNEL_MFMA_STRIP && g.flags)
         return fail(HALO_ERR_UNSUPPORTED, "the strip kernel runs the default semantics only (flags=%d)", g.flags);
+    if (kernel == HALO_KERNEL_MFMA_STRIP && g.d == 64)
+        return fail(HALO_ERR_UNSUPPORTED, "the strip kernel takes d = 16 and 32 only (d=%d)", g.d);
     if (kernel == HALO_KERNEL_MFMA_STRIP && g.d == 32 && g.r > 32)
         return fail(HALO_ERR_UNSUPPORTED, "the strip kernel takes windows of up to 32 columns at d = 32 (r=%d)", g.r);
     const bool use_mfma = forced || (kernel == HALO_KERNEL_AUTO && mfma_ok);

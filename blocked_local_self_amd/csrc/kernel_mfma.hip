@@ -382,7 +382,7 @@ static MfmaPlan make_plan(const Geometry& g, int nch, int qt, int nbx, int waves
 bool mfma_supported(int d, int r, int block, int stride, bool bf16)
 {
     (void)stride;
-    return bf16 && block % 4 == 0 && (d == 16 || d == 32) && r <= 40;
+    return bf16 && block % 4 == 0 && ((d == 16 || d == 32) && r <= 40 || d == 64 && r <= 32);
 }
 
 // Largest dynamic LDS one workgroup may use on the current device.
@@ -489,6 +489,7 @@ hipError_t launch_mfma(const void* q, const void* k, const void* v, const void* 
     case MfmaKernel::strip: break;
     }
     const bool wide = g.r > 16;
+    if (g.d == 64) return hipErrorInvalidValue;                // 64 channels run on the streaming kernel only
     if (g.d == 32 && g.r > 32) return hipErrorInvalidValue;   // the strip kernel holds 32 columns at d = 32
     if (g.d == 16 && g.r > 32) return launch_dn<16, 3>(q, k, v, rh, rw, out, lse, g, st);
     if (g.d == 16) return wide ? launch_dn<16, 2>(q, k, v, rh, rw, out, lse, g, st)

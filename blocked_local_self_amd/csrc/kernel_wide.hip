@@ -1,5 +1,6 @@
-// Halo attention for windows wider than 32 columns (gfx950 matrix cores,
-// bf16 in, fp32 accumulate): the detection setting of "Scaling Local
+// Halo attention for windows wider than 32 columns, and for 64-channel
+// heads at any window of up to 32 columns (gfx950 matrix cores, bf16 in,
+// fp32 accumulate): the detection setting of "Scaling Local
 // Self-Attention for Parameter Efficient Visual Backbones", section 4.6
 // (block 32, halo 3: 38x38 windows), with the method of section 2.2
 // (Figures 1 and 2) and the relative logits of section 2.1 / appendix A as
@@ -41,6 +42,24 @@ namespace halo {
 constexpr int kWideWaves = HALO_WIDE_WAVES;
 constexpr int kWideRows = HALO_WIDE_ROWS;   // window rows per LDS chunk
 
+// QK^T operands of this kernel: those of the other kernels for 16 and 32
+// channels; for 64, a lane holds 16 consecutive channels (quarter gq of the
+// head) and the contraction is two K = 32 MFMAs over its two halves.  Both
+// operands use the same lane -> channel map, so the sum runs over exactly the
+// d channels.
+typedef short s16x16 __attribute__((ext_vector_type(16)));
+template <int D> struct WFrag : Frag<D> {};
+template <> struct WFrag<64> {
+    typedef s16x16 T;
+    __device__ static inline f32x4 mma(T a, T b, f32x4 c) {
+        const s16x8 a0 = __builtin_shufflevector(a, a, 0, 1, 2, 3, 4, 5, 6, 7);
+        const s16x8 a1 = __builtin_shufflevector(a, a, 8, 9, 10, 11, 12, 13, 14, 15);
+        const s16x8 b0 = __builtin_shufflevector(b, b, 0, 1, 2, 3, 4, 5, 6, 7);
+        const s16x8 b1 = __builtin_shufflevector(b, b, 8, 9, 10, 11, 12, 13, 14, 15);
+        return mma_k32(a1, b1, mma_k32(a0, b0, c));
+    }
+};
+
 struct WidePlan {
     int groups;       // workgroups per block
     int SW;           // LDS row pitch in columns (16 * NCH)
@@ -61,7 +80,7 @@ void wide_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 {
     constexpr int KPL = D / 4;
     constexpr int CPP = D / 8;                // 16-byte chunks per pixel
-    typedef typename Frag<D>::T FragT;
+    typedef typename WFrag<D>::T FragT;
     extern __shared__ __align__(16) unsigned char smem[];
     __bf16* Kc = reinterpret_cast<__bf16*>(smem);                  // [kWideRows][SW][D]
     __bf16* Vc = reinterpret_cast<__bf16*>(smem + p.off_v);        // [D][kWideRows][SW]
@@ -142,7 +161,7 @@ void wide_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 const __bf16* tab = pass == 0 ? Rw : Rh;
                 for (int rt = 0; rt < rp16; ++rt) {
                     const FragT a = *reinterpret_cast<const FragT*>(tab + (rt * 16 + n) * D + gq * KPL);
-                    const f32x4 gr = Frag<D>::mma(a, qf[u], f32x4{0.f, 0.f, 0.f, 0.f});
+                    const f32x4 gr = WFrag<D>::mma(a, qf[u], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
                     for (int i = 0; i < 4; ++i) scr[(rt * 16 + gq * 4 + i) * 16 + n] = gr[i];
                 }
@@ -253,8 +272,8 @@ void wide_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                     float mx0 = -3.0e38f, mx1 = -3.0e38f;
 #pragma unroll
                     for (int ch = 0; ch < NCH; ++ch) {
-                        s[0][ch] = Frag<D>::mma(a[0][ch], qf[u], cinit[u][ch]);
-                        s[1][ch] = Frag<D>::mma(a[1][ch], qf[u], cinit[u][ch]);
+                        s[0][ch] = WFrag<D>::mma(a[0][ch], qf[u], cinit[u][ch]);
+                        s[1][ch] = WFrag<D>::mma(a[1][ch], qf[u], cinit[u][ch]);
                         mx0 = fmaxf(mx0, max4(s[0][ch]));
                         mx1 = fmaxf(mx1, max4(s[1][ch]));
                     }
@@ -318,10 +337,15 @@ void wide_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 static int wround(int x, int m) { return (x + m - 1) / m * m; }
 
 // Windows of 33..48 columns (three 16-column chunks) for d = 16 and 32
-// (two chunk buffers of 14 rows x 48 columns: 43 KB each at d = 32).
+// (two chunk buffers of 14 rows x 48 columns: 43 KB each at d = 32), and
+// every window of up to 32 columns (one or two chunks) for d = 64, which
+// the other matrix-core kernels do not take (two buffers of 14 rows x 32
+// columns x 64 channels: 57 KB each).
 bool wide_supported(const Geometry& g, bool bf16)
 {
-    return bf16 && (g.d == 16 || g.d == 32) && g.r > 32 && g.r <= 48 && g.block % 4 == 0;
+    if (!bf16 || g.block % 4 != 0) return false;
+    if (g.d == 64) return g.r <= 32;
+    return (g.d == 16 || g.d == 32) && g.r > 32 && g.r <= 48;
 }
 
 template <int D, int NCH, int QT>
@@ -357,6 +381,8 @@ static hipError_t wide_t(const void* q, const void* k, const void* v, const void
 hipError_t launch_wide(const void* q, const void* k, const void* v, const void* rh, const void* rw, void* out,
                        float* lse, const Geometry& g, hipStream_t st)
 {
+    if (g.d == 64) return g.r <= 16 ? wide_t<64, 1, HALO_WIDE_QT>(q, k, v, rh, rw, out, lse, g, st)
+                                    : wide_t<64, 2, HALO_WIDE_QT>(q, k, v, rh, rw, out, lse, g, st);
     if (g.d == 32) return wide_t<32, 3, HALO_WIDE_QT>(q, k, v, rh, rw, out, lse, g, st);
     return wide_t<16, 3, HALO_WIDE_QT>(q, k, v, rh, rw, out, lse, g, st);
 }

@@ -59,14 +59,16 @@ typedef enum halo_dtype {
 
 /* Which implementation runs.  AUTO picks the fastest one that supports the
  * arguments.  GENERIC is the fp32-vector kernel for every supported shape.
- * MFMA is the fused matrix-core path: bf16, block % 4 == 0, d in {16, 32}
- * and window side r <= 40 (r <= 32 for the semantic variants).  Inside
- * it the forward picks, by shape: a persistent kernel of 16-query groups
- * (d in {16, 32} with r <= 16, d == 32 with r <= 20; default semantics); a
- * persistent kernel that walks each image down its block rows with the
- * window rows in an LDS ring (r <= 32, and every semantic variant); a
- * streaming kernel for windows of 33..40 columns; or a kernel that stages
- * each strip of blocks separately (d == 16, or d == 32 with r <= 32).
+ * MFMA is the fused matrix-core path: bf16, block % 4 == 0, and d in
+ * {16, 32} with window side r <= 40 (r <= 32 for the semantic variants) or
+ * d == 64 with r <= 32 (default semantics).  Inside it the forward picks,
+ * by shape: a persistent kernel of 16-query groups (d in {16, 32} with
+ * r <= 16, d == 32 with r <= 20; default semantics); a persistent kernel
+ * that walks each image down its block rows with the window rows in an LDS
+ * ring (d in {16, 32}, r <= 32, and every semantic variant); a streaming
+ * kernel for windows of 33..40 columns and for d == 64; or a kernel that
+ * stages each strip of blocks separately (d == 16, or d == 32 with
+ * r <= 32).  The backward of d == 64 runs on the generic kernels.
  * MFMA_STRIP forces the last one and MFMA_RING the ring kernel where it
  * applies (for cross-checking; the
  * backward treats both as MFMA).  Asking for a matrix-core path with other

@@ -64,7 +64,9 @@ def call(lib, *, q=1, k=1, v=1, rh=1, rw=1, out=1 << 40, B=1, heads=1, H=8, W=8,
     (dict(stride=0), -2), (dict(stride=3, block=4), -2), (dict(stride=2, H=9), -2),
     (dict(B=-1), -2), (dict(W=-3), -2), (dict(kernel=9), -2),
     (dict(block=200, halo=30), -2), (dict(scale=float("inf")), -2), (dict(scale=float("nan")), -2),
-    (dict(kernel=2, dtype=0), -4), (dict(kernel=2, d=64), -4), (dict(kernel=2, block=6), -4),
+    (dict(kernel=2, dtype=0), -4), (dict(kernel=2, d=48), -4), (dict(kernel=2, block=6), -4),
+    (dict(kernel=2, d=64, block=8, halo=13), -4),          # d = 64 takes windows of up to 32 columns
+    (dict(kernel=3, d=64), -4),                            # the strip kernel takes d = 16 and 32 only
     (dict(kernel=2, block=8, halo=17), -4), (dict(kernel=2, block=8, halo=17, d=32), -4),
     (dict(kernel=3, block=8, halo=13, d=32), -4),          # the strip kernel holds 32 columns at d = 32
     (dict(B=1 << 30, heads=1 << 30, H=1 << 15, W=1 << 15), -2),
@@ -94,7 +96,9 @@ def test_kernel_selection():
     assert select_kernel(16, 8, 3, 2, "bf16") == "mfma"
     assert select_kernel(32, 12, 3, 1, "bf16") == "mfma"
     assert select_kernel(16, 4, 1, 1, "fp32") == "generic"
-    assert select_kernel(64, 8, 3, 1, "bf16") == "generic"
+    assert select_kernel(64, 8, 3, 1, "bf16") == "mfma"        # 64 channels: the streaming kernel
+    assert select_kernel(64, 8, 13, 1, "bf16") == "generic"    # ... for windows of up to 32 columns
+    assert select_kernel(48, 8, 3, 1, "bf16") == "generic"
     assert select_kernel(16, 2, 1, 1, "bf16") == "generic"
     assert select_kernel(16, 8, 13, 1, "bf16") == "mfma"      # r = 34: three column chunks (d = 16)
     assert select_kernel(32, 8, 13, 1, "bf16") == "mfma"      # r = 34 with d = 32: the streaming kernel
@@ -110,6 +114,7 @@ def test_kernel_name_query_on_the_host():
     assert _native.fwd_kernel_name(1, 2, 16, 16, 16, 4, 1, 1, _native.HALO_BF16,
                                    kernel=_native.HALO_KERNEL_GENERIC) == "generic"
     assert _native.fwd_kernel_name(0, 2, 16, 16, 16, 4, 1, 1, _native.HALO_BF16) == "none"
+    assert _native.fwd_kernel_name(1, 2, 24, 24, 64, 8, 3, 1, _native.HALO_BF16) == "wide"     # d = 64
     with pytest.raises(ValueError, match="query_stride"):
         _native.fwd_kernel_name(1, 2, 16, 16, 16, 4, 1, 3, _native.HALO_BF16)
     with pytest.raises(ValueError, match="matrix-core"):

@@ -83,7 +83,17 @@ SMALL = [
     (1, 2, 40, 44, 32, 12, 3, 1),   # 18x18 window (4x4 key patches), ragged last block row and column
     (1, 2, 48, 40, 32, 16, 2, 1),   # 20x20 window, block 16
     (1, 2, 48, 48, 32, 12, 4, 2),   # 20x20 window, strided
+    (1, 2, 24, 24, 64, 8, 3, 1),    # d = 64 (streaming kernel, one column chunk)
+    (1, 2, 36, 36, 64, 12, 3, 1),   # d = 64, 18x18 window (two column chunks)
+    (1, 1, 20, 28, 64, 8, 3, 1),    # d = 64, ragged
+    (2, 2, 24, 24, 64, 8, 3, 2),    # d = 64, strided
 ]
+
+
+def mfma_shape(s):
+    # shapes the matrix-core path takes (bf16)
+    d, block, r = s[4], s[5], s[5] + 2 * s[6]
+    return block % 4 == 0 and (d in (16, 32) or (d == 64 and r <= 32))
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
@@ -168,8 +178,7 @@ def test_lse_full_workload(name):
     assert np.abs(have - want).max() <= LSE_TOL["bf16"]
 
 
-@pytest.mark.parametrize("shape", [s for s in SMALL if s[4] in (16, 32) and s[5] % 4 == 0],
-                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("shape", [s for s in SMALL if mfma_shape(s)], ids=lambda s: "x".join(map(str, s)))
 def test_matrix_core_kernel_matches_oracle(shape):
     B, heads, H, W, d, block, halo, stride = shape
     say(f"mfma case {shape}")
@@ -343,6 +352,23 @@ def test_deterministic_and_stream_aware():
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_d64_every_slice_matches_generic():
+    # 64-channel heads at a size with many workgroups: every slice against the
+    # independent fp32 vector kernel, sampled slices against the oracle
+    B, heads, H, W, d, block, halo = 4, 4, 64, 64, 64, 8, 3
+    say("d = 64, 4 x 4 heads 64x64: streaming kernel vs generic and oracle")
+    inp = make_inputs(B, heads, H, W, d, block, halo, dtype="bf16", seed=31)
+    a = f64(run(inp, block, halo, 1, "generic"))
+    b = f64(run(inp, block, halo, 1, "auto"))
+    assert np.abs(a - b).max() <= TOL["bf16"]
+    q, k, v, rh, rw = inp
+    slices = [(0, 0), (1, 3), (3, 3)]
+    pick = lambda t: np.stack([f64(t[n, hd]) for n, hd in slices])[:, None]
+    want = oracle.halo_attn_ref(pick(q), pick(k), pick(v), f64(rh), f64(rw), block, halo, 1)
+    have = np.stack([b[n, hd] for n, hd in slices])[:, None]
+    assert np.abs(have - want).max() <= TOL["bf16"]
 
 
 def test_concurrent_streams():
