@@ -381,8 +381,17 @@ static hipError_t wide_t(const void* q, const void* k, const void* v, const void
 hipError_t launch_wide(const void* q, const void* k, const void* v, const void* rh, const void* rw, void* out,
                        float* lse, const Geometry& g, hipStream_t st)
 {
-    if (g.d == 64) return g.r <= 16 ? wide_t<64, 1, HALO_WIDE_QT>(q, k, v, rh, rw, out, lse, g, st)
-                                    : wide_t<64, 2, HALO_WIDE_QT>(q, k, v, rh, rw, out, lse, g, st);
+    if (g.d == 64) {
+        // a block of 9..16 query tiles in one workgroup of two tiles per wave
+        // rather than two workgroups (each staging the whole window), the
+        // second nearly idle
+        const int side = (g.block + g.stride - 1) / g.stride;
+        const bool two = (side * side + 15) / 16 > kWideWaves;
+        if (g.r <= 16) return two ? wide_t<64, 1, 2>(q, k, v, rh, rw, out, lse, g, st)
+                                  : wide_t<64, 1, 1>(q, k, v, rh, rw, out, lse, g, st);
+        return two ? wide_t<64, 2, 2>(q, k, v, rh, rw, out, lse, g, st)
+                   : wide_t<64, 2, 1>(q, k, v, rh, rw, out, lse, g, st);
+    }
     if (g.d == 32) return wide_t<32, 3, HALO_WIDE_QT>(q, k, v, rh, rw, out, lse, g, st);
     return wide_t<16, 3, HALO_WIDE_QT>(q, k, v, rh, rw, out, lse, g, st);
 }

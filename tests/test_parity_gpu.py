@@ -87,6 +87,7 @@ SMALL = [
     (1, 2, 36, 36, 64, 12, 3, 1),   # d = 64, 18x18 window (two column chunks)
     (1, 1, 20, 28, 64, 8, 3, 1),    # d = 64, ragged
     (2, 2, 24, 24, 64, 8, 3, 2),    # d = 64, strided
+    (1, 2, 24, 28, 64, 12, 2, 1),   # d = 64, 9 query tiles per block: two tiles per wave, ragged
 ]
 
 
