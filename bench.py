@@ -236,6 +236,14 @@ def issue_rates(iters=8000):
     print(json.dumps({"issue_rates": res}), flush=True)
 
 
+def device_info():
+    """The GPU the line was measured on (name, architecture, compute units)."""
+    import torch
+    pr = torch.cuda.get_device_properties(0)
+    return {"name": pr.name, "arch": getattr(pr, "gcnArchName", ""), "cus": pr.multi_processor_count,
+            "memory_gib": round(pr.total_memory / 2 ** 30, 1)}
+
+
 def copy_bandwidth_gbs(mib=512, reps=10):
     """Achievable HBM bandwidth as context for the spec peak: a plain device
     copy (torch copy_) of `mib` MiB, event-timed over `reps` copies after two
@@ -735,6 +743,7 @@ def _measure(args, wl, step, stream, nsets, lib, dcode, flags, variants, bwd, st
             "kernel_sources": src_hash,
         },
         "launch_stats": launch_stats,
+        "device": device_info(),
     }
     return line
 
