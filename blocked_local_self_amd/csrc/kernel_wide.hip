@@ -65,6 +65,7 @@ struct WidePlan {
     int SW;           // LDS row pitch in columns (16 * NCH)
     int RP;           // relative-table rows padded to 16
     int HR;           // height rows kept per query tile (r rounded up to 16)
+    int CPv;          // V^T channel pitch in elements (kWideRows * SW, padded)
     int off_v, off_rel, off_hgt, lds_bytes;
     int remap_xcd;
     int64_t nwg;
@@ -82,8 +83,14 @@ void wide_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     constexpr int CPP = D / 8;                // 16-byte chunks per pixel
     typedef typename WFrag<D>::T FragT;
     extern __shared__ __align__(16) unsigned char smem[];
-    __bf16* Kc = reinterpret_cast<__bf16*>(smem);                  // [kWideRows][SW][D]
-    __bf16* Vc = reinterpret_cast<__bf16*>(smem + p.off_v);        // [D][kWideRows][SW]
+    __bf16* Kc = reinterpret_cast<__bf16*>(smem);                  // [kWideRows][SW][D], swizzled
+    // K pixels hold their 16-byte (8-channel) units in an order XOR-ed with
+    // bits of the column, so the 16 (8-byte reads) or 8 (16-byte reads)
+    // lanes of one LDS pass, which read one unit of consecutive columns, fall
+    // on different banks (two lanes per bank pair at d = 16)
+    constexpr int KSH = D == 16 ? 2 : D == 32 ? 1 : 0;
+    auto kunit = [](int col, int unit) { return (unit ^ ((col >> KSH) & (CPP - 1))) * 8; };
+    __bf16* Vc = reinterpret_cast<__bf16*>(smem + p.off_v);        // [D][CPv >= kWideRows * SW]
     __bf16* Rh = reinterpret_cast<__bf16*>(smem + p.off_rel);      // [RP][D]
     __bf16* Rw = Rh + p.RP * D;                                     // [RP][D]
 
@@ -231,28 +238,39 @@ void wide_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 }
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<u32x4*>(Kc + ((size_t)(tr * SW + 4 * c4 + j) * D + ch * 8)) = kk[j];
+                    *reinterpret_cast<u32x4*>(Kc + ((size_t)(tr * SW + 4 * c4 + j) * D + kunit(4 * c4 + j, ch))) = kk[j];
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
                     const u32x2 lo = {__builtin_amdgcn_perm(vv[1][w], vv[0][w], 0x05040100u),
                                       __builtin_amdgcn_perm(vv[3][w], vv[2][w], 0x05040100u)};
                     const u32x2 hi = {__builtin_amdgcn_perm(vv[1][w], vv[0][w], 0x07060302u),
                                       __builtin_amdgcn_perm(vv[3][w], vv[2][w], 0x07060302u)};
-                    *reinterpret_cast<u32x2*>(Vc + ((size_t)(ch * 8 + 2 * w) * kWideRows + tr) * SW + 4 * c4) = lo;
-                    *reinterpret_cast<u32x2*>(Vc + ((size_t)(ch * 8 + 2 * w + 1) * kWideRows + tr) * SW + 4 * c4) = hi;
+                    *reinterpret_cast<u32x2*>(Vc + (size_t)(ch * 8 + 2 * w) * p.CPv + tr * SW + 4 * c4) = lo;
+                    *reinterpret_cast<u32x2*>(Vc + (size_t)(ch * 8 + 2 * w + 1) * p.CPv + tr * SW + 4 * c4) = hi;
                 }
             }
         }
         __syncthreads();
 
         if (active) {
-            const __bf16* kfrag = Kc + ((size_t)n * D + gq * KPL);
+            // lane (n, g): column n of a 16-column chunk (the swizzle depends
+            // on n only: 16 is a multiple of CPP << KSH), channels g*KPL..+KPL-1
+            const __bf16* kfrag0 = Kc + (size_t)n * D + (D == 16 ? kunit(n, gq >> 1) + (gq & 1) * 4
+                                                                : kunit(n, D == 32 ? gq : 2 * gq));
+            const __bf16* kfrag1 = Kc + (size_t)n * D + (D == 64 ? kunit(n, 2 * gq + 1) : 0);
             auto kload = [&](int tr, int ch) -> FragT {
-                return *reinterpret_cast<const FragT*>(kfrag + (size_t)(tr * SW + ch * 16) * D);
+                const size_t o = (size_t)(tr * SW + ch * 16) * D;
+                if constexpr (D == 64) {
+                    const s16x8 lo = *reinterpret_cast<const s16x8*>(kfrag0 + o);
+                    const s16x8 hi = *reinterpret_cast<const s16x8*>(kfrag1 + o);
+                    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+                } else {
+                    return *reinterpret_cast<const FragT*>(kfrag0 + o);
+                }
             };
-            const __bf16* vfrag = Vc + (size_t)n * kWideRows * SW + gq * 4;
+            const __bf16* vfrag = Vc + (size_t)n * p.CPv + gq * 4;
             auto vload = [&](int mt, int tr, int ch) -> u32x2 {
-                return *reinterpret_cast<const u32x2*>(vfrag + (size_t)(mt * 16 * kWideRows + tr) * SW + ch * 16);
+                return *reinterpret_cast<const u32x2*>(vfrag + (size_t)mt * 16 * p.CPv + tr * SW + ch * 16);
             };
             // groups of two window rows (the last may hold one)
             for (int t = c0; t < c1; t += 2) {
@@ -357,9 +375,13 @@ static hipError_t wide_t(const void* q, const void* k, const void* v, const void
     p.RP = wround(2 * g.r - 1, 16);
     p.HR = wround(g.r, 16);
     const int chunk = kWideRows * p.SW * D * 2;
+    // V^T channel pitch: (pitch / 2) = 2 (mod 32) dwords, so the 16 channels
+    // of a fragment read (8 bytes per lane) cover the 32 banks once
+    p.CPv = kWideRows * p.SW;
+    while (p.CPv % 2 || (p.CPv / 2) % 32 != 2) ++p.CPv;
     p.off_v = chunk;
     const int scratch = kWideWaves * p.RP * 16 * 4;             // aliases the chunk buffers
-    p.off_rel = wround(std::max(2 * chunk, scratch), 16);
+    p.off_rel = wround(std::max(chunk + D * p.CPv * 2, scratch), 16);
     p.off_hgt = wround(p.off_rel + 2 * p.RP * D * 2, 16);
     p.lds_bytes = p.off_hgt + kWideWaves * QT * p.HR * 16 * 4;
     const int side = (g.block + g.stride - 1) / g.stride;
