@@ -84,8 +84,8 @@ MEASURED_TRAFFIC = {
             "kernel": "ring", "sources": "aa21a7f49d15e703"},
         "mid_stage_bf16_32x32_d32_b8h3": {"bytes_per_launch": 135622814, "read": 101019806, "write": 34603008,
             "kernel": "ring", "sources": "aa21a7f49d15e703"},
-        "detection_bf16_64x64_d16_b32h3": {"bytes_per_launch": 33733529, "read": 25344921, "write": 8388608,
-            "kernel": "wide", "sources": "84017ea3b487bce8"},
+        "detection_bf16_64x64_d16_b32h3": {"bytes_per_launch": 33729341, "read": 25340733, "write": 8388608,
+            "kernel": "wide", "sources": "270953bdef674c85"},
         "global_bf16_16x16_d16_b16h0": {"bytes_per_launch": 17115746, "read": 12921442, "write": 4194304,
             "kernel": "ring", "sources": "aa21a7f49d15e703"},
     },

@@ -414,7 +414,16 @@ hipError_t launch_wide(const void* q, const void* k, const void* v, const void* 
         return two ? wide_t<64, 2, 2>(q, k, v, rh, rw, out, lse, g, st)
                    : wide_t<64, 2, 1>(q, k, v, rh, rw, out, lse, g, st);
     }
-    if (g.d == 32) return wide_t<32, 3, HALO_WIDE_QT>(q, k, v, rh, rw, out, lse, g, st);
+    if (g.d == 32) {
+        // one workgroup per CU (121 KB of LDS), two waves per SIMD: two query
+        // tiles per wave give each wave independent MFMA -> exp -> MFMA chains
+        // to interleave (r = 38 at block 32: 189 -> 151 us), where a block
+        // has the tiles to keep all eight waves busy; at d = 16 (two
+        // workgroups per CU) a second tile per wave measured slower
+        const int side = (g.block + g.stride - 1) / g.stride;
+        if ((side * side + 15) / 16 >= 2 * kWideWaves) return wide_t<32, 3, 2>(q, k, v, rh, rw, out, lse, g, st);
+        return wide_t<32, 3, HALO_WIDE_QT>(q, k, v, rh, rw, out, lse, g, st);
+    }
     return wide_t<16, 3, HALO_WIDE_QT>(q, k, v, rh, rw, out, lse, g, st);
 }
 
